@@ -1,0 +1,187 @@
+"""Seeded synthetic inputs for the bit-nested quantized linear.
+
+This module only draws random numbers and lays them out in the canonical
+storage format that the C-ABI and the oracle both accept.  It holds none of
+the method's arithmetic (no rotation, no dequantisation, no contraction):
+both the oracle and the HIP path consume what it produces.
+
+Canonical storage format (per linear, W is d_out x d_in, G = ceil(d_in/128)
+groups of 128 consecutive input columns per output row; the "bit-nested"
+forum post, POC recipe sections 2 and 3):
+
+* base_codes  uint8 [d_out][G][32]: two bit-planes of 16 bytes each.  Bytes
+  0..15 hold bit 0 of every 2-bit code, bytes 16..31 bit 1.  Code j of the
+  group sits at bit (j & 7) of byte (j >> 3) of each plane (LSB first).
+  Code c selects levels[c]; levels are ascending.
+* base_scales uint16 [d_out][G]: IEEE fp16 bit patterns.
+* resid_codes uint8 [d_out][G][16*b]: the group's 128 b-bit two's-complement
+  fields, field j at bits [j*b, (j+1)*b) of the group's little-endian bit
+  string.
+* resid_scales uint16 [d_out][G]: fp16 bit patterns.
+* sign_in int8 [d_in], sign_out int8 [d_out] (or None): +-1.
+* x uint16 [T][d_in]: bf16 bit patterns.
+
+A ragged last group (d_in not a multiple of 128; only the oracle accepts it)
+keeps the full-size byte block with the unused fields zero.
+
+Seeds: every array is a pure function of SeedSequence([20261008, cfg,
+linear_idx, stream]) with numpy's PCG64, so the host regenerates one linear
+at a time.  Stream ids: 0 sign_in, 1 sign_out, 2 base codes, 3 base scales,
+4 residual codes, 5 residual scales, 6 x, 7 router logits.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+SEED0 = 20261008
+GROUP = 128
+
+# The four base levels of the synthetic workloads: the Gaussian 4-level
+# Lloyd-Max quantiser, as fitted in the forum post's POC section 2 (its
+# fitted values are within 0.5% of these).
+LEVELS = np.array([-1.5104, -0.4528, 0.4528, 1.5104], dtype=np.float32)
+
+STREAM_SIGN_IN, STREAM_SIGN_OUT, STREAM_BASE, STREAM_BASE_SCALE = 0, 1, 2, 3
+STREAM_RESID, STREAM_RESID_SCALE, STREAM_X, STREAM_ROUTER = 4, 5, 6, 7
+
+
+def rng(cfg: int, linear_idx: int, stream: int) -> np.random.Generator:
+    return np.random.Generator(
+        np.random.PCG64(np.random.SeedSequence([SEED0, cfg, linear_idx, stream])))
+
+
+def groups(d_in: int) -> int:
+    return (d_in + GROUP - 1) // GROUP
+
+
+def qmax(bits: int) -> int:
+    return (1 << (bits - 1)) - 1
+
+
+def resid_sigma(bits: int) -> float:
+    """Spread of the synthetic residual codes: N(0, 20) for 8-bit, scaled by
+    qm/127 for narrower grids, so every width uses the same share of its
+    range."""
+    return 20.0 * qmax(bits) / 127.0
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 (nearest-even) and return the 16-bit patterns."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint32) << 16).view(np.float32)
+
+
+def _pad_cols(a: np.ndarray, d_in: int) -> np.ndarray:
+    g = groups(d_in)
+    if g * GROUP == d_in:
+        return a
+    out = np.zeros(a.shape[:-1] + (g * GROUP,), dtype=a.dtype)
+    out[..., :d_in] = a
+    return out
+
+
+def pack_base(codes: np.ndarray) -> np.ndarray:
+    """codes uint8 [d_out][d_in] in 0..3 -> canonical [d_out][G][32] bytes."""
+    d_out, d_in = codes.shape
+    c = _pad_cols(codes.astype(np.uint8), d_in).reshape(d_out, groups(d_in), GROUP)
+    p0 = np.packbits(c & 1, axis=-1, bitorder="little")          # [d_out][G][16]
+    p1 = np.packbits((c >> 1) & 1, axis=-1, bitorder="little")
+    return np.ascontiguousarray(np.concatenate([p0, p1], axis=-1))
+
+
+def pack_resid(q: np.ndarray, bits: int) -> np.ndarray:
+    """q int [d_out][d_in] in [-2^(b-1), 2^(b-1)-1] -> canonical
+    [d_out][G][16*b] bytes of LSB-first b-bit two's-complement fields."""
+    d_out, d_in = q.shape
+    u = _pad_cols(q.astype(np.int64), d_in).reshape(d_out, groups(d_in), GROUP)
+    u = u & ((1 << bits) - 1)
+    bitarr = ((u[..., None] >> np.arange(bits)) & 1).astype(np.uint8)  # [.., 128, b]
+    bitarr = bitarr.reshape(d_out, groups(d_in), GROUP * bits)
+    return np.ascontiguousarray(np.packbits(bitarr, axis=-1, bitorder="little"))
+
+
+def make_signs(n: int, cfg: int, idx: int, stream: int) -> np.ndarray:
+    return (rng(cfg, idx, stream).integers(0, 2, size=n, dtype=np.int8) * 2 - 1).astype(np.int8)
+
+
+def make_scales(d_out: int, d_in: int, cfg: int, idx: int, stream: int,
+                lo: float = 0.005, hi: float = 0.02) -> np.ndarray:
+    s = rng(cfg, idx, stream).uniform(lo, hi, size=(d_out, groups(d_in)))
+    return np.ascontiguousarray(s.astype(np.float16).view(np.uint16))
+
+
+def make_base_codes(d_out: int, d_in: int, cfg: int, idx: int) -> np.ndarray:
+    return rng(cfg, idx, STREAM_BASE).integers(0, 4, size=(d_out, d_in), dtype=np.uint8)
+
+
+def make_resid_codes(d_out: int, d_in: int, bits: int, cfg: int, idx: int) -> np.ndarray:
+    qm = qmax(bits)
+    v = rng(cfg, idx, STREAM_RESID).normal(0.0, resid_sigma(bits), size=(d_out, d_in))
+    return np.clip(np.rint(v), -qm, qm).astype(np.int8)
+
+
+def make_linear(d_out: int, d_in: int, bits: int, cfg: int = 0, idx: int = 0,
+                two_sided: bool = True, keep_codes: bool = False) -> dict:
+    """One synthetic nested linear in the canonical format.
+
+    bits = 0 gives a draft-only linear (no residual arrays)."""
+    lin = {
+        "d_out": d_out, "d_in": d_in, "bits": bits,
+        "levels": LEVELS.copy(),
+        "sign_in": make_signs(d_in, cfg, idx, STREAM_SIGN_IN),
+        "sign_out": make_signs(d_out, cfg, idx, STREAM_SIGN_OUT) if two_sided else None,
+    }
+    codes = make_base_codes(d_out, d_in, cfg, idx)
+    lin["base_codes"] = pack_base(codes)
+    lin["base_scales"] = make_scales(d_out, d_in, cfg, idx, STREAM_BASE_SCALE)
+    if keep_codes:
+        lin["base_idx"] = codes
+    if bits:
+        q = make_resid_codes(d_out, d_in, bits, cfg, idx)
+        lin["resid_codes"] = pack_resid(q, bits)
+        lin["resid_scales"] = make_scales(d_out, d_in, cfg, idx, STREAM_RESID_SCALE)
+        if keep_codes:
+            lin["resid_q"] = q
+    else:
+        lin["resid_codes"] = None
+        lin["resid_scales"] = None
+    return lin
+
+
+def make_x(T: int, d_in: int, cfg: int = 0, idx: int = 0, scale: float = 1.0) -> np.ndarray:
+    """bf16 activations N(0, scale^2) as uint16 bit patterns [T][d_in]."""
+    v = rng(cfg, idx, STREAM_X).standard_normal(size=(T, d_in)).astype(np.float32) * scale
+    return f32_to_bf16_bits(v)
+
+
+def router_topk(T: int, n_experts: int, k: int, rho: float, cfg: int = 4, idx: int = 0):
+    """Router logits for a block of T tokens: every logit is marginally N(0,1);
+    tokens of the block share a common component with correlation rho
+    (rho = 0 is iid routing).  Returns (experts [T][k] int32, sorted pairs).
+
+    The pairs are (token, expert) sorted by expert, then token; returns
+    pair_token int32 [P], expert_offsets int32 [n_experts+1]."""
+    r = rng(cfg, idx, STREAM_ROUTER)
+    g = r.standard_normal(n_experts)
+    z = r.standard_normal((T, n_experts))
+    logits = np.sqrt(rho) * g[None, :] + np.sqrt(1.0 - rho) * z
+    top = np.argsort(-logits, axis=1, kind="stable")[:, :k].astype(np.int32)
+    pairs = sorted((int(e), t) for t in range(T) for e in top[t])
+    pair_token = np.array([t for _, t in pairs], dtype=np.int32)
+    counts = np.bincount(np.array([e for e, _ in pairs], dtype=np.int64), minlength=n_experts)
+    offsets = np.zeros(n_experts + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    return top, pair_token, offsets
+
+
+def bytes_per_weight(bits: int) -> float:
+    """Streamed bytes per weight of one pass: codes plus fp16 group scales."""
+    b = (2 * GROUP + 16) / 8 / GROUP            # 2-bit base + fp16 scale
+    if bits:
+        b += (bits * GROUP + 16) / 8 / GROUP
+    return b
