@@ -1,0 +1,233 @@
+"""Python binding of libnested_linear.so, the bit-nested quantized linear for
+AMD MI355X (gfx950).
+
+Argument marshalling only: every step of the draft/verify forward runs in the
+library's HIP kernels.  The functions carry the C ABI's names
+(include/nested_linear.h); tensors are torch device tensors, the stream is
+the current torch stream unless given.  A failing call raises NLError with
+the library's message.  The library is built in-tree by
+``bit_nested_quantized_amd.build.build()``; importing this package never
+falls back to anything else: if the library is missing, the first call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libnested_linear.so")
+
+NL_OK, NL_EINVAL, NL_ENOMEM, NL_EHIP, NL_EUNSUPPORTED = 0, 1, 2, 3, 4
+NL_MAX_T = 64
+
+# Every symbol the C header declares (checked by the CPU tests).
+EXPORTS = (
+    "nested_linear_create", "nested_linear_destroy", "nested_linear_workspace_bytes",
+    "nested_linear_verify", "nested_linear_draft", "nested_linear_prepare_input",
+    "nested_linear_contract", "nested_linear_finish", "nested_linear_group_create",
+    "nested_linear_group_destroy", "nested_linear_group_workspace_bytes",
+    "nested_linear_verify_grouped", "nested_linear_draft_grouped", "nested_linear_decode",
+    "nested_linear_info", "nested_linear_last_error",
+)
+
+
+class NLError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"status {status}: {msg}")
+        self.status = status
+
+
+class nl_desc(ctypes.Structure):
+    _fields_ = [
+        ("d_out", ctypes.c_int32), ("d_in", ctypes.c_int32), ("residual_bits", ctypes.c_int32),
+        ("base_codes", ctypes.c_void_p), ("base_scales", ctypes.c_void_p),
+        ("resid_codes", ctypes.c_void_p), ("resid_scales", ctypes.c_void_p),
+        ("sign_in", ctypes.c_void_p), ("sign_out", ctypes.c_void_p),
+        ("levels", ctypes.c_float * 4),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run bit_nested_quantized_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        sig = {
+            "nested_linear_create": [ctypes.POINTER(nl_desc), ctypes.POINTER(P)],
+            "nested_linear_destroy": [P],
+            "nested_linear_workspace_bytes": [P, i32, ctypes.POINTER(sz)],
+            "nested_linear_verify": [P, P, i32, P, P, sz, P],
+            "nested_linear_draft": [P, P, i32, P, P, sz, P],
+            "nested_linear_prepare_input": [P, P, i32, P, sz, P],
+            "nested_linear_contract": [P, i32, i32, P, P, sz, P],
+            "nested_linear_finish": [P, i32, P, P, sz, P],
+            "nested_linear_group_create": [P, i32, ctypes.POINTER(P)],
+            "nested_linear_group_destroy": [P],
+            "nested_linear_group_workspace_bytes": [P, i32, ctypes.POINTER(sz)],
+            "nested_linear_verify_grouped": [P, P, P, i32, P, i32, P, P, sz, P],
+            "nested_linear_draft_grouped": [P, P, P, i32, P, i32, P, P, sz, P],
+            "nested_linear_decode": [P, i32, i32, P, P, P],
+            "nested_linear_info": [P] + [ctypes.POINTER(i32)] * 5 + [ctypes.POINTER(ctypes.c_float)],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.nested_linear_last_error.argtypes = []
+        L.nested_linear_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(st: int):
+    if st != NL_OK:
+        raise NLError(st, lib().nested_linear_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(getattr(stream, "cuda_stream", stream))
+
+
+def nested_linear_create(d_out: int, d_in: int, residual_bits: int, base_codes, base_scales,
+                         resid_codes, resid_scales, sign_in, sign_out, levels) -> ctypes.c_void_p:
+    """Device tensors of the canonical format (uint8 codes, fp16-bit scales as
+    int16/uint16, int8 signs); levels is a host sequence of 4 floats."""
+    d = nl_desc(int(d_out), int(d_in), int(residual_bits), _ptr(base_codes), _ptr(base_scales),
+                _ptr(resid_codes), _ptr(resid_scales), _ptr(sign_in), _ptr(sign_out),
+                (ctypes.c_float * 4)(*[float(v) for v in levels]))
+    h = ctypes.c_void_p()
+    _check(lib().nested_linear_create(ctypes.byref(d), ctypes.byref(h)))
+    return h
+
+
+def nested_linear_destroy(h):
+    _check(lib().nested_linear_destroy(h))
+
+
+def nested_linear_workspace_bytes(h, T_max: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().nested_linear_workspace_bytes(h, int(T_max), ctypes.byref(n)))
+    return n.value
+
+
+def nested_linear_verify(h, x, T: int, y, ws, stream=None):
+    _check(lib().nested_linear_verify(h, _ptr(x), int(T), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
+                                      _stream(stream)))
+
+
+def nested_linear_draft(h, x, T: int, y, ws, stream=None):
+    _check(lib().nested_linear_draft(h, _ptr(x), int(T), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
+                                     _stream(stream)))
+
+
+def nested_linear_prepare_input(h, x, T: int, ws, stream=None):
+    _check(lib().nested_linear_prepare_input(h, _ptr(x), int(T), _ptr(ws), ws.numel() * ws.element_size(),
+                                             _stream(stream)))
+
+
+def nested_linear_contract(h, verify: bool, T: int, y, ws, stream=None):
+    _check(lib().nested_linear_contract(h, int(bool(verify)), int(T), _ptr(y), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def nested_linear_finish(h, T: int, y, ws, stream=None):
+    _check(lib().nested_linear_finish(h, int(T), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
+                                      _stream(stream)))
+
+
+def nested_linear_group_create(handles) -> ctypes.c_void_p:
+    arr = (ctypes.c_void_p * len(handles))(*[h.value for h in handles])
+    g = ctypes.c_void_p()
+    _check(lib().nested_linear_group_create(arr, len(handles), ctypes.byref(g)))
+    return g
+
+
+def nested_linear_group_destroy(g):
+    _check(lib().nested_linear_group_destroy(g))
+
+
+def nested_linear_group_workspace_bytes(g, P_max: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().nested_linear_group_workspace_bytes(g, int(P_max), ctypes.byref(n)))
+    return n.value
+
+
+def nested_linear_verify_grouped(g, pair_token, offsets, P: int, x, T: int, y, ws, stream=None):
+    _check(lib().nested_linear_verify_grouped(g, _ptr(pair_token), _ptr(offsets), int(P), _ptr(x), int(T),
+                                              _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
+                                              _stream(stream)))
+
+
+def nested_linear_draft_grouped(g, pair_token, offsets, P: int, x, T: int, y, ws, stream=None):
+    _check(lib().nested_linear_draft_grouped(g, _ptr(pair_token), _ptr(offsets), int(P), _ptr(x), int(T),
+                                             _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
+                                             _stream(stream)))
+
+
+def nested_linear_decode(h, row0: int, nrows: int, base_idx, resid, stream=None):
+    _check(lib().nested_linear_decode(h, int(row0), int(nrows), _ptr(base_idx), _ptr(resid), _stream(stream)))
+
+
+def nested_linear_info(h) -> dict:
+    v = [ctypes.c_int32() for _ in range(5)]
+    e = ctypes.c_float()
+    _check(lib().nested_linear_info(h, *[ctypes.byref(x) for x in v], ctypes.byref(e)))
+    return {"d_out": v[0].value, "d_in": v[1].value, "bits": v[2].value, "block_in": v[3].value,
+            "block_out": v[4].value, "level_rel_err": e.value}
+
+
+class Linear:
+    """Owns one nested linear built from a canonical dict (numpy arrays as
+    produced by ``synth.make_linear``), copied to ``device`` first."""
+
+    def __init__(self, lin: dict, device="cuda"):
+        import numpy as np
+        import torch
+
+        def dev(a, dt):
+            return None if a is None else torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(device)
+
+        bufs = dict(
+            base_codes=dev(lin["base_codes"], np.uint8), base_scales=dev(lin["base_scales"], np.int16),
+            resid_codes=dev(lin["resid_codes"], np.uint8), resid_scales=dev(lin["resid_scales"], np.int16),
+            sign_in=dev(lin["sign_in"], np.int8), sign_out=dev(lin["sign_out"], np.int8))
+        self.d_out, self.d_in, self.bits = lin["d_out"], lin["d_in"], lin["bits"]
+        self.h = nested_linear_create(self.d_out, self.d_in, self.bits, levels=lin["levels"], **bufs)
+
+    def close(self):
+        if self.h is not None:
+            nested_linear_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace(self, T_max: int, device="cuda"):
+        import torch
+        n = nested_linear_workspace_bytes(self.h, T_max)
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+    def forward(self, x, verify: bool, ws=None, y=None, stream=None):
+        """x: int16/uint16 bf16-bit tensor [T][d_in] (or torch.bfloat16)."""
+        import torch
+        T = x.shape[0]
+        ws = self.workspace(T) if ws is None else ws
+        y = torch.empty((T, self.d_out), dtype=torch.float32, device=x.device) if y is None else y
+        (nested_linear_verify if verify else nested_linear_draft)(self.h, x, T, y, ws, stream)
+        return y

@@ -1,0 +1,602 @@
+// nl_api.hip -- the C ABI (include/nested_linear.h): validation, create-time
+// repack, workspace layout, launch configuration.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+#include "../../include/nested_linear.h"
+#include "nl_kernels.h"
+
+using namespace nl;
+
+static thread_local std::string g_err;
+
+static nl_status fail(nl_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+static nl_status fail(nl_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+static nl_status ok() {
+  g_err.clear();
+  return NL_OK;
+}
+
+#define HIP_OR_FAIL(expr)                                                              \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess)                                                              \
+      return fail(NL_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_));            \
+  } while (0)
+
+static constexpr uint32_t kMagic = 0x4E4C4C31u;   // "NLL1"
+static constexpr uint32_t kGroupMagic = 0x4E4C4731u;
+
+struct nl_linear {
+  uint32_t magic;
+  int d_out, d_in, bits, G, n_tiles, n_chunks, b_in, b_out;
+  bool has_sign_out;
+  float level_err;
+  void *mem;
+  size_t mem_bytes;
+  LinearDev dev;
+};
+
+struct nl_group {
+  uint32_t magic;
+  int n, d_out, d_in, bits, n_tiles, n_chunks, b_in, b_out;
+  bool has_sign_out;
+  LinearDev *dev_array;  // device copy of the experts' descriptors
+};
+
+static int block_size(int n) {  // POC section 1 "Block size" rule
+  int b = 1;
+  while (n % (2 * b) == 0 && 2 * b <= 4096) b *= 2;
+  return b;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Round a float to the nearest fp16 (ties to even) and return its bits.
+static uint16_t f2h_bits(float f) {
+  _Float16 h = (_Float16)f;
+  uint16_t b;
+  memcpy(&b, &h, 2);
+  return b;
+}
+
+static float h_bits2f(uint16_t b) {
+  _Float16 h;
+  memcpy(&h, &b, 2);
+  return (float)h;
+}
+
+// Pick kappa so that fp16(kappa * levels[c]) is as close as possible to
+// kappa * levels[c] for all four levels (relative error), then build the
+// fp16x2 pair table used by the kernels' base unpack.
+static void build_lut(const float levels[4], uint32_t lut[16], float *kinv, float *err_out) {
+  float lmax = 0.f;
+  for (int c = 0; c < 4; ++c) lmax = fmaxf(lmax, fabsf(levels[c]));
+  double best_err = 1e30;
+  double best_kappa = 1.0;
+  if (lmax > 0.f) {
+    // kappa * lmax spans one binade of fp16 in steps of 1/8 ulp.
+    for (int n = 1024 * 8; n < 2048 * 8; ++n) {
+      const double kappa = (n / 8.0) / (double)lmax;
+      double e = 0.0;
+      for (int c = 0; c < 4; ++c) {
+        if (levels[c] == 0.f) continue;
+        const double want = kappa * (double)levels[c];
+        const double got = (double)h_bits2f(f2h_bits((float)want));
+        e = fmax(e, fabs(got - want) / fabs(want));
+      }
+      if (e < best_err) {
+        best_err = e;
+        best_kappa = kappa;
+      }
+    }
+  } else {
+    best_err = 0.0;
+  }
+  uint16_t hb[4];
+  for (int c = 0; c < 4; ++c) hb[c] = f2h_bits((float)(best_kappa * (double)levels[c]));
+  for (int i = 0; i < 16; ++i) lut[i] = (uint32_t)hb[i & 3] | ((uint32_t)hb[i >> 2] << 16);
+  *kinv = (float)(1.0 / best_kappa);
+  *err_out = (float)best_err;
+}
+
+// Live handles, so that NULL, destroyed or foreign pointers are rejected
+// without being dereferenced.
+static std::mutex g_live_mu;
+static std::unordered_set<const void *> g_live;
+
+static void live_add(const void *p) {
+  std::lock_guard<std::mutex> lk(g_live_mu);
+  g_live.insert(p);
+}
+static void live_del(const void *p) {
+  std::lock_guard<std::mutex> lk(g_live_mu);
+  g_live.erase(p);
+}
+static bool live(const void *p) {
+  std::lock_guard<std::mutex> lk(g_live_mu);
+  return g_live.count(p) != 0;
+}
+static bool valid(nl_handle h) { return h && live(h) && h->magic == kMagic; }
+static bool valid(nl_group_handle g) { return g && live(g) && g->magic == kGroupMagic; }
+
+extern "C" const char *nested_linear_last_error(void) { return g_err.c_str(); }
+
+extern "C" nl_status nested_linear_create(const nl_desc *d, nl_handle *out) {
+  if (!d || !out) return fail(NL_EINVAL, "create: NULL desc or out");
+  if (d->d_out < 1) return fail(NL_EINVAL, "create: d_out must be >= 1 (got %d)", d->d_out);
+  if (d->d_in < NL_GROUP || d->d_in % NL_GROUP)
+    return fail(NL_EINVAL, "create: d_in must be a positive multiple of 128 (got %d)", d->d_in);
+  const int bits = d->residual_bits;
+  if (bits != 0 && bits != 6 && bits != 7 && bits != 8)
+    return fail(NL_EINVAL, "create: residual_bits must be 0, 6, 7 or 8 (got %d)", bits);
+  if (!d->base_codes || !d->base_scales || !d->sign_in)
+    return fail(NL_EINVAL, "create: base_codes, base_scales and sign_in are required");
+  if (bits && (!d->resid_codes || !d->resid_scales))
+    return fail(NL_EINVAL, "create: residual arrays are required when residual_bits > 0");
+  if (!bits && (d->resid_codes || d->resid_scales))
+    return fail(NL_EINVAL, "create: residual arrays given with residual_bits == 0");
+  for (int c = 0; c < 4; ++c)
+    if (!std::isfinite(d->levels[c])) return fail(NL_EINVAL, "create: level %d is not finite", c);
+
+  // Signs: copied to the host once and checked to be +-1.
+  std::vector<int8_t> si(d->d_in), so(d->sign_out ? d->d_out : 0);
+  HIP_OR_FAIL(hipMemcpy(si.data(), d->sign_in, si.size(), hipMemcpyDeviceToHost));
+  if (d->sign_out) HIP_OR_FAIL(hipMemcpy(so.data(), d->sign_out, so.size(), hipMemcpyDeviceToHost));
+  for (size_t i = 0; i < si.size(); ++i)
+    if (si[i] != 1 && si[i] != -1) return fail(NL_EINVAL, "create: sign_in[%zu] = %d is not +-1", i, si[i]);
+  for (size_t i = 0; i < so.size(); ++i)
+    if (so[i] != 1 && so[i] != -1) return fail(NL_EINVAL, "create: sign_out[%zu] = %d is not +-1", i, so[i]);
+
+  nl_linear *h = new (std::nothrow) nl_linear();
+  if (!h) return fail(NL_ENOMEM, "create: host allocation failed");
+  h->d_out = d->d_out;
+  h->d_in = d->d_in;
+  h->bits = bits;
+  h->G = d->d_in / NL_GROUP;
+  h->n_tiles = (d->d_out + kTileRows - 1) / kTileRows;
+  h->n_chunks = (d->d_in + kChunk - 1) / kChunk;
+  h->b_in = block_size(d->d_in);
+  h->b_out = block_size(d->d_out);
+  h->has_sign_out = d->sign_out != nullptr;
+
+  const size_t tcs = (size_t)h->n_tiles * h->n_chunks;
+  const size_t o_base = 0;
+  const size_t o_resid = align256(o_base + tcs * kBaseBlockBytes);
+  const size_t o_bsc = align256(o_resid + (bits ? tcs * resid_block_bytes(bits) : 0));
+  const size_t o_rsc = align256(o_bsc + tcs * kScaleBlockBytes);
+  const size_t o_si = align256(o_rsc + (bits ? tcs * kScaleBlockBytes : 0));
+  const size_t o_so = align256(o_si + d->d_in);
+  const size_t total = align256(o_so + (d->sign_out ? d->d_out : 0));
+  hipError_t e = hipMalloc(&h->mem, total);
+  if (e != hipSuccess) {
+    delete h;
+    (void)hipGetLastError();
+    return fail(NL_ENOMEM, "create: hipMalloc(%zu) failed: %s", total, hipGetErrorString(e));
+  }
+  h->mem_bytes = total;
+  char *m = (char *)h->mem;
+  LinearDev &L = h->dev;
+  memset(&L, 0, sizeof L);
+  L.base = (const uint4 *)(m + o_base);
+  L.resid = bits ? (const uint4 *)(m + o_resid) : nullptr;
+  L.bscale = (const uint2 *)(m + o_bsc);
+  L.rscale = bits ? (const uint2 *)(m + o_rsc) : nullptr;
+  L.sign_in = (const int8_t *)(m + o_si);
+  L.sign_out = d->sign_out ? (const int8_t *)(m + o_so) : nullptr;
+  build_lut(d->levels, L.lut, &L.kinv, &h->level_err);
+
+  RepackArgs ra;
+  ra.base_codes = d->base_codes;
+  ra.base_scales = d->base_scales;
+  ra.resid_codes = d->resid_codes;
+  ra.resid_scales = d->resid_scales;
+  ra.base = (uint4 *)(m + o_base);
+  ra.resid = bits ? (uint4 *)(m + o_resid) : nullptr;
+  ra.bscale = (uint16_t *)(m + o_bsc);
+  ra.rscale = bits ? (uint16_t *)(m + o_rsc) : nullptr;
+  ra.d_out = h->d_out;
+  ra.d_in = h->d_in;
+  ra.G = h->G;
+  ra.n_tiles = h->n_tiles;
+  ra.n_chunks = h->n_chunks;
+  e = launch_repack(ra, bits, nullptr);
+  if (e == hipSuccess) e = hipMemcpy(m + o_si, si.data(), si.size(), hipMemcpyHostToDevice);
+  if (e == hipSuccess && d->sign_out) e = hipMemcpy(m + o_so, so.data(), so.size(), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    (void)hipFree(h->mem);
+    delete h;
+    return fail(NL_EHIP, "create: repack failed: %s", hipGetErrorString(e));
+  }
+  h->magic = kMagic;
+  live_add(h);
+  *out = h;
+  return ok();
+}
+
+extern "C" nl_status nested_linear_destroy(nl_handle h) {
+  if (!valid(h)) return fail(NL_EINVAL, "destroy: invalid handle");
+  live_del(h);
+  h->magic = 0;
+  hipError_t e = hipFree(h->mem);
+  delete h;
+  if (e != hipSuccess) return fail(NL_EHIP, "destroy: hipFree failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+extern "C" nl_status nested_linear_info(nl_handle h, int32_t *d_out, int32_t *d_in, int32_t *bits,
+                                        int32_t *block_in, int32_t *block_out, float *level_rel_err) {
+  if (!valid(h)) return fail(NL_EINVAL, "info: invalid handle");
+  if (d_out) *d_out = h->d_out;
+  if (d_in) *d_in = h->d_in;
+  if (bits) *bits = h->bits;
+  if (block_in) *block_in = h->b_in;
+  if (block_out) *block_out = h->b_out;
+  if (level_rel_err) *level_rel_err = h->level_err;
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// Launch plan and workspace layout of one call.
+// ---------------------------------------------------------------------------
+struct Plan {
+  int rows;       // rows of x' (tokens, or pairs for a grouped call)
+  int mt;         // 16-token MFMA tiles
+  int n_rb;       // 64-row workgroups per linear
+  int S, cps;     // split-K count and chunks per split
+  bool finish;    // a finish pass is needed
+  size_t o_xh, o_xs, o_tsc, o_part, total;
+};
+
+static Plan make_plan(int d_out, int n_tiles, int n_chunks, bool sign_out, int rows, int mt,
+                      int n_linears) {
+  Plan p;
+  p.rows = rows;
+  p.mt = mt;
+  p.n_rb = (n_tiles + 3) / 4;
+  // Split K until the grid holds ~2 workgroups per CU (256 CUs), keeping at
+  // least 2 chunks per split.
+  const int want = 512;
+  int S = (want + p.n_rb * n_linears - 1) / (p.n_rb * n_linears);
+  S = S < 1 ? 1 : S;
+  const int smax = n_chunks / 2 > 0 ? n_chunks / 2 : 1;
+  S = S > smax ? smax : S;
+  p.cps = (n_chunks + S - 1) / S;
+  p.S = (n_chunks + p.cps - 1) / p.cps;
+  p.finish = sign_out || p.S > 1 || n_linears > 1;
+  const size_t Kp = (size_t)n_chunks * kChunk;
+  p.o_xh = 0;
+  p.o_xs = align256(p.o_xh + (size_t)rows * Kp * 2);
+  p.o_tsc = align256(p.o_xs + (size_t)rows * n_chunks * 4 * 4);
+  p.o_part = align256(p.o_tsc + (size_t)rows * n_chunks * 4);
+  p.total = align256(p.o_part + (p.finish ? (size_t)p.S * rows * d_out * 4 : 0));
+  return p;
+}
+
+static int mt_for(int T) { return (T + 15) / 16; }
+
+extern "C" nl_status nested_linear_workspace_bytes(nl_handle h, int32_t T_max, size_t *bytes) {
+  if (!valid(h)) return fail(NL_EINVAL, "workspace_bytes: invalid handle");
+  if (!bytes) return fail(NL_EINVAL, "workspace_bytes: NULL bytes");
+  if (T_max < 1) return fail(NL_EINVAL, "workspace_bytes: T_max must be >= 1");
+  if (T_max > NL_MAX_T) return fail(NL_EUNSUPPORTED, "workspace_bytes: T_max > %d", NL_MAX_T);
+  size_t mx = 0;
+  for (int T = 1; T <= T_max; ++T) {
+    Plan p = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, T, mt_for(T), 1);
+    mx = p.total > mx ? p.total : mx;
+  }
+  *bytes = mx;
+  return ok();
+}
+
+static nl_status check_call(nl_handle h, const char *who, int verify, int32_t T, const void *ws,
+                            size_t ws_bytes, Plan *plan) {
+  if (!valid(h)) return fail(NL_EINVAL, "%s: invalid handle", who);
+  if (verify && !h->bits) return fail(NL_EINVAL, "%s: the linear has no residual (draft only)", who);
+  if (T < 1) return fail(NL_EINVAL, "%s: T must be >= 1 (got %d)", who, T);
+  if (T > NL_MAX_T) return fail(NL_EUNSUPPORTED, "%s: T = %d exceeds %d", who, T, NL_MAX_T);
+  if (!ws) return fail(NL_EINVAL, "%s: NULL workspace", who);
+  if ((uintptr_t)ws & 255) return fail(NL_EINVAL, "%s: workspace must be 256-byte aligned", who);
+  *plan = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, T, mt_for(T), 1);
+  if (ws_bytes < plan->total)
+    return fail(NL_EINVAL, "%s: workspace too small (%zu < %zu)", who, ws_bytes, plan->total);
+  return NL_OK;
+}
+
+static RotInArgs rot_args(nl_handle h, const void *x, int T, char *ws, const Plan &p) {
+  RotInArgs r;
+  memset(&r, 0, sizeof r);
+  r.x = (const uint16_t *)x;
+  r.sign = h->dev.sign_in;
+  r.x_rows = T;
+  r.xh = (uint16_t *)(ws + p.o_xh);
+  r.xs = (float *)(ws + p.o_xs);
+  r.tsc = (float *)(ws + p.o_tsc);
+  r.d_in = h->d_in;
+  r.b = h->b_in;
+  r.SB = h->b_in > kChunk ? h->b_in : kChunk;
+  r.Kp = h->n_chunks * kChunk;
+  r.Gp = h->n_chunks * 4;
+  r.n_chunks = h->n_chunks;
+  r.rsqrt_b = (float)(1.0 / std::sqrt((double)h->b_in));
+  return r;
+}
+
+extern "C" nl_status nested_linear_prepare_input(nl_handle h, const void *x, int32_t T, void *ws,
+                                                 size_t ws_bytes, void *stream) {
+  Plan p;
+  nl_status st = check_call(h, "prepare_input", 0, T, ws, ws_bytes, &p);
+  if (st != NL_OK) return st;
+  if (!x) return fail(NL_EINVAL, "prepare_input: NULL x");
+  RotInArgs r = rot_args(h, x, T, (char *)ws, p);
+  HIP_OR_FAIL(launch_rotate_in(r, T, (hipStream_t)stream));
+  return ok();
+}
+
+extern "C" nl_status nested_linear_contract(nl_handle h, int32_t verify, int32_t T, float *y,
+                                            void *ws, size_t ws_bytes, void *stream) {
+  Plan p;
+  nl_status st = check_call(h, "contract", verify, T, ws, ws_bytes, &p);
+  if (st != NL_OK) return st;
+  if (!y && !p.finish) return fail(NL_EINVAL, "contract: NULL y");
+  char *w = (char *)ws;
+  GemmArgs g;
+  memset(&g, 0, sizeof g);
+  g.lin = h->dev;
+  g.xh = (const uint16_t *)(w + p.o_xh);
+  g.xs = (const float *)(w + p.o_xs);
+  g.tsc = (const float *)(w + p.o_tsc);
+  g.out = p.finish ? (float *)(w + p.o_part) : y;
+  g.split_stride = (size_t)T * h->d_out;
+  g.T = T;
+  g.d_out = h->d_out;
+  g.n_tiles = h->n_tiles;
+  g.n_chunks = h->n_chunks;
+  g.Kp = h->n_chunks * kChunk;
+  g.Gp = h->n_chunks * 4;
+  g.cps = p.cps;
+  g.ldo = h->d_out;
+  g.n_rb = p.n_rb;
+  g.n_experts = 1;
+  HIP_OR_FAIL(launch_gemm(g, verify ? h->bits : 0, p.mt, p.S, (hipStream_t)stream));
+  return ok();
+}
+
+extern "C" nl_status nested_linear_finish(nl_handle h, int32_t T, float *y, void *ws, size_t ws_bytes,
+                                          void *stream) {
+  Plan p;
+  nl_status st = check_call(h, "finish", 0, T, ws, ws_bytes, &p);
+  if (st != NL_OK) return st;
+  if (!y) return fail(NL_EINVAL, "finish: NULL y");
+  if (!p.finish) return ok();
+  FinishArgs f;
+  memset(&f, 0, sizeof f);
+  f.part = (const float *)((char *)ws + p.o_part);
+  f.split_stride = (size_t)T * h->d_out;
+  f.y = y;
+  f.sign_out = h->dev.sign_out;
+  f.T = T;
+  f.d_out = h->d_out;
+  f.S = p.S;
+  f.b = h->b_out;
+  f.OB = h->has_sign_out ? h->b_out : 4096;
+  f.rsqrt_b = (float)(1.0 / std::sqrt((double)h->b_out));
+  HIP_OR_FAIL(launch_finish(f, (hipStream_t)stream));
+  return ok();
+}
+
+static nl_status forward(nl_handle h, int verify, const void *x, int32_t T, float *y, void *ws,
+                         size_t ws_bytes, void *stream, const char *who) {
+  Plan p;
+  nl_status st = check_call(h, who, verify, T, ws, ws_bytes, &p);
+  if (st != NL_OK) return st;
+  if (!x || !y) return fail(NL_EINVAL, "%s: NULL x or y", who);
+  if ((st = nested_linear_prepare_input(h, x, T, ws, ws_bytes, stream)) != NL_OK) return st;
+  if ((st = nested_linear_contract(h, verify, T, y, ws, ws_bytes, stream)) != NL_OK) return st;
+  return nested_linear_finish(h, T, y, ws, ws_bytes, stream);
+}
+
+extern "C" nl_status nested_linear_verify(nl_handle h, const void *x, int32_t T, float *y, void *ws,
+                                          size_t ws_bytes, void *stream) {
+  return forward(h, 1, x, T, y, ws, ws_bytes, stream, "verify");
+}
+
+extern "C" nl_status nested_linear_draft(nl_handle h, const void *x, int32_t T, float *y, void *ws,
+                                         size_t ws_bytes, void *stream) {
+  return forward(h, 0, x, T, y, ws, ws_bytes, stream, "draft");
+}
+
+extern "C" nl_status nested_linear_decode(nl_handle h, int32_t row0, int32_t nrows, uint8_t *base_idx,
+                                          int8_t *resid, void *stream) {
+  if (!valid(h)) return fail(NL_EINVAL, "decode: invalid handle");
+  if (!base_idx) return fail(NL_EINVAL, "decode: NULL base_idx");
+  if (row0 < 0 || nrows < 1 || row0 + nrows > h->d_out)
+    return fail(NL_EINVAL, "decode: rows [%d, %d) outside [0, %d)", row0, row0 + nrows, h->d_out);
+  DecodeArgs a;
+  memset(&a, 0, sizeof a);
+  a.lin = h->dev;
+  a.base_idx = base_idx;
+  a.resid = h->bits ? resid : nullptr;
+  a.d_in = h->d_in;
+  a.n_chunks = h->n_chunks;
+  a.row0 = row0;
+  a.nrows = nrows;
+  a.tile0 = row0 / kTileRows;
+  const int tile1 = (row0 + nrows - 1) / kTileRows;
+  HIP_OR_FAIL(launch_decode(a, h->bits, tile1 - a.tile0 + 1, (hipStream_t)stream));
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// Grouped (mixture-of-experts) calls.
+// ---------------------------------------------------------------------------
+extern "C" nl_status nested_linear_group_create(const nl_handle *experts, int32_t n,
+                                                nl_group_handle *out) {
+  if (!experts || !out || n < 1) return fail(NL_EINVAL, "group_create: bad arguments");
+  for (int i = 0; i < n; ++i)
+    if (!valid(experts[i])) return fail(NL_EINVAL, "group_create: expert %d is not a valid handle", i);
+  const nl_linear *e0 = experts[0];
+  for (int i = 1; i < n; ++i) {
+    const nl_linear *e = experts[i];
+    if (e->d_out != e0->d_out || e->d_in != e0->d_in || e->bits != e0->bits ||
+        e->has_sign_out != e0->has_sign_out)
+      return fail(NL_EINVAL, "group_create: expert %d differs in shape, bits or sign_out", i);
+  }
+  std::vector<LinearDev> devs(n);
+  for (int i = 0; i < n; ++i) devs[i] = experts[i]->dev;
+  nl_group *g = new (std::nothrow) nl_group();
+  if (!g) return fail(NL_ENOMEM, "group_create: host allocation failed");
+  hipError_t e = hipMalloc(&g->dev_array, sizeof(LinearDev) * n);
+  if (e != hipSuccess) {
+    delete g;
+    (void)hipGetLastError();
+    return fail(NL_ENOMEM, "group_create: hipMalloc failed: %s", hipGetErrorString(e));
+  }
+  e = hipMemcpy(g->dev_array, devs.data(), sizeof(LinearDev) * n, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(g->dev_array);
+    delete g;
+    return fail(NL_EHIP, "group_create: copy failed: %s", hipGetErrorString(e));
+  }
+  g->n = n;
+  g->d_out = e0->d_out;
+  g->d_in = e0->d_in;
+  g->bits = e0->bits;
+  g->n_tiles = e0->n_tiles;
+  g->n_chunks = e0->n_chunks;
+  g->b_in = e0->b_in;
+  g->b_out = e0->b_out;
+  g->has_sign_out = e0->has_sign_out;
+  g->magic = kGroupMagic;
+  live_add(g);
+  *out = g;
+  return ok();
+}
+
+extern "C" nl_status nested_linear_group_destroy(nl_group_handle g) {
+  if (!valid(g)) return fail(NL_EINVAL, "group_destroy: invalid handle");
+  live_del(g);
+  g->magic = 0;
+  hipError_t e = hipFree(g->dev_array);
+  delete g;
+  if (e != hipSuccess) return fail(NL_EHIP, "group_destroy: hipFree failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+static Plan group_plan(nl_group_handle g, int P, int T) {
+  return make_plan(g->d_out, g->n_tiles, g->n_chunks, g->has_sign_out, P, mt_for(T), g->n);
+}
+
+extern "C" nl_status nested_linear_group_workspace_bytes(nl_group_handle g, int32_t P_max,
+                                                         size_t *bytes) {
+  if (!valid(g)) return fail(NL_EINVAL, "group_workspace_bytes: invalid handle");
+  if (!bytes || P_max < 1) return fail(NL_EINVAL, "group_workspace_bytes: bad arguments");
+  *bytes = group_plan(g, P_max, NL_MAX_T).total;
+  return ok();
+}
+
+static nl_status grouped(nl_group_handle g, int verify, const int32_t *pair_token,
+                         const int32_t *offsets, int32_t P, const void *x, int32_t T, float *y,
+                         void *ws, size_t ws_bytes, void *stream, const char *who) {
+  if (!valid(g)) return fail(NL_EINVAL, "%s: invalid handle", who);
+  if (verify && !g->bits) return fail(NL_EINVAL, "%s: the experts have no residual", who);
+  if (!pair_token || !offsets || !x || !y || !ws) return fail(NL_EINVAL, "%s: NULL pointer", who);
+  if (P < 1 || T < 1) return fail(NL_EINVAL, "%s: P and T must be >= 1", who);
+  if (T > NL_MAX_T) return fail(NL_EUNSUPPORTED, "%s: T = %d exceeds %d", who, T, NL_MAX_T);
+  if ((uintptr_t)ws & 255) return fail(NL_EINVAL, "%s: workspace must be 256-byte aligned", who);
+  Plan p = group_plan(g, P, T);
+  if (ws_bytes < p.total) return fail(NL_EINVAL, "%s: workspace too small (%zu < %zu)", who, ws_bytes, p.total);
+  char *w = (char *)ws;
+  hipStream_t s = (hipStream_t)stream;
+
+  RotInArgs r;
+  memset(&r, 0, sizeof r);
+  r.x = (const uint16_t *)x;
+  r.lins = g->dev_array;
+  r.pair_token = pair_token;
+  r.offsets = offsets;
+  r.n_experts = g->n;
+  r.x_rows = T;
+  r.xh = (uint16_t *)(w + p.o_xh);
+  r.xs = (float *)(w + p.o_xs);
+  r.tsc = (float *)(w + p.o_tsc);
+  r.d_in = g->d_in;
+  r.b = g->b_in;
+  r.SB = g->b_in > kChunk ? g->b_in : kChunk;
+  r.Kp = g->n_chunks * kChunk;
+  r.Gp = g->n_chunks * 4;
+  r.n_chunks = g->n_chunks;
+  r.rsqrt_b = (float)(1.0 / std::sqrt((double)g->b_in));
+  HIP_OR_FAIL(launch_rotate_in(r, P, s));
+
+  GemmArgs ga;
+  memset(&ga, 0, sizeof ga);
+  ga.lins = g->dev_array;
+  ga.offsets = offsets;
+  ga.xh = (const uint16_t *)(w + p.o_xh);
+  ga.xs = (const float *)(w + p.o_xs);
+  ga.tsc = (const float *)(w + p.o_tsc);
+  ga.out = (float *)(w + p.o_part);
+  ga.split_stride = (size_t)P * g->d_out;
+  ga.T = P;
+  ga.d_out = g->d_out;
+  ga.n_tiles = g->n_tiles;
+  ga.n_chunks = g->n_chunks;
+  ga.Kp = r.Kp;
+  ga.Gp = r.Gp;
+  ga.cps = p.cps;
+  ga.ldo = g->d_out;
+  ga.n_rb = p.n_rb;
+  ga.n_experts = g->n;
+  HIP_OR_FAIL(launch_gemm(ga, verify ? g->bits : 0, p.mt, p.S, s));
+
+  FinishArgs f;
+  memset(&f, 0, sizeof f);
+  f.part = (const float *)(w + p.o_part);
+  f.split_stride = (size_t)P * g->d_out;
+  f.y = y;
+  f.lins = g->has_sign_out ? g->dev_array : nullptr;
+  f.offsets = offsets;
+  f.n_experts = g->n;
+  f.T = P;
+  f.d_out = g->d_out;
+  f.S = p.S;
+  f.b = g->b_out;
+  f.OB = g->has_sign_out ? g->b_out : 4096;
+  f.rsqrt_b = (float)(1.0 / std::sqrt((double)g->b_out));
+  HIP_OR_FAIL(launch_finish(f, s));
+  return ok();
+}
+
+extern "C" nl_status nested_linear_verify_grouped(nl_group_handle g, const int32_t *pair_token,
+                                                  const int32_t *offsets, int32_t P, const void *x,
+                                                  int32_t T, float *y, void *ws, size_t ws_bytes,
+                                                  void *stream) {
+  return grouped(g, 1, pair_token, offsets, P, x, T, y, ws, ws_bytes, stream, "verify_grouped");
+}
+
+extern "C" nl_status nested_linear_draft_grouped(nl_group_handle g, const int32_t *pair_token,
+                                                 const int32_t *offsets, int32_t P, const void *x,
+                                                 int32_t T, float *y, void *ws, size_t ws_bytes,
+                                                 void *stream) {
+  return grouped(g, 0, pair_token, offsets, P, x, T, y, ws, ws_bytes, stream, "draft_grouped");
+}

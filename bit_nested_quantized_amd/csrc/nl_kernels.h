@@ -1,0 +1,78 @@
+// nl_kernels.h -- argument blocks and host launchers of the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nl_layout.h"
+
+namespace nl {
+
+struct RepackArgs {
+  const uint8_t *base_codes;
+  const uint16_t *base_scales;
+  const uint8_t *resid_codes;
+  const uint16_t *resid_scales;
+  uint4 *base;
+  uint4 *resid;
+  uint16_t *bscale;
+  uint16_t *rscale;
+  int d_out, d_in, G, n_tiles, n_chunks;
+};
+
+struct DecodeArgs {
+  LinearDev lin;
+  uint8_t *base_idx;
+  int8_t *resid;
+  int d_in, n_chunks, row0, nrows, tile0;
+};
+
+// Input rotation.  Grid (tokens, superblocks of SB columns); for a grouped
+// call token t of the grid is pair t, its activation row is pair_token[t]
+// and its signs those of its expert.
+struct RotInArgs {
+  const uint16_t *x;        // [T][d_in] bf16
+  const int8_t *sign;       // [d_in] (single linear)
+  const LinearDev *lins;    // expert array (grouped) or null
+  const int32_t *pair_token;
+  const int32_t *offsets;
+  int n_experts;
+  int x_rows;               // rows of x (bounds for pair_token)
+  uint16_t *xh;             // [rows][Kp] fp16, scaled per (row, chunk)
+  float *xs;                // [rows][Gp] group sums of xh
+  float *tsc;               // [rows][n_chunks] 2^-s / sqrt(b)
+  int d_in, b, SB, Kp, Gp, n_chunks;
+  float rsqrt_b;
+};
+
+struct GemmArgs {
+  LinearDev lin;            // single linear
+  const LinearDev *lins;    // expert array (grouped) or null
+  const int32_t *offsets;   // grouped: [n_experts + 1]
+  const uint16_t *xh;
+  const float *xs;
+  const float *tsc;
+  float *out;               // [split][rows][ldo]
+  size_t split_stride;
+  int T;                    // rows of x' (tokens or pairs)
+  int d_out, n_tiles, n_chunks, Kp, Gp, cps, ldo, n_rb, n_experts;
+};
+
+struct FinishArgs {
+  const float *part;        // [S][rows][d_out]
+  size_t split_stride;
+  float *y;                 // [rows][d_out]
+  const int8_t *sign_out;   // single linear (or null)
+  const LinearDev *lins;    // grouped: per-pair expert sign_out
+  const int32_t *offsets;
+  int n_experts;
+  int T, d_out, S, b, OB;
+  float rsqrt_b;
+};
+
+hipError_t launch_repack(const RepackArgs &a, int bits, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, int bits, int ntiles, hipStream_t s);
+hipError_t launch_rotate_in(const RotInArgs &a, int rows, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs &a, int bits, int mt, int splits, hipStream_t s);
+hipError_t launch_finish(const FinishArgs &a, hipStream_t s);
+
+}  // namespace nl

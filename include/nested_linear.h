@@ -1,0 +1,204 @@
+/*
+ * nested_linear.h -- C ABI of the bit-nested quantized linear for AMD MI355X
+ * (gfx950).
+ *
+ * The layer is the verifier Linear of the forum post "bit-nested" (page 1 of
+ * the source pages), POC recipe section 4: for a batch of T draft-tree
+ * tokens x[t] (bf16),
+ *
+ *     x'  = H_i S_i x                      (section 1: randomized Hadamard)
+ *     y~  = (Q_base + Q_resid) x'          (sections 2 and 3)
+ *     y   = S_o H_o y~                     (section 1, output side)
+ *
+ * where Q_base[r,k] = levels[c(r,k)] * s_base[r, k/128] is the 2-bit
+ * Lloyd-Max base and Q_resid[r,k] = q(r,k) * s_resid[r, k/128] the uniform
+ * b-bit residual (b = 6, 7 or 8), both in the rotated basis.  The draft
+ * forward is the same without Q_resid ("The draft forward is the same but
+ * without y_r", section 4); it reads only the base planes, the dual-plane
+ * principle of the BitNest paper (page 2, section 3.3 "Dual-Plane Weight
+ * Storage").  H is the normalised Sylvester-Hadamard matrix applied
+ * block-diagonally with block b = the largest power of two dividing the
+ * dimension, capped at 4096 (section 1, "Block size").
+ *
+ * All calls return an nl_status and never abort or throw.  On failure
+ * nested_linear_last_error() returns a message for the calling thread.
+ * Pointers are DEVICE pointers unless marked "host".  Compute calls are
+ * asynchronous on the given hipStream_t (passed as void*, NULL = the null
+ * stream); they never synchronise the host.  Faults inside kernels surface at
+ * the caller's next synchronisation.
+ */
+#ifndef NESTED_LINEAR_H
+#define NESTED_LINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct nl_linear *nl_handle;      /* one nested linear, opaque */
+typedef struct nl_group *nl_group_handle; /* experts of one MoE projection, opaque */
+
+typedef enum {
+  NL_OK = 0,
+  NL_EINVAL = 1,        /* bad argument: shape, pointer, T, bits, workspace */
+  NL_ENOMEM = 2,        /* device allocation failed */
+  NL_EHIP = 3,          /* a HIP runtime call or kernel launch failed */
+  NL_EUNSUPPORTED = 4   /* valid request outside this library's range (T > 64) */
+} nl_status;
+
+#define NL_MAX_T 64       /* largest draft tree per call (prefill is out of scope) */
+#define NL_GROUP 128      /* weights per scale group along d_in */
+
+/*
+ * Canonical packed input of one linear (W is d_out x d_in, G = d_in / 128):
+ *   base_codes   [d_out][G][32] bytes: bytes 0..15 = bit 0 of the group's
+ *                128 codes, bytes 16..31 = bit 1; code j at bit (j & 7) of
+ *                byte (j >> 3) (POC section 2: "2 bit-planes").  Code c
+ *                selects levels[c].
+ *   base_scales  [d_out][G] fp16 bit patterns (one scale per row and 128-group).
+ *   resid_codes  [d_out][G][16*b] bytes: 128 b-bit two's-complement fields,
+ *                field j at bits [j*b, j*b + b) of the group's little-endian
+ *                bit string (POC section 3: "uniform symmetric b-bit").
+ *   resid_scales [d_out][G] fp16 bit patterns.
+ *   sign_in      [d_in] int8, each +1 or -1 (S_i).
+ *   sign_out     [d_out] int8 (S_o), or NULL: the output then stays in the
+ *                rotated basis, y = y~ (the one-sided form).
+ * All arrays are device pointers; they are read only during create.
+ */
+typedef struct {
+  int32_t d_out;              /* >= 1 */
+  int32_t d_in;               /* >= 128 and a multiple of 128 */
+  int32_t residual_bits;      /* 0 (draft-only linear), 6, 7 or 8 */
+  const uint8_t *base_codes;
+  const uint16_t *base_scales;
+  const uint8_t *resid_codes;   /* NULL iff residual_bits == 0 */
+  const uint16_t *resid_scales; /* NULL iff residual_bits == 0 */
+  const int8_t *sign_in;
+  const int8_t *sign_out;       /* may be NULL */
+  float levels[4];              /* host values of the 4 base levels, finite */
+} nl_desc;
+
+/*
+ * Build a linear from the canonical arrays (POC sections 2-3 storage).
+ * Copies and repacks everything into library-owned device memory laid out
+ * for the gfx950 kernels; the caller may free its arrays when this returns.
+ * Synchronises the device.  Errors: NL_EINVAL (shape, bits, NULL pointer,
+ * a sign not +-1, non-finite level), NL_ENOMEM, NL_EHIP.  *out is set only
+ * on success.  A handle is immutable after create: concurrent calls on
+ * different streams are safe when each uses its own workspace.
+ */
+nl_status nested_linear_create(const nl_desc *desc, nl_handle *out);
+
+/* Free a linear.  The caller ensures no call on it is still running. */
+nl_status nested_linear_destroy(nl_handle h);
+
+/*
+ * Bytes of workspace a draft or verify call with up to T_max tokens needs
+ * (host output *bytes).  The workspace is caller-owned device memory,
+ * 256-byte aligned, needs no initialisation, and must not be shared by calls
+ * that may run concurrently.
+ */
+nl_status nested_linear_workspace_bytes(nl_handle h, int32_t T_max, size_t *bytes);
+
+/*
+ * Verify forward (POC section 4): y = S_o H_o ((Q_base + Q_resid) H_i S_i x)
+ * for T tokens, or the rotated-basis y~ when the linear has no sign_out.
+ *   x   [T][d_in] bf16 bit patterns (row-major); y [T][d_out] fp32 output,
+ *       must not overlap x or ws.
+ *   ws  workspace of ws_bytes >= nested_linear_workspace_bytes(h, T).
+ * Weight bytes are streamed from HBM once per call for all T tokens.
+ * Errors: NL_EINVAL (NULL pointer, T < 1, small or misaligned ws, linear
+ * without a residual), NL_EUNSUPPORTED (T > 64), NL_EHIP (launch failure).
+ */
+nl_status nested_linear_verify(nl_handle h, const void *x_bf16, int32_t T, float *y,
+                               void *ws, size_t ws_bytes, void *hip_stream);
+
+/*
+ * Draft forward (POC section 4, "the same but without y_r"): as verify with
+ * Q_resid omitted; only the base planes and base scales are read.
+ */
+nl_status nested_linear_draft(nl_handle h, const void *x_bf16, int32_t T, float *y,
+                              void *ws, size_t ws_bytes, void *hip_stream);
+
+/*
+ * The three stages a draft/verify call runs, exposed for callers that fuse or
+ * time them separately.  They must run in this order, on one stream, with one
+ * workspace and the same T:
+ *   prepare_input  x' = H_i S_i x into ws (POC section 1, "rotate the
+ *                  activation once per Linear");
+ *   contract       y~ = Q x' from the packed planes (verify != 0 adds the
+ *                  residual); writes partial sums into ws, or y directly
+ *                  when the linear is one-sided and needs no reduction;
+ *   finish         sums the partials and applies y = S_o H_o y~ (a no-op
+ *                  when contract already wrote y).
+ * Arguments and errors are those of nested_linear_verify.
+ */
+nl_status nested_linear_prepare_input(nl_handle h, const void *x_bf16, int32_t T,
+                                      void *ws, size_t ws_bytes, void *hip_stream);
+nl_status nested_linear_contract(nl_handle h, int32_t verify, int32_t T, float *y,
+                                 void *ws, size_t ws_bytes, void *hip_stream);
+nl_status nested_linear_finish(nl_handle h, int32_t T, float *y, void *ws, size_t ws_bytes,
+                               void *hip_stream);
+
+/*
+ * Grouped forward of a mixture-of-experts projection (DFlash write-up,
+ * "The verify's own cost": tokens sorted by expert, one grouped launch per
+ * projection instead of a per-expert loop).  All experts share d_out, d_in,
+ * residual_bits and the presence of sign_out; each keeps its own planes,
+ * scales, levels and signs.  group_create copies the experts' device
+ * descriptors; the expert handles must outlive the group.
+ */
+nl_status nested_linear_group_create(const nl_handle *experts /* host array */, int32_t n,
+                                     nl_group_handle *out);
+nl_status nested_linear_group_destroy(nl_group_handle g);
+nl_status nested_linear_group_workspace_bytes(nl_group_handle g, int32_t P_max,
+                                              size_t *bytes);
+/*
+ * Pair p (0 <= p < P) routes token pair_token[p] to the expert e with
+ * expert_offsets[e] <= p < expert_offsets[e+1]; pairs are sorted by expert
+ * and each expert receives at most 64 pairs.
+ *   pair_token     [P] int32 device, values in [0, T)
+ *   expert_offsets [n+1] int32 device, non-decreasing, [0] = 0, [n] = P
+ *   x              [T][d_in] bf16; y [P][d_out] fp32, row p = expert e's
+ *                  forward of token pair_token[p].
+ * Offsets and tokens stay on the device: experts with no pairs cost no
+ * weight traffic and the host never synchronises.  The offsets and tokens
+ * are trusted to satisfy the rules above (they are not validated on the
+ * device).  Errors: NL_EINVAL, NL_EUNSUPPORTED (P > 64 * n or T > 4096),
+ * NL_EHIP.
+ */
+nl_status nested_linear_verify_grouped(nl_group_handle g, const int32_t *pair_token,
+                                       const int32_t *expert_offsets, int32_t P,
+                                       const void *x_bf16, int32_t T, float *y,
+                                       void *ws, size_t ws_bytes, void *hip_stream);
+nl_status nested_linear_draft_grouped(nl_group_handle g, const int32_t *pair_token,
+                                      const int32_t *expert_offsets, int32_t P,
+                                      const void *x_bf16, int32_t T, float *y,
+                                      void *ws, size_t ws_bytes, void *hip_stream);
+
+/*
+ * Test hook: decode rows [row0, row0 + nrows) of the library's internal
+ * packed layout back to integers through the same unpack code the kernels
+ * use.  base_idx [nrows][d_in] uint8 receives the level index 0..3;
+ * resid [nrows][d_in] int8 the residual integer (may be NULL; ignored for a
+ * draft-only linear).  Asynchronous on hip_stream.
+ */
+nl_status nested_linear_decode(nl_handle h, int32_t row0, int32_t nrows, uint8_t *base_idx,
+                               int8_t *resid, void *hip_stream);
+
+/* Host queries: shape, residual bits, the split of d_in into rotation
+ * blocks, and the largest relative error of the base levels as the kernels
+ * hold them (fp16 after a per-linear exact rescale; 0 when exact). */
+nl_status nested_linear_info(nl_handle h, int32_t *d_out, int32_t *d_in, int32_t *bits,
+                             int32_t *block_in, int32_t *block_out, float *level_rel_err);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *nested_linear_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NESTED_LINEAR_H */

@@ -1,0 +1,80 @@
+"""The C-ABI library loads, exports every symbol include/*.h declares, and
+rejects bad arguments before touching the GPU (no compute calls here)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import bit_nested_quantized_amd as nl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        txt = open(h).read()
+        txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+        names |= set(re.findall(r"\b(nested_linear_\w+)\s*\(", txt))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    L = nl.lib()
+    names = declared_symbols()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(L, n), n
+    assert names == set(nl.EXPORTS)
+
+
+def test_last_error_is_empty_string_initially():
+    assert isinstance(nl.lib().nested_linear_last_error(), bytes)
+
+
+def _status(fn, *args):
+    return getattr(nl.lib(), fn)(*args)
+
+
+def test_create_rejects_null_and_bad_shapes():
+    L = nl.lib()
+    h = ctypes.c_void_p()
+    assert L.nested_linear_create(None, ctypes.byref(h)) == nl.NL_EINVAL
+    for d_out, d_in, bits in [(0, 1024, 8), (16, 100, 8), (16, 0, 8), (16, 1024, 5), (16, 1024, 9)]:
+        d = nl.nl_desc(d_out, d_in, bits, 1, 1, 1, 1, 1, None, (ctypes.c_float * 4)(-1.5, -.5, .5, 1.5))
+        assert L.nested_linear_create(ctypes.byref(d), ctypes.byref(h)) == nl.NL_EINVAL
+        assert L.nested_linear_last_error()
+    # residual arrays missing / present with bits == 0
+    d = nl.nl_desc(16, 1024, 8, 1, 1, None, None, 1, None, (ctypes.c_float * 4)(-1.5, -.5, .5, 1.5))
+    assert L.nested_linear_create(ctypes.byref(d), ctypes.byref(h)) == nl.NL_EINVAL
+    d = nl.nl_desc(16, 1024, 0, 1, 1, 1, 1, 1, None, (ctypes.c_float * 4)(-1.5, -.5, .5, 1.5))
+    assert L.nested_linear_create(ctypes.byref(d), ctypes.byref(h)) == nl.NL_EINVAL
+    # non-finite level
+    d = nl.nl_desc(16, 1024, 0, 1, 1, None, None, 1, None, (ctypes.c_float * 4)(-1.5, float("nan"), .5, 1.5))
+    assert L.nested_linear_create(ctypes.byref(d), ctypes.byref(h)) == nl.NL_EINVAL
+    assert b"level" in L.nested_linear_last_error()
+
+
+def test_calls_reject_invalid_handles():
+    L = nl.lib()
+    n = ctypes.c_size_t()
+    bogus = ctypes.c_void_p(0)
+    assert L.nested_linear_destroy(bogus) == nl.NL_EINVAL
+    assert L.nested_linear_workspace_bytes(bogus, 16, ctypes.byref(n)) == nl.NL_EINVAL
+    assert L.nested_linear_verify(bogus, 1, 16, 1, 1, 1 << 20, None) == nl.NL_EINVAL
+    assert L.nested_linear_draft(bogus, 1, 16, 1, 1, 1 << 20, None) == nl.NL_EINVAL
+    assert L.nested_linear_decode(bogus, 0, 1, 1, 1, None) == nl.NL_EINVAL
+    assert L.nested_linear_group_destroy(bogus) == nl.NL_EINVAL
+    g = ctypes.c_void_p()
+    assert L.nested_linear_group_create(None, 0, ctypes.byref(g)) == nl.NL_EINVAL
+    arr = (ctypes.c_void_p * 1)(None)
+    assert L.nested_linear_group_create(arr, 1, ctypes.byref(g)) == nl.NL_EINVAL
+    assert L.nested_linear_info(bogus, None, None, None, None, None, None) == nl.NL_EINVAL
+
+
+def test_binding_raises_nlerror():
+    with pytest.raises(nl.NLError) as ei:
+        nl.nested_linear_destroy(ctypes.c_void_p(0))
+    assert ei.value.status == nl.NL_EINVAL

@@ -1,0 +1,263 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Bars: code unpacking bit-exact; outputs max|dy| <= 2e-3 * max|y_oracle|
+over all T x d_out outputs of a call (fp32 accumulation, bf16 activations).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch
+
+
+@pytest.fixture(scope="module")
+def nl(torch_cuda):
+    import bit_nested_quantized_amd as m
+    m.lib()
+    return m
+
+
+def to_dev(torch, a, dt=np.int16):
+    return torch.from_numpy(np.ascontiguousarray(a).view(dt)).to("cuda")
+
+
+def rel_err(y, ref):
+    return float(np.abs(y.astype(np.float64) - ref).max() / max(np.abs(ref).max(), 1e-300))
+
+
+def run(nl, torch, lin, x, verify, L=None):
+    L = L or nl.Linear(lin)
+    y = L.forward(to_dev(torch, x), verify)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+# --- unpacking: bit-exact --------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [0, 6, 7, 8])
+def test_decode_every_pattern_every_position(nl, torch_cuda, bits):
+    torch = torch_cuda
+    nb = bits if bits else 2
+    n = 1 << nb
+    rows = max(n, 16) + 5                               # ragged last tile
+    r = np.arange(rows)[:, None]
+    p = np.arange(640)[None, :]                         # 5 groups: a ragged chunk
+    codes = ((r + p) % 4).astype(np.uint8)
+    lin = synth.make_linear(rows, 640, bits, cfg=50, idx=bits)
+    lin["base_codes"] = synth.pack_base(codes)
+    if bits:
+        q = ((r + p) % n) - n // 2
+        lin["resid_codes"] = synth.pack_resid(q, bits)
+    L = nl.Linear(lin)
+    for row0, nrows in [(0, rows), (3, 17), (rows - 1, 1)]:
+        bi = torch.zeros((nrows, 640), dtype=torch.uint8, device="cuda")
+        rq = torch.zeros((nrows, 640), dtype=torch.int8, device="cuda")
+        nl.nested_linear_decode(L.h, row0, nrows, bi, rq)
+        torch.cuda.synchronize()
+        ob, orq = oracle.decode(lin, row0, nrows)
+        np.testing.assert_array_equal(bi.cpu().numpy(), ob)
+        if bits:
+            np.testing.assert_array_equal(rq.cpu().numpy(), orq)
+
+
+def test_decode_random_linear(nl, torch_cuda):
+    lin = synth.make_linear(200, 1536, 7, cfg=51, idx=0)
+    L = nl.Linear(lin)
+    torch = torch_cuda
+    bi = torch.zeros((200, 1536), dtype=torch.uint8, device="cuda")
+    rq = torch.zeros((200, 1536), dtype=torch.int8, device="cuda")
+    nl.nested_linear_decode(L.h, 0, 200, bi, rq)
+    torch.cuda.synchronize()
+    ob, orq = oracle.decode(lin)
+    np.testing.assert_array_equal(bi.cpu().numpy(), ob)
+    np.testing.assert_array_equal(rq.cpu().numpy(), orq)
+
+
+def test_level_table_is_near_exact(nl, torch_cuda):
+    L = nl.Linear(synth.make_linear(16, 128, 0, cfg=52, idx=0))
+    info = nl.nested_linear_info(L.h)
+    assert info["level_rel_err"] < 2e-5
+    assert info["block_in"] == 128 and info["block_out"] == 16
+
+
+# --- the input rotation (white box: the workspace holds x' as fp16 * 2^s) ----------
+
+def test_prepare_input_matches_oracle_rotation(nl, torch_cuda):
+    torch = torch_cuda
+    d_in, T = 14336, 5                                  # block 2048, 7 blocks, 28 chunks
+    lin = synth.make_linear(64, d_in, 6, cfg=53, idx=0)
+    x = synth.make_x(T, d_in, cfg=53, idx=0, scale=3.0)
+    L = nl.Linear(lin)
+    ws = L.workspace(T)
+    nl.nested_linear_prepare_input(L.h, to_dev(torch, x), T, ws)
+    torch.cuda.synchronize()
+    nch = d_in // 512
+    xh = ws[: T * d_in * 2].view(torch.float16).reshape(T, d_in).float().cpu().numpy()
+    o_xs = (T * d_in * 2 + 255) // 256 * 256
+    o_tsc = (o_xs + T * nch * 16 + 255) // 256 * 256
+    tsc = ws[o_tsc: o_tsc + T * nch * 4].view(torch.float32).reshape(T, nch).cpu().numpy()
+    xs = ws[o_xs: o_xs + T * nch * 16].view(torch.float32).reshape(T, nch * 4).cpu().numpy()
+    got = xh * np.repeat(tsc, 512, axis=1)
+    ref = oracle.rotate_input(lin, x)
+    for t in range(T):
+        for c in range(nch):
+            seg = slice(512 * c, 512 * (c + 1))
+            m = np.abs(ref[t, seg]).max()
+            assert np.abs(got[t, seg] - ref[t, seg]).max() <= m * 2.0 ** -11
+            # the chunk's scaled maximum lands in [2^14, 2^15)
+            assert 2 ** 14 <= np.abs(xh[t, seg]).max() <= 2 ** 15
+    gsum = xh.reshape(T, -1, 128)
+    assert np.all(np.abs(xs - gsum.sum(-1)) <= 1e-6 * np.abs(gsum).sum(-1) + 1e-6)
+
+
+# --- end-to-end parity ---------------------------------------------------------
+
+@pytest.mark.parametrize("T", [1, 16])
+@pytest.mark.parametrize("verify", [False, True])
+def test_single_1024_int8(nl, torch_cuda, T, verify):
+    # 1024 x 1024, int8 residual, T = 1 and 16: the small single-linear workload
+    lin = synth.make_linear(1024, 1024, 8, cfg=0, idx=0)
+    x = synth.make_x(T, 1024, cfg=0, idx=T)
+    y = run(nl, torch_cuda, lin, x, verify)
+    assert rel_err(y, oracle.forward(lin, x, verify)) <= TOL
+
+
+SHAPES = [
+    # d_out, d_in, bits, T, two-sided
+    (64, 512, 6, 1, True),
+    (48, 384, 7, 5, False),     # block 128, one partial chunk
+    (100, 640, 8, 17, True),    # ragged rows (block_out 4), two token tiles
+    (1000, 1152, 6, 33, True),  # block_in 128, ragged tile, three token tiles
+    (256, 2048, 7, 64, True),   # four token tiles
+    (512, 2048, 8, 48, False),
+    (4096, 4096, 6, 16, True),
+    (2048, 5120, 8, 64, True),  # block_in 1024
+]
+
+
+@pytest.mark.parametrize("d_out,d_in,bits,T,two", SHAPES)
+@pytest.mark.parametrize("verify", [False, True])
+def test_shapes(nl, torch_cuda, d_out, d_in, bits, T, two, verify):
+    lin = synth.make_linear(d_out, d_in, bits, cfg=60, idx=d_out + d_in, two_sided=two)
+    x = synth.make_x(T, d_in, cfg=60, idx=T)
+    y = run(nl, torch_cuda, lin, x, verify)
+    assert rel_err(y, oracle.forward(lin, x, verify)) <= TOL
+
+
+CFG1 = [(4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336)]
+
+
+@pytest.mark.parametrize("d_out,d_in", CFG1)
+def test_llama8b_projections_6bit(nl, torch_cuda, d_out, d_in):
+    # 7B/8B-class projections, 6-bit residual, draft and verify at T = 1..32
+    torch = torch_cuda
+    lin = synth.make_linear(d_out, d_in, 6, cfg=1, idx=d_out * 7 + d_in)
+    x = synth.make_x(32, d_in, cfg=1, idx=d_in)
+    L = nl.Linear(lin)
+    ws = L.workspace(32)
+    xd = to_dev(torch, x)
+    for verify in (False, True):
+        ref = oracle.forward(lin, x, verify)
+        for T in (1, 4, 8, 16, 32):
+            y = L.forward(xd[:T].contiguous(), verify, ws=ws).cpu().numpy()
+            e = rel_err(y, ref[:T])
+            assert e <= TOL, (verify, T, e)
+
+
+# --- properties ----------------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [6, 7, 8])
+def test_nesting_zero_residual_equals_draft_bitwise(nl, torch_cuda, bits):
+    lin = synth.make_linear(512, 2048, bits, cfg=61, idx=bits)
+    zs = dict(lin, resid_scales=np.zeros_like(lin["resid_scales"]))
+    x = synth.make_x(12, 2048, cfg=61, idx=bits)
+    d = run(nl, torch_cuda, lin, x, False)
+    v0 = run(nl, torch_cuda, zs, x, True)
+    np.testing.assert_array_equal(v0, d)
+
+
+def test_repeat_runs_are_bitwise_identical(nl, torch_cuda):
+    torch = torch_cuda
+    lin = synth.make_linear(4096, 4096, 7, cfg=62, idx=0)
+    x = to_dev(torch, synth.make_x(16, 4096, cfg=62, idx=0))
+    L = nl.Linear(lin)
+    ws = L.workspace(16)
+    a = L.forward(x, True, ws=ws).cpu().numpy()
+    for _ in range(3):
+        np.testing.assert_array_equal(L.forward(x, True, ws=ws).cpu().numpy(), a)
+
+
+def test_staged_calls_equal_fused_call(nl, torch_cuda):
+    torch = torch_cuda
+    lin = synth.make_linear(2048, 4096, 8, cfg=63, idx=0)
+    x = to_dev(torch, synth.make_x(8, 4096, cfg=63, idx=0))
+    L = nl.Linear(lin)
+    ws = L.workspace(8)
+    a = L.forward(x, True, ws=ws)
+    y = torch.empty_like(a)
+    nl.nested_linear_prepare_input(L.h, x, 8, ws)
+    nl.nested_linear_contract(L.h, True, 8, y, ws)
+    nl.nested_linear_finish(L.h, 8, y, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, y)
+
+
+def test_unit_column_closed_form(nl, torch_cuda):
+    # x = S_i H_i e_j makes the one-sided output column j of W~.
+    torch = torch_cuda
+    d_in = 1024
+    lin = synth.make_linear(256, d_in, 8, cfg=64, idx=0, two_sided=False, keep_codes=True)
+    H = np.ones((1, 1))
+    while H.shape[0] < d_in:
+        H = np.block([[H, H], [H, -H]])
+    js = [0, 3, 1023]
+    X = (H[:, js].T / 32.0) * lin["sign_in"]
+    xb = synth.f32_to_bf16_bits(X.astype(np.float32))
+    y = run(nl, torch, lin, xb, True)
+    g_of_k = np.arange(d_in) // 128
+    W = lin["levels"].astype(np.float64)[lin["base_idx"]] * lin["base_scales"].view(np.float16).astype(np.float64)[:, g_of_k]
+    W += lin["resid_q"] * lin["resid_scales"].view(np.float16).astype(np.float64)[:, g_of_k]
+    for t, j in enumerate(js):
+        assert np.abs(y[t] - W[:, j]).max() <= TOL * np.abs(W[:, j]).max()
+
+
+# --- error paths on the device ---------------------------------------------------
+
+def test_call_errors(nl, torch_cuda):
+    torch = torch_cuda
+    lin = synth.make_linear(64, 512, 6, cfg=65, idx=0)
+    L = nl.Linear(lin)
+    x = to_dev(torch, synth.make_x(4, 512, cfg=65, idx=0))
+    y = torch.empty((4, 64), dtype=torch.float32, device="cuda")
+    ws = L.workspace(4)
+    with pytest.raises(nl.NLError) as e:
+        nl.nested_linear_verify(L.h, x, 0, y, ws)
+    assert e.value.status == nl.NL_EINVAL
+    with pytest.raises(nl.NLError) as e:
+        nl.nested_linear_verify(L.h, x, 65, y, ws)
+    assert e.value.status == nl.NL_EUNSUPPORTED
+    with pytest.raises(nl.NLError) as e:
+        nl.nested_linear_verify(L.h, x, 4, y, ws[:128])
+    assert e.value.status == nl.NL_EINVAL
+    D = nl.Linear(synth.make_linear(64, 512, 0, cfg=65, idx=1))
+    with pytest.raises(nl.NLError):
+        nl.nested_linear_verify(D.h, x, 4, y, D.workspace(4))
+    bad = synth.make_linear(64, 512, 6, cfg=65, idx=2)
+    bad["sign_in"] = bad["sign_in"].copy()
+    bad["sign_in"][7] = 0
+    with pytest.raises(nl.NLError) as e:
+        nl.Linear(bad)
+    assert e.value.status == nl.NL_EINVAL
+    with pytest.raises(nl.NLError):
+        nl.nested_linear_decode(L.h, 60, 10, torch.zeros((10, 512), dtype=torch.uint8, device="cuda"), None)
