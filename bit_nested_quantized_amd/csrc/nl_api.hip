@@ -68,6 +68,18 @@ static int block_size(int n) {  // POC section 1 "Block size" rule
   return b;
 }
 
+static int log2i(int b) {
+  int l = 0;
+  while ((1 << l) < b) ++l;
+  return l;
+}
+
+// Rows per finish workgroup: one superblock of 256*E outputs, E in {2..16}.
+static int finish_rows(bool sign_out, int b_out) {
+  if (!sign_out) return 4096;
+  return b_out > kChunk ? b_out : kChunk;
+}
+
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Round a float to the nearest fp16 (ties to even) and return its bits.
@@ -264,7 +276,7 @@ struct Plan {
   int n_rb;       // 64-row workgroups per linear
   int S, cps;     // split-K count and chunks per split
   bool finish;    // a finish pass is needed
-  size_t o_xh, o_xs, o_tsc, o_part, total;
+  size_t o_xh, o_meta, o_part, total;
 };
 
 static Plan make_plan(int d_out, int n_tiles, int n_chunks, bool sign_out, int rows, int mt,
@@ -285,9 +297,8 @@ static Plan make_plan(int d_out, int n_tiles, int n_chunks, bool sign_out, int r
   p.finish = sign_out || p.S > 1 || n_linears > 1;
   const size_t Kp = (size_t)n_chunks * kChunk;
   p.o_xh = 0;
-  p.o_xs = align256(p.o_xh + (size_t)rows * Kp * 2);
-  p.o_tsc = align256(p.o_xs + (size_t)rows * n_chunks * 4 * 4);
-  p.o_part = align256(p.o_tsc + (size_t)rows * n_chunks * 4);
+  p.o_meta = align256(p.o_xh + (size_t)rows * Kp * 2);
+  p.o_part = align256(p.o_meta + (size_t)rows * n_chunks * 5 * 4);
   p.total = align256(p.o_part + (p.finish ? (size_t)p.S * rows * d_out * 4 : 0));
   return p;
 }
@@ -328,9 +339,10 @@ static RotInArgs rot_args(nl_handle h, const void *x, int T, char *ws, const Pla
   r.x = (const uint16_t *)x;
   r.sign = h->dev.sign_in;
   r.x_rows = T;
+  r.rows = T;
+  r.lb = log2i(h->b_in);
   r.xh = (uint16_t *)(ws + p.o_xh);
-  r.xs = (float *)(ws + p.o_xs);
-  r.tsc = (float *)(ws + p.o_tsc);
+  r.meta = (float *)(ws + p.o_meta);
   r.d_in = h->d_in;
   r.b = h->b_in;
   r.SB = h->b_in > kChunk ? h->b_in : kChunk;
@@ -363,8 +375,7 @@ extern "C" nl_status nested_linear_contract(nl_handle h, int32_t verify, int32_t
   memset(&g, 0, sizeof g);
   g.lin = h->dev;
   g.xh = (const uint16_t *)(w + p.o_xh);
-  g.xs = (const float *)(w + p.o_xs);
-  g.tsc = (const float *)(w + p.o_tsc);
+  g.meta = (const float *)(w + p.o_meta);
   g.out = p.finish ? (float *)(w + p.o_part) : y;
   g.split_stride = (size_t)T * h->d_out;
   g.T = T;
@@ -398,7 +409,8 @@ extern "C" nl_status nested_linear_finish(nl_handle h, int32_t T, float *y, void
   f.d_out = h->d_out;
   f.S = p.S;
   f.b = h->b_out;
-  f.OB = h->has_sign_out ? h->b_out : 4096;
+  f.lb = log2i(h->b_out);
+  f.OB = finish_rows(h->has_sign_out, h->b_out);
   f.rsqrt_b = (float)(1.0 / std::sqrt((double)h->b_out));
   HIP_OR_FAIL(launch_finish(f, (hipStream_t)stream));
   return ok();
@@ -536,9 +548,10 @@ static nl_status grouped(nl_group_handle g, int verify, const int32_t *pair_toke
   r.offsets = offsets;
   r.n_experts = g->n;
   r.x_rows = T;
+  r.rows = P;
+  r.lb = log2i(g->b_in);
   r.xh = (uint16_t *)(w + p.o_xh);
-  r.xs = (float *)(w + p.o_xs);
-  r.tsc = (float *)(w + p.o_tsc);
+  r.meta = (float *)(w + p.o_meta);
   r.d_in = g->d_in;
   r.b = g->b_in;
   r.SB = g->b_in > kChunk ? g->b_in : kChunk;
@@ -553,8 +566,7 @@ static nl_status grouped(nl_group_handle g, int verify, const int32_t *pair_toke
   ga.lins = g->dev_array;
   ga.offsets = offsets;
   ga.xh = (const uint16_t *)(w + p.o_xh);
-  ga.xs = (const float *)(w + p.o_xs);
-  ga.tsc = (const float *)(w + p.o_tsc);
+  ga.meta = (const float *)(w + p.o_meta);
   ga.out = (float *)(w + p.o_part);
   ga.split_stride = (size_t)P * g->d_out;
   ga.T = P;
@@ -581,7 +593,8 @@ static nl_status grouped(nl_group_handle g, int verify, const int32_t *pair_toke
   f.d_out = g->d_out;
   f.S = p.S;
   f.b = g->b_out;
-  f.OB = g->has_sign_out ? g->b_out : 4096;
+  f.lb = log2i(g->b_out);
+  f.OB = finish_rows(g->has_sign_out, g->b_out);
   f.rsqrt_b = (float)(1.0 / std::sqrt((double)g->b_out));
   HIP_OR_FAIL(launch_finish(f, s));
   return ok();

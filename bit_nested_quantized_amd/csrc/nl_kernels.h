@@ -37,10 +37,10 @@ struct RotInArgs {
   const int32_t *offsets;
   int n_experts;
   int x_rows;               // rows of x (bounds for pair_token)
-  uint16_t *xh;             // [rows][Kp] fp16, scaled per (row, chunk)
-  float *xs;                // [rows][Gp] group sums of xh
-  float *tsc;               // [rows][n_chunks] 2^-s / sqrt(b)
-  int d_in, b, SB, Kp, Gp, n_chunks;
+  uint16_t *xh;             // fp16 in the contraction's run layout (see xa_index)
+  float *meta;              // [n_chunks][5][rows]: 4 group sums of xh, then 2^-s / sqrt(b)
+  int rows;                 // rows of x' (tokens, or pairs of a grouped call)
+  int d_in, b, lb, SB, Kp, Gp, n_chunks;
   float rsqrt_b;
 };
 
@@ -49,8 +49,7 @@ struct GemmArgs {
   const LinearDev *lins;    // expert array (grouped) or null
   const int32_t *offsets;   // grouped: [n_experts + 1]
   const uint16_t *xh;
-  const float *xs;
-  const float *tsc;
+  const float *meta;
   float *out;               // [split][rows][ldo]
   size_t split_stride;
   int T;                    // rows of x' (tokens or pairs)
@@ -65,7 +64,7 @@ struct FinishArgs {
   const LinearDev *lins;    // grouped: per-pair expert sign_out
   const int32_t *offsets;
   int n_experts;
-  int T, d_out, S, b, OB;
+  int T, d_out, S, b, lb, OB;   // OB = 256*E rows per workgroup
   float rsqrt_b;
 };
 

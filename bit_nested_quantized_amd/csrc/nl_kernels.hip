@@ -176,20 +176,79 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
 }
 
 // ===========================================================================
-// Input rotation (POC section 1: x' = H_i S_i x, "once per Linear").
-// One workgroup per (row of x', superblock of SB columns); SB = max(b, 512)
-// so every 512-column chunk lies in one workgroup.  The butterflies run
-// unnormalised in fp32 in LDS; each chunk is then scaled by 2^s (s chosen so
-// its largest magnitude lands in [2^14, 2^15)) and rounded to fp16, the
-// kernels' MFMA operand.  tsc = 2^-s / sqrt(b) undoes both factors.
+// Workgroup Walsh-Hadamard transform (POC section 1: Sylvester H, applied
+// block-diagonally).  The 256 threads hold 256*E consecutive values, thread t
+// elements [t*E, t*E + E); butterflies run unnormalised over the low `lb`
+// index bits (block 2^lb): first inside each thread, then across lanes of a
+// wave with xor shuffles, then across waves through LDS.
 // ===========================================================================
+template <int E>
+__device__ __forceinline__ void fwht_wg(float (&v)[E], int lb, float *xch) {
+  constexpr int LE = (E == 2) ? 1 : (E == 4) ? 2 : (E == 8) ? 3 : 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+#pragma unroll
+  for (int p = 0; p < LE; ++p) {
+    if (p < lb) {
+      const int h = 1 << p;
+#pragma unroll
+      for (int j = 0; j < E; ++j)
+        if (!(j & h)) {
+          const float x0 = v[j], x1 = v[j | h];
+          v[j] = x0 + x1;
+          v[j | h] = x0 - x1;
+        }
+    }
+  }
+  for (int p = LE; p < lb && p < LE + 6; ++p) {
+    const int m = 1 << (p - LE);
+    const bool up = (lane & m) != 0;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const float o = __shfl_xor(v[j], m, 64);
+      v[j] = up ? (o - v[j]) : (v[j] + o);
+    }
+  }
+  for (int p = LE + 6; p < lb; ++p) {
+    const int m = 1 << (p - LE);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < E; ++j) xch[tid * E + j] = v[j];
+    __syncthreads();
+    const bool up = (tid & m) != 0;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const float o = xch[(tid ^ m) * E + j];
+      v[j] = up ? (o - v[j]) : (v[j] + o);
+    }
+  }
+}
+
+// Index of column k of row r in the activation layout the contraction reads:
+// runs of 8 consecutive columns, run = (((chunk*4 + group)*4 + step)*4 + quarter),
+// each run holding all R rows (16 bytes per row).
+__device__ __forceinline__ size_t xa_index(int k, int r, int R) {
+  const int run = (k >> 3 & 3) * 4 + (k >> 5 & 3) + ((k >> 7) << 4);  // (c*4+g)*16 + s*4 + kq
+  return ((size_t)run * R + r) * 8 + (k & 7);
+}
+
+// ===========================================================================
+// Input rotation (POC section 1: x' = H_i S_i x, "once per Linear").
+// One workgroup per (row of x', superblock of SB = 256*E = max(b, 512)
+// columns), so every 512-column chunk lies in one workgroup.  Each chunk is
+// scaled by 2^s (its largest magnitude lands in [2^14, 2^15)) and rounded to
+// fp16, the contraction's MFMA operand; tsc = 2^-s / sqrt(b) undoes both.
+// Outputs (R = rows of x'): xh in the layout of xa_index; meta[(c*5+g)*R + r]
+// = sum of the fp16 values of group g (g < 4) and meta[(c*5+4)*R + r] = tsc.
+// ===========================================================================
+template <int E>
 __global__ __launch_bounds__(256) void rotate_in_kernel(const RotInArgs a) {
-  __shared__ float v[4096];
-  __shared__ float red[8][4];
-  __shared__ int s_exp[8];
-  const int row = blockIdx.x, sbk = blockIdx.y;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int k0 = sbk * a.SB;
+  constexpr int SB = 256 * E;
+  constexpr int TPC = kChunk / E;  // threads per 512-column chunk
+  constexpr int TPG = kGroup / E;  // threads per 128-column group
+  __shared__ float xch[SB];
+  __shared__ float red[4];
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k0 = blockIdx.y * SB + tid * E;
 
   int xrow = row;
   const int8_t *sign = a.sign;
@@ -203,85 +262,101 @@ __global__ __launch_bounds__(256) void rotate_in_kernel(const RotInArgs a) {
     }
     sign = a.lins[lo].sign_in;
   }
+  float v[E];
   const uint16_t *xr = a.x + (size_t)(xrow < 0 ? 0 : xrow) * a.d_in;
-  for (int i = tid; i < a.SB; i += 256) {
-    const int k = k0 + i;
-    v[i] = (k < a.d_in && xrow >= 0) ? bf16_to_float(xr[k]) * (float)sign[k] : 0.0f;
-  }
-  __syncthreads();
-  for (int h = 1; h < a.b; h <<= 1) {
-    for (int p = tid; p < (a.SB >> 1); p += 256) {
-      const int i = ((p / h) * 2 * h) + (p % h);
-      const float x0 = v[i], x1 = v[i + h];
-      v[i] = x0 + x1;
-      v[i + h] = x0 - x1;
-    }
-    __syncthreads();
-  }
-  const int nck = a.SB / kChunk;
-  for (int cc = 0; cc < nck; ++cc) {
-    float m = fmaxf(fabsf(v[cc * kChunk + tid]), fabsf(v[cc * kChunk + 256 + tid]));
-    m = wave_max(m);
-    if (lane == 0) red[cc][wave] = m;
-  }
-  __syncthreads();
-  if (tid < nck) {
-    const float m = fmaxf(fmaxf(red[tid][0], red[tid][1]), fmaxf(red[tid][2], red[tid][3]));
-    int e = 0;
-    int s = 0;
-    if (m > 0.0f) {
-      frexpf(m, &e);
-      s = 15 - e;
-      s = s > 120 ? 120 : (s < -120 ? -120 : s);
-    }
-    s_exp[tid] = s;
-    a.tsc[(size_t)row * a.n_chunks + k0 / kChunk + tid] = ldexpf(a.rsqrt_b, -s);
-  }
-  __syncthreads();
-  uint16_t *xo = a.xh + (size_t)row * a.Kp + k0;
-  for (int cc = 0; cc < nck; ++cc) {
-    const int s = s_exp[cc];
-    float gs[2];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int i = cc * kChunk + hh * 256 + tid;
-      const _Float16 q = (_Float16)ldexpf(v[i], s);
-      xo[i] = __builtin_bit_cast(uint16_t, q);
-      gs[hh] = wave_sum((float)q);
-    }
-    // wave w covers columns [64w, 64w + 64) of each half: groups 2*hh + (w >> 1)
-    __syncthreads();
-    if (lane == 0) { red[0][wave] = gs[0]; red[1][wave] = gs[1]; }
-    __syncthreads();
-    if (tid < 4) {
-      const int hh = tid >> 1, w2 = (tid & 1) * 2;
-      a.xs[(size_t)row * a.Gp + k0 / kGroup + cc * 4 + tid] = red[hh][w2] + red[hh][w2 + 1];
-    }
+  for (int j = 0; j < E; ++j) {
+    const int k = k0 + j;
+    v[j] = (k < a.d_in && xrow >= 0) ? bf16_to_float(xr[k]) * (float)sign[k] : 0.0f;
   }
+  fwht_wg<E>(v, a.lb, xch);
+
+  float m = 0.f;
+#pragma unroll
+  for (int j = 0; j < E; ++j) m = fmaxf(m, fabsf(v[j]));
+#pragma unroll
+  for (int o = 1; o < (TPC < 64 ? TPC : 64); o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if constexpr (TPC > 64) {
+    __syncthreads();
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    m = (TPC == 128) ? fmaxf(red[wave & ~1], red[wave | 1])
+                     : fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  }
+  int s = 0;
+  if (m > 0.0f) {
+    int e;
+    frexpf(m, &e);
+    s = 15 - e;
+    s = s > 120 ? 120 : (s < -120 ? -120 : s);
+  }
+  _Float16 q[E];
+  float gs = 0.f;
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    q[j] = (_Float16)ldexpf(v[j], s);
+    gs += (float)q[j];
+  }
+#pragma unroll
+  for (int o = 1; o < TPG; o <<= 1) gs += __shfl_xor(gs, o, 64);
+
+  const int R = a.rows;
+  uint16_t *xo = a.xh;
+  if constexpr (E >= 8) {
+#pragma unroll
+    for (int j8 = 0; j8 < E; j8 += 8) {
+      uint32_t w[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        w[h] = (uint32_t)__builtin_bit_cast(uint16_t, q[j8 + 2 * h]) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, q[j8 + 2 * h + 1]) << 16);
+      *reinterpret_cast<uint4 *>(xo + xa_index(k0 + j8, row, R)) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < E; ++j) xo[xa_index(k0 + j, row, R)] = __builtin_bit_cast(uint16_t, q[j]);
+  }
+  if (tid % TPG == 0) a.meta[((size_t)(k0 >> 9) * 5 + ((k0 >> 7) & 3)) * R + row] = gs;
+  if (tid % TPC == 0) a.meta[((size_t)(k0 >> 9) * 5 + 4) * R + row] = ldexpf(a.rsqrt_b, -s);
 }
 
 // ===========================================================================
 // Fused contraction.  Workgroup = 4 waves = 4 row tiles (64 rows) over a
-// K-range of `cps` chunks (split-K index blockIdx.y).  The workgroup stages
-// WCH chunks of x' at a time in LDS; each wave streams its own tile's codes
-// from HBM with a one-chunk register prefetch.
+// K-range of `cps` chunks (split-K index blockIdx.y).  Per chunk the
+// workgroup copies that chunk's x' (and its group sums / scales) from global
+// memory straight into one of two LDS buffers with global_load_lds (no
+// registers), one chunk ahead; each wave streams its own tile's codes from
+// HBM into registers, also one chunk ahead.  One s_barrier per chunk; the
+// waits before it are counted so the weight prefetch stays in flight.
 // Per group: base and residual planes -> fp16 B operands; 4 MFMA steps per
 // plane and token tile; fp32 epilogue
 //   acc_chunk = fma(s_b / kappa, A_base, acc_chunk)
 //   acc_chunk = fma(s_r, A_resid - bias * sum(x'), acc_chunk)
-// and at the end of each chunk acc += tsc * acc_chunk.
+// and at the end of each chunk acc = fma(tsc, acc_chunk, acc).
 // ===========================================================================
+#define NL_GLOBAL __attribute__((address_space(1)))
+#define NL_LOCAL __attribute__((address_space(3)))
+
+template <int BITS>
+struct WRegs {
+  u32x4 b[kBasePieces];
+  u32x4 r[BITS > 0 ? BITS : 1];
+  uint64_t sb, sr;  // the row's 4 group scales (fp16) of each plane
+};
+
 template <int BITS, int MT>
 __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
-  constexpr int WCH = (MT == 1) ? 2 : 1;
-  constexpr int XROW = WCH * kChunk + 8;  // fp16 per LDS row (+16 B pad)
-  constexpr int NR = MT * 16;
+  // (wave index read as a scalar so per-wave choices stay uniform branches)
+  constexpr int TR = 16 * MT;          // token rows staged per chunk
+  constexpr int XH = 64 * TR * 8;      // fp16 per chunk buffer (TR KiB)
+  constexpr int NMETA = 5 * TR;        // per chunk: 4 group sums + 1 scale per row
+  constexpr int NMI = ((NMETA + 255) / 256) * 4;  // metadata copies, a multiple of 4
+  constexpr int NW = kBasePieces + 1 + (BITS > 0 ? BITS + 1 : 0);  // weight loads per chunk
+  __shared__ __attribute__((aligned(16))) _Float16 s_x[2][XH];
+  __shared__ __attribute__((aligned(16))) float s_m[2][NMI * 64];
   __shared__ uint32_t s_lut[16];
-  __shared__ float s_xsb[NR][WCH * 4];
-  __shared__ float s_tsc[NR][WCH];
-  __shared__ __attribute__((aligned(16))) _Float16 s_x[NR * XROW];
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   int rb = blockIdx.x;
   const LinearDev *Lp = &a.lin;
   int row_base = 0, nrows = a.T;
@@ -292,47 +367,84 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
     nrows = a.offsets[e + 1] - row_base;
     // idle expert (or offsets outside [0, rows)): uniform exit before any barrier
     if (nrows <= 0 || row_base < 0 || row_base >= a.T) return;
-    nrows = min(min(nrows, NR), a.T - row_base);
     Lp = a.lins + e;
   }
+  nrows = min(min(nrows, TR), a.T - row_base);
   const LinearDev &L = *Lp;
-  const int tile = rb * 4 + wave;
-  const bool active = tile < a.n_tiles;
+  const int tile_id = rb * 4 + wave;
+  const bool active = tile_id < a.n_tiles;
+  // waves past the last tile stream the last tile again (uniform control
+  // flow, exact wait counts) and store nothing
+  const int tile = active ? tile_id : a.n_tiles - 1;
   const int c_begin = blockIdx.y * a.cps;
   const int c_end = min(a.n_chunks, c_begin + a.cps);
   if (threadIdx.x < 16) s_lut[threadIdx.x] = L.lut[threadIdx.x];
   const float kinv = L.kinv;
-  const int tokl = lane & 15, kq = lane >> 4;
+  const int tl = lane & 15, kq = lane >> 4;
+  const int R = a.T;
   const float bias = BITS > 0 ? resid_bias(BITS > 0 ? BITS : 8) : 0.0f;
+
+  // --- global -> LDS copies of one chunk of activations and its metadata.
+  // Issued as inline asm so the compiler's wait insertion knows nothing of
+  // them (it would otherwise drain all loads before every m0 write and LDS
+  // read); their completion is covered by the counted wait in sync_chunk.
+  // Branch-free: rows past nrows re-read row nrows-1 (their LDS rows only feed
+  // output rows that are never stored), so every wave issues a fixed number
+  // of copies.
+  const uint32_t xs_lds0 = (uint32_t)(uintptr_t)(NL_LOCAL void *)&s_x[0][0];
+  const uint32_t xs_lds1 = (uint32_t)(uintptr_t)(NL_LOCAL void *)&s_x[1][0];
+  const uint32_t m_lds0 = (uint32_t)(uintptr_t)(NL_LOCAL void *)&s_m[0][0];
+  const uint32_t m_lds1 = (uint32_t)(uintptr_t)(NL_LOCAL void *)&s_m[1][0];
+  auto dma = [&](int c, int buf) {
+    const uint32_t xl = buf ? xs_lds1 : xs_lds0, ml = buf ? m_lds1 : m_lds0;
+#pragma unroll
+    for (int jj = 0; jj < TR / 4; ++jj) {
+      const int j = 4 * jj + wave;
+      const int slot = 64 * j + lane;
+      const int run = slot / TR, t = min(slot % TR, nrows - 1);
+      const uint32_t voff = (uint32_t)(((c * 64 + run) * R + row_base + t) * 16);
+      const uint32_t m0v = __builtin_amdgcn_readfirstlane(xl + 64 * 16 * j);
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   ::"s"(m0v), "v"(voff), "s"(a.xh) : "memory", "m0");
+    }
+#pragma unroll
+    for (int jj = 0; jj < NMI / 4; ++jj) {
+      const int j = 4 * jj + wave;
+      const int slot = min(64 * j + lane, NMETA - 1);
+      const uint32_t voff =
+          (uint32_t)(((c * 5 + slot / TR) * R + row_base + min(slot % TR, nrows - 1)) * 4);
+      const uint32_t m0v = __builtin_amdgcn_readfirstlane(ml + 64 * 4 * j);
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                   ::"s"(m0v), "v"(voff), "s"(a.meta) : "memory", "m0");
+    }
+  };
+
+  // --- this wave's tile codes for one chunk
+  const NL_GLOBAL u32x4 *bptr = (const NL_GLOBAL u32x4 *)L.base + (size_t)tile * a.n_chunks * 128 + lane;
+  const NL_GLOBAL u32x4 *rptr =
+      (const NL_GLOBAL u32x4 *)L.resid + (size_t)tile * a.n_chunks * (64 * (BITS > 0 ? BITS : 1)) + lane;
+  const NL_GLOBAL uint64_t *sbp = (const NL_GLOBAL uint64_t *)L.bscale + (size_t)tile * a.n_chunks * 16 + tl;
+  const NL_GLOBAL uint64_t *srp = (const NL_GLOBAL uint64_t *)L.rscale + (size_t)tile * a.n_chunks * 16 + tl;
+  auto loadw = [&](WRegs<BITS> &w, int c) {
+#pragma unroll
+    for (int i = 0; i < kBasePieces; ++i) w.b[i] = __builtin_nontemporal_load(bptr + (size_t)c * 128 + i * 64);
+    w.sb = sbp[(size_t)c * 16];
+    if constexpr (BITS > 0) {
+#pragma unroll
+      for (int i = 0; i < BITS; ++i) w.r[i] = __builtin_nontemporal_load(rptr + (size_t)c * (64 * BITS) + i * 64);
+      w.sr = srp[(size_t)c * 16];
+    }
+  };
 
   floatx4 acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  auto fill = [&](int c0) {
-    const int nw = min(WCH, c_end - c0);
-    __syncthreads();
-    const int per_row = nw * (kChunk / 8);
-    for (int idx = threadIdx.x; idx < nrows * per_row; idx += 256) {
-      const int t = idx / per_row, u = idx - t * per_row;
-      const uint4 val = *reinterpret_cast<const uint4 *>(
-          a.xh + (size_t)(row_base + t) * a.Kp + (size_t)c0 * kChunk + u * 8);
-      *reinterpret_cast<uint4 *>(s_x + t * XROW + u * 8) = val;
-    }
-    for (int idx = threadIdx.x; idx < nrows * nw * 4; idx += 256) {
-      const int t = idx / (nw * 4), gg = idx - t * (nw * 4);
-      s_xsb[t][gg] = bias * a.xs[(size_t)(row_base + t) * a.Gp + c0 * 4 + gg];
-    }
-    for (int idx = threadIdx.x; idx < nrows * nw; idx += 256) {
-      const int t = idx / nw, cc = idx - t * nw;
-      s_tsc[t][cc] = a.tsc[(size_t)(row_base + t) * a.n_chunks + c0 + cc];
-    }
-    __syncthreads();
-  };
-
-  auto process = [&](const ChunkRegs<BITS> &w, int ci) {
+  auto compute = [&](const WRegs<BITS> &w, int buf) {
     const uint32_t *bw = reinterpret_cast<const uint32_t *>(w.b);
     const uint32_t *rw = reinterpret_cast<const uint32_t *>(w.r);
+    const _Float16 *xb = &s_x[buf][(kq * TR + tl) * 8];
+    const float *mb = &s_m[buf][4 * kq];
     floatx4 accC[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) accC[m] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -342,58 +454,75 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
       unpack_base(bw + 2 * g, s_lut, bq);
       uint32_t rq[16];
       if constexpr (BITS > 0) unpack_resid<BITS>(rw + g * BITS, rq);
-      const uint32_t sbh = (g < 2 ? w.sb.x : w.sb.y) >> (16 * (g & 1));
-      const float sb = h2f(sbh & 0xFFFFu) * kinv;
+      const float sb = h2f((uint32_t)(w.sb >> (16 * g)) & 0xFFFFu) * kinv;
       float sr = 0.f;
-      if constexpr (BITS > 0) sr = h2f(((g < 2 ? w.sr.x : w.sr.y) >> (16 * (g & 1))) & 0xFFFFu);
+      if constexpr (BITS > 0) sr = h2f((uint32_t)(w.sr >> (16 * g)) & 0xFFFFu);
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         floatx4 aB = {0.f, 0.f, 0.f, 0.f}, aR = {0.f, 0.f, 0.f, 0.f};
-        const int t = m * 16 + tokl;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          half8 A = {0, 0, 0, 0, 0, 0, 0, 0};
-          if (t < nrows)
-            A = *reinterpret_cast<const half8 *>(s_x + t * XROW + ci * kChunk + g * kGroup +
-                                                 32 * kq + 8 * s);
+          const half8 A = *reinterpret_cast<const half8 *>(xb + ((g * 4 + s) * 4 * TR + 16 * m) * 8);
           aB = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, as_half8(bq + 4 * s), aB, 0, 0, 0);
           if constexpr (BITS > 0)
             aR = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, as_half8(rq + 4 * s), aR, 0, 0, 0);
         }
+        floatx4 xsv = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (BITS > 0) xsv = *reinterpret_cast<const floatx4 *>(mb + g * TR + 16 * m);
         // Draft and verify round identically: with s_r = 0 the residual
         // fma returns accC unchanged, so verify(0 residual) == draft bitwise.
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int tt = m * 16 + 4 * kq + i;
           accC[m][i] = fmaf(sb, aB[i], accC[m][i]);
-          if constexpr (BITS > 0) accC[m][i] = fmaf(sr, aR[i] - s_xsb[tt][ci * 4 + g], accC[m][i]);
+          if constexpr (BITS > 0) accC[m][i] = fmaf(sr, aR[i] - bias * xsv[i], accC[m][i]);
         }
       }
     }
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MT; ++m) {
+      const floatx4 ts = *reinterpret_cast<const floatx4 *>(mb + 4 * TR + 16 * m);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tt = m * 16 + 4 * kq + i;
-        acc[m][i] = fmaf(s_tsc[tt][ci], accC[m][i], acc[m][i]);
-      }
+      for (int i = 0; i < 4; ++i) acc[m][i] = fmaf(ts[i], accC[m][i], acc[m][i]);
+    }
   };
 
-  ChunkRegs<BITS> w0, w1;
-  if (active && c_begin < c_end) load_chunk<BITS>(w0, L, a.n_chunks, tile, c_begin, lane);
+  // wait for this wave's copies of the current chunk (issued before its NW
+  // weight loads), then the workgroup barrier makes every wave's copies
+  // visible and frees the other buffer.
+  auto sync_chunk = [&]() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(NW) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // Software pipeline, one chunk deep: at the top of each step the copies of
+  // chunk c (issued before the NW weight loads of chunk c) are waited for,
+  // the barrier publishes them, then chunk c+1 is requested and chunk c
+  // computed.  The last chunk's prefetch slot re-requests the last chunk, so
+  // every step issues the same loads.
+  WRegs<BITS> w0, w1;
+  if (c_begin < c_end) {
+    dma(c_begin, 0);
+    loadw(w0, c_begin);
+  }
   for (int c = c_begin; c < c_end; c += 2) {
-    if (active && c + 1 < c_end) load_chunk<BITS>(w1, L, a.n_chunks, tile, c + 1, lane);
-    if ((c - c_begin) % WCH == 0) fill(c);
-    if (active) process(w0, (c - c_begin) % WCH);
-    if (c + 1 < c_end) {
-      if (active && c + 2 < c_end) load_chunk<BITS>(w0, L, a.n_chunks, tile, c + 2, lane);
-      if ((c + 1 - c_begin) % WCH == 0) fill(c + 1);
-      if (active) process(w1, (c + 1 - c_begin) % WCH);
-    }
+    const int n1 = min(c + 1, c_end - 1);
+    sync_chunk();
+    dma(n1, 1);
+    loadw(w1, n1);
+    asm volatile("" ::: "memory");  // keep the prefetch here, ahead of compute
+    compute(w0, 0);
+    if (c + 1 >= c_end) break;
+    const int n2 = min(c + 2, c_end - 1);
+    sync_chunk();
+    dma(n2, 0);
+    loadw(w0, n2);
+    asm volatile("" ::: "memory");
+    compute(w1, 1);
   }
 
   if (!active) return;
-  const int row = tile * kTileRows + tokl;  // output row of this lane (B column)
+  const int row = tile * kTileRows + tl;  // output row of this lane (B column)
   if (row >= a.d_out) return;
   float *out = a.out + blockIdx.y * a.split_stride;
 #pragma unroll
@@ -407,13 +536,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
 
 // ===========================================================================
 // Finish: y = S_o H_o (sum over splits of the partial y~) per (row of y,
-// output block of b rows); without S_o it only sums the splits.
+// superblock of 256*E output rows); without S_o it only sums the splits.
 // ===========================================================================
+template <int E>
 __global__ __launch_bounds__(256) void finish_kernel(const FinishArgs a) {
-  __shared__ float v[4096];
-  const int t = blockIdx.x, r0 = blockIdx.y * a.OB;
-  const int tid = threadIdx.x;
-  const int n = min(a.OB, a.d_out - r0);
+  __shared__ float xch[256 * E];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int r0 = blockIdx.y * (256 * E) + tid * E;
   const int8_t *so = a.sign_out;
   if (a.lins) {
     int lo = 0, hi = a.n_experts;
@@ -423,32 +552,29 @@ __global__ __launch_bounds__(256) void finish_kernel(const FinishArgs a) {
     }
     so = a.lins[lo].sign_out;
   }
-  const float *p = a.part + (size_t)t * a.d_out + r0;
-  float *y = a.y + (size_t)t * a.d_out + r0;
-  if (!so) {
-    for (int i = tid; i < n; i += 256) {
-      float s = 0.f;
-      for (int sp = 0; sp < a.S; ++sp) s += p[sp * a.split_stride + i];
-      y[i] = s;
-    }
-    return;
-  }
-  for (int i = tid; i < n; i += 256) {
+  const float *p = a.part + (size_t)t * a.d_out;
+  float *y = a.y + (size_t)t * a.d_out;
+  float v[E];
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const int r = r0 + j;
     float s = 0.f;
-    for (int sp = 0; sp < a.S; ++sp) s += p[sp * a.split_stride + i];
-    v[i] = s;
+    if (r < a.d_out)
+      for (int sp = 0; sp < a.S; ++sp) s += p[sp * a.split_stride + r];
+    v[j] = s;
   }
-  __syncthreads();
-  for (int h = 1; h < a.b; h <<= 1) {
-    for (int q = tid; q < (n >> 1); q += 256) {
-      const int i = ((q / h) * 2 * h) + (q % h);
-      const float x0 = v[i], x1 = v[i + h];
-      v[i] = x0 + x1;
-      v[i + h] = x0 - x1;
+  if (so) {
+    fwht_wg<E>(v, a.lb, xch);
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int r = r0 + j;
+      if (r < a.d_out) y[r] = v[j] * a.rsqrt_b * (float)so[r];
     }
-    __syncthreads();
+  } else {
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+      if (r0 + j < a.d_out) y[r0 + j] = v[j];
   }
-  for (int i = tid; i < n; i += 256) y[i] = v[i] * a.rsqrt_b * (float)so[r0 + i];
 }
 
 // ===========================================================================
@@ -480,7 +606,13 @@ hipError_t launch_decode(const DecodeArgs &a, int bits, int ntiles, hipStream_t 
 
 hipError_t launch_rotate_in(const RotInArgs &a, int rows, hipStream_t s) {
   const dim3 grid(rows, a.Kp / a.SB);
-  rotate_in_kernel<<<grid, 256, 0, s>>>(a);
+  switch (a.SB) {
+    case 512: rotate_in_kernel<2><<<grid, 256, 0, s>>>(a); break;
+    case 1024: rotate_in_kernel<4><<<grid, 256, 0, s>>>(a); break;
+    case 2048: rotate_in_kernel<8><<<grid, 256, 0, s>>>(a); break;
+    case 4096: rotate_in_kernel<16><<<grid, 256, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -509,7 +641,13 @@ hipError_t launch_gemm(const GemmArgs &a, int bits, int mt, int splits, hipStrea
 
 hipError_t launch_finish(const FinishArgs &a, hipStream_t s) {
   const dim3 grid(a.T, (a.d_out + a.OB - 1) / a.OB);
-  finish_kernel<<<grid, 256, 0, s>>>(a);
+  switch (a.OB) {
+    case 512: finish_kernel<2><<<grid, 256, 0, s>>>(a); break;
+    case 1024: finish_kernel<4><<<grid, 256, 0, s>>>(a); break;
+    case 2048: finish_kernel<8><<<grid, 256, 0, s>>>(a); break;
+    case 4096: finish_kernel<16><<<grid, 256, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

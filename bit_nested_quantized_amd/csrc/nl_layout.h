@@ -77,31 +77,57 @@ struct LinearDev {
 //   hold pairs 14 (bits 0-1 in dword 0, 2-3 in 1, 4-5 in 2, 6 in dword 3 bit
 //   14) and 15 (bit 0 in dword 3 bit 15, 1-2 in 4, 3-4 in 5, 5-6 in 6).
 // ---------------------------------------------------------------------------
+// A constant the optimiser cannot fold into literals: materialised once in an
+// SGPR, so (a & m) | o selects a single v_and_or_b32 (GFX9 VOP3 encodings
+// take no literal operands) while the compiler still schedules the VALU work
+// and its MFMA hazards itself.
+__device__ __forceinline__ uint32_t sconst(uint32_t c) {
+  uint32_t r;
+  asm("s_mov_b32 %0, %1" : "=s"(r) : "i"(c));
+  return r;
+}
+
+// The or-constant of and_or lives in a VGPR (one SGPR read per VOP3).  Only
+// VALU instructions read it, so the asm's VGPR write needs no MFMA hazard
+// handling.
+__device__ __forceinline__ uint32_t vconst(uint32_t c) {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
+  return r;
+}
+
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  return (a & sconst(m)) | o;
+}
+
 template <int BITS>
 __device__ __forceinline__ void unpack_resid(const uint32_t *d, uint32_t *out) {
-  constexpr uint32_t K = 0x64006400u;
+  const uint32_t K = vconst(0x64006400u);
   if constexpr (BITS == 8) {
+    const uint32_t K8 = 0x64646464u;
 #pragma unroll
     for (int P = 0; P < 16; ++P)
-      out[P] = __builtin_amdgcn_perm(0x64646464u, d[P >> 1], (P & 1) ? 0x04030402u : 0x04010400u);
+      out[P] = __builtin_amdgcn_perm(K8, d[P >> 1], (P & 1) ? 0x04030402u : 0x04010400u);
   } else if constexpr (BITS == 6) {
 #pragma unroll
-    for (int P = 0; P < 6; ++P) out[P] = (d[P] & 0x003F003Fu) | K;
+    for (int P = 0; P < 6; ++P) out[P] = and_or(d[P], 0x003F003Fu, K);
 #pragma unroll
-    for (int P = 0; P < 6; ++P) out[6 + P] = ((d[P] >> 6) & 0x003F003Fu) | K;
+    for (int P = 0; P < 6; ++P) out[6 + P] = and_or(d[P] >> 6, 0x003F003Fu, K);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      out[12 + j] = ((d[j] >> 12) & 0x000F000Fu) |
-                    ((d[4 + (j >> 1)] >> (8 + 2 * (j & 1))) & 0x00300030u) | K;
+      out[12 + j] = and_or(d[j] >> 12, 0x000F000Fu,
+                           and_or(d[4 + (j >> 1)] >> (8 + 2 * (j & 1)), 0x00300030u, K));
   } else if constexpr (BITS == 7) {
 #pragma unroll
-    for (int P = 0; P < 7; ++P) out[P] = (d[P] & 0x007F007Fu) | K;
+    for (int P = 0; P < 7; ++P) out[P] = and_or(d[P], 0x007F007Fu, K);
 #pragma unroll
-    for (int P = 0; P < 7; ++P) out[7 + P] = ((d[P] >> 7) & 0x007F007Fu) | K;
-    out[14] = ((d[0] >> 14) & 0x00030003u) | ((d[1] >> 12) & 0x000C000Cu) |
-              ((d[2] >> 10) & 0x00300030u) | ((d[3] >> 8) & 0x00400040u) | K;
-    out[15] = ((d[3] >> 15) & 0x00010001u) | ((d[4] >> 13) & 0x00060006u) |
-              ((d[5] >> 11) & 0x00180018u) | ((d[6] >> 9) & 0x00600060u) | K;
+    for (int P = 0; P < 7; ++P) out[7 + P] = and_or(d[P] >> 7, 0x007F007Fu, K);
+    out[14] = and_or(d[3] >> 8, 0x00400040u,
+                     and_or(d[2] >> 10, 0x00300030u,
+                            and_or(d[1] >> 12, 0x000C000Cu, and_or(d[0] >> 14, 0x00030003u, K))));
+    out[15] = and_or(d[6] >> 9, 0x00600060u,
+                     and_or(d[5] >> 11, 0x00180018u,
+                            and_or(d[4] >> 13, 0x00060006u, and_or(d[3] >> 15, 0x00010001u, K))));
   }
 }
 
@@ -158,8 +184,18 @@ __device__ __forceinline__ void pack_resid(const uint32_t *v, uint32_t *d) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void unpack_base(const uint32_t *b, const uint32_t *lut_lds,
                                             uint32_t *out) {
+  // Byte q of ev (od) holds 4 * the even (odd) 4-bit pair index of byte q of
+  // b: the LDS byte offset of the pair's table entry.
+  const char *lut = reinterpret_cast<const char *>(lut_lds);
 #pragma unroll
-  for (int P = 0; P < 16; ++P) out[P] = lut_lds[(b[P >> 3] >> (4 * (P & 7))) & 15u];
+  for (int w = 0; w < 2; ++w) {
+    const uint32_t ev = (b[w] << 2) & 0x3C3C3C3Cu, od = (b[w] >> 2) & 0x3C3C3C3Cu;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      out[8 * w + 2 * q] = *reinterpret_cast<const uint32_t *>(lut + ((ev >> (8 * q)) & 0xFFu));
+      out[8 * w + 2 * q + 1] = *reinterpret_cast<const uint32_t *>(lut + ((od >> (8 * q)) & 0xFFu));
+    }
+  }
 }
 
 }  // namespace nl

@@ -59,6 +59,8 @@ def lib():
         L.nlo_forward_rows.argtypes = [i, i, i, i, P, P, P, P, P, P, P, P, i, i, i, P]
         L.nlo_forward_rows.restype = i
         L.nlo_decode.argtypes = [i, i, P, P, i, i, P, P]
+        L.nlo_num_threads.argtypes = []
+        L.nlo_num_threads.restype = i
         _lib = L
     return _lib
 
@@ -89,6 +91,11 @@ def fwht(v: np.ndarray, b: int | None = None) -> np.ndarray:
         else:
             lib().nlo_fwht_b(_p(row), n, int(b))
     return flat.reshape(a.shape)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's row loops use."""
+    return lib().nlo_num_threads()
 
 
 def half_to_double(h: int) -> float:

@@ -251,3 +251,11 @@ void nlo_decode(int d_in, int bits, const uint8_t *base_codes, const uint8_t *re
                     (int8_t)nlo_resid_code(resid_codes, d_in, bits, row0 + r, k);
         }
 }
+
+/* Threads the OpenMP loops use (reported with the CPU baseline timing). */
+#ifdef _OPENMP
+#include <omp.h>
+int nlo_num_threads(void) { return omp_get_max_threads(); }
+#else
+int nlo_num_threads(void) { return 1; }
+#endif

@@ -103,22 +103,27 @@ def test_prepare_input_matches_oracle_rotation(nl, torch_cuda):
     nl.nested_linear_prepare_input(L.h, to_dev(torch, x), T, ws)
     torch.cuda.synchronize()
     nch = d_in // 512
-    xh = ws[: T * d_in * 2].view(torch.float16).reshape(T, d_in).float().cpu().numpy()
-    o_xs = (T * d_in * 2 + 255) // 256 * 256
-    o_tsc = (o_xs + T * nch * 16 + 255) // 256 * 256
-    tsc = ws[o_tsc: o_tsc + T * nch * 4].view(torch.float32).reshape(T, nch).cpu().numpy()
-    xs = ws[o_xs: o_xs + T * nch * 16].view(torch.float32).reshape(T, nch * 4).cpu().numpy()
-    got = xh * np.repeat(tsc, 512, axis=1)
+    raw = ws[: T * d_in * 2].view(torch.float16).float().cpu().numpy()
+    # activation layout: runs of 8 columns, run = ((c*4+g)*4+s)*4+q, all T rows per run
+    k = np.arange(d_in)
+    run = ((k >> 3) & 3) * 4 + ((k >> 5) & 3) + ((k >> 7) << 4)
+    idx = (run[None, :] * T + np.arange(T)[:, None]) * 8 + (k & 7)[None, :]
+    xh = raw[idx]
+    o_meta = (T * d_in * 2 + 255) // 256 * 256
+    meta = ws[o_meta: o_meta + T * nch * 20].view(torch.float32).reshape(nch, 5, T).cpu().numpy()
+    xs, tsc = meta[:, :4, :], meta[:, 4, :]
+    got = xh * np.repeat(tsc.T, 512, axis=1)
     ref = oracle.rotate_input(lin, x)
     for t in range(T):
         for c in range(nch):
             seg = slice(512 * c, 512 * (c + 1))
             m = np.abs(ref[t, seg]).max()
             assert np.abs(got[t, seg] - ref[t, seg]).max() <= m * 2.0 ** -11
-            # the chunk's scaled maximum lands in [2^14, 2^15)
+            # the chunk's scaled maximum lands in [2^14, 2^15]
             assert 2 ** 14 <= np.abs(xh[t, seg]).max() <= 2 ** 15
-    gsum = xh.reshape(T, -1, 128)
-    assert np.all(np.abs(xs - gsum.sum(-1)) <= 1e-6 * np.abs(gsum).sum(-1) + 1e-6)
+    gsum = xh.reshape(T, nch, 4, 128)
+    want = gsum.sum(-1).transpose(1, 2, 0)
+    assert np.all(np.abs(xs - want) <= 1e-6 * np.abs(gsum).sum(-1).transpose(1, 2, 0) + 1e-6)
 
 
 # --- end-to-end parity ---------------------------------------------------------
