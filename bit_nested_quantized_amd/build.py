@@ -13,6 +13,8 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
     # packed fp32 VALU ops stay off: the compiler's own scalar code is used
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the epilogue reads them every group
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -279,6 +280,15 @@ struct Plan {
   size_t o_xh, o_meta, o_part, total;
 };
 
+// Launch tuning knobs, read once: NL_WG_TARGET (workgroups the split-K aims
+// for, default 512) and NL_SPLITS (force the split count).
+static int env_int(const char *name, int dflt) {
+  const char *v = getenv(name);
+  return (v && *v) ? atoi(v) : dflt;
+}
+static const int g_wg_target = env_int("NL_WG_TARGET", 512);
+static const int g_splits = env_int("NL_SPLITS", 0);
+
 static Plan make_plan(int d_out, int n_tiles, int n_chunks, bool sign_out, int rows, int mt,
                       int n_linears) {
   Plan p;
@@ -287,11 +297,11 @@ static Plan make_plan(int d_out, int n_tiles, int n_chunks, bool sign_out, int r
   p.n_rb = (n_tiles + 3) / 4;
   // Split K until the grid holds ~2 workgroups per CU (256 CUs), keeping at
   // least 2 chunks per split.
-  const int want = 512;
-  int S = (want + p.n_rb * n_linears - 1) / (p.n_rb * n_linears);
+  int S = (g_wg_target + p.n_rb * n_linears - 1) / (p.n_rb * n_linears);
   S = S < 1 ? 1 : S;
   const int smax = n_chunks / 2 > 0 ? n_chunks / 2 : 1;
   S = S > smax ? smax : S;
+  if (g_splits > 0) S = g_splits < n_chunks ? g_splits : n_chunks;
   p.cps = (n_chunks + S - 1) / S;
   p.S = (n_chunks + p.cps - 1) / p.cps;
   p.finish = sign_out || p.S > 1 || n_linears > 1;

@@ -36,18 +36,6 @@ __device__ __forceinline__ float bf16_to_float(uint16_t b) {
   return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
 // ===========================================================================
 // Create-time repack.  One wave per tile-chunk; lane l handles row
 // tile*16 + (l & 15) and columns [32*(l >> 4), +32) of the chunk's 4 groups.
@@ -140,12 +128,14 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<BITS> &w, const LinearDev &
 // ===========================================================================
 template <int BITS>
 __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
-  __shared__ uint32_t lut[16];
+  __shared__ uint2 lut[256];
   const int lane = threadIdx.x;
-  if (lane < 16) {
+  {
     // fp16 of the codes themselves: 0, 1, 2, 3
     const uint32_t h[4] = {0x0000u, 0x3C00u, 0x4000u, 0x4200u};
-    lut[lane] = h[lane & 3] | (h[lane >> 2] << 16);
+    uint32_t l16[16];
+    for (int i = 0; i < 16; ++i) l16[i] = h[i & 3] | (h[i >> 2] << 16);
+    for (int i = lane; i < 256; i += 64) lut[i] = base_table_entry(l16, i);
   }
   __syncthreads();
   const int tile = a.tile0 + blockIdx.x / a.n_chunks, chunk = blockIdx.x % a.n_chunks;
@@ -176,51 +166,55 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
 }
 
 // ===========================================================================
-// Workgroup Walsh-Hadamard transform (POC section 1: Sylvester H, applied
-// block-diagonally).  The 256 threads hold 256*E consecutive values, thread t
-// elements [t*E, t*E + E); butterflies run unnormalised over the low `lb`
-// index bits (block 2^lb): first inside each thread, then across lanes of a
-// wave with xor shuffles, then across waves through LDS.
+// Workgroup Walsh-Hadamard transforms (POC section 1: Sylvester H, applied
+// block-diagonally).  A workgroup of 256 threads transforms 4096 values:
+// 4096/SB independent "tasks" of SB = 2^n values (n in 9..12), TPS = SB/16
+// threads per task, 16 values per thread.  Butterflies run unnormalised over
+// the low `lb` bits of the element index i (block 2^lb).  The 16 values of a
+// thread pass through three layouts (the stages commute, so their order is
+// free):
+//   A  i = TPS*j + lt          top 4 bits in registers; coalesced loads
+//   C  i = (lt&15) + 16*j + 256*(lt>>4)   bits 4..7 in registers
+//   B  i = 16*lt + j           low 4 bits in registers; contiguous values
+// with padded (conflict-free) LDS transposes A->C->B in between.
 // ===========================================================================
-template <int E>
-__device__ __forceinline__ void fwht_wg(float (&v)[E], int lb, float *xch) {
-  constexpr int LE = (E == 2) ? 1 : (E == 4) ? 2 : (E == 8) ? 3 : 4;
-  const int tid = threadIdx.x, lane = tid & 63;
+__device__ __forceinline__ int lds_pad(int i) { return i + (i >> 4); }
+
+__device__ __forceinline__ void bfly16(float (&v)[16], int bit) {
+  const int h = 1 << bit;
 #pragma unroll
-  for (int p = 0; p < LE; ++p) {
-    if (p < lb) {
-      const int h = 1 << p;
-#pragma unroll
-      for (int j = 0; j < E; ++j)
-        if (!(j & h)) {
-          const float x0 = v[j], x1 = v[j | h];
-          v[j] = x0 + x1;
-          v[j | h] = x0 - x1;
-        }
+  for (int j = 0; j < 16; ++j)
+    if (!(j & h)) {
+      const float x0 = v[j], x1 = v[j | h];
+      v[j] = x0 + x1;
+      v[j | h] = x0 - x1;
     }
-  }
-  for (int p = LE; p < lb && p < LE + 6; ++p) {
-    const int m = 1 << (p - LE);
-    const bool up = (lane & m) != 0;
+}
+
+// v: layout A on entry, layout B on exit.  xch: this task's LDS (SB + SB/16).
+__device__ __forceinline__ void fwht_tasks(float (&v)[16], float *xch, int lt, int TPS, int n, int lb) {
 #pragma unroll
-    for (int j = 0; j < E; ++j) {
-      const float o = __shfl_xor(v[j], m, 64);
-      v[j] = up ? (o - v[j]) : (v[j] + o);
-    }
-  }
-  for (int p = LE + 6; p < lb; ++p) {
-    const int m = 1 << (p - LE);
-    __syncthreads();
+  for (int q = 0; q < 4; ++q)
+    if (n - 4 + q < lb) bfly16(v, q);
+  __syncthreads();
 #pragma unroll
-    for (int j = 0; j < E; ++j) xch[tid * E + j] = v[j];
-    __syncthreads();
-    const bool up = (tid & m) != 0;
+  for (int j = 0; j < 16; ++j) xch[lds_pad(TPS * j + lt)] = v[j];
+  __syncthreads();
+  const int cbase = (lt & 15) + 256 * (lt >> 4);
 #pragma unroll
-    for (int j = 0; j < E; ++j) {
-      const float o = xch[(tid ^ m) * E + j];
-      v[j] = up ? (o - v[j]) : (v[j] + o);
-    }
-  }
+  for (int j = 0; j < 16; ++j) v[j] = xch[lds_pad(cbase + 16 * j)];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (4 + q < n - 4 && 4 + q < lb) bfly16(v, q);
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 16; ++j) xch[lds_pad(cbase + 16 * j)] = v[j];
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = xch[lds_pad(16 * lt + j)];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (q < lb) bfly16(v, q);
 }
 
 // Index of column k of row r in the activation layout the contraction reads:
@@ -231,58 +225,67 @@ __device__ __forceinline__ size_t xa_index(int k, int r, int R) {
   return ((size_t)run * R + r) * 8 + (k & 7);
 }
 
+// Largest e with offsets[e] <= row (the expert of a pair).
+__device__ __forceinline__ int expert_of(const int32_t *offsets, int n, int row) {
+  int lo = 0, hi = n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (offsets[mid] <= row) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
 // ===========================================================================
 // Input rotation (POC section 1: x' = H_i S_i x, "once per Linear").
-// One workgroup per (row of x', superblock of SB = 256*E = max(b, 512)
-// columns), so every 512-column chunk lies in one workgroup.  Each chunk is
-// scaled by 2^s (its largest magnitude lands in [2^14, 2^15)) and rounded to
-// fp16, the contraction's MFMA operand; tsc = 2^-s / sqrt(b) undoes both.
+// Task = (row of x', superblock of SB = max(b, 512) columns), so every
+// 512-column chunk lies in one task.  Each chunk is scaled by 2^s (its
+// largest magnitude lands in [2^14, 2^15]) and rounded to fp16, the
+// contraction's MFMA operand; tsc = 2^-s / sqrt(b) undoes both factors.
 // Outputs (R = rows of x'): xh in the layout of xa_index; meta[(c*5+g)*R + r]
 // = sum of the fp16 values of group g (g < 4) and meta[(c*5+4)*R + r] = tsc.
 // ===========================================================================
-template <int E>
 __global__ __launch_bounds__(256) void rotate_in_kernel(const RotInArgs a) {
-  constexpr int SB = 256 * E;
-  constexpr int TPC = kChunk / E;  // threads per 512-column chunk
-  constexpr int TPG = kGroup / E;  // threads per 128-column group
-  __shared__ float xch[SB];
-  __shared__ float red[4];
-  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int k0 = blockIdx.y * SB + tid * E;
+  __shared__ float xch[4096 + 256];
+  const int SB = a.SB, TPS = SB >> 4, n = 31 - __builtin_clz(SB);
+  const int tid = threadIdx.x, lt = tid % TPS, tl = tid / TPS;
+  const int n_sb = a.Kp / SB;
+  const int task = blockIdx.x * (256 / TPS) + tl;
+  const bool valid = task < a.rows * n_sb;
+  const int row = valid ? task / n_sb : 0, sb = valid ? task % n_sb : 0;
+  const int kb = sb * SB;
+  float *x = xch + tl * (SB + (SB >> 4));
 
-  int xrow = row;
+  int xrow = valid ? row : -1;
   const int8_t *sign = a.sign;
-  if (a.lins) {  // grouped: pair -> (token, expert)
+  if (a.lins && valid) {  // grouped: pair -> (token, expert)
     xrow = a.pair_token[row];
     if (xrow < 0 || xrow >= a.x_rows) xrow = -1;
-    int lo = 0, hi = a.n_experts;  // largest e with offsets[e] <= row
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.offsets[mid] <= row) lo = mid; else hi = mid;
-    }
-    sign = a.lins[lo].sign_in;
+    sign = a.lins[expert_of(a.offsets, a.n_experts, row)].sign_in;
   }
-  float v[E];
+  // layout A, unconditional loads (clamped index) so all 16 are in flight
   const uint16_t *xr = a.x + (size_t)(xrow < 0 ? 0 : xrow) * a.d_in;
+  uint16_t xv[16];
+  int8_t sv[16];
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
-    const int k = k0 + j;
-    v[j] = (k < a.d_in && xrow >= 0) ? bf16_to_float(xr[k]) * (float)sign[k] : 0.0f;
+  for (int j = 0; j < 16; ++j) {
+    const int k = min(kb + TPS * j + lt, a.d_in - 1);
+    xv[j] = xr[k];
+    sv[j] = sign[k];
   }
-  fwht_wg<E>(v, a.lb, xch);
+  float v[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int k = kb + TPS * j + lt;
+    v[j] = (k < a.d_in && xrow >= 0) ? bf16_to_float(xv[j]) * (float)sv[j] : 0.0f;
+  }
+  fwht_tasks(v, x, lt, TPS, n, a.lb);
 
+  // layout B: 16 consecutive columns; a chunk is 32 threads, a group 8
   float m = 0.f;
 #pragma unroll
-  for (int j = 0; j < E; ++j) m = fmaxf(m, fabsf(v[j]));
+  for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(v[j]));
 #pragma unroll
-  for (int o = 1; o < (TPC < 64 ? TPC : 64); o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  if constexpr (TPC > 64) {
-    __syncthreads();
-    if (lane == 0) red[wave] = m;
-    __syncthreads();
-    m = (TPC == 128) ? fmaxf(red[wave & ~1], red[wave | 1])
-                     : fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  }
+  for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
   int s = 0;
   if (m > 0.0f) {
     int e;
@@ -290,34 +293,23 @@ __global__ __launch_bounds__(256) void rotate_in_kernel(const RotInArgs a) {
     s = 15 - e;
     s = s > 120 ? 120 : (s < -120 ? -120 : s);
   }
-  _Float16 q[E];
+  uint32_t w[8];
   float gs = 0.f;
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
-    q[j] = (_Float16)ldexpf(v[j], s);
-    gs += (float)q[j];
+  for (int h = 0; h < 8; ++h) {
+    const _Float16 q0 = (_Float16)ldexpf(v[2 * h], s), q1 = (_Float16)ldexpf(v[2 * h + 1], s);
+    gs += (float)q0 + (float)q1;
+    w[h] = (uint32_t)__builtin_bit_cast(uint16_t, q0) | ((uint32_t)__builtin_bit_cast(uint16_t, q1) << 16);
   }
 #pragma unroll
-  for (int o = 1; o < TPG; o <<= 1) gs += __shfl_xor(gs, o, 64);
-
+  for (int o = 1; o < 8; o <<= 1) gs += __shfl_xor(gs, o, 64);
+  if (!valid) return;
   const int R = a.rows;
-  uint16_t *xo = a.xh;
-  if constexpr (E >= 8) {
-#pragma unroll
-    for (int j8 = 0; j8 < E; j8 += 8) {
-      uint32_t w[4];
-#pragma unroll
-      for (int h = 0; h < 4; ++h)
-        w[h] = (uint32_t)__builtin_bit_cast(uint16_t, q[j8 + 2 * h]) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, q[j8 + 2 * h + 1]) << 16);
-      *reinterpret_cast<uint4 *>(xo + xa_index(k0 + j8, row, R)) = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < E; ++j) xo[xa_index(k0 + j, row, R)] = __builtin_bit_cast(uint16_t, q[j]);
-  }
-  if (tid % TPG == 0) a.meta[((size_t)(k0 >> 9) * 5 + ((k0 >> 7) & 3)) * R + row] = gs;
-  if (tid % TPC == 0) a.meta[((size_t)(k0 >> 9) * 5 + 4) * R + row] = ldexpf(a.rsqrt_b, -s);
+  const int k0 = kb + 16 * lt;
+  *reinterpret_cast<uint4 *>(a.xh + xa_index(k0, row, R)) = make_uint4(w[0], w[1], w[2], w[3]);
+  *reinterpret_cast<uint4 *>(a.xh + xa_index(k0 + 8, row, R)) = make_uint4(w[4], w[5], w[6], w[7]);
+  if ((lt & 7) == 0) a.meta[((size_t)(k0 >> 9) * 5 + ((k0 >> 7) & 3)) * R + row] = gs;
+  if ((lt & 31) == 0) a.meta[((size_t)(k0 >> 9) * 5 + 4) * R + row] = ldexpf(a.rsqrt_b, -s);
 }
 
 // ===========================================================================
@@ -354,7 +346,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
   constexpr int NW = kBasePieces + 1 + (BITS > 0 ? BITS + 1 : 0);  // weight loads per chunk
   __shared__ __attribute__((aligned(16))) _Float16 s_x[2][XH];
   __shared__ __attribute__((aligned(16))) float s_m[2][NMI * 64];
-  __shared__ uint32_t s_lut[16];
+  __shared__ uint2 s_lut[256];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   int rb = blockIdx.x;
@@ -378,7 +370,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
   const int tile = active ? tile_id : a.n_tiles - 1;
   const int c_begin = blockIdx.y * a.cps;
   const int c_end = min(a.n_chunks, c_begin + a.cps);
-  if (threadIdx.x < 16) s_lut[threadIdx.x] = L.lut[threadIdx.x];
+  s_lut[threadIdx.x] = base_table_entry(L.lut, threadIdx.x);
   const float kinv = L.kinv;
   const int tl = lane & 15, kq = lane >> 4;
   const int R = a.T;
@@ -535,45 +527,60 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
 }
 
 // ===========================================================================
-// Finish: y = S_o H_o (sum over splits of the partial y~) per (row of y,
-// superblock of 256*E output rows); without S_o it only sums the splits.
+// Finish: y = S_o H_o (sum over splits of the partial y~) per task = (row of
+// y, superblock of SB = max(b, 512) output rows), the FWHT of fwht_tasks;
+// without S_o it only sums the splits (SB = 4096, same task mapping).
 // ===========================================================================
-template <int E>
 __global__ __launch_bounds__(256) void finish_kernel(const FinishArgs a) {
-  __shared__ float xch[256 * E];
-  const int t = blockIdx.x, tid = threadIdx.x;
-  const int r0 = blockIdx.y * (256 * E) + tid * E;
+  __shared__ float xch[4096 + 256];
+  const int SB = a.OB, TPS = SB >> 4, n = 31 - __builtin_clz(SB);
+  const int tid = threadIdx.x, lt = tid % TPS, tl = tid / TPS;
+  const int n_sb = (a.d_out + SB - 1) / SB;
+  const int task = blockIdx.x * (256 / TPS) + tl;
+  const bool valid = task < a.T * n_sb;
+  const int t = valid ? task / n_sb : 0, sb = valid ? task % n_sb : 0;
+  const int rb = sb * SB;
+  float *x = xch + tl * (SB + (SB >> 4));
   const int8_t *so = a.sign_out;
-  if (a.lins) {
-    int lo = 0, hi = a.n_experts;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.offsets[mid] <= t) lo = mid; else hi = mid;
-    }
-    so = a.lins[lo].sign_out;
-  }
+  if (a.lins && valid) so = a.lins[expert_of(a.offsets, a.n_experts, t)].sign_out;
   const float *p = a.part + (size_t)t * a.d_out;
   float *y = a.y + (size_t)t * a.d_out;
-  float v[E];
+  // layout A; splits in a fixed order, the 16 loads of a split independent
+  float v[16];
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
-    const int r = r0 + j;
-    float s = 0.f;
-    if (r < a.d_out)
-      for (int sp = 0; sp < a.S; ++sp) s += p[sp * a.split_stride + r];
-    v[j] = s;
+  for (int j = 0; j < 16; ++j) v[j] = 0.f;
+  // four splits per round, all 64 loads issued before any add; the adds
+  // keep the split order, so the sum is deterministic
+  for (int sp0 = 0; sp0 < a.S; sp0 += 4) {
+    float u[4][16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int sp = min(sp0 + q, a.S - 1);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) u[q][j] = p[sp * a.split_stride + min(rb + TPS * j + lt, a.d_out - 1)];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] += (sp0 + q < a.S) ? u[q][j] : 0.f;
   }
   if (so) {
-    fwht_wg<E>(v, a.lb, xch);
+    fwht_tasks(v, x, lt, TPS, n, a.lb);
+    // layout B: 16 consecutive outputs per thread
+    const int r0 = rb + 16 * lt;
+    if (!valid) return;
 #pragma unroll
-    for (int j = 0; j < E; ++j) {
+    for (int j = 0; j < 16; ++j) {
       const int r = r0 + j;
       if (r < a.d_out) y[r] = v[j] * a.rsqrt_b * (float)so[r];
     }
   } else {
+    if (!valid) return;
 #pragma unroll
-    for (int j = 0; j < E; ++j)
-      if (r0 + j < a.d_out) y[r0 + j] = v[j];
+    for (int j = 0; j < 16; ++j) {
+      const int r = rb + TPS * j + lt;
+      if (r < a.d_out) y[r] = v[j];
+    }
   }
 }
 
@@ -605,14 +612,9 @@ hipError_t launch_decode(const DecodeArgs &a, int bits, int ntiles, hipStream_t 
 }
 
 hipError_t launch_rotate_in(const RotInArgs &a, int rows, hipStream_t s) {
-  const dim3 grid(rows, a.Kp / a.SB);
-  switch (a.SB) {
-    case 512: rotate_in_kernel<2><<<grid, 256, 0, s>>>(a); break;
-    case 1024: rotate_in_kernel<4><<<grid, 256, 0, s>>>(a); break;
-    case 2048: rotate_in_kernel<8><<<grid, 256, 0, s>>>(a); break;
-    case 4096: rotate_in_kernel<16><<<grid, 256, 0, s>>>(a); break;
-    default: return hipErrorInvalidValue;
-  }
+  if (a.SB < 512 || a.SB > 4096) return hipErrorInvalidValue;
+  const int tasks = rows * (a.Kp / a.SB), per_wg = 4096 / a.SB;
+  rotate_in_kernel<<<dim3((tasks + per_wg - 1) / per_wg), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -640,14 +642,9 @@ hipError_t launch_gemm(const GemmArgs &a, int bits, int mt, int splits, hipStrea
 }
 
 hipError_t launch_finish(const FinishArgs &a, hipStream_t s) {
-  const dim3 grid(a.T, (a.d_out + a.OB - 1) / a.OB);
-  switch (a.OB) {
-    case 512: finish_kernel<2><<<grid, 256, 0, s>>>(a); break;
-    case 1024: finish_kernel<4><<<grid, 256, 0, s>>>(a); break;
-    case 2048: finish_kernel<8><<<grid, 256, 0, s>>>(a); break;
-    case 4096: finish_kernel<16><<<grid, 256, 0, s>>>(a); break;
-    default: return hipErrorInvalidValue;
-  }
+  if (a.OB < 512 || a.OB > 4096) return hipErrorInvalidValue;
+  const int tasks = a.T * ((a.d_out + a.OB - 1) / a.OB), per_wg = 4096 / a.OB;
+  finish_kernel<<<dim3((tasks + per_wg - 1) / per_wg), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -177,25 +177,27 @@ __device__ __forceinline__ void pack_resid(const uint32_t *v, uint32_t *d) {
 
 // ---------------------------------------------------------------------------
 // Base unpack: the lane's 2 dwords of one group (code j of the lane's 32 at
-// bits 2*(j & 15) of dword j >> 4) -> 16 fp16x2 pairs looked up in a 16-entry
-// LDS table indexed by the pair's 4 code bits.  The table holds the levels
-// scaled by a per-linear constant kappa chosen so that fp16 represents them
-// (nearly) exactly; 1/kappa is folded into the base scale.
+// bits 2*(j & 15) of dword j >> 4) -> 16 fp16x2 pairs.  Each byte of the
+// codes (4 codes = 2 pairs) indexes a 256-entry LDS table of two fp16x2
+// dwords, so one ds_read_b64 yields two B-operand dwords.  The table holds
+// the levels scaled by a per-linear constant kappa chosen so that fp16
+// represents them (nearly) exactly; 1/kappa is folded into the base scale.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void unpack_base(const uint32_t *b, const uint32_t *lut_lds,
-                                            uint32_t *out) {
-  // Byte q of ev (od) holds 4 * the even (odd) 4-bit pair index of byte q of
-  // b: the LDS byte offset of the pair's table entry.
-  const char *lut = reinterpret_cast<const char *>(lut_lds);
+__device__ __forceinline__ void unpack_base(const uint32_t *b, const uint2 *lut_lds, uint32_t *out) {
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
-    const uint32_t ev = (b[w] << 2) & 0x3C3C3C3Cu, od = (b[w] >> 2) & 0x3C3C3C3Cu;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      out[8 * w + 2 * q] = *reinterpret_cast<const uint32_t *>(lut + ((ev >> (8 * q)) & 0xFFu));
-      out[8 * w + 2 * q + 1] = *reinterpret_cast<const uint32_t *>(lut + ((od >> (8 * q)) & 0xFFu));
+      const uint2 e = lut_lds[(b[w] >> (8 * q)) & 0xFFu];
+      out[8 * w + 2 * q] = e.x;
+      out[8 * w + 2 * q + 1] = e.y;
     }
   }
+}
+
+// Entry i of the byte-indexed table from the 16-entry pair table.
+__device__ __forceinline__ uint2 base_table_entry(const uint32_t *lut16, int i) {
+  return make_uint2(lut16[i & 15], lut16[i >> 4]);
 }
 
 }  // namespace nl
