@@ -71,7 +71,7 @@ def main():
         handles.append([nl.nested_linear_create(o, i, BITS, levels=lin["levels"], **d) for _ in range(ncopy)])
         del d
         xs.append(torch.from_numpy(synth.make_x(max(TS), i, cfg=1, idx=si).view(np.int16)).to(dev))
-        wss.append(torch.empty(nl.nested_linear_workspace_bytes(handles[-1][0], max(TS)), dtype=torch.uint8,
+        wss.append(torch.zeros(nl.nested_linear_workspace_bytes(handles[-1][0], max(TS)), dtype=torch.uint8,
                                device=dev))
         ys.append(torch.empty((max(TS), o), dtype=torch.float32, device=dev))
         log(f"[bench] {name} {o}x{i}: {ncopy} copies created ({time.time() - t0:.1f}s)")

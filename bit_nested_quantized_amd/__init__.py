@@ -221,7 +221,9 @@ class Linear:
     def workspace(self, T_max: int, device="cuda"):
         import torch
         n = nested_linear_workspace_bytes(self.h, T_max)
-        return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+        # zero-filled once: the calls hand work over through counters at its
+        # start and leave them at zero
+        return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 
     def forward(self, x, verify: bool, ws=None, y=None, stream=None):
         """x: int16/uint16 bf16-bit tensor [T][d_in] (or torch.bfloat16)."""

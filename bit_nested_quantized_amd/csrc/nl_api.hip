@@ -276,8 +276,11 @@ struct Plan {
   int mt;         // 16-token MFMA tiles
   int n_rb;       // 64-row workgroups per linear
   int S, cps;     // split-K count and chunks per split
-  bool finish;    // a finish pass is needed
-  size_t o_xh, o_meta, o_part, total;
+  bool finish;    // the staged path needs a finish pass
+  int mode;       // single launch: kOutDirect, kOutSplit or kOutTwoSided
+  int n_sb, sb_rows;  // output superblocks per linear and their rows
+  int n_ctr;      // counters at the start of the workspace
+  size_t o_xh, o_meta, o_part, o_ysum, total;
 };
 
 // Launch tuning knobs, read once: NL_WG_TARGET (workgroups the split-K aims
@@ -289,7 +292,7 @@ static int env_int(const char *name, int dflt) {
 static const int g_wg_target = env_int("NL_WG_TARGET", 512);
 static const int g_splits = env_int("NL_SPLITS", 0);
 
-static Plan make_plan(int d_out, int n_tiles, int n_chunks, bool sign_out, int rows, int mt,
+static Plan make_plan(int d_out, int n_tiles, int n_chunks, bool sign_out, int b_out, int rows, int mt,
                       int n_linears) {
   Plan p;
   p.rows = rows;
@@ -305,11 +308,16 @@ static Plan make_plan(int d_out, int n_tiles, int n_chunks, bool sign_out, int r
   p.cps = (n_chunks + S - 1) / S;
   p.S = (n_chunks + p.cps - 1) / p.cps;
   p.finish = sign_out || p.S > 1 || n_linears > 1;
+  p.mode = sign_out ? kOutTwoSided : (p.S > 1 ? kOutSplit : kOutDirect);
+  p.sb_rows = finish_rows(sign_out, b_out);
+  p.n_sb = (d_out + p.sb_rows - 1) / p.sb_rows;
+  p.n_ctr = kCtrFixed + n_linears * p.n_rb + 2 * n_linears * p.n_sb;
   const size_t Kp = (size_t)n_chunks * kChunk;
-  p.o_xh = 0;
+  p.o_xh = kCtrBytes;
   p.o_meta = align256(p.o_xh + (size_t)rows * Kp * 2);
   p.o_part = align256(p.o_meta + (size_t)rows * n_chunks * 5 * 4);
-  p.total = align256(p.o_part + (p.finish ? (size_t)p.S * rows * d_out * 4 : 0));
+  p.o_ysum = align256(p.o_part + (p.finish ? (size_t)p.S * rows * d_out * 4 : 0));
+  p.total = align256(p.o_ysum + (sign_out ? (size_t)rows * d_out * 4 : 0));
   return p;
 }
 
@@ -322,7 +330,7 @@ extern "C" nl_status nested_linear_workspace_bytes(nl_handle h, int32_t T_max, s
   if (T_max > NL_MAX_T) return fail(NL_EUNSUPPORTED, "workspace_bytes: T_max > %d", NL_MAX_T);
   size_t mx = 0;
   for (int T = 1; T <= T_max; ++T) {
-    Plan p = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, T, mt_for(T), 1);
+    Plan p = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, h->b_out, T, mt_for(T), 1);
     mx = p.total > mx ? p.total : mx;
   }
   *bytes = mx;
@@ -337,9 +345,11 @@ static nl_status check_call(nl_handle h, const char *who, int verify, int32_t T,
   if (T > NL_MAX_T) return fail(NL_EUNSUPPORTED, "%s: T = %d exceeds %d", who, T, NL_MAX_T);
   if (!ws) return fail(NL_EINVAL, "%s: NULL workspace", who);
   if ((uintptr_t)ws & 255) return fail(NL_EINVAL, "%s: workspace must be 256-byte aligned", who);
-  *plan = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, T, mt_for(T), 1);
+  *plan = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, h->b_out, T, mt_for(T), 1);
   if (ws_bytes < plan->total)
     return fail(NL_EINVAL, "%s: workspace too small (%zu < %zu)", who, ws_bytes, plan->total);
+  if (plan->n_ctr > kCtrLines)
+    return fail(NL_EUNSUPPORTED, "%s: d_out = %d needs %d counters (> %d)", who, h->d_out, plan->n_ctr, kCtrLines);
   return NL_OK;
 }
 
@@ -426,15 +436,63 @@ extern "C" nl_status nested_linear_finish(nl_handle h, int32_t T, float *y, void
   return ok();
 }
 
+// Counter bases, grid sizes and semaphore lines of one single-launch call.
+static void fill_launch(FwdArgs &f, const Plan &p, int n_linears, char *ws, float *y, int d_out) {
+  f.hv.ctr = (uint32_t *)ws;
+  f.hv.y = y;
+  f.hv.ysum = p.mode == kOutTwoSided ? (float *)(ws + p.o_ysum) : nullptr;
+  f.hv.mode = p.mode;
+  f.hv.S = p.S;
+  f.hv.sb_rows = p.sb_rows;
+  f.hv.n_sb = p.n_sb;
+  f.hv.rb_base = kCtrFixed;
+  f.hv.ob_base = kCtrFixed + n_linears * p.n_rb;
+  f.hv.obr_base = f.hv.ob_base + n_linears * p.n_sb;
+  f.n_rot = rotate_workgroups(p.rows, f.rot.Kp, f.rot.SB);
+  const int per = p.n_rb * p.S;
+  f.n_gemm = n_linears * per;
+  for (int k = 0; k < 8; ++k) f.per_line[k] = k < per ? (per - 1 - k) / 8 + 1 : 0;
+  f.g.out = p.mode == kOutDirect ? y : (float *)(ws + p.o_part);
+  f.g.split_stride = (size_t)p.rows * d_out;
+  f.fin.y = y;
+  f.fin.T = p.rows;
+  f.fin.d_out = d_out;
+  f.fin.S = 1;
+  f.fin.OB = p.sb_rows;
+}
+
 static nl_status forward(nl_handle h, int verify, const void *x, int32_t T, float *y, void *ws,
                          size_t ws_bytes, void *stream, const char *who) {
   Plan p;
   nl_status st = check_call(h, who, verify, T, ws, ws_bytes, &p);
   if (st != NL_OK) return st;
   if (!x || !y) return fail(NL_EINVAL, "%s: NULL x or y", who);
-  if ((st = nested_linear_prepare_input(h, x, T, ws, ws_bytes, stream)) != NL_OK) return st;
-  if ((st = nested_linear_contract(h, verify, T, y, ws, ws_bytes, stream)) != NL_OK) return st;
-  return nested_linear_finish(h, T, y, ws, ws_bytes, stream);
+  char *w = (char *)ws;
+  FwdArgs f;
+  memset(&f, 0, sizeof f);
+  f.rot = rot_args(h, x, T, w, p);
+  GemmArgs &g = f.g;
+  g.lin = h->dev;
+  g.xh = (const uint16_t *)(w + p.o_xh);
+  g.meta = (const float *)(w + p.o_meta);
+  g.T = T;
+  g.d_out = h->d_out;
+  g.n_tiles = h->n_tiles;
+  g.n_chunks = h->n_chunks;
+  g.Kp = h->n_chunks * kChunk;
+  g.Gp = h->n_chunks * 4;
+  g.cps = p.cps;
+  g.ldo = h->d_out;
+  g.n_rb = p.n_rb;
+  g.n_experts = 1;
+  f.fin.sign_out = h->dev.sign_out;
+  f.fin.b = h->b_out;
+  f.fin.lb = log2i(h->b_out);
+  f.fin.rsqrt_b = (float)(1.0 / std::sqrt((double)h->b_out));
+  fill_launch(f, p, 1, w, y, h->d_out);
+  const int n_fin = p.mode == kOutTwoSided ? finish_workgroups(T, h->d_out, p.sb_rows) : 0;
+  HIP_OR_FAIL(launch_forward(f, verify ? h->bits : 0, p.mt, n_fin, (hipStream_t)stream));
+  return ok();
 }
 
 extern "C" nl_status nested_linear_verify(nl_handle h, const void *x, int32_t T, float *y, void *ws,
@@ -525,7 +583,7 @@ extern "C" nl_status nested_linear_group_destroy(nl_group_handle g) {
 }
 
 static Plan group_plan(nl_group_handle g, int P, int T) {
-  return make_plan(g->d_out, g->n_tiles, g->n_chunks, g->has_sign_out, P, mt_for(T), g->n);
+  return make_plan(g->d_out, g->n_tiles, g->n_chunks, g->has_sign_out, g->b_out, P, mt_for(T), g->n);
 }
 
 extern "C" nl_status nested_linear_group_workspace_bytes(nl_group_handle g, int32_t P_max,
@@ -547,11 +605,13 @@ static nl_status grouped(nl_group_handle g, int verify, const int32_t *pair_toke
   if ((uintptr_t)ws & 255) return fail(NL_EINVAL, "%s: workspace must be 256-byte aligned", who);
   Plan p = group_plan(g, P, T);
   if (ws_bytes < p.total) return fail(NL_EINVAL, "%s: workspace too small (%zu < %zu)", who, ws_bytes, p.total);
+  if (p.n_ctr > kCtrLines)
+    return fail(NL_EUNSUPPORTED, "%s: %d experts of d_out = %d need %d counters (> %d)", who, g->n, g->d_out,
+                p.n_ctr, kCtrLines);
   char *w = (char *)ws;
-  hipStream_t s = (hipStream_t)stream;
-
-  RotInArgs r;
-  memset(&r, 0, sizeof r);
+  FwdArgs f;
+  memset(&f, 0, sizeof f);
+  RotInArgs &r = f.rot;
   r.x = (const uint16_t *)x;
   r.lins = g->dev_array;
   r.pair_token = pair_token;
@@ -569,16 +629,12 @@ static nl_status grouped(nl_group_handle g, int verify, const int32_t *pair_toke
   r.Gp = g->n_chunks * 4;
   r.n_chunks = g->n_chunks;
   r.rsqrt_b = (float)(1.0 / std::sqrt((double)g->b_in));
-  HIP_OR_FAIL(launch_rotate_in(r, P, s));
 
-  GemmArgs ga;
-  memset(&ga, 0, sizeof ga);
+  GemmArgs &ga = f.g;
   ga.lins = g->dev_array;
   ga.offsets = offsets;
   ga.xh = (const uint16_t *)(w + p.o_xh);
   ga.meta = (const float *)(w + p.o_meta);
-  ga.out = (float *)(w + p.o_part);
-  ga.split_stride = (size_t)P * g->d_out;
   ga.T = P;
   ga.d_out = g->d_out;
   ga.n_tiles = g->n_tiles;
@@ -589,24 +645,17 @@ static nl_status grouped(nl_group_handle g, int verify, const int32_t *pair_toke
   ga.ldo = g->d_out;
   ga.n_rb = p.n_rb;
   ga.n_experts = g->n;
-  HIP_OR_FAIL(launch_gemm(ga, verify ? g->bits : 0, p.mt, p.S, s));
 
-  FinishArgs f;
-  memset(&f, 0, sizeof f);
-  f.part = (const float *)(w + p.o_part);
-  f.split_stride = (size_t)P * g->d_out;
-  f.y = y;
-  f.lins = g->has_sign_out ? g->dev_array : nullptr;
-  f.offsets = offsets;
-  f.n_experts = g->n;
-  f.T = P;
-  f.d_out = g->d_out;
-  f.S = p.S;
-  f.b = g->b_out;
-  f.lb = log2i(g->b_out);
-  f.OB = finish_rows(g->has_sign_out, g->b_out);
-  f.rsqrt_b = (float)(1.0 / std::sqrt((double)g->b_out));
-  HIP_OR_FAIL(launch_finish(f, s));
+  FinishArgs &fa = f.fin;
+  fa.lins = g->has_sign_out ? g->dev_array : nullptr;
+  fa.offsets = offsets;
+  fa.n_experts = g->n;
+  fa.b = g->b_out;
+  fa.lb = log2i(g->b_out);
+  fa.rsqrt_b = (float)(1.0 / std::sqrt((double)g->b_out));
+  fill_launch(f, p, g->n, w, y, g->d_out);
+  const int n_fin = p.mode == kOutTwoSided ? finish_workgroups(P, g->d_out, p.sb_rows) : 0;
+  HIP_OR_FAIL(launch_forward(f, verify ? g->bits : 0, p.mt, n_fin, (hipStream_t)stream));
   return ok();
 }
 

@@ -68,10 +68,56 @@ struct FinishArgs {
   float rsqrt_b;
 };
 
+// Counters of the single-launch forward: 32-bit words, one per 64-byte
+// line, in a region of fixed size at the start of every workspace (so calls
+// of any shape can share a workspace).  Fixed slots, then per linear the
+// row-block arrival counters (split-K) and per output superblock the arrival
+// counters and finish tokens (two-sided form).
+constexpr int kCtrStride = 16;  // words
+constexpr int kCtrLines = 16384;
+constexpr size_t kCtrBytes = (size_t)kCtrLines * kCtrStride * 4;  // 1 MiB
+enum : int {
+  kCtrErr = 0,       // waits that hit the spin limit (diagnostic; stays zero)
+  kCtrRotSub = 1,    // 8 rotation arrival counters
+  kCtrRotTop = 9,    // arrival counter of the 8 above
+  kCtrReady = 10,    // 8 semaphores: tokens for the contraction workgroups
+  kCtrActive = 18,   // grouped: experts with rows (set and cleared each call)
+  kCtrFixed = 19,
+};
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+enum : int { kOutDirect = 0, kOutSplit = 1, kOutTwoSided = 2 };
+
+// What a contraction workgroup of the single launch does with its result.
+struct Handover {
+  uint32_t *ctr;
+  float *y;           // [rows][d_out] output
+  float *ysum;        // two-sided: [rows][d_out] split sums before H_o
+  int mode;           // kOutDirect, kOutSplit or kOutTwoSided
+  int S;              // splits
+  int sb_rows;        // rows per output superblock (two-sided)
+  int n_sb;           // output superblocks per linear
+  int rb_base, ob_base, obr_base;  // first counter of each kind
+  int line;           // semaphore line of the workgroup (set per workgroup)
+};
+
+struct FwdArgs {
+  RotInArgs rot;
+  GemmArgs g;         // g.out = y (direct) or the split partials
+  FinishArgs fin;
+  Handover hv;
+  int n_rot, n_gemm;
+  int per_line[8];    // contraction workgroups per semaphore line and linear
+};
+
+int rotate_workgroups(int rows, int Kp, int SB);
+int finish_workgroups(int rows, int d_out, int OB);
+
 hipError_t launch_repack(const RepackArgs &a, int bits, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, int bits, int ntiles, hipStream_t s);
 hipError_t launch_rotate_in(const RotInArgs &a, int rows, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs &a, int bits, int mt, int splits, hipStream_t s);
 hipError_t launch_finish(const FinishArgs &a, hipStream_t s);
+hipError_t launch_forward(const FwdArgs &f, int bits, int mt, int n_fin, hipStream_t s);
 
 }  // namespace nl

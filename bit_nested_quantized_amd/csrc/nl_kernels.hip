@@ -235,21 +235,72 @@ __device__ __forceinline__ int expert_of(const int32_t *offsets, int n, int row)
   return lo;
 }
 
+// An expert takes part in a grouped call when it owns at least one pair and
+// its first pair lies inside the call's R rows.  The contraction, the count
+// of waiting workgroups and the finish all use this one predicate.
+__device__ __forceinline__ bool expert_active(const int32_t *offsets, int e, int R) {
+  const int r0 = offsets[e], r1 = offsets[e + 1];
+  return r1 > r0 && r0 >= 0 && r0 < R;
+}
+
+// ===========================================================================
+// Hand-over between the workgroups of one launch.  Data written by one
+// workgroup and read by another (on any XCD) goes through agent-scope (sc1)
+// stores and loads, and a counter is bumped only after the writer's stores
+// are acknowledged (s_waitcnt vmcnt(0) in every thread, then a barrier), so
+// no L2 write-back or invalidate is needed.  Counters are 64-byte apart; the
+// launch leaves every counter at zero.
+// ===========================================================================
+__device__ __forceinline__ void st_dev(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t *p) {
+  return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ctr_add(uint32_t *p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ uint32_t *ctr_at(uint32_t *c, int i) { return c + kCtrStride * i; }
+
+// Wait for a token on semaphore `sem` and take it.  Only a workgroup whose
+// producers have lower indices waits, and workgroups are dispatched in index
+// order, so the producers are running or done; the spin limit (seconds) only
+// bounds the wait if that ever fails, and counts the event in the error word.
+__device__ void take_token(uint32_t *sem, uint32_t *err) {
+  for (uint32_t it = 0; ld_dev(sem) == 0u; ++it) {
+    if (it == kSpinLimit) {
+      ctr_add(err, 1u);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  __hip_atomic_fetch_sub(sem, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ===========================================================================
 // Input rotation (POC section 1: x' = H_i S_i x, "once per Linear").
 // Task = (row of x', superblock of SB = max(b, 512) columns), so every
-// 512-column chunk lies in one task.  Each chunk is scaled by 2^s (its
-// largest magnitude lands in [2^14, 2^15]) and rounded to fp16, the
-// contraction's MFMA operand; tsc = 2^-s / sqrt(b) undoes both factors.
-// Outputs (R = rows of x'): xh in the layout of xa_index; meta[(c*5+g)*R + r]
-// = sum of the fp16 values of group g (g < 4) and meta[(c*5+4)*R + r] = tsc.
+// 512-column chunk lies in one task; a workgroup runs 4096/SB tasks.  Each
+// chunk is scaled by 2^s (its largest magnitude lands in [2^14, 2^15]) and
+// rounded to fp16, the contraction's MFMA operand; tsc = 2^-s / sqrt(b)
+// undoes both factors.  Outputs (R = rows of x'): xh in the layout of
+// xa_index; meta[(c*5+g)*R + r] = sum of the fp16 values of group g (g < 4)
+// and meta[(c*5+4)*R + r] = tsc.  COH: agent-scope stores (read by other
+// workgroups of the same launch).
 // ===========================================================================
-__global__ __launch_bounds__(256) void rotate_in_kernel(const RotInArgs a) {
-  __shared__ float xch[4096 + 256];
+template <bool COH>
+__device__ __forceinline__ void rotate_body(const RotInArgs &a, int wg, float *xch) {
   const int SB = a.SB, TPS = SB >> 4, n = 31 - __builtin_clz(SB);
   const int tid = threadIdx.x, lt = tid % TPS, tl = tid / TPS;
   const int n_sb = a.Kp / SB;
-  const int task = blockIdx.x * (256 / TPS) + tl;
+  const int task = wg * (256 / TPS) + tl;
   const bool valid = task < a.rows * n_sb;
   const int row = valid ? task / n_sb : 0, sb = valid ? task % n_sb : 0;
   const int kb = sb * SB;
@@ -306,20 +357,39 @@ __global__ __launch_bounds__(256) void rotate_in_kernel(const RotInArgs a) {
   if (!valid) return;
   const int R = a.rows;
   const int k0 = kb + 16 * lt;
-  *reinterpret_cast<uint4 *>(a.xh + xa_index(k0, row, R)) = make_uint4(w[0], w[1], w[2], w[3]);
-  *reinterpret_cast<uint4 *>(a.xh + xa_index(k0 + 8, row, R)) = make_uint4(w[4], w[5], w[6], w[7]);
-  if ((lt & 7) == 0) a.meta[((size_t)(k0 >> 9) * 5 + ((k0 >> 7) & 3)) * R + row] = gs;
-  if ((lt & 31) == 0) a.meta[((size_t)(k0 >> 9) * 5 + 4) * R + row] = ldexpf(a.rsqrt_b, -s);
+  uint32_t *d0 = reinterpret_cast<uint32_t *>(a.xh + xa_index(k0, row, R));
+  uint32_t *d1 = reinterpret_cast<uint32_t *>(a.xh + xa_index(k0 + 8, row, R));
+  float *mg = a.meta + ((size_t)(k0 >> 9) * 5 + ((k0 >> 7) & 3)) * R + row;
+  float *ms = a.meta + ((size_t)(k0 >> 9) * 5 + 4) * R + row;
+  if constexpr (COH) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      st_dev(d0 + i, w[i]);
+      st_dev(d1 + i, w[4 + i]);
+    }
+    if ((lt & 7) == 0) st_dev(mg, gs);
+    if ((lt & 31) == 0) st_dev(ms, ldexpf(a.rsqrt_b, -s));
+  } else {
+    *reinterpret_cast<uint4 *>(d0) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4 *>(d1) = make_uint4(w[4], w[5], w[6], w[7]);
+    if ((lt & 7) == 0) *mg = gs;
+    if ((lt & 31) == 0) *ms = ldexpf(a.rsqrt_b, -s);
+  }
+}
+
+__global__ __launch_bounds__(256) void rotate_in_kernel(const RotInArgs a) {
+  __shared__ float xch[4096 + 256];
+  rotate_body<false>(a, blockIdx.x, xch);
 }
 
 // ===========================================================================
 // Fused contraction.  Workgroup = 4 waves = 4 row tiles (64 rows) over a
-// K-range of `cps` chunks (split-K index blockIdx.y).  Per chunk the
-// workgroup copies that chunk's x' (and its group sums / scales) from global
-// memory straight into one of two LDS buffers with global_load_lds (no
-// registers), one chunk ahead; each wave streams its own tile's codes from
-// HBM into registers, also one chunk ahead.  One s_barrier per chunk; the
-// waits before it are counted so the weight prefetch stays in flight.
+// K-range of `cps` chunks (split-K index `split`).  Per chunk the workgroup
+// copies that chunk's x' (and its group sums / scales) from global memory
+// straight into one of two LDS buffers with global_load_lds (no registers),
+// one chunk ahead; each wave streams its own tile's codes from HBM into
+// registers, one chunk ahead (two at the start).  One s_barrier per chunk;
+// the waits before it are counted so the weight prefetch stays in flight.
 // Per group: base and residual planes -> fp16 B operands; 4 MFMA steps per
 // plane and token tile; fp32 epilogue
 //   acc_chunk = fma(s_b / kappa, A_base, acc_chunk)
@@ -336,29 +406,37 @@ struct WRegs {
   uint64_t sb, sr;  // the row's 4 group scales (fp16) of each plane
 };
 
-template <int BITS, int MT>
-__global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
-  // (wave index read as a scalar so per-wave choices stay uniform branches)
-  constexpr int TR = 16 * MT;          // token rows staged per chunk
-  constexpr int XH = 64 * TR * 8;      // fp16 per chunk buffer (TR KiB)
-  constexpr int NMETA = 5 * TR;        // per chunk: 4 group sums + 1 scale per row
-  constexpr int NMI = ((NMETA + 255) / 256) * 4;  // metadata copies, a multiple of 4
-  constexpr int NW = kBasePieces + 1 + (BITS > 0 ? BITS + 1 : 0);  // weight loads per chunk
-  __shared__ __attribute__((aligned(16))) _Float16 s_x[2][XH];
-  __shared__ __attribute__((aligned(16))) float s_m[2][NMI * 64];
-  __shared__ uint2 s_lut[256];
+template <int MT>
+struct GemmLds {
+  static constexpr int TR = 16 * MT;          // token rows staged per chunk
+  static constexpr int XH = 64 * TR * 8;      // fp16 per chunk buffer (TR KiB)
+  static constexpr int NMETA = 5 * TR;        // per chunk: 4 group sums + 1 scale per row
+  static constexpr int NMI = ((NMETA + 255) / 256) * 4;  // metadata copies, a multiple of 4
+  static constexpr int o_m = 2 * XH * 2;
+  static constexpr int o_lut = o_m + 2 * NMI * 64 * 4;
+  static constexpr int bytes = o_lut + 256 * 8;
+};
 
+template <int BITS, int MT, bool FUSED>
+__device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, int split, char *smem,
+                                              const Handover &hv) {
+  using Lay = GemmLds<MT>;
+  constexpr int TR = Lay::TR, XH = Lay::XH, NMETA = Lay::NMETA, NMI = Lay::NMI;
+  constexpr int NW = kBasePieces + 1 + (BITS > 0 ? BITS + 1 : 0);  // weight loads per chunk
+  _Float16(*s_x)[XH] = reinterpret_cast<_Float16(*)[XH]>(smem);
+  float(*s_m)[NMI * 64] = reinterpret_cast<float(*)[NMI * 64]>(smem + Lay::o_m);
+  uint2 *s_lut = reinterpret_cast<uint2 *>(smem + Lay::o_lut);
+  __shared__ uint32_t s_flag;
+
+  // (wave index read as a scalar so per-wave choices stay uniform branches)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  int rb = blockIdx.x;
   const LinearDev *Lp = &a.lin;
   int row_base = 0, nrows = a.T;
-  if (a.lins) {  // grouped: blockIdx.x = expert * n_rb + row block
-    const int e = rb / a.n_rb;
-    rb -= e * a.n_rb;
+  if (a.lins) {
     row_base = a.offsets[e];
     nrows = a.offsets[e + 1] - row_base;
     // idle expert (or offsets outside [0, rows)): uniform exit before any barrier
-    if (nrows <= 0 || row_base < 0 || row_base >= a.T) return;
+    if (!expert_active(a.offsets, e, a.T)) return;
     Lp = a.lins + e;
   }
   nrows = min(min(nrows, TR), a.T - row_base);
@@ -368,7 +446,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
   // waves past the last tile stream the last tile again (uniform control
   // flow, exact wait counts) and store nothing
   const int tile = active ? tile_id : a.n_tiles - 1;
-  const int c_begin = blockIdx.y * a.cps;
+  const int c_begin = split * a.cps;
   const int c_end = min(a.n_chunks, c_begin + a.cps);
   s_lut[threadIdx.x] = base_table_entry(L.lut, threadIdx.x);
   const float kinv = L.kinv;
@@ -379,7 +457,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
   // --- global -> LDS copies of one chunk of activations and its metadata.
   // Issued as inline asm so the compiler's wait insertion knows nothing of
   // them (it would otherwise drain all loads before every m0 write and LDS
-  // read); their completion is covered by the counted wait in sync_chunk.
+  // read); their completion is covered by the counted waits below.
   // Branch-free: rows past nrows re-read row nrows-1 (their LDS rows only feed
   // output rows that are never stored), so every wave issues a fixed number
   // of copies.
@@ -478,91 +556,196 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
     }
   };
 
-  // wait for this wave's copies of the current chunk (issued before its NW
-  // weight loads), then the workgroup barrier makes every wave's copies
-  // visible and frees the other buffer.
+  // Wait for this wave's copies of the chunk about to be computed (issued
+  // before the NW weight loads that follow them), then the workgroup barrier
+  // makes every wave's copies visible and frees the other buffer.
   auto sync_chunk = [&]() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(NW) : "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
+  auto fence = []() { asm volatile("" ::: "memory"); };
 
-  // Software pipeline, one chunk deep: at the top of each step the copies of
-  // chunk c (issued before the NW weight loads of chunk c) are waited for,
-  // the barrier publishes them, then chunk c+1 is requested and chunk c
-  // computed.  The last chunk's prefetch slot re-requests the last chunk, so
-  // every step issues the same loads.
+  // Software pipeline.  Prologue: the weights of the first two chunks are
+  // requested before the (single-launch) wait for x', so the weight stream
+  // overlaps the rotation.  Steady state, two chunks per trip (no exit in
+  // the middle, so the compiler's waits at the loop head stay counted):
+  //   A: copy x'(c+1) -> buf1, compute c from (w0, buf0), w0 <- W(c+2), sync
+  //   B: copy x'(c+2) -> buf0, compute c+1 from (w1, buf1), w1 <- W(c+3), sync
+  // Requests past the last chunk re-request the last chunk, so every trip
+  // issues the same loads; an odd chunk count ends with one more A compute.
   WRegs<BITS> w0, w1;
-  if (c_begin < c_end) {
-    dma(c_begin, 0);
-    loadw(w0, c_begin);
+  const int c_last = c_end - 1;
+  loadw(w0, c_begin);
+  loadw(w1, min(c_begin + 1, c_last));
+  fence();
+  if constexpr (FUSED) {
+    if (threadIdx.x == 0) take_token(ctr_at(hv.ctr, kCtrReady + hv.line), ctr_at(hv.ctr, kCtrErr));
+    __builtin_amdgcn_s_barrier();
+    fence();
   }
-  for (int c = c_begin; c < c_end; c += 2) {
-    const int n1 = min(c + 1, c_end - 1);
-    sync_chunk();
-    dma(n1, 1);
-    loadw(w1, n1);
-    asm volatile("" ::: "memory");  // keep the prefetch here, ahead of compute
+  dma(c_begin, 0);
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  fence();
+  int c = c_begin;
+  for (; c + 1 < c_end; c += 2) {
+    dma(c + 1, 1);
+    fence();
     compute(w0, 0);
-    if (c + 1 >= c_end) break;
-    const int n2 = min(c + 2, c_end - 1);
+    fence();
+    loadw(w0, min(c + 2, c_last));
     sync_chunk();
-    dma(n2, 0);
-    loadw(w0, n2);
-    asm volatile("" ::: "memory");
+    dma(min(c + 2, c_last), 0);
+    fence();
     compute(w1, 1);
+    fence();
+    loadw(w1, min(c + 3, c_last));
+    sync_chunk();
   }
+  if (c < c_end) compute(w0, 0);
 
-  if (!active) return;
   const int row = tile * kTileRows + tl;  // output row of this lane (B column)
-  if (row >= a.d_out) return;
-  float *out = a.out + blockIdx.y * a.split_stride;
+  const bool store = active && row < a.d_out;
+  auto put = [&](float *out, size_t ld, bool coh) {
+    if (!store) return;
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = m * 16 + 4 * kq + i;
-      if (t < nrows) out[(size_t)(row_base + t) * a.ldo + row] = acc[m][i];
+      for (int i = 0; i < 4; ++i) {
+        const int t = m * 16 + 4 * kq + i;
+        if (t < nrows) {
+          float *p = out + (size_t)(row_base + t) * ld + row;
+          if (coh) st_dev(p, acc[m][i]); else *p = acc[m][i];
+        }
+      }
+  };
+  if constexpr (!FUSED) {
+    put(a.out + split * a.split_stride, a.ldo, false);
+    return;
+  } else {
+    const int lin = a.lins ? e : 0;
+    if (hv.mode == kOutDirect) {
+      put(a.out, a.ldo, false);
+      return;
     }
+    // Split partials, then the last workgroup of the row block to arrive sums
+    // them in split order (deterministic) into y (one-sided) or ysum.
+    float *dst = hv.mode == kOutTwoSided ? hv.ysum : hv.y;
+    if (hv.S > 1) {
+      put(a.out + split * a.split_stride, a.ldo, true);
+      wait_stores();
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        uint32_t *cnt = ctr_at(hv.ctr, hv.rb_base + lin * a.n_rb + rb);
+        const bool last = ctr_add(cnt, 1u) == (uint32_t)(hv.S - 1);
+        if (last) st_dev(cnt, 0u);
+        s_flag = last;
+      }
+      __syncthreads();
+      if (!s_flag) return;
+      const float *part = a.out;
+      const int rows_here = min(64, a.d_out - rb * 64);
+      for (int idx = threadIdx.x; idx < nrows * 64; idx += 256) {
+        const int t = idx >> 6, r = idx & 63;
+        if (r >= rows_here) continue;
+        const size_t o = (size_t)(row_base + t) * a.ldo + rb * 64 + r;
+        float u[4];
+        float v = 0.f;
+        for (int sp0 = 0; sp0 < hv.S; sp0 += 4) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) u[q] = ld_dev(part + min(sp0 + q, hv.S - 1) * a.split_stride + o);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v += (sp0 + q < hv.S) ? u[q] : 0.f;
+        }
+        if (hv.mode == kOutTwoSided) st_dev(dst + o, v); else dst[o] = v;
+      }
+    } else {
+      put(dst, a.ldo, hv.mode == kOutTwoSided);
+    }
+    if (hv.mode != kOutTwoSided) return;
+    // Two-sided: count the row block into its output superblock; the last
+    // one releases one token per finish task of the superblock.
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int sbi = (rb * 64) / hv.sb_rows;
+      const int rb_in_sb = (min(hv.sb_rows, a.d_out - sbi * hv.sb_rows) + 63) / 64;
+      uint32_t *cnt = ctr_at(hv.ctr, hv.ob_base + lin * hv.n_sb + sbi);
+      if (ctr_add(cnt, 1u) == (uint32_t)(rb_in_sb - 1)) {
+        st_dev(cnt, 0u);
+        const int tasks = a.lins ? min(a.offsets[e + 1], a.T) - a.offsets[e] : a.T;
+        ctr_add(ctr_at(hv.ctr, hv.obr_base + lin * hv.n_sb + sbi), (uint32_t)tasks);
+      }
+    }
+  }
+}
+
+template <int BITS, int MT>
+__global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[GemmLds<MT>::bytes];
+  int rb = blockIdx.x, e = 0;
+  if (a.lins) {  // grouped: blockIdx.x = expert * n_rb + row block
+    e = rb / a.n_rb;
+    rb -= e * a.n_rb;
+  }
+  Handover hv{};
+  contract_body<BITS, MT, false>(a, e, rb, blockIdx.y, smem, hv);
 }
 
 // ===========================================================================
-// Finish: y = S_o H_o (sum over splits of the partial y~) per task = (row of
-// y, superblock of SB = max(b, 512) output rows), the FWHT of fwht_tasks;
-// without S_o it only sums the splits (SB = 4096, same task mapping).
+// Finish: y = S_o H_o y~ per task = (row of y, superblock of SB = max(b, 512)
+// output rows), the FWHT of fwht_tasks; without S_o it only sums the splits
+// (SB = 4096, same task mapping).  Staged: y~ = sum of the split partials.
+// Single launch: y~ comes summed (ysum) once the task's superblock is
+// complete, signalled by one token per task.
 // ===========================================================================
-__global__ __launch_bounds__(256) void finish_kernel(const FinishArgs a) {
-  __shared__ float xch[4096 + 256];
+template <bool FUSED>
+__device__ __forceinline__ void finish_body(const FinishArgs &a, int wg, float *xch, const Handover &hv) {
   const int SB = a.OB, TPS = SB >> 4, n = 31 - __builtin_clz(SB);
   const int tid = threadIdx.x, lt = tid % TPS, tl = tid / TPS;
   const int n_sb = (a.d_out + SB - 1) / SB;
-  const int task = blockIdx.x * (256 / TPS) + tl;
+  const int task = wg * (256 / TPS) + tl;
   const bool valid = task < a.T * n_sb;
   const int t = valid ? task / n_sb : 0, sb = valid ? task % n_sb : 0;
   const int rb = sb * SB;
   float *x = xch + tl * (SB + (SB >> 4));
   const int8_t *so = a.sign_out;
-  if (a.lins && valid) so = a.lins[expert_of(a.offsets, a.n_experts, t)].sign_out;
-  const float *p = a.part + (size_t)t * a.d_out;
+  int e = 0;
+  if (a.lins && valid) {
+    e = expert_of(a.offsets, a.n_experts, t);
+    so = a.lins[e].sign_out;
+  }
   float *y = a.y + (size_t)t * a.d_out;
-  // layout A; splits in a fixed order, the 16 loads of a split independent
   float v[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) v[j] = 0.f;
-  // four splits per round, all 64 loads issued before any add; the adds
-  // keep the split order, so the sum is deterministic
-  for (int sp0 = 0; sp0 < a.S; sp0 += 4) {
-    float u[4][16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int sp = min(sp0 + q, a.S - 1);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) u[q][j] = p[sp * a.split_stride + min(rb + TPS * j + lt, a.d_out - 1)];
+  if constexpr (FUSED) {
+    if (lt == 0 && valid) {
+      const bool waits = !a.lins || (expert_active(a.offsets, e, a.T) && t < a.offsets[e + 1]);
+      if (waits) take_token(ctr_at(hv.ctr, hv.obr_base + e * n_sb + sb), ctr_at(hv.ctr, kCtrErr));
     }
+    __syncthreads();
+    const float *ys = hv.ysum + (size_t)t * a.d_out;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int j = 0; j < 16; ++j) v[j] = ld_dev(ys + min(rb + TPS * j + lt, a.d_out - 1));
+  } else {
+    const float *p = a.part + (size_t)t * a.d_out;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] += (sp0 + q < a.S) ? u[q][j] : 0.f;
+    for (int j = 0; j < 16; ++j) v[j] = 0.f;
+    // four splits per round, all 64 loads issued before any add; the adds
+    // keep the split order, so the sum is deterministic
+    for (int sp0 = 0; sp0 < a.S; sp0 += 4) {
+      float u[4][16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int sp = min(sp0 + q, a.S - 1);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) u[q][j] = p[sp * a.split_stride + min(rb + TPS * j + lt, a.d_out - 1)];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] += (sp0 + q < a.S) ? u[q][j] : 0.f;
+    }
   }
   if (so) {
     fwht_tasks(v, x, lt, TPS, n, a.lb);
@@ -582,6 +765,69 @@ __global__ __launch_bounds__(256) void finish_kernel(const FinishArgs a) {
       if (r < a.d_out) y[r] = v[j];
     }
   }
+}
+
+__global__ __launch_bounds__(256) void finish_kernel(const FinishArgs a) {
+  __shared__ float xch[4096 + 256];
+  Handover hv{};
+  finish_body<false>(a, blockIdx.x, xch, hv);
+}
+
+// ===========================================================================
+// Single-launch forward: workgroups [0, n_rot) rotate x, the next n_gemm
+// contract (each takes a token once x' is complete), the rest (two-sided
+// only) finish.  Every wait is on workgroups of lower index.
+// ===========================================================================
+template <int BITS, int MT>
+__global__ __launch_bounds__(256) void forward_kernel(const FwdArgs f) {
+  constexpr int kLds = GemmLds<MT>::bytes > (4096 + 256) * 4 ? GemmLds<MT>::bytes : (4096 + 256) * 4;
+  __shared__ __attribute__((aligned(16))) char smem[kLds];
+  __shared__ uint32_t s_cnt[4];
+  int b = blockIdx.x;
+  uint32_t *ctr = f.hv.ctr;
+  if (b < f.n_rot) {
+    rotate_body<true>(f.rot, b, reinterpret_cast<float *>(smem));
+    if (f.rot.lins && b == 0) {  // grouped: number of experts that will wait for x'
+      uint32_t cnt = 0;
+      for (int e = threadIdx.x; e < f.rot.n_experts; e += 256) cnt += expert_active(f.rot.offsets, e, f.rot.rows);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+      if ((threadIdx.x & 63) == 0) s_cnt[threadIdx.x >> 6] = cnt;
+      __syncthreads();
+      if (threadIdx.x == 0) st_dev(ctr_at(ctr, kCtrActive), s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3]);
+    }
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      // two-level arrival count (8 lines, then one); the last rotation
+      // workgroup resets both and releases one token per waiting workgroup
+      const int sub = b & 7;
+      const uint32_t in_sub = (uint32_t)((f.n_rot - 1 - sub) / 8 + 1);
+      if (ctr_add(ctr_at(ctr, kCtrRotSub + sub), 1u) == in_sub - 1) {
+        st_dev(ctr_at(ctr, kCtrRotSub + sub), 0u);
+        const uint32_t n_subs = (uint32_t)min(f.n_rot, 8);
+        if (ctr_add(ctr_at(ctr, kCtrRotTop), 1u) == n_subs - 1) {
+          st_dev(ctr_at(ctr, kCtrRotTop), 0u);
+          const uint32_t act = f.rot.lins ? ld_dev(ctr_at(ctr, kCtrActive)) : 1u;
+          if (f.rot.lins) st_dev(ctr_at(ctr, kCtrActive), 0u);
+          for (int k = 0; k < 8; ++k)
+            if (f.per_line[k] && act) ctr_add(ctr_at(ctr, kCtrReady + k), act * (uint32_t)f.per_line[k]);
+        }
+      }
+    }
+    return;
+  }
+  b -= f.n_rot;
+  if (b < f.n_gemm) {
+    const int per = f.g.n_rb * f.hv.S;
+    const int e = b / per, j = b - e * per;
+    const int split = j / f.g.n_rb, rb = j - split * f.g.n_rb;
+    Handover hv = f.hv;
+    hv.line = j & 7;
+    contract_body<BITS, MT, true>(f.g, e, rb, split, smem, hv);
+    return;
+  }
+  finish_body<true>(f.fin, b - f.n_gemm, reinterpret_cast<float *>(smem), f.hv);
 }
 
 // ===========================================================================
@@ -611,10 +857,19 @@ hipError_t launch_decode(const DecodeArgs &a, int bits, int ntiles, hipStream_t 
   return hipGetLastError();
 }
 
+int rotate_workgroups(int rows, int Kp, int SB) {
+  const int tasks = rows * (Kp / SB), per_wg = 4096 / SB;
+  return (tasks + per_wg - 1) / per_wg;
+}
+
+int finish_workgroups(int rows, int d_out, int OB) {
+  const int tasks = rows * ((d_out + OB - 1) / OB), per_wg = 4096 / OB;
+  return (tasks + per_wg - 1) / per_wg;
+}
+
 hipError_t launch_rotate_in(const RotInArgs &a, int rows, hipStream_t s) {
   if (a.SB < 512 || a.SB > 4096) return hipErrorInvalidValue;
-  const int tasks = rows * (a.Kp / a.SB), per_wg = 4096 / a.SB;
-  rotate_in_kernel<<<dim3((tasks + per_wg - 1) / per_wg), 256, 0, s>>>(a);
+  rotate_in_kernel<<<dim3(rotate_workgroups(rows, a.Kp, a.SB)), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -643,9 +898,33 @@ hipError_t launch_gemm(const GemmArgs &a, int bits, int mt, int splits, hipStrea
 
 hipError_t launch_finish(const FinishArgs &a, hipStream_t s) {
   if (a.OB < 512 || a.OB > 4096) return hipErrorInvalidValue;
-  const int tasks = a.T * ((a.d_out + a.OB - 1) / a.OB), per_wg = 4096 / a.OB;
-  finish_kernel<<<dim3((tasks + per_wg - 1) / per_wg), 256, 0, s>>>(a);
+  finish_kernel<<<dim3(finish_workgroups(a.T, a.d_out, a.OB)), 256, 0, s>>>(a);
   return hipGetLastError();
+}
+
+template <int BITS>
+static hipError_t launch_forward_bits(const FwdArgs &f, int mt, dim3 grid, hipStream_t s) {
+  switch (mt) {
+    case 1: forward_kernel<BITS, 1><<<grid, 256, 0, s>>>(f); break;
+    case 2: forward_kernel<BITS, 2><<<grid, 256, 0, s>>>(f); break;
+    case 3: forward_kernel<BITS, 3><<<grid, 256, 0, s>>>(f); break;
+    case 4: forward_kernel<BITS, 4><<<grid, 256, 0, s>>>(f); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_forward(const FwdArgs &f, int bits, int mt, int n_fin, hipStream_t s) {
+  if (f.rot.SB < 512 || f.rot.SB > 4096) return hipErrorInvalidValue;
+  if (f.hv.mode == kOutTwoSided && (f.fin.OB < 512 || f.fin.OB > 4096)) return hipErrorInvalidValue;
+  const dim3 grid(f.n_rot + f.n_gemm + n_fin);
+  switch (bits) {
+    case 0: return launch_forward_bits<0>(f, mt, grid, s);
+    case 6: return launch_forward_bits<6>(f, mt, grid, s);
+    case 7: return launch_forward_bits<7>(f, mt, grid, s);
+    case 8: return launch_forward_bits<8>(f, mt, grid, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace nl

@@ -97,8 +97,13 @@ nl_status nested_linear_destroy(nl_handle h);
 /*
  * Bytes of workspace a draft or verify call with up to T_max tokens needs
  * (host output *bytes).  The workspace is caller-owned device memory,
- * 256-byte aligned, needs no initialisation, and must not be shared by calls
- * that may run concurrently.
+ * 256-byte aligned, and must not be shared by calls that may run
+ * concurrently.  It must be zero-filled once before its first use: its
+ * first 1 MiB holds the counters through which the workgroups of one launch
+ * hand work to each other, and every call leaves them at zero again, so later
+ * calls (of any linear, any T) need no clearing.  Its first 32-bit word counts waits
+ * that ran into the kernels' spin limit; it stays zero unless the
+ * workgroup-ordering assumption the launch relies on is broken.
  */
 nl_status nested_linear_workspace_bytes(nl_handle h, int32_t T_max, size_t *bytes);
 
@@ -108,9 +113,14 @@ nl_status nested_linear_workspace_bytes(nl_handle h, int32_t T_max, size_t *byte
  *   x   [T][d_in] bf16 bit patterns (row-major); y [T][d_out] fp32 output,
  *       must not overlap x or ws.
  *   ws  workspace of ws_bytes >= nested_linear_workspace_bytes(h, T).
- * Weight bytes are streamed from HBM once per call for all T tokens.
+ * Weight bytes are streamed from HBM once per call for all T tokens.  One
+ * kernel launch: its first workgroups rotate x, the next contract (each
+ * waits for the rotation through the workspace counters, after requesting
+ * its first weights), the last (two-sided form only) apply S_o H_o.
  * Errors: NL_EINVAL (NULL pointer, T < 1, small or misaligned ws, linear
- * without a residual), NL_EUNSUPPORTED (T > 64), NL_EHIP (launch failure).
+ * without a residual), NL_EUNSUPPORTED (T > 64, or d_out beyond what the
+ * counter region serves: about 16000 row blocks of 64), NL_EHIP (launch
+ * failure).
  */
 nl_status nested_linear_verify(nl_handle h, const void *x_bf16, int32_t T, float *y,
                                void *ws, size_t ws_bytes, void *hip_stream);
@@ -123,9 +133,11 @@ nl_status nested_linear_draft(nl_handle h, const void *x_bf16, int32_t T, float 
                               void *ws, size_t ws_bytes, void *hip_stream);
 
 /*
- * The three stages a draft/verify call runs, exposed for callers that fuse or
- * time them separately.  They must run in this order, on one stream, with one
- * workspace and the same T:
+ * The three stages of a draft/verify call as separate kernel launches, for
+ * callers that time them apart or run their own work in between (draft and
+ * verify fuse them into one launch).  They must run in this order, on one
+ * stream, with one workspace and the same T; they leave the workspace
+ * counters untouched:
  *   prepare_input  x' = H_i S_i x into ws (POC section 1, "rotate the
  *                  activation once per Linear");
  *   contract       y~ = Q x' from the packed planes (verify != 0 adds the
@@ -158,7 +170,8 @@ nl_status nested_linear_group_workspace_bytes(nl_group_handle g, int32_t P_max,
 /*
  * Pair p (0 <= p < P) routes token pair_token[p] to the expert e with
  * expert_offsets[e] <= p < expert_offsets[e+1]; pairs are sorted by expert
- * and each expert receives at most 64 pairs.
+ * and an expert receives each token at most once, so at most T pairs (rows
+ * of an expert past the first 16 * ceil(T / 16) are not computed).
  *   pair_token     [P] int32 device, values in [0, T)
  *   expert_offsets [n+1] int32 device, non-decreasing, [0] = 0, [n] = P
  *   x              [T][d_in] bf16; y [P][d_out] fp32, row p = expert e's
@@ -166,8 +179,9 @@ nl_status nested_linear_group_workspace_bytes(nl_group_handle g, int32_t P_max,
  * Offsets and tokens stay on the device: experts with no pairs cost no
  * weight traffic and the host never synchronises.  The offsets and tokens
  * are trusted to satisfy the rules above (they are not validated on the
- * device).  Errors: NL_EINVAL, NL_EUNSUPPORTED (P > 64 * n or T > 4096),
- * NL_EHIP.
+ * device); offsets that break them can leave the launch waiting until the
+ * spin limit.  The workspace rules are those of nested_linear_workspace_bytes.
+ * Errors: NL_EINVAL, NL_EUNSUPPORTED (T > 64), NL_EHIP.
  */
 nl_status nested_linear_verify_grouped(nl_group_handle g, const int32_t *pair_token,
                                        const int32_t *expert_offsets, int32_t P,

@@ -36,6 +36,18 @@ def rel_err(y, ref):
     return float(np.abs(y.astype(np.float64) - ref).max() / max(np.abs(ref).max(), 1e-300))
 
 
+# White box: every workspace starts with a 1 MiB region of counters, zero
+# between calls; x' follows it.
+COUNTER_BYTES = 1 << 20
+
+
+def block(n):
+    b = 1
+    while n % (2 * b) == 0 and 2 * b <= 4096:
+        b *= 2
+    return b
+
+
 def run(nl, torch, lin, x, verify, L=None):
     L = L or nl.Linear(lin)
     y = L.forward(to_dev(torch, x), verify)
@@ -103,13 +115,14 @@ def test_prepare_input_matches_oracle_rotation(nl, torch_cuda):
     nl.nested_linear_prepare_input(L.h, to_dev(torch, x), T, ws)
     torch.cuda.synchronize()
     nch = d_in // 512
-    raw = ws[: T * d_in * 2].view(torch.float16).float().cpu().numpy()
+    o_xh = COUNTER_BYTES
+    raw = ws[o_xh: o_xh + T * d_in * 2].view(torch.float16).float().cpu().numpy()
     # activation layout: runs of 8 columns, run = ((c*4+g)*4+s)*4+q, all T rows per run
     k = np.arange(d_in)
     run = ((k >> 3) & 3) * 4 + ((k >> 5) & 3) + ((k >> 7) << 4)
     idx = (run[None, :] * T + np.arange(T)[:, None]) * 8 + (k & 7)[None, :]
     xh = raw[idx]
-    o_meta = (T * d_in * 2 + 255) // 256 * 256
+    o_meta = o_xh + (T * d_in * 2 + 255) // 256 * 256
     meta = ws[o_meta: o_meta + T * nch * 20].view(torch.float32).reshape(nch, 5, T).cpu().numpy()
     xs, tsc = meta[:, :4, :], meta[:, 4, :]
     got = xh * np.repeat(tsc.T, 512, axis=1)
@@ -266,3 +279,119 @@ def test_call_errors(nl, torch_cuda):
     assert e.value.status == nl.NL_EINVAL
     with pytest.raises(nl.NLError):
         nl.nested_linear_decode(L.h, 60, 10, torch.zeros((10, 512), dtype=torch.uint8, device="cuda"), None)
+
+
+# --- single-launch hand-over: one workspace across shapes and modes -------------
+
+# (d_out, d_in, bits, two-sided): direct store, split-K reduction, two-sided
+# with one and with several output superblocks
+MIXED = [(1024, 4096, 6, False), (4096, 4096, 6, True), (14336, 4096, 7, True),
+         (3000, 1536, 8, False), (256, 512, 8, True)]
+
+
+def test_one_workspace_many_calls_counters_return_to_zero(nl, torch_cuda):
+    torch = torch_cuda
+    Ls, xs, lins = [], [], []
+    for i, (o, d, b, two) in enumerate(MIXED):
+        lin = synth.make_linear(o, d, b, cfg=66, idx=i, two_sided=two)
+        lins.append(lin)
+        Ls.append(nl.Linear(lin))
+        xs.append(synth.make_x(64, d, cfg=66, idx=i))
+    n = max(nl.nested_linear_workspace_bytes(L.h, 64) for L in Ls)
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    for rnd in range(2):
+        for i, (o, d, b, two) in enumerate(MIXED):
+            for T in (1, 16, 64) if rnd == 0 else (7,):
+                for verify in (False, True):
+                    x = xs[i][:T]
+                    y = Ls[i].forward(to_dev(torch, x), verify, ws=ws).cpu().numpy()
+                    e = rel_err(y, oracle.forward(lins[i], x, verify))
+                    assert e <= TOL, (o, d, b, two, T, verify, e)
+                    assert int(ws[:COUNTER_BYTES].count_nonzero()) == 0, (o, d, T, verify)
+
+
+def test_split_k_shape_matches_oracle(nl, torch_cuda):
+    # every split count gives the same result within the bar
+    torch = torch_cuda
+    lin = synth.make_linear(512, 4096, 6, cfg=67, idx=0)
+    x = synth.make_x(16, 4096, cfg=67, idx=0)
+    ref = oracle.forward(lin, x, True)
+    y = run(nl, torch, lin, x, True)
+    assert rel_err(y, ref) <= TOL
+
+
+# --- grouped mixture-of-experts projections ---------------------------------------
+
+def make_moe(n_exp, d_out, d_in, bits, T, k, rho, two, cfg, shared=True):
+    experts = [synth.make_linear(d_out, d_in, bits, cfg=cfg, idx=e, two_sided=two)
+               for e in range(n_exp + int(shared))]
+    _, pt, off = synth.router_topk(T, n_exp, k, rho, cfg=cfg, idx=0)
+    if shared:  # the shared expert takes every token, after the routed ones
+        pt = np.concatenate([pt, np.arange(T, dtype=np.int32)])
+        off = np.concatenate([off, [off[-1] + T]]).astype(np.int32)
+    return experts, pt.astype(np.int32), off
+
+
+def run_grouped(nl, torch, experts, pt, off, x, verify):
+    Ls = [nl.Linear(e) for e in experts]
+    g = nl.nested_linear_group_create([L.h for L in Ls])
+    try:
+        P, T = len(pt), x.shape[0]
+        ws = torch.zeros(nl.nested_linear_group_workspace_bytes(g, P), dtype=torch.uint8, device="cuda")
+        y = torch.full((P, experts[0]["d_out"]), float("nan"), dtype=torch.float32, device="cuda")
+        fn = nl.nested_linear_verify_grouped if verify else nl.nested_linear_draft_grouped
+        pt_d = torch.from_numpy(pt).to("cuda")
+        off_d = torch.from_numpy(off).to("cuda")
+        xd = to_dev(torch, x)
+        fn(g, pt_d, off_d, P, xd, T, y, ws)
+        a = y.cpu().numpy()
+        fn(g, pt_d, off_d, P, xd, T, y, ws)   # same workspace again
+        b = y.cpu().numpy()
+        torch.cuda.synchronize()
+        assert int(ws[:COUNTER_BYTES].count_nonzero()) == 0
+        return a, b, ws
+    finally:
+        nl.nested_linear_group_destroy(g)
+
+
+@pytest.mark.parametrize("d_out,d_in", [(512, 2048), (2048, 512)])
+@pytest.mark.parametrize("two", [False, True])
+@pytest.mark.parametrize("verify", [False, True])
+def test_grouped_moe_block(nl, torch_cuda, d_out, d_in, two, verify):
+    # 64 routed experts + 1 shared, top-8 routing of a 16-token block with
+    # correlated logits (rho = 0.62), 8-bit residual
+    experts, pt, off = make_moe(64, d_out, d_in, 8, 16, 8, 0.62, two, cfg=70 + d_out % 7)
+    x = synth.make_x(16, d_in, cfg=70, idx=d_in)
+    a, b, _ = run_grouped(nl, torch_cuda, experts, pt, off, x, verify)
+    ref = oracle.forward_grouped(experts, pt, off, x, verify)
+    assert rel_err(a, ref) <= TOL
+    np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("rho", [0.0, 0.9])
+def test_grouped_routing_mixes(nl, torch_cuda, rho):
+    experts, pt, off = make_moe(32, 256, 1024, 7, 16, 4, rho, True, cfg=71)
+    x = synth.make_x(16, 1024, cfg=71, idx=int(rho * 10))
+    a, _, _ = run_grouped(nl, torch_cuda, experts, pt, off, x, True)
+    assert rel_err(a, oracle.forward_grouped(experts, pt, off, x, True)) <= TOL
+
+
+def test_grouped_many_tokens_per_expert(nl, torch_cuda):
+    # 40 tokens, top-2 of 6 experts: experts get up to 40 rows (3 token tiles)
+    experts, pt, off = make_moe(6, 384, 1536, 6, 40, 2, 0.3, False, cfg=72)
+    x = synth.make_x(40, 1536, cfg=72, idx=0)
+    for verify in (False, True):
+        a, _, _ = run_grouped(nl, torch_cuda, experts, pt, off, x, verify)
+        assert rel_err(a, oracle.forward_grouped(experts, pt, off, x, verify)) <= TOL
+
+
+def test_grouped_single_expert_equals_single_linear(nl, torch_cuda):
+    # one expert holding every token == the single-linear call, bit for bit
+    torch = torch_cuda
+    lin = synth.make_linear(1024, 2048, 8, cfg=73, idx=0)
+    x = synth.make_x(16, 2048, cfg=73, idx=0)
+    pt = np.arange(16, dtype=np.int32)
+    off = np.array([0, 16], dtype=np.int32)
+    a, _, _ = run_grouped(nl, torch, [lin], pt, off, x, True)
+    y = run(nl, torch, lin, x, True)
+    np.testing.assert_array_equal(a, y)
