@@ -295,23 +295,28 @@ __device__ void take_token(uint32_t *sem, uint32_t *err) {
 // and meta[(c*5+4)*R + r] = tsc.  COH: agent-scope stores (read by other
 // workgroups of the same launch).
 // ===========================================================================
+// Threads past the first 256 (the fifth wave of the single launch) run the
+// same code on a spare LDS area (`spare`, SB + SB/16 floats) and store nothing.
 template <bool COH>
-__device__ __forceinline__ void rotate_body(const RotInArgs &a, int wg, float *xch) {
+__device__ __forceinline__ void rotate_body(const RotInArgs &a, int wg, float *xch, float *spare) {
   const int SB = a.SB, TPS = SB >> 4, n = 31 - __builtin_clz(SB);
-  const int tid = threadIdx.x, lt = tid % TPS, tl = tid / TPS;
+  const bool extra = threadIdx.x >= 256;
+  const int tid = extra ? 0 : threadIdx.x, lt = tid % TPS, tl = tid / TPS;
   const int n_sb = a.Kp / SB;
   const int task = wg * (256 / TPS) + tl;
-  const bool valid = task < a.rows * n_sb;
+  const bool valid = !extra && task < a.rows * n_sb;
   const int row = valid ? task / n_sb : 0, sb = valid ? task % n_sb : 0;
   const int kb = sb * SB;
-  float *x = xch + tl * (SB + (SB >> 4));
+  float *x = extra ? spare : xch + tl * (SB + (SB >> 4));
 
   int xrow = valid ? row : -1;
   const int8_t *sign = a.sign;
-  if (a.lins && valid) {  // grouped: pair -> (token, expert)
-    xrow = a.pair_token[row];
-    if (xrow < 0 || xrow >= a.x_rows) xrow = -1;
-    sign = a.lins[expert_of(a.offsets, a.n_experts, row)].sign_in;
+  if (a.lins) {  // grouped: pair -> (token, expert); lanes without a task read expert 0's signs
+    if (valid) {
+      xrow = a.pair_token[row];
+      if (xrow < 0 || xrow >= a.x_rows) xrow = -1;
+    }
+    sign = a.lins[valid ? expert_of(a.offsets, a.n_experts, row) : 0].sign_in;
   }
   // layout A, unconditional loads (clamped index) so all 16 are in flight
   const uint16_t *xr = a.x + (size_t)(xrow < 0 ? 0 : xrow) * a.d_in;
@@ -379,17 +384,22 @@ __device__ __forceinline__ void rotate_body(const RotInArgs &a, int wg, float *x
 
 __global__ __launch_bounds__(256) void rotate_in_kernel(const RotInArgs a) {
   __shared__ float xch[4096 + 256];
-  rotate_body<false>(a, blockIdx.x, xch);
+  rotate_body<false>(a, blockIdx.x, xch, nullptr);
 }
 
 // ===========================================================================
-// Fused contraction.  Workgroup = 4 waves = 4 row tiles (64 rows) over a
-// K-range of `cps` chunks (split-K index `split`).  Per chunk the workgroup
-// copies that chunk's x' (and its group sums / scales) from global memory
-// straight into one of two LDS buffers with global_load_lds (no registers),
-// one chunk ahead; each wave streams its own tile's codes from HBM into
-// registers, one chunk ahead (two at the start).  One s_barrier per chunk;
-// the waits before it are counted so the weight prefetch stays in flight.
+// Fused contraction.  Workgroup = 5 waves: waves 0-3 each own one 16-row
+// tile of a 64-row block over a K-range of chunks (split-K index `split`),
+// wave 4 stages the activations.  Every global load is a global_load_lds
+// (no registers) issued in inline asm, and every wait is an explicit count:
+//   - each tile wave streams its own tile-chunks (2 + b KiB of codes plus
+//     256 B of scales) into a private LDS ring of NBUF slots, NBUF - 1
+//     chunks ahead of the one it computes, and waits only on its own loads;
+//   - the loader wave copies x' (fp16) and its group sums / scales in stages
+//     of XG groups into two LDS buffers, one stage ahead; one s_barrier per
+//     stage hands a buffer from the loader to the tile waves and back.
+// In the single launch only the loader waits for the rotation, so the tile
+// waves' first NBUF chunks stream in meanwhile.
 // Per group: base and residual planes -> fp16 B operands; 4 MFMA steps per
 // plane and token tile; fp32 epilogue
 //   acc_chunk = fma(s_b / kappa, A_base, acc_chunk)
@@ -399,37 +409,83 @@ __global__ __launch_bounds__(256) void rotate_in_kernel(const RotInArgs a) {
 #define NL_GLOBAL __attribute__((address_space(1)))
 #define NL_LOCAL __attribute__((address_space(3)))
 
-template <int BITS>
-struct WRegs {
-  u32x4 b[kBasePieces];
-  u32x4 r[BITS > 0 ? BITS : 1];
-  uint64_t sb, sr;  // the row's 4 group scales (fp16) of each plane
+constexpr int kTileWaves = 4;
+constexpr int kThreads = 64 * (kTileWaves + 1);
+constexpr int kLdsBytes = 160 * 1024;
+
+template <int BITS, int MT>
+struct LdsPlan {
+  static constexpr int TR = 16 * MT;               // token rows staged
+  static constexpr int XG = MT <= 2 ? 4 : 2;       // groups per x' stage
+  static constexpr int NST = kChunkGroups / XG;    // stages per chunk
+  static constexpr int XI = XG * TR / 4;           // x' copies per stage (1 KiB each)
+  static constexpr int XB = XI * 1024;             // bytes per x' stage buffer
+  static constexpr int MI = ((XG + 1) * TR + 63) / 64;  // metadata copies per stage (256 B each)
+  static constexpr int MB = MI * 256;
+  static constexpr int NP = kBasePieces + BITS;    // 1 KiB pieces per tile-chunk
+  static constexpr int KW = NP + 1;                // weight copies per tile-chunk (+ scales)
+  static constexpr int SLOT = NP * 1024 + 256;
+  static constexpr int o_x = 0;
+  static constexpr int o_m = 2 * XB;
+  static constexpr int o_lut = o_m + 2 * MB;
+  static constexpr int o_w = o_lut + 256 * 8;
+  static constexpr int NBUF_FIT = (kLdsBytes - o_w) / (kTileWaves * SLOT);
+  static constexpr int NBUF = NBUF_FIT > 8 ? 8 : NBUF_FIT;
+  static constexpr int bytes = o_w + kTileWaves * NBUF * SLOT;
+  static_assert(NBUF >= 2, "LDS too small for a two-slot weight ring");
 };
 
-template <int MT>
-struct GemmLds {
-  static constexpr int TR = 16 * MT;          // token rows staged per chunk
-  static constexpr int XH = 64 * TR * 8;      // fp16 per chunk buffer (TR KiB)
-  static constexpr int NMETA = 5 * TR;        // per chunk: 4 group sums + 1 scale per row
-  static constexpr int NMI = ((NMETA + 255) / 256) * 4;  // metadata copies, a multiple of 4
-  static constexpr int o_m = 2 * XH * 2;
-  static constexpr int o_lut = o_m + 2 * NMI * 64 * 4;
-  static constexpr int bytes = o_lut + 256 * 8;
-};
+// Wait until at most n of this wave's vector-memory loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+template <int KW, int NB>
+__device__ __forceinline__ void wait_ahead(int ahead) {  // ahead in [0, NB - 1]
+  static_assert(NB <= 8, "");
+  switch (ahead) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<KW>(); break;
+    case 2: wait_vm<(2 * KW < 63 ? 2 * KW : 63)>(); break;
+    case 3: wait_vm<(3 * KW < 63 ? 3 * KW : 63)>(); break;
+    case 4: wait_vm<(4 * KW < 63 ? 4 * KW : 63)>(); break;
+    case 5: wait_vm<(5 * KW < 63 ? 5 * KW : 63)>(); break;
+    case 6: wait_vm<(6 * KW < 63 ? 6 * KW : 63)>(); break;
+    default: wait_vm<(7 * KW < 63 ? 7 * KW : 63)>(); break;
+  }
+}
+
+// A wave-uniform pointer in an SGPR pair (the copies' scalar base operand).
+__device__ __forceinline__ const void *sgpr_ptr(const void *p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, const void *base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               ::"s"(lds), "v"(voff), "s"(base) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(uint32_t lds, uint32_t voff, const void *base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               ::"s"(lds), "v"(voff), "s"(base) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_abs(uint32_t lds, const void *addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               ::"s"(lds), "v"(addr) : "memory", "m0");
+}
 
 template <int BITS, int MT, bool FUSED>
 __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, int split, char *smem,
                                               const Handover &hv) {
-  using Lay = GemmLds<MT>;
-  constexpr int TR = Lay::TR, XH = Lay::XH, NMETA = Lay::NMETA, NMI = Lay::NMI;
-  constexpr int NW = kBasePieces + 1 + (BITS > 0 ? BITS + 1 : 0);  // weight loads per chunk
-  _Float16(*s_x)[XH] = reinterpret_cast<_Float16(*)[XH]>(smem);
-  float(*s_m)[NMI * 64] = reinterpret_cast<float(*)[NMI * 64]>(smem + Lay::o_m);
-  uint2 *s_lut = reinterpret_cast<uint2 *>(smem + Lay::o_lut);
+  using Pl = LdsPlan<BITS, MT>;
+  constexpr int TR = Pl::TR, XG = Pl::XG, NST = Pl::NST, NP = Pl::NP, NBUF = Pl::NBUF, KW = Pl::KW;
   __shared__ uint32_t s_flag;
 
   // (wave index read as a scalar so per-wave choices stay uniform branches)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const bool loader = wave == kTileWaves;
   const LinearDev *Lp = &a.lin;
   int row_base = 0, nrows = a.T;
   if (a.lins) {
@@ -441,169 +497,163 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
   }
   nrows = min(min(nrows, TR), a.T - row_base);
   const LinearDev &L = *Lp;
-  const int tile_id = rb * 4 + wave;
-  const bool active = tile_id < a.n_tiles;
-  // waves past the last tile stream the last tile again (uniform control
-  // flow, exact wait counts) and store nothing
-  const int tile = active ? tile_id : a.n_tiles - 1;
+  const int tile_id = rb * kTileWaves + (loader ? 0 : wave);
+  const bool active = !loader && tile_id < a.n_tiles;
+  const int tile = min(tile_id, a.n_tiles - 1);
   const int c_begin = split * a.cps;
   const int c_end = min(a.n_chunks, c_begin + a.cps);
-  s_lut[threadIdx.x] = base_table_entry(L.lut, threadIdx.x);
-  const float kinv = L.kinv;
+  const int nchk = c_end - c_begin;
+  if (threadIdx.x < 256) {
+    uint2 *s_lut = reinterpret_cast<uint2 *>(smem + Pl::o_lut);
+    s_lut[threadIdx.x] = base_table_entry(L.lut, threadIdx.x);
+  }
   const int tl = lane & 15, kq = lane >> 4;
   const int R = a.T;
-  const float bias = BITS > 0 ? resid_bias(BITS > 0 ? BITS : 8) : 0.0f;
-
-  // --- global -> LDS copies of one chunk of activations and its metadata.
-  // Issued as inline asm so the compiler's wait insertion knows nothing of
-  // them (it would otherwise drain all loads before every m0 write and LDS
-  // read); their completion is covered by the counted waits below.
-  // Branch-free: rows past nrows re-read row nrows-1 (their LDS rows only feed
-  // output rows that are never stored), so every wave issues a fixed number
-  // of copies.
-  const uint32_t xs_lds0 = (uint32_t)(uintptr_t)(NL_LOCAL void *)&s_x[0][0];
-  const uint32_t xs_lds1 = (uint32_t)(uintptr_t)(NL_LOCAL void *)&s_x[1][0];
-  const uint32_t m_lds0 = (uint32_t)(uintptr_t)(NL_LOCAL void *)&s_m[0][0];
-  const uint32_t m_lds1 = (uint32_t)(uintptr_t)(NL_LOCAL void *)&s_m[1][0];
-  auto dma = [&](int c, int buf) {
-    const uint32_t xl = buf ? xs_lds1 : xs_lds0, ml = buf ? m_lds1 : m_lds0;
-#pragma unroll
-    for (int jj = 0; jj < TR / 4; ++jj) {
-      const int j = 4 * jj + wave;
-      const int slot = 64 * j + lane;
-      const int run = slot / TR, t = min(slot % TR, nrows - 1);
-      const uint32_t voff = (uint32_t)(((c * 64 + run) * R + row_base + t) * 16);
-      const uint32_t m0v = __builtin_amdgcn_readfirstlane(xl + 64 * 16 * j);
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                   ::"s"(m0v), "v"(voff), "s"(a.xh) : "memory", "m0");
-    }
-#pragma unroll
-    for (int jj = 0; jj < NMI / 4; ++jj) {
-      const int j = 4 * jj + wave;
-      const int slot = min(64 * j + lane, NMETA - 1);
-      const uint32_t voff =
-          (uint32_t)(((c * 5 + slot / TR) * R + row_base + min(slot % TR, nrows - 1)) * 4);
-      const uint32_t m0v = __builtin_amdgcn_readfirstlane(ml + 64 * 4 * j);
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
-                   ::"s"(m0v), "v"(voff), "s"(a.meta) : "memory", "m0");
-    }
-  };
-
-  // --- this wave's tile codes for one chunk
-  const NL_GLOBAL u32x4 *bptr = (const NL_GLOBAL u32x4 *)L.base + (size_t)tile * a.n_chunks * 128 + lane;
-  const NL_GLOBAL u32x4 *rptr =
-      (const NL_GLOBAL u32x4 *)L.resid + (size_t)tile * a.n_chunks * (64 * (BITS > 0 ? BITS : 1)) + lane;
-  const NL_GLOBAL uint64_t *sbp = (const NL_GLOBAL uint64_t *)L.bscale + (size_t)tile * a.n_chunks * 16 + tl;
-  const NL_GLOBAL uint64_t *srp = (const NL_GLOBAL uint64_t *)L.rscale + (size_t)tile * a.n_chunks * 16 + tl;
-  auto loadw = [&](WRegs<BITS> &w, int c) {
-#pragma unroll
-    for (int i = 0; i < kBasePieces; ++i) w.b[i] = __builtin_nontemporal_load(bptr + (size_t)c * 128 + i * 64);
-    w.sb = sbp[(size_t)c * 16];
-    if constexpr (BITS > 0) {
-#pragma unroll
-      for (int i = 0; i < BITS; ++i) w.r[i] = __builtin_nontemporal_load(rptr + (size_t)c * (64 * BITS) + i * 64);
-      w.sr = srp[(size_t)c * 16];
-    }
-  };
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(NL_LOCAL void *)smem;
 
   floatx4 acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const WRegs<BITS> &w, int buf) {
-    const uint32_t *bw = reinterpret_cast<const uint32_t *>(w.b);
-    const uint32_t *rw = reinterpret_cast<const uint32_t *>(w.r);
-    const _Float16 *xb = &s_x[buf][(kq * TR + tl) * 8];
-    const float *mb = &s_m[buf][4 * kq];
-    floatx4 accC[MT];
+  if (loader) {
+    // ---- x' stager: stage q = (chunk c_begin + q / NST, groups [g0, g0 + XG))
+    // rows past nrows re-read row nrows - 1 (they only feed output rows that
+    // are never stored), so every stage issues the same copies.
+    const void *xsrc = sgpr_ptr(a.xh), *msrc = sgpr_ptr(a.meta);
+    auto stage = [&](int q, int buf) {
+      const int c = c_begin + q / NST, g0 = (q % NST) * XG;
+      const uint32_t xl = lds0 + Pl::o_x + buf * Pl::XB, ml = lds0 + Pl::o_m + buf * Pl::MB;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) accC[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < Pl::XI; ++j) {
+        const int slot = 64 * j + lane;
+        const int run = slot / TR, t = min(slot % TR, nrows - 1);
+        dma16(xl + 1024 * j, (uint32_t)((((c * 4 + g0) * 16 + run) * R + row_base + t) * 16), xsrc);
+      }
 #pragma unroll
-    for (int g = 0; g < kChunkGroups; ++g) {
-      uint32_t bq[16];
-      unpack_base(bw + 2 * g, s_lut, bq);
-      uint32_t rq[16];
-      if constexpr (BITS > 0) unpack_resid<BITS>(rw + g * BITS, rq);
-      const float sb = h2f((uint32_t)(w.sb >> (16 * g)) & 0xFFFFu) * kinv;
-      float sr = 0.f;
-      if constexpr (BITS > 0) sr = h2f((uint32_t)(w.sr >> (16 * g)) & 0xFFFFu);
+      for (int j = 0; j < Pl::MI; ++j) {
+        const int slot = min(64 * j + lane, (XG + 1) * TR - 1);
+        const int k = slot / TR, t = min(slot % TR, nrows - 1);
+        const int gi = k < XG ? g0 + k : 4;
+        dma4(ml + 256 * j, (uint32_t)(((c * 5 + gi) * R + row_base + t) * 4), msrc);
+      }
+    };
+    if constexpr (FUSED) {
+      if (lane == 0) take_token(ctr_at(hv.ctr, kCtrReady + hv.line), ctr_at(hv.ctr, kCtrErr));
+    }
+    const int Q = nchk * NST;
+#pragma unroll 1
+    for (int q = 0; q < Q; ++q) {
+      stage(q, q & 1);
+      wait_vm<0>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+  } else {
+    // ---- tile wave: codes and scales of this wave's tile, one chunk per slot
+    const uint32_t ring = lds0 + Pl::o_w + wave * NBUF * Pl::SLOT;
+    const size_t tc0 = (size_t)tile * a.n_chunks;
+    const void *bbase = sgpr_ptr(L.base + tc0 * 128);
+    const void *rbase = sgpr_ptr(L.resid + tc0 * (64 * (BITS > 0 ? BITS : 1)));
+    const char *scale_src = lane < 32 ? reinterpret_cast<const char *>(L.bscale + tc0 * 16) + 4 * lane
+                                      : reinterpret_cast<const char *>((BITS > 0 ? L.rscale : L.bscale) + tc0 * 16) +
+                                            4 * (lane - 32);
+    auto wdma = [&](int c, int slot) {
+      const uint32_t sl = ring + slot * Pl::SLOT;
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        floatx4 aB = {0.f, 0.f, 0.f, 0.f}, aR = {0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < kBasePieces; ++i) dma16(sl + 1024 * i, (uint32_t)((c * 128 + i * 64 + lane) * 16), bbase);
+      if constexpr (BITS > 0) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const half8 A = *reinterpret_cast<const half8 *>(xb + ((g * 4 + s) * 4 * TR + 16 * m) * 8);
-          aB = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, as_half8(bq + 4 * s), aB, 0, 0, 0);
-          if constexpr (BITS > 0)
-            aR = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, as_half8(rq + 4 * s), aR, 0, 0, 0);
+        for (int i = 0; i < BITS; ++i)
+          dma16(sl + 1024 * (kBasePieces + i), (uint32_t)((c * 64 * BITS + i * 64 + lane) * 16), rbase);
+      }
+      dma4_abs(sl + 1024 * NP, scale_src + (size_t)c * 128);
+    };
+    const int npro = min(NBUF, nchk);
+    for (int i = 0; i < npro; ++i) wdma(c_begin + i, i);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // lookup table written
+    __builtin_amdgcn_s_barrier();                         // stage 0 of x' ready
+    asm volatile("" ::: "memory");
+
+    const uint2 *s_lut = reinterpret_cast<const uint2 *>(smem + Pl::o_lut);
+    const float kinv = L.kinv;
+    const float bias = BITS > 0 ? resid_bias(BITS > 0 ? BITS : 8) : 0.0f;
+    int slot = 0;
+#pragma unroll 1
+    for (int ci = 0; ci < nchk; ++ci, slot = slot + 1 == NBUF ? 0 : slot + 1) {
+      wait_ahead<KW, NBUF>(min(NBUF - 1, nchk - 1 - ci));
+      const char *sp = smem + Pl::o_w + (wave * NBUF + slot) * Pl::SLOT;
+      u32x4 bwv[kBasePieces];
+      u32x4 rwv[BITS > 0 ? BITS : 1];
+#pragma unroll
+      for (int i = 0; i < kBasePieces; ++i) bwv[i] = *reinterpret_cast<const u32x4 *>(sp + 1024 * i + 16 * lane);
+      if constexpr (BITS > 0) {
+#pragma unroll
+        for (int i = 0; i < BITS; ++i)
+          rwv[i] = *reinterpret_cast<const u32x4 *>(sp + 1024 * (kBasePieces + i) + 16 * lane);
+      }
+      const uint64_t wsb = *reinterpret_cast<const uint64_t *>(sp + 1024 * NP + 8 * tl);
+      uint64_t wsr = 0;
+      if constexpr (BITS > 0) wsr = *reinterpret_cast<const uint64_t *>(sp + 1024 * NP + 128 + 8 * tl);
+      const uint32_t *bw = reinterpret_cast<const uint32_t *>(bwv);
+      const uint32_t *rw = reinterpret_cast<const uint32_t *>(rwv);
+      floatx4 accC[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) accC[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
+        const int q = ci * NST + st, buf = q & 1;
+        if (q > 0) {  // stage q published, stage q - 1's buffer released
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::: "memory");
         }
-        floatx4 xsv = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (BITS > 0) xsv = *reinterpret_cast<const floatx4 *>(mb + g * TR + 16 * m);
-        // Draft and verify round identically: with s_r = 0 the residual
-        // fma returns accC unchanged, so verify(0 residual) == draft bitwise.
+        const _Float16 *xb = reinterpret_cast<const _Float16 *>(smem + Pl::o_x + buf * Pl::XB) + (kq * TR + tl) * 8;
+        const float *mb = reinterpret_cast<const float *>(smem + Pl::o_m + buf * Pl::MB) + 4 * kq;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          accC[m][i] = fmaf(sb, aB[i], accC[m][i]);
-          if constexpr (BITS > 0) accC[m][i] = fmaf(sr, aR[i] - bias * xsv[i], accC[m][i]);
+        for (int gl = 0; gl < XG; ++gl) {
+          const int g = st * XG + gl;
+          uint32_t bq[16];
+          unpack_base(bw + 2 * g, s_lut, bq);
+          uint32_t rq[16];
+          if constexpr (BITS > 0) unpack_resid<BITS>(rw + g * BITS, rq);
+          const float sb = h2f((uint32_t)(wsb >> (16 * g)) & 0xFFFFu) * kinv;
+          float sr = 0.f;
+          if constexpr (BITS > 0) sr = h2f((uint32_t)(wsr >> (16 * g)) & 0xFFFFu);
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            floatx4 aB = {0.f, 0.f, 0.f, 0.f}, aR = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              const half8 A = *reinterpret_cast<const half8 *>(xb + ((gl * 4 + s) * 4 * TR + 16 * m) * 8);
+              aB = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, as_half8(bq + 4 * s), aB, 0, 0, 0);
+              if constexpr (BITS > 0)
+                aR = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, as_half8(rq + 4 * s), aR, 0, 0, 0);
+            }
+            floatx4 xsv = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (BITS > 0) xsv = *reinterpret_cast<const floatx4 *>(mb + gl * TR + 16 * m);
+            // Draft and verify round identically: with s_r = 0 the residual
+            // fma returns accC unchanged, so verify(0 residual) == draft bitwise.
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              accC[m][i] = fmaf(sb, aB[i], accC[m][i]);
+              if constexpr (BITS > 0) accC[m][i] = fmaf(sr, aR[i] - bias * xsv[i], accC[m][i]);
+            }
+          }
+        }
+        if (st == NST - 1) {
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            const floatx4 ts = *reinterpret_cast<const floatx4 *>(mb + XG * TR + 16 * m);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[m][i] = fmaf(ts[i], accC[m][i], acc[m][i]);
+          }
         }
       }
+      // the slot's reads have returned: refill it with chunk ci + NBUF
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (ci + NBUF < nchk) wdma(c_begin + ci + NBUF, slot);
     }
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const floatx4 ts = *reinterpret_cast<const floatx4 *>(mb + 4 * TR + 16 * m);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[m][i] = fmaf(ts[i], accC[m][i], acc[m][i]);
-    }
-  };
-
-  // Wait for this wave's copies of the chunk about to be computed (issued
-  // before the NW weight loads that follow them), then the workgroup barrier
-  // makes every wave's copies visible and frees the other buffer.
-  auto sync_chunk = [&]() {
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(NW) : "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
-  auto fence = []() { asm volatile("" ::: "memory"); };
-
-  // Software pipeline.  Prologue: the weights of the first two chunks are
-  // requested before the (single-launch) wait for x', so the weight stream
-  // overlaps the rotation.  Steady state, two chunks per trip (no exit in
-  // the middle, so the compiler's waits at the loop head stay counted):
-  //   A: copy x'(c+1) -> buf1, compute c from (w0, buf0), w0 <- W(c+2), sync
-  //   B: copy x'(c+2) -> buf0, compute c+1 from (w1, buf1), w1 <- W(c+3), sync
-  // Requests past the last chunk re-request the last chunk, so every trip
-  // issues the same loads; an odd chunk count ends with one more A compute.
-  WRegs<BITS> w0, w1;
-  const int c_last = c_end - 1;
-  loadw(w0, c_begin);
-  loadw(w1, min(c_begin + 1, c_last));
-  fence();
-  if constexpr (FUSED) {
-    if (threadIdx.x == 0) take_token(ctr_at(hv.ctr, kCtrReady + hv.line), ctr_at(hv.ctr, kCtrErr));
-    __builtin_amdgcn_s_barrier();
-    fence();
   }
-  dma(c_begin, 0);
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  fence();
-  int c = c_begin;
-  for (; c + 1 < c_end; c += 2) {
-    dma(c + 1, 1);
-    fence();
-    compute(w0, 0);
-    fence();
-    loadw(w0, min(c + 2, c_last));
-    sync_chunk();
-    dma(min(c + 2, c_last), 0);
-    fence();
-    compute(w1, 1);
-    fence();
-    loadw(w1, min(c + 3, c_last));
-    sync_chunk();
-  }
-  if (c < c_end) compute(w0, 0);
 
   const int row = tile * kTileRows + tl;  // output row of this lane (B column)
   const bool store = active && row < a.d_out;
@@ -646,7 +696,7 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
       if (!s_flag) return;
       const float *part = a.out;
       const int rows_here = min(64, a.d_out - rb * 64);
-      for (int idx = threadIdx.x; idx < nrows * 64; idx += 256) {
+      for (int idx = threadIdx.x; idx < nrows * 64; idx += kThreads) {
         const int t = idx >> 6, r = idx & 63;
         if (r >= rows_here) continue;
         const size_t o = (size_t)(row_base + t) * a.ldo + rb * 64 + r;
@@ -682,8 +732,8 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
 }
 
 template <int BITS, int MT>
-__global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[GemmLds<MT>::bytes];
+__global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[LdsPlan<BITS, MT>::bytes];
   int rb = blockIdx.x, e = 0;
   if (a.lins) {  // grouped: blockIdx.x = expert * n_rb + row block
     e = rb / a.n_rb;
@@ -701,19 +751,24 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
 // complete, signalled by one token per task.
 // ===========================================================================
 template <bool FUSED>
-__device__ __forceinline__ void finish_body(const FinishArgs &a, int wg, float *xch, const Handover &hv) {
+__device__ __forceinline__ void finish_body(const FinishArgs &a, int wg, float *xch, float *spare,
+                                            const Handover &hv) {
   const int SB = a.OB, TPS = SB >> 4, n = 31 - __builtin_clz(SB);
-  const int tid = threadIdx.x, lt = tid % TPS, tl = tid / TPS;
+  const bool extra = threadIdx.x >= 256;
+  const int tid = extra ? 0 : threadIdx.x, lt = tid % TPS, tl = tid / TPS;
   const int n_sb = (a.d_out + SB - 1) / SB;
   const int task = wg * (256 / TPS) + tl;
-  const bool valid = task < a.T * n_sb;
+  const bool valid = !extra && task < a.T * n_sb;
   const int t = valid ? task / n_sb : 0, sb = valid ? task % n_sb : 0;
   const int rb = sb * SB;
-  float *x = xch + tl * (SB + (SB >> 4));
+  float *x = extra ? spare : xch + tl * (SB + (SB >> 4));
+  // the output rotation is a property of the call (uniform: fwht_tasks has
+  // barriers); lanes without a task read expert 0's signs and store nothing
+  const bool rotate_out = a.lins ? a.lins[0].sign_out != nullptr : a.sign_out != nullptr;
   const int8_t *so = a.sign_out;
   int e = 0;
-  if (a.lins && valid) {
-    e = expert_of(a.offsets, a.n_experts, t);
+  if (a.lins) {
+    if (valid) e = expert_of(a.offsets, a.n_experts, t);
     so = a.lins[e].sign_out;
   }
   float *y = a.y + (size_t)t * a.d_out;
@@ -747,7 +802,7 @@ __device__ __forceinline__ void finish_body(const FinishArgs &a, int wg, float *
         for (int j = 0; j < 16; ++j) v[j] += (sp0 + q < a.S) ? u[q][j] : 0.f;
     }
   }
-  if (so) {
+  if (rotate_out) {
     fwht_tasks(v, x, lt, TPS, n, a.lb);
     // layout B: 16 consecutive outputs per thread
     const int r0 = rb + 16 * lt;
@@ -770,7 +825,7 @@ __device__ __forceinline__ void finish_body(const FinishArgs &a, int wg, float *
 __global__ __launch_bounds__(256) void finish_kernel(const FinishArgs a) {
   __shared__ float xch[4096 + 256];
   Handover hv{};
-  finish_body<false>(a, blockIdx.x, xch, hv);
+  finish_body<false>(a, blockIdx.x, xch, nullptr, hv);
 }
 
 // ===========================================================================
@@ -779,20 +834,23 @@ __global__ __launch_bounds__(256) void finish_kernel(const FinishArgs a) {
 // only) finish.  Every wait is on workgroups of lower index.
 // ===========================================================================
 template <int BITS, int MT>
-__global__ __launch_bounds__(256) void forward_kernel(const FwdArgs f) {
-  constexpr int kLds = GemmLds<MT>::bytes > (4096 + 256) * 4 ? GemmLds<MT>::bytes : (4096 + 256) * 4;
+__global__ __launch_bounds__(kThreads) void forward_kernel(const FwdArgs f) {
+  constexpr int kFwht = (4096 + 256) * 4;  // one workgroup FWHT area (bytes)
+  constexpr int kLds = LdsPlan<BITS, MT>::bytes > 2 * kFwht ? LdsPlan<BITS, MT>::bytes : 2 * kFwht;
   __shared__ __attribute__((aligned(16))) char smem[kLds];
   __shared__ uint32_t s_cnt[4];
+  float *xch = reinterpret_cast<float *>(smem), *spare = reinterpret_cast<float *>(smem + kFwht);
   int b = blockIdx.x;
   uint32_t *ctr = f.hv.ctr;
   if (b < f.n_rot) {
-    rotate_body<true>(f.rot, b, reinterpret_cast<float *>(smem));
+    rotate_body<true>(f.rot, b, xch, spare);
     if (f.rot.lins && b == 0) {  // grouped: number of experts that will wait for x'
       uint32_t cnt = 0;
-      for (int e = threadIdx.x; e < f.rot.n_experts; e += 256) cnt += expert_active(f.rot.offsets, e, f.rot.rows);
+      if (threadIdx.x < 256)
+        for (int e = threadIdx.x; e < f.rot.n_experts; e += 256) cnt += expert_active(f.rot.offsets, e, f.rot.rows);
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
-      if ((threadIdx.x & 63) == 0) s_cnt[threadIdx.x >> 6] = cnt;
+      if ((threadIdx.x & 63) == 0 && threadIdx.x < 256) s_cnt[threadIdx.x >> 6] = cnt;
       __syncthreads();
       if (threadIdx.x == 0) st_dev(ctr_at(ctr, kCtrActive), s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3]);
     }
@@ -827,7 +885,7 @@ __global__ __launch_bounds__(256) void forward_kernel(const FwdArgs f) {
     contract_body<BITS, MT, true>(f.g, e, rb, split, smem, hv);
     return;
   }
-  finish_body<true>(f.fin, b - f.n_gemm, reinterpret_cast<float *>(smem), f.hv);
+  finish_body<true>(f.fin, b - f.n_gemm, xch, spare, f.hv);
 }
 
 // ===========================================================================
@@ -876,10 +934,10 @@ hipError_t launch_rotate_in(const RotInArgs &a, int rows, hipStream_t s) {
 template <int BITS>
 static hipError_t launch_gemm_bits(const GemmArgs &a, int mt, dim3 grid, hipStream_t s) {
   switch (mt) {
-    case 1: gemm_kernel<BITS, 1><<<grid, 256, 0, s>>>(a); break;
-    case 2: gemm_kernel<BITS, 2><<<grid, 256, 0, s>>>(a); break;
-    case 3: gemm_kernel<BITS, 3><<<grid, 256, 0, s>>>(a); break;
-    case 4: gemm_kernel<BITS, 4><<<grid, 256, 0, s>>>(a); break;
+    case 1: gemm_kernel<BITS, 1><<<grid, kThreads, 0, s>>>(a); break;
+    case 2: gemm_kernel<BITS, 2><<<grid, kThreads, 0, s>>>(a); break;
+    case 3: gemm_kernel<BITS, 3><<<grid, kThreads, 0, s>>>(a); break;
+    case 4: gemm_kernel<BITS, 4><<<grid, kThreads, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -905,10 +963,10 @@ hipError_t launch_finish(const FinishArgs &a, hipStream_t s) {
 template <int BITS>
 static hipError_t launch_forward_bits(const FwdArgs &f, int mt, dim3 grid, hipStream_t s) {
   switch (mt) {
-    case 1: forward_kernel<BITS, 1><<<grid, 256, 0, s>>>(f); break;
-    case 2: forward_kernel<BITS, 2><<<grid, 256, 0, s>>>(f); break;
-    case 3: forward_kernel<BITS, 3><<<grid, 256, 0, s>>>(f); break;
-    case 4: forward_kernel<BITS, 4><<<grid, 256, 0, s>>>(f); break;
+    case 1: forward_kernel<BITS, 1><<<grid, kThreads, 0, s>>>(f); break;
+    case 2: forward_kernel<BITS, 2><<<grid, kThreads, 0, s>>>(f); break;
+    case 3: forward_kernel<BITS, 3><<<grid, kThreads, 0, s>>>(f); break;
+    case 4: forward_kernel<BITS, 4><<<grid, kThreads, 0, s>>>(f); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -395,3 +395,14 @@ def test_grouped_single_expert_equals_single_linear(nl, torch_cuda):
     a, _, _ = run_grouped(nl, torch, [lin], pt, off, x, True)
     y = run(nl, torch, lin, x, True)
     np.testing.assert_array_equal(a, y)
+
+
+def test_grouped_partial_workgroups(nl, torch_cuda):
+    # 14 pairs over 1024-wide blocks: the rotation and finish workgroups (4
+    # tasks each) end half full, so lanes without a task run in every role
+    experts, pt, off = make_moe(5, 1024, 1024, 6, 7, 1, 0.5, True, cfg=74)
+    x = synth.make_x(7, 1024, cfg=74, idx=0)
+    assert len(pt) % 4 != 0
+    for verify in (False, True):
+        a, _, _ = run_grouped(nl, torch_cuda, experts, pt, off, x, verify)
+        assert rel_err(a, oracle.forward_grouped(experts, pt, off, x, verify)) <= TOL
