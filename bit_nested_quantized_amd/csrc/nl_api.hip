@@ -280,35 +280,37 @@ struct Plan {
   int mode;       // single launch: kOutDirect, kOutSplit or kOutTwoSided
   int n_sb, sb_rows;  // output superblocks per linear and their rows
   int n_ctr;      // counters at the start of the workspace
+  bool local;     // single launch rotates x inside the contraction workgroups
   size_t o_xh, o_meta, o_part, o_ysum, total;
 };
 
 // Launch tuning knobs, read once: NL_WG_TARGET (workgroups the split-K aims
-// for, default 512) and NL_SPLITS (force the split count).
+// for, default 256: one per CU) and NL_SPLITS (force the split count).
 static int env_int(const char *name, int dflt) {
   const char *v = getenv(name);
   return (v && *v) ? atoi(v) : dflt;
 }
-static const int g_wg_target = env_int("NL_WG_TARGET", 512);
+static const int g_wg_target = env_int("NL_WG_TARGET", 256);
 static const int g_splits = env_int("NL_SPLITS", 0);
 
+// tokens: rows of x per linear (T; a grouped call routes each token to an
+// expert at most once).
 static Plan make_plan(int d_out, int n_tiles, int n_chunks, bool sign_out, int b_out, int rows, int mt,
-                      int n_linears) {
+                      int n_linears, int tokens) {
   Plan p;
   p.rows = rows;
   p.mt = mt;
   p.n_rb = (n_tiles + 3) / 4;
-  // Split K until the grid holds ~2 workgroups per CU (256 CUs), keeping at
-  // least 2 chunks per split.
-  int S = (g_wg_target + p.n_rb * n_linears - 1) / (p.n_rb * n_linears);
-  S = S < 1 ? 1 : S;
-  const int smax = n_chunks / 2 > 0 ? n_chunks / 2 : 1;
-  S = S > smax ? smax : S;
+  // Split K while the grid stays within one workgroup per CU (256 CUs).
+  int S = g_wg_target / (p.n_rb * n_linears);
+  S = S < 1 ? 1 : (S > n_chunks ? n_chunks : S);
   if (g_splits > 0) S = g_splits < n_chunks ? g_splits : n_chunks;
   p.cps = (n_chunks + S - 1) / S;
   p.S = (n_chunks + p.cps - 1) / p.cps;
   p.finish = sign_out || p.S > 1 || n_linears > 1;
   p.mode = sign_out ? kOutTwoSided : (p.S > 1 ? kOutSplit : kOutDirect);
+  p.local = mt == 1 && tokens <= kLocalRows && p.cps <= kLocalChunks;
+  if (p.local) p.mt = 0;
   p.sb_rows = finish_rows(sign_out, b_out);
   p.n_sb = (d_out + p.sb_rows - 1) / p.sb_rows;
   p.n_ctr = kCtrFixed + n_linears * p.n_rb + 2 * n_linears * p.n_sb;
@@ -330,7 +332,7 @@ extern "C" nl_status nested_linear_workspace_bytes(nl_handle h, int32_t T_max, s
   if (T_max > NL_MAX_T) return fail(NL_EUNSUPPORTED, "workspace_bytes: T_max > %d", NL_MAX_T);
   size_t mx = 0;
   for (int T = 1; T <= T_max; ++T) {
-    Plan p = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, h->b_out, T, mt_for(T), 1);
+    Plan p = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, h->b_out, T, mt_for(T), 1, T);
     mx = p.total > mx ? p.total : mx;
   }
   *bytes = mx;
@@ -345,7 +347,7 @@ static nl_status check_call(nl_handle h, const char *who, int verify, int32_t T,
   if (T > NL_MAX_T) return fail(NL_EUNSUPPORTED, "%s: T = %d exceeds %d", who, T, NL_MAX_T);
   if (!ws) return fail(NL_EINVAL, "%s: NULL workspace", who);
   if ((uintptr_t)ws & 255) return fail(NL_EINVAL, "%s: workspace must be 256-byte aligned", who);
-  *plan = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, h->b_out, T, mt_for(T), 1);
+  *plan = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, h->b_out, T, mt_for(T), 1, T);
   if (ws_bytes < plan->total)
     return fail(NL_EINVAL, "%s: workspace too small (%zu < %zu)", who, ws_bytes, plan->total);
   if (plan->n_ctr > kCtrLines)
@@ -408,7 +410,7 @@ extern "C" nl_status nested_linear_contract(nl_handle h, int32_t verify, int32_t
   g.ldo = h->d_out;
   g.n_rb = p.n_rb;
   g.n_experts = 1;
-  HIP_OR_FAIL(launch_gemm(g, verify ? h->bits : 0, p.mt, p.S, (hipStream_t)stream));
+  HIP_OR_FAIL(launch_gemm(g, verify ? h->bits : 0, mt_for(T), p.S, (hipStream_t)stream));
   return ok();
 }
 
@@ -448,7 +450,7 @@ static void fill_launch(FwdArgs &f, const Plan &p, int n_linears, char *ws, floa
   f.hv.rb_base = kCtrFixed;
   f.hv.ob_base = kCtrFixed + n_linears * p.n_rb;
   f.hv.obr_base = f.hv.ob_base + n_linears * p.n_sb;
-  f.n_rot = rotate_workgroups(p.rows, f.rot.Kp, f.rot.SB);
+  f.n_rot = p.local ? 0 : rotate_workgroups(p.rows, f.rot.Kp, f.rot.SB);
   const int per = p.n_rb * p.S;
   f.n_gemm = n_linears * per;
   for (int k = 0; k < 8; ++k) f.per_line[k] = k < per ? (per - 1 - k) / 8 + 1 : 0;
@@ -583,7 +585,7 @@ extern "C" nl_status nested_linear_group_destroy(nl_group_handle g) {
 }
 
 static Plan group_plan(nl_group_handle g, int P, int T) {
-  return make_plan(g->d_out, g->n_tiles, g->n_chunks, g->has_sign_out, g->b_out, P, mt_for(T), g->n);
+  return make_plan(g->d_out, g->n_tiles, g->n_chunks, g->has_sign_out, g->b_out, P, mt_for(T), g->n, T);
 }
 
 extern "C" nl_status nested_linear_group_workspace_bytes(nl_group_handle g, int32_t P_max,

@@ -192,26 +192,32 @@ __device__ __forceinline__ void bfly16(float (&v)[16], int bit) {
 }
 
 // v: layout A on entry, layout B on exit.  xch: this task's LDS (SB + SB/16).
-__device__ __forceinline__ void fwht_tasks(float (&v)[16], float *xch, int lt, int TPS, int n, int lb) {
+// idle: a thread (uniformly per wave) that only keeps the barrier count.
+__device__ __forceinline__ void fwht_tasks(float (&v)[16], float *xch, int lt, int TPS, int n, int lb,
+                                           bool idle = false) {
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     if (n - 4 + q < lb) bfly16(v, q);
   __syncthreads();
+  if (!idle)
 #pragma unroll
-  for (int j = 0; j < 16; ++j) xch[lds_pad(TPS * j + lt)] = v[j];
+    for (int j = 0; j < 16; ++j) xch[lds_pad(TPS * j + lt)] = v[j];
   __syncthreads();
   const int cbase = (lt & 15) + 256 * (lt >> 4);
+  if (!idle)
 #pragma unroll
-  for (int j = 0; j < 16; ++j) v[j] = xch[lds_pad(cbase + 16 * j)];
+    for (int j = 0; j < 16; ++j) v[j] = xch[lds_pad(cbase + 16 * j)];
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     if (4 + q < n - 4 && 4 + q < lb) bfly16(v, q);
   __syncthreads();
+  if (!idle)
 #pragma unroll
-  for (int j = 0; j < 16; ++j) xch[lds_pad(cbase + 16 * j)] = v[j];
+    for (int j = 0; j < 16; ++j) xch[lds_pad(cbase + 16 * j)] = v[j];
   __syncthreads();
+  if (!idle)
 #pragma unroll
-  for (int j = 0; j < 16; ++j) v[j] = xch[lds_pad(16 * lt + j)];
+    for (int j = 0; j < 16; ++j) v[j] = xch[lds_pad(16 * lt + j)];
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     if (q < lb) bfly16(v, q);
@@ -390,16 +396,16 @@ __global__ __launch_bounds__(256) void rotate_in_kernel(const RotInArgs a) {
 // ===========================================================================
 // Fused contraction.  Workgroup = 5 waves: waves 0-3 each own one 16-row
 // tile of a 64-row block over a K-range of chunks (split-K index `split`),
-// wave 4 stages the activations.  Every global load is a global_load_lds
-// (no registers) issued in inline asm, and every wait is an explicit count:
-//   - each tile wave streams its own tile-chunks (2 + b KiB of codes plus
-//     256 B of scales) into a private LDS ring of NBUF slots, NBUF - 1
-//     chunks ahead of the one it computes, and waits only on its own loads;
-//   - the loader wave copies x' (fp16) and its group sums / scales in stages
-//     of XG groups into two LDS buffers, one stage ahead; one s_barrier per
-//     stage hands a buffer from the loader to the tile waves and back.
+// wave 4 stages the activations.
+//   - each tile wave streams its own tile-chunks (2 + b pieces of 1 KiB plus
+//     the scales) from HBM into registers, two chunks in flight; it issues no
+//     other loads, so the compiler's waits on them are exact;
+//   - the loader wave copies x' (fp16) and its group sums / scales with
+//     global_load_lds into a ring of NX LDS stages of XG groups, NX - 1
+//     stages ahead; one s_barrier per stage hands a stage to the tile waves
+//     and the stage before it back to the loader.
 // In the single launch only the loader waits for the rotation, so the tile
-// waves' first NBUF chunks stream in meanwhile.
+// waves' first two chunks stream in meanwhile.  Two workgroups fit a CU.
 // Per group: base and residual planes -> fp16 B operands; 4 MFMA steps per
 // plane and token tile; fp32 epilogue
 //   acc_chunk = fma(s_b / kappa, A_base, acc_chunk)
@@ -419,39 +425,58 @@ struct LdsPlan {
   static constexpr int XG = MT <= 2 ? 4 : 2;       // groups per x' stage
   static constexpr int NST = kChunkGroups / XG;    // stages per chunk
   static constexpr int XI = XG * TR / 4;           // x' copies per stage (1 KiB each)
-  static constexpr int XB = XI * 1024;             // bytes per x' stage buffer
   static constexpr int MI = ((XG + 1) * TR + 63) / 64;  // metadata copies per stage (256 B each)
-  static constexpr int MB = MI * 256;
-  static constexpr int NP = kBasePieces + BITS;    // 1 KiB pieces per tile-chunk
-  static constexpr int KW = NP + 1;                // weight copies per tile-chunk (+ scales)
-  static constexpr int SLOT = NP * 1024 + 256;
-  static constexpr int o_x = 0;
-  static constexpr int o_m = 2 * XB;
-  static constexpr int o_lut = o_m + 2 * MB;
-  static constexpr int o_w = o_lut + 256 * 8;
-  static constexpr int NBUF_FIT = (kLdsBytes - o_w) / (kTileWaves * SLOT);
-  static constexpr int NBUF = NBUF_FIT > 8 ? 8 : NBUF_FIT;
-  static constexpr int bytes = o_w + kTileWaves * NBUF * SLOT;
-  static_assert(NBUF >= 2, "LDS too small for a two-slot weight ring");
+  static constexpr int XB = XI * 1024 + MI * 256;  // bytes per x' stage (activations, then metadata)
+  static constexpr int NW = kBasePieces + 1 + (BITS > 0 ? BITS + 1 : 0);  // weight loads per chunk
+  static constexpr int o_lut = 0;
+  static constexpr int o_x = 256 * 8;
+  // x' stages in flight: up to 4 while two workgroups still fit one CU
+  static constexpr int NX_FIT = (kLdsBytes / 2 - o_x) / XB;
+  static constexpr int NX_CNT = 2 + 63 / (XI + MI);  // the loader's wait count fits vmcnt
+  static constexpr int NX_A = NX_FIT < NX_CNT ? NX_FIT : NX_CNT;
+  static constexpr int NX = NX_A > 4 ? 4 : (NX_A < 2 ? 2 : NX_A);
+  static constexpr int bytes = o_x + NX * XB;
+  static constexpr int XWAIT = (NX - 2) * (XI + MI);  // loader copies after the stage it waits for
+  static_assert(bytes <= kLdsBytes && XWAIT <= 63, "x' ring does not fit");
 };
 
-// Wait until at most n of this wave's vector-memory loads are outstanding.
+// Local rotation (at most kLocalRows rows of x'): the workgroup rotates the x
+// blocks its K-range touches itself and keeps x' for the whole range in LDS,
+// laid out [chunk][run][kLocalRows rows][8 fp16], with the group sums and
+// scales as [chunk][5][kLocalRows] floats.
+struct LocalPlan {
+  static constexpr int o_lut = 0;
+  static constexpr int o_x = 256 * 8;
+  static constexpr int XC = 64 * kLocalRows * 16;            // bytes per chunk
+  static constexpr int o_m = o_x + kLocalChunks * XC;
+  static constexpr int o_f = o_m + kLocalChunks * 5 * kLocalRows * 4;
+  static constexpr int bytes = o_f + (4096 + 256) * 4;      // + one FWHT area
+};
+
+// Wait until at most n of this wave's vector-memory operations are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-template <int KW, int NB>
-__device__ __forceinline__ void wait_ahead(int ahead) {  // ahead in [0, NB - 1]
-  static_assert(NB <= 8, "");
-  switch (ahead) {
-    case 0: wait_vm<0>(); break;
-    case 1: wait_vm<KW>(); break;
-    case 2: wait_vm<(2 * KW < 63 ? 2 * KW : 63)>(); break;
-    case 3: wait_vm<(3 * KW < 63 ? 3 * KW : 63)>(); break;
-    case 4: wait_vm<(4 * KW < 63 ? 4 * KW : 63)>(); break;
-    case 5: wait_vm<(5 * KW < 63 ? 5 * KW : 63)>(); break;
-    case 6: wait_vm<(6 * KW < 63 ? 6 * KW : 63)>(); break;
-    default: wait_vm<(7 * KW < 63 ? 7 * KW : 63)>(); break;
+
+template <int BITS>
+struct WRegs {
+  u32x4 b[kBasePieces];
+  u32x4 r[BITS > 0 ? BITS : 1];
+  uint64_t sb, sr;  // the row's 4 group scales (fp16) of each plane
+};
+
+// An ordered no-op on every register of a set: work on the set cannot be
+// scheduled above it, so the wait for the set's loads lands here.
+template <int BITS>
+__device__ __forceinline__ void pin(WRegs<BITS> &w) {
+#pragma unroll
+  for (int i = 0; i < kBasePieces; ++i) asm volatile("" : "+v"(w.b[i]));
+  asm volatile("" : "+v"(w.sb));
+  if constexpr (BITS > 0) {
+#pragma unroll
+    for (int i = 0; i < BITS; ++i) asm volatile("" : "+v"(w.r[i]));
+    asm volatile("" : "+v"(w.sr));
   }
 }
 
@@ -471,16 +496,16 @@ __device__ __forceinline__ void dma4(uint32_t lds, uint32_t voff, const void *ba
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
                ::"s"(lds), "v"(voff), "s"(base) : "memory", "m0");
 }
-__device__ __forceinline__ void dma4_abs(uint32_t lds, const void *addr) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-               ::"s"(lds), "v"(addr) : "memory", "m0");
-}
-
+// MT = 0: local rotation mode (single launch only; rot describes x).
 template <int BITS, int MT, bool FUSED>
 __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, int split, char *smem,
-                                              const Handover &hv) {
-  using Pl = LdsPlan<BITS, MT>;
-  constexpr int TR = Pl::TR, XG = Pl::XG, NST = Pl::NST, NP = Pl::NP, NBUF = Pl::NBUF, KW = Pl::KW;
+                                              const Handover &hv, const RotInArgs &rot) {
+  constexpr bool LOCAL = MT == 0;
+  constexpr int MTC = LOCAL ? 1 : MT;  // 16-row MFMA token tiles
+  using Pl = LdsPlan<BITS, MTC>;
+  constexpr int TR = LOCAL ? kLocalRows : Pl::TR, XG = LOCAL ? 4 : Pl::XG, NST = LOCAL ? 1 : Pl::NST;
+  constexpr int NX = Pl::NX;
+  static_assert(!LOCAL || FUSED, "local rotation runs in the single launch only");
   __shared__ uint32_t s_flag;
 
   // (wave index read as a scalar so per-wave choices stay uniform branches)
@@ -503,26 +528,28 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
   const int c_begin = split * a.cps;
   const int c_end = min(a.n_chunks, c_begin + a.cps);
   const int nchk = c_end - c_begin;
-  if (threadIdx.x < 256) {
-    uint2 *s_lut = reinterpret_cast<uint2 *>(smem + Pl::o_lut);
+  if (threadIdx.x < 256) {  // (LocalPlan::o_lut == LdsPlan::o_lut == 0)
+    uint2 *s_lut = reinterpret_cast<uint2 *>(smem);
     s_lut[threadIdx.x] = base_table_entry(L.lut, threadIdx.x);
   }
   const int tl = lane & 15, kq = lane >> 4;
   const int R = a.T;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(NL_LOCAL void *)smem;
 
-  floatx4 acc[MT];
+  floatx4 acc[MTC];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < MTC; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  if (loader) {
+  if (!LOCAL && loader) {
     // ---- x' stager: stage q = (chunk c_begin + q / NST, groups [g0, g0 + XG))
     // rows past nrows re-read row nrows - 1 (they only feed output rows that
     // are never stored), so every stage issues the same copies.
     const void *xsrc = sgpr_ptr(a.xh), *msrc = sgpr_ptr(a.meta);
-    auto stage = [&](int q, int buf) {
+    const int Q = nchk * NST;
+    auto stage = [&](int q) {
+      q = min(q, Q - 1);  // past the end: re-copy the last stage into a free buffer
       const int c = c_begin + q / NST, g0 = (q % NST) * XG;
-      const uint32_t xl = lds0 + Pl::o_x + buf * Pl::XB, ml = lds0 + Pl::o_m + buf * Pl::MB;
+      const uint32_t xl = lds0 + Pl::o_x + (q % NX) * Pl::XB, ml = xl + Pl::XI * 1024;
 #pragma unroll
       for (int j = 0; j < Pl::XI; ++j) {
         const int slot = 64 * j + lane;
@@ -537,78 +564,78 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
         dma4(ml + 256 * j, (uint32_t)(((c * 5 + gi) * R + row_base + t) * 4), msrc);
       }
     };
-    if constexpr (FUSED) {
+    if constexpr (FUSED && !LOCAL) {
       if (lane == 0) take_token(ctr_at(hv.ctr, kCtrReady + hv.line), ctr_at(hv.ctr, kCtrErr));
     }
-    const int Q = nchk * NST;
+    // Stage q lives in buffer q % NX.  Barrier #q publishes stage q and
+    // tells the loader the tile waves are done with stage q - 1, whose
+    // buffer then receives stage q + NX - 1.
+    for (int q = 0; q < NX - 1; ++q) stage(q);
 #pragma unroll 1
     for (int q = 0; q < Q; ++q) {
-      stage(q, q & 1);
-      wait_vm<0>();
+      wait_vm<Pl::XWAIT>();
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
+      stage(q + NX - 1);
     }
+    wait_vm<0>();
   } else {
-    // ---- tile wave: codes and scales of this wave's tile, one chunk per slot
-    const uint32_t ring = lds0 + Pl::o_w + wave * NBUF * Pl::SLOT;
-    const size_t tc0 = (size_t)tile * a.n_chunks;
-    const void *bbase = sgpr_ptr(L.base + tc0 * 128);
-    const void *rbase = sgpr_ptr(L.resid + tc0 * (64 * (BITS > 0 ? BITS : 1)));
-    const char *scale_src = lane < 32 ? reinterpret_cast<const char *>(L.bscale + tc0 * 16) + 4 * lane
-                                      : reinterpret_cast<const char *>((BITS > 0 ? L.rscale : L.bscale) + tc0 * 16) +
-                                            4 * (lane - 32);
-    auto wdma = [&](int c, int slot) {
-      const uint32_t sl = ring + slot * Pl::SLOT;
+    // ---- tile wave: this wave's tile codes, two chunks in flight in registers
+    const NL_GLOBAL u32x4 *bptr = (const NL_GLOBAL u32x4 *)L.base + (size_t)tile * a.n_chunks * 128 + lane;
+    const NL_GLOBAL u32x4 *rptr =
+        (const NL_GLOBAL u32x4 *)L.resid + (size_t)tile * a.n_chunks * (64 * (BITS > 0 ? BITS : 1)) + lane;
+    const NL_GLOBAL uint64_t *sbp = (const NL_GLOBAL uint64_t *)L.bscale + (size_t)tile * a.n_chunks * 16 + tl;
+    const NL_GLOBAL uint64_t *srp = (const NL_GLOBAL uint64_t *)L.rscale + (size_t)tile * a.n_chunks * 16 + tl;
+    // one fixed issue order everywhere (the fences keep the scheduler from
+    // interleaving), so the waits the compiler counts agree on every path
+    auto fence = []() { asm volatile("" ::: "memory"); };
+    auto loadw = [&](WRegs<BITS> &w, int c) {
 #pragma unroll
-      for (int i = 0; i < kBasePieces; ++i) dma16(sl + 1024 * i, (uint32_t)((c * 128 + i * 64 + lane) * 16), bbase);
+      for (int i = 0; i < kBasePieces; ++i) {
+        w.b[i] = __builtin_nontemporal_load(bptr + (size_t)c * 128 + i * 64);
+        fence();
+      }
+      w.sb = sbp[(size_t)c * 16];
+      fence();
       if constexpr (BITS > 0) {
 #pragma unroll
-        for (int i = 0; i < BITS; ++i)
-          dma16(sl + 1024 * (kBasePieces + i), (uint32_t)((c * 64 * BITS + i * 64 + lane) * 16), rbase);
+        for (int i = 0; i < BITS; ++i) {
+          w.r[i] = __builtin_nontemporal_load(rptr + (size_t)c * (64 * BITS) + i * 64);
+          fence();
+        }
+        w.sr = srp[(size_t)c * 16];
+        fence();
       }
-      dma4_abs(sl + 1024 * NP, scale_src + (size_t)c * 128);
     };
-    const int npro = min(NBUF, nchk);
-    for (int i = 0; i < npro; ++i) wdma(c_begin + i, i);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // lookup table written
-    __builtin_amdgcn_s_barrier();                         // stage 0 of x' ready
-    asm volatile("" ::: "memory");
-
-    const uint2 *s_lut = reinterpret_cast<const uint2 *>(smem + Pl::o_lut);
+    const uint2 *s_lut = reinterpret_cast<const uint2 *>(smem);
     const float kinv = L.kinv;
     const float bias = BITS > 0 ? resid_bias(BITS > 0 ? BITS : 8) : 0.0f;
-    int slot = 0;
-#pragma unroll 1
-    for (int ci = 0; ci < nchk; ++ci, slot = slot + 1 == NBUF ? 0 : slot + 1) {
-      wait_ahead<KW, NBUF>(min(NBUF - 1, nchk - 1 - ci));
-      const char *sp = smem + Pl::o_w + (wave * NBUF + slot) * Pl::SLOT;
-      u32x4 bwv[kBasePieces];
-      u32x4 rwv[BITS > 0 ? BITS : 1];
+    // compute chunk ci (its NST stages, a barrier before every stage but the first overall)
+    auto compute = [&](WRegs<BITS> &w, int ci) {
+      pin(w);
+      const uint32_t *bw = reinterpret_cast<const uint32_t *>(w.b);
+      const uint32_t *rw = reinterpret_cast<const uint32_t *>(w.r);
+      floatx4 accC[MTC];
 #pragma unroll
-      for (int i = 0; i < kBasePieces; ++i) bwv[i] = *reinterpret_cast<const u32x4 *>(sp + 1024 * i + 16 * lane);
-      if constexpr (BITS > 0) {
-#pragma unroll
-        for (int i = 0; i < BITS; ++i)
-          rwv[i] = *reinterpret_cast<const u32x4 *>(sp + 1024 * (kBasePieces + i) + 16 * lane);
-      }
-      const uint64_t wsb = *reinterpret_cast<const uint64_t *>(sp + 1024 * NP + 8 * tl);
-      uint64_t wsr = 0;
-      if constexpr (BITS > 0) wsr = *reinterpret_cast<const uint64_t *>(sp + 1024 * NP + 128 + 8 * tl);
-      const uint32_t *bw = reinterpret_cast<const uint32_t *>(bwv);
-      const uint32_t *rw = reinterpret_cast<const uint32_t *>(rwv);
-      floatx4 accC[MT];
-#pragma unroll
-      for (int m = 0; m < MT; ++m) accC[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int m = 0; m < MTC; ++m) accC[m] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < NST; ++st) {
-        const int q = ci * NST + st, buf = q & 1;
-        if (q > 0) {  // stage q published, stage q - 1's buffer released
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-          __builtin_amdgcn_s_barrier();
-          asm volatile("" ::: "memory");
+        const _Float16 *xb;
+        const float *mb;
+        if constexpr (LOCAL) {  // resident x': rows past kLocalRows repeat (never stored)
+          xb = reinterpret_cast<const _Float16 *>(smem + LocalPlan::o_x + ci * LocalPlan::XC) +
+               (kq * TR + (tl & (TR - 1))) * 8;
+          mb = reinterpret_cast<const float *>(smem + LocalPlan::o_m) + ci * 5 * TR;
+        } else {
+          const int q = ci * NST + st, buf = q % NX;
+          if (q > 0) {  // stage q published, stage q - 1's buffer released
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+          }
+          xb = reinterpret_cast<const _Float16 *>(smem + Pl::o_x + buf * Pl::XB) + (kq * TR + tl) * 8;
+          mb = reinterpret_cast<const float *>(smem + Pl::o_x + buf * Pl::XB + Pl::XI * 1024) + 4 * kq;
         }
-        const _Float16 *xb = reinterpret_cast<const _Float16 *>(smem + Pl::o_x + buf * Pl::XB) + (kq * TR + tl) * 8;
-        const float *mb = reinterpret_cast<const float *>(smem + Pl::o_m + buf * Pl::MB) + 4 * kq;
 #pragma unroll
         for (int gl = 0; gl < XG; ++gl) {
           const int g = st * XG + gl;
@@ -616,11 +643,11 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
           unpack_base(bw + 2 * g, s_lut, bq);
           uint32_t rq[16];
           if constexpr (BITS > 0) unpack_resid<BITS>(rw + g * BITS, rq);
-          const float sb = h2f((uint32_t)(wsb >> (16 * g)) & 0xFFFFu) * kinv;
+          const float sb = h2f((uint32_t)(w.sb >> (16 * g)) & 0xFFFFu) * kinv;
           float sr = 0.f;
-          if constexpr (BITS > 0) sr = h2f((uint32_t)(wsr >> (16 * g)) & 0xFFFFu);
+          if constexpr (BITS > 0) sr = h2f((uint32_t)(w.sr >> (16 * g)) & 0xFFFFu);
 #pragma unroll
-          for (int m = 0; m < MT; ++m) {
+          for (int m = 0; m < MTC; ++m) {
             floatx4 aB = {0.f, 0.f, 0.f, 0.f}, aR = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
@@ -642,16 +669,133 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
         }
         if (st == NST - 1) {
 #pragma unroll
-          for (int m = 0; m < MT; ++m) {
+          for (int m = 0; m < MTC; ++m) {
             const floatx4 ts = *reinterpret_cast<const floatx4 *>(mb + XG * TR + 16 * m);
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[m][i] = fmaf(ts[i], accC[m][i], acc[m][i]);
           }
         }
       }
-      // the slot's reads have returned: refill it with chunk ci + NBUF
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      if (ci + NBUF < nchk) wdma(c_begin + ci + NBUF, slot);
+    };
+    // Two chunks per trip and no exit in the middle, so the compiler's
+    // waits on the weight registers stay counted; requests past the last
+    // chunk re-request the last one (uniform loads), and an odd count ends
+    // with one more compute.
+    const int c_last = c_end - 1;
+    WRegs<BITS> w0, w1;
+    if constexpr (LOCAL) {
+      // ---- x' of this K-range, rotated here (the rotation role's arithmetic):
+      // tasks (row t, superblock of SB columns), 4096/SB per pass over the
+      // first four waves; the fifth wave only keeps the barrier count.  The
+      // first pass's x loads go out before the weights, so waiting for them
+      // leaves the weight loads in flight.
+      const RotInArgs &ra = rot;
+      const int SB = ra.SB, TPS = SB >> 4, nlog = 31 - __builtin_clz(SB);
+      const bool idle = threadIdx.x >= 256;
+      const int rtid = idle ? 0 : threadIdx.x, lt = rtid % TPS, tg = rtid / TPS;
+      const int kbeg = c_begin * kChunk, kend = c_end * kChunk;
+      const int sb0 = kbeg / SB, nsb = (kend - 1) / SB - sb0 + 1;
+      const int per_pass = 4096 / SB, ntask = nrows * nsb, npass = (ntask + per_pass - 1) / per_pass;
+      const int8_t *sign = a.lins ? a.lins[e].sign_in : ra.sign;
+      float *xs = reinterpret_cast<float *>(smem + LocalPlan::o_f) + tg * (SB + (SB >> 4));
+      char *xres = smem + LocalPlan::o_x;
+      float *mres = reinterpret_cast<float *>(smem + LocalPlan::o_m);
+      uint16_t xv[16];
+      int8_t sv[16];
+      int t = 0, kb = 0, xrow = -1;
+      bool valid = false;
+      auto rload = [&](int p) __attribute__((always_inline)) {
+        const int task = p * per_pass + tg;
+        valid = !idle && task < ntask;
+        t = valid ? task % nrows : 0;
+        kb = (sb0 + (valid ? task / nrows : 0)) * SB;
+        xrow = valid ? row_base + t : -1;
+        if (a.lins && valid) {
+          xrow = ra.pair_token[row_base + t];
+          if (xrow < 0 || xrow >= ra.x_rows) xrow = -1;
+        }
+        if (idle) return;
+        const uint16_t *xr = ra.x + (size_t)(xrow < 0 ? 0 : xrow) * ra.d_in;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int k = min(kb + TPS * j + lt, ra.d_in - 1);
+          xv[j] = xr[k];
+          sv[j] = sign[k];
+        }
+      };
+      auto rproc = [&]() __attribute__((always_inline)) {
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int k = kb + TPS * j + lt;
+          v[j] = (k < ra.d_in && xrow >= 0) ? bf16_to_float(xv[j]) * (float)sv[j] : 0.0f;
+        }
+        fwht_tasks(v, xs, lt, TPS, nlog, ra.lb, idle);
+        float mx = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(v[j]));
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        int sc = 0;
+        if (mx > 0.0f) {
+          int ex;
+          frexpf(mx, &ex);
+          sc = 15 - ex;
+          sc = sc > 120 ? 120 : (sc < -120 ? -120 : sc);
+        }
+        uint32_t wv[8];
+        float gs = 0.f;
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+          const _Float16 q0 = (_Float16)ldexpf(v[2 * h], sc), q1 = (_Float16)ldexpf(v[2 * h + 1], sc);
+          gs += (float)q0 + (float)q1;
+          wv[h] = (uint32_t)__builtin_bit_cast(uint16_t, q0) | ((uint32_t)__builtin_bit_cast(uint16_t, q1) << 16);
+        }
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) gs += __shfl_xor(gs, o, 64);
+        const int k0 = kb + 16 * lt;
+        if (!valid || k0 < kbeg || k0 >= kend) return;
+        const int cl = (k0 >> 9) - c_begin;
+        const int run0 = ((k0 >> 3) & 3) * 4 + ((k0 >> 5) & 3) + ((k0 >> 7) & 3) * 16;
+        const int run1 = (((k0 + 8) >> 3) & 3) * 4 + ((k0 >> 5) & 3) + ((k0 >> 7) & 3) * 16;
+        *reinterpret_cast<uint4 *>(xres + ((cl * 64 + run0) * TR + t) * 16) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        *reinterpret_cast<uint4 *>(xres + ((cl * 64 + run1) * TR + t) * 16) = make_uint4(wv[4], wv[5], wv[6], wv[7]);
+        if ((lt & 7) == 0) mres[(cl * 5 + ((k0 >> 7) & 3)) * TR + t] = gs;
+        if ((lt & 31) == 0) mres[(cl * 5 + 4) * TR + t] = ldexpf(ra.rsqrt_b, -sc);
+      };
+      rload(0);
+      if (!loader) {
+        fence();
+        loadw(w0, c_begin);
+        loadw(w1, min(c_begin + 1, c_last));
+      }
+      rproc();
+#pragma unroll 1
+      for (int p = 1; p < npass; ++p) {
+        rload(p);
+        rproc();
+      }
+      __syncthreads();  // x' resident, lookup table written
+    } else {
+      fence();
+      loadw(w0, c_begin);
+      loadw(w1, min(c_begin + 1, c_last));
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // lookup table written
+      __builtin_amdgcn_s_barrier();                         // stage 0 of x' ready
+      asm volatile("" ::: "memory");
+    }
+    if (!loader) {
+      int ci = 0;
+#pragma unroll 1
+      for (; ci + 1 < nchk; ci += 2) {
+        compute(w0, ci);
+        fence();
+        loadw(w0, min(c_begin + ci + 2, c_last));
+        compute(w1, ci + 1);
+        fence();
+        loadw(w1, min(c_begin + ci + 3, c_last));
+      }
+      if (ci < nchk) compute(w0, ci);
     }
   }
 
@@ -660,7 +804,7 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
   auto put = [&](float *out, size_t ld, bool coh) {
     if (!store) return;
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MTC; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = m * 16 + 4 * kq + i;
@@ -740,7 +884,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmArgs a) {
     rb -= e * a.n_rb;
   }
   Handover hv{};
-  contract_body<BITS, MT, false>(a, e, rb, blockIdx.y, smem, hv);
+  const RotInArgs none{};
+  contract_body<BITS, MT, false>(a, e, rb, blockIdx.y, smem, hv, none);
 }
 
 // ===========================================================================
@@ -836,7 +981,8 @@ __global__ __launch_bounds__(256) void finish_kernel(const FinishArgs a) {
 template <int BITS, int MT>
 __global__ __launch_bounds__(kThreads) void forward_kernel(const FwdArgs f) {
   constexpr int kFwht = (4096 + 256) * 4;  // one workgroup FWHT area (bytes)
-  constexpr int kLds = LdsPlan<BITS, MT>::bytes > 2 * kFwht ? LdsPlan<BITS, MT>::bytes : 2 * kFwht;
+  constexpr int kPlan = MT == 0 ? LocalPlan::bytes : LdsPlan<BITS, (MT == 0 ? 1 : MT)>::bytes;
+  constexpr int kLds = kPlan > 2 * kFwht ? kPlan : 2 * kFwht;
   __shared__ __attribute__((aligned(16))) char smem[kLds];
   __shared__ uint32_t s_cnt[4];
   float *xch = reinterpret_cast<float *>(smem), *spare = reinterpret_cast<float *>(smem + kFwht);
@@ -882,7 +1028,7 @@ __global__ __launch_bounds__(kThreads) void forward_kernel(const FwdArgs f) {
     const int split = j / f.g.n_rb, rb = j - split * f.g.n_rb;
     Handover hv = f.hv;
     hv.line = j & 7;
-    contract_body<BITS, MT, true>(f.g, e, rb, split, smem, hv);
+    contract_body<BITS, MT, true>(f.g, e, rb, split, smem, hv, f.rot);
     return;
   }
   finish_body<true>(f.fin, b - f.n_gemm, xch, spare, f.hv);
@@ -963,6 +1109,7 @@ hipError_t launch_finish(const FinishArgs &a, hipStream_t s) {
 template <int BITS>
 static hipError_t launch_forward_bits(const FwdArgs &f, int mt, dim3 grid, hipStream_t s) {
   switch (mt) {
+    case 0: forward_kernel<BITS, 0><<<grid, kThreads, 0, s>>>(f); break;
     case 1: forward_kernel<BITS, 1><<<grid, kThreads, 0, s>>>(f); break;
     case 2: forward_kernel<BITS, 2><<<grid, kThreads, 0, s>>>(f); break;
     case 3: forward_kernel<BITS, 3><<<grid, kThreads, 0, s>>>(f); break;

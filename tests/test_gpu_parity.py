@@ -216,17 +216,22 @@ def test_repeat_runs_are_bitwise_identical(nl, torch_cuda):
         np.testing.assert_array_equal(L.forward(x, True, ws=ws).cpu().numpy(), a)
 
 
-def test_staged_calls_equal_fused_call(nl, torch_cuda):
+@pytest.mark.parametrize("T", [1, 3, 8])
+@pytest.mark.parametrize("two", [False, True])
+def test_staged_calls_equal_fused_call(nl, torch_cuda, T, two):
+    # The staged kernels rotate x in their own launch; the single launch
+    # rotates it in rotation workgroups (T > 4) or inside every contraction
+    # workgroup (T <= 4).  Same arithmetic, so the outputs agree bit for bit.
     torch = torch_cuda
-    lin = synth.make_linear(2048, 4096, 8, cfg=63, idx=0)
-    x = to_dev(torch, synth.make_x(8, 4096, cfg=63, idx=0))
+    lin = synth.make_linear(2048, 4096, 8, cfg=63, idx=T, two_sided=two)
+    x = to_dev(torch, synth.make_x(T, 4096, cfg=63, idx=T))
     L = nl.Linear(lin)
-    ws = L.workspace(8)
+    ws = L.workspace(T)
     a = L.forward(x, True, ws=ws)
     y = torch.empty_like(a)
-    nl.nested_linear_prepare_input(L.h, x, 8, ws)
-    nl.nested_linear_contract(L.h, True, 8, y, ws)
-    nl.nested_linear_finish(L.h, 8, y, ws)
+    nl.nested_linear_prepare_input(L.h, x, T, ws)
+    nl.nested_linear_contract(L.h, True, T, y, ws)
+    nl.nested_linear_finish(L.h, T, y, ws)
     torch.cuda.synchronize()
     assert torch.equal(a, y)
 
@@ -406,3 +411,16 @@ def test_grouped_partial_workgroups(nl, torch_cuda):
     for verify in (False, True):
         a, _, _ = run_grouped(nl, torch_cuda, experts, pt, off, x, verify)
         assert rel_err(a, oracle.forward_grouped(experts, pt, off, x, verify)) <= TOL
+
+
+@pytest.mark.parametrize("T", [1, 4])
+@pytest.mark.parametrize("two", [False, True])
+def test_grouped_few_tokens(nl, torch_cuda, T, two):
+    # a block of at most 4 tokens: each contraction workgroup rotates its
+    # expert's rows itself
+    experts, pt, off = make_moe(16, 512, 2048, 8, T, 4, 0.62, two, cfg=75 + T)
+    x = synth.make_x(T, 2048, cfg=75, idx=T)
+    for verify in (False, True):
+        a, b, _ = run_grouped(nl, torch_cuda, experts, pt, off, x, verify)
+        assert rel_err(a, oracle.forward_grouped(experts, pt, off, x, verify)) <= TOL
+        np.testing.assert_array_equal(a, b)
