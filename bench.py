@@ -2,20 +2,27 @@
 """Benchmark of the bit-nested quantized linear on one MI355X.
 
 Workload: the 7B/8B-class projections (4096x4096, 1024x4096, 14336x4096,
-4096x14336), 2-bit base + 6-bit residual with fp16 group-128 scales, bf16
-N(0,1) activations.  One step = draft and verify passes over all four
-projections at T = 1, 4, 8, 16 and 32 draft-tree tokens (40 calls), captured
-in one HIP graph.  Weights rotate through a pool of distinct copies larger
-than the 256 MB Infinity Cache, so every call streams its weights from HBM.
+4096x14336), 2-bit Lloyd-Max base + 6-bit residual with fp16 group-128
+scales, bf16 N(0,1) activations, in the one-sided form y = (Q_b + Q_r) H S x.
+One step = a draft and a verify pass over all four projections at each of
+T = 1, 4, 8, 16 and 32 draft-tree tokens (40 calls, one kernel launch each),
+captured in one HIP graph.  Weights rotate through a pool of distinct copies
+larger than the 256 MB Infinity Cache, so every call streams its weights from
+HBM.  Inputs are resident in HBM before the timed region.
 
-value = effective weight GB/s of a step (algorithmic bytes: codes + fp16
-scales, 0.265625 B/weight draft, 1.03125 B/weight verify, over the step's
-time).  Prints one JSON line on stdout; progress goes to stderr.
+value = effective weight GB/s of a step: algorithmic bytes (codes + fp16
+scales: 0.265625 B/weight draft, 1.03125 B/weight verify) over the step time.
+per_case gives the microseconds per pass over the four projections and the
+weight GB/s for T = 1, 4, 8, 16, 32 and 64 (graph-amortised), the
+launch-inclusive time of one eager call, and the two-sided form at T = 1, 16.
+Prints one JSON line on stdout; progress goes to stderr.
 """
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -23,13 +30,39 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 SHAPES = [("q/o", 4096, 4096), ("k/v", 1024, 4096), ("gate/up", 14336, 4096), ("down", 4096, 14336)]
-TS = [1, 4, 8, 16, 32]
+STEP_TS = [1, 4, 8, 16, 32]
+CASE_TS = [1, 4, 8, 16, 32, 64]
 BITS = 6
 HBM_PEAK_GBPS = 8000.0
+ROOFLINE_TS = (8, 16)   # verify launches of forward_kernel<6, 1> (one 16-token tile, rotation workgroups)
+ROOFLINE_KERNEL = "forward_kernel<6, 1>"
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest():
+    """Digest of the kernel sources, to tie stored counter readings to them."""
+    h = hashlib.sha256()
+    for f in ("nl_kernels.hip", "nl_kernels.h", "nl_layout.h"):
+        with open(os.path.join(ROOT, "bit_nested_quantized_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(digest):
+    """HBM bytes per launch of the roofline kernel from the committed counter
+    summary, when it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "forward_kernel_verify_T8_T16_cfg1_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"kernel source digest:\s*([0-9a-f]+)", text)
+    m_val = re.search(r"hbm bytes per launch:\s*([0-9.]+)", text)
+    if not m_src or not m_val or m_src.group(1) != digest:
+        return None
+    return float(m_val.group(1))
 
 
 def main():
@@ -39,11 +72,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--pool-gib", type=float, default=1.2)
     ap.add_argument("--reps", type=int, default=10, help="graph replays per per-case timing")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures the single-GPU path only; run it with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: this build has no multi-GPU path (run it with --gpus 1)",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -57,74 +92,88 @@ def main():
     dev = "cuda"
     torch.cuda.set_device(0)
 
+    def bpw(verify):
+        return synth.bytes_per_weight(BITS if verify else 0)
+
     # ---- weights: one synthetic linear per shape, repacked into a pool of copies
-    set_bytes = sum(o * i for _, o, i in SHAPES) * synth.bytes_per_weight(BITS)
+    set_bytes = sum(o * i for _, o, i in SHAPES) * bpw(True)
     ncopy = max(2, math.ceil(args.pool_gib * 2 ** 30 / set_bytes))
     lins, handles, xs, wss, ys = [], [], [], [], []
     t0 = time.time()
+
+    def to_dev(lin):
+        return {k: (None if lin[k] is None else torch.from_numpy(np.ascontiguousarray(lin[k]).view(dt)).to(dev))
+                for k, dt in [("base_codes", np.uint8), ("base_scales", np.int16), ("resid_codes", np.uint8),
+                              ("resid_scales", np.int16), ("sign_in", np.int8), ("sign_out", np.int8)]}
+
     for si, (name, o, i) in enumerate(SHAPES):
-        lin = synth.make_linear(o, i, BITS, cfg=1, idx=si)
+        lin = synth.make_linear(o, i, BITS, cfg=1, idx=si, two_sided=False)
         lins.append(lin)
-        d = {k: (None if lin[k] is None else torch.from_numpy(np.ascontiguousarray(lin[k]).view(dt)).to(dev))
-             for k, dt in [("base_codes", np.uint8), ("base_scales", np.int16), ("resid_codes", np.uint8),
-                           ("resid_scales", np.int16), ("sign_in", np.int8), ("sign_out", np.int8)]}
+        d = to_dev(lin)
         handles.append([nl.nested_linear_create(o, i, BITS, levels=lin["levels"], **d) for _ in range(ncopy)])
         del d
-        xs.append(torch.from_numpy(synth.make_x(max(TS), i, cfg=1, idx=si).view(np.int16)).to(dev))
-        wss.append(torch.zeros(nl.nested_linear_workspace_bytes(handles[-1][0], max(TS)), dtype=torch.uint8,
-                               device=dev))
-        ys.append(torch.empty((max(TS), o), dtype=torch.float32, device=dev))
+        xs.append(torch.from_numpy(synth.make_x(max(CASE_TS), i, cfg=1, idx=si).view(np.int16)).to(dev))
+        wss.append(torch.zeros(nl.nested_linear_workspace_bytes(handles[-1][0], max(CASE_TS)),
+                               dtype=torch.uint8, device=dev))
+        ys.append(torch.empty((max(CASE_TS), o), dtype=torch.float32, device=dev))
         log(f"[bench] {name} {o}x{i}: {ncopy} copies created ({time.time() - t0:.1f}s)")
     torch.cuda.synchronize()
-
-    def bpw(verify):
-        return synth.bytes_per_weight(BITS if verify else 0)
 
     def call(si, copy, T, verify, stream):
         fn = nl.nested_linear_verify if verify else nl.nested_linear_draft
         fn(handles[si][copy], xs[si], T, ys[si], wss[si], stream)
 
-    # ---- the step: 40 calls, weights rotating through the pool
-    seq, c = [], 0
-    for T in TS:
-        for verify in (True, False):
-            for si in range(len(SHAPES)):
-                seq.append((si, c % ncopy, T, verify))
-                c += 1
-    step_bytes = sum(SHAPES[si][1] * SHAPES[si][2] * bpw(v) for si, _, _, v in seq)
-
-    def capture(calls):
+    def capture(calls, call_fn=call):
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
             for cl in calls:
-                call(*cl, stream=s)
+                call_fn(*cl, stream=s)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         with torch.cuda.graph(g):
             cs = torch.cuda.current_stream()
             for cl in calls:
-                call(*cl, stream=cs)
+                call_fn(*cl, stream=cs)
         return g
 
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+
+    def time_graph(g, reps):
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps  # us per replay
+
+    # ---- the step: 40 calls, weights rotating through the pool
+    seq, c = [], 0
+    for T in STEP_TS:
+        for verify in (True, False):
+            for si in range(len(SHAPES)):
+                seq.append((si, c % ncopy, T, verify))
+                c += 1
+    step_bytes = sum(SHAPES[si][1] * SHAPES[si][2] * bpw(v) for si, _, _, v in seq)
     g = capture(seq)
-    # replay check: a replay reproduces the eager outputs bit for bit
-    eager = [y.clone() for y in ys]
+    # a replay reproduces the eager outputs bit for bit (rows the step writes)
+    rows = max(STEP_TS)
+    eager = [y[:rows].clone() for y in ys]
     for y in ys:
         y.zero_()
     g.replay()
     torch.cuda.synchronize()
     for a, b in zip(eager, ys):
-        assert torch.equal(a, b), "graph replay differs from eager run"
-
+        assert torch.equal(a, b[:rows]), "graph replay differs from eager run"
     for _ in range(args.warmup):
         g.replay()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
-    for k in range(args.steps):
+    for _ in range(args.steps):
         g.replay()
     e1.record()
     e1.synchronize()
@@ -132,60 +181,99 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     log(f"[bench] step: {ms_per_step:.3f} ms, {value:.1f} GB/s ({args.steps} steps)")
 
-    # ---- per case: graphs of `ncopy` calls of one (shape, mode, T), amortised launches
+    # ---- per case: graphs of ncopy calls of one (shape, mode, T)
     per_case = {}
-    for T in TS:
+    for T in CASE_TS:
         for verify in (True, False):
-            tot_us, tot_b = 0.0, 0.0
-            shp = {}
+            tot_us, tot_b, shp = 0.0, 0.0, {}
             for si, (name, o, i) in enumerate(SHAPES):
                 gc = capture([(si, cp, T, verify) for cp in range(ncopy)])
-                gc.replay()
-                torch.cuda.synchronize()
-                e0.record()
-                for _ in range(args.reps):
-                    gc.replay()
-                e1.record()
-                e1.synchronize()
-                us = e0.elapsed_time(e1) * 1e3 / (args.reps * ncopy)
+                us = time_graph(gc, args.reps) / ncopy
+                del gc
                 b = o * i * bpw(verify)
                 shp[name] = {"us": round(us, 2), "GBps": round(b / us / 1e3, 1)}
                 tot_us += us
                 tot_b += b
-                del gc
             key = f"{'verify' if verify else 'draft'}_T{T}"
             per_case[key] = {"us_per_pass": round(tot_us, 2), "GBps": round(tot_b / tot_us / 1e3, 1),
                              "frac_hbm_peak": round(tot_b / tot_us / 1e3 / HBM_PEAK_GBPS, 3), "shapes": shp}
-            log(f"[bench] {key}: {tot_us:.1f} us per pass over the 4 projections, "
-                f"{tot_b / tot_us / 1e3:.0f} GB/s")
+            log(f"[bench] {key}: {tot_us:.1f} us per pass over the 4 projections, {tot_b / tot_us / 1e3:.0f} GB/s")
 
-    # ---- roofline of the dominant kernel: the verify contraction (T <= 16),
-    # per-launch HIP events on the launch stream, eager launches
+    # ---- launch-inclusive single calls (eager, one call between events), verify
     stream = torch.cuda.current_stream()
+    single = {}
+    for T in (1, 16):
+        tot = 0.0
+        for si in range(len(SHAPES)):
+            durs = []
+            for r in range(20):
+                torch.cuda.synchronize()
+                e0.record(stream)
+                call(si, r % ncopy, T, True, stream)
+                e1.record(stream)
+                e1.synchronize()
+                durs.append(e0.elapsed_time(e1) * 1e3)
+            durs.sort()
+            tot += durs[len(durs) // 2]
+        single[f"verify_T{T}_us_per_pass_median"] = round(tot, 2)
+
+    # ---- the two-sided form (y = S_o H_o y~) at T = 1 and 16, verify
+    two_handles, two_ws = [], []
+    for si, (name, o, i) in enumerate(SHAPES):
+        lin2 = synth.make_linear(o, i, BITS, cfg=1, idx=si, two_sided=True)
+        d = to_dev(lin2)
+        two_handles.append([nl.nested_linear_create(o, i, BITS, levels=lin2["levels"], **d)
+                            for _ in range(ncopy)])
+        two_ws.append(torch.zeros(nl.nested_linear_workspace_bytes(two_handles[-1][0], 16),
+                                  dtype=torch.uint8, device=dev))
+        del d
+
+    def call2(si, copy, T, verify, stream):
+        fn = nl.nested_linear_verify if verify else nl.nested_linear_draft
+        fn(two_handles[si][copy], xs[si], T, ys[si], two_ws[si], stream)
+
+    two_sided = {}
+    for T in (1, 16):
+        tot_us, tot_b = 0.0, 0.0
+        for si, (name, o, i) in enumerate(SHAPES):
+            gc = capture([(si, cp, T, True) for cp in range(ncopy)], call2)
+            tot_us += time_graph(gc, args.reps) / ncopy
+            tot_b += o * i * bpw(True)
+            del gc
+        two_sided[f"verify_T{T}"] = {"us_per_pass": round(tot_us, 2), "GBps": round(tot_b / tot_us / 1e3, 1)}
+    for hs in two_handles:
+        for h in hs:
+            nl.nested_linear_destroy(h)
+    del two_handles, two_ws
+
+    # ---- roofline of the dominant kernel: per-launch HIP events on the
+    # launch stream around eager verify launches of forward_kernel<6, 1>
     evs, launches = [], []
     for si, (name, o, i) in enumerate(SHAPES):
-        for T in (1, 4, 8, 16):
-            nl.nested_linear_prepare_input(handles[si][0], xs[si], T, wss[si], stream)
+        for T in ROOFLINE_TS:
             for r in range(2):
                 for cp in range(ncopy):
                     a = torch.cuda.Event(enable_timing=True)
                     b = torch.cuda.Event(enable_timing=True)
                     a.record(stream)
-                    nl.nested_linear_contract(handles[si][cp], True, T, ys[si], wss[si], stream)
+                    call(si, cp, T, True, stream)
                     b.record(stream)
                     evs.append((a, b))
                     launches.append(o * i * bpw(True))
     torch.cuda.synchronize()
-    durs = [a.elapsed_time(b) * 1e3 for a, b in evs]  # us
+    durs = [a.elapsed_time(b) * 1e3 for a, b in evs]
     avg_us = sum(durs) / len(durs)
     avg_bytes = sum(launches) / len(launches)
     achieved = avg_bytes / avg_us / 1e3
+    digest = kernel_source_digest()
+    traffic = stored_traffic(digest)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                "kernel": "gemm_kernel<6,1> (verify contraction, T<=16)",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": None if traffic is None else round(traffic),
+                "kernel": ROOFLINE_KERNEL + " (verify, T = 8 and 16, the four projections)",
                 "avg_launch_us": round(avg_us, 2), "avg_algorithmic_bytes": int(avg_bytes),
-                "launches": len(durs)}
-    log(f"[bench] roofline gemm_kernel<6,1>: {avg_us:.2f} us/launch, {achieved:.0f} GB/s")
+                "launches": len(durs), "kernel_source_digest": digest}
+    log(f"[bench] roofline {ROOFLINE_KERNEL}: {avg_us:.2f} us/launch, {achieved:.0f} GB/s")
 
     # ---- streaming reference on the same GPU (torch reduction over 2 GiB)
     big = torch.ones(2 ** 29, dtype=torch.float32, device=dev)
@@ -199,32 +287,40 @@ def main():
     stream_gbps = 5 * big.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del big
 
-    # ---- CPU baseline: the fp64 oracle on the same step's calls, host cores
+    # ---- CPU baseline: the fp64 oracle on the step's calls, host cores
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        xh = [synth.make_x(max(TS), i, cfg=1, idx=si) for si, (_, o, i) in enumerate(SHAPES)]
-        log(f"[bench] cpu baseline: oracle on one step (40 calls), {oracle.num_threads()} threads")
+        xh = [synth.make_x(max(STEP_TS), i, cfg=1, idx=si) for si, (_, o, i) in enumerate(SHAPES)]
+        log(f"[bench] cpu baseline: oracle over the step's 40 calls, {oracle.num_threads()} threads")
         t0 = time.time()
-        for si, _, T, verify in seq:
-            oracle.forward(lins[si], xh[si][:T], verify)
+        nsteps = 0
+        while True:
+            for si, _, T, verify in seq:
+                oracle.forward(lins[si], xh[si][:T], verify)
+            nsteps += 1
+            if time.time() - t0 >= args.cpu_seconds:
+                break
         dt = time.time() - t0
-        cpu = {"value": round(step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-               "kind": "oracle", "sample": f"one full step (40 calls, {step_bytes / 1e9:.2f} GB of weights) "
-                                           f"in {dt:.1f} s"}
+        cpu = {"value": round(nsteps * step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+               "kind": "oracle",
+               "sample": f"{nsteps} full step(s) of the same workload (40 calls, {step_bytes / 1e9:.3f} GB of "
+                         f"weights each) in {dt:.1f} s"}
         log(f"[bench] cpu baseline: {dt:.1f} s, {cpu['value']} GB/s")
 
     out = {
-        "metric": "effective weight GB/s of draft+verify passes (us per pass vs T in per_case)",
+        "metric": "µs/verify pass + effective weight GB/s (frac of HBM peak) vs tree size T=1..64",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp16-mfma/fp32", "data": "synthetic",
         "config": {"workload": "7B/8B-class projections 4096x4096, 1024x4096, 14336x4096, 4096x14336; "
                                "2-bit Lloyd-Max base + 6-bit residual, fp16 group-128 scales; bf16 x; "
-                               "draft and verify at T=1,4,8,16,32; two-sided rotation",
+                               "one-sided y = (Q_b + Q_r) H S x; draft and verify at T=1,4,8,16,32",
                    "calls_per_step": len(seq), "weight_bytes_per_step": int(step_bytes),
                    "pool_copies": ncopy, "pool_bytes": int(ncopy * set_bytes)},
         "per_case": per_case,
+        "single_call": single,
+        "two_sided": two_sided,
         "stream_read_GBps_torch_sum": round(stream_gbps, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -309,7 +309,7 @@ static Plan make_plan(int d_out, int n_tiles, int n_chunks, bool sign_out, int b
   p.S = (n_chunks + p.cps - 1) / p.cps;
   p.finish = sign_out || p.S > 1 || n_linears > 1;
   p.mode = sign_out ? kOutTwoSided : (p.S > 1 ? kOutSplit : kOutDirect);
-  p.local = mt == 1 && tokens <= kLocalRows && p.cps <= kLocalChunks;
+  p.local = mt == 1 && tokens <= kLocalTokens && p.cps <= kLocalChunks;
   if (p.local) p.mt = 0;
   p.sb_rows = finish_rows(sign_out, b_out);
   p.n_sb = (d_out + p.sb_rows - 1) / p.sb_rows;

@@ -88,10 +88,12 @@ constexpr uint32_t kSpinLimit = 1u << 22;
 
 enum : int { kOutDirect = 0, kOutSplit = 1, kOutTwoSided = 2 };
 
-// Calls with at most kLocalRows rows per linear and at most kLocalChunks
+// Calls with at most kLocalTokens rows per linear and at most kLocalChunks
 // chunks per split rotate x inside each contraction workgroup (no rotation
-// workgroups, no hand-over); they launch with MT = 0.
-constexpr int kLocalRows = 4;
+// workgroups, no hand-over); they launch with MT = 0.  (Each extra row costs
+// the workgroup one more 4096-point transform pass, so the limit is small.)
+constexpr int kLocalRows = 4;   // rows of the resident x' layout (>= kLocalTokens)
+constexpr int kLocalTokens = 2;
 constexpr int kLocalChunks = 8;
 
 // What a contraction workgroup of the single launch does with its result.
