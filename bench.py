@@ -247,8 +247,12 @@ def main():
     del two_handles, two_ws
 
     # ---- roofline of the dominant kernel: per-launch HIP events on the
-    # launch stream around eager verify launches of forward_kernel<6, 1>
+    # launch stream around eager verify launches of forward_kernel<6, 1>.
+    # The stream is held by a short spin kernel while the launches are
+    # queued, so each event pair brackets GPU time, not host enqueue time.
     evs, launches = [], []
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(5e7))
     for si, (name, o, i) in enumerate(SHAPES):
         for T in ROOFLINE_TS:
             for r in range(2):

@@ -581,6 +581,7 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
     wait_vm<0>();
   } else {
     // ---- tile wave: this wave's tile codes, two chunks in flight in registers
+    const int c_last = c_end - 1;
     const NL_GLOBAL u32x4 *bptr = (const NL_GLOBAL u32x4 *)L.base + (size_t)tile * a.n_chunks * 128 + lane;
     const NL_GLOBAL u32x4 *rptr =
         (const NL_GLOBAL u32x4 *)L.resid + (size_t)tile * a.n_chunks * (64 * (BITS > 0 ? BITS : 1)) + lane;
@@ -589,21 +590,29 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
     // one fixed issue order everywhere (the fences keep the scheduler from
     // interleaving), so the waits the compiler counts agree on every path
     auto fence = []() { asm volatile("" ::: "memory"); };
+    // Requests for a chunk past the split's last one (c > c_last) read a
+    // small L2-resident dummy area instead: every trip still issues the same
+    // loads, and no HBM traffic is spent on them.
+    const NL_GLOBAL u32x4 *dmy = (const NL_GLOBAL u32x4 *)a.dummy + lane;
+    const NL_GLOBAL uint64_t *dmy_s = (const NL_GLOBAL uint64_t *)a.dummy + tl;
     auto loadw = [&](WRegs<BITS> &w, int c) {
+      const bool real = c <= c_last;
+      const NL_GLOBAL u32x4 *bp = real ? bptr + (size_t)c * 128 : dmy;
 #pragma unroll
       for (int i = 0; i < kBasePieces; ++i) {
-        w.b[i] = __builtin_nontemporal_load(bptr + (size_t)c * 128 + i * 64);
+        w.b[i] = __builtin_nontemporal_load(bp + i * 64);
         fence();
       }
-      w.sb = sbp[(size_t)c * 16];
+      w.sb = real ? sbp[(size_t)c * 16] : dmy_s[0];
       fence();
       if constexpr (BITS > 0) {
+        const NL_GLOBAL u32x4 *rp = real ? rptr + (size_t)c * (64 * BITS) : dmy;
 #pragma unroll
         for (int i = 0; i < BITS; ++i) {
-          w.r[i] = __builtin_nontemporal_load(rptr + (size_t)c * (64 * BITS) + i * 64);
+          w.r[i] = __builtin_nontemporal_load(rp + i * 64);
           fence();
         }
-        w.sr = srp[(size_t)c * 16];
+        w.sr = real ? srp[(size_t)c * 16] : dmy_s[0];
         fence();
       }
     };
@@ -681,7 +690,6 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
     // waits on the weight registers stay counted; requests past the last
     // chunk re-request the last one (uniform loads), and an odd count ends
     // with one more compute.
-    const int c_last = c_end - 1;
     WRegs<BITS> w0, w1;
     if constexpr (LOCAL) {
       // ---- x' of this K-range, rotated here (the rotation role's arithmetic):
@@ -767,7 +775,7 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
       if (!loader) {
         fence();
         loadw(w0, c_begin);
-        loadw(w1, min(c_begin + 1, c_last));
+        loadw(w1, c_begin + 1);
       }
       rproc();
 #pragma unroll 1
@@ -779,7 +787,7 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
     } else {
       fence();
       loadw(w0, c_begin);
-      loadw(w1, min(c_begin + 1, c_last));
+      loadw(w1, c_begin + 1);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // lookup table written
       __builtin_amdgcn_s_barrier();                         // stage 0 of x' ready
       asm volatile("" ::: "memory");
@@ -790,10 +798,10 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
       for (; ci + 1 < nchk; ci += 2) {
         compute(w0, ci);
         fence();
-        loadw(w0, min(c_begin + ci + 2, c_last));
+        loadw(w0, c_begin + ci + 2);
         compute(w1, ci + 1);
         fence();
-        loadw(w1, min(c_begin + ci + 3, c_last));
+        loadw(w1, c_begin + ci + 3);
       }
       if (ci < nchk) compute(w0, ci);
     }
