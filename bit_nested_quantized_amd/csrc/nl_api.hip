@@ -410,7 +410,6 @@ extern "C" nl_status nested_linear_contract(nl_handle h, int32_t verify, int32_t
   g.ldo = h->d_out;
   g.n_rb = p.n_rb;
   g.n_experts = 1;
-  g.dummy = w + kDummyOffset;
   HIP_OR_FAIL(launch_gemm(g, verify ? h->bits : 0, mt_for(T), p.S, (hipStream_t)stream));
   return ok();
 }
@@ -488,7 +487,6 @@ static nl_status forward(nl_handle h, int verify, const void *x, int32_t T, floa
   g.ldo = h->d_out;
   g.n_rb = p.n_rb;
   g.n_experts = 1;
-  g.dummy = w + kDummyOffset;
   f.fin.sign_out = h->dev.sign_out;
   f.fin.b = h->b_out;
   f.fin.lb = log2i(h->b_out);
@@ -649,7 +647,6 @@ static nl_status grouped(nl_group_handle g, int verify, const int32_t *pair_toke
   ga.ldo = g->d_out;
   ga.n_rb = p.n_rb;
   ga.n_experts = g->n;
-  ga.dummy = w + kDummyOffset;
 
   FinishArgs &fa = f.fin;
   fa.lins = g->has_sign_out ? g->dev_array : nullptr;

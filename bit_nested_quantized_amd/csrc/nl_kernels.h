@@ -54,7 +54,6 @@ struct GemmArgs {
   size_t split_stride;
   int T;                    // rows of x' (tokens or pairs)
   int d_out, n_tiles, n_chunks, Kp, Gp, cps, ldo, n_rb, n_experts;
-  const void *dummy;        // >= 16 KiB the weight loads past a split's last chunk read instead
 };
 
 struct FinishArgs {
@@ -77,9 +76,6 @@ struct FinishArgs {
 constexpr int kCtrStride = 16;  // words
 constexpr int kCtrLines = 16384;
 constexpr size_t kCtrBytes = (size_t)kCtrLines * kCtrStride * 4;  // 1 MiB
-// 16 KiB inside the counter region that no counter of an ordinary call
-// reaches (read-only use: the target of padding loads, kept hot in L2).
-constexpr size_t kDummyOffset = 960 * 1024;
 enum : int {
   kCtrErr = 0,       // waits that hit the spin limit (diagnostic; stays zero)
   kCtrRotSub = 1,    // 8 rotation arrival counters

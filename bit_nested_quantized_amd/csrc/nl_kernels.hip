@@ -580,39 +580,43 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
     }
     wait_vm<0>();
   } else {
-    // ---- tile wave: this wave's tile codes, two chunks in flight in registers
-    const int c_last = c_end - 1;
-    const NL_GLOBAL u32x4 *bptr = (const NL_GLOBAL u32x4 *)L.base + (size_t)tile * a.n_chunks * 128 + lane;
-    const NL_GLOBAL u32x4 *rptr =
-        (const NL_GLOBAL u32x4 *)L.resid + (size_t)tile * a.n_chunks * (64 * (BITS > 0 ? BITS : 1)) + lane;
-    const NL_GLOBAL uint64_t *sbp = (const NL_GLOBAL uint64_t *)L.bscale + (size_t)tile * a.n_chunks * 16 + tl;
-    const NL_GLOBAL uint64_t *srp = (const NL_GLOBAL uint64_t *)L.rscale + (size_t)tile * a.n_chunks * 16 + tl;
+    // ---- tile wave: this wave's tile codes, two chunks in flight in registers.
+    // Raw buffer loads through descriptors that end at the split's last
+    // chunk: a request past it (the pipeline's padding) returns zeros without
+    // a memory access, and every trip still issues the same loads.
+    const size_t tc0 = (size_t)tile * a.n_chunks;
+    constexpr int kRaw = 0x00020000;  // raw 32-bit buffer descriptor word 3
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc((void *)sgpr_ptr(L.base + tc0 * 128), 0, c_end * kBaseBlockBytes, kRaw);
+    const __amdgpu_buffer_rsrc_t rsb =
+        __builtin_amdgcn_make_buffer_rsrc((void *)sgpr_ptr(L.bscale + tc0 * 16), 0, c_end * kScaleBlockBytes, kRaw);
+    __amdgpu_buffer_rsrc_t rr = rb, rsr = rsb;
+    if constexpr (BITS > 0) {
+      rr = __builtin_amdgcn_make_buffer_rsrc((void *)sgpr_ptr(L.resid + tc0 * (64 * BITS)), 0,
+                                             c_end * resid_block_bytes(BITS), kRaw);
+      rsr = __builtin_amdgcn_make_buffer_rsrc((void *)sgpr_ptr(L.rscale + tc0 * 16), 0, c_end * kScaleBlockBytes,
+                                              kRaw);
+    }
+    constexpr int kNt = 2;  // non-temporal: the codes are streamed once
     // one fixed issue order everywhere (the fences keep the scheduler from
     // interleaving), so the waits the compiler counts agree on every path
     auto fence = []() { asm volatile("" ::: "memory"); };
-    // Requests for a chunk past the split's last one (c > c_last) read a
-    // small L2-resident dummy area instead: every trip still issues the same
-    // loads, and no HBM traffic is spent on them.
-    const NL_GLOBAL u32x4 *dmy = (const NL_GLOBAL u32x4 *)a.dummy + lane;
-    const NL_GLOBAL uint64_t *dmy_s = (const NL_GLOBAL uint64_t *)a.dummy + tl;
     auto loadw = [&](WRegs<BITS> &w, int c) {
-      const bool real = c <= c_last;
-      const NL_GLOBAL u32x4 *bp = real ? bptr + (size_t)c * 128 : dmy;
 #pragma unroll
       for (int i = 0; i < kBasePieces; ++i) {
-        w.b[i] = __builtin_nontemporal_load(bp + i * 64);
+        w.b[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, (c * 128 + i * 64 + lane) * 16, 0, kNt));
         fence();
       }
-      w.sb = real ? sbp[(size_t)c * 16] : dmy_s[0];
+      w.sb = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rsb, (c * 16 + tl) * 8, 0, 0));
       fence();
       if constexpr (BITS > 0) {
-        const NL_GLOBAL u32x4 *rp = real ? rptr + (size_t)c * (64 * BITS) : dmy;
 #pragma unroll
         for (int i = 0; i < BITS; ++i) {
-          w.r[i] = __builtin_nontemporal_load(rp + i * 64);
+          w.r[i] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, (c * 64 * BITS + i * 64 + lane) * 16, 0, kNt));
           fence();
         }
-        w.sr = real ? srp[(size_t)c * 16] : dmy_s[0];
+        w.sr = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rsr, (c * 16 + tl) * 8, 0, 0));
         fence();
       }
     };
