@@ -466,6 +466,16 @@ struct WRegs {
   uint64_t sb, sr;  // the row's 4 group scales (fp16) of each plane
 };
 
+// Register sets in the weight ring of a tile wave: deeper where the
+// accumulators leave room (one or two token tiles), deepest for the draft,
+// whose sets are a quarter the size.  The in-workgroup rotation (MT = 0)
+// holds its transform registers while the first sets are in flight.
+template <int BITS, int MT>
+__host__ __device__ constexpr int ring_sets() {
+  if constexpr (MT == 0) return BITS == 0 ? 3 : 2;
+  return MT >= 3 ? 2 : (BITS == 0 ? 4 : 3);
+}
+
 // An ordered no-op on every register of a set: work on the set cannot be
 // scheduled above it, so the wait for the set's loads lands here.
 template <int BITS>
@@ -690,11 +700,13 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
         }
       }
     };
-    // Two chunks per trip and no exit in the middle, so the compiler's
-    // waits on the weight registers stay counted; requests past the last
-    // chunk re-request the last one (uniform loads), and an odd count ends
-    // with one more compute.
-    WRegs<BITS> w0, w1;
+    // A ring of NS register sets: while one set is computed the other NS - 1
+    // are in flight.  NS chunks per trip and no exit in the middle, so the
+    // compiler's waits on the weight registers stay counted; requests past
+    // the split's last chunk fall outside the descriptors (zeros, no memory
+    // access), and the last nchk % NS chunks are computed after the loop.
+    constexpr int NS = ring_sets<BITS, MT>();
+    WRegs<BITS> w[NS];
     if constexpr (LOCAL) {
       // ---- x' of this K-range, rotated here (the rotation role's arithmetic):
       // tasks (row t, superblock of SB columns), 4096/SB per pass over the
@@ -778,8 +790,8 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
       rload(0);
       if (!loader) {
         fence();
-        loadw(w0, c_begin);
-        loadw(w1, c_begin + 1);
+#pragma unroll
+        for (int k = 0; k < NS; ++k) loadw(w[k], c_begin + k);
       }
       rproc();
 #pragma unroll 1
@@ -790,8 +802,8 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
       __syncthreads();  // x' resident, lookup table written
     } else {
       fence();
-      loadw(w0, c_begin);
-      loadw(w1, c_begin + 1);
+#pragma unroll
+      for (int k = 0; k < NS; ++k) loadw(w[k], c_begin + k);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // lookup table written
       __builtin_amdgcn_s_barrier();                         // stage 0 of x' ready
       asm volatile("" ::: "memory");
@@ -799,15 +811,17 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
     if (!loader) {
       int ci = 0;
 #pragma unroll 1
-      for (; ci + 1 < nchk; ci += 2) {
-        compute(w0, ci);
-        fence();
-        loadw(w0, c_begin + ci + 2);
-        compute(w1, ci + 1);
-        fence();
-        loadw(w1, c_begin + ci + 3);
+      for (; ci + NS - 1 < nchk; ci += NS) {
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+          compute(w[k], ci + k);
+          fence();
+          loadw(w[k], c_begin + ci + k + NS);
+        }
       }
-      if (ci < nchk) compute(w0, ci);
+#pragma unroll
+      for (int k = 0; k < NS - 1; ++k)
+        if (ci + k < nchk) compute(w[k], ci + k);
     }
   }
 
