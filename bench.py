@@ -36,6 +36,7 @@ BITS = 6
 HBM_PEAK_GBPS = 8000.0
 ROOFLINE_TS = (8, 16)   # verify launches of forward_kernel<6, 1> (one 16-token tile, rotation workgroups)
 ROOFLINE_KERNEL = "forward_kernel<6, 1>"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "forward_kernel_6bit_verify_T8_T16_proj7b8b_traffic.txt")
 
 
 def log(*a):
@@ -54,7 +55,7 @@ def kernel_source_digest():
 def stored_traffic(digest):
     """HBM bytes per launch of the roofline kernel from the committed counter
     summary, when it was taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", "forward_kernel_verify_T8_T16_cfg1_traffic.txt")
+    path = TRAFFIC_FILE
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -63,6 +64,105 @@ def stored_traffic(digest):
     if not m_src or not m_val or m_src.group(1) != digest:
         return None
     return float(m_val.group(1))
+
+
+def roofline_leg(nl, call, ncopy, stream, bpw):
+    """Roofline of the dominant kernel, forward_kernel<6, 1>: eager verify
+    launches at T = 8 and 16 over the four projections, each timed by a HIP
+    event pair attached to its own dispatch (the library's timing hook), so
+    a duration is the kernel's execution as the kernel trace reports it."""
+    import torch
+    n = 0
+    plan = []
+    for si, (name, o, i) in enumerate(SHAPES):
+        for T in ROOFLINE_TS:
+            for r in range(2):
+                for cp in range(ncopy):
+                    plan.append((si, cp, T, o * i * bpw(True)))
+    for si, cp, T, _ in plan[:8]:          # warm the code objects
+        call(si, cp, T, True, stream)
+    torch.cuda.synchronize()
+    nl.nested_linear_timing_begin(len(plan))
+    for si, cp, T, _ in plan:
+        call(si, cp, T, True, stream)
+    durs = nl.nested_linear_timing_end(len(plan))
+    assert len(durs) == len(plan), (len(durs), len(plan))
+    avg_us = sum(durs) / len(durs)
+    avg_bytes = sum(b for *_, b in plan) / len(plan)
+    achieved = avg_bytes / avg_us / 1e3
+    digest = kernel_source_digest()
+    traffic = stored_traffic(digest)
+    log(f"[bench] roofline {ROOFLINE_KERNEL}: {avg_us:.2f} us/launch, {achieved:.0f} GB/s")
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None if traffic is None else round(traffic),
+            "kernel": ROOFLINE_KERNEL + " (verify, T = 8 and 16, the four projections)",
+            "avg_launch_us": round(avg_us, 2), "avg_algorithmic_bytes": int(avg_bytes),
+            "launches": len(durs), "timing": "HIP events attached to each dispatch",
+            "kernel_source_digest": digest}
+
+
+COPY_FLOATS = 64 << 20  # 256 MiB read + 256 MiB written per copy
+
+
+def copy_calibration(torch):
+    """A plain elementwise copy of known size, for scaling the HBM counters."""
+    src = torch.ones(COPY_FLOATS, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    return {"kernel": "torch elementwise mul (copy)", "read_bytes": COPY_FLOATS * 4,
+            "write_bytes": COPY_FLOATS * 4, "launches": 3}
+
+
+def pmc_summary(fetch_dir, write_dir, out_path):
+    """Per-launch HBM traffic of the roofline kernel from two rocprofv3 --pmc
+    runs of `bench.py --roofline-only` (FETCH_SIZE, then WRITE_SIZE), each
+    counter scaled by what it reads for the calibration copy."""
+    import csv
+    import glob
+
+    def rows(d, counter):
+        out = []
+        for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter:
+                    out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+        return out
+
+    def split(rs):
+        fwd = [v for k, v in rs if k.startswith("void nl::forward_kernel<6, 1>")]
+        cpy = [v for k, v in rs if "elementwise" in k and "MulFunctor" in k]
+        return fwd, cpy
+
+    f_fwd, f_cpy = split(rows(fetch_dir, "FETCH_SIZE"))
+    w_fwd, w_cpy = split(rows(write_dir, "WRITE_SIZE"))
+    if not f_fwd or not w_fwd or not f_cpy or not w_cpy:
+        raise SystemExit(f"pmc summary: missing rows ({len(f_fwd)} {len(w_fwd)} {len(f_cpy)} {len(w_cpy)})")
+    known = COPY_FLOATS * 4
+    kf = known / (sorted(f_cpy)[len(f_cpy) // 2] * 1024)
+    kw = known / (sorted(w_cpy)[len(w_cpy) // 2] * 1024)
+    fetch = sum(f_fwd) / len(f_fwd) * 1024 * kf
+    write = sum(w_fwd) / len(w_fwd) * 1024 * kw
+    text = (f"HBM traffic of forward_kernel<6, 1> (verify, T = 8 and 16, 4096x4096, 1024x4096, 14336x4096,\n"
+            f"4096x14336, 2-bit base + 6-bit residual, one-sided)\n"
+            f"commands:\n"
+            f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -o p -- python3 bench.py --roofline-only\n"
+            f"  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -o p -- python3 bench.py --roofline-only\n"
+            f"  python3 bench.py --pmc-summary <fetch_dir> <write_dir>\n"
+            f"launches: {len(f_fwd)} (fetch run), {len(w_fwd)} (write run)\n"
+            f"FETCH_SIZE per launch (raw): {sum(f_fwd) / len(f_fwd):.1f} KiB\n"
+            f"WRITE_SIZE per launch (raw): {sum(w_fwd) / len(w_fwd):.1f} KiB\n"
+            f"calibration copy ({known} bytes read and written): FETCH_SIZE {sorted(f_cpy)[len(f_cpy) // 2]:.1f} KiB, "
+            f"WRITE_SIZE {sorted(w_cpy)[len(w_cpy) // 2]:.1f} KiB -> scale {kf:.3f} (fetch), {kw:.3f} (write)\n"
+            f"hbm read bytes per launch: {fetch:.0f}\n"
+            f"hbm write bytes per launch: {write:.0f}\n"
+            f"hbm bytes per launch: {fetch + write:.0f}\n"
+            f"kernel source digest: {kernel_source_digest()}\n")
+    with open(out_path, "w") as fh:
+        fh.write(text)
+    print(text, end="")
 
 
 def main():
@@ -74,7 +174,14 @@ def main():
     ap.add_argument("--reps", type=int, default=10, help="graph replays per per-case timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--roofline-only", action="store_true",
+                    help="run only the roofline launches and the counter calibration copy (for rocprofv3)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the traffic summary from two rocprofv3 --pmc runs of --roofline-only")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary, TRAFFIC_FILE)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run it with --gpus 1)",
@@ -151,6 +258,13 @@ def main():
         e1.synchronize()
         return e0.elapsed_time(e1) * 1e3 / reps  # us per replay
 
+    stream = torch.cuda.current_stream()
+    if args.roofline_only:
+        roofline = roofline_leg(nl, call, ncopy, stream, bpw)
+        calib = copy_calibration(torch)
+        print(json.dumps({"roofline": roofline, "copy_calibration": calib}), flush=True)
+        return
+
     # ---- the step: 40 calls, weights rotating through the pool
     seq, c = [], 0
     for T in STEP_TS:
@@ -200,7 +314,6 @@ def main():
             log(f"[bench] {key}: {tot_us:.1f} us per pass over the 4 projections, {tot_b / tot_us / 1e3:.0f} GB/s")
 
     # ---- launch-inclusive single calls (eager, one call between events), verify
-    stream = torch.cuda.current_stream()
     single = {}
     for T in (1, 16):
         tot = 0.0
@@ -246,38 +359,7 @@ def main():
             nl.nested_linear_destroy(h)
     del two_handles, two_ws
 
-    # ---- roofline of the dominant kernel: per-launch HIP events on the
-    # launch stream around eager verify launches of forward_kernel<6, 1>.
-    # The stream is held by a short spin kernel while the launches are
-    # queued, so each event pair brackets GPU time, not host enqueue time.
-    evs, launches = [], []
-    torch.cuda.synchronize()
-    torch.cuda._sleep(int(5e7))
-    for si, (name, o, i) in enumerate(SHAPES):
-        for T in ROOFLINE_TS:
-            for r in range(2):
-                for cp in range(ncopy):
-                    a = torch.cuda.Event(enable_timing=True)
-                    b = torch.cuda.Event(enable_timing=True)
-                    a.record(stream)
-                    call(si, cp, T, True, stream)
-                    b.record(stream)
-                    evs.append((a, b))
-                    launches.append(o * i * bpw(True))
-    torch.cuda.synchronize()
-    durs = [a.elapsed_time(b) * 1e3 for a, b in evs]
-    avg_us = sum(durs) / len(durs)
-    avg_bytes = sum(launches) / len(launches)
-    achieved = avg_bytes / avg_us / 1e3
-    digest = kernel_source_digest()
-    traffic = stored_traffic(digest)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": None if traffic is None else round(traffic),
-                "kernel": ROOFLINE_KERNEL + " (verify, T = 8 and 16, the four projections)",
-                "avg_launch_us": round(avg_us, 2), "avg_algorithmic_bytes": int(avg_bytes),
-                "launches": len(durs), "kernel_source_digest": digest}
-    log(f"[bench] roofline {ROOFLINE_KERNEL}: {avg_us:.2f} us/launch, {achieved:.0f} GB/s")
+    roofline = roofline_leg(nl, call, ncopy, stream, bpw)
 
     # ---- streaming reference on the same GPU (torch reduction over 2 GiB)
     big = torch.ones(2 ** 29, dtype=torch.float32, device=dev)

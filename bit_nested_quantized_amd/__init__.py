@@ -28,7 +28,8 @@ EXPORTS = (
     "nested_linear_contract", "nested_linear_finish", "nested_linear_group_create",
     "nested_linear_group_destroy", "nested_linear_group_workspace_bytes",
     "nested_linear_verify_grouped", "nested_linear_draft_grouped", "nested_linear_decode",
-    "nested_linear_info", "nested_linear_last_error",
+    "nested_linear_info", "nested_linear_timing_begin", "nested_linear_timing_end",
+    "nested_linear_last_error",
 )
 
 
@@ -74,6 +75,8 @@ def lib() -> ctypes.CDLL:
             "nested_linear_draft_grouped": [P, P, P, i32, P, i32, P, P, sz, P],
             "nested_linear_decode": [P, i32, i32, P, P, P],
             "nested_linear_info": [P] + [ctypes.POINTER(i32)] * 5 + [ctypes.POINTER(ctypes.c_float)],
+            "nested_linear_timing_begin": [i32],
+            "nested_linear_timing_end": [ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(i32)],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -179,6 +182,18 @@ def nested_linear_draft_grouped(g, pair_token, offsets, P: int, x, T: int, y, ws
 
 def nested_linear_decode(h, row0: int, nrows: int, base_idx, resid, stream=None):
     _check(lib().nested_linear_decode(h, int(row0), int(nrows), _ptr(base_idx), _ptr(resid), _stream(stream)))
+
+
+def nested_linear_timing_begin(capacity: int):
+    _check(lib().nested_linear_timing_begin(capacity))
+
+
+def nested_linear_timing_end(capacity: int) -> list:
+    """Kernel durations (microseconds) of the launches recorded since begin."""
+    buf = (ctypes.c_float * max(capacity, 1))()
+    n = ctypes.c_int32(0)
+    _check(lib().nested_linear_timing_end(buf, capacity, ctypes.byref(n)))
+    return [float(buf[i]) for i in range(n.value)]
 
 
 def nested_linear_info(h) -> dict:

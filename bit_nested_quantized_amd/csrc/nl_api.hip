@@ -463,6 +463,72 @@ static void fill_launch(FwdArgs &f, const Plan &p, int n_linears, char *ws, floa
   f.fin.OB = p.sb_rows;
 }
 
+// ---------------------------------------------------------------------------
+// Kernel timing: event pairs attached to the single launch of each call.
+// ---------------------------------------------------------------------------
+static struct {
+  std::vector<hipEvent_t> ev;  // 2 per slot
+  int used = 0;
+  bool on = false;
+} g_timing;
+
+static void release_timing() {
+  for (hipEvent_t e : g_timing.ev) (void)hipEventDestroy(e);
+  g_timing.ev.clear();
+  g_timing.used = 0;
+  g_timing.on = false;
+}
+
+// The next free event pair, or nulls when timing is off, full, or the
+// stream is being captured into a graph.
+static void timing_slot(hipStream_t s, hipEvent_t *e0, hipEvent_t *e1) {
+  *e0 = *e1 = nullptr;
+  if (!g_timing.on || 2 * g_timing.used >= (int)g_timing.ev.size()) return;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
+  *e0 = g_timing.ev[2 * g_timing.used];
+  *e1 = g_timing.ev[2 * g_timing.used + 1];
+  ++g_timing.used;
+}
+
+extern "C" nl_status nested_linear_timing_begin(int32_t capacity) {
+  if (capacity < 1 || capacity > (1 << 20)) return fail(NL_EINVAL, "timing_begin: capacity must be in [1, 2^20]");
+  release_timing();
+  g_timing.ev.assign(2 * (size_t)capacity, nullptr);
+  for (hipEvent_t &e : g_timing.ev) {
+    const hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      e = nullptr;
+      release_timing();
+      return fail(NL_EHIP, "timing_begin: %s", hipGetErrorString(r));
+    }
+  }
+  g_timing.on = true;
+  return ok();
+}
+
+extern "C" nl_status nested_linear_timing_end(float *us, int32_t capacity, int32_t *count) {
+  if (!g_timing.on) return fail(NL_EINVAL, "timing_end: timing was not begun");
+  if (!count || (capacity > 0 && !us)) {
+    release_timing();
+    return fail(NL_EINVAL, "timing_end: NULL us or count");
+  }
+  const int n = g_timing.used < capacity ? g_timing.used : capacity;
+  for (int i = 0; i < n; ++i) {
+    float ms = 0.f;
+    hipError_t r = hipEventSynchronize(g_timing.ev[2 * i + 1]);
+    if (r == hipSuccess) r = hipEventElapsedTime(&ms, g_timing.ev[2 * i], g_timing.ev[2 * i + 1]);
+    if (r != hipSuccess) {
+      release_timing();
+      return fail(NL_EHIP, "timing_end: %s", hipGetErrorString(r));
+    }
+    us[i] = ms * 1000.f;
+  }
+  *count = n;
+  release_timing();
+  return ok();
+}
+
 static nl_status forward(nl_handle h, int verify, const void *x, int32_t T, float *y, void *ws,
                          size_t ws_bytes, void *stream, const char *who) {
   Plan p;
@@ -493,7 +559,9 @@ static nl_status forward(nl_handle h, int verify, const void *x, int32_t T, floa
   f.fin.rsqrt_b = (float)(1.0 / std::sqrt((double)h->b_out));
   fill_launch(f, p, 1, w, y, h->d_out);
   const int n_fin = p.mode == kOutTwoSided ? finish_workgroups(T, h->d_out, p.sb_rows) : 0;
-  HIP_OR_FAIL(launch_forward(f, verify ? h->bits : 0, p.mt, n_fin, (hipStream_t)stream));
+  hipEvent_t e0, e1;
+  timing_slot((hipStream_t)stream, &e0, &e1);
+  HIP_OR_FAIL(launch_forward(f, verify ? h->bits : 0, p.mt, n_fin, (hipStream_t)stream, e0, e1));
   return ok();
 }
 
@@ -657,7 +725,9 @@ static nl_status grouped(nl_group_handle g, int verify, const int32_t *pair_toke
   fa.rsqrt_b = (float)(1.0 / std::sqrt((double)g->b_out));
   fill_launch(f, p, g->n, w, y, g->d_out);
   const int n_fin = p.mode == kOutTwoSided ? finish_workgroups(P, g->d_out, p.sb_rows) : 0;
-  HIP_OR_FAIL(launch_forward(f, verify ? g->bits : 0, p.mt, n_fin, (hipStream_t)stream));
+  hipEvent_t e0, e1;
+  timing_slot((hipStream_t)stream, &e0, &e1);
+  HIP_OR_FAIL(launch_forward(f, verify ? g->bits : 0, p.mt, n_fin, (hipStream_t)stream, e0, e1));
   return ok();
 }
 

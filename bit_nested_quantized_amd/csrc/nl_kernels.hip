@@ -12,6 +12,7 @@
 // The method is the verifier forward of the forum post "bit-nested", POC
 // recipe section 4 (rotation: section 1; base: section 2; residual:
 // section 3).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
@@ -1132,28 +1133,38 @@ hipError_t launch_finish(const FinishArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int BITS, int MT>
+static void launch_forward_mt(const FwdArgs &f, dim3 grid, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  if (ev0)
+    hipExtLaunchKernelGGL(forward_kernel<BITS, MT>, grid, dim3(kThreads), 0, s, ev0, ev1, 0, f);
+  else
+    forward_kernel<BITS, MT><<<grid, kThreads, 0, s>>>(f);
+}
+
 template <int BITS>
-static hipError_t launch_forward_bits(const FwdArgs &f, int mt, dim3 grid, hipStream_t s) {
+static hipError_t launch_forward_bits(const FwdArgs &f, int mt, dim3 grid, hipStream_t s, hipEvent_t ev0,
+                                      hipEvent_t ev1) {
   switch (mt) {
-    case 0: forward_kernel<BITS, 0><<<grid, kThreads, 0, s>>>(f); break;
-    case 1: forward_kernel<BITS, 1><<<grid, kThreads, 0, s>>>(f); break;
-    case 2: forward_kernel<BITS, 2><<<grid, kThreads, 0, s>>>(f); break;
-    case 3: forward_kernel<BITS, 3><<<grid, kThreads, 0, s>>>(f); break;
-    case 4: forward_kernel<BITS, 4><<<grid, kThreads, 0, s>>>(f); break;
+    case 0: launch_forward_mt<BITS, 0>(f, grid, s, ev0, ev1); break;
+    case 1: launch_forward_mt<BITS, 1>(f, grid, s, ev0, ev1); break;
+    case 2: launch_forward_mt<BITS, 2>(f, grid, s, ev0, ev1); break;
+    case 3: launch_forward_mt<BITS, 3>(f, grid, s, ev0, ev1); break;
+    case 4: launch_forward_mt<BITS, 4>(f, grid, s, ev0, ev1); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_forward(const FwdArgs &f, int bits, int mt, int n_fin, hipStream_t s) {
+hipError_t launch_forward(const FwdArgs &f, int bits, int mt, int n_fin, hipStream_t s, hipEvent_t ev0,
+                          hipEvent_t ev1) {
   if (f.rot.SB < 512 || f.rot.SB > 4096) return hipErrorInvalidValue;
   if (f.hv.mode == kOutTwoSided && (f.fin.OB < 512 || f.fin.OB > 4096)) return hipErrorInvalidValue;
   const dim3 grid(f.n_rot + f.n_gemm + n_fin);
   switch (bits) {
-    case 0: return launch_forward_bits<0>(f, mt, grid, s);
-    case 6: return launch_forward_bits<6>(f, mt, grid, s);
-    case 7: return launch_forward_bits<7>(f, mt, grid, s);
-    case 8: return launch_forward_bits<8>(f, mt, grid, s);
+    case 0: return launch_forward_bits<0>(f, mt, grid, s, ev0, ev1);
+    case 6: return launch_forward_bits<6>(f, mt, grid, s, ev0, ev1);
+    case 7: return launch_forward_bits<7>(f, mt, grid, s, ev0, ev1);
+    case 8: return launch_forward_bits<8>(f, mt, grid, s, ev0, ev1);
     default: return hipErrorInvalidValue;
   }
 }

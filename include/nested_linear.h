@@ -208,6 +208,24 @@ nl_status nested_linear_decode(nl_handle h, int32_t row0, int32_t nrows, uint8_t
 nl_status nested_linear_info(nl_handle h, int32_t *d_out, int32_t *d_in, int32_t *bits,
                              int32_t *block_in, int32_t *block_out, float *level_rel_err);
 
+/*
+ * Kernel timing, a profiling aid that changes no result.  Between
+ * nested_linear_timing_begin(capacity) and nested_linear_timing_end(), the
+ * single kernel launch of each verify / draft call (single or grouped) is
+ * made with a pair of HIP events attached to the dispatch itself, so the
+ * pair brackets the kernel's execution (not the queue around it), for the
+ * first `capacity` such launches of the process; launches into a stream that
+ * is being captured into a graph are not recorded.  timing_end waits for the
+ * recorded launches, writes their durations in microseconds, in launch
+ * order, to us[0 .. min(recorded, capacity)), stores that number in *count
+ * and releases the events.  begin allocates 2 * capacity HIP events (host
+ * objects, no device memory); a second begin discards the first.  Not
+ * thread-safe.  Errors: NL_EINVAL (capacity outside [1, 2^20], end without
+ * begin, NULL pointers), NL_EHIP (event creation or query failed).
+ */
+nl_status nested_linear_timing_begin(int32_t capacity);
+nl_status nested_linear_timing_end(float *us, int32_t capacity, int32_t *count);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char *nested_linear_last_error(void);
 

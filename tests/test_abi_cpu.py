@@ -78,3 +78,14 @@ def test_binding_raises_nlerror():
     with pytest.raises(nl.NLError) as ei:
         nl.nested_linear_destroy(ctypes.c_void_p(0))
     assert ei.value.status == nl.NL_EINVAL
+
+
+def test_timing_rejects_bad_use():
+    # no HIP call is made on these paths
+    L = nl.lib()
+    n = ctypes.c_int32(7)
+    buf = (ctypes.c_float * 4)()
+    assert L.nested_linear_timing_end(buf, 4, ctypes.byref(n)) == nl.NL_EINVAL  # end without begin
+    assert b"not begun" in L.nested_linear_last_error()
+    assert L.nested_linear_timing_begin(0) == nl.NL_EINVAL
+    assert L.nested_linear_timing_begin(-3) == nl.NL_EINVAL
