@@ -381,6 +381,7 @@ extern "C" nl_status nested_linear_prepare_input(nl_handle h, const void *x, int
   nl_status st = check_call(h, "prepare_input", 0, T, ws, ws_bytes, &p);
   if (st != NL_OK) return st;
   if (!x) return fail(NL_EINVAL, "prepare_input: NULL x");
+  if ((uintptr_t)x & 15) return fail(NL_EINVAL, "prepare_input: x must be 16-byte aligned");
   RotInArgs r = rot_args(h, x, T, (char *)ws, p);
   HIP_OR_FAIL(launch_rotate_in(r, T, (hipStream_t)stream));
   return ok();
@@ -453,7 +454,7 @@ static void fill_launch(FwdArgs &f, const Plan &p, int n_linears, char *ws, floa
   f.n_rot = p.local ? 0 : rotate_workgroups(p.rows, f.rot.Kp, f.rot.SB);
   const int per = p.n_rb * p.S;
   f.n_gemm = n_linears * per;
-  for (int k = 0; k < 8; ++k) f.per_line[k] = k < per ? (per - 1 - k) / 8 + 1 : 0;
+  f.hv.n_rot = f.n_rot;
   f.g.out = p.mode == kOutDirect ? y : (float *)(ws + p.o_part);
   f.g.split_stride = (size_t)p.rows * d_out;
   f.fin.y = y;
@@ -535,6 +536,7 @@ static nl_status forward(nl_handle h, int verify, const void *x, int32_t T, floa
   nl_status st = check_call(h, who, verify, T, ws, ws_bytes, &p);
   if (st != NL_OK) return st;
   if (!x || !y) return fail(NL_EINVAL, "%s: NULL x or y", who);
+  if ((uintptr_t)x & 15) return fail(NL_EINVAL, "%s: x must be 16-byte aligned", who);
   char *w = (char *)ws;
   FwdArgs f;
   memset(&f, 0, sizeof f);
@@ -670,6 +672,7 @@ static nl_status grouped(nl_group_handle g, int verify, const int32_t *pair_toke
   if (!valid(g)) return fail(NL_EINVAL, "%s: invalid handle", who);
   if (verify && !g->bits) return fail(NL_EINVAL, "%s: the experts have no residual", who);
   if (!pair_token || !offsets || !x || !y || !ws) return fail(NL_EINVAL, "%s: NULL pointer", who);
+  if ((uintptr_t)x & 15) return fail(NL_EINVAL, "%s: x must be 16-byte aligned", who);
   if (P < 1 || T < 1) return fail(NL_EINVAL, "%s: P and T must be >= 1", who);
   if (T > NL_MAX_T) return fail(NL_EUNSUPPORTED, "%s: T = %d exceeds %d", who, T, NL_MAX_T);
   if ((uintptr_t)ws & 255) return fail(NL_EINVAL, "%s: workspace must be 256-byte aligned", who);

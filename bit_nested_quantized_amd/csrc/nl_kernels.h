@@ -72,17 +72,18 @@ struct FinishArgs {
 // line, in a region of fixed size at the start of every workspace (so calls
 // of any shape can share a workspace).  Fixed slots, then per linear the
 // row-block arrival counters (split-K) and per output superblock the arrival
-// counters and finish tokens (two-sided form).
+// counters and finish tokens (two-sided form).  Every rotation workgroup adds
+// one to each of the 8 ready lines once its x' is stored; a contraction
+// workgroup polls one line until it reads n_rot; the last contraction
+// workgroup to finish clears the lines and the exit counter.
 constexpr int kCtrStride = 16;  // words
 constexpr int kCtrLines = 16384;
 constexpr size_t kCtrBytes = (size_t)kCtrLines * kCtrStride * 4;  // 1 MiB
 enum : int {
   kCtrErr = 0,       // waits that hit the spin limit (diagnostic; stays zero)
-  kCtrRotSub = 1,    // 8 rotation arrival counters
-  kCtrRotTop = 9,    // arrival counter of the 8 above
-  kCtrReady = 10,    // 8 semaphores: tokens for the contraction workgroups
-  kCtrActive = 18,   // grouped: experts with rows (set and cleared each call)
-  kCtrFixed = 19,
+  kCtrReady = 1,     // 8 ready lines: rotation workgroups done
+  kCtrExit = 9,      // contraction workgroups done
+  kCtrFixed = 10,
 };
 constexpr uint32_t kSpinLimit = 1u << 22;
 
@@ -106,7 +107,8 @@ struct Handover {
   int sb_rows;        // rows per output superblock (two-sided)
   int n_sb;           // output superblocks per linear
   int rb_base, ob_base, obr_base;  // first counter of each kind
-  int line;           // semaphore line of the workgroup (set per workgroup)
+  int line;           // ready line of the workgroup (set per workgroup)
+  int n_rot;          // rotation workgroups of the launch
 };
 
 struct FwdArgs {
@@ -115,7 +117,6 @@ struct FwdArgs {
   FinishArgs fin;
   Handover hv;
   int n_rot, n_gemm;
-  int per_line[8];    // contraction workgroups per semaphore line and linear
 };
 
 int rotate_workgroups(int rows, int Kp, int SB);

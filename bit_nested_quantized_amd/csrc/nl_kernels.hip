@@ -18,6 +18,10 @@
 
 #include "nl_kernels.h"
 
+#define NL_GLOBAL __attribute__((address_space(1)))
+#define NL_LOCAL __attribute__((address_space(3)))
+#define NL_CONST __attribute__((address_space(4)))
+
 namespace nl {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -174,10 +178,11 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
 // the low `lb` bits of the element index i (block 2^lb).  The 16 values of a
 // thread pass through three layouts (the stages commute, so their order is
 // free):
-//   A  i = TPS*j + lt          top 4 bits in registers; coalesced loads
-//   C  i = (lt&15) + 16*j + 256*(lt>>4)   bits 4..7 in registers
 //   B  i = 16*lt + j           low 4 bits in registers; contiguous values
-// with padded (conflict-free) LDS transposes A->C->B in between.
+//                              (16-byte loads of x, 16-byte stores of x')
+//   C  i = (lt&15) + 16*j + 256*(lt>>4)   bits 4..7 in registers
+//   A  i = TPS*j + lt          top 4 bits in registers
+// with padded LDS transposes B->C->A->B in between.
 // ===========================================================================
 __device__ __forceinline__ int lds_pad(int i) { return i + (i >> 4); }
 
@@ -192,25 +197,29 @@ __device__ __forceinline__ void bfly16(float (&v)[16], int bit) {
     }
 }
 
-// v: layout A on entry, layout B on exit.  xch: this task's LDS (SB + SB/16).
-// idle: a thread (uniformly per wave) that only keeps the barrier count.
-__device__ __forceinline__ void fwht_tasks(float (&v)[16], float *xch, int lt, int TPS, int n, int lb,
-                                           bool idle = false) {
+// v: layout B on entry and on exit (thread lt of the task holds points
+// 16*lt + j).  The transform is a butterfly on every index bit below lb;
+// four bits are done in registers at a time, with LDS transposes
+//   B (bits 0-3 in registers) -> C (bits 4-7) -> A (bits n-4..n-1, those
+//   from 8 up) -> B.
+// xch: this task's LDS (SB + SB/16 floats).  idle: a thread (uniformly per
+// wave) that only keeps the barrier count.
+__device__ __forceinline__ void fwht_b(float (&v)[16], float *xch, int lt, int TPS, int n, int lb, bool idle) {
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    if (n - 4 + q < lb) bfly16(v, q);
+    if (q < lb) bfly16(v, q);
+  const int cbase = (lt & 15) + 256 * (lt >> 4);
   __syncthreads();
   if (!idle)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) xch[lds_pad(TPS * j + lt)] = v[j];
+    for (int j = 0; j < 16; ++j) xch[lds_pad(16 * lt + j)] = v[j];
   __syncthreads();
-  const int cbase = (lt & 15) + 256 * (lt >> 4);
   if (!idle)
 #pragma unroll
     for (int j = 0; j < 16; ++j) v[j] = xch[lds_pad(cbase + 16 * j)];
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    if (4 + q < n - 4 && 4 + q < lb) bfly16(v, q);
+    if (4 + q < lb) bfly16(v, q);
   __syncthreads();
   if (!idle)
 #pragma unroll
@@ -218,19 +227,88 @@ __device__ __forceinline__ void fwht_tasks(float (&v)[16], float *xch, int lt, i
   __syncthreads();
   if (!idle)
 #pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = xch[lds_pad(TPS * j + lt)];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int bit = n - 4 + q;
+    if (bit >= 8 && bit < lb) bfly16(v, q);
+  }
+  __syncthreads();
+  if (!idle)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) xch[lds_pad(TPS * j + lt)] = v[j];
+  __syncthreads();
+  if (!idle)
+#pragma unroll
     for (int j = 0; j < 16; ++j) v[j] = xch[lds_pad(16 * lt + j)];
+}
+
+// v: layout A on entry, layout B on exit (the output rotation, whose input
+// loads are coalesced in layout A).
+__device__ __forceinline__ void fwht_tasks(float (&v)[16], float *xch, int lt, int TPS, int n, int lb) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (n - 4 + q < lb) bfly16(v, q);
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 16; ++j) xch[lds_pad(TPS * j + lt)] = v[j];
+  __syncthreads();
+  const int cbase = (lt & 15) + 256 * (lt >> 4);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = xch[lds_pad(cbase + 16 * j)];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (4 + q < n - 4 && 4 + q < lb) bfly16(v, q);
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 16; ++j) xch[lds_pad(cbase + 16 * j)] = v[j];
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = xch[lds_pad(16 * lt + j)];
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     if (q < lb) bfly16(v, q);
 }
 
-// Index of column k of row r in the activation layout the contraction reads:
-// runs of 8 consecutive columns, run = (((chunk*4 + group)*4 + step)*4 + quarter),
-// each run holding all R rows (16 bytes per row).
-__device__ __forceinline__ size_t xa_index(int k, int r, int R) {
-  const int run = (k >> 3 & 3) * 4 + (k >> 5 & 3) + ((k >> 7) << 4);  // (c*4+g)*16 + s*4 + kq
-  return ((size_t)run * R + r) * 8 + (k & 7);
+// 16 consecutive activations (columns k0 .. k0 + 15 of row xrow) and their
+// signs: two 16-byte loads of x, one of the signs.  Rows of x and the sign
+// vector are 16-byte aligned and d_in is a multiple of 128, so a group of 16
+// is wholly inside or wholly past d_in.  Outside (xrow < 0 or k0 >= d_in)
+// the loads read the first 16 columns and the values become zeros.
+struct XRaw {
+  u32x4 a, b, s;
+  bool in;
+};
+__device__ __forceinline__ XRaw load_x16(const uint16_t *x, const int8_t *sign, int xrow, int k0, int d_in) {
+  XRaw r;
+  r.in = xrow >= 0 && k0 < d_in;
+  const size_t off = r.in ? (size_t)xrow * d_in + k0 : 0;
+  // global address space: a generic (flat) load would also count in lgkmcnt,
+  // and waiting for it would wait for every load in flight
+  const NL_GLOBAL u32x4 *xp = (const NL_GLOBAL u32x4 *)(x + off);
+  const NL_GLOBAL u32x4 *sp = (const NL_GLOBAL u32x4 *)(sign + (r.in ? k0 : 0));
+  r.a = xp[0];
+  r.b = xp[1];
+  r.s = sp[0];
+  return r;
 }
+// x * sign in fp32 (exact: bf16 widens exactly, signs are +-1)
+__device__ __forceinline__ void cvt_x16(float (&v)[16], const XRaw &r) {
+  const uint32_t xw[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+  const uint32_t sw[4] = {r.s.x, r.s.y, r.s.z, r.s.w};
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t h = (xw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+    const int sg = (int)(int8_t)((sw[j >> 2] >> (8 * (j & 3))) & 0xFFu);
+    v[j] = r.in ? __uint_as_float(h << 16) * (float)sg : 0.0f;
+  }
+}
+
+// Column offset, inside its 128-column group, of run r (0..15) of the
+// contraction's activation layout: run = step * 4 + quarter holds the 8
+// columns 32 * quarter + 8 * step .. + 8 (the MFMA A operand of lanes with
+// l >> 4 == quarter at step `step`).
+__device__ __forceinline__ int run_col(int r) { return 32 * (r & 3) + 8 * (r >> 2); }
 
 // Largest e with offsets[e] <= row (the expert of a pair).
 __device__ __forceinline__ int expert_of(const int32_t *offsets, int n, int row) {
@@ -258,6 +336,7 @@ __device__ __forceinline__ bool expert_active(const int32_t *offsets, int e, int
 // no L2 write-back or invalidate is needed.  Counters are 64-byte apart; the
 // launch leaves every counter at zero.
 // ===========================================================================
+constexpr int kSc1 = 16;  // cache policy of a buffer op: agent-coherent (sc1), as st_dev
 __device__ __forceinline__ void st_dev(float *p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -276,10 +355,8 @@ __device__ __forceinline__ uint32_t ctr_add(uint32_t *p, uint32_t v) {
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ uint32_t *ctr_at(uint32_t *c, int i) { return c + kCtrStride * i; }
 
-// Wait for a token on semaphore `sem` and take it.  Only a workgroup whose
-// producers have lower indices waits, and workgroups are dispatched in index
-// order, so the producers are running or done; the spin limit (seconds) only
-// bounds the wait if that ever fails, and counts the event in the error word.
+// Wait for a token on semaphore `sem` and take it (the output rotation's
+// hand-over; same dispatch-order argument and spin limit as wait_ready).
 __device__ void take_token(uint32_t *sem, uint32_t *err) {
   for (uint32_t it = 0; ld_dev(sem) == 0u; ++it) {
     if (it == kSpinLimit) {
@@ -291,16 +368,31 @@ __device__ void take_token(uint32_t *sem, uint32_t *err) {
   __hip_atomic_fetch_sub(sem, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Wait until the ready line `line` has counted `n` rotation workgroups.
+// Only a workgroup whose producers have lower indices waits, and workgroups
+// are dispatched in index order, so the producers are running or done; the
+// spin limit (seconds) only bounds the wait if that ever fails, and counts
+// the event in the error word.
+__device__ void wait_ready(const uint32_t *line, uint32_t n, uint32_t *err) {
+  for (uint32_t it = 0; ld_dev(line) < n; ++it) {
+    if (it == kSpinLimit) {
+      ctr_add(err, 1u);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
 // ===========================================================================
 // Input rotation (POC section 1: x' = H_i S_i x, "once per Linear").
 // Task = (row of x', superblock of SB = max(b, 512) columns), so every
 // 512-column chunk lies in one task; a workgroup runs 4096/SB tasks.  Each
 // chunk is scaled by 2^s (its largest magnitude lands in [2^14, 2^15]) and
 // rounded to fp16, the contraction's MFMA operand; tsc = 2^-s / sqrt(b)
-// undoes both factors.  Outputs (R = rows of x'): xh in the layout of
-// xa_index; meta[(c*5+g)*R + r] = sum of the fp16 values of group g (g < 4)
-// and meta[(c*5+4)*R + r] = tsc.  COH: agent-scope stores (read by other
-// workgroups of the same launch).
+// undoes both factors.  Outputs (R = rows of x'): xh row-major [R][Kp];
+// meta[(c*5+g)*R + r] = sum of the fp16 values of group g (g < 4) and
+// meta[(c*5+4)*R + r] = tsc.  COH: agent-scope stores (read by other
+// workgroups of the same launch), 16 bytes per store.
 // ===========================================================================
 // Threads past the first 256 (the fifth wave of the single launch) run the
 // same code on a spare LDS area (`spare`, SB + SB/16 floats) and store nothing.
@@ -323,25 +415,12 @@ __device__ __forceinline__ void rotate_body(const RotInArgs &a, int wg, float *x
       xrow = a.pair_token[row];
       if (xrow < 0 || xrow >= a.x_rows) xrow = -1;
     }
-    sign = a.lins[valid ? expert_of(a.offsets, a.n_experts, row) : 0].sign_in;
+    sign = ((const NL_GLOBAL LinearDev *)a.lins)[valid ? expert_of(a.offsets, a.n_experts, row) : 0].sign_in;
   }
-  // layout A, unconditional loads (clamped index) so all 16 are in flight
-  const uint16_t *xr = a.x + (size_t)(xrow < 0 ? 0 : xrow) * a.d_in;
-  uint16_t xv[16];
-  int8_t sv[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int k = min(kb + TPS * j + lt, a.d_in - 1);
-    xv[j] = xr[k];
-    sv[j] = sign[k];
-  }
+  const int k0 = kb + 16 * lt;
   float v[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int k = kb + TPS * j + lt;
-    v[j] = (k < a.d_in && xrow >= 0) ? bf16_to_float(xv[j]) * (float)sv[j] : 0.0f;
-  }
-  fwht_tasks(v, x, lt, TPS, n, a.lb);
+  cvt_x16(v, load_x16(a.x, sign, xrow, k0, a.d_in));
+  fwht_b(v, x, lt, TPS, n, a.lb, extra);
 
   // layout B: 16 consecutive columns; a chunk is 32 threads, a group 8
   float m = 0.f;
@@ -368,22 +447,20 @@ __device__ __forceinline__ void rotate_body(const RotInArgs &a, int wg, float *x
   for (int o = 1; o < 8; o <<= 1) gs += __shfl_xor(gs, o, 64);
   if (!valid) return;
   const int R = a.rows;
-  const int k0 = kb + 16 * lt;
-  uint32_t *d0 = reinterpret_cast<uint32_t *>(a.xh + xa_index(k0, row, R));
-  uint32_t *d1 = reinterpret_cast<uint32_t *>(a.xh + xa_index(k0 + 8, row, R));
+  const size_t xo = (size_t)row * a.Kp + k0;  // element offset of the thread's 16 columns
   float *mg = a.meta + ((size_t)(k0 >> 9) * 5 + ((k0 >> 7) & 3)) * R + row;
   float *ms = a.meta + ((size_t)(k0 >> 9) * 5 + 4) * R + row;
+  const u32x4 lo = {w[0], w[1], w[2], w[3]}, hi = {w[4], w[5], w[6], w[7]};
   if constexpr (COH) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      st_dev(d0 + i, w[i]);
-      st_dev(d1 + i, w[4 + i]);
-    }
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)a.xh, 0, 0x7FFFFFF0, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(lo, xr, (int)(xo * 2), 0, kSc1);
+    __builtin_amdgcn_raw_buffer_store_b128(hi, xr, (int)(xo * 2 + 16), 0, kSc1);
     if ((lt & 7) == 0) st_dev(mg, gs);
     if ((lt & 31) == 0) st_dev(ms, ldexpf(a.rsqrt_b, -s));
   } else {
-    *reinterpret_cast<uint4 *>(d0) = make_uint4(w[0], w[1], w[2], w[3]);
-    *reinterpret_cast<uint4 *>(d1) = make_uint4(w[4], w[5], w[6], w[7]);
+    *reinterpret_cast<u32x4 *>(a.xh + xo) = lo;
+    *reinterpret_cast<u32x4 *>(a.xh + xo + 8) = hi;
     if ((lt & 7) == 0) *mg = gs;
     if ((lt & 31) == 0) *ms = ldexpf(a.rsqrt_b, -s);
   }
@@ -413,8 +490,6 @@ __global__ __launch_bounds__(256) void rotate_in_kernel(const RotInArgs a) {
 //   acc_chunk = fma(s_r, A_resid - bias * sum(x'), acc_chunk)
 // and at the end of each chunk acc = fma(tsc, acc_chunk, acc).
 // ===========================================================================
-#define NL_GLOBAL __attribute__((address_space(1)))
-#define NL_LOCAL __attribute__((address_space(3)))
 
 constexpr int kTileWaves = 4;
 constexpr int kThreads = 64 * (kTileWaves + 1);
@@ -522,26 +597,37 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
   // (wave index read as a scalar so per-wave choices stay uniform branches)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const bool loader = wave == kTileWaves;
-  const LinearDev *Lp = &a.lin;
+  // The descriptor by value, read with scalar loads (the expert array is
+  // read-only for the launch and e is uniform): a generic pointer that may
+  // point at the kernel arguments would turn every field into a flat load
+  // and a full wait at the start of the workgroup.
   int row_base = 0, nrows = a.T;
   if (a.lins) {
     row_base = a.offsets[e];
     nrows = a.offsets[e + 1] - row_base;
     // idle expert (or offsets outside [0, rows)): uniform exit before any barrier
     if (!expert_active(a.offsets, e, a.T)) return;
-    Lp = a.lins + e;
   }
+  const NL_CONST LinearDev &L = *(const NL_CONST LinearDev *)(a.lins ? a.lins + e : &a.lin);
   nrows = min(min(nrows, TR), a.T - row_base);
-  const LinearDev &L = *Lp;
   const int tile_id = rb * kTileWaves + (loader ? 0 : wave);
   const bool active = !loader && tile_id < a.n_tiles;
   const int tile = min(tile_id, a.n_tiles - 1);
   const int c_begin = split * a.cps;
   const int c_end = min(a.n_chunks, c_begin + a.cps);
   const int nchk = c_end - c_begin;
-  if (threadIdx.x < 256) {  // (LocalPlan::o_lut == LdsPlan::o_lut == 0)
-    uint2 *s_lut = reinterpret_cast<uint2 *>(smem);
-    s_lut[threadIdx.x] = base_table_entry(L.lut, threadIdx.x);
+  {  // byte-indexed base table (LocalPlan::o_lut == LdsPlan::o_lut == 0) from
+     // the descriptor's 16 pair words, staged through LDS by one thread (they
+     // are scalar loads; a per-lane choice among them would become an
+     // indexed memory load and a full wait)
+    __shared__ uint32_t s_l16[16];
+    if (threadIdx.x == 0) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) s_l16[k] = L.lut[k];
+    }
+    __syncthreads();
+    if (threadIdx.x < 256)
+      reinterpret_cast<uint2 *>(smem)[threadIdx.x] = make_uint2(s_l16[threadIdx.x & 15], s_l16[threadIdx.x >> 4]);
   }
   const int tl = lane & 15, kq = lane >> 4;
   const int R = a.T;
@@ -562,10 +648,11 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
       const int c = c_begin + q / NST, g0 = (q % NST) * XG;
       const uint32_t xl = lds0 + Pl::o_x + (q % NX) * Pl::XB, ml = xl + Pl::XI * 1024;
 #pragma unroll
-      for (int j = 0; j < Pl::XI; ++j) {
+      for (int j = 0; j < Pl::XI; ++j) {  // x' is row-major [R][Kp]: gather 16-byte runs into the stage
         const int slot = 64 * j + lane;
         const int run = slot / TR, t = min(slot % TR, nrows - 1);
-        dma16(xl + 1024 * j, (uint32_t)((((c * 4 + g0) * 16 + run) * R + row_base + t) * 16), xsrc);
+        const int col = (c * 4 + g0 + (run >> 4)) * 128 + run_col(run & 15);
+        dma16(xl + 1024 * j, (uint32_t)(((size_t)(row_base + t) * a.Kp + col) * 2), xsrc);
       }
 #pragma unroll
       for (int j = 0; j < Pl::MI; ++j) {
@@ -576,7 +663,7 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
       }
     };
     if constexpr (FUSED && !LOCAL) {
-      if (lane == 0) take_token(ctr_at(hv.ctr, kCtrReady + hv.line), ctr_at(hv.ctr, kCtrErr));
+      if (lane == 0) wait_ready(ctr_at(hv.ctr, kCtrReady + hv.line), (uint32_t)hv.n_rot, ctr_at(hv.ctr, kCtrErr));
     }
     // Stage q lives in buffer q % NX.  Barrier #q publishes stage q and
     // tells the loader the tile waves are done with stage q - 1, whose
@@ -721,12 +808,11 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
       const int kbeg = c_begin * kChunk, kend = c_end * kChunk;
       const int sb0 = kbeg / SB, nsb = (kend - 1) / SB - sb0 + 1;
       const int per_pass = 4096 / SB, ntask = nrows * nsb, npass = (ntask + per_pass - 1) / per_pass;
-      const int8_t *sign = a.lins ? a.lins[e].sign_in : ra.sign;
+      const int8_t *sign = L.sign_in;
       float *xs = reinterpret_cast<float *>(smem + LocalPlan::o_f) + tg * (SB + (SB >> 4));
       char *xres = smem + LocalPlan::o_x;
       float *mres = reinterpret_cast<float *>(smem + LocalPlan::o_m);
-      uint16_t xv[16];
-      int8_t sv[16];
+      XRaw xraw{};
       int t = 0, kb = 0, xrow = -1;
       bool valid = false;
       auto rload = [&](int p) __attribute__((always_inline)) {
@@ -740,22 +826,12 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
           if (xrow < 0 || xrow >= ra.x_rows) xrow = -1;
         }
         if (idle) return;
-        const uint16_t *xr = ra.x + (size_t)(xrow < 0 ? 0 : xrow) * ra.d_in;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int k = min(kb + TPS * j + lt, ra.d_in - 1);
-          xv[j] = xr[k];
-          sv[j] = sign[k];
-        }
+        xraw = load_x16(ra.x, sign, xrow, kb + 16 * lt, ra.d_in);  // converted in rproc
       };
       auto rproc = [&]() __attribute__((always_inline)) {
         float v[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int k = kb + TPS * j + lt;
-          v[j] = (k < ra.d_in && xrow >= 0) ? bf16_to_float(xv[j]) * (float)sv[j] : 0.0f;
-        }
-        fwht_tasks(v, xs, lt, TPS, nlog, ra.lb, idle);
+        cvt_x16(v, xraw);
+        fwht_b(v, xs, lt, TPS, nlog, ra.lb, idle);
         float mx = 0.f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(v[j]));
@@ -789,11 +865,12 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
         if ((lt & 31) == 0) mres[(cl * 5 + 4) * TR + t] = ldexpf(ra.rsqrt_b, -sc);
       };
       rload(0);
-      if (!loader) {
-        fence();
+      fence();
+      // the fifth wave issues the same loads past its descriptors' range
+      // (zeros, no memory access), so every wave counts the same loads and
+      // the wait for x above leaves the weights in flight
 #pragma unroll
-        for (int k = 0; k < NS; ++k) loadw(w[k], c_begin + k);
-      }
+      for (int k = 0; k < NS; ++k) loadw(w[k], (loader ? c_end : c_begin) + k);
       rproc();
 #pragma unroll 1
       for (int p = 1; p < npass; ++p) {
@@ -865,21 +942,37 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
       }
       __syncthreads();
       if (!s_flag) return;
+      // up to 4 outputs per thread and 8 splits per round, every load of a
+      // round issued before its adds (one memory round trip for T <= 16 and
+      // S <= 8); each output still sums its splits in order from zero
       const float *part = a.out;
-      const int rows_here = min(64, a.d_out - rb * 64);
-      for (int idx = threadIdx.x; idx < nrows * 64; idx += kThreads) {
-        const int t = idx >> 6, r = idx & 63;
-        if (r >= rows_here) continue;
-        const size_t o = (size_t)(row_base + t) * a.ldo + rb * 64 + r;
-        float u[4];
-        float v = 0.f;
-        for (int sp0 = 0; sp0 < hv.S; sp0 += 4) {
+      const int rows_here = min(64, a.d_out - rb * 64), total = nrows * 64;
+      for (int base = 0; base < total; base += 4 * kThreads) {
+        size_t o[4];
+        bool ok[4];
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int q = 0; q < 4; ++q) u[q] = ld_dev(part + min(sp0 + q, hv.S - 1) * a.split_stride + o);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) v += (sp0 + q < hv.S) ? u[q] : 0.f;
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int idx = base + e4 * kThreads + threadIdx.x, t = idx >> 6, r = idx & 63;
+          ok[e4] = idx < total && r < rows_here;
+          o[e4] = (size_t)(row_base + (ok[e4] ? t : 0)) * a.ldo + rb * 64 + (ok[e4] ? r : 0);
         }
-        if (hv.mode == kOutTwoSided) st_dev(dst + o, v); else dst[o] = v;
+        for (int sp0 = 0; sp0 < hv.S; sp0 += 8) {
+          float u[4][8];
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) u[e4][q] = ld_dev(part + min(sp0 + q, hv.S - 1) * a.split_stride + o[e4]);
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[e4] += (sp0 + q < hv.S) ? u[e4][q] : 0.f;
+        }
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          if (!ok[e4]) continue;
+          if (hv.mode == kOutTwoSided) st_dev(dst + o[e4], v[e4]); else dst[o[e4]] = v[e4];
+        }
       }
     } else {
       put(dst, a.ldo, hv.mode == kOutTwoSided);
@@ -1002,8 +1095,8 @@ __global__ __launch_bounds__(256) void finish_kernel(const FinishArgs a) {
 
 // ===========================================================================
 // Single-launch forward: workgroups [0, n_rot) rotate x, the next n_gemm
-// contract (each takes a token once x' is complete), the rest (two-sided
-// only) finish.  Every wait is on workgroups of lower index.
+// contract (each once all of x' is stored), the rest (two-sided only)
+// finish.  Every wait is on workgroups of lower index.
 // ===========================================================================
 template <int BITS, int MT>
 __global__ __launch_bounds__(kThreads) void forward_kernel(const FwdArgs f) {
@@ -1011,41 +1104,14 @@ __global__ __launch_bounds__(kThreads) void forward_kernel(const FwdArgs f) {
   constexpr int kPlan = MT == 0 ? LocalPlan::bytes : LdsPlan<BITS, (MT == 0 ? 1 : MT)>::bytes;
   constexpr int kLds = kPlan > 2 * kFwht ? kPlan : 2 * kFwht;
   __shared__ __attribute__((aligned(16))) char smem[kLds];
-  __shared__ uint32_t s_cnt[4];
   float *xch = reinterpret_cast<float *>(smem), *spare = reinterpret_cast<float *>(smem + kFwht);
   int b = blockIdx.x;
   uint32_t *ctr = f.hv.ctr;
   if (b < f.n_rot) {
     rotate_body<true>(f.rot, b, xch, spare);
-    if (f.rot.lins && b == 0) {  // grouped: number of experts that will wait for x'
-      uint32_t cnt = 0;
-      if (threadIdx.x < 256)
-        for (int e = threadIdx.x; e < f.rot.n_experts; e += 256) cnt += expert_active(f.rot.offsets, e, f.rot.rows);
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
-      if ((threadIdx.x & 63) == 0 && threadIdx.x < 256) s_cnt[threadIdx.x >> 6] = cnt;
-      __syncthreads();
-      if (threadIdx.x == 0) st_dev(ctr_at(ctr, kCtrActive), s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3]);
-    }
-    wait_stores();
+    wait_stores();  // x' and its metadata acknowledged in every thread
     __syncthreads();
-    if (threadIdx.x == 0) {
-      // two-level arrival count (8 lines, then one); the last rotation
-      // workgroup resets both and releases one token per waiting workgroup
-      const int sub = b & 7;
-      const uint32_t in_sub = (uint32_t)((f.n_rot - 1 - sub) / 8 + 1);
-      if (ctr_add(ctr_at(ctr, kCtrRotSub + sub), 1u) == in_sub - 1) {
-        st_dev(ctr_at(ctr, kCtrRotSub + sub), 0u);
-        const uint32_t n_subs = (uint32_t)min(f.n_rot, 8);
-        if (ctr_add(ctr_at(ctr, kCtrRotTop), 1u) == n_subs - 1) {
-          st_dev(ctr_at(ctr, kCtrRotTop), 0u);
-          const uint32_t act = f.rot.lins ? ld_dev(ctr_at(ctr, kCtrActive)) : 1u;
-          if (f.rot.lins) st_dev(ctr_at(ctr, kCtrActive), 0u);
-          for (int k = 0; k < 8; ++k)
-            if (f.per_line[k] && act) ctr_add(ctr_at(ctr, kCtrReady + k), act * (uint32_t)f.per_line[k]);
-        }
-      }
-    }
+    if (threadIdx.x < 8) ctr_add(ctr_at(ctr, kCtrReady + threadIdx.x), 1u);
     return;
   }
   b -= f.n_rot;
@@ -1056,6 +1122,16 @@ __global__ __launch_bounds__(kThreads) void forward_kernel(const FwdArgs f) {
     Handover hv = f.hv;
     hv.line = j & 7;
     contract_body<BITS, MT, true>(f.g, e, rb, split, smem, hv, f.rot);
+    // Thread 0 passed a barrier after its loader's wait (or the workgroup
+    // had nothing to do), so the last contraction workgroup to get here is
+    // after every wait on the ready lines.  It clears them once they hold
+    // their final count (they already do unless no workgroup waited).
+    if (f.n_rot > 0 && threadIdx.x == 0 &&
+        ctr_add(ctr_at(ctr, kCtrExit), 1u) == (uint32_t)(f.n_gemm - 1)) {
+      for (int k = 0; k < 8; ++k) wait_ready(ctr_at(ctr, kCtrReady + k), (uint32_t)f.n_rot, ctr_at(ctr, kCtrErr));
+      for (int k = 0; k < 8; ++k) st_dev(ctr_at(ctr, kCtrReady + k), 0u);
+      st_dev(ctr_at(ctr, kCtrExit), 0u);
+    }
     return;
   }
   finish_body<true>(f.fin, b - f.n_gemm, xch, spare, f.hv);

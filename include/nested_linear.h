@@ -110,15 +110,16 @@ nl_status nested_linear_workspace_bytes(nl_handle h, int32_t T_max, size_t *byte
 /*
  * Verify forward (POC section 4): y = S_o H_o ((Q_base + Q_resid) H_i S_i x)
  * for T tokens, or the rotated-basis y~ when the linear has no sign_out.
- *   x   [T][d_in] bf16 bit patterns (row-major); y [T][d_out] fp32 output,
- *       must not overlap x or ws.
+ *   x   [T][d_in] bf16 bit patterns (row-major), 16-byte aligned (rows are
+ *       read 16 bytes at a time); y [T][d_out] fp32 output, must not
+ *       overlap x or ws.
  *   ws  workspace of ws_bytes >= nested_linear_workspace_bytes(h, T).
  * Weight bytes are streamed from HBM once per call for all T tokens.  One
  * kernel launch: its first workgroups rotate x, the next contract (each
  * waits for the rotation through the workspace counters, after requesting
  * its first weights), the last (two-sided form only) apply S_o H_o.
- * Errors: NL_EINVAL (NULL pointer, T < 1, small or misaligned ws, linear
- * without a residual), NL_EUNSUPPORTED (T > 64, or d_out beyond what the
+ * Errors: NL_EINVAL (NULL pointer, T < 1, x not 16-byte aligned, small or
+ * misaligned ws, linear without a residual), NL_EUNSUPPORTED (T > 64, or d_out beyond what the
  * counter region serves: about 16000 row blocks of 64), NL_EHIP (launch
  * failure).
  */

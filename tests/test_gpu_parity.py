@@ -116,12 +116,8 @@ def test_prepare_input_matches_oracle_rotation(nl, torch_cuda):
     torch.cuda.synchronize()
     nch = d_in // 512
     o_xh = COUNTER_BYTES
-    raw = ws[o_xh: o_xh + T * d_in * 2].view(torch.float16).float().cpu().numpy()
-    # activation layout: runs of 8 columns, run = ((c*4+g)*4+s)*4+q, all T rows per run
-    k = np.arange(d_in)
-    run = ((k >> 3) & 3) * 4 + ((k >> 5) & 3) + ((k >> 7) << 4)
-    idx = (run[None, :] * T + np.arange(T)[:, None]) * 8 + (k & 7)[None, :]
-    xh = raw[idx]
+    # x' is row-major fp16 [T][Kp], Kp = chunks * 512 (= d_in here)
+    xh = ws[o_xh: o_xh + T * d_in * 2].view(torch.float16).float().cpu().numpy().reshape(T, d_in)
     o_meta = o_xh + (T * d_in * 2 + 255) // 256 * 256
     meta = ws[o_meta: o_meta + T * nch * 20].view(torch.float32).reshape(nch, 5, T).cpu().numpy()
     xs, tsc = meta[:, :4, :], meta[:, 4, :]
@@ -424,3 +420,21 @@ def test_grouped_few_tokens(nl, torch_cuda, T, two):
         a, b, _ = run_grouped(nl, torch_cuda, experts, pt, off, x, verify)
         assert rel_err(a, oracle.forward_grouped(experts, pt, off, x, verify)) <= TOL
         np.testing.assert_array_equal(a, b)
+
+
+def test_misaligned_x_is_rejected(nl, torch_cuda):
+    torch = torch_cuda
+    lin = synth.make_linear(256, 256, 6, cfg=0, idx=5)
+    L = nl.Linear(lin)
+    x = torch.zeros(4 * 256 + 8, dtype=torch.int16, device="cuda")
+    ws = L.workspace(4)
+    y = torch.empty((4, 256), dtype=torch.float32, device="cuda")
+    lib = nl.lib()
+    import ctypes
+    base = x.data_ptr()
+    st = lib.nested_linear_verify(L.h, ctypes.c_void_p(base + 2), 4, ctypes.c_void_p(y.data_ptr()),
+                                  ctypes.c_void_p(ws.data_ptr()), ws.numel(), None)
+    assert st == nl.NL_EINVAL and b"16-byte" in lib.nested_linear_last_error()
+    assert lib.nested_linear_verify(L.h, ctypes.c_void_p(base + 16), 4, ctypes.c_void_p(y.data_ptr()),
+                                    ctypes.c_void_p(ws.data_ptr()), ws.numel(), None) == nl.NL_OK
+    torch.cuda.synchronize()
