@@ -198,49 +198,69 @@ __device__ __forceinline__ void bfly16(float (&v)[16], int bit) {
 }
 
 // v: layout B on entry and on exit (thread lt of the task holds points
-// 16*lt + j).  The transform is a butterfly on every index bit below lb;
+// 16*lt + j).  The transform is a butterfly on every index bit below LB;
 // four bits are done in registers at a time, with LDS transposes
-//   B (bits 0-3 in registers) -> C (bits 4-7) -> A (bits n-4..n-1, those
+//   B (bits 0-3 in registers) -> C (bits 4-7) -> A (bits N-4..N-1, those
 //   from 8 up) -> B.
+// N = log2 of the task size SB, LB = log2 of the Hadamard block (LB <= N);
+// both compile-time, so every LDS address is a base plus an immediate.
 // xch: this task's LDS (SB + SB/16 floats).  idle: a thread (uniformly per
 // wave) that only keeps the barrier count.
-__device__ __forceinline__ void fwht_b(float (&v)[16], float *xch, int lt, int TPS, int n, int lb, bool idle) {
+template <int N, int LB>
+__device__ __forceinline__ void fwht_bt(float (&v)[16], float *xch, int lt, bool idle) {
+  constexpr int TPS = 1 << (N - 4);
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    if (q < lb) bfly16(v, q);
+    if (q < LB) bfly16(v, q);
   const int cbase = (lt & 15) + 256 * (lt >> 4);
+  float *pb = xch + lds_pad(16 * lt);             // B: + j
+  float *pc = xch + lds_pad(cbase);               // C: + 17 j
+  float *pa = xch + lt + (lt >> 4);               // A: + (TPS + TPS / 16) j
   __syncthreads();
   if (!idle)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) xch[lds_pad(16 * lt + j)] = v[j];
+    for (int j = 0; j < 16; ++j) pb[j] = v[j];
   __syncthreads();
   if (!idle)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = xch[lds_pad(cbase + 16 * j)];
+    for (int j = 0; j < 16; ++j) v[j] = pc[17 * j];
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    if (4 + q < lb) bfly16(v, q);
+    if (4 + q < LB) bfly16(v, q);
   __syncthreads();
   if (!idle)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) xch[lds_pad(cbase + 16 * j)] = v[j];
+    for (int j = 0; j < 16; ++j) pc[17 * j] = v[j];
   __syncthreads();
   if (!idle)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = xch[lds_pad(TPS * j + lt)];
+    for (int j = 0; j < 16; ++j) v[j] = pa[(TPS + TPS / 16) * j];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int bit = n - 4 + q;
-    if (bit >= 8 && bit < lb) bfly16(v, q);
+    constexpr int base = N - 4;
+    if (base + q >= 8 && base + q < LB) bfly16(v, q);
   }
   __syncthreads();
   if (!idle)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) xch[lds_pad(TPS * j + lt)] = v[j];
+    for (int j = 0; j < 16; ++j) pa[(TPS + TPS / 16) * j] = v[j];
   __syncthreads();
   if (!idle)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = xch[lds_pad(16 * lt + j)];
+    for (int j = 0; j < 16; ++j) v[j] = pb[j];
+}
+
+// The transform for a task of SB = max(2^lb, 512) points (one uniform
+// dispatch on the block size; lb is 7..12 since d_in is a multiple of 128).
+__device__ __forceinline__ void fwht_b(float (&v)[16], float *xch, int lt, int lb, bool idle) {
+  switch (lb) {
+    case 7: fwht_bt<9, 7>(v, xch, lt, idle); break;
+    case 8: fwht_bt<9, 8>(v, xch, lt, idle); break;
+    case 9: fwht_bt<9, 9>(v, xch, lt, idle); break;
+    case 10: fwht_bt<10, 10>(v, xch, lt, idle); break;
+    case 11: fwht_bt<11, 11>(v, xch, lt, idle); break;
+    default: fwht_bt<12, 12>(v, xch, lt, idle); break;
+  }
 }
 
 // v: layout A on entry, layout B on exit (the output rotation, whose input
@@ -398,7 +418,7 @@ __device__ void wait_ready(const uint32_t *line, uint32_t n, uint32_t *err) {
 // same code on a spare LDS area (`spare`, SB + SB/16 floats) and store nothing.
 template <bool COH>
 __device__ __forceinline__ void rotate_body(const RotInArgs &a, int wg, float *xch, float *spare) {
-  const int SB = a.SB, TPS = SB >> 4, n = 31 - __builtin_clz(SB);
+  const int SB = a.SB, TPS = SB >> 4;
   const bool extra = threadIdx.x >= 256;
   const int tid = extra ? 0 : threadIdx.x, lt = tid % TPS, tl = tid / TPS;
   const int n_sb = a.Kp / SB;
@@ -420,7 +440,7 @@ __device__ __forceinline__ void rotate_body(const RotInArgs &a, int wg, float *x
   const int k0 = kb + 16 * lt;
   float v[16];
   cvt_x16(v, load_x16(a.x, sign, xrow, k0, a.d_in));
-  fwht_b(v, x, lt, TPS, n, a.lb, extra);
+  fwht_b(v, x, lt, a.lb, extra);
 
   // layout B: 16 consecutive columns; a chunk is 32 threads, a group 8
   float m = 0.f;
@@ -718,11 +738,33 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
         fence();
       }
     };
+    // the same loads in four parts: part g is issued after group g of the
+    // compute in progress (refilling the set computed just before it), so
+    // the memory pipeline takes them between groups rather than in bursts
+    auto loadpart = [&](WRegs<BITS> &w, int c, int g) {
+      if (g == 0) {
+#pragma unroll
+        for (int i = 0; i < kBasePieces; ++i)
+          w.b[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, (c * 128 + i * 64 + lane) * 16, 0, kNt));
+        w.sb = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rsb, (c * 16 + tl) * 8, 0, 0));
+      }
+      if constexpr (BITS > 0) {
+        constexpr int per = (BITS + 2) / 3;
+        if (g > 0) {
+#pragma unroll
+          for (int i = (g - 1) * per; i < (g == 3 ? BITS : g * per); ++i)
+            w.r[i] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, (c * 64 * BITS + i * 64 + lane) * 16, 0, kNt));
+        }
+        if (g == 3) w.sr = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rsr, (c * 16 + tl) * 8, 0, 0));
+      }
+    };
     const uint2 *s_lut = reinterpret_cast<const uint2 *>(smem);
     const float kinv = L.kinv;
     const float bias = BITS > 0 ? resid_bias(BITS > 0 ? BITS : 8) : 0.0f;
-    // compute chunk ci (its NST stages, a barrier before every stage but the first overall)
-    auto compute = [&](WRegs<BITS> &w, int ci) {
+    // compute chunk ci (its NST stages, a barrier before every stage but the
+    // first overall); refill(g) runs after group g
+    auto compute = [&](WRegs<BITS> &w, int ci, auto refill) {
       pin(w);
       const uint32_t *bw = reinterpret_cast<const uint32_t *>(w.b);
       const uint32_t *rw = reinterpret_cast<const uint32_t *>(w.r);
@@ -777,6 +819,7 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
               if constexpr (BITS > 0) accC[m][i] = fmaf(sr, aR[i] - bias * xsv[i], accC[m][i]);
             }
           }
+          refill(g);
         }
         if (st == NST - 1) {
 #pragma unroll
@@ -802,7 +845,7 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
       // first pass's x loads go out before the weights, so waiting for them
       // leaves the weight loads in flight.
       const RotInArgs &ra = rot;
-      const int SB = ra.SB, TPS = SB >> 4, nlog = 31 - __builtin_clz(SB);
+      const int SB = ra.SB, TPS = SB >> 4;
       const bool idle = threadIdx.x >= 256;
       const int rtid = idle ? 0 : threadIdx.x, lt = rtid % TPS, tg = rtid / TPS;
       const int kbeg = c_begin * kChunk, kend = c_end * kChunk;
@@ -831,7 +874,7 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
       auto rproc = [&]() __attribute__((always_inline)) {
         float v[16];
         cvt_x16(v, xraw);
-        fwht_b(v, xs, lt, TPS, nlog, ra.lb, idle);
+        fwht_b(v, xs, lt, ra.lb, idle);
         float mx = 0.f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(v[j]));
@@ -886,20 +929,39 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
       __builtin_amdgcn_s_barrier();                         // stage 0 of x' ready
       asm volatile("" ::: "memory");
     }
-    if (!loader) {
+    if (!loader && MT >= 3) {
+      // (three or more token tiles: a chunk's compute is long, so each set is
+      // refilled in one piece right after it is computed)
       int ci = 0;
 #pragma unroll 1
       for (; ci + NS - 1 < nchk; ci += NS) {
 #pragma unroll
         for (int k = 0; k < NS; ++k) {
-          compute(w[k], ci + k);
+          compute(w[k], ci + k, [](int) {});
           fence();
           loadw(w[k], c_begin + ci + k + NS);
         }
       }
 #pragma unroll
       for (int k = 0; k < NS - 1; ++k)
-        if (ci + k < nchk) compute(w[k], ci + k);
+        if (ci + k < nchk) compute(w[k], ci + k, [](int) {});
+    } else if (!loader) {
+      // chunk j is computed from set j % NS while set (j - 1) % NS, computed
+      // just before, is refilled with chunk j - 1 + NS; chunk 0 refills
+      // nothing.  NS chunks per trip, the last < NS after the loop.
+      compute(w[0], 0, [](int) {});
+      int j = 1;
+#pragma unroll 1
+      for (; j + NS <= nchk; j += NS) {
+#pragma unroll
+        for (int k = 1; k <= NS; ++k) {
+          const int s = k % NS, pr = k - 1;
+          compute(w[s], j + k - 1, [&](int g) { loadpart(w[pr], c_begin + j + k - 2 + NS, g); });
+        }
+      }
+#pragma unroll
+      for (int k = 1; k < NS; ++k)
+        if (j + k - 1 < nchk) compute(w[k], j + k - 1, [&](int g) { loadpart(w[k - 1], c_begin + j + k - 2 + NS, g); });
     }
   }
 
