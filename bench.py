@@ -66,6 +66,94 @@ def stored_traffic(digest):
     return float(m_val.group(1))
 
 
+MOE_EXPERTS, MOE_HIDDEN, MOE_INTER, MOE_TOPK, MOE_T, MOE_BITS, MOE_RHO = 256, 2048, 512, 8, 16, 8, 0.62
+MOE_ROUTINGS = 8
+
+
+def moe_leg(nl, torch, synth, reps):
+    """MoE block verify and draft: 256 routed experts (hidden 2048, expert
+    intermediate 512) plus one shared expert, top-8 routing of a 16-token block
+    with correlated router logits, 2-bit base + 8-bit residual; one grouped
+    call per projection (gate, up, down).  Every expert owns its own device
+    copy of its planes (all made from one synthetic linear per shape: values
+    do not change the work), and passes cycle through 8 routings so the 1 GB
+    expert set streams from HBM."""
+    import numpy as np
+    n = MOE_EXPERTS + 1
+    shapes = {"gate": (MOE_INTER, MOE_HIDDEN), "up": (MOE_INTER, MOE_HIDDEN), "down": (MOE_HIDDEN, MOE_INTER)}
+    groups, handles = {}, []
+    for k, (o, i) in shapes.items():
+        lin = synth.make_linear(o, i, MOE_BITS, cfg=4, idx=len(groups), two_sided=False)
+        d = {key: (None if lin[key] is None else torch.from_numpy(np.ascontiguousarray(lin[key]).view(dt)).cuda())
+             for key, dt in [("base_codes", np.uint8), ("base_scales", np.int16), ("resid_codes", np.uint8),
+                             ("resid_scales", np.int16), ("sign_in", np.int8), ("sign_out", np.int8)]}
+        hs = [nl.nested_linear_create(o, i, MOE_BITS, levels=lin["levels"], **d) for _ in range(n)]
+        handles += hs
+        groups[k] = nl.nested_linear_group_create(hs)
+        del d
+    routes = []
+    for r in range(MOE_ROUTINGS):
+        _, pt, off = synth.router_topk(MOE_T, MOE_EXPERTS, MOE_TOPK, MOE_RHO, cfg=4, idx=r)
+        pt = np.concatenate([pt, np.arange(MOE_T, dtype=np.int32)]).astype(np.int32)   # shared expert last
+        off = np.concatenate([off, [off[-1] + MOE_T]]).astype(np.int32)
+        P = len(pt)
+        active = int(np.count_nonzero(np.diff(off)))
+        routes.append((torch.from_numpy(pt).cuda(), None, torch.from_numpy(off).cuda(), P, active))
+    Pmax = max(r[3] for r in routes)
+    ws = {k: torch.zeros(nl.nested_linear_group_workspace_bytes(g, Pmax), dtype=torch.uint8, device="cuda")
+          for k, g in groups.items()}
+    x = torch.from_numpy(synth.make_x(MOE_T, MOE_HIDDEN, cfg=4, idx=100).view(np.int16)).cuda()
+    # down-projection inputs: one synthetic 512-vector per token, routed by the
+    # same pairs (the grouped call takes at most 64 input rows)
+    h = torch.from_numpy(synth.make_x(MOE_T, MOE_INTER, cfg=4, idx=101).view(np.int16)).cuda()
+    yg = torch.empty((Pmax, MOE_INTER), dtype=torch.float32, device="cuda")
+    yu = torch.empty_like(yg)
+    yd = torch.empty((Pmax, MOE_HIDDEN), dtype=torch.float32, device="cuda")
+    out = {}
+    for verify in (True, False):
+        fn = nl.nested_linear_verify_grouped if verify else nl.nested_linear_draft_grouped
+
+        def passes(s):
+            for pt, pd, off, P, _ in routes:
+                fn(groups["gate"], pt, off, P, x, MOE_T, yg, ws["gate"], s)
+                fn(groups["up"], pt, off, P, x, MOE_T, yu, ws["up"], s)
+                fn(groups["down"], pt, off, P, h, MOE_T, yd, ws["down"], s)
+
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            passes(st)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            passes(torch.cuda.current_stream())
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        e1.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * MOE_ROUTINGS)
+        per_expert = 3 * MOE_INTER * MOE_HIDDEN * synth.bytes_per_weight(MOE_BITS if verify else 0)
+        touched = sum(r[4] for r in routes) / MOE_ROUTINGS * per_expert
+        out["verify" if verify else "draft"] = {"us_per_block": round(us, 2), "GBps": round(touched / us / 1e3, 1),
+                                                "frac_hbm_peak": round(touched / us / 1e3 / HBM_PEAK_GBPS, 3)}
+        del g
+    out["active_experts_avg"] = round(sum(r[4] for r in routes) / MOE_ROUTINGS, 1)
+    out["workload"] = (f"{MOE_EXPERTS} experts + 1 shared, hidden {MOE_HIDDEN}, expert intermediate {MOE_INTER}, "
+                       f"top-{MOE_TOPK} of a {MOE_T}-token block (router correlation {MOE_RHO}), "
+                       f"{MOE_BITS}-bit residual; gate, up, down: one grouped call each")
+    for g in groups.values():
+        nl.nested_linear_group_destroy(g)
+    for hnd in handles:
+        nl.nested_linear_destroy(hnd)
+    log(f"[bench] moe block: verify {out['verify']['us_per_block']} us, draft {out['draft']['us_per_block']} us")
+    return out
+
+
 def roofline_leg(nl, call, ncopy, stream, bpw):
     """Roofline of the dominant kernel, forward_kernel<6, 1>: eager verify
     launches at T = 8 and 16 over the four projections, each timed by a HIP
@@ -361,6 +449,9 @@ def main():
 
     roofline = roofline_leg(nl, call, ncopy, stream, bpw)
 
+    # ---- the MoE block (grouped calls)
+    moe = moe_leg(nl, torch, synth, args.reps)
+
     # ---- streaming reference on the same GPU (torch reduction over 2 GiB)
     big = torch.ones(2 ** 29, dtype=torch.float32, device=dev)
     big.sum()
@@ -407,6 +498,7 @@ def main():
         "per_case": per_case,
         "single_call": single,
         "two_sided": two_sided,
+        "moe_block": moe,
         "stream_read_GBps_torch_sum": round(stream_gbps, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -2,6 +2,7 @@
 // repack, workspace layout, launch configuration.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -452,8 +453,15 @@ static void fill_launch(FwdArgs &f, const Plan &p, int n_linears, char *ws, floa
   f.hv.ob_base = kCtrFixed + n_linears * p.n_rb;
   f.hv.obr_base = f.hv.ob_base + n_linears * p.n_sb;
   f.n_rot = p.local ? 0 : rotate_workgroups(p.rows, f.rot.Kp, f.rot.SB);
+  // Contraction workgroups: one slot of them per linear, or, when that
+  // halves the grid, one per linear that can have rows (each has one at
+  // least, so at most rows of them do).  The slot's workgroups then find
+  // their expert with a scan of the offsets, one memory round trip ahead of
+  // the descriptor: that pays only where idle experts outnumber the rest.
   const int per = p.n_rb * p.S;
-  f.n_gemm = n_linears * per;
+  const int cap = std::min(n_linears, p.rows);
+  f.g.slots = n_linears > 1 && 2 * cap < n_linears;
+  f.n_gemm = (f.g.slots ? cap : n_linears) * per;
   f.hv.n_rot = f.n_rot;
   f.g.out = p.mode == kOutDirect ? y : (float *)(ws + p.o_part);
   f.g.split_stride = (size_t)p.rows * d_out;

@@ -54,6 +54,7 @@ struct GemmArgs {
   size_t split_stride;
   int T;                    // rows of x' (tokens or pairs)
   int d_out, n_tiles, n_chunks, Kp, Gp, cps, ldo, n_rb, n_experts;
+  int slots;                // grouped: grid slots map to the experts with rows (else slot = expert)
 };
 
 struct FinishArgs {
@@ -74,16 +75,19 @@ struct FinishArgs {
 // row-block arrival counters (split-K) and per output superblock the arrival
 // counters and finish tokens (two-sided form).  Every rotation workgroup adds
 // one to each of the 8 ready lines once its x' is stored; a contraction
-// workgroup polls one line until it reads n_rot; the last contraction
-// workgroup to finish clears the lines and the exit counter.
+// workgroup that has rows to compute polls one line until it reads n_rot,
+// and counts itself on that line's exit counter when done.  The line's
+// target (active linears x its workgroups per linear) is published by the
+// first rotation workgroup; the last exit clears the line's three words.
 constexpr int kCtrStride = 16;  // words
 constexpr int kCtrLines = 16384;
 constexpr size_t kCtrBytes = (size_t)kCtrLines * kCtrStride * 4;  // 1 MiB
 enum : int {
   kCtrErr = 0,       // waits that hit the spin limit (diagnostic; stays zero)
   kCtrReady = 1,     // 8 ready lines: rotation workgroups done
-  kCtrExit = 9,      // contraction workgroups done
-  kCtrFixed = 10,
+  kCtrExit = 9,      // 8 lines: waiting contraction workgroups done
+  kCtrActive = 17,   // 8 lines: linears with rows (1, or the active experts)
+  kCtrFixed = 25,
 };
 constexpr uint32_t kSpinLimit = 1u << 22;
 

@@ -343,8 +343,50 @@ __device__ __forceinline__ int expert_of(const int32_t *offsets, int n, int row)
 // An expert takes part in a grouped call when it owns at least one pair and
 // its first pair lies inside the call's R rows.  The contraction, the count
 // of waiting workgroups and the finish all use this one predicate.
+__device__ __forceinline__ bool expert_active(const int32_t *offsets, int e, int R);
+
+// Index of the slot-th linear (in index order) that has rows by the test
+// of expert_active, or -1 when fewer have.  Each lane tests 8 consecutive
+// experts per round of 512 (one batch of loads), a wave-wide prefix count
+// finds the lane holding the slot, its bit mask the expert.  The result is
+// wave-uniform; every wave of a workgroup computes it alike.
+__device__ int nth_active_expert(const int32_t *offsets, int n, int R, int slot) {
+  const NL_GLOBAL int32_t *o = (const NL_GLOBAL int32_t *)offsets;
+  const int lane = threadIdx.x & 63;
+  int seen = 0;
+  for (int r0 = 0; r0 < n; r0 += 512) {
+    const int e0 = r0 + 8 * lane;
+    int v[9];
+#pragma unroll
+    for (int i = 0; i < 9; ++i) v[i] = o[min(e0 + i, n)];  // offsets holds n + 1 entries
+    uint32_t bits = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      bits |= (uint32_t)(e0 + i < n && v[i + 1] > v[i] && v[i] >= 0 && v[i] < R) << i;
+    const int c = __popc(bits);
+    int incl = c;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int u = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += u;
+    }
+    const int total = __shfl(incl, 63, 64);
+    if (slot < seen + total) {
+      const int want = slot - seen;
+      const unsigned long long m = __ballot(want >= incl - c && want < incl);
+      const int L = __ffsll(m) - 1;
+      uint32_t bl = __shfl(bits, L, 64);
+      for (int q = want - __shfl(incl - c, L, 64); q > 0; --q) bl &= bl - 1;  // drop lower set bits
+      return __builtin_amdgcn_readfirstlane(r0 + 8 * L + __ffs(bl) - 1);
+    }
+    seen += total;
+  }
+  return -1;
+}
+
 __device__ __forceinline__ bool expert_active(const int32_t *offsets, int e, int R) {
-  const int r0 = offsets[e], r1 = offsets[e + 1];
+  const NL_CONST int32_t *o = (const NL_CONST int32_t *)offsets;  // scalar loads when e is uniform
+  const int r0 = o[e], r1 = o[e + 1];
   return r1 > r0 && r0 >= 0 && r0 < R;
 }
 
@@ -1171,28 +1213,55 @@ __global__ __launch_bounds__(kThreads) void forward_kernel(const FwdArgs f) {
   uint32_t *ctr = f.hv.ctr;
   if (b < f.n_rot) {
     rotate_body<true>(f.rot, b, xch, spare);
-    wait_stores();  // x' and its metadata acknowledged in every thread
+    // linears whose contraction workgroups will wait: those with rows, up
+    // to the number of linear slots in the grid
+    const int per = f.g.n_rb * f.hv.S;
+    uint32_t n_active = 1;
+    if (f.rot.lins) {
+      n_active = 0;
+      if (threadIdx.x < 64)
+        for (int e = threadIdx.x; e < f.rot.n_experts; e += 64) n_active += expert_active(f.rot.offsets, e, f.rot.rows);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) n_active += __shfl_xor(n_active, o, 64);
+      n_active = min(n_active, (uint32_t)(f.n_gemm / per));
+    }
+    // line k is waited on iff some linear has rows and owns a workgroup on it
+    const int k = threadIdx.x;
+    const bool waiters = n_active > 0 && k < per;
+    if (b == 0 && k < 8 && waiters) st_dev(ctr_at(ctr, kCtrActive + k), n_active);
+    wait_stores();  // x' and its metadata (and the active count) acknowledged in every thread
     __syncthreads();
-    if (threadIdx.x < 8) ctr_add(ctr_at(ctr, kCtrReady + threadIdx.x), 1u);
+    // a line nobody waits on is cleared by the last rotation workgroup
+    if (k < 8 && ctr_add(ctr_at(ctr, kCtrReady + k), 1u) == (uint32_t)(f.n_rot - 1) && !waiters)
+      st_dev(ctr_at(ctr, kCtrReady + k), 0u);
     return;
   }
   b -= f.n_rot;
   if (b < f.n_gemm) {
     const int per = f.g.n_rb * f.hv.S;
-    const int e = b / per, j = b - e * per;
+    int e = b / per;
+    const int j = b - e * per;
     const int split = j / f.g.n_rb, rb = j - split * f.g.n_rb;
+    if (f.g.lins && f.g.slots) {  // slot e of the grid takes the e-th expert with rows
+      e = nth_active_expert(f.g.offsets, f.g.n_experts, f.g.T, e);
+      if (e < 0) return;
+    }
     Handover hv = f.hv;
     hv.line = j & 7;
     contract_body<BITS, MT, true>(f.g, e, rb, split, smem, hv, f.rot);
-    // Thread 0 passed a barrier after its loader's wait (or the workgroup
-    // had nothing to do), so the last contraction workgroup to get here is
-    // after every wait on the ready lines.  It clears them once they hold
-    // their final count (they already do unless no workgroup waited).
-    if (f.n_rot > 0 && threadIdx.x == 0 &&
-        ctr_add(ctr_at(ctr, kCtrExit), 1u) == (uint32_t)(f.n_gemm - 1)) {
-      for (int k = 0; k < 8; ++k) wait_ready(ctr_at(ctr, kCtrReady + k), (uint32_t)f.n_rot, ctr_at(ctr, kCtrErr));
-      for (int k = 0; k < 8; ++k) st_dev(ctr_at(ctr, kCtrReady + k), 0u);
-      st_dev(ctr_at(ctr, kCtrExit), 0u);
+    // A workgroup that waited on its ready line (thread 0 passed a barrier
+    // after the loader's wait) counts itself on the line's exit counter; the
+    // line's last one clears the line.  Idle experts neither wait nor count.
+    const bool waited = f.n_rot > 0 && (!f.g.lins || f.g.slots || expert_active(f.g.offsets, e, f.g.T));
+    if (waited && threadIdx.x == 0) {
+      const int k = j & 7;
+      const uint32_t per_k = (uint32_t)((per - 1 - k) / 8 + 1);  // workgroups of a linear on line k
+      const uint32_t target = ld_dev(ctr_at(ctr, kCtrActive + k)) * per_k;
+      if (ctr_add(ctr_at(ctr, kCtrExit + k), 1u) == target - 1) {
+        st_dev(ctr_at(ctr, kCtrReady + k), 0u);
+        st_dev(ctr_at(ctr, kCtrExit + k), 0u);
+        st_dev(ctr_at(ctr, kCtrActive + k), 0u);
+      }
     }
     return;
   }

@@ -422,6 +422,25 @@ def test_grouped_few_tokens(nl, torch_cuda, T, two):
         np.testing.assert_array_equal(a, b)
 
 
+def test_grouped_many_experts_few_active(nl, torch_cuda):
+    # 600 experts (8 distinct weight sets, expert e holds set e % 8), rows
+    # only at experts 3, 511, 512 and 598: the grid has one slot per pair at
+    # most and each slot finds its expert past the first 512 as well
+    base = [synth.make_linear(256, 256, 6, cfg=76, idx=i) for i in range(8)]
+    experts = [base[e % 8] for e in range(600)]
+    rows = {3: [0, 1], 511: [2], 512: [0, 3], 598: [1, 2, 3]}
+    pt = np.array([t for e in sorted(rows) for t in rows[e]], dtype=np.int32)
+    counts = np.zeros(600, np.int32)
+    for e, ts in rows.items():
+        counts[e] = len(ts)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    x = synth.make_x(4, 256, cfg=76, idx=0)
+    for verify in (False, True):
+        a, b, _ = run_grouped(nl, torch_cuda, experts, pt, off, x, verify)
+        assert rel_err(a, oracle.forward_grouped(experts, pt, off, x, verify)) <= TOL
+        np.testing.assert_array_equal(a, b)
+
+
 def test_misaligned_x_is_rejected(nl, torch_cuda):
     torch = torch_cuda
     lin = synth.make_linear(256, 256, 6, cfg=0, idx=5)
