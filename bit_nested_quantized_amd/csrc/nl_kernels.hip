@@ -458,38 +458,60 @@ __device__ void wait_ready(const uint32_t *line, uint32_t n, uint32_t *err) {
 // ===========================================================================
 // Threads past the first 256 (the fifth wave of the single launch) run the
 // same code on a spare LDS area (`spare`, SB + SB/16 floats) and store nothing.
-template <bool COH>
-__device__ __forceinline__ void rotate_body(const RotInArgs &a, int wg, float *xch, float *spare) {
+// Rotation workgroup-task wg: 256 threads transform 4096 values as 4096/SB
+// tasks (row, superblock of SB columns) of TPS = SB/16 threads, 16 values
+// each.  Thread ids from 256 up only keep the barrier count (extra).
+struct RotTask {
+  int row, k0, lt, tl, xrow;
+  bool valid, extra;
+  const int8_t *sign;
+};
+__device__ __forceinline__ RotTask rot_task(const RotInArgs &a, int wg, int tid) {
+  RotTask t;
   const int SB = a.SB, TPS = SB >> 4;
-  const bool extra = threadIdx.x >= 256;
-  const int tid = extra ? 0 : threadIdx.x, lt = tid % TPS, tl = tid / TPS;
+  t.extra = tid >= 256;
+  if (t.extra) tid = 0;
+  t.lt = tid % TPS;
+  t.tl = tid / TPS;
   const int n_sb = a.Kp / SB;
-  const int task = wg * (256 / TPS) + tl;
-  const bool valid = !extra && task < a.rows * n_sb;
-  const int row = valid ? task / n_sb : 0, sb = valid ? task % n_sb : 0;
-  const int kb = sb * SB;
-  float *x = extra ? spare : xch + tl * (SB + (SB >> 4));
-
-  int xrow = valid ? row : -1;
-  const int8_t *sign = a.sign;
+  const int task = wg * (256 / TPS) + t.tl;
+  t.valid = !t.extra && task < a.rows * n_sb;
+  t.row = t.valid ? task / n_sb : 0;
+  t.k0 = (t.valid ? task % n_sb : 0) * SB + 16 * t.lt;
+  t.xrow = t.valid ? t.row : -1;
+  t.sign = a.sign;
   if (a.lins) {  // grouped: pair -> (token, expert); lanes without a task read expert 0's signs
-    if (valid) {
-      xrow = a.pair_token[row];
-      if (xrow < 0 || xrow >= a.x_rows) xrow = -1;
+    if (t.valid) {
+      t.xrow = a.pair_token[t.row];
+      if (t.xrow < 0 || t.xrow >= a.x_rows) t.xrow = -1;
     }
-    sign = ((const NL_GLOBAL LinearDev *)a.lins)[valid ? expert_of(a.offsets, a.n_experts, row) : 0].sign_in;
+    t.sign = ((const NL_GLOBAL LinearDev *)a.lins)[t.valid ? expert_of(a.offsets, a.n_experts, t.row) : 0].sign_in;
   }
-  const int k0 = kb + 16 * lt;
-  float v[16];
-  cvt_x16(v, load_x16(a.x, sign, xrow, k0, a.d_in));
-  fwht_b(v, x, lt, a.lb, extra);
+  return t;
+}
 
+// One thread's 16 rotated values as fp16 pairs under the (row, chunk)
+// power-of-two scale 2^s, and the sum of its 128-column group.
+struct RotOut {
+  uint32_t w[8];
+  float gs;
+  int s;
+};
+
+// x' of one thread: x * sign, the block transform (xch: the thread's task
+// area), then the scale of its 512-column chunk (32 threads) from the
+// chunk's largest magnitude and the fp16 group sums (8 threads).
+__device__ __forceinline__ void rot_transform(const RotInArgs &a, const RotTask &t, const XRaw &xr, float *xch,
+                                              RotOut &o) {
+  float v[16];
+  cvt_x16(v, xr);
+  fwht_b(v, xch, t.lt, a.lb, t.extra);
   // layout B: 16 consecutive columns; a chunk is 32 threads, a group 8
   float m = 0.f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(v[j]));
 #pragma unroll
-  for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  for (int d = 1; d < 32; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
   int s = 0;
   if (m > 0.0f) {
     int e;
@@ -497,21 +519,31 @@ __device__ __forceinline__ void rotate_body(const RotInArgs &a, int wg, float *x
     s = 15 - e;
     s = s > 120 ? 120 : (s < -120 ? -120 : s);
   }
-  uint32_t w[8];
   float gs = 0.f;
 #pragma unroll
   for (int h = 0; h < 8; ++h) {
     const _Float16 q0 = (_Float16)ldexpf(v[2 * h], s), q1 = (_Float16)ldexpf(v[2 * h + 1], s);
     gs += (float)q0 + (float)q1;
-    w[h] = (uint32_t)__builtin_bit_cast(uint16_t, q0) | ((uint32_t)__builtin_bit_cast(uint16_t, q1) << 16);
+    o.w[h] = (uint32_t)__builtin_bit_cast(uint16_t, q0) | ((uint32_t)__builtin_bit_cast(uint16_t, q1) << 16);
   }
 #pragma unroll
-  for (int o = 1; o < 8; o <<= 1) gs += __shfl_xor(gs, o, 64);
-  if (!valid) return;
-  const int R = a.rows;
-  const size_t xo = (size_t)row * a.Kp + k0;  // element offset of the thread's 16 columns
-  float *mg = a.meta + ((size_t)(k0 >> 9) * 5 + ((k0 >> 7) & 3)) * R + row;
-  float *ms = a.meta + ((size_t)(k0 >> 9) * 5 + 4) * R + row;
+  for (int d = 1; d < 8; d <<= 1) gs += __shfl_xor(gs, d, 64);
+  o.gs = gs;
+  o.s = s;
+}
+
+// x' row-major [rows][Kp] fp16 (16 columns of the thread) and the metadata
+// [chunk][5][rows]: four group sums and the chunk's inverse scale times
+// 1/sqrt(block).  COH: device-coherent stores for a reader elsewhere in the
+// same launch.
+template <bool COH>
+__device__ __forceinline__ void rot_store(const RotInArgs &a, const RotTask &t, const uint32_t (&w)[8], float gs,
+                                          int s) {
+  if (!t.valid) return;
+  const int R = a.rows, k0 = t.k0, lt = t.lt;
+  const size_t xo = (size_t)t.row * a.Kp + k0;  // element offset of the thread's 16 columns
+  float *mg = a.meta + ((size_t)(k0 >> 9) * 5 + ((k0 >> 7) & 3)) * R + t.row;
+  float *ms = a.meta + ((size_t)(k0 >> 9) * 5 + 4) * R + t.row;
   const u32x4 lo = {w[0], w[1], w[2], w[3]}, hi = {w[4], w[5], w[6], w[7]};
   if constexpr (COH) {
     const __amdgpu_buffer_rsrc_t xr =
@@ -526,6 +558,15 @@ __device__ __forceinline__ void rotate_body(const RotInArgs &a, int wg, float *x
     if ((lt & 7) == 0) *mg = gs;
     if ((lt & 31) == 0) *ms = ldexpf(a.rsqrt_b, -s);
   }
+}
+
+template <bool COH>
+__device__ __forceinline__ void rotate_body(const RotInArgs &a, int wg, float *xch, float *spare) {
+  const RotTask t = rot_task(a, wg, threadIdx.x);
+  const XRaw xr = load_x16(a.x, t.sign, t.xrow, t.k0, a.d_in);
+  RotOut o;
+  rot_transform(a, t, xr, t.extra ? spare : xch + t.tl * (a.SB + (a.SB >> 4)), o);
+  rot_store<COH>(a, t, o.w, o.gs, o.s);
 }
 
 __global__ __launch_bounds__(256) void rotate_in_kernel(const RotInArgs a) {
@@ -644,6 +685,15 @@ __device__ __forceinline__ void dma4(uint32_t lds, uint32_t voff, const void *ba
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
                ::"s"(lds), "v"(voff), "s"(base) : "memory", "m0");
 }
+// A rotation task's x' is acknowledged (wait_stores) by the thread calling
+// this with k < 8: it adds one to ready line k.  The last task to count on
+// a line no contraction workgroup waits on clears it.  waiters: line k has
+// waiting workgroups (some linear has rows and owns a workgroup on it).
+__device__ __forceinline__ void publish_ready(uint32_t *ctr, int n_rot, int k, bool waiters) {
+  if (ctr_add(ctr_at(ctr, kCtrReady + k), 1u) == (uint32_t)(n_rot - 1) && !waiters)
+    st_dev(ctr_at(ctr, kCtrReady + k), 0u);
+}
+
 // MT = 0: local rotation mode (single launch only; rot describes x).
 template <int BITS, int MT, bool FUSED>
 __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, int split, char *smem,
@@ -834,6 +884,26 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
 #pragma unroll
         for (int gl = 0; gl < XG; ++gl) {
           const int g = st * XG + gl;
+          // One token tile: the group's activations and sums are read first,
+          // so their LDS latency passes under the unpacking below (more
+          // tiles read theirs at the MFMAs: the registers would not fit).
+          constexpr int HA = MTC == 1 ? 1 : 0;
+          half8 A[1][4];
+          floatx4 xs[1];
+          auto act = [&](int m, int s) -> half8 {
+            if constexpr (HA) return A[0][s];
+            return *reinterpret_cast<const half8 *>(xb + ((gl * 4 + s) * 4 * TR + 16 * m) * 8);
+          };
+          auto sums = [&](int m) -> floatx4 {
+            if constexpr (BITS == 0) return floatx4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (HA) return xs[0];
+            return *reinterpret_cast<const floatx4 *>(mb + gl * TR + 16 * m);
+          };
+          if constexpr (HA) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) A[0][s] = *reinterpret_cast<const half8 *>(xb + (gl * 4 + s) * 4 * TR * 8);
+            if constexpr (BITS > 0) xs[0] = *reinterpret_cast<const floatx4 *>(mb + gl * TR);
+          }
           uint32_t bq[16];
           unpack_base(bw + 2 * g, s_lut, bq);
           uint32_t rq[16];
@@ -846,13 +916,12 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
             floatx4 aB = {0.f, 0.f, 0.f, 0.f}, aR = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-              const half8 A = *reinterpret_cast<const half8 *>(xb + ((gl * 4 + s) * 4 * TR + 16 * m) * 8);
-              aB = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, as_half8(bq + 4 * s), aB, 0, 0, 0);
+              const half8 a = act(m, s);
+              aB = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, as_half8(bq + 4 * s), aB, 0, 0, 0);
               if constexpr (BITS > 0)
-                aR = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, as_half8(rq + 4 * s), aR, 0, 0, 0);
+                aR = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, as_half8(rq + 4 * s), aR, 0, 0, 0);
             }
-            floatx4 xsv = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (BITS > 0) xsv = *reinterpret_cast<const floatx4 *>(mb + gl * TR + 16 * m);
+            const floatx4 xsv = sums(m);
             // Draft and verify round identically: with s_r = 0 the residual
             // fma returns accC unchanged, so verify(0 residual) == draft bitwise.
 #pragma unroll
@@ -1231,9 +1300,7 @@ __global__ __launch_bounds__(kThreads) void forward_kernel(const FwdArgs f) {
     if (b == 0 && k < 8 && waiters) st_dev(ctr_at(ctr, kCtrActive + k), n_active);
     wait_stores();  // x' and its metadata (and the active count) acknowledged in every thread
     __syncthreads();
-    // a line nobody waits on is cleared by the last rotation workgroup
-    if (k < 8 && ctr_add(ctr_at(ctr, kCtrReady + k), 1u) == (uint32_t)(f.n_rot - 1) && !waiters)
-      st_dev(ctr_at(ctr, kCtrReady + k), 0u);
+    if (k < 8) publish_ready(ctr, f.n_rot, k, waiters);
     return;
   }
   b -= f.n_rot;
