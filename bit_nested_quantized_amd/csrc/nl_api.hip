@@ -275,7 +275,7 @@ extern "C" nl_status nested_linear_info(nl_handle h, int32_t *d_out, int32_t *d_
 struct Plan {
   int rows;       // rows of x' (tokens, or pairs for a grouped call)
   int mt;         // 16-token MFMA tiles
-  int n_rb;       // 64-row workgroups per linear
+  int n_rb;       // row blocks (16 x tile waves rows) per linear
   int S, cps;     // split-K count and chunks per split
   bool finish;    // the staged path needs a finish pass
   int mode;       // single launch: kOutDirect, kOutSplit or kOutTwoSided
@@ -301,7 +301,7 @@ static Plan make_plan(int d_out, int n_tiles, int n_chunks, bool sign_out, int b
   Plan p;
   p.rows = rows;
   p.mt = mt;
-  p.n_rb = (n_tiles + 3) / 4;
+  p.n_rb = (n_tiles + tile_waves(mt) - 1) / tile_waves(mt);
   // Split K while the grid stays within one workgroup per CU (256 CUs).
   int S = g_wg_target / (p.n_rb * n_linears);
   S = S < 1 ? 1 : (S > n_chunks ? n_chunks : S);

@@ -123,6 +123,12 @@ struct FwdArgs {
   int n_rot, n_gemm;
 };
 
+// Tile waves (16 output rows each) of a contraction workgroup, plus one x'
+// loader wave: eight for three or more 16-token tiles, whose chunks are long
+// enough that two tile waves per SIMD pay, else four.
+constexpr int tile_waves(int mt) { return mt >= 3 ? 8 : 4; }
+constexpr int wg_threads(int mt) { return 64 * (tile_waves(mt) + 1); }
+
 int rotate_workgroups(int rows, int Kp, int SB);
 int finish_workgroups(int rows, int d_out, int OB);
 

@@ -575,18 +575,19 @@ __global__ __launch_bounds__(256) void rotate_in_kernel(const RotInArgs a) {
 }
 
 // ===========================================================================
-// Fused contraction.  Workgroup = 5 waves: waves 0-3 each own one 16-row
-// tile of a 64-row block over a K-range of chunks (split-K index `split`),
-// wave 4 stages the activations.
+// Fused contraction.  Workgroup = TW tile waves + 1: each tile wave owns one
+// 16-row tile of a 16*TW-row block over a K-range of chunks (split-K index
+// `split`), wave TW stages the activations (TW = 4, or 8 for three or more
+// token tiles).
 //   - each tile wave streams its own tile-chunks (2 + b pieces of 1 KiB plus
-//     the scales) from HBM into registers, two chunks in flight; it issues no
-//     other loads, so the compiler's waits on them are exact;
+//     the scales) from HBM into a ring of register sets; it issues no other
+//     loads, so the compiler's waits on them are exact;
 //   - the loader wave copies x' (fp16) and its group sums / scales with
 //     global_load_lds into a ring of NX LDS stages of XG groups, NX - 1
 //     stages ahead; one s_barrier per stage hands a stage to the tile waves
 //     and the stage before it back to the loader.
 // In the single launch only the loader waits for the rotation, so the tile
-// waves' first two chunks stream in meanwhile.  Two workgroups fit a CU.
+// waves' first chunks stream in meanwhile.  One workgroup per CU (LDS).
 // Per group: base and residual planes -> fp16 B operands; 4 MFMA steps per
 // plane and token tile; fp32 epilogue
 //   acc_chunk = fma(s_b / kappa, A_base, acc_chunk)
@@ -594,8 +595,6 @@ __global__ __launch_bounds__(256) void rotate_in_kernel(const RotInArgs a) {
 // and at the end of each chunk acc = fma(tsc, acc_chunk, acc).
 // ===========================================================================
 
-constexpr int kTileWaves = 4;
-constexpr int kThreads = 64 * (kTileWaves + 1);
 constexpr int kLdsBytes = 160 * 1024;
 
 template <int BITS, int MT>
@@ -652,7 +651,8 @@ struct WRegs {
 template <int BITS, int MT>
 __host__ __device__ constexpr int ring_sets() {
   if constexpr (MT == 0) return BITS == 0 ? 3 : 2;
-  return MT >= 3 ? 2 : (BITS == 0 ? 4 : 3);
+  if constexpr (MT >= 3) return BITS == 0 ? 2 : 1;  // eight tile waves: 168 registers each
+  return BITS == 0 ? 4 : 3;
 }
 
 // An ordered no-op on every register of a set: work on the set cannot be
@@ -704,11 +704,12 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
   constexpr int TR = LOCAL ? kLocalRows : Pl::TR, XG = LOCAL ? 4 : Pl::XG, NST = LOCAL ? 1 : Pl::NST;
   constexpr int NX = Pl::NX;
   static_assert(!LOCAL || FUSED, "local rotation runs in the single launch only");
+  constexpr int TW = tile_waves(MT), NT = wg_threads(MT), RB = 16 * TW;  // tile waves, threads, rows per block
   __shared__ uint32_t s_flag;
 
   // (wave index read as a scalar so per-wave choices stay uniform branches)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const bool loader = wave == kTileWaves;
+  const bool loader = wave == TW;
   // The descriptor by value, read with scalar loads (the expert array is
   // read-only for the launch and e is uniform): a generic pointer that may
   // point at the kernel arguments would turn every field into a flat load
@@ -722,7 +723,7 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
   }
   const NL_CONST LinearDev &L = *(const NL_CONST LinearDev *)(a.lins ? a.lins + e : &a.lin);
   nrows = min(min(nrows, TR), a.T - row_base);
-  const int tile_id = rb * kTileWaves + (loader ? 0 : wave);
+  const int tile_id = rb * TW + (loader ? 0 : wave);
   const bool active = !loader && tile_id < a.n_tiles;
   const int tile = min(tile_id, a.n_tiles - 1);
   const int c_begin = split * a.cps;
@@ -1119,16 +1120,16 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
       // round issued before its adds (one memory round trip for T <= 16 and
       // S <= 8); each output still sums its splits in order from zero
       const float *part = a.out;
-      const int rows_here = min(64, a.d_out - rb * 64), total = nrows * 64;
-      for (int base = 0; base < total; base += 4 * kThreads) {
+      const int rows_here = min(RB, a.d_out - rb * RB), total = nrows * RB;
+      for (int base = 0; base < total; base += 4 * NT) {
         size_t o[4];
         bool ok[4];
         float v[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
-          const int idx = base + e4 * kThreads + threadIdx.x, t = idx >> 6, r = idx & 63;
+          const int idx = base + e4 * NT + threadIdx.x, t = idx / RB, r = idx % RB;
           ok[e4] = idx < total && r < rows_here;
-          o[e4] = (size_t)(row_base + (ok[e4] ? t : 0)) * a.ldo + rb * 64 + (ok[e4] ? r : 0);
+          o[e4] = (size_t)(row_base + (ok[e4] ? t : 0)) * a.ldo + rb * RB + (ok[e4] ? r : 0);
         }
         for (int sp0 = 0; sp0 < hv.S; sp0 += 8) {
           float u[4][8];
@@ -1156,8 +1157,8 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
     wait_stores();
     __syncthreads();
     if (threadIdx.x == 0) {
-      const int sbi = (rb * 64) / hv.sb_rows;
-      const int rb_in_sb = (min(hv.sb_rows, a.d_out - sbi * hv.sb_rows) + 63) / 64;
+      const int sbi = (rb * RB) / hv.sb_rows;
+      const int rb_in_sb = (min(hv.sb_rows, a.d_out - sbi * hv.sb_rows) + RB - 1) / RB;
       uint32_t *cnt = ctr_at(hv.ctr, hv.ob_base + lin * hv.n_sb + sbi);
       if (ctr_add(cnt, 1u) == (uint32_t)(rb_in_sb - 1)) {
         st_dev(cnt, 0u);
@@ -1169,7 +1170,7 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
 }
 
 template <int BITS, int MT>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmArgs a) {
+__global__ __launch_bounds__(wg_threads(MT)) void gemm_kernel(const GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[LdsPlan<BITS, MT>::bytes];
   int rb = blockIdx.x, e = 0;
   if (a.lins) {  // grouped: blockIdx.x = expert * n_rb + row block
@@ -1272,7 +1273,7 @@ __global__ __launch_bounds__(256) void finish_kernel(const FinishArgs a) {
 // finish.  Every wait is on workgroups of lower index.
 // ===========================================================================
 template <int BITS, int MT>
-__global__ __launch_bounds__(kThreads) void forward_kernel(const FwdArgs f) {
+__global__ __launch_bounds__(wg_threads(MT)) void forward_kernel(const FwdArgs f) {
   constexpr int kFwht = (4096 + 256) * 4;  // one workgroup FWHT area (bytes)
   constexpr int kPlan = MT == 0 ? LocalPlan::bytes : LdsPlan<BITS, (MT == 0 ? 1 : MT)>::bytes;
   constexpr int kLds = kPlan > 2 * kFwht ? kPlan : 2 * kFwht;
@@ -1381,10 +1382,10 @@ hipError_t launch_rotate_in(const RotInArgs &a, int rows, hipStream_t s) {
 template <int BITS>
 static hipError_t launch_gemm_bits(const GemmArgs &a, int mt, dim3 grid, hipStream_t s) {
   switch (mt) {
-    case 1: gemm_kernel<BITS, 1><<<grid, kThreads, 0, s>>>(a); break;
-    case 2: gemm_kernel<BITS, 2><<<grid, kThreads, 0, s>>>(a); break;
-    case 3: gemm_kernel<BITS, 3><<<grid, kThreads, 0, s>>>(a); break;
-    case 4: gemm_kernel<BITS, 4><<<grid, kThreads, 0, s>>>(a); break;
+    case 1: gemm_kernel<BITS, 1><<<grid, wg_threads(1), 0, s>>>(a); break;
+    case 2: gemm_kernel<BITS, 2><<<grid, wg_threads(2), 0, s>>>(a); break;
+    case 3: gemm_kernel<BITS, 3><<<grid, wg_threads(3), 0, s>>>(a); break;
+    case 4: gemm_kernel<BITS, 4><<<grid, wg_threads(4), 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1410,9 +1411,9 @@ hipError_t launch_finish(const FinishArgs &a, hipStream_t s) {
 template <int BITS, int MT>
 static void launch_forward_mt(const FwdArgs &f, dim3 grid, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   if (ev0)
-    hipExtLaunchKernelGGL(forward_kernel<BITS, MT>, grid, dim3(kThreads), 0, s, ev0, ev1, 0, f);
+    hipExtLaunchKernelGGL(forward_kernel<BITS, MT>, grid, dim3(wg_threads(MT)), 0, s, ev0, ev1, 0, f);
   else
-    forward_kernel<BITS, MT><<<grid, kThreads, 0, s>>>(f);
+    forward_kernel<BITS, MT><<<grid, wg_threads(MT), 0, s>>>(f);
 }
 
 template <int BITS>
