@@ -690,8 +690,11 @@ __device__ __forceinline__ void dma4(uint32_t lds, uint32_t voff, const void *ba
 // a line no contraction workgroup waits on clears it.  waiters: line k has
 // waiting workgroups (some linear has rows and owns a workgroup on it).
 __device__ __forceinline__ void publish_ready(uint32_t *ctr, int n_rot, int k, bool waiters) {
-  if (ctr_add(ctr_at(ctr, kCtrReady + k), 1u) == (uint32_t)(n_rot - 1) && !waiters)
-    st_dev(ctr_at(ctr, kCtrReady + k), 0u);
+  uint32_t *line = ctr_at(ctr, kCtrReady + k);
+  if (waiters)
+    ctr_add(line, 1u);  // result unused: no return trip before the workgroup ends
+  else if (ctr_add(line, 1u) == (uint32_t)(n_rot - 1))
+    st_dev(line, 0u);
 }
 
 // MT = 0: local rotation mode (single launch only; rot describes x).
