@@ -275,6 +275,7 @@ extern "C" nl_status nested_linear_info(nl_handle h, int32_t *d_out, int32_t *d_
 struct Plan {
   int rows;       // rows of x' (tokens, or pairs for a grouped call)
   int mt;         // 16-token MFMA tiles
+  int tw;         // tile waves per contraction workgroup
   int n_rb;       // row blocks (16 x tile waves rows) per linear
   int S, cps;     // split-K count and chunks per split
   bool finish;    // the staged path needs a finish pass
@@ -297,11 +298,12 @@ static const int g_splits = env_int("NL_SPLITS", 0);
 // tokens: rows of x per linear (T; a grouped call routes each token to an
 // expert at most once).
 static Plan make_plan(int d_out, int n_tiles, int n_chunks, bool sign_out, int b_out, int rows, int mt,
-                      int n_linears, int tokens) {
+                      int n_linears, int tokens, int tw) {
   Plan p;
   p.rows = rows;
   p.mt = mt;
-  p.n_rb = (n_tiles + tile_waves(mt) - 1) / tile_waves(mt);
+  p.tw = tw;
+  p.n_rb = (n_tiles + tw - 1) / tw;
   // Split K while the grid stays within one workgroup per CU (256 CUs).
   int S = g_wg_target / (p.n_rb * n_linears);
   S = S < 1 ? 1 : (S > n_chunks ? n_chunks : S);
@@ -310,7 +312,7 @@ static Plan make_plan(int d_out, int n_tiles, int n_chunks, bool sign_out, int b
   p.S = (n_chunks + p.cps - 1) / p.cps;
   p.finish = sign_out || p.S > 1 || n_linears > 1;
   p.mode = sign_out ? kOutTwoSided : (p.S > 1 ? kOutSplit : kOutDirect);
-  p.local = mt == 1 && tokens <= kLocalTokens && p.cps <= kLocalChunks;
+  p.local = tw == 4 && mt == 1 && tokens <= kLocalTokens && p.cps <= kLocalChunks;
   if (p.local) p.mt = 0;
   p.sb_rows = finish_rows(sign_out, b_out);
   p.n_sb = (d_out + p.sb_rows - 1) / p.sb_rows;
@@ -333,7 +335,8 @@ extern "C" nl_status nested_linear_workspace_bytes(nl_handle h, int32_t T_max, s
   if (T_max > NL_MAX_T) return fail(NL_EUNSUPPORTED, "workspace_bytes: T_max > %d", NL_MAX_T);
   size_t mx = 0;
   for (int T = 1; T <= T_max; ++T) {
-    Plan p = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, h->b_out, T, mt_for(T), 1, T);
+    Plan p = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, h->b_out, T, mt_for(T), 1, T,
+                       tile_waves(mt_for(T)));
     mx = p.total > mx ? p.total : mx;
   }
   *bytes = mx;
@@ -348,7 +351,8 @@ static nl_status check_call(nl_handle h, const char *who, int verify, int32_t T,
   if (T > NL_MAX_T) return fail(NL_EUNSUPPORTED, "%s: T = %d exceeds %d", who, T, NL_MAX_T);
   if (!ws) return fail(NL_EINVAL, "%s: NULL workspace", who);
   if ((uintptr_t)ws & 255) return fail(NL_EINVAL, "%s: workspace must be 256-byte aligned", who);
-  *plan = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, h->b_out, T, mt_for(T), 1, T);
+  *plan = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, h->b_out, T, mt_for(T), 1, T,
+                       tile_waves(mt_for(T)));
   if (ws_bytes < plan->total)
     return fail(NL_EINVAL, "%s: workspace too small (%zu < %zu)", who, ws_bytes, plan->total);
   if (plan->n_ctr > kCtrLines)
@@ -571,7 +575,7 @@ static nl_status forward(nl_handle h, int verify, const void *x, int32_t T, floa
   const int n_fin = p.mode == kOutTwoSided ? finish_workgroups(T, h->d_out, p.sb_rows) : 0;
   hipEvent_t e0, e1;
   timing_slot((hipStream_t)stream, &e0, &e1);
-  HIP_OR_FAIL(launch_forward(f, verify ? h->bits : 0, p.mt, n_fin, (hipStream_t)stream, e0, e1));
+  HIP_OR_FAIL(launch_forward(f, verify ? h->bits : 0, p.mt, p.tw, n_fin, (hipStream_t)stream, e0, e1));
   return ok();
 }
 
@@ -663,14 +667,19 @@ extern "C" nl_status nested_linear_group_destroy(nl_group_handle g) {
 }
 
 static Plan group_plan(nl_group_handle g, int P, int T) {
-  return make_plan(g->d_out, g->n_tiles, g->n_chunks, g->has_sign_out, g->b_out, P, mt_for(T), g->n, T);
+  // short experts (K of at most two chunks): eight tile waves, half the
+  // workgroups; longer ones keep the deeper register ring of four
+  const int tw = T > kLocalTokens && g->n_chunks <= 2 ? 8 : tile_waves(mt_for(T));
+  return make_plan(g->d_out, g->n_tiles, g->n_chunks, g->has_sign_out, g->b_out, P, mt_for(T), g->n, T, tw);
 }
 
 extern "C" nl_status nested_linear_group_workspace_bytes(nl_group_handle g, int32_t P_max,
                                                          size_t *bytes) {
   if (!valid(g)) return fail(NL_EINVAL, "group_workspace_bytes: invalid handle");
   if (!bytes || P_max < 1) return fail(NL_EINVAL, "group_workspace_bytes: bad arguments");
-  *bytes = group_plan(g, P_max, NL_MAX_T).total;
+  // the two tile-wave counts give different split counts: the larger plan
+  const size_t a = group_plan(g, P_max, 1).total, b = group_plan(g, P_max, NL_MAX_T).total;
+  *bytes = a > b ? a : b;
   return ok();
 }
 
@@ -738,7 +747,7 @@ static nl_status grouped(nl_group_handle g, int verify, const int32_t *pair_toke
   const int n_fin = p.mode == kOutTwoSided ? finish_workgroups(P, g->d_out, p.sb_rows) : 0;
   hipEvent_t e0, e1;
   timing_slot((hipStream_t)stream, &e0, &e1);
-  HIP_OR_FAIL(launch_forward(f, verify ? g->bits : 0, p.mt, n_fin, (hipStream_t)stream, e0, e1));
+  HIP_OR_FAIL(launch_forward(f, verify ? g->bits : 0, p.mt, p.tw, n_fin, (hipStream_t)stream, e0, e1));
   return ok();
 }
 

@@ -125,7 +125,10 @@ struct FwdArgs {
 
 // Tile waves (16 output rows each) of a contraction workgroup, plus one x'
 // loader wave: eight for three or more 16-token tiles, whose chunks are long
-// enough that two tile waves per SIMD pay, else four.
+// enough that two tile waves per SIMD pay, else four.  Grouped calls (more
+// than kLocalTokens tokens) whose experts span at most two chunks of K take
+// eight at any tile count: their workgroups are short, and half as many of
+// them pay more than the register ring they give up.
 constexpr int tile_waves(int mt) { return mt >= 3 ? 8 : 4; }
 constexpr int wg_threads(int mt) { return 64 * (tile_waves(mt) + 1); }
 
@@ -139,7 +142,7 @@ hipError_t launch_gemm(const GemmArgs &a, int bits, int mt, int splits, hipStrea
 hipError_t launch_finish(const FinishArgs &a, hipStream_t s);
 // ev0/ev1 (optional): events that record the kernel's own start and end
 // (attached to the dispatch, not queued beside it).
-hipError_t launch_forward(const FwdArgs &f, int bits, int mt, int n_fin, hipStream_t s,
+hipError_t launch_forward(const FwdArgs &f, int bits, int mt, int tw, int n_fin, hipStream_t s,
                           hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 }  // namespace nl

@@ -648,10 +648,10 @@ struct WRegs {
 // accumulators leave room (one or two token tiles), deepest for the draft,
 // whose sets are a quarter the size.  The in-workgroup rotation (MT = 0)
 // holds its transform registers while the first sets are in flight.
-template <int BITS, int MT>
+template <int BITS, int MT, int TW>
 __host__ __device__ constexpr int ring_sets() {
   if constexpr (MT == 0) return BITS == 0 ? 3 : 2;
-  if constexpr (MT >= 3) return BITS == 0 ? 2 : 1;  // eight tile waves: 168 registers each
+  if constexpr (TW == 8) return BITS == 0 ? 2 : 1;  // eight tile waves: 168 registers each
   return BITS == 0 ? 4 : 3;
 }
 
@@ -698,7 +698,7 @@ __device__ __forceinline__ void publish_ready(uint32_t *ctr, int n_rot, int k, b
 }
 
 // MT = 0: local rotation mode (single launch only; rot describes x).
-template <int BITS, int MT, bool FUSED>
+template <int BITS, int MT, bool FUSED, int TW = tile_waves(MT)>
 __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, int split, char *smem,
                                               const Handover &hv, const RotInArgs &rot) {
   constexpr bool LOCAL = MT == 0;
@@ -707,7 +707,8 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
   constexpr int TR = LOCAL ? kLocalRows : Pl::TR, XG = LOCAL ? 4 : Pl::XG, NST = LOCAL ? 1 : Pl::NST;
   constexpr int NX = Pl::NX;
   static_assert(!LOCAL || FUSED, "local rotation runs in the single launch only");
-  constexpr int TW = tile_waves(MT), NT = wg_threads(MT), RB = 16 * TW;  // tile waves, threads, rows per block
+  static_assert(TW == 4 || (TW == 8 && MT > 0), "four tile waves, or eight outside the in-workgroup rotation");
+  constexpr int NT = 64 * (TW + 1), RB = 16 * TW;  // threads, rows per block
   __shared__ uint32_t s_flag;
 
   // (wave index read as a scalar so per-wave choices stay uniform branches)
@@ -891,7 +892,7 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
           // One token tile: the group's activations and sums are read first,
           // so their LDS latency passes under the unpacking below (more
           // tiles read theirs at the MFMAs: the registers would not fit).
-          constexpr int HA = MTC == 1 ? 1 : 0;
+          constexpr int HA = MTC == 1 && TW == 4 ? 1 : 0;
           half8 A[1][4];
           floatx4 xs[1];
           auto act = [&](int m, int s) -> half8 {
@@ -951,7 +952,7 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
     // compiler's waits on the weight registers stay counted; requests past
     // the split's last chunk fall outside the descriptors (zeros, no memory
     // access), and the last nchk % NS chunks are computed after the loop.
-    constexpr int NS = ring_sets<BITS, MT>();
+    constexpr int NS = ring_sets<BITS, MT, TW>();
     WRegs<BITS> w[NS];
     if constexpr (LOCAL) {
       // ---- x' of this K-range, rotated here (the rotation role's arithmetic):
@@ -1044,9 +1045,10 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
       __builtin_amdgcn_s_barrier();                         // stage 0 of x' ready
       asm volatile("" ::: "memory");
     }
-    if (!loader && MT >= 3) {
+    if (!loader && (MT >= 3 || NS == 1)) {
       // (three or more token tiles: a chunk's compute is long, so each set is
-      // refilled in one piece right after it is computed)
+      // refilled in one piece right after it is computed; a one-set ring
+      // has no other set to refill during the compute)
       int ci = 0;
 #pragma unroll 1
       for (; ci + NS - 1 < nchk; ci += NS) {
@@ -1275,8 +1277,8 @@ __global__ __launch_bounds__(256) void finish_kernel(const FinishArgs a) {
 // contract (each once all of x' is stored), the rest (two-sided only)
 // finish.  Every wait is on workgroups of lower index.
 // ===========================================================================
-template <int BITS, int MT>
-__global__ __launch_bounds__(wg_threads(MT)) void forward_kernel(const FwdArgs f) {
+template <int BITS, int MT, int TW>
+__global__ __launch_bounds__(64 * (TW + 1)) void forward_kernel(const FwdArgs f) {
   constexpr int kFwht = (4096 + 256) * 4;  // one workgroup FWHT area (bytes)
   constexpr int kPlan = MT == 0 ? LocalPlan::bytes : LdsPlan<BITS, (MT == 0 ? 1 : MT)>::bytes;
   constexpr int kLds = kPlan > 2 * kFwht ? kPlan : 2 * kFwht;
@@ -1319,7 +1321,7 @@ __global__ __launch_bounds__(wg_threads(MT)) void forward_kernel(const FwdArgs f
     }
     Handover hv = f.hv;
     hv.line = j & 7;
-    contract_body<BITS, MT, true>(f.g, e, rb, split, smem, hv, f.rot);
+    contract_body<BITS, MT, true, TW>(f.g, e, rb, split, smem, hv, f.rot);
     // A workgroup that waited on its ready line (thread 0 passed a barrier
     // after the loader's wait) counts itself on the line's exit counter; the
     // line's last one clears the line.  Idle experts neither wait nor count.
@@ -1411,38 +1413,42 @@ hipError_t launch_finish(const FinishArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BITS, int MT>
+template <int BITS, int MT, int TW>
 static void launch_forward_mt(const FwdArgs &f, dim3 grid, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   if (ev0)
-    hipExtLaunchKernelGGL(forward_kernel<BITS, MT>, grid, dim3(wg_threads(MT)), 0, s, ev0, ev1, 0, f);
+    hipExtLaunchKernelGGL(forward_kernel<BITS, MT, TW>, grid, dim3(64 * (TW + 1)), 0, s, ev0, ev1, 0, f);
   else
-    forward_kernel<BITS, MT><<<grid, wg_threads(MT), 0, s>>>(f);
+    forward_kernel<BITS, MT, TW><<<grid, 64 * (TW + 1), 0, s>>>(f);
 }
 
+// (mt, tw): four tile waves up to two token tiles (and always for the
+// in-workgroup rotation), eight from one token tile up.
 template <int BITS>
-static hipError_t launch_forward_bits(const FwdArgs &f, int mt, dim3 grid, hipStream_t s, hipEvent_t ev0,
+static hipError_t launch_forward_bits(const FwdArgs &f, int mt, int tw, dim3 grid, hipStream_t s, hipEvent_t ev0,
                                       hipEvent_t ev1) {
-  switch (mt) {
-    case 0: launch_forward_mt<BITS, 0>(f, grid, s, ev0, ev1); break;
-    case 1: launch_forward_mt<BITS, 1>(f, grid, s, ev0, ev1); break;
-    case 2: launch_forward_mt<BITS, 2>(f, grid, s, ev0, ev1); break;
-    case 3: launch_forward_mt<BITS, 3>(f, grid, s, ev0, ev1); break;
-    case 4: launch_forward_mt<BITS, 4>(f, grid, s, ev0, ev1); break;
+  switch (mt * 16 + tw) {
+    case 0 * 16 + 4: launch_forward_mt<BITS, 0, 4>(f, grid, s, ev0, ev1); break;
+    case 1 * 16 + 4: launch_forward_mt<BITS, 1, 4>(f, grid, s, ev0, ev1); break;
+    case 1 * 16 + 8: launch_forward_mt<BITS, 1, 8>(f, grid, s, ev0, ev1); break;
+    case 2 * 16 + 4: launch_forward_mt<BITS, 2, 4>(f, grid, s, ev0, ev1); break;
+    case 2 * 16 + 8: launch_forward_mt<BITS, 2, 8>(f, grid, s, ev0, ev1); break;
+    case 3 * 16 + 8: launch_forward_mt<BITS, 3, 8>(f, grid, s, ev0, ev1); break;
+    case 4 * 16 + 8: launch_forward_mt<BITS, 4, 8>(f, grid, s, ev0, ev1); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_forward(const FwdArgs &f, int bits, int mt, int n_fin, hipStream_t s, hipEvent_t ev0,
+hipError_t launch_forward(const FwdArgs &f, int bits, int mt, int tw, int n_fin, hipStream_t s, hipEvent_t ev0,
                           hipEvent_t ev1) {
   if (f.rot.SB < 512 || f.rot.SB > 4096) return hipErrorInvalidValue;
   if (f.hv.mode == kOutTwoSided && (f.fin.OB < 512 || f.fin.OB > 4096)) return hipErrorInvalidValue;
   const dim3 grid(f.n_rot + f.n_gemm + n_fin);
   switch (bits) {
-    case 0: return launch_forward_bits<0>(f, mt, grid, s, ev0, ev1);
-    case 6: return launch_forward_bits<6>(f, mt, grid, s, ev0, ev1);
-    case 7: return launch_forward_bits<7>(f, mt, grid, s, ev0, ev1);
-    case 8: return launch_forward_bits<8>(f, mt, grid, s, ev0, ev1);
+    case 0: return launch_forward_bits<0>(f, mt, tw, grid, s, ev0, ev1);
+    case 6: return launch_forward_bits<6>(f, mt, tw, grid, s, ev0, ev1);
+    case 7: return launch_forward_bits<7>(f, mt, tw, grid, s, ev0, ev1);
+    case 8: return launch_forward_bits<8>(f, mt, tw, grid, s, ev0, ev1);
     default: return hipErrorInvalidValue;
   }
 }
