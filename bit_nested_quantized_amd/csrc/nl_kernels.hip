@@ -958,8 +958,9 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
       // ---- x' of this K-range, rotated here (the rotation role's arithmetic):
       // tasks (row t, superblock of SB columns), 4096/SB per pass over the
       // first four waves; the fifth wave only keeps the barrier count.  The
-      // first pass's x loads go out before the weights, so waiting for them
-      // leaves the weight loads in flight.
+      // first pass's x lands before the weights are requested (behind the
+      // weight burst of every workgroup it would arrive later); the weight
+      // loads are then in flight during the transform.
       const RotInArgs &ra = rot;
       const int SB = ra.SB, TPS = SB >> 4;
       const bool idle = threadIdx.x >= 256;
@@ -1025,9 +1026,9 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
       };
       rload(0);
       fence();
+      wait_vm<0>();
       // the fifth wave issues the same loads past its descriptors' range
-      // (zeros, no memory access), so every wave counts the same loads and
-      // the wait for x above leaves the weights in flight
+      // (zeros, no memory access), so every wave counts the same loads
 #pragma unroll
       for (int k = 0; k < NS; ++k) loadw(w[k], (loader ? c_end : c_begin) + k);
       rproc();
