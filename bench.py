@@ -34,8 +34,8 @@ STEP_TS = [1, 4, 8, 16, 32]
 CASE_TS = [1, 4, 8, 16, 32, 64]
 BITS = 6
 HBM_PEAK_GBPS = 8000.0
-ROOFLINE_TS = (8, 16)   # verify launches of forward_kernel<6, 1> (one 16-token tile, rotation workgroups)
-ROOFLINE_KERNEL = "forward_kernel<6, 1>"
+ROOFLINE_TS = (8, 16)   # verify launches of forward_kernel<6, 1, 4> (one 16-token tile, rotation workgroups)
+ROOFLINE_KERNEL = "forward_kernel<6, 1, 4>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "forward_kernel_6bit_verify_T8_T16_proj7b8b_traffic.txt")
 
 
@@ -98,8 +98,8 @@ def moe_leg(nl, torch, synth, reps):
         off = np.concatenate([off, [off[-1] + MOE_T]]).astype(np.int32)
         P = len(pt)
         active = int(np.count_nonzero(np.diff(off)))
-        routes.append((torch.from_numpy(pt).cuda(), None, torch.from_numpy(off).cuda(), P, active))
-    Pmax = max(r[3] for r in routes)
+        routes.append((torch.from_numpy(pt).cuda(), torch.from_numpy(off).cuda(), P, active))
+    Pmax = max(r[2] for r in routes)
     ws = {k: torch.zeros(nl.nested_linear_group_workspace_bytes(g, Pmax), dtype=torch.uint8, device="cuda")
           for k, g in groups.items()}
     x = torch.from_numpy(synth.make_x(MOE_T, MOE_HIDDEN, cfg=4, idx=100).view(np.int16)).cuda()
@@ -114,7 +114,7 @@ def moe_leg(nl, torch, synth, reps):
         fn = nl.nested_linear_verify_grouped if verify else nl.nested_linear_draft_grouped
 
         def passes(s):
-            for pt, pd, off, P, _ in routes:
+            for pt, off, P, _ in routes:
                 fn(groups["gate"], pt, off, P, x, MOE_T, yg, ws["gate"], s)
                 fn(groups["up"], pt, off, P, x, MOE_T, yu, ws["up"], s)
                 fn(groups["down"], pt, off, P, h, MOE_T, yd, ws["down"], s)
@@ -138,11 +138,11 @@ def moe_leg(nl, torch, synth, reps):
         e1.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / (reps * MOE_ROUTINGS)
         per_expert = 3 * MOE_INTER * MOE_HIDDEN * synth.bytes_per_weight(MOE_BITS if verify else 0)
-        touched = sum(r[4] for r in routes) / MOE_ROUTINGS * per_expert
+        touched = sum(r[3] for r in routes) / MOE_ROUTINGS * per_expert
         out["verify" if verify else "draft"] = {"us_per_block": round(us, 2), "GBps": round(touched / us / 1e3, 1),
                                                 "frac_hbm_peak": round(touched / us / 1e3 / HBM_PEAK_GBPS, 3)}
         del g
-    out["active_experts_avg"] = round(sum(r[4] for r in routes) / MOE_ROUTINGS, 1)
+    out["active_experts_avg"] = round(sum(r[3] for r in routes) / MOE_ROUTINGS, 1)
     out["workload"] = (f"{MOE_EXPERTS} experts + 1 shared, hidden {MOE_HIDDEN}, expert intermediate {MOE_INTER}, "
                        f"top-{MOE_TOPK} of a {MOE_T}-token block (router correlation {MOE_RHO}), "
                        f"{MOE_BITS}-bit residual; gate, up, down: one grouped call each")
@@ -155,7 +155,7 @@ def moe_leg(nl, torch, synth, reps):
 
 
 def roofline_leg(nl, call, ncopy, stream, bpw):
-    """Roofline of the dominant kernel, forward_kernel<6, 1>: eager verify
+    """Roofline of the dominant kernel, forward_kernel<6, 1, 4>: eager verify
     launches at T = 8 and 16 over the four projections, each timed by a HIP
     event pair attached to its own dispatch (the library's timing hook), so
     a duration is the kernel's execution as the kernel trace reports it."""
@@ -220,7 +220,7 @@ def pmc_summary(fetch_dir, write_dir, out_path):
         return out
 
     def split(rs):
-        fwd = [v for k, v in rs if k.startswith("void nl::forward_kernel<6, 1>")]
+        fwd = [v for k, v in rs if k.startswith("void nl::forward_kernel<6, 1, 4>")]
         cpy = [v for k, v in rs if "elementwise" in k and "MulFunctor" in k]
         return fwd, cpy
 
@@ -233,7 +233,7 @@ def pmc_summary(fetch_dir, write_dir, out_path):
     kw = known / (sorted(w_cpy)[len(w_cpy) // 2] * 1024)
     fetch = sum(f_fwd) / len(f_fwd) * 1024 * kf
     write = sum(w_fwd) / len(w_fwd) * 1024 * kw
-    text = (f"HBM traffic of forward_kernel<6, 1> (verify, T = 8 and 16, 4096x4096, 1024x4096, 14336x4096,\n"
+    text = (f"HBM traffic of forward_kernel<6, 1, 4> (verify, T = 8 and 16, 4096x4096, 1024x4096, 14336x4096,\n"
             f"4096x14336, 2-bit base + 6-bit residual, one-sided)\n"
             f"commands:\n"
             f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -o p -- python3 bench.py --roofline-only\n"
