@@ -15,6 +15,8 @@ scales: 0.265625 B/weight draft, 1.03125 B/weight verify) over the step time.
 per_case gives the microseconds per pass over the four projections and the
 weight GB/s for T = 1, 4, 8, 16, 32 and 64 (graph-amortised), the
 launch-inclusive time of one eager call, and the two-sided form at T = 1, 16.
+decoder_layer sums the seven calls of one layer (q, k, v, o, gate, up, down)
+from those per-shape times; moe_block times one MoE block of grouped calls.
 Prints one JSON line on stdout; progress goes to stderr.
 """
 import argparse
@@ -34,6 +36,7 @@ STEP_TS = [1, 4, 8, 16, 32]
 CASE_TS = [1, 4, 8, 16, 32, 64]
 BITS = 6
 HBM_PEAK_GBPS = 8000.0
+LAYERS = 32             # decoder layers of the 7B/8B-class model
 ROOFLINE_TS = (8, 16)   # verify launches of forward_kernel<6, 1, 4> (one 16-token tile, rotation workgroups)
 ROOFLINE_KERNEL = "forward_kernel<6, 1, 4>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "forward_kernel_6bit_verify_T8_T16_proj7b8b_traffic.txt")
@@ -401,6 +404,18 @@ def main():
                              "frac_hbm_peak": round(tot_b / tot_us / 1e3 / HBM_PEAK_GBPS, 3), "shapes": shp}
             log(f"[bench] {key}: {tot_us:.1f} us per pass over the 4 projections, {tot_b / tot_us / 1e3:.0f} GB/s")
 
+    # ---- one decoder layer of the 7B/8B-class model: q, k, v, o, gate, up and
+    # down run as seven sequential calls of the four shapes above
+    layer = {"linears": "q, o: 4096x4096; k, v: 1024x4096; gate, up: 14336x4096; down: 4096x14336",
+             "layers": LAYERS, "us_per_layer": {}, "ms_per_model": {}}
+    for key, c in per_case.items():
+        sh = c["shapes"]
+        us = 2 * sh["q/o"]["us"] + 2 * sh["k/v"]["us"] + 2 * sh["gate/up"]["us"] + sh["down"]["us"]
+        layer["us_per_layer"][key] = round(us, 1)
+        layer["ms_per_model"][key] = round(us * LAYERS / 1e3, 2)
+    log(f"[bench] decoder layer, verify T=16: {layer['us_per_layer']['verify_T16']:.1f} us "
+        f"({layer['ms_per_model']['verify_T16']:.2f} ms for {LAYERS} layers)")
+
     # ---- launch-inclusive single calls (eager, one call between events), verify
     single = {}
     for T in (1, 16):
@@ -499,6 +514,7 @@ def main():
         "single_call": single,
         "two_sided": two_sided,
         "moe_block": moe,
+        "decoder_layer": layer,
         "stream_read_GBps_torch_sum": round(stream_gbps, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -422,6 +422,19 @@ def test_grouped_few_tokens(nl, torch_cuda, T, two):
         np.testing.assert_array_equal(a, b)
 
 
+@pytest.mark.parametrize("two", [False, True])
+def test_grouped_two_token_tiles_short_experts(nl, torch_cuda, two):
+    # 24 tokens, top-4 of 16 experts + shared, K of two chunks: experts hold
+    # up to 24 rows (two token tiles) and the workgroups run eight tile waves
+    experts, pt, off = make_moe(16, 384, 1024, 7, 24, 4, 0.5, two, cfg=77)
+    x = synth.make_x(24, 1024, cfg=77, idx=0)
+    assert max(np.diff(off)) > 16
+    for verify in (False, True):
+        a, b, _ = run_grouped(nl, torch_cuda, experts, pt, off, x, verify)
+        assert rel_err(a, oracle.forward_grouped(experts, pt, off, x, verify)) <= TOL
+        np.testing.assert_array_equal(a, b)
+
+
 def test_grouped_many_experts_few_active(nl, torch_cuda):
     # 600 experts (8 distinct weight sets, expert e holds set e % 8), rows
     # only at experts 3, 511, 512 and 598: the grid has one slot per pair at
