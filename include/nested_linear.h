@@ -120,8 +120,8 @@ nl_status nested_linear_workspace_bytes(nl_handle h, int32_t T_max, size_t *byte
  * its first weights), the last (two-sided form only) apply S_o H_o.
  * Errors: NL_EINVAL (NULL pointer, T < 1, x not 16-byte aligned, small or
  * misaligned ws, linear without a residual), NL_EUNSUPPORTED (T > 64, or d_out beyond what the
- * counter region serves: about 16000 row blocks of 64), NL_EHIP (launch
- * failure).
+ * counter region serves: about 16000 row blocks of 64 or 128 rows), NL_EHIP
+ * (launch failure).
  */
 nl_status nested_linear_verify(nl_handle h, const void *x_bf16, int32_t T, float *y,
                                void *ws, size_t ws_bytes, void *hip_stream);
