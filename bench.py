@@ -223,7 +223,7 @@ def pmc_summary(fetch_dir, write_dir, out_path):
         return out
 
     def split(rs):
-        fwd = [v for k, v in rs if k.startswith("void nl::forward_kernel<6, 1, 4>")]
+        fwd = [v for k, v in rs if k.startswith(f"void nl::{ROOFLINE_KERNEL}")]
         cpy = [v for k, v in rs if "elementwise" in k and "MulFunctor" in k]
         return fwd, cpy
 
@@ -236,7 +236,7 @@ def pmc_summary(fetch_dir, write_dir, out_path):
     kw = known / (sorted(w_cpy)[len(w_cpy) // 2] * 1024)
     fetch = sum(f_fwd) / len(f_fwd) * 1024 * kf
     write = sum(w_fwd) / len(w_fwd) * 1024 * kw
-    text = (f"HBM traffic of forward_kernel<6, 1, 4> (verify, T = 8 and 16, 4096x4096, 1024x4096, 14336x4096,\n"
+    text = (f"HBM traffic of {ROOFLINE_KERNEL} (verify, T = 8 and 16, 4096x4096, 1024x4096, 14336x4096,\n"
             f"4096x14336, 2-bit base + 6-bit residual, one-sided)\n"
             f"commands:\n"
             f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -o p -- python3 bench.py --roofline-only\n"
@@ -275,7 +275,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run it with --gpus 1)",
+        print("bench.py measures one GPU: the library has no multi-GPU path (run it with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
 
