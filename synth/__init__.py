@@ -31,6 +31,8 @@ at a time.  Stream ids: 0 sign_in, 1 sign_out, 2 base codes, 3 base scales,
 """
 from __future__ import annotations
 
+import sys
+
 import numpy as np
 
 SEED0 = 20261008
@@ -96,13 +98,20 @@ def pack_base(codes: np.ndarray) -> np.ndarray:
 
 def pack_resid(q: np.ndarray, bits: int) -> np.ndarray:
     """q int [d_out][d_in] in [-2^(b-1), 2^(b-1)-1] -> canonical
-    [d_out][G][16*b] bytes of LSB-first b-bit two's-complement fields."""
+    [d_out][G][16*b] bytes of LSB-first b-bit two's-complement fields.
+
+    Eight consecutive fields fill exactly b bytes: they are combined into one
+    little-endian 64-bit word whose low b bytes are the packed bytes."""
+    assert sys.byteorder == "little"
     d_out, d_in = q.shape
-    u = _pad_cols(q.astype(np.int64), d_in).reshape(d_out, groups(d_in), GROUP)
-    u = u & ((1 << bits) - 1)
-    bitarr = ((u[..., None] >> np.arange(bits)) & 1).astype(np.uint8)  # [.., 128, b]
-    bitarr = bitarr.reshape(d_out, groups(d_in), GROUP * bits)
-    return np.ascontiguousarray(np.packbits(bitarr, axis=-1, bitorder="little"))
+    g = groups(d_in)
+    u = _pad_cols(q.astype(np.int64), d_in).reshape(d_out, g, GROUP // 8, 8)
+    u = (u & ((1 << bits) - 1)).astype(np.uint64)
+    w = np.zeros(u.shape[:-1], np.uint64)
+    for i in range(8):
+        w |= u[..., i] << np.uint64(bits * i)
+    by = w[..., None].view(np.uint8).reshape(d_out, g, GROUP // 8, 8)[..., :bits]
+    return np.ascontiguousarray(by.reshape(d_out, g, 16 * bits))
 
 
 def make_signs(n: int, cfg: int, idx: int, stream: int) -> np.ndarray:
@@ -120,9 +129,15 @@ def make_base_codes(d_out: int, d_in: int, cfg: int, idx: int) -> np.ndarray:
 
 
 def make_resid_codes(d_out: int, d_in: int, bits: int, cfg: int, idx: int) -> np.ndarray:
+    """clip(rint(N(0, sigma_b))) drawn row-major; in row blocks (the same
+    stream as one draw) so the float temporaries stay small."""
     qm = qmax(bits)
-    v = rng(cfg, idx, STREAM_RESID).normal(0.0, resid_sigma(bits), size=(d_out, d_in))
-    return np.clip(np.rint(v), -qm, qm).astype(np.int8)
+    g = rng(cfg, idx, STREAM_RESID)
+    out = np.empty((d_out, d_in), np.int8)
+    for r in range(0, d_out, 4096):
+        v = g.normal(0.0, resid_sigma(bits), size=(min(4096, d_out - r), d_in))
+        out[r:r + v.shape[0]] = np.clip(np.rint(v), -qm, qm)
+    return out
 
 
 def make_linear(d_out: int, d_in: int, bits: int, cfg: int = 0, idx: int = 0,
