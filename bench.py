@@ -16,9 +16,10 @@ per_case gives the microseconds per pass over the four projections and the
 weight GB/s for T = 1, 4, 8, 16, 32 and 64 (graph-amortised), the
 launch-inclusive time of one eager call, and the two-sided form at T = 1, 16.
 decoder_layer sums the seven calls of one layer (q, k, v, o, gate, up, down)
-from those per-shape times; model_pass times the whole Llama-8B-shaped pass
-(7-bit, T = 16, lm_head included) as one graph; moe_block times one MoE block
-of grouped calls.
+from those per-shape times; model_pass times whole passes as one graph each:
+the Llama-8B-shaped one (7-bit, T = 16, lm_head included) and the 31B-class
+dense one (8-bit, 64 layers, draft at T = 1, verify at T = 64); moe_block times
+one MoE block of grouped calls.
 Prints one JSON line on stdout; progress goes to stderr.
 """
 import argparse
@@ -72,33 +73,39 @@ def stored_traffic(digest):
 
 
 MOE_EXPERTS, MOE_HIDDEN, MOE_INTER, MOE_TOPK, MOE_T, MOE_BITS, MOE_RHO = 256, 2048, 512, 8, 16, 8, 0.62
-MODEL_BITS, MODEL_T, MODEL_VOCAB = 7, 16, 128256   # Llama-8B-shaped verify pass
-MODEL_LAYER = [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096), (14336, 4096), (14336, 4096), (4096, 14336)]
+# whole-model passes: (name, layer shapes q k v o gate up down, layers, residual bits, verify T, draft T,
+# lm_head shape or None, synthetic config id)
+MODELS = [
+    ("llama8b_shaped", [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096), (14336, 4096), (14336, 4096),
+                        (4096, 14336)], 32, 7, 16, 16, (128256, 4096), 2),
+    ("dense31b_class", [(5120, 5120), (1024, 5120), (1024, 5120), (5120, 5120), (25600, 5120), (25600, 5120),
+                        (5120, 25600)], 64, 8, 64, 1, None, 3),
+]
 MOE_ROUTINGS = 8
 
 
-def model_leg(nl, torch, synth, reps):
-    """Verify (and draft) pass over every linear weight of a Llama-8B-shaped
-    model: 32 layers of q, k, v, o, gate, up, down plus the 128256x4096
-    lm_head, 7-bit residual, T = 16, captured as one graph of 225 calls.
-    Every linear owns its own device copy of its planes, made from one
-    synthetic linear per shape (values do not change the work); the lm_head
-    repeats the codes of a generated 4096-row block with per-row scales."""
+def model_leg(nl, torch, synth, reps, spec):
+    """Verify and draft passes over every linear weight of a dense model,
+    each captured as one graph: per layer q, k, v, o, gate, up, down, then
+    the lm_head if there is one.  Every linear owns its own device copy of
+    its planes, made from one synthetic linear per shape (values do not
+    change the work); an lm_head repeats the codes of a generated 4096-row
+    block with per-row scales."""
     import numpy as np
+    name, layer, n_layers, bits, t_verify, t_draft, head, cfg = spec
 
     def make(o, i, idx):
-        if o <= 8192:
-            return synth.make_linear(o, i, MODEL_BITS, cfg=2, idx=idx, two_sided=False)
-        lin = dict(synth.make_linear(4096, i, MODEL_BITS, cfg=2, idx=idx, two_sided=False))
-        reps_ = -(-o // 4096)
+        if o <= 2 * 4096 or (o, i) != head:
+            return synth.make_linear(o, i, bits, cfg=cfg, idx=idx, two_sided=False)
+        lin = dict(synth.make_linear(4096, i, bits, cfg=cfg, idx=idx, two_sided=False))
         lin["d_out"] = o
         for k in ("base_codes", "resid_codes"):
-            lin[k] = np.ascontiguousarray(np.tile(lin[k], (reps_, 1, 1))[:o])
-        lin["base_scales"] = synth.make_scales(o, i, 2, idx, synth.STREAM_BASE_SCALE)
-        lin["resid_scales"] = synth.make_scales(o, i, 2, idx, synth.STREAM_RESID_SCALE)
+            lin[k] = np.ascontiguousarray(np.tile(lin[k], (-(-o // 4096), 1, 1))[:o])
+        lin["base_scales"] = synth.make_scales(o, i, cfg, idx, synth.STREAM_BASE_SCALE)
+        lin["resid_scales"] = synth.make_scales(o, i, cfg, idx, synth.STREAM_RESID_SCALE)
         return lin
 
-    shapes = sorted(set(MODEL_LAYER)) + [(MODEL_VOCAB, 4096)]
+    shapes = sorted(set(layer) | ({head} if head else set()))
     dev = {}
     for si, (o, i) in enumerate(shapes):
         lin = make(o, i, si)
@@ -107,22 +114,30 @@ def model_leg(nl, torch, synth, reps):
             for key, dt in [("base_codes", np.uint8), ("base_scales", np.int16), ("resid_codes", np.uint8),
                             ("resid_scales", np.int16), ("sign_in", np.int8), ("sign_out", np.int8)]})
         del lin
-    seq = [(o, i) for _ in range(LAYERS) for (o, i) in MODEL_LAYER] + [(MODEL_VOCAB, 4096)]
-    handles = [nl.nested_linear_create(o, i, MODEL_BITS, levels=dev[(o, i)][0], **dev[(o, i)][1]) for o, i in seq]
+    seq = [s_ for _ in range(n_layers) for s_ in layer] + ([head] if head else [])
+    handles = [nl.nested_linear_create(o, i, bits, levels=dev[(o, i)][0], **dev[(o, i)][1]) for o, i in seq]
     del dev
-    ws = torch.zeros(max(nl.nested_linear_workspace_bytes(h, MODEL_T) for h in handles[:len(MODEL_LAYER)] + handles[-1:]),
+    t_max = max(t_verify, t_draft)
+    first = {}
+    for h, sh in zip(handles, seq):
+        first.setdefault(sh, h)
+    ws = torch.zeros(max(nl.nested_linear_workspace_bytes(h, t_max) for h in first.values()),
                      dtype=torch.uint8, device="cuda")
-    xs = {i: torch.from_numpy(synth.make_x(MODEL_T, i, cfg=2, idx=200 + i).view(np.int16)).cuda() for i in (4096, 14336)}
-    ys = {o: torch.empty((MODEL_T, o), dtype=torch.float32, device="cuda") for o, _ in shapes}
-    out = {"linears": len(seq), "layers": LAYERS,
-           "workload": f"Llama-8B-shaped: {LAYERS} x (q, k, v, o, gate, up, down) + lm_head {MODEL_VOCAB}x4096, "
-                       f"{MODEL_BITS}-bit residual, T = {MODEL_T}, one graph per pass"}
+    xs = {i: torch.from_numpy(synth.make_x(t_max, i, cfg=cfg, idx=200 + i).view(np.int16)).cuda()
+          for i in sorted({i for _, i in shapes})}
+    ys = {o: torch.empty((t_max, o), dtype=torch.float32, device="cuda") for o, _ in shapes}
+    out = {"linears": len(seq), "layers": n_layers,
+           "workload": f"{name}: {n_layers} layers of q, k, v, o, gate, up, down ("
+                       + ", ".join(f"{o}x{i}" for o, i in layer) + ")"
+                       + (f" + lm_head {head[0]}x{head[1]}" if head else "")
+                       + f", {bits}-bit residual; verify at T = {t_verify}, draft at T = {t_draft}; one graph per pass"}
     for verify in (True, False):
         fn = nl.nested_linear_verify if verify else nl.nested_linear_draft
+        T = t_verify if verify else t_draft
 
         def passes(st):
             for h, (o, i) in zip(handles, seq):
-                fn(h, xs[i], MODEL_T, ys[o], ws, st)
+                fn(h, xs[i], T, ys[o], ws, st)
 
         g = torch.cuda.CUDAGraph()
         st = torch.cuda.Stream()
@@ -142,13 +157,14 @@ def model_leg(nl, torch, synth, reps):
         e1.record()
         e1.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
-        wb = sum(o * i for o, i in seq) * synth.bytes_per_weight(MODEL_BITS if verify else 0)
-        out["verify" if verify else "draft"] = {"us_per_pass": round(us, 1), "weight_bytes": int(wb),
+        wb = sum(o * i for o, i in seq) * synth.bytes_per_weight(bits if verify else 0)
+        out["verify" if verify else "draft"] = {"T": T, "us_per_pass": round(us, 1), "weight_bytes": int(wb),
                                                 "GBps": round(wb / us / 1e3, 1),
                                                 "frac_hbm_peak": round(wb / us / 1e3 / HBM_PEAK_GBPS, 3)}
         del g
     for h in handles:
         nl.nested_linear_destroy(h)
+    torch.cuda.empty_cache()
     return out
 
 
@@ -546,10 +562,14 @@ def main():
     # ---- the MoE block (grouped calls)
     moe = moe_leg(nl, torch, synth, args.reps)
 
-    # ---- the whole Llama-8B-shaped pass (one graph of 225 calls)
-    model = model_leg(nl, torch, synth, max(3, args.reps // 4))
-    log(f"[bench] model pass: verify {model['verify']['us_per_pass']:.0f} us "
-        f"({model['verify']['GBps']:.0f} GB/s), draft {model['draft']['us_per_pass']:.0f} us")
+    # ---- whole dense-model passes (one graph per pass)
+    model = {}
+    for spec in MODELS:
+        m = model_leg(nl, torch, synth, 3, spec)
+        model[spec[0]] = m
+        log(f"[bench] {spec[0]} pass: verify T={m['verify']['T']} {m['verify']['us_per_pass']:.0f} us "
+            f"({m['verify']['GBps']:.0f} GB/s), draft T={m['draft']['T']} {m['draft']['us_per_pass']:.0f} us "
+            f"({m['draft']['GBps']:.0f} GB/s)")
 
     # ---- streaming reference on the same GPU (torch reduction over 2 GiB)
     big = torch.ones(2 ** 29, dtype=torch.float32, device=dev)
