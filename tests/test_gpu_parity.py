@@ -422,11 +422,13 @@ def test_grouped_few_tokens(nl, torch_cuda, T, two):
         np.testing.assert_array_equal(a, b)
 
 
+@pytest.mark.parametrize("d_out", [384, 100])
 @pytest.mark.parametrize("two", [False, True])
-def test_grouped_two_token_tiles_short_experts(nl, torch_cuda, two):
+def test_grouped_two_token_tiles_short_experts(nl, torch_cuda, two, d_out):
     # 24 tokens, top-4 of 16 experts + shared, K of two chunks: experts hold
     # up to 24 rows (two token tiles) and the workgroups run eight tile waves
-    experts, pt, off = make_moe(16, 384, 1024, 7, 24, 4, 0.5, two, cfg=77)
+    # (100 rows: a ragged last tile and idle tile waves)
+    experts, pt, off = make_moe(16, d_out, 1024, 7, 24, 4, 0.5, two, cfg=77)
     x = synth.make_x(24, 1024, cfg=77, idx=0)
     assert max(np.diff(off)) > 16
     for verify in (False, True):
