@@ -27,7 +27,8 @@ keeps the full-size byte block with the unused fields zero.
 Seeds: every array is a pure function of SeedSequence([20261008, cfg,
 linear_idx, stream]) with numpy's PCG64, so the host regenerates one linear
 at a time.  Stream ids: 0 sign_in, 1 sign_out, 2 base codes, 3 base scales,
-4 residual codes, 5 residual scales, 6 x, 7 router logits.
+4 residual codes, 5 residual scales, 6 x, 7 router logits, 8 dense weights
+(the encoder's input).
 """
 from __future__ import annotations
 
@@ -45,6 +46,7 @@ LEVELS = np.array([-1.5104, -0.4528, 0.4528, 1.5104], dtype=np.float32)
 
 STREAM_SIGN_IN, STREAM_SIGN_OUT, STREAM_BASE, STREAM_BASE_SCALE = 0, 1, 2, 3
 STREAM_RESID, STREAM_RESID_SCALE, STREAM_X, STREAM_ROUTER = 4, 5, 6, 7
+STREAM_DENSE = 8
 
 
 def rng(cfg: int, linear_idx: int, stream: int) -> np.random.Generator:
@@ -137,6 +139,25 @@ def make_resid_codes(d_out: int, d_in: int, bits: int, cfg: int, idx: int) -> np
     for r in range(0, d_out, 4096):
         v = g.normal(0.0, resid_sigma(bits), size=(min(4096, d_out - r), d_in))
         out[r:r + v.shape[0]] = np.clip(np.rint(v), -qm, qm)
+    return out
+
+
+def make_dense_weights(d_out: int, d_in: int, cfg: int = 0, idx: int = 0, sigma: float = 0.02,
+                       outlier_frac: float = 0.01, outlier_gain: float = 8.0) -> np.ndarray:
+    """A dense fp32 weight matrix [d_out][d_in] shaped like a trained
+    Linear's: N(0, sigma^2) entries, a lognormal gain per output row (log-sd
+    0.3) and a few input columns (outlier_frac of them, at least one) scaled
+    by outlier_gain, the outlier channels the rotation is meant to spread.
+    Drawn in row blocks of 4096 from one stream."""
+    g = rng(cfg, idx, STREAM_DENSE)
+    row_gain = np.exp(g.normal(0.0, 0.3, size=d_out)) * sigma
+    col_gain = np.ones(d_in)
+    col_gain[g.choice(d_in, max(1, int(d_in * outlier_frac)), replace=False)] = outlier_gain
+    out = np.empty((d_out, d_in), np.float32)
+    for r in range(0, d_out, 4096):
+        n = min(4096, d_out - r)
+        z = g.standard_normal(size=(n, d_in), dtype=np.float32)
+        out[r:r + n] = z * row_gain[r:r + n, None].astype(np.float32) * col_gain[None, :].astype(np.float32)
     return out
 
 
