@@ -30,6 +30,8 @@ EXPORTS = (
     "nested_linear_verify_grouped", "nested_linear_draft_grouped", "nested_linear_decode",
     "nested_linear_info", "nested_linear_timing_begin", "nested_linear_timing_end",
     "nested_linear_last_error",
+    "nested_encode_rotate", "nested_encode_quantize", "nested_encode_workspace_bytes", "nested_encode",
+    "nested_encode_normalize", "nested_encode_fit_workspace_bytes", "nested_encode_fit_levels",
 )
 
 
@@ -46,6 +48,15 @@ class nl_desc(ctypes.Structure):
         ("resid_codes", ctypes.c_void_p), ("resid_scales", ctypes.c_void_p),
         ("sign_in", ctypes.c_void_p), ("sign_out", ctypes.c_void_p),
         ("levels", ctypes.c_float * 4),
+    ]
+
+
+class nl_codes(ctypes.Structure):
+    _fields_ = [
+        ("d_out", ctypes.c_int32), ("d_in", ctypes.c_int32), ("residual_bits", ctypes.c_int32),
+        ("levels", ctypes.c_float * 4),
+        ("base_codes", ctypes.c_void_p), ("base_scales", ctypes.c_void_p),
+        ("resid_codes", ctypes.c_void_p), ("resid_scales", ctypes.c_void_p),
     ]
 
 
@@ -77,6 +88,13 @@ def lib() -> ctypes.CDLL:
             "nested_linear_info": [P] + [ctypes.POINTER(i32)] * 5 + [ctypes.POINTER(ctypes.c_float)],
             "nested_linear_timing_begin": [i32],
             "nested_linear_timing_end": [ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(i32)],
+            "nested_encode_rotate": [i32, i32, P, P, P, P, P],
+            "nested_encode_quantize": [P, ctypes.POINTER(nl_codes), P],
+            "nested_encode_workspace_bytes": [i32, i32, i32, ctypes.POINTER(sz)],
+            "nested_encode": [P, P, P, ctypes.POINTER(nl_codes), P, sz, P],
+            "nested_encode_normalize": [i32, i32, P, P, P],
+            "nested_encode_fit_workspace_bytes": [ctypes.c_int64, ctypes.POINTER(sz)],
+            "nested_encode_fit_levels": [P, ctypes.c_int64, i32, ctypes.POINTER(ctypes.c_double), P, sz, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -202,6 +220,93 @@ def nested_linear_info(h) -> dict:
     _check(lib().nested_linear_info(h, *[ctypes.byref(x) for x in v], ctypes.byref(e)))
     return {"d_out": v[0].value, "d_in": v[1].value, "bits": v[2].value, "block_in": v[3].value,
             "block_out": v[4].value, "level_rel_err": e.value}
+
+
+# --- encoder (include/nested_encode.h) ----------------------------------------
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def nested_encode_rotate(d_out: int, d_in: int, w, sign_in, sign_out, wt, stream=None):
+    _check(lib().nested_encode_rotate(int(d_out), int(d_in), _ptr(w), _ptr(sign_in), _ptr(sign_out),
+                                      _ptr(wt), _stream(stream)))
+
+
+def nested_encode_quantize(wt, codes: nl_codes, stream=None):
+    _check(lib().nested_encode_quantize(_ptr(wt), ctypes.byref(codes), _stream(stream)))
+
+
+def nested_encode_workspace_bytes(d_out: int, d_in: int, two_sided: bool) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().nested_encode_workspace_bytes(int(d_out), int(d_in), int(bool(two_sided)), ctypes.byref(n)))
+    return n.value
+
+
+def nested_encode(w, sign_in, sign_out, codes: nl_codes, ws=None, stream=None):
+    _check(lib().nested_encode(_ptr(w), _ptr(sign_in), _ptr(sign_out), ctypes.byref(codes), _ptr(ws),
+                               _nbytes(ws), _stream(stream)))
+
+
+def nested_encode_normalize(d_out: int, d_in: int, wt, v, stream=None):
+    _check(lib().nested_encode_normalize(int(d_out), int(d_in), _ptr(wt), _ptr(v), _stream(stream)))
+
+
+def nested_encode_fit_workspace_bytes(n: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().nested_encode_fit_workspace_bytes(int(n), ctypes.byref(b)))
+    return b.value
+
+
+def nested_encode_fit_levels(v, n: int, iters: int, ws, stream=None) -> list:
+    """Returns the four fitted levels (host floats, fp64); synchronises."""
+    out = (ctypes.c_double * 4)()
+    _check(lib().nested_encode_fit_levels(_ptr(v), int(n), int(iters), out, _ptr(ws), _nbytes(ws),
+                                          _stream(stream)))
+    return [float(x) for x in out]
+
+
+class Codes:
+    """Device arrays of one linear's canonical planes, written by the encoder
+    (torch uint8 / int16 tensors), and the nl_codes descriptor that points at
+    them."""
+
+    def __init__(self, d_out: int, d_in: int, bits: int, levels, device="cuda"):
+        import torch
+        G = d_in // 128
+        self.d_out, self.d_in, self.bits = d_out, d_in, bits
+        self.levels = [float(x) for x in levels]
+        self.base_codes = torch.empty((d_out, G, 32), dtype=torch.uint8, device=device)
+        self.base_scales = torch.empty((d_out, G), dtype=torch.int16, device=device)
+        self.resid_codes = torch.empty((d_out, G, 16 * bits), dtype=torch.uint8, device=device) if bits else None
+        self.resid_scales = torch.empty((d_out, G), dtype=torch.int16, device=device) if bits else None
+        self.desc = nl_codes(int(d_out), int(d_in), int(bits), (ctypes.c_float * 4)(*self.levels),
+                             _ptr(self.base_codes), _ptr(self.base_scales), _ptr(self.resid_codes),
+                             _ptr(self.resid_scales))
+
+    def host(self) -> dict:
+        """The canonical dict (numpy) that synth.make_linear produces."""
+        import numpy as np
+
+        def h(t, dt):
+            return None if t is None else t.cpu().numpy().view(dt)
+
+        return {"d_out": self.d_out, "d_in": self.d_in, "bits": self.bits,
+                "levels": np.array(self.levels, np.float32),
+                "base_codes": h(self.base_codes, np.uint8), "base_scales": h(self.base_scales, np.uint16),
+                "resid_codes": h(self.resid_codes, np.uint8), "resid_scales": h(self.resid_scales, np.uint16)}
+
+
+def encode(w, sign_in, sign_out, bits: int, levels, stream=None) -> Codes:
+    """Encode a dense fp32 device matrix w [d_out][d_in] (nested_encode);
+    the two-sided form gets its workspace from torch."""
+    import torch
+    d_out, d_in = w.shape
+    c = Codes(d_out, d_in, bits, levels, device=w.device)
+    nws = nested_encode_workspace_bytes(d_out, d_in, sign_out is not None)
+    ws = torch.empty(nws, dtype=torch.uint8, device=w.device) if nws else None
+    nested_encode(w, sign_in, sign_out, c.desc, ws, stream)
+    return c
 
 
 class Linear:

@@ -37,6 +37,16 @@ static nl_status ok() {
   return NL_OK;
 }
 
+// The encoder's translation unit reports its errors through the same
+// per-thread message (NL_OK clears it).
+namespace nl {
+__attribute__((visibility("hidden"))) nl_status api_error(nl_status st, const char *msg) {
+  if (st == NL_OK) g_err.clear();
+  else g_err = msg;
+  return st;
+}
+}  // namespace nl
+
 #define HIP_OR_FAIL(expr)                                                              \
   do {                                                                                 \
     hipError_t e_ = (expr);                                                            \
