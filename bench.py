@@ -43,25 +43,32 @@ LAYERS = 32             # decoder layers of the 7B/8B-class model
 ROOFLINE_TS = (8, 16)   # verify launches of forward_kernel<6, 1, 4> (one 16-token tile, rotation workgroups)
 ROOFLINE_KERNEL = "forward_kernel<6, 1, 4>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "forward_kernel_6bit_verify_T8_T16_proj7b8b_traffic.txt")
+ENC_BITS = 7            # the encoder leg writes 7-bit residuals (the post's bf16-noise-floor width)
+ENC_KERNEL = "tile_kernel<0, 7>"
+ENC_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encoder_tile_kernel_7bit_fused_proj7b8b_traffic.txt")
+FIT_ROWS = 512          # 512 x 4096 = 2^21 samples, the post's ~2M
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_digest():
+def kernel_source_digest(files=("nl_kernels.hip", "nl_kernels.h", "nl_layout.h")):
     """Digest of the kernel sources, to tie stored counter readings to them."""
     h = hashlib.sha256()
-    for f in ("nl_kernels.hip", "nl_kernels.h", "nl_layout.h"):
+    for f in files:
         with open(os.path.join(ROOT, "bit_nested_quantized_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic(digest):
+ENC_SOURCES = ("nl_encode.hip",)
+
+
+def stored_traffic(digest, path=None):
     """HBM bytes per launch of the roofline kernel from the committed counter
     summary, when it was taken on the current kernel sources."""
-    path = TRAFFIC_FILE
+    path = TRAFFIC_FILE if path is None else path
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -288,6 +295,110 @@ def roofline_leg(nl, call, ncopy, stream, bpw):
             "kernel_source_digest": digest}
 
 
+def encoder_bytes_per_weight(bits):
+    """Algorithmic HBM bytes per weight of the fused one-sided encode: the
+    fp32 weight read; the 2-bit base planes, the b-bit residual and two fp16
+    scales per 128 weights written (the d_in sign bytes are left out)."""
+    return 4.0 + (2 + bits) / 8.0 + 4.0 / 128
+
+
+def encoder_leg(nl, torch, synth, reps, cpu_seconds=0.0):
+    """The round-to-nearest encoder on the 7B/8B-class projections (dense
+    fp32 W -> 2-bit base + 7-bit residual planes, one-sided: one fused launch
+    per linear, back to back on the stream between two events), the
+    two-sided form on the 14336x4096 projection, and the level fit on 2^21
+    normalised rotated weights (quantile start + 60 Lloyd iterations)."""
+    import numpy as np
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    per, tot_b, tot_us = {}, 0.0, 0.0
+    keep = None
+    for si, (name, o, i) in enumerate(SHAPES):
+        Wh = synth.make_dense_weights(o, i, cfg=30, idx=si)
+        sh = synth.make_signs(i, 30, si, synth.STREAM_SIGN_IN)
+        W, sg = torch.from_numpy(Wh).cuda(), torch.from_numpy(sh).cuda()
+        c = nl.Codes(o, i, ENC_BITS, synth.LEVELS)
+        for _ in range(2):
+            nl.nested_encode(W, sg, None, c.desc)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            nl.nested_encode(W, sg, None, c.desc)
+        e1.record()
+        e1.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        b = o * i * encoder_bytes_per_weight(ENC_BITS)
+        per[name] = {"shape": [o, i], "us": round(us, 1), "GBps": round(b / us / 1e3, 1)}
+        tot_b += b
+        tot_us += us
+        if name == "gate/up":
+            keep = (Wh, sh, W, sg, o, i)
+        del W, c
+        log(f"[bench] encode {name} {o}x{i}: {us:.1f} us, {b / us / 1e3:.0f} GB/s")
+    layer_us = 2 * per["q/o"]["us"] + 2 * per["k/v"]["us"] + 2 * per["gate/up"]["us"] + per["down"]["us"]
+    Wh, sh, W, sg, o, i = keep
+    # two-sided form: input-side tiles into an fp64 workspace, column passes, quantise
+    so = torch.from_numpy(synth.make_signs(o, 30, 2, synth.STREAM_SIGN_OUT)).cuda()
+    c = nl.Codes(o, i, ENC_BITS, synth.LEVELS)
+    ws = torch.empty(nl.nested_encode_workspace_bytes(o, i, True), dtype=torch.uint8, device="cuda")
+    nl.nested_encode(W, sg, so, c.desc, ws)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(max(1, reps // 4)):
+        nl.nested_encode(W, sg, so, c.desc, ws)
+    e1.record()
+    e1.synchronize()
+    two_us = e0.elapsed_time(e1) * 1e3 / max(1, reps // 4)
+    del ws, c
+    # level fit on 2^21 samples
+    wt = torch.empty((FIT_ROWS, i), dtype=torch.float64, device="cuda")
+    nl.nested_encode_rotate(FIT_ROWS, i, W[:FIT_ROWS].contiguous(), sg, None, wt)
+    v = torch.empty_like(wt)
+    nl.nested_encode_normalize(FIT_ROWS, i, wt, v)
+    fws = torch.empty(nl.nested_encode_fit_workspace_bytes(v.numel()), dtype=torch.uint8, device="cuda")
+    fit = {}
+    for iters in (0, 60):
+        nl.nested_encode_fit_levels(v, v.numel(), iters, fws)
+        t0 = time.perf_counter()
+        for _ in range(3):
+            lev = nl.nested_encode_fit_levels(v, v.numel(), iters, fws)
+        fit[iters] = ((time.perf_counter() - t0) / 3 * 1e3, lev)
+    del wt, v, fws
+    achieved = tot_b / tot_us / 1e3
+    out = {
+        "per_linear": per, "decoder_layer_us": round(layer_us, 1),
+        "model_32_layers_ms": round(LAYERS * layer_us / 1e3, 2),
+        "two_sided_gate_up_us": round(two_us, 1),
+        "fit_levels_ms": {"samples": FIT_ROWS * i, "quantile_start_only": round(fit[0][0], 2),
+                          "quantile_start_plus_60_iterations": round(fit[60][0], 2),
+                          "levels": [round(x, 5) for x in fit[60][1]]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "kernel": ENC_KERNEL + " (one-sided fused encode, the four projections)",
+                     "bytes_per_weight": encoder_bytes_per_weight(ENC_BITS),
+                     "avg_launch_us": round(tot_us / len(SHAPES), 2),
+                     "avg_algorithmic_bytes": int(tot_b / len(SHAPES)),
+                     "timing": "HIP events around back-to-back launches on the stream",
+                     "kernel_source_digest": kernel_source_digest(ENC_SOURCES)},
+    }
+    tr = stored_traffic(kernel_source_digest(ENC_SOURCES), ENC_TRAFFIC_FILE)
+    out["roofline"]["traffic"] = None if tr is None else round(tr)
+    if cpu_seconds > 0:
+        import oracle.encode as oenc
+        rows, t0, n = 64, time.time(), 0
+        while True:
+            r0 = (n * rows) % o
+            oenc.encode(Wh[r0:r0 + rows], sh, None, ENC_BITS, synth.LEVELS)
+            n += 1
+            if time.time() - t0 >= cpu_seconds:
+                break
+        dt = time.time() - t0
+        out["cpu_baseline"] = {"value": round(n * rows * i * encoder_bytes_per_weight(ENC_BITS) / dt / 1e9, 4),
+                               "unit": "GB/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{n} blocks of {rows} rows of the 14336x4096 projection in {dt:.1f} s"}
+    return out
+
+
 COPY_FLOATS = 64 << 20  # 256 MiB read + 256 MiB written per copy
 
 
@@ -302,10 +413,19 @@ def copy_calibration(torch):
             "write_bytes": COPY_FLOATS * 4, "launches": 3}
 
 
-def pmc_summary(fetch_dir, write_dir, out_path):
+ROOFLINE_TITLE = ("verify, T = 8 and 16, 4096x4096, 1024x4096, 14336x4096,\n"
+                  "4096x14336, 2-bit base + 6-bit residual, one-sided")
+ENC_TITLE = ("one-sided fused encode of dense fp32 4096x4096, 1024x4096, 14336x4096,\n"
+             "4096x14336 into 2-bit base + 7-bit residual planes")
+
+
+def pmc_summary(fetch_dir, write_dir, out_path, kernel=ROOFLINE_KERNEL, prefix="void nl::",
+                title=ROOFLINE_TITLE, flag="--roofline-only", digest=None):
     """Per-launch HBM traffic of the roofline kernel from two rocprofv3 --pmc
     runs of `bench.py --roofline-only` (FETCH_SIZE, then WRITE_SIZE), each
-    counter scaled by what it reads for the calibration copy."""
+    counter scaled by what it reads for the calibration copy.  The encoder's
+    kernel is summarised the same way from runs of `bench.py --encoder-only`
+    (any kernel-name prefix)."""
     import csv
     import glob
 
@@ -318,7 +438,7 @@ def pmc_summary(fetch_dir, write_dir, out_path):
         return out
 
     def split(rs):
-        fwd = [v for k, v in rs if k.startswith(f"void nl::{ROOFLINE_KERNEL}")]
+        fwd = [v for k, v in rs if (k.startswith(prefix + kernel) if prefix else kernel in k)]
         cpy = [v for k, v in rs if "elementwise" in k and "MulFunctor" in k]
         return fwd, cpy
 
@@ -331,12 +451,12 @@ def pmc_summary(fetch_dir, write_dir, out_path):
     kw = known / (sorted(w_cpy)[len(w_cpy) // 2] * 1024)
     fetch = sum(f_fwd) / len(f_fwd) * 1024 * kf
     write = sum(w_fwd) / len(w_fwd) * 1024 * kw
-    text = (f"HBM traffic of {ROOFLINE_KERNEL} (verify, T = 8 and 16, 4096x4096, 1024x4096, 14336x4096,\n"
-            f"4096x14336, 2-bit base + 6-bit residual, one-sided)\n"
+    summ = "--pmc-summary" if flag == "--roofline-only" else "--pmc-summary-encoder"
+    text = (f"HBM traffic of {kernel} ({title})\n"
             f"commands:\n"
-            f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -o p -- python3 bench.py --roofline-only\n"
-            f"  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -o p -- python3 bench.py --roofline-only\n"
-            f"  python3 bench.py --pmc-summary <fetch_dir> <write_dir>\n"
+            f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -o p -- python3 bench.py {flag}\n"
+            f"  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -o p -- python3 bench.py {flag}\n"
+            f"  python3 bench.py {summ} <fetch_dir> <write_dir>\n"
             f"launches: {len(f_fwd)} (fetch run), {len(w_fwd)} (write run)\n"
             f"FETCH_SIZE per launch (raw): {sum(f_fwd) / len(f_fwd):.1f} KiB\n"
             f"WRITE_SIZE per launch (raw): {sum(w_fwd) / len(w_fwd):.1f} KiB\n"
@@ -345,7 +465,7 @@ def pmc_summary(fetch_dir, write_dir, out_path):
             f"hbm read bytes per launch: {fetch:.0f}\n"
             f"hbm write bytes per launch: {write:.0f}\n"
             f"hbm bytes per launch: {fetch + write:.0f}\n"
-            f"kernel source digest: {kernel_source_digest()}\n")
+            f"kernel source digest: {kernel_source_digest() if digest is None else digest}\n")
     with open(out_path, "w") as fh:
         fh.write(text)
     print(text, end="")
@@ -364,9 +484,17 @@ def main():
                     help="run only the roofline launches and the counter calibration copy (for rocprofv3)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary from two rocprofv3 --pmc runs of --roofline-only")
+    ap.add_argument("--encoder-only", action="store_true",
+                    help="run only the encoder leg and the counter calibration copy (for rocprofv3)")
+    ap.add_argument("--pmc-summary-encoder", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the encoder's traffic summary from two rocprofv3 --pmc runs of --encoder-only")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary, TRAFFIC_FILE)
+        return
+    if args.pmc_summary_encoder:
+        pmc_summary(*args.pmc_summary_encoder, ENC_TRAFFIC_FILE, kernel=ENC_KERNEL, prefix="", title=ENC_TITLE,
+                    flag="--encoder-only", digest=kernel_source_digest(ENC_SOURCES))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -384,6 +512,12 @@ def main():
     nl.lib()
     dev = "cuda"
     torch.cuda.set_device(0)
+
+    if args.encoder_only:
+        enc = encoder_leg(nl, torch, synth, args.reps)
+        calib = copy_calibration(torch)
+        print(json.dumps({"encoder": enc, "copy_calibration": calib}), flush=True)
+        return
 
     def bpw(verify):
         return synth.bytes_per_weight(BITS if verify else 0)
@@ -571,6 +705,9 @@ def main():
             f"({m['verify']['GBps']:.0f} GB/s), draft T={m['draft']['T']} {m['draft']['us_per_pass']:.0f} us "
             f"({m['draft']['GBps']:.0f} GB/s)")
 
+    # ---- the offline encoder (dense W -> planes) and the level fit
+    encoder = encoder_leg(nl, torch, synth, args.reps, cpu_seconds=0.0 if args.no_cpu_baseline else 3.0)
+
     # ---- streaming reference on the same GPU (torch reduction over 2 GiB)
     big = torch.ones(2 ** 29, dtype=torch.float32, device=dev)
     big.sum()
@@ -619,6 +756,7 @@ def main():
         "two_sided": two_sided,
         "moe_block": moe,
         "model_pass": model,
+        "encoder": encoder,
         "decoder_layer": layer,
         "stream_read_GBps_torch_sum": round(stream_gbps, 1),
         "roofline": roofline,

@@ -42,6 +42,8 @@ constexpr int kLds = kTile + kTile / 16;  // one pad double per 16
 
 enum Mode { kFused = 0, kRotate = 1, kQuant = 2, kNorm = 3 };
 
+
+
 struct TileArgs {
   const float *w;        // fused, rotate: dense fp32 input
   const double *wt;      // quant, norm: rotated fp64 input
@@ -60,25 +62,32 @@ struct TileArgs {
   uint16_t *rscale;
 };
 
-__device__ __forceinline__ int lpos(int i) { return i + (i >> 4); }
-
+// LDS slot of tile index i: i + i/16 (one pad double per 16).  In each layout
+// a thread's 16 slots are one base plus constant strides:
+//   P1  i = 16t + j                              -> 17t + j
+//   P2  i = (t & 15) + 16j + 256(t >> 4)         -> (t & 15) + 272(t >> 4) + 17j
+//   P3  i = t + 256j                             -> t + (t >> 4) + 272j
 template <int L>
-__device__ __forceinline__ int lay(int t, int j) {
-  if constexpr (L == 1) return (t << 4) | j;
-  else if constexpr (L == 2) return (t & 15) | (j << 4) | ((t >> 4) << 8);
-  else return t | (j << 8);
+__device__ __forceinline__ int lds_base(int t) {
+  if constexpr (L == 1) return 17 * t;
+  else if constexpr (L == 2) return (t & 15) + 272 * (t >> 4);
+  else return t + (t >> 4);
 }
+template <int L>
+constexpr int lds_stride() { return L == 1 ? 1 : L == 2 ? 17 : 272; }
 
 template <int L>
 __device__ __forceinline__ void lds_put(double *s, const double (&v)[16], int t) {
+  double *p = s + lds_base<L>(t);
 #pragma unroll
-  for (int j = 0; j < 16; ++j) s[lpos(lay<L>(t, j))] = v[j];
+  for (int j = 0; j < 16; ++j) p[j * lds_stride<L>()] = v[j];
 }
 
 template <int L>
 __device__ __forceinline__ void lds_get(const double *s, double (&v)[16], int t) {
+  const double *p = s + lds_base<L>(t);
 #pragma unroll
-  for (int j = 0; j < 16; ++j) v[j] = s[lpos(lay<L>(t, j))];
+  for (int j = 0; j < 16; ++j) v[j] = p[j * lds_stride<L>()];
 }
 
 // Butterflies (a, c) -> (a + c, a - c) over register-index bit M.
@@ -93,12 +102,21 @@ __device__ __forceinline__ void reg_stage(double (&v)[16]) {
     }
 }
 
-// Register-index bits 0..n-1, in increasing order.
-__device__ __forceinline__ void reg_stages(double (&v)[16], int n) {
-  if (n > 0) reg_stage<0>(v);
-  if (n > 1) reg_stage<1>(v);
-  if (n > 2) reg_stage<2>(v);
-  if (n > 3) reg_stage<3>(v);
+// Register-index bits 0..N-1, in increasing order.
+template <int N>
+__device__ __forceinline__ void reg_stages(double (&v)[16]) {
+  if constexpr (N > 0) reg_stage<0>(v);
+  if constexpr (N > 1) reg_stage<1>(v);
+  if constexpr (N > 2) reg_stage<2>(v);
+  if constexpr (N > 3) reg_stage<3>(v);
+}
+
+// The largest double below m: "x > below(m)" is "x >= m".
+__device__ __forceinline__ double below(double m) {
+  const long long b = __double_as_longlong(m);
+  if (m > 0.0) return __longlong_as_double(b - 1);
+  if (m < 0.0) return __longlong_as_double(b + 1);
+  return -4.9406564584124654e-324;   // m is +-0: the negative of the smallest subnormal
 }
 
 // fp64 -> fp16 bits, round to nearest even straight from fp64 (no detour
@@ -132,45 +150,48 @@ __device__ __forceinline__ double h2d(uint16_t h) {
   return (h & 0x8000) ? -v : v;
 }
 
-template <int MODE, int BITS>
+__device__ __forceinline__ int tile_valid(const TileArgs &a, int64_t tile) {
+  const int64_t left = a.total - tile * kTile;
+  return left < kTile ? (int)left : kTile;
+}
+
+// One tile per workgroup.  LOG2B (the input-side block, 7..12) fixes the
+// butterfly stages of each layout; the fp64-input modes take LOG2B = 0.
+// Threads past the end of a partial tile read the first 16 elements (in
+// bounds, never stored) instead of selecting zeros.
+template <int MODE, int BITS, int LOG2B>
 __global__ __launch_bounds__(kThreads) void tile_kernel(TileArgs a) {
   __shared__ double s[kLds];
   const int t = threadIdx.x;
-  const int64_t base = (int64_t)blockIdx.x * kTile;
-  const int64_t left = a.total - base;
-  const int valid = left < kTile ? (int)left : kTile;
-  const bool act = (t << 4) < valid;
+  const int64_t tile = blockIdx.x;
+  const int64_t base = tile * kTile;
+  const bool act = (t << 4) < tile_valid(a, tile);
+  const int64_t off = act ? base + (t << 4) : 0;
   double v[16];
-
   if constexpr (MODE == kFused || MODE == kRotate) {
-    if (act) {
-      const float4 *p = reinterpret_cast<const float4 *>(a.w + base + (t << 4));
-      const int col = (int)((base + (t << 4)) % a.d_in);
-      const uint4 sg = *reinterpret_cast<const uint4 *>(a.sign_in + col);
-      const int8_t *sb = reinterpret_cast<const int8_t *>(&sg);
+    const float4 *p = reinterpret_cast<const float4 *>(a.w + off);
+    const uint4 sg = *reinterpret_cast<const uint4 *>(a.sign_in + (int)(off % a.d_in));
+    const int8_t *sb = reinterpret_cast<const int8_t *>(&sg);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 f = p[q];
-        v[4 * q + 0] = (double)f.x * (double)sb[4 * q + 0];
-        v[4 * q + 1] = (double)f.y * (double)sb[4 * q + 1];
-        v[4 * q + 2] = (double)f.z * (double)sb[4 * q + 2];
-        v[4 * q + 3] = (double)f.w * (double)sb[4 * q + 3];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = 0.0;
+    for (int q = 0; q < 4; ++q) {
+      const float4 f = p[q];
+      v[4 * q + 0] = (double)f.x * (double)sb[4 * q + 0];
+      v[4 * q + 1] = (double)f.y * (double)sb[4 * q + 1];
+      v[4 * q + 2] = (double)f.z * (double)sb[4 * q + 2];
+      v[4 * q + 3] = (double)f.w * (double)sb[4 * q + 3];
     }
-    reg_stages(v, 4);                       // strides 1..8 (b >= 128)
+    static_assert(LOG2B >= 7 && LOG2B <= 12, "block size");
+    reg_stages<4>(v);                                  // strides 1..8
     lds_put<1>(s, v, t);
     __syncthreads();
     lds_get<2>(s, v, t);
-    reg_stages(v, a.log2b - 4 < 4 ? a.log2b - 4 : 4);   // strides 16..128
+    reg_stages<(LOG2B - 4 < 4 ? LOG2B - 4 : 4)>(v);    // strides 16..128
     __syncthreads();
     lds_put<2>(s, v, t);
-    if (a.log2b > 8) {                      // strides 256..2048
+    if constexpr (LOG2B > 8) {                         // strides 256..2048
       __syncthreads();
       lds_get<3>(s, v, t);
-      reg_stages(v, a.log2b - 8);
+      reg_stages<LOG2B - 8>(v);
       __syncthreads();
       lds_put<3>(s, v, t);
     }
@@ -187,17 +208,12 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(TileArgs a) {
       return;
     }
   } else {
-    if (act) {
-      const double2 *p = reinterpret_cast<const double2 *>(a.wt + base + (t << 4));
+    const double2 *p = reinterpret_cast<const double2 *>(a.wt + off);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const double2 d = p[q];
-        v[2 * q] = d.x;
-        v[2 * q + 1] = d.y;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = 0.0;
+    for (int q = 0; q < 8; ++q) {
+      const double2 d = p[q];
+      v[2 * q] = d.x;
+      v[2 * q + 1] = d.y;
     }
   }
 
@@ -219,25 +235,30 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(TileArgs a) {
         for (int q = 0; q < 8; ++q)
           o[q] = sd > 0.0 ? make_double2(v[2 * q] / sd, v[2 * q + 1] / sd) : make_double2(0.0, 0.0);
       }
-      return;
     } else {
-      double pt[4], mid[3];
+      double pt[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) pt[c] = (double)a.lev[c] * sd;       // exact
+      for (int c = 0; c < 4; ++c) pt[c] = (double)a.lev[c] * sd;        // exact
+      // Boundary k (between points k and k+1) is their midpoint, exact in
+      // fp64; a weight on it goes up when tie_up says so, i.e. the test is
+      // "> below(mid)".  A zero scale makes every point 0 and the code
+      // zero_code: boundaries below it at -inf, the others at +inf.
+      double th[3];
 #pragma unroll
-      for (int k = 0; k < 3; ++k) mid[k] = (pt[k] + pt[k + 1]) * 0.5;  // exact
-      int code[16];
+      for (int k = 0; k < 3; ++k) {
+        const double mid = (pt[k] + pt[k + 1]) * 0.5;
+        const double tk = ((a.tie_up >> k) & 1) ? below(mid) : mid;
+        th[k] = sd == 0.0 ? (k < a.zero_code ? -INFINITY : INFINITY) : tk;
+      }
+      // The three flags are monotone (b2 => b1 => b0), so the code is their
+      // sum: bit 1 = b1, bit 0 = b0 ^ b1 ^ b2.  v becomes the residual.
       uint32_t p0 = 0, p1 = 0;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        int c = 0;
-#pragma unroll
-        for (int k = 0; k < 3; ++k)
-          c += (v[j] > mid[k] || (v[j] == mid[k] && ((a.tie_up >> k) & 1))) ? 1 : 0;
-        if (sd == 0.0) c = a.zero_code;
-        code[j] = c;
-        p0 |= (uint32_t)(c & 1) << j;
-        p1 |= (uint32_t)(c >> 1) << j;
+        const bool b0 = v[j] > th[0], b1 = v[j] > th[1], b2 = v[j] > th[2];
+        p0 |= (uint32_t)(b0 ^ b1 ^ b2) << j;
+        p1 |= (uint32_t)b1 << j;
+        v[j] -= b1 ? (b2 ? pt[3] : pt[2]) : (b0 ? pt[1] : pt[0]);
       }
       const int64_t g = (base >> 7) + (t >> 3);
       const int q8 = t & 7;
@@ -249,15 +270,9 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(TileArgs a) {
       }
       if constexpr (BITS > 0) {
         constexpr int qm = (1 << (BITS - 1)) - 1;
-        double r[16];
         double am = 0.0;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int c = code[j];
-          const double pc = c == 0 ? pt[0] : c == 1 ? pt[1] : c == 2 ? pt[2] : pt[3];
-          r[j] = v[j] - pc;
-          am = fmax(am, fabs(r[j]));
-        }
+        for (int j = 0; j < 16; ++j) am = fmax(am, fabs(v[j]));
         am = fmax(am, __shfl_xor(am, 1));
         am = fmax(am, __shfl_xor(am, 2));
         am = fmax(am, __shfl_xor(am, 4));
@@ -266,8 +281,8 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(TileArgs a) {
         uint64_t lo = 0, hi = 0;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          int qi = 0;
-          if (rd > 0.0) qi = (int)fmin(fmax(rint(r[j] / rd), (double)-qm), (double)qm);
+          const double x = fmin(fmax(rint(v[j] / rd), (double)-qm), (double)qm);
+          const int qi = rd > 0.0 ? (int)x : 0;
           const uint64_t f = (uint64_t)(qi & ((1 << BITS) - 1));
           if (j < 8) lo |= f << (BITS * j);
           else hi |= f << (BITS * (j - 8));
@@ -472,9 +487,25 @@ __device__ __forceinline__ double ld_agent(const double *p) {
 }
 
 // One Lloyd iteration: cell sums per workgroup, then the last workgroup to
-// finish adds them in workgroup order and moves the levels.
+// finish adds them in a fixed order and moves the levels.  Each thread reads
+// its samples eight at a time (independent loads in flight).
+constexpr int kLloydUnroll = 8;
+
+__device__ __forceinline__ void lloyd_add(double x, const double (&mid)[3], const bool (&up)[3], double (&sm)[4],
+                                          uint32_t (&ct)[4]) {
+  int c = 0;
+#pragma unroll
+  for (int k = 0; k < 3; ++k) c += (x > mid[k] || (x == mid[k] && up[k])) ? 1 : 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (c == k) {
+      sm[k] += x;
+      ct[k] += 1;
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void lloyd_kernel(const double *v, int64_t n, char *ws) {
-  __shared__ double red[4][8];
+  __shared__ double red[32][8];
   __shared__ int last;
   FitState *st = reinterpret_cast<FitState *>(ws);
   double *part = reinterpret_cast<double *>(ws + kPartOff);
@@ -491,18 +522,16 @@ __global__ __launch_bounds__(kThreads) void lloyd_kernel(const double *v, int64_
   }
   double sm[4] = {0.0, 0.0, 0.0, 0.0};
   uint32_t ct[4] = {0u, 0u, 0u, 0u};
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + t; i < n; i += (int64_t)gridDim.x * kThreads) {
-    const double x = v[i];
-    int c = 0;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + t;
+  for (; i + (kLloydUnroll - 1) * stride < n; i += kLloydUnroll * stride) {
+    double x[kLloydUnroll];
 #pragma unroll
-    for (int k = 0; k < 3; ++k) c += (x > mid[k] || (x == mid[k] && up[k])) ? 1 : 0;
+    for (int u = 0; u < kLloydUnroll; ++u) x[u] = v[i + u * stride];
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (c == k) {
-        sm[k] += x;
-        ct[k] += 1;
-      }
+    for (int u = 0; u < kLloydUnroll; ++u) lloyd_add(x[u], mid, up, sm, ct);
   }
+  for (; i < n; i += stride) lloyd_add(v[i], mid, up, sm, ct);
   double val[8];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -526,14 +555,19 @@ __global__ __launch_bounds__(kThreads) void lloyd_kernel(const double *v, int64_
   __syncthreads();
   if (!last) return;
   __threadfence();
-  if (t < 4) {
-    double S = 0.0, C = 0.0;
-    for (unsigned b = 0; b < gridDim.x; ++b) {
-      S += ld_agent(part + b * 8 + t);
-      C += ld_agent(part + b * 8 + 4 + t);
-    }
-    if (C > 0.0) st->lev[t] = S / C;
+  // quantity k = t & 7 over workgroups j, j + 32, ... (j = t >> 3), then a
+  // fixed tree over j
+  const int k = t & 7, j = t >> 3;
+  double acc = 0.0;
+  for (unsigned b = j; b < gridDim.x; b += 32) acc += ld_agent(part + b * 8 + k);
+  __syncthreads();
+  red[j][k] = acc;
+  __syncthreads();
+  for (int w = 16; w >= 1; w >>= 1) {
+    if (j < w) red[j][k] += red[j + w][k];
+    __syncthreads();
   }
+  if (t < 4 && red[0][4 + t] > 0.0) st->lev[t] = red[0][t] / red[0][4 + t];
   if (t == 0) __hip_atomic_store(&st->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -636,17 +670,38 @@ nl_status check_codes(const char *who, const nl_codes *o, TileArgs &a) {
   return NL_OK;
 }
 
-template <int MODE>
-hipError_t launch_tiles(const TileArgs &a, int bits, hipStream_t s) {
+template <int MODE, int LOG2B>
+hipError_t launch_tiles_b(const TileArgs &a, int bits, hipStream_t s) {
   const dim3 grid((unsigned)((a.total + kTile - 1) / kTile)), block(kThreads);
-  switch (bits) {
-    case 0: hipLaunchKernelGGL((tile_kernel<MODE, 0>), grid, block, 0, s, a); break;
-    case 6: hipLaunchKernelGGL((tile_kernel<MODE, 6>), grid, block, 0, s, a); break;
-    case 7: hipLaunchKernelGGL((tile_kernel<MODE, 7>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((tile_kernel<MODE, 8>), grid, block, 0, s, a); break;
-    default: return hipErrorInvalidValue;
+  if constexpr (MODE == kRotate || MODE == kNorm) {
+    hipLaunchKernelGGL((tile_kernel<MODE, 0, LOG2B>), grid, block, 0, s, a);
+  } else {
+    switch (bits) {
+      case 0: hipLaunchKernelGGL((tile_kernel<MODE, 0, LOG2B>), grid, block, 0, s, a); break;
+      case 6: hipLaunchKernelGGL((tile_kernel<MODE, 6, LOG2B>), grid, block, 0, s, a); break;
+      case 7: hipLaunchKernelGGL((tile_kernel<MODE, 7, LOG2B>), grid, block, 0, s, a); break;
+      case 8: hipLaunchKernelGGL((tile_kernel<MODE, 8, LOG2B>), grid, block, 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_tiles(const TileArgs &a, int bits, hipStream_t s) {
+  if constexpr (MODE == kQuant || MODE == kNorm) {
+    return launch_tiles_b<MODE, 0>(a, bits, s);
+  } else {
+    switch (a.log2b) {
+      case 7: return launch_tiles_b<MODE, 7>(a, bits, s);
+      case 8: return launch_tiles_b<MODE, 8>(a, bits, s);
+      case 9: return launch_tiles_b<MODE, 9>(a, bits, s);
+      case 10: return launch_tiles_b<MODE, 10>(a, bits, s);
+      case 11: return launch_tiles_b<MODE, 11>(a, bits, s);
+      case 12: return launch_tiles_b<MODE, 12>(a, bits, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
 }
 
 hipError_t launch_cols(double *wt, int d_out, int d_in, const int8_t *sign_out, hipStream_t s) {
