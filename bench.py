@@ -44,7 +44,8 @@ ROOFLINE_TS = (8, 16)   # verify launches of forward_kernel<6, 1, 4> (one 16-tok
 ROOFLINE_KERNEL = "forward_kernel<6, 1, 4>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "forward_kernel_6bit_verify_T8_T16_proj7b8b_traffic.txt")
 ENC_BITS = 7            # the encoder leg writes 7-bit residuals (the post's bf16-noise-floor width)
-ENC_KERNEL = "tile_kernel<0, 7>"
+ENC_KERNEL = "tile_kernel<0, 7,"   # fused 7-bit encode, any block size (kernel-name match)
+ENC_KERNEL_NAME = "tile_kernel<0, 7, LOG2B>"
 ENC_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encoder_tile_kernel_7bit_fused_proj7b8b_traffic.txt")
 FIT_ROWS = 512          # 512 x 4096 = 2^21 samples, the post's ~2M
 
@@ -374,7 +375,7 @@ def encoder_leg(nl, torch, synth, reps, cpu_seconds=0.0):
                           "levels": [round(x, 5) for x in fit[60][1]]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "kernel": ENC_KERNEL + " (one-sided fused encode, the four projections)",
+                     "traffic": None, "kernel": ENC_KERNEL_NAME + " (one-sided fused encode, the four projections)",
                      "bytes_per_weight": encoder_bytes_per_weight(ENC_BITS),
                      "avg_launch_us": round(tot_us / len(SHAPES), 2),
                      "avg_algorithmic_bytes": int(tot_b / len(SHAPES)),
@@ -420,7 +421,7 @@ ENC_TITLE = ("one-sided fused encode of dense fp32 4096x4096, 1024x4096, 14336x4
 
 
 def pmc_summary(fetch_dir, write_dir, out_path, kernel=ROOFLINE_KERNEL, prefix="void nl::",
-                title=ROOFLINE_TITLE, flag="--roofline-only", digest=None):
+                title=ROOFLINE_TITLE, flag="--roofline-only", digest=None, display=None):
     """Per-launch HBM traffic of the roofline kernel from two rocprofv3 --pmc
     runs of `bench.py --roofline-only` (FETCH_SIZE, then WRITE_SIZE), each
     counter scaled by what it reads for the calibration copy.  The encoder's
@@ -452,7 +453,7 @@ def pmc_summary(fetch_dir, write_dir, out_path, kernel=ROOFLINE_KERNEL, prefix="
     fetch = sum(f_fwd) / len(f_fwd) * 1024 * kf
     write = sum(w_fwd) / len(w_fwd) * 1024 * kw
     summ = "--pmc-summary" if flag == "--roofline-only" else "--pmc-summary-encoder"
-    text = (f"HBM traffic of {kernel} ({title})\n"
+    text = (f"HBM traffic of {display or kernel} ({title})\n"
             f"commands:\n"
             f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -o p -- python3 bench.py {flag}\n"
             f"  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -o p -- python3 bench.py {flag}\n"
@@ -494,7 +495,7 @@ def main():
         return
     if args.pmc_summary_encoder:
         pmc_summary(*args.pmc_summary_encoder, ENC_TRAFFIC_FILE, kernel=ENC_KERNEL, prefix="", title=ENC_TITLE,
-                    flag="--encoder-only", digest=kernel_source_digest(ENC_SOURCES))
+                    flag="--encoder-only", digest=kernel_source_digest(ENC_SOURCES), display=ENC_KERNEL_NAME)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
