@@ -89,3 +89,44 @@ def test_timing_rejects_bad_use():
     assert b"not begun" in L.nested_linear_last_error()
     assert L.nested_linear_timing_begin(0) == nl.NL_EINVAL
     assert L.nested_linear_timing_begin(-3) == nl.NL_EINVAL
+
+
+def test_encoder_rejects_bad_arguments_without_touching_the_gpu():
+    L = nl.lib()
+    lev = (ctypes.c_float * 4)(-1.5, -0.45, 0.45, 1.5)
+    sz = ctypes.c_size_t()
+    # shapes
+    for d_out, d_in in [(0, 128), (4, 100), (4, 0), (-1, 256)]:
+        assert L.nested_encode_workspace_bytes(d_out, d_in, 1, ctypes.byref(sz)) == nl.NL_EINVAL
+        assert L.nested_encode_rotate(d_out, d_in, 16, 16, None, 4096, None) == nl.NL_EINVAL
+        assert L.nested_linear_last_error()
+    assert L.nested_encode_workspace_bytes(4, 256, 0, ctypes.byref(sz)) == nl.NL_OK and sz.value == 0
+    assert L.nested_encode_workspace_bytes(4, 256, 1, ctypes.byref(sz)) == nl.NL_OK and sz.value == 8 * 4 * 256
+    # codes descriptor: bits, levels, missing or extra residual arrays, alignment
+    bad = [nl.nl_codes(4, 256, 5, lev, 16, 16, 16, 16),
+           nl.nl_codes(4, 256, 7, (ctypes.c_float * 4)(-1.5, 0.45, -0.45, 1.5), 16, 16, 16, 16),
+           nl.nl_codes(4, 256, 7, (ctypes.c_float * 4)(-1.5, float("inf"), 0.45, 1.5), 16, 16, 16, 16),
+           nl.nl_codes(4, 256, 7, lev, 16, 16, None, None),
+           nl.nl_codes(4, 256, 0, lev, 16, 16, 16, 16),
+           nl.nl_codes(4, 256, 7, lev, 18, 16, 16, 16)]
+    for c in bad:
+        assert L.nested_encode(16, 16, None, ctypes.byref(c), None, 0, None) == nl.NL_EINVAL
+        assert L.nested_encode_quantize(16, ctypes.byref(c), None) == nl.NL_EINVAL
+    assert L.nested_encode_quantize(16, ctypes.byref(bad[1]), None) == nl.NL_EINVAL
+    assert b"ascending" in L.nested_linear_last_error()
+    good = nl.nl_codes(4, 256, 7, lev, 16, 16, 16, 16)
+    # two-sided without a workspace; misaligned w; NULL inputs
+    assert L.nested_encode(16, 16, 16, ctypes.byref(good), None, 0, None) == nl.NL_EINVAL
+    assert L.nested_encode(20, 16, None, ctypes.byref(good), None, 0, None) == nl.NL_EINVAL
+    assert L.nested_encode(None, 16, None, ctypes.byref(good), None, 0, None) == nl.NL_EINVAL
+    # overlapping rotate / normalise buffers
+    assert L.nested_encode_rotate(4, 256, 4096, 16, None, 4096 + 256, None) == nl.NL_EINVAL
+    assert L.nested_encode_normalize(4, 256, 4096, 4096 + 256, None) == nl.NL_EINVAL
+    # level fit: n, iters, workspace
+    assert L.nested_encode_fit_workspace_bytes(0, ctypes.byref(sz)) == nl.NL_EINVAL
+    assert L.nested_encode_fit_workspace_bytes(1000, ctypes.byref(sz)) == nl.NL_OK and sz.value > 0
+    out = (ctypes.c_double * 4)()
+    assert L.nested_encode_fit_levels(16, 0, 60, out, 256, sz.value, None) == nl.NL_EINVAL
+    assert L.nested_encode_fit_levels(16, 100, -1, out, 256, sz.value, None) == nl.NL_EINVAL
+    assert L.nested_encode_fit_levels(16, 100, 60, out, 256, sz.value - 8, None) == nl.NL_EINVAL
+    assert L.nested_encode_fit_levels(16, 100, 60, out, 300, sz.value, None) == nl.NL_EINVAL
