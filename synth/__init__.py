@@ -28,7 +28,8 @@ Seeds: every array is a pure function of SeedSequence([20261008, cfg,
 linear_idx, stream]) with numpy's PCG64, so the host regenerates one linear
 at a time.  Stream ids: 0 sign_in, 1 sign_out, 2 base codes, 3 base scales,
 4 residual codes, 5 residual scales, 6 x, 7 router logits, 8 dense weights
-(the encoder's input).
+(the encoder's input), 9-11 the W4 codes, refinement codes and scales of the
+W4/W8 dual-plane format.
 """
 from __future__ import annotations
 
@@ -47,6 +48,7 @@ LEVELS = np.array([-1.5104, -0.4528, 0.4528, 1.5104], dtype=np.float32)
 STREAM_SIGN_IN, STREAM_SIGN_OUT, STREAM_BASE, STREAM_BASE_SCALE = 0, 1, 2, 3
 STREAM_RESID, STREAM_RESID_SCALE, STREAM_X, STREAM_ROUTER = 4, 5, 6, 7
 STREAM_DENSE = 8
+STREAM_W4, STREAM_W4_REF, STREAM_W4_SCALE = 9, 10, 11
 
 
 def rng(cfg: int, linear_idx: int, stream: int) -> np.random.Generator:
@@ -159,6 +161,29 @@ def make_dense_weights(d_out: int, d_in: int, cfg: int = 0, idx: int = 0, sigma:
         z = g.standard_normal(size=(n, d_in), dtype=np.float32)
         out[r:r + n] = z * row_gain[r:r + n, None].astype(np.float32) * col_gain[None, :].astype(np.float32)
     return out
+
+
+def pack_nibbles(q: np.ndarray) -> np.ndarray:
+    """[d_out][d_in] values in [-8, 7] -> [d_out][d_in/2] uint8 of
+    two's-complement nibbles, weight 2i in the low nibble of byte i."""
+    u = (np.asarray(q, np.int16) & 0x0F).astype(np.uint8)
+    return np.ascontiguousarray(u[:, 0::2] | (u[:, 1::2] << 4))
+
+
+def make_w4w8_linear(d_out: int, d_in: int, cfg: int = 0, idx: int = 0, keep_codes: bool = False) -> dict:
+    """One synthetic BitNest W4/W8 linear (page 2, section 3.3 dual planes):
+    base codes clip(rint(N(0, 3^2)), -8, 7), refinement codes uniform in
+    [-8, 7] except [0, 7] where the base code is -8 (the boundary rule of
+    eq. 9), fp16 scales U(0.005, 0.02) per (row, 128-group)."""
+    assert d_in % GROUP == 0 and d_in % 2 == 0
+    q4 = np.clip(np.rint(rng(cfg, idx, STREAM_W4).normal(0.0, 3.0, size=(d_out, d_in))), -8, 7).astype(np.int8)
+    qr = rng(cfg, idx, STREAM_W4_REF).integers(-8, 8, size=(d_out, d_in), dtype=np.int8)
+    qr = np.where(q4 == -8, np.abs(qr) % 8, qr).astype(np.int8)
+    lin = {"d_out": d_out, "d_in": d_in, "base_plane": pack_nibbles(q4), "ref_plane": pack_nibbles(qr),
+           "scales": make_scales(d_out, d_in, cfg, idx, STREAM_W4_SCALE)}
+    if keep_codes:
+        lin["q4"], lin["qr"] = q4, qr
+    return lin
 
 
 def make_linear(d_out: int, d_in: int, bits: int, cfg: int = 0, idx: int = 0,
