@@ -32,6 +32,8 @@ EXPORTS = (
     "nested_linear_last_error",
     "nested_encode_rotate", "nested_encode_quantize", "nested_encode_workspace_bytes", "nested_encode",
     "nested_encode_normalize", "nested_encode_fit_workspace_bytes", "nested_encode_fit_levels",
+    "nested_w4w8_create", "nested_w4w8_destroy", "nested_w4w8_workspace_bytes", "nested_w4w8_verify",
+    "nested_w4w8_draft",
 )
 
 
@@ -58,6 +60,11 @@ class nl_codes(ctypes.Structure):
         ("base_codes", ctypes.c_void_p), ("base_scales", ctypes.c_void_p),
         ("resid_codes", ctypes.c_void_p), ("resid_scales", ctypes.c_void_p),
     ]
+
+
+class nl_w4w8_desc(ctypes.Structure):
+    _fields_ = [("d_out", ctypes.c_int32), ("d_in", ctypes.c_int32), ("base_plane", ctypes.c_void_p),
+                ("ref_plane", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
 
 
 _lib = None
@@ -95,6 +102,11 @@ def lib() -> ctypes.CDLL:
             "nested_encode_normalize": [i32, i32, P, P, P],
             "nested_encode_fit_workspace_bytes": [ctypes.c_int64, ctypes.POINTER(sz)],
             "nested_encode_fit_levels": [P, ctypes.c_int64, i32, ctypes.POINTER(ctypes.c_double), P, sz, P],
+            "nested_w4w8_create": [ctypes.POINTER(nl_w4w8_desc), ctypes.POINTER(P)],
+            "nested_w4w8_destroy": [P],
+            "nested_w4w8_workspace_bytes": [P, i32, ctypes.POINTER(sz)],
+            "nested_w4w8_verify": [P, P, i32, P, P, sz, P],
+            "nested_w4w8_draft": [P, P, i32, P, P, sz, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -307,6 +319,73 @@ def encode(w, sign_in, sign_out, bits: int, levels, stream=None) -> Codes:
     ws = torch.empty(nws, dtype=torch.uint8, device=w.device) if nws else None
     nested_encode(w, sign_in, sign_out, c.desc, ws, stream)
     return c
+
+
+# --- W4/W8 dual-plane linear (include/nested_w4w8.h) -------------------------
+
+def nested_w4w8_create(d_out: int, d_in: int, base_plane, ref_plane, scales) -> ctypes.c_void_p:
+    d = nl_w4w8_desc(int(d_out), int(d_in), _ptr(base_plane), _ptr(ref_plane), _ptr(scales))
+    h = ctypes.c_void_p()
+    _check(lib().nested_w4w8_create(ctypes.byref(d), ctypes.byref(h)))
+    return h
+
+
+def nested_w4w8_destroy(h):
+    _check(lib().nested_w4w8_destroy(h))
+
+
+def nested_w4w8_workspace_bytes(h, T_max: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().nested_w4w8_workspace_bytes(h, int(T_max), ctypes.byref(n)))
+    return n.value
+
+
+def nested_w4w8_verify(h, x, T: int, y, ws, stream=None):
+    _check(lib().nested_w4w8_verify(h, _ptr(x), int(T), _ptr(y), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def nested_w4w8_draft(h, x, T: int, y, ws, stream=None):
+    _check(lib().nested_w4w8_draft(h, _ptr(x), int(T), _ptr(y), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+class W4W8Linear:
+    """Owns one W4/W8 dual-plane linear built from a canonical dict (numpy
+    arrays as produced by ``synth.make_w4w8_linear``)."""
+
+    def __init__(self, lin: dict, device="cuda"):
+        import numpy as np
+        import torch
+
+        def dev(a, dt):
+            return None if a is None else torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(device)
+
+        self.d_out, self.d_in = lin["d_out"], lin["d_in"]
+        self.h = nested_w4w8_create(self.d_out, self.d_in, dev(lin["base_plane"], np.uint8),
+                                    dev(lin.get("ref_plane"), np.uint8), dev(lin["scales"], np.int16))
+
+    def close(self):
+        if self.h is not None:
+            nested_w4w8_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace(self, T_max: int, device="cuda"):
+        import torch
+        n = nested_w4w8_workspace_bytes(self.h, T_max)
+        return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+
+    def forward(self, x, verify: bool, ws=None, y=None, stream=None):
+        import torch
+        T = x.shape[0]
+        ws = self.workspace(T) if ws is None else ws
+        y = torch.empty((T, self.d_out), dtype=torch.float32, device=x.device) if y is None else y
+        (nested_w4w8_verify if verify else nested_w4w8_draft)(self.h, x, T, y, ws, stream)
+        return y
 
 
 class Linear:

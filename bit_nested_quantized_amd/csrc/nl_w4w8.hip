@@ -1,0 +1,467 @@
+// nl_w4w8.hip -- the BitNest W4/W8 dual-plane linear (include/nested_w4w8.h).
+//
+// One launch per call.  A workgroup (4 waves) owns 64 rows and one K-split
+// of whole 128-column groups:
+//   * it stages its K-range of x for all tokens in LDS as fp16, each
+//     (token, group) scaled by a power of two that puts its largest
+//     magnitude in [2^14, 2^15) (bf16 -> fp16 is then exact), with the
+//     group's sum of x' and the inverse scale beside it;
+//   * each wave streams its 16-row tile's planes straight from the
+//     canonical layout through a ring of register sets: per group and lane
+//     16 bytes of the base plane (32 nibbles: the lane's 32 columns), 16 of
+//     the refinement plane (verify) and the row's fp16 scale;
+//   * the nibbles become the MFMA B operand as fp16 1024 + u, u the offset
+//     code (q4 + 8 for the draft, 16 (q4 + 8) + (q_r + 8) = 136 + 16 q4 + q_r
+//     for verify, so one v_mfma_f32_16x16x32_f16 per 32 columns and 16 tokens
+//     serves both); the group's fp32 result minus bias * sum(x') times
+//     scale * inverse x scale goes into the row's accumulators;
+//   * with several splits, partials go to the workspace and the row block's
+//     last workgroup (ticket) adds them in split order.
+// Lane l holds row (l & 15) and the group's columns 32 (l >> 4) .. +32; MFMA
+// step s feeds columns 8s .. 8s + 7 of that run, on both operands.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <unordered_set>
+
+#include "../../include/nested_w4w8.h"
+
+namespace nl {
+nl_status api_error(nl_status st, const char *msg);  // nl_api.hip
+}
+
+struct nl_w4w8 {
+  uint32_t magic;
+  int d_out, d_in, rows_pad, G;
+  bool has_ref;
+  uint8_t *base;
+  uint8_t *ref;
+  uint16_t *scales;
+};
+
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kMagic = 0x4E573438u;  // "NW48"
+constexpr int kGroup = 128;
+constexpr int kRows = 64;       // rows per workgroup: 4 waves x 16
+constexpr int kThreads = 256;
+constexpr int kRing = 6;        // groups in flight per wave
+constexpr int kLds = 60 * 1024;    // dynamic LDS budget (x' and its metadata)
+constexpr int kFillWgs = 512;   // workgroups a call aims for (2 per CU)
+
+struct W48Args {
+  const uint8_t *base;
+  const uint8_t *ref;
+  const uint16_t *scales;
+  const uint16_t *x;
+  float *y;
+  float *part;      // [S][T][rows_pad]
+  uint32_t *tick;   // [rows_pad / 64]
+  int d_out, d_in, rows_pad, G, T, S, gps, pitch;
+};
+
+__device__ __forceinline__ float h2f(uint16_t h) {
+  _Float16 v;
+  __builtin_memcpy(&v, &h, 2);
+  return (float)v;
+}
+
+__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ float ld_agent(const float *p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Four fp16 pairs 1024 + u from one dword of each plane (8 columns).
+// lo/hi: per byte j, the offset code of column 2j / 2j + 1.
+__device__ __forceinline__ void pairs(uint32_t lo, uint32_t hi, uint32_t *out) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    out[j] = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u + 0x00010001u * j) | 0x64006400u;
+}
+
+template <bool VERIFY>
+__device__ __forceinline__ void unpack(const uint4 &b, const uint4 &r, uint32_t (&B)[4][4]) {
+  const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
+  const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const uint32_t xb = bw[s] ^ 0x88888888u;  // two's complement -> offset nibbles
+    if constexpr (VERIFY) {
+      const uint32_t xr = rw[s] ^ 0x88888888u;
+      const uint32_t even = ((xb << 4) & 0xF0F0F0F0u) | (xr & 0x0F0F0F0Fu);
+      const uint32_t odd = (xb & 0xF0F0F0F0u) | ((xr >> 4) & 0x0F0F0F0Fu);
+      pairs(even, odd, B[s]);
+    } else {
+      pairs(xb & 0x0F0F0F0Fu, (xb >> 4) & 0x0F0F0F0Fu, B[s]);
+    }
+  }
+}
+
+template <bool VERIFY, int MT>
+__global__ __launch_bounds__(kThreads) void w48_kernel(W48Args a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int T16 = MT * 16;
+  constexpr float kBias = VERIFY ? 1160.0f : 1032.0f;
+  _Float16 *xs = reinterpret_cast<_Float16 *>(smem);
+  float2 *meta = reinterpret_cast<float2 *>(smem + (size_t)T16 * a.pitch * 2);
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int rb = blockIdx.x / a.S, sp = blockIdx.x - rb * a.S;
+  const int g0 = sp * a.gps;
+  const int ng = min(a.G, g0 + a.gps) - g0;
+  const int row = rb * kRows + wave * 16 + (lane & 15);
+  const int kb = lane >> 4;
+  const uint8_t *bp = a.base + (size_t)row * (a.d_in / 2) + kb * 16;
+  const uint8_t *rp = VERIFY ? a.ref + (size_t)row * (a.d_in / 2) + kb * 16 : nullptr;
+  const uint16_t *sc = a.scales + (size_t)row * a.G;
+
+  // x: first batch of loads before the weight ring's
+  const int items = T16 * ng * 16;   // (token, group, 16-byte piece)
+  constexpr int kFirst = 4;
+  uint4 xv[kFirst];
+#pragma unroll
+  for (int j = 0; j < kFirst; ++j) {
+    const int it = t + j * kThreads;
+    const int tt = it / (ng * 16), gp = it - tt * ng * 16;
+    xv[j] = make_uint4(0, 0, 0, 0);
+    if (it < items && tt < a.T)
+      xv[j] = *reinterpret_cast<const uint4 *>(a.x + (size_t)tt * a.d_in + (size_t)g0 * kGroup + gp * 8);
+  }
+
+  uint4 wb[kRing], wr[kRing];
+  uint16_t ws[kRing];
+#pragma unroll
+  for (int i = 0; i < kRing; ++i)
+    if (i < ng) {
+      wb[i] = *reinterpret_cast<const uint4 *>(bp + (size_t)(g0 + i) * 64);
+      if constexpr (VERIFY) wr[i] = *reinterpret_cast<const uint4 *>(rp + (size_t)(g0 + i) * 64);
+      ws[i] = sc[g0 + i];
+    }
+
+  // x -> fp16 in LDS: the 16 lanes of a (token, group) are consecutive
+  auto stage = [&](int it, const uint4 &v) {
+    const int tt = it / (ng * 16), gp = it - tt * ng * 16, gi = gp >> 4, p = gp & 15;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float f[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f[2 * q] = bf2f(w[q] & 0xFFFFu);
+      f[2 * q + 1] = bf2f(w[q] >> 16);
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(f[q]));
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    int e = 0;
+    if (m > 0.0f) {
+      int E;
+      frexpf(m, &E);
+      e = 15 - E;   // m * 2^e in [2^14, 2^15)
+    }
+    half8 h;
+    float gs = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      h[q] = (_Float16)ldexpf(f[q], e);
+      gs += (float)h[q];
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) gs += __shfl_xor(gs, o);
+    *reinterpret_cast<half8 *>(xs + (size_t)tt * a.pitch + gi * kGroup + p * 8) = h;
+    if (p == 0) meta[gi * T16 + tt] = make_float2(ldexpf(1.0f, -e), kBias * gs);
+  };
+#pragma unroll
+  for (int j = 0; j < kFirst; ++j)
+    if (t + j * kThreads < items) stage(t + j * kThreads, xv[j]);
+  for (int it = t + kFirst * kThreads; it < items; it += kThreads) {
+    const int tt = it / (ng * 16), gp = it - tt * ng * 16;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (tt < a.T) v = *reinterpret_cast<const uint4 *>(a.x + (size_t)tt * a.d_in + (size_t)g0 * kGroup + gp * 8);
+    stage(it, v);
+  }
+  __syncthreads();
+
+  floatx4 yacc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) yacc[mt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  const float sdiv = VERIFY ? 1.0f / 16.0f : 1.0f;
+  for (int gg = 0; gg < ng; gg += kRing) {
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) {
+      const int gi = gg + i;
+      if (gi < ng) {
+        uint32_t B[4][4];
+        unpack<VERIFY>(wb[i], VERIFY ? wr[i] : wb[i], B);
+        const float s = h2f(ws[i]) * sdiv;
+        if (gi + kRing < ng) {
+          wb[i] = *reinterpret_cast<const uint4 *>(bp + (size_t)(g0 + gi + kRing) * 64);
+          if constexpr (VERIFY) wr[i] = *reinterpret_cast<const uint4 *>(rp + (size_t)(g0 + gi + kRing) * 64);
+          ws[i] = sc[g0 + gi + kRing];
+        }
+        floatx4 acc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          half8 bh;
+          __builtin_memcpy(&bh, B[st], 16);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const half8 ah = *reinterpret_cast<const half8 *>(xs + (size_t)(mt * 16 + (lane & 15)) * a.pitch +
+                                                               gi * kGroup + kb * 32 + st * 8);
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc[mt], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const float4 *mp = reinterpret_cast<const float4 *>(meta + gi * T16 + mt * 16 + kb * 4);
+          const float4 m01 = mp[0], m23 = mp[1];   // {inv, bias*sum} of tokens 4kb .. 4kb+3
+          yacc[mt][0] += s * m01.x * (acc[mt][0] - m01.y);
+          yacc[mt][1] += s * m01.z * (acc[mt][1] - m01.w);
+          yacc[mt][2] += s * m23.x * (acc[mt][2] - m23.y);
+          yacc[mt][3] += s * m23.z * (acc[mt][3] - m23.w);
+        }
+      }
+    }
+  }
+
+  // outputs: token m = 16 mt + 4 kb + i of this lane's row
+  if (a.S == 1) {
+    if (row < a.d_out)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = mt * 16 + kb * 4 + i;
+          if (m < a.T) a.y[(size_t)m * a.d_out + row] = yacc[mt][i];
+        }
+    return;
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = mt * 16 + kb * 4 + i;
+      if (m < a.T) a.part[((size_t)sp * a.T + m) * a.rows_pad + row] = yacc[mt][i];
+    }
+  __threadfence();
+  __syncthreads();
+  __shared__ int last;
+  if (t == 0) last = atomicAdd(&a.tick[rb], 1u) == (uint32_t)(a.S - 1);
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  for (int idx = t; idx < a.T * kRows; idx += kThreads) {
+    const int m = idx / kRows, r = rb * kRows + (idx - m * kRows);
+    float acc = 0.0f;
+    for (int s2 = 0; s2 < a.S; ++s2) acc += ld_agent(a.part + ((size_t)s2 * a.T + m) * a.rows_pad + r);
+    if (r < a.d_out) a.y[(size_t)m * a.d_out + r] = acc;
+  }
+  if (t == 0) __hip_atomic_store(&a.tick[rb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+char g_msg[512];
+
+nl_status fail(nl_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+nl_status fail(nl_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof g_msg, fmt, ap);
+  va_end(ap);
+  return nl::api_error(st, g_msg);
+}
+
+nl_status ok() { return nl::api_error(NL_OK, ""); }
+
+#define HIP_OR_FAIL(expr)                                                              \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess)                                                              \
+      return fail(NL_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_));            \
+  } while (0)
+
+std::mutex g_mu;
+std::unordered_set<const void *> g_live;
+
+bool valid(nl_w4w8_handle h) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  return h && g_live.count(h) && h->magic == kMagic;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Plan {
+  int mt, S, gps, pitch;
+  size_t lds, tick_bytes, part_bytes;
+};
+
+// Split count: enough workgroups to fill the chip, few enough that the fp32
+// partials stay a small share of the weight bytes, and K-ranges whose x'
+// fits the LDS.
+Plan make_plan(const nl_w4w8 *h, int T) {
+  Plan p{};
+  p.mt = (T + 15) / 16;
+  const int T16 = 16 * p.mt;
+  const int kr_max = (int)((kLds / T16 - 16) / 2.0625);
+  const int gps_max = std::max(1, kr_max / kGroup);
+  const int n_rb = h->rows_pad / kRows;
+  const int s_min = (h->G + gps_max - 1) / gps_max;
+  const int s_fill = (kFillWgs + n_rb - 1) / n_rb;
+  const int s_traffic = std::max(1, (int)(0.03 * h->d_in / T));
+  int S = std::max(s_min, std::min(s_fill, s_traffic));
+  S = std::min(std::max(S, 1), h->G);
+  p.gps = (h->G + S - 1) / S;
+  p.S = (h->G + p.gps - 1) / p.gps;
+  p.pitch = p.gps * kGroup + 8;
+  p.lds = (size_t)T16 * p.pitch * 2 + (size_t)p.gps * T16 * 8;
+  p.tick_bytes = align256((size_t)n_rb * 4);
+  p.part_bytes = p.S > 1 ? (size_t)p.S * T * h->rows_pad * 4 : 0;
+  return p;
+}
+
+template <bool V, int MT>
+hipError_t launch_mt(const W48Args &a, const Plan &p, hipStream_t s) {
+  const dim3 grid((unsigned)(a.rows_pad / kRows * p.S)), block(kThreads);
+  hipLaunchKernelGGL((w48_kernel<V, MT>), grid, block, p.lds, s, a);
+  return hipGetLastError();
+}
+
+template <bool V>
+hipError_t launch(const W48Args &a, const Plan &p, hipStream_t s) {
+  switch (p.mt) {
+    case 1: return launch_mt<V, 1>(a, p, s);
+    case 2: return launch_mt<V, 2>(a, p, s);
+    case 3: return launch_mt<V, 3>(a, p, s);
+    case 4: return launch_mt<V, 4>(a, p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+nl_status forward(nl_w4w8_handle h, bool verify, const void *x, int32_t T, float *y, void *ws, size_t ws_bytes,
+                  void *stream, const char *who) {
+  if (!valid(h)) return fail(NL_EINVAL, "%s: invalid handle", who);
+  if (!x || !y || !ws) return fail(NL_EINVAL, "%s: x, y and ws must not be NULL", who);
+  if (T < 1) return fail(NL_EINVAL, "%s: T must be >= 1 (got %d)", who, T);
+  if (T > NL_MAX_T) return fail(NL_EUNSUPPORTED, "%s: T = %d exceeds %d", who, T, NL_MAX_T);
+  if ((uintptr_t)x & 15) return fail(NL_EINVAL, "%s: x must be 16-byte aligned", who);
+  if ((uintptr_t)ws & 255) return fail(NL_EINVAL, "%s: ws must be 256-byte aligned", who);
+  if (verify && !h->has_ref) return fail(NL_EINVAL, "%s: the linear has no refinement plane", who);
+  const Plan p = make_plan(h, T);
+  if (ws_bytes < p.tick_bytes + p.part_bytes)
+    return fail(NL_EINVAL, "%s: workspace of %zu bytes is smaller than %zu", who, ws_bytes,
+                p.tick_bytes + p.part_bytes);
+  W48Args a{};
+  a.base = h->base;
+  a.ref = h->ref;
+  a.scales = h->scales;
+  a.x = static_cast<const uint16_t *>(x);
+  a.y = y;
+  a.tick = static_cast<uint32_t *>(ws);
+  a.part = reinterpret_cast<float *>(static_cast<char *>(ws) + p.tick_bytes);
+  a.d_out = h->d_out;
+  a.d_in = h->d_in;
+  a.rows_pad = h->rows_pad;
+  a.G = h->G;
+  a.T = T;
+  a.S = p.S;
+  a.gps = p.gps;
+  a.pitch = p.pitch;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  HIP_OR_FAIL(verify ? launch<true>(a, p, s) : launch<false>(a, p, s));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" nl_status nested_w4w8_create(const nl_w4w8_desc *d, nl_w4w8_handle *out) {
+  static const char *who = "nested_w4w8_create";
+  if (!d || !out) return fail(NL_EINVAL, "%s: desc and out must not be NULL", who);
+  if (d->d_out < 1 || d->d_in < kGroup || d->d_in % kGroup)
+    return fail(NL_EINVAL, "%s: need d_out >= 1 and d_in a positive multiple of 128 (got %d x %d)", who, d->d_out,
+                d->d_in);
+  if (!d->base_plane || !d->scales) return fail(NL_EINVAL, "%s: base_plane and scales must not be NULL", who);
+  auto *h = new (std::nothrow) nl_w4w8{};
+  if (!h) return fail(NL_ENOMEM, "%s: host allocation failed", who);
+  h->magic = kMagic;
+  h->d_out = d->d_out;
+  h->d_in = d->d_in;
+  h->rows_pad = (d->d_out + kRows - 1) / kRows * kRows;
+  h->G = d->d_in / kGroup;
+  h->has_ref = d->ref_plane != nullptr;
+  const size_t plane = (size_t)h->rows_pad * (d->d_in / 2), sc = (size_t)h->rows_pad * h->G * 2;
+  const size_t used = (size_t)d->d_out * (d->d_in / 2), usc = (size_t)d->d_out * h->G * 2;
+  hipError_t e = hipMalloc(&h->base, plane);
+  if (e == hipSuccess && h->has_ref) e = hipMalloc(&h->ref, plane);
+  if (e == hipSuccess) e = hipMalloc(&h->scales, sc);
+  if (e == hipSuccess) e = hipMemset(h->base, 0, plane);
+  if (e == hipSuccess && h->has_ref) e = hipMemset(h->ref, 0, plane);
+  if (e == hipSuccess) e = hipMemset(h->scales, 0, sc);
+  if (e == hipSuccess) e = hipMemcpy(h->base, d->base_plane, used, hipMemcpyDeviceToDevice);
+  if (e == hipSuccess && h->has_ref) e = hipMemcpy(h->ref, d->ref_plane, used, hipMemcpyDeviceToDevice);
+  if (e == hipSuccess) e = hipMemcpy(h->scales, d->scales, usc, hipMemcpyDeviceToDevice);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    (void)hipFree(h->base);
+    (void)hipFree(h->ref);
+    (void)hipFree(h->scales);
+    delete h;
+    return fail(e == hipErrorOutOfMemory ? NL_ENOMEM : NL_EHIP, "%s: %s", who, hipGetErrorString(e));
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_live.insert(h);
+  }
+  *out = h;
+  return ok();
+}
+
+extern "C" nl_status nested_w4w8_destroy(nl_w4w8_handle h) {
+  if (!valid(h)) return fail(NL_EINVAL, "nested_w4w8_destroy: invalid handle");
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_live.erase(h);
+  }
+  (void)hipFree(h->base);
+  (void)hipFree(h->ref);
+  (void)hipFree(h->scales);
+  h->magic = 0;
+  delete h;
+  return ok();
+}
+
+extern "C" nl_status nested_w4w8_workspace_bytes(nl_w4w8_handle h, int32_t T_max, size_t *bytes) {
+  static const char *who = "nested_w4w8_workspace_bytes";
+  if (!valid(h)) return fail(NL_EINVAL, "%s: invalid handle", who);
+  if (!bytes) return fail(NL_EINVAL, "%s: bytes is NULL", who);
+  if (T_max < 1) return fail(NL_EINVAL, "%s: T_max must be >= 1", who);
+  if (T_max > NL_MAX_T) return fail(NL_EUNSUPPORTED, "%s: T_max = %d exceeds %d", who, T_max, NL_MAX_T);
+  size_t need = 0;
+  for (int T = 1; T <= T_max; ++T) {
+    const Plan p = make_plan(h, T);
+    need = std::max(need, p.tick_bytes + p.part_bytes);
+  }
+  *bytes = need;
+  return ok();
+}
+
+extern "C" nl_status nested_w4w8_verify(nl_w4w8_handle h, const void *x, int32_t T, float *y, void *ws,
+                                        size_t ws_bytes, void *stream) {
+  return forward(h, true, x, T, y, ws, ws_bytes, stream, "nested_w4w8_verify");
+}
+
+extern "C" nl_status nested_w4w8_draft(nl_w4w8_handle h, const void *x, int32_t T, float *y, void *ws,
+                                       size_t ws_bytes, void *stream) {
+  return forward(h, false, x, T, y, ws, ws_bytes, stream, "nested_w4w8_draft");
+}

@@ -17,7 +17,7 @@ def declared_symbols():
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
         txt = open(h).read()
         txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-        names |= set(re.findall(r"\b(nested_(?:linear|encode)\w*)\s*\(", txt))
+        names |= set(re.findall(r"\b(nested_(?:linear|encode|w4w8)\w*)\s*\(", txt))
     return names
 
 
