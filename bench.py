@@ -48,6 +48,10 @@ ENC_KERNEL = "tile_kernel<0, 7,"   # fused 7-bit encode, any block size (kernel-
 ENC_KERNEL_NAME = "tile_kernel<0, 7, LOG2B>"
 ENC_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encoder_tile_kernel_7bit_fused_proj7b8b_traffic.txt")
 FIT_ROWS = 512          # 512 x 4096 = 2^21 samples, the post's ~2M
+W48_TS = (1, 16, 64)
+W48_KERNEL = "w48_kernel<true, 1>"   # verify, one 16-token tile
+W48_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w48_kernel_verify_T16_proj7b8b_traffic.txt")
+W48_SOURCES = ("nl_w4w8.hip",)
 
 
 def log(*a):
@@ -400,6 +404,96 @@ def encoder_leg(nl, torch, synth, reps, cpu_seconds=0.0):
     return out
 
 
+def w4w8_bytes_per_weight(verify):
+    """Algorithmic bytes per weight of the W4/W8 dual-plane linear: one or
+    two 4-bit planes and one fp16 scale per 128 weights."""
+    return (1.0 if verify else 0.5) + 2.0 / 128
+
+
+def w4w8_leg(nl, torch, synth, reps, pool_gib, roofline_only=False):
+    """The BitNest W4/W8 dual-plane linear on the 7B/8B-class projections:
+    draft and verify at T = 1, 16 and 64, each (shape, mode, T) as a graph of
+    calls over a pool of distinct weight copies (so weights stream from HBM),
+    timed by events around the replays."""
+    import numpy as np
+    set_bytes = sum(o * i for _, o, i in SHAPES) * w4w8_bytes_per_weight(True)
+    ncopy = max(2, math.ceil(pool_gib * 2 ** 30 / set_bytes))
+    handles, xs, wss, ys = [], [], [], []
+    for si, (name, o, i) in enumerate(SHAPES):
+        lin = synth.make_w4w8_linear(o, i, cfg=60, idx=si)
+        d = [torch.from_numpy(np.ascontiguousarray(lin[k]).view(dt)).cuda()
+             for k, dt in (("base_plane", np.uint8), ("ref_plane", np.uint8), ("scales", np.int16))]
+        handles.append([nl.nested_w4w8_create(o, i, *d) for _ in range(ncopy)])
+        del d
+        xs.append(torch.from_numpy(synth.make_x(max(W48_TS), i, cfg=60, idx=si).view(np.int16)).cuda())
+        wss.append(torch.zeros(nl.nested_w4w8_workspace_bytes(handles[-1][0], max(W48_TS)), dtype=torch.uint8,
+                               device="cuda"))
+        ys.append(torch.empty((max(W48_TS), o), dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+
+    def call(si, cp, T, verify, stream):
+        (nl.nested_w4w8_verify if verify else nl.nested_w4w8_draft)(handles[si][cp], xs[si], T, ys[si], wss[si],
+                                                                     stream)
+
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    per_case, roof = {}, None
+    for T in ((16,) if roofline_only else W48_TS):
+        for verify in ((True,) if roofline_only else (True, False)):
+            tot_us = tot_b = 0.0
+            shp = {}
+            for si, (name, o, i) in enumerate(SHAPES):
+                s = torch.cuda.Stream()
+                s.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(s):
+                    for cp in range(ncopy):
+                        call(si, cp, T, verify, s)
+                torch.cuda.current_stream().wait_stream(s)
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    cs = torch.cuda.current_stream()
+                    for cp in range(ncopy):
+                        call(si, cp, T, verify, cs)
+                g.replay()
+                torch.cuda.synchronize()
+                e0.record()
+                for _ in range(reps):
+                    g.replay()
+                e1.record()
+                e1.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / reps / ncopy
+                del g
+                b = o * i * w4w8_bytes_per_weight(verify)
+                shp[name] = {"us": round(us, 2), "GBps": round(b / us / 1e3, 1)}
+                tot_us += us
+                tot_b += b
+            key = f"{'verify' if verify else 'draft'}_T{T}"
+            per_case[key] = {"us_per_pass": round(tot_us, 2), "GBps": round(tot_b / tot_us / 1e3, 1),
+                             "frac_hbm_peak": round(tot_b / tot_us / 1e3 / HBM_PEAK_GBPS, 3), "shapes": shp}
+            log(f"[bench] w4w8 {key}: {tot_us:.1f} us per pass, {tot_b / tot_us / 1e3:.0f} GB/s")
+            if verify and T == 16:
+                achieved = tot_b / tot_us / 1e3
+                digest = kernel_source_digest(W48_SOURCES)
+                tr = stored_traffic(digest, W48_TRAFFIC_FILE)
+                roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None if tr is None else round(tr),
+                        "kernel": W48_KERNEL + " (verify, T = 16, the four projections)",
+                        "avg_launch_us": round(tot_us / len(SHAPES), 2),
+                        "avg_algorithmic_bytes": int(tot_b / len(SHAPES)),
+                        "timing": "HIP events around graph replays of one launch per weight copy",
+                        "kernel_source_digest": digest}
+    for hs in handles:
+        for h in hs:
+            nl.nested_w4w8_destroy(h)
+    if roofline_only:
+        return {"per_case": per_case, "roofline": roof}
+    v1, v16 = per_case["verify_T1"]["us_per_pass"], per_case["verify_T16"]["us_per_pass"]
+    return {"format": "BitNest W4 base + 4-bit refinement planes, fp16 group-128 scales, no online rotation",
+            "pool_copies": ncopy, "per_case": per_case, "verify_T16_over_T1": round(v16 / v1, 3),
+            "roofline": roof}
+
+
 COPY_FLOATS = 64 << 20  # 256 MiB read + 256 MiB written per copy
 
 
@@ -416,6 +510,8 @@ def copy_calibration(torch):
 
 ROOFLINE_TITLE = ("verify, T = 8 and 16, 4096x4096, 1024x4096, 14336x4096,\n"
                   "4096x14336, 2-bit base + 6-bit residual, one-sided")
+W48_TITLE = ("verify at T = 16, W4 base + 4-bit refinement planes of 4096x4096, 1024x4096,\n"
+             "14336x4096, 4096x14336")
 ENC_TITLE = ("one-sided fused encode of dense fp32 4096x4096, 1024x4096, 14336x4096,\n"
              "4096x14336 into 2-bit base + 7-bit residual planes")
 
@@ -489,9 +585,17 @@ def main():
                     help="run only the encoder leg and the counter calibration copy (for rocprofv3)")
     ap.add_argument("--pmc-summary-encoder", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the encoder's traffic summary from two rocprofv3 --pmc runs of --encoder-only")
+    ap.add_argument("--w4w8-only", action="store_true",
+                    help="run only the W4/W8 leg and the counter calibration copy (for rocprofv3)")
+    ap.add_argument("--pmc-summary-w4w8", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the W4/W8 kernel's traffic summary from two rocprofv3 --pmc runs of --w4w8-only")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary, TRAFFIC_FILE)
+        return
+    if args.pmc_summary_w4w8:
+        pmc_summary(*args.pmc_summary_w4w8, W48_TRAFFIC_FILE, kernel=W48_KERNEL, prefix="", title=W48_TITLE,
+                    flag="--w4w8-only", digest=kernel_source_digest(W48_SOURCES))
         return
     if args.pmc_summary_encoder:
         pmc_summary(*args.pmc_summary_encoder, ENC_TRAFFIC_FILE, kernel=ENC_KERNEL, prefix="", title=ENC_TITLE,
@@ -514,6 +618,11 @@ def main():
     dev = "cuda"
     torch.cuda.set_device(0)
 
+    if args.w4w8_only:
+        w48 = w4w8_leg(nl, torch, synth, args.reps, args.pool_gib, roofline_only=True)
+        calib = copy_calibration(torch)
+        print(json.dumps({"w4w8": w48, "copy_calibration": calib}), flush=True)
+        return
     if args.encoder_only:
         enc = encoder_leg(nl, torch, synth, args.reps)
         calib = copy_calibration(torch)
@@ -706,6 +815,9 @@ def main():
             f"({m['verify']['GBps']:.0f} GB/s), draft T={m['draft']['T']} {m['draft']['us_per_pass']:.0f} us "
             f"({m['draft']['GBps']:.0f} GB/s)")
 
+    # ---- the BitNest W4/W8 dual-plane format (same contraction, other planes)
+    w4w8 = w4w8_leg(nl, torch, synth, args.reps, args.pool_gib)
+
     # ---- the offline encoder (dense W -> planes) and the level fit
     encoder = encoder_leg(nl, torch, synth, args.reps, cpu_seconds=0.0 if args.no_cpu_baseline else 3.0)
 
@@ -757,6 +869,7 @@ def main():
         "two_sided": two_sided,
         "moe_block": moe,
         "model_pass": model,
+        "w4w8": w4w8,
         "encoder": encoder,
         "decoder_layer": layer,
         "stream_read_GBps_torch_sum": round(stream_gbps, 1),

@@ -545,16 +545,18 @@ __global__ __launch_bounds__(kThreads) void lloyd_kernel(const double *v, int64_
 #pragma unroll
     for (int k = 0; k < 8; ++k) red[t >> 6][k] = val[k];
   __syncthreads();
+  // hand-over without fences (an agent-scope fence writes back the whole
+  // L2): agent-scope stores, acknowledged before the ticket is taken
   if (t < 8) {
     const double p = ((red[0][t] + red[1][t]) + red[2][t]) + red[3][t];
-    part[blockIdx.x * 8 + t] = p;
+    __hip_atomic_store(part + blockIdx.x * 8 + t, p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __threadfence();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (t == 0) last = atomicAdd(&st->ticket, 1u) == gridDim.x - 1;
+  if (t == 0)
+    last = __hip_atomic_fetch_add(&st->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
   __syncthreads();
   if (!last) return;
-  __threadfence();
   // quantity k = t & 7 over workgroups j, j + 32, ... (j = t >> 3), then a
   // fixed tree over j
   const int k = t & 7, j = t >> 3;

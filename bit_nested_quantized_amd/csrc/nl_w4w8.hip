@@ -1,15 +1,20 @@
 // nl_w4w8.hip -- the BitNest W4/W8 dual-plane linear (include/nested_w4w8.h).
 //
-// One launch per call.  A workgroup (4 waves) owns 64 rows and one K-split
-// of whole 128-column groups:
-//   * it stages its K-range of x for all tokens in LDS as fp16, each
-//     (token, group) scaled by a power of two that puts its largest
-//     magnitude in [2^14, 2^15) (bf16 -> fp16 is then exact), with the
-//     group's sum of x' and the inverse scale beside it;
-//   * each wave streams its 16-row tile's planes straight from the
-//     canonical layout through a ring of register sets: per group and lane
-//     16 bytes of the base plane (32 nibbles: the lane's 32 columns), 16 of
-//     the refinement plane (verify) and the row's fp16 scale;
+// Two launches per call.  w48_prep_kernel writes x' to the workspace once:
+// x as fp16, each (token, group) scaled by a power of two that puts its
+// largest magnitude in [2^14, 2^15) (bf16 -> fp16 is then exact), with the
+// inverse scale and the group's sum of x' beside it.  In w48_kernel a
+// workgroup (8 waves) owns 128 rows and one K-split of whole 128-column
+// groups:
+//   * it copies its K-range of x' and the metadata into LDS;
+//   * each wave streams its 16-row tile's planes through a ring of register
+//     sets: per group and lane 16 bytes of the base plane (32 nibbles: the
+//     lane's 32 columns), 16 of the refinement plane (verify) and the row's
+//     fp16 scale.  Create repacks the canonical planes tile-major: block
+//     (tile, group) holds lane l's 16 bytes at l * 16, so a wave reads one
+//     contiguous 1 KiB per plane and group, and its tile is one contiguous
+//     range (read straight from the row-major planes, a wave touched 16
+//     rows 2-7 KiB apart per load and HBM ran at a tenth of its rate);
 //   * the nibbles become the MFMA B operand as fp16 1024 + u, u the offset
 //     code (q4 + 8 for the draft, 16 (q4 + 8) + (q_r + 8) = 136 + 16 q4 + q_r
 //     for verify, so one v_mfma_f32_16x16x32_f16 per 32 columns and 16 tokens
@@ -50,8 +55,8 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kMagic = 0x4E573438u;  // "NW48"
 constexpr int kGroup = 128;
-constexpr int kRows = 64;       // rows per workgroup: 4 waves x 16
-constexpr int kThreads = 256;
+constexpr int kRows = 128;      // rows per workgroup: 8 waves x 16
+constexpr int kThreads = 512;
 constexpr int kRing = 6;        // groups in flight per wave
 constexpr int kLds = 60 * 1024;    // dynamic LDS budget (x' and its metadata)
 constexpr int kFillWgs = 512;   // workgroups a call aims for (2 per CU)
@@ -60,12 +65,54 @@ struct W48Args {
   const uint8_t *base;
   const uint8_t *ref;
   const uint16_t *scales;
-  const uint16_t *x;
+  const uint16_t *x;      // [T][d_in] bf16
+  _Float16 *xp;           // x' [T16][d_in] fp16 (workspace)
+  float2 *xm;             // [G][T16] {2^-e, sum of x'} (workspace)
   float *y;
-  float *part;      // [S][T][rows_pad]
-  uint32_t *tick;   // [rows_pad / 64]
-  int d_out, d_in, rows_pad, G, T, S, gps, pitch;
+  float *part;            // [S][T][rows_pad]
+  uint32_t *tick;         // [rows_pad / kRows]
+  int d_out, d_in, rows_pad, G, T, T16, S, gps, pitch;
 };
+
+// x -> x': one wave per 4 (token, group) pairs, 16 lanes of 8 columns each;
+// tokens T .. T16-1 get zeros.
+__global__ __launch_bounds__(256) void w48_prep_kernel(W48Args a) {
+  const int t = threadIdx.x;
+  const int pair = (blockIdx.x * 256 + t) >> 4, p = t & 15;
+  const int tt = pair / a.G, g = pair - tt * a.G;
+  if (tt >= a.T16) return;   // whole 16-lane groups leave together
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (tt < a.T) v = *reinterpret_cast<const uint4 *>(a.x + (size_t)tt * a.d_in + (size_t)g * kGroup + p * 8);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float f[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f[2 * q] = __uint_as_float(w[q] << 16);
+    f[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(f[q]));
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+  int e = 0;
+  if (m > 0.0f) {
+    int E;
+    frexpf(m, &E);
+    e = 15 - E;   // m * 2^e in [2^14, 2^15)
+  }
+  half8 h;
+  float gs = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    h[q] = (_Float16)ldexpf(f[q], e);
+    gs += (float)h[q];
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) gs += __shfl_xor(gs, o);
+  *reinterpret_cast<half8 *>(a.xp + (size_t)tt * a.d_in + (size_t)g * kGroup + p * 8) = h;
+  if (p == 0) a.xm[(size_t)g * a.T16 + tt] = make_float2(ldexpf(1.0f, -e), gs);
+}
 
 __device__ __forceinline__ float h2f(uint16_t h) {
   _Float16 v;
@@ -73,12 +120,17 @@ __device__ __forceinline__ float h2f(uint16_t h) {
   return (float)v;
 }
 
-__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
-
+// Split-K hand-over without fences (an agent-scope fence writes back the
+// whole L2): partials go out as agent-scope (sc1) stores, every thread waits
+// until its stores are acknowledged, and only then is the ticket taken; the
+// last workgroup reads them with agent-scope loads.
 __device__ __forceinline__ float ld_agent(const float *p) {
-  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT));
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void st_agent(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Four fp16 pairs 1024 + u from one dword of each plane (8 columns).
 // lo/hi: per byte j, the offset code of column 2j / 2j + 1.
@@ -107,7 +159,10 @@ __device__ __forceinline__ void unpack(const uint4 &b, const uint4 &r, uint32_t 
 }
 
 template <bool VERIFY, int MT>
-__global__ __launch_bounds__(kThreads) void w48_kernel(W48Args a) {
+// Two workgroups per CU (4 waves per SIMD, <= 128 VGPRs) up to two token
+// tiles; with three or four the accumulators need more registers and one
+// workgroup per CU runs.
+__global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int T16 = MT * 16;
   constexpr float kBias = VERIFY ? 1160.0f : 1032.0f;
@@ -119,74 +174,47 @@ __global__ __launch_bounds__(kThreads) void w48_kernel(W48Args a) {
   const int ng = min(a.G, g0 + a.gps) - g0;
   const int row = rb * kRows + wave * 16 + (lane & 15);
   const int kb = lane >> 4;
-  const uint8_t *bp = a.base + (size_t)row * (a.d_in / 2) + kb * 16;
-  const uint8_t *rp = VERIFY ? a.ref + (size_t)row * (a.d_in / 2) + kb * 16 : nullptr;
-  const uint16_t *sc = a.scales + (size_t)row * a.G;
+  const size_t tile = (size_t)rb * (kRows / 16) + wave;
+  const uint8_t *bp = a.base + tile * a.G * 1024 + lane * 16;            // + g * 1024
+  const uint8_t *rp = VERIFY ? a.ref + tile * a.G * 1024 + lane * 16 : nullptr;
+  const uint16_t *sc = a.scales + tile * a.G * 16 + (lane & 15);          // + g * 16
 
-  // x: first batch of loads before the weight ring's
-  const int items = T16 * ng * 16;   // (token, group, 16-byte piece)
-  constexpr int kFirst = 4;
-  uint4 xv[kFirst];
-#pragma unroll
-  for (int j = 0; j < kFirst; ++j) {
-    const int it = t + j * kThreads;
-    const int tt = it / (ng * 16), gp = it - tt * ng * 16;
-    xv[j] = make_uint4(0, 0, 0, 0);
-    if (it < items && tt < a.T)
-      xv[j] = *reinterpret_cast<const uint4 *>(a.x + (size_t)tt * a.d_in + (size_t)g0 * kGroup + gp * 8);
-  }
-
+  // The ring's loads are unconditional (group index clamped into the split)
+  // so the compiler can count them and wait for one set at a time; slots
+  // past the split's last group repeat it and are weighted 0.
   uint4 wb[kRing], wr[kRing];
   uint16_t ws[kRing];
 #pragma unroll
-  for (int i = 0; i < kRing; ++i)
-    if (i < ng) {
-      wb[i] = *reinterpret_cast<const uint4 *>(bp + (size_t)(g0 + i) * 64);
-      if constexpr (VERIFY) wr[i] = *reinterpret_cast<const uint4 *>(rp + (size_t)(g0 + i) * 64);
-      ws[i] = sc[g0 + i];
-    }
+  for (int i = 0; i < kRing; ++i) {
+    const int g = g0 + min(i, ng - 1);
+    wb[i] = *reinterpret_cast<const uint4 *>(bp + (size_t)g * 1024);
+    if constexpr (VERIFY) wr[i] = *reinterpret_cast<const uint4 *>(rp + (size_t)g * 1024);
+    ws[i] = sc[(size_t)g * 16];
+  }
 
-  // x -> fp16 in LDS: the 16 lanes of a (token, group) are consecutive
-  auto stage = [&](int it, const uint4 &v) {
-    const int tt = it / (ng * 16), gp = it - tt * ng * 16, gi = gp >> 4, p = gp & 15;
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    float f[8];
+  // x' of the K-range into LDS (16-byte pieces, four loads in flight per
+  // thread), then the metadata with the bias folded in
+  const int pieces = ng * 16, items = T16 * pieces;
+  for (int it0 = t; it0 < items; it0 += 4 * kThreads) {
+    uint4 v[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      f[2 * q] = bf2f(w[q] & 0xFFFFu);
-      f[2 * q + 1] = bf2f(w[q] >> 16);
-    }
-    float m = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(f[q]));
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-    int e = 0;
-    if (m > 0.0f) {
-      int E;
-      frexpf(m, &E);
-      e = 15 - E;   // m * 2^e in [2^14, 2^15)
-    }
-    half8 h;
-    float gs = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      h[q] = (_Float16)ldexpf(f[q], e);
-      gs += (float)h[q];
+    for (int j = 0; j < 4; ++j) {   // past the end: reload the last piece (in bounds, not stored)
+      const int it = min(it0 + j * kThreads, items - 1);
+      const int tt = it / pieces, pc = it - tt * pieces;
+      v[j] = *reinterpret_cast<const uint4 *>(a.xp + (size_t)tt * a.d_in + (size_t)g0 * kGroup + pc * 8);
     }
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) gs += __shfl_xor(gs, o);
-    *reinterpret_cast<half8 *>(xs + (size_t)tt * a.pitch + gi * kGroup + p * 8) = h;
-    if (p == 0) meta[gi * T16 + tt] = make_float2(ldexpf(1.0f, -e), kBias * gs);
-  };
-#pragma unroll
-  for (int j = 0; j < kFirst; ++j)
-    if (t + j * kThreads < items) stage(t + j * kThreads, xv[j]);
-  for (int it = t + kFirst * kThreads; it < items; it += kThreads) {
-    const int tt = it / (ng * 16), gp = it - tt * ng * 16;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (tt < a.T) v = *reinterpret_cast<const uint4 *>(a.x + (size_t)tt * a.d_in + (size_t)g0 * kGroup + gp * 8);
-    stage(it, v);
+    for (int j = 0; j < 4; ++j) {
+      const int it = it0 + j * kThreads;
+      if (it < items) {
+        const int tt = it / pieces, pc = it - tt * pieces;
+        *reinterpret_cast<uint4 *>(xs + (size_t)tt * a.pitch + pc * 8) = v[j];
+      }
+    }
+  }
+  for (int i = t; i < ng * T16; i += kThreads) {
+    const float2 mv = a.xm[(size_t)g0 * T16 + i];
+    meta[i] = make_float2(mv.x, kBias * mv.y);
   }
   __syncthreads();
 
@@ -194,42 +222,43 @@ __global__ __launch_bounds__(kThreads) void w48_kernel(W48Args a) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) yacc[mt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   const float sdiv = VERIFY ? 1.0f / 16.0f : 1.0f;
-  for (int gg = 0; gg < ng; gg += kRing) {
+  const int ngp = (ng + kRing - 1) / kRing * kRing;
+  for (int gg = 0; gg < ngp; gg += kRing) {
 #pragma unroll
     for (int i = 0; i < kRing; ++i) {
       const int gi = gg + i;
-      if (gi < ng) {
-        uint32_t B[4][4];
-        unpack<VERIFY>(wb[i], VERIFY ? wr[i] : wb[i], B);
-        const float s = h2f(ws[i]) * sdiv;
-        if (gi + kRing < ng) {
-          wb[i] = *reinterpret_cast<const uint4 *>(bp + (size_t)(g0 + gi + kRing) * 64);
-          if constexpr (VERIFY) wr[i] = *reinterpret_cast<const uint4 *>(rp + (size_t)(g0 + gi + kRing) * 64);
-          ws[i] = sc[g0 + gi + kRing];
-        }
-        floatx4 acc[MT];
+      const int gc = min(gi, ng - 1);
+      uint32_t B[4][4];
+      unpack<VERIFY>(wb[i], VERIFY ? wr[i] : wb[i], B);
+      const float s = gi < ng ? h2f(ws[i]) * sdiv : 0.0f;
+      {
+        const int g = g0 + min(gi + kRing, ng - 1);
+        wb[i] = *reinterpret_cast<const uint4 *>(bp + (size_t)g * 1024);
+        if constexpr (VERIFY) wr[i] = *reinterpret_cast<const uint4 *>(rp + (size_t)g * 1024);
+        ws[i] = sc[(size_t)g * 16];
+      }
+      floatx4 acc[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          half8 bh;
-          __builtin_memcpy(&bh, B[st], 16);
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            const half8 ah = *reinterpret_cast<const half8 *>(xs + (size_t)(mt * 16 + (lane & 15)) * a.pitch +
-                                                               gi * kGroup + kb * 32 + st * 8);
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc[mt], 0, 0, 0);
-          }
-        }
+      for (int st = 0; st < 4; ++st) {
+        half8 bh;
+        __builtin_memcpy(&bh, B[st], 16);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const float4 *mp = reinterpret_cast<const float4 *>(meta + gi * T16 + mt * 16 + kb * 4);
-          const float4 m01 = mp[0], m23 = mp[1];   // {inv, bias*sum} of tokens 4kb .. 4kb+3
-          yacc[mt][0] += s * m01.x * (acc[mt][0] - m01.y);
-          yacc[mt][1] += s * m01.z * (acc[mt][1] - m01.w);
-          yacc[mt][2] += s * m23.x * (acc[mt][2] - m23.y);
-          yacc[mt][3] += s * m23.z * (acc[mt][3] - m23.w);
+          const half8 ah = *reinterpret_cast<const half8 *>(xs + (size_t)(mt * 16 + (lane & 15)) * a.pitch +
+                                                             gc * kGroup + kb * 32 + st * 8);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc[mt], 0, 0, 0);
         }
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const float4 *mp = reinterpret_cast<const float4 *>(meta + gc * T16 + mt * 16 + kb * 4);
+        const float4 m01 = mp[0], m23 = mp[1];   // {inv, bias*sum} of tokens 4kb .. 4kb+3
+        yacc[mt][0] += s * m01.x * (acc[mt][0] - m01.y);
+        yacc[mt][1] += s * m01.z * (acc[mt][1] - m01.w);
+        yacc[mt][2] += s * m23.x * (acc[mt][2] - m23.y);
+        yacc[mt][3] += s * m23.z * (acc[mt][3] - m23.w);
       }
     }
   }
@@ -251,22 +280,60 @@ __global__ __launch_bounds__(kThreads) void w48_kernel(W48Args a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = mt * 16 + kb * 4 + i;
-      if (m < a.T) a.part[((size_t)sp * a.T + m) * a.rows_pad + row] = yacc[mt][i];
+      if (m < a.T) st_agent(a.part + ((size_t)sp * a.T + m) * a.rows_pad + row, yacc[mt][i]);
     }
-  __threadfence();
+  stores_done();
   __syncthreads();
   __shared__ int last;
-  if (t == 0) last = atomicAdd(&a.tick[rb], 1u) == (uint32_t)(a.S - 1);
+  if (t == 0)
+    last = __hip_atomic_fetch_add(&a.tick[rb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           (uint32_t)(a.S - 1);
   __syncthreads();
   if (!last) return;
-  __threadfence();
+  // partials in split order, eight loads in flight per output
   for (int idx = t; idx < a.T * kRows; idx += kThreads) {
     const int m = idx / kRows, r = rb * kRows + (idx - m * kRows);
+    const float *pp = a.part + (size_t)m * a.rows_pad + r;
+    const size_t stride = (size_t)a.T * a.rows_pad;
     float acc = 0.0f;
-    for (int s2 = 0; s2 < a.S; ++s2) acc += ld_agent(a.part + ((size_t)s2 * a.T + m) * a.rows_pad + r);
+    for (int s0 = 0; s0 < a.S; s0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = ld_agent(pp + (size_t)min(s0 + u, a.S - 1) * stride);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (s0 + u < a.S) acc += v[u];
+    }
     if (r < a.d_out) a.y[(size_t)m * a.d_out + r] = acc;
   }
   if (t == 0) __hip_atomic_store(&a.tick[rb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Canonical row-major planes -> tile-major blocks: thread = one lane's 16
+// bytes of one (tile, group) block of one plane; rows past d_out are zeros.
+__global__ __launch_bounds__(256) void w48_repack_kernel(const uint8_t *src, uint8_t *dst, int d_out, int d_in,
+                                                         int G, int64_t n_pieces) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_pieces) return;
+  const int lane = (int)(i & 63);
+  const int64_t blk = i >> 6;                  // tile * G + g
+  const int64_t tile = blk / G;
+  const int g = (int)(blk - tile * G);
+  const int64_t row = tile * 16 + (lane & 15);
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (row < d_out) v = *reinterpret_cast<const uint4 *>(src + row * (d_in / 2) + (int64_t)g * 64 + (lane >> 4) * 16);
+  *reinterpret_cast<uint4 *>(dst + i * 16) = v;
+}
+
+__global__ __launch_bounds__(256) void w48_repack_scales_kernel(const uint16_t *src, uint16_t *dst, int d_out,
+                                                                int G, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (tile * G + g) * 16 + r
+  if (i >= n) return;
+  const int r = (int)(i & 15);
+  const int64_t blk = i >> 4, tile = blk / G;
+  const int g = (int)(blk - tile * G);
+  const int64_t row = tile * 16 + r;
+  dst[i] = row < d_out ? src[row * G + g] : (uint16_t)0;
 }
 
 // ---------------------------------------------------------------------------
@@ -304,7 +371,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Plan {
   int mt, S, gps, pitch;
-  size_t lds, tick_bytes, part_bytes;
+  size_t lds, tick_bytes, xp_bytes, xm_bytes, part_bytes;
+  size_t total() const { return tick_bytes + xp_bytes + xm_bytes + part_bytes; }
 };
 
 // Split count: enough workgroups to fill the chip, few enough that the fp32
@@ -327,12 +395,18 @@ Plan make_plan(const nl_w4w8 *h, int T) {
   p.pitch = p.gps * kGroup + 8;
   p.lds = (size_t)T16 * p.pitch * 2 + (size_t)p.gps * T16 * 8;
   p.tick_bytes = align256((size_t)n_rb * 4);
+  p.xp_bytes = align256((size_t)T16 * h->d_in * 2);
+  p.xm_bytes = align256((size_t)h->G * T16 * 8);
   p.part_bytes = p.S > 1 ? (size_t)p.S * T * h->rows_pad * 4 : 0;
   return p;
 }
 
 template <bool V, int MT>
 hipError_t launch_mt(const W48Args &a, const Plan &p, hipStream_t s) {
+  const int pairs = a.T16 * a.G;   // (token, group) pairs, 16 per 256-thread workgroup
+  hipLaunchKernelGGL(w48_prep_kernel, dim3((unsigned)((pairs + 15) / 16)), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const dim3 grid((unsigned)(a.rows_pad / kRows * p.S)), block(kThreads);
   hipLaunchKernelGGL((w48_kernel<V, MT>), grid, block, p.lds, s, a);
   return hipGetLastError();
@@ -359,22 +433,25 @@ nl_status forward(nl_w4w8_handle h, bool verify, const void *x, int32_t T, float
   if ((uintptr_t)ws & 255) return fail(NL_EINVAL, "%s: ws must be 256-byte aligned", who);
   if (verify && !h->has_ref) return fail(NL_EINVAL, "%s: the linear has no refinement plane", who);
   const Plan p = make_plan(h, T);
-  if (ws_bytes < p.tick_bytes + p.part_bytes)
-    return fail(NL_EINVAL, "%s: workspace of %zu bytes is smaller than %zu", who, ws_bytes,
-                p.tick_bytes + p.part_bytes);
+  if (ws_bytes < p.total())
+    return fail(NL_EINVAL, "%s: workspace of %zu bytes is smaller than %zu", who, ws_bytes, p.total());
   W48Args a{};
   a.base = h->base;
   a.ref = h->ref;
   a.scales = h->scales;
   a.x = static_cast<const uint16_t *>(x);
   a.y = y;
-  a.tick = static_cast<uint32_t *>(ws);
-  a.part = reinterpret_cast<float *>(static_cast<char *>(ws) + p.tick_bytes);
+  char *w = static_cast<char *>(ws);
+  a.tick = reinterpret_cast<uint32_t *>(w);
+  a.xp = reinterpret_cast<_Float16 *>(w + p.tick_bytes);
+  a.xm = reinterpret_cast<float2 *>(w + p.tick_bytes + p.xp_bytes);
+  a.part = reinterpret_cast<float *>(w + p.tick_bytes + p.xp_bytes + p.xm_bytes);
   a.d_out = h->d_out;
   a.d_in = h->d_in;
   a.rows_pad = h->rows_pad;
   a.G = h->G;
   a.T = T;
+  a.T16 = 16 * p.mt;
   a.S = p.S;
   a.gps = p.gps;
   a.pitch = p.pitch;
@@ -401,16 +478,25 @@ extern "C" nl_status nested_w4w8_create(const nl_w4w8_desc *d, nl_w4w8_handle *o
   h->G = d->d_in / kGroup;
   h->has_ref = d->ref_plane != nullptr;
   const size_t plane = (size_t)h->rows_pad * (d->d_in / 2), sc = (size_t)h->rows_pad * h->G * 2;
-  const size_t used = (size_t)d->d_out * (d->d_in / 2), usc = (size_t)d->d_out * h->G * 2;
+  const int64_t pieces = (int64_t)(h->rows_pad / 16) * h->G * 64, nsc = (int64_t)(h->rows_pad / 16) * h->G * 16;
   hipError_t e = hipMalloc(&h->base, plane);
   if (e == hipSuccess && h->has_ref) e = hipMalloc(&h->ref, plane);
   if (e == hipSuccess) e = hipMalloc(&h->scales, sc);
-  if (e == hipSuccess) e = hipMemset(h->base, 0, plane);
-  if (e == hipSuccess && h->has_ref) e = hipMemset(h->ref, 0, plane);
-  if (e == hipSuccess) e = hipMemset(h->scales, 0, sc);
-  if (e == hipSuccess) e = hipMemcpy(h->base, d->base_plane, used, hipMemcpyDeviceToDevice);
-  if (e == hipSuccess && h->has_ref) e = hipMemcpy(h->ref, d->ref_plane, used, hipMemcpyDeviceToDevice);
-  if (e == hipSuccess) e = hipMemcpy(h->scales, d->scales, usc, hipMemcpyDeviceToDevice);
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(w48_repack_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, nullptr,
+                       d->base_plane, h->base, h->d_out, h->d_in, h->G, pieces);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess && h->has_ref) {
+    hipLaunchKernelGGL(w48_repack_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, nullptr,
+                       d->ref_plane, h->ref, h->d_out, h->d_in, h->G, pieces);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(w48_repack_scales_kernel, dim3((unsigned)((nsc + 255) / 256)), dim3(256), 0, nullptr,
+                       d->scales, h->scales, h->d_out, h->G, nsc);
+    e = hipGetLastError();
+  }
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     (void)hipFree(h->base);
@@ -450,7 +536,7 @@ extern "C" nl_status nested_w4w8_workspace_bytes(nl_w4w8_handle h, int32_t T_max
   size_t need = 0;
   for (int T = 1; T <= T_max; ++T) {
     const Plan p = make_plan(h, T);
-    need = std::max(need, p.tick_bytes + p.part_bytes);
+    need = std::max(need, p.total());
   }
   *bytes = need;
   return ok();

@@ -50,9 +50,10 @@ typedef struct {
 } nl_w4w8_desc;
 
 /*
- * Copy the arrays into library-owned device memory (rows padded to a
- * multiple of 64 with zeros; the planes keep their canonical layout).
- * Synchronises the device.  Errors: NL_EINVAL (shape, NULL pointer),
+ * Copy the arrays into library-owned device memory, repacked tile-major
+ * (16 rows x one 128-column group per 1 KiB block, rows padded to a multiple
+ * of 128 with zeros) so the kernels stream contiguous memory.  The caller
+ * may free its arrays when this returns.  Synchronises the device.  Errors: NL_EINVAL (shape, NULL pointer),
  * NL_ENOMEM, NL_EHIP.  *out is set only on success.
  */
 nl_status nested_w4w8_create(const nl_w4w8_desc *desc, nl_w4w8_handle *out);
