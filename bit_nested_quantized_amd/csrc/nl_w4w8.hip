@@ -1,12 +1,12 @@
 // nl_w4w8.hip -- the BitNest W4/W8 dual-plane linear (include/nested_w4w8.h).
 //
-// Two launches per call.  w48_prep_kernel writes x' to the workspace once:
-// x as fp16, each (token, group) scaled by a power of two that puts its
-// largest magnitude in [2^14, 2^15) (bf16 -> fp16 is then exact), with the
-// inverse scale and the group's sum of x' beside it.  In w48_kernel a
-// workgroup (8 waves) owns 128 rows and one K-split of whole 128-column
-// groups:
-//   * it copies its K-range of x' and the metadata into LDS;
+// One launch per call.  A workgroup (8 waves) owns 128 rows and one K-split
+// of whole 128-column groups:
+//   * it converts its K-range of x into LDS as fp16, each (token, group)
+//     scaled by a power of two that puts its largest magnitude in
+//     [2^14, 2^15) (bf16 -> fp16 is then exact), with the inverse scale and
+//     the group's sum of x' beside it (a separate conversion launch cost
+//     more than the repeated conversion: x is small and stays in L2);
 //   * each wave streams its 16-row tile's planes through a ring of register
 //     sets: per group and lane 16 bytes of the base plane (32 nibbles: the
 //     lane's 32 columns), 16 of the refinement plane (verify) and the row's
@@ -57,62 +57,27 @@ constexpr uint32_t kMagic = 0x4E573438u;  // "NW48"
 constexpr int kGroup = 128;
 constexpr int kRows = 128;      // rows per workgroup: 8 waves x 16
 constexpr int kThreads = 512;
-constexpr int kRing = 6;        // groups in flight per wave
-constexpr int kLds = 60 * 1024;    // dynamic LDS budget (x' and its metadata)
-constexpr int kFillWgs = 512;   // workgroups a call aims for (2 per CU)
+// Groups in flight per wave: 6, or 4 for verify with two token tiles (there
+// the x conversion's registers and the accumulators leave no room for more
+// within 128 VGPRs).
+template <bool VERIFY, int MT>
+constexpr int ring_depth() { return VERIFY && MT == 2 ? 4 : 6; }
+// Dynamic LDS budget for x' and its metadata, and the workgroups resident
+// per CU: two of 60 KiB up to two token tiles, one of 120 KiB beyond.
+constexpr int lds_budget(int mt) { return mt <= 2 ? 60 * 1024 : 120 * 1024; }
+constexpr int wgs_per_cu(int mt) { return mt <= 2 ? 2 : 1; }
+constexpr int kCus = 256;
 
 struct W48Args {
   const uint8_t *base;
   const uint8_t *ref;
   const uint16_t *scales;
   const uint16_t *x;      // [T][d_in] bf16
-  _Float16 *xp;           // x' [T16][d_in] fp16 (workspace)
-  float2 *xm;             // [G][T16] {2^-e, sum of x'} (workspace)
   float *y;
   float *part;            // [S][T][rows_pad]
   uint32_t *tick;         // [rows_pad / kRows]
-  int d_out, d_in, rows_pad, G, T, T16, S, gps, pitch;
+  int d_out, d_in, rows_pad, G, T, S, gps, pitch;
 };
-
-// x -> x': one wave per 4 (token, group) pairs, 16 lanes of 8 columns each;
-// tokens T .. T16-1 get zeros.
-__global__ __launch_bounds__(256) void w48_prep_kernel(W48Args a) {
-  const int t = threadIdx.x;
-  const int pair = (blockIdx.x * 256 + t) >> 4, p = t & 15;
-  const int tt = pair / a.G, g = pair - tt * a.G;
-  if (tt >= a.T16) return;   // whole 16-lane groups leave together
-  uint4 v = make_uint4(0, 0, 0, 0);
-  if (tt < a.T) v = *reinterpret_cast<const uint4 *>(a.x + (size_t)tt * a.d_in + (size_t)g * kGroup + p * 8);
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  float f[8];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    f[2 * q] = __uint_as_float(w[q] << 16);
-    f[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
-  }
-  float m = 0.0f;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(f[q]));
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-  int e = 0;
-  if (m > 0.0f) {
-    int E;
-    frexpf(m, &E);
-    e = 15 - E;   // m * 2^e in [2^14, 2^15)
-  }
-  half8 h;
-  float gs = 0.0f;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    h[q] = (_Float16)ldexpf(f[q], e);
-    gs += (float)h[q];
-  }
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) gs += __shfl_xor(gs, o);
-  *reinterpret_cast<half8 *>(a.xp + (size_t)tt * a.d_in + (size_t)g * kGroup + p * 8) = h;
-  if (p == 0) a.xm[(size_t)g * a.T16 + tt] = make_float2(ldexpf(1.0f, -e), gs);
-}
 
 __device__ __forceinline__ float h2f(uint16_t h) {
   _Float16 v;
@@ -166,6 +131,7 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int T16 = MT * 16;
   constexpr float kBias = VERIFY ? 1160.0f : 1032.0f;
+  constexpr int kRing = ring_depth<VERIFY, MT>();
   _Float16 *xs = reinterpret_cast<_Float16 *>(smem);
   float2 *meta = reinterpret_cast<float2 *>(smem + (size_t)T16 * a.pitch * 2);
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
@@ -192,29 +158,56 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
     ws[i] = sc[(size_t)g * 16];
   }
 
-  // x' of the K-range into LDS (16-byte pieces, four loads in flight per
-  // thread), then the metadata with the bias folded in
+  // x -> x' in LDS.  Item = (token, group, 16-byte piece); the 16 lanes of a
+  // (token, group) are consecutive, so its max and sum are lane exchanges.
+  // Four loads in flight per thread; items past the end reload the last one
+  // (in bounds) and are not staged.
   const int pieces = ng * 16, items = T16 * pieces;
   for (int it0 = t; it0 < items; it0 += 4 * kThreads) {
     uint4 v[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {   // past the end: reload the last piece (in bounds, not stored)
+    for (int j = 0; j < 4; ++j) {
       const int it = min(it0 + j * kThreads, items - 1);
       const int tt = it / pieces, pc = it - tt * pieces;
-      v[j] = *reinterpret_cast<const uint4 *>(a.xp + (size_t)tt * a.d_in + (size_t)g0 * kGroup + pc * 8);
+      v[j] = *reinterpret_cast<const uint4 *>(a.x + (size_t)min(tt, a.T - 1) * a.d_in + (size_t)g0 * kGroup +
+                                              pc * 8);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int it = it0 + j * kThreads;
       if (it < items) {
-        const int tt = it / pieces, pc = it - tt * pieces;
-        *reinterpret_cast<uint4 *>(xs + (size_t)tt * a.pitch + pc * 8) = v[j];
+        const int tt = it / pieces, pc = it - tt * pieces, gi = pc >> 4, p = pc & 15;
+        const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        float f[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f[2 * q] = tt < a.T ? __uint_as_float(w[q] << 16) : 0.0f;
+          f[2 * q + 1] = tt < a.T ? __uint_as_float(w[q] & 0xFFFF0000u) : 0.0f;
+        }
+        float m = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(f[q]));
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+        int e = 0;
+        if (m > 0.0f) {
+          int E;
+          frexpf(m, &E);
+          e = 15 - E;   // m * 2^e in [2^14, 2^15)
+        }
+        half8 h;
+        float gs = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          h[q] = (_Float16)ldexpf(f[q], e);
+          gs += (float)h[q];
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) gs += __shfl_xor(gs, o);
+        *reinterpret_cast<half8 *>(xs + (size_t)tt * a.pitch + pc * 8) = h;
+        if (p == 0) meta[gi * T16 + tt] = make_float2(ldexpf(1.0f, -e), kBias * gs);
       }
     }
-  }
-  for (int i = t; i < ng * T16; i += kThreads) {
-    const float2 mv = a.xm[(size_t)g0 * T16 + i];
-    meta[i] = make_float2(mv.x, kBias * mv.y);
   }
   __syncthreads();
 
@@ -371,42 +364,53 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Plan {
   int mt, S, gps, pitch;
-  size_t lds, tick_bytes, xp_bytes, xm_bytes, part_bytes;
-  size_t total() const { return tick_bytes + xp_bytes + xm_bytes + part_bytes; }
+  size_t lds, tick_bytes, part_bytes;
+  size_t total() const { return tick_bytes + part_bytes; }
 };
 
-// Split count: enough workgroups to fill the chip, few enough that the fp32
-// partials stay a small share of the weight bytes, and K-ranges whose x'
-// fits the LDS.
+// Split count: as many workgroups as fit the chip in one round, partials a
+// small share of the weight bytes (8 S T bytes per row written and read
+// against d_in: S <= 0.03 d_in / T keeps them under a quarter), and K-ranges
+// whose x' fits the LDS.
 Plan make_plan(const nl_w4w8 *h, int T) {
   Plan p{};
   p.mt = (T + 15) / 16;
   const int T16 = 16 * p.mt;
-  const int kr_max = (int)((kLds / T16 - 16) / 2.0625);
+  const int kr_max = (int)((lds_budget(p.mt) / T16 - 16) / 2.0625);
   const int gps_max = std::max(1, kr_max / kGroup);
   const int n_rb = h->rows_pad / kRows;
   const int s_min = (h->G + gps_max - 1) / gps_max;
-  const int s_fill = (kFillWgs + n_rb - 1) / n_rb;
-  const int s_traffic = std::max(1, (int)(0.03 * h->d_in / T));
-  int S = std::max(s_min, std::min(s_fill, s_traffic));
+  const int s_fill = std::max(1, wgs_per_cu(p.mt) * kCus / n_rb);
+  const int s_part = std::max(1, (int)(0.03 * h->d_in / T));
+  int S = std::max(s_min, std::min(s_fill, s_part));
   S = std::min(std::max(S, 1), h->G);
   p.gps = (h->G + S - 1) / S;
   p.S = (h->G + p.gps - 1) / p.gps;
   p.pitch = p.gps * kGroup + 8;
   p.lds = (size_t)T16 * p.pitch * 2 + (size_t)p.gps * T16 * 8;
   p.tick_bytes = align256((size_t)n_rb * 4);
-  p.xp_bytes = align256((size_t)T16 * h->d_in * 2);
-  p.xm_bytes = align256((size_t)h->G * T16 * 8);
   p.part_bytes = p.S > 1 ? (size_t)p.S * T * h->rows_pad * 4 : 0;
   return p;
 }
 
+// Kernels with more than 64 KiB of dynamic LDS must say so once per process.
+hipError_t allow_lds() {
+  static hipError_t e = [] {
+    hipError_t r = hipSuccess;
+    auto set = [&](const void *f) {
+      if (r == hipSuccess) r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds_budget(3));
+    };
+    set(reinterpret_cast<const void *>(&w48_kernel<true, 3>));
+    set(reinterpret_cast<const void *>(&w48_kernel<true, 4>));
+    set(reinterpret_cast<const void *>(&w48_kernel<false, 3>));
+    set(reinterpret_cast<const void *>(&w48_kernel<false, 4>));
+    return r;
+  }();
+  return e;
+}
+
 template <bool V, int MT>
 hipError_t launch_mt(const W48Args &a, const Plan &p, hipStream_t s) {
-  const int pairs = a.T16 * a.G;   // (token, group) pairs, 16 per 256-thread workgroup
-  hipLaunchKernelGGL(w48_prep_kernel, dim3((unsigned)((pairs + 15) / 16)), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const dim3 grid((unsigned)(a.rows_pad / kRows * p.S)), block(kThreads);
   hipLaunchKernelGGL((w48_kernel<V, MT>), grid, block, p.lds, s, a);
   return hipGetLastError();
@@ -443,15 +447,12 @@ nl_status forward(nl_w4w8_handle h, bool verify, const void *x, int32_t T, float
   a.y = y;
   char *w = static_cast<char *>(ws);
   a.tick = reinterpret_cast<uint32_t *>(w);
-  a.xp = reinterpret_cast<_Float16 *>(w + p.tick_bytes);
-  a.xm = reinterpret_cast<float2 *>(w + p.tick_bytes + p.xp_bytes);
-  a.part = reinterpret_cast<float *>(w + p.tick_bytes + p.xp_bytes + p.xm_bytes);
+  a.part = reinterpret_cast<float *>(w + p.tick_bytes);
   a.d_out = h->d_out;
   a.d_in = h->d_in;
   a.rows_pad = h->rows_pad;
   a.G = h->G;
   a.T = T;
-  a.T16 = 16 * p.mt;
   a.S = p.S;
   a.gps = p.gps;
   a.pitch = p.pitch;
@@ -498,6 +499,7 @@ extern "C" nl_status nested_w4w8_create(const nl_w4w8_desc *d, nl_w4w8_handle *o
     e = hipGetLastError();
   }
   if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = allow_lds();
   if (e != hipSuccess) {
     (void)hipFree(h->base);
     (void)hipFree(h->ref);
