@@ -548,7 +548,8 @@ def pmc_summary(fetch_dir, write_dir, out_path, kernel=ROOFLINE_KERNEL, prefix="
     kw = known / (sorted(w_cpy)[len(w_cpy) // 2] * 1024)
     fetch = sum(f_fwd) / len(f_fwd) * 1024 * kf
     write = sum(w_fwd) / len(w_fwd) * 1024 * kw
-    summ = "--pmc-summary" if flag == "--roofline-only" else "--pmc-summary-encoder"
+    summ = {"--roofline-only": "--pmc-summary", "--encoder-only": "--pmc-summary-encoder",
+            "--w4w8-only": "--pmc-summary-w4w8"}[flag]
     text = (f"HBM traffic of {display or kernel} ({title})\n"
             f"commands:\n"
             f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -o p -- python3 bench.py {flag}\n"
