@@ -29,7 +29,7 @@ linear_idx, stream]) with numpy's PCG64, so the host regenerates one linear
 at a time.  Stream ids: 0 sign_in, 1 sign_out, 2 base codes, 3 base scales,
 4 residual codes, 5 residual scales, 6 x, 7 router logits, 8 dense weights
 (the encoder's input), 9-11 the W4 codes, refinement codes and scales of the
-W4/W8 dual-plane format.
+W4/W8 dual-plane format, 12-13 draft-tree rank statistics and tokens.
 """
 from __future__ import annotations
 
@@ -49,6 +49,7 @@ STREAM_SIGN_IN, STREAM_SIGN_OUT, STREAM_BASE, STREAM_BASE_SCALE = 0, 1, 2, 3
 STREAM_RESID, STREAM_RESID_SCALE, STREAM_X, STREAM_ROUTER = 4, 5, 6, 7
 STREAM_DENSE = 8
 STREAM_W4, STREAM_W4_REF, STREAM_W4_SCALE = 9, 10, 11
+STREAM_TREE = 12
 
 
 def rng(cfg: int, linear_idx: int, stream: int) -> np.random.Generator:
@@ -184,6 +185,45 @@ def make_w4w8_linear(d_out: int, d_in: int, cfg: int = 0, idx: int = 0, keep_cod
     if keep_codes:
         lin["q4"], lin["qr"] = q4, qr
     return lin
+
+
+def make_rank_stats(D: int = 8, R: int = 16, cfg: int = 0, idx: int = 0) -> np.ndarray:
+    """Synthetic rank statistics p[D][R]: at depth d the verifier's token has
+    draft rank r with probability proportional to exp(-r / tau_d) (tau
+    shrinking with depth: the draft gets worse further out), scaled by a
+    per-depth acceptance mass a_d decaying from 0.8; rows sum to a_d <= 1.
+    A little noise keeps products distinct."""
+    g = rng(cfg, idx, STREAM_TREE)
+    out = np.zeros((D, R))
+    for d in range(D):
+        tau = 1.5 / (1.0 + 0.25 * d)
+        w = np.exp(-np.arange(R) / tau) * g.uniform(0.9, 1.1, R)
+        out[d] = 0.8 * (0.95 ** d) * w / w.sum()
+    return out
+
+
+def make_tree_tokens(parent: np.ndarray, B: int, vocab: int = 32000, p_match: float = 0.7, cfg: int = 0,
+                     idx: int = 0):
+    """Draft tokens of a tree's nodes for B sequences (siblings distinct) and
+    the verifier's argmax after the root and after each node: with
+    probability p_match the argmax is the token of one of the node's
+    children (if it has any), else a token no child carries."""
+    g = rng(cfg, idx, STREAM_TREE + 1)
+    N = len(parent)
+    draft = np.zeros((B, N), np.int32)
+    argmax = np.zeros((B, N + 1), np.int32)
+    kids = [[c for c in range(N) if parent[c] == u] for u in range(-1, N)]
+    for b in range(B):
+        for u in range(-1, N):
+            ks = kids[u + 1]
+            toks = g.choice(vocab - 1, size=len(ks) + 1, replace=False).astype(np.int32)
+            for c, tkn in zip(ks, toks[:-1]):
+                draft[b, c] = tkn
+            if ks and g.random() < p_match:
+                argmax[b, u + 1] = draft[b, ks[g.integers(len(ks))]]
+            else:
+                argmax[b, u + 1] = toks[-1]
+    return draft, argmax
 
 
 def make_linear(d_out: int, d_in: int, bits: int, cfg: int = 0, idx: int = 0,
