@@ -300,6 +300,61 @@ def roofline_leg(nl, call, ncopy, stream, bpw):
             "kernel_source_digest": digest}
 
 
+def tree_leg(nl, torch, synth, reps, cpu_seconds=0.0):
+    """The draft tree: best-first build of 64 nodes from 8 x 16 rank
+    statistics (one workgroup), and greedy acceptance for a batch of 1024
+    sequences sharing that tree (one wave each).  Both are latency work;
+    each is timed over back-to-back launches on the stream between two
+    events."""
+    import numpy as np
+    D, R, N, B = 8, 16, 64, 1024
+    p = synth.make_rank_stats(D, R, cfg=90)
+    pd = torch.from_numpy(p).cuda()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t = nl.tree_build(pd, N)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        nl.nested_tree_build(pd, D, R, N, t["parent"], t["depth"], t["rank"], t["prio"], t["anc"], t["count"])
+    e1.record()
+    e1.synchronize()
+    build_us = e0.elapsed_time(e1) * 1e3 / reps
+    par = t["parent"].cpu().numpy()
+    draft, argmax = synth.make_tree_tokens(par, B, cfg=90)
+    dd = torch.from_numpy(draft).cuda()
+    da = torch.from_numpy(argmax).cuda()
+    n, path, bonus = nl.tree_accept(t["parent"], dd, da)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        nl.nested_tree_accept(t["parent"], N, B, dd, da, n, path, bonus)
+    e1.record()
+    e1.synchronize()
+    acc_us = e0.elapsed_time(e1) * 1e3 / reps
+    mean_acc = float(n.float().mean().item()) + 1.0
+    # expected tokens per check from the statistics: the sum of the node priorities + 1
+    out = {"build": {"D": D, "R": R, "N": N, "us": round(build_us, 2)},
+           "accept": {"B": B, "N": N, "us_per_batch": round(acc_us, 2),
+                      "sequences_per_s": round(B / acc_us * 1e6),
+                      "mean_tokens_per_check": round(mean_acc, 3)},
+           "expected_tokens_per_check_from_stats": round(float(t["prio"].sum().item()) + 1.0, 3),
+           "bound": "latency (one wave per tree or sequence)"}
+    if cpu_seconds > 0:
+        import oracle.tree as otree
+        t0, k = time.time(), 0
+        while time.time() - t0 < cpu_seconds:
+            otree.build(p, N)
+            for b in range(B):
+                otree.accept(par, draft[b], argmax[b])
+            k += 1
+        dt = time.time() - t0
+        out["cpu_baseline"] = {"value": round(k * B / dt), "unit": "sequences/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{k} build(s) + {k * B} acceptances in {dt:.1f} s"}
+    log(f"[bench] tree: build {build_us:.1f} us, accept {acc_us:.1f} us per {B} sequences")
+    return out
+
+
 def encoder_bytes_per_weight(bits):
     """Algorithmic HBM bytes per weight of the fused one-sided encode: the
     fp32 weight read; the 2-bit base planes, the b-bit residual and two fp16
@@ -819,6 +874,9 @@ def main():
     # ---- the BitNest W4/W8 dual-plane format (same contraction, other planes)
     w4w8 = w4w8_leg(nl, torch, synth, args.reps, args.pool_gib)
 
+    # ---- the draft tree (build once from the statistics, accept per step)
+    draft_tree = tree_leg(nl, torch, synth, args.reps, cpu_seconds=0.0 if args.no_cpu_baseline else 2.0)
+
     # ---- the offline encoder (dense W -> planes) and the level fit
     encoder = encoder_leg(nl, torch, synth, args.reps, cpu_seconds=0.0 if args.no_cpu_baseline else 3.0)
 
@@ -871,6 +929,7 @@ def main():
         "moe_block": moe,
         "model_pass": model,
         "w4w8": w4w8,
+        "draft_tree": draft_tree,
         "encoder": encoder,
         "decoder_layer": layer,
         "stream_read_GBps_torch_sum": round(stream_gbps, 1),

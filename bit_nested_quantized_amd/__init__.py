@@ -33,7 +33,7 @@ EXPORTS = (
     "nested_encode_rotate", "nested_encode_quantize", "nested_encode_workspace_bytes", "nested_encode",
     "nested_encode_normalize", "nested_encode_fit_workspace_bytes", "nested_encode_fit_levels",
     "nested_w4w8_create", "nested_w4w8_destroy", "nested_w4w8_workspace_bytes", "nested_w4w8_verify",
-    "nested_w4w8_draft",
+    "nested_w4w8_draft", "nested_tree_build", "nested_tree_accept",
 )
 
 
@@ -107,6 +107,8 @@ def lib() -> ctypes.CDLL:
             "nested_w4w8_workspace_bytes": [P, i32, ctypes.POINTER(sz)],
             "nested_w4w8_verify": [P, P, i32, P, P, sz, P],
             "nested_w4w8_draft": [P, P, i32, P, P, sz, P],
+            "nested_tree_build": [P, i32, i32, i32, P, P, P, P, P, P, P],
+            "nested_tree_accept": [P, i32, i32, P, P, P, P, P, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -386,6 +388,43 @@ class W4W8Linear:
         y = torch.empty((T, self.d_out), dtype=torch.float32, device=x.device) if y is None else y
         (nested_w4w8_verify if verify else nested_w4w8_draft)(self.h, x, T, y, ws, stream)
         return y
+
+
+# --- draft tree (include/nested_tree.h) ----------------------------------------
+
+def nested_tree_build(p, D: int, R: int, N: int, parent, depth, rank, prio, anc, count, stream=None):
+    _check(lib().nested_tree_build(_ptr(p), int(D), int(R), int(N), _ptr(parent), _ptr(depth), _ptr(rank),
+                                   _ptr(prio), _ptr(anc), _ptr(count), _stream(stream)))
+
+
+def nested_tree_accept(parent, N: int, B: int, draft_token, argmax, n_accepted, path, bonus, stream=None):
+    _check(lib().nested_tree_accept(_ptr(parent), int(N), int(B), _ptr(draft_token), _ptr(argmax),
+                                    _ptr(n_accepted), _ptr(path), _ptr(bonus), _stream(stream)))
+
+
+def tree_build(p, N: int, stream=None) -> dict:
+    """Best-first tree from a device fp64 tensor p [D][R]; device outputs."""
+    import torch
+    D, R = p.shape
+    dev = p.device
+    out = {"parent": torch.empty(N, dtype=torch.int32, device=dev), "depth": torch.empty(N, dtype=torch.int32, device=dev),
+           "rank": torch.empty(N, dtype=torch.int32, device=dev), "prio": torch.empty(N, dtype=torch.float64, device=dev),
+           "anc": torch.empty(N, dtype=torch.int64, device=dev), "count": torch.empty(1, dtype=torch.int32, device=dev)}
+    nested_tree_build(p, D, R, N, out["parent"], out["depth"], out["rank"], out["prio"], out["anc"], out["count"],
+                      stream)
+    return out
+
+
+def tree_accept(parent, draft_token, argmax, stream=None):
+    """Greedy acceptance for B sequences (device int32 tensors)."""
+    import torch
+    B, N = draft_token.shape
+    dev = draft_token.device
+    n = torch.empty(B, dtype=torch.int32, device=dev)
+    path = torch.full((B, N), -1, dtype=torch.int32, device=dev)
+    bonus = torch.empty(B, dtype=torch.int32, device=dev)
+    nested_tree_accept(parent, N, B, draft_token, argmax, n, path, bonus, stream)
+    return n, path, bonus
 
 
 class Linear:

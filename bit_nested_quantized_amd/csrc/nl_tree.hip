@@ -1,0 +1,144 @@
+// nl_tree.hip -- best-first draft tree and greedy acceptance
+// (include/nested_tree.h).
+//
+// Build: one wave.  Candidate slot s < R is the root's child of rank s; slot
+// R + k R + r is node k's child of rank r, so slot order is push order and
+// "largest priority, then smallest slot" is the heap-with-counter order.
+// Each step is a wave-wide argmax over the live slots in LDS; the winner
+// becomes node k and its R children are written by R lanes.
+//
+// Accept: one wave per sequence; lane c holds node c's parent and token, and
+// each step is one ballot for the child of the current node whose token is
+// the verifier's argmax.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+
+#include "../../include/nested_tree.h"
+
+namespace nl {
+nl_status api_error(nl_status st, const char *msg);  // nl_api.hip
+}
+
+namespace {
+
+constexpr int kMaxSlots = NL_TREE_MAX_RANKS * (1 + NL_TREE_MAX_NODES);
+
+__global__ __launch_bounds__(64) void tree_build_kernel(const double *p, int D, int R, int N, int32_t *parent,
+                                                        int32_t *depth, int32_t *rank, double *prio,
+                                                        uint64_t *anc, int32_t *count) {
+  __shared__ double cp[kMaxSlots];
+  __shared__ int ndep[NL_TREE_MAX_NODES];
+  __shared__ uint64_t nanc[NL_TREE_MAX_NODES];
+  const int lane = threadIdx.x;
+  const int S = R + N * R;
+  for (int s = lane; s < S; s += 64) cp[s] = s < R ? p[s] : -1.0;   // depth-1 paths
+  __syncthreads();
+  int k = 0;
+  for (; k < N; ++k) {
+    double bp = -1.0;
+    int bs = 0x7FFFFFFF;
+    for (int s = lane; s < S; s += 64)
+      if (cp[s] > bp) {   // ascending slots: an equal later slot never wins
+        bp = cp[s];
+        bs = s;
+      }
+    for (int o = 32; o >= 1; o >>= 1) {
+      const double op = __shfl_xor(bp, o);
+      const int os = __shfl_xor(bs, o);
+      if (op > bp || (op == bp && os < bs)) {
+        bp = op;
+        bs = os;
+      }
+    }
+    if (bp < 0.0) break;   // no live candidate (uniform)
+    const int par = bs < R ? -1 : (bs - R) / R;
+    const int rk = bs < R ? bs : (bs - R) % R;
+    const int dep = par < 0 ? 1 : ndep[par] + 1;
+    const uint64_t am = (par < 0 ? 0ull : nanc[par]) | (1ull << k);
+    __syncthreads();
+    if (lane == 0) {
+      cp[bs] = -1.0;
+      ndep[k] = dep;
+      nanc[k] = am;
+      parent[k] = par;
+      depth[k] = dep;
+      rank[k] = rk;
+      prio[k] = bp;
+      anc[k] = am;
+    }
+    if (dep < D && lane < R) cp[R + k * R + lane] = bp * p[dep * R + lane];
+    __syncthreads();
+  }
+  if (lane == 0) *count = k;
+}
+
+__global__ __launch_bounds__(64) void tree_accept_kernel(const int32_t *parent, int N, const int32_t *draft,
+                                                         const int32_t *argmax, int32_t *n_acc, int32_t *path,
+                                                         int32_t *bonus) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int par = lane < N ? parent[lane] : -2;
+  const int tok = lane < N ? draft[(size_t)b * N + lane] : 0;
+  const int32_t *am = argmax + (size_t)b * (N + 1);
+  int u = -1, len = 0;
+  for (int step = 0; step < N; ++step) {
+    const int target = am[u + 1];
+    const unsigned long long m = __ballot(par == u && tok == target);
+    if (!m) break;
+    const int c = __ffsll((long long)m) - 1;
+    if (lane == 0) path[(size_t)b * N + len] = c;
+    ++len;
+    u = c;
+  }
+  if (lane == 0) {
+    n_acc[b] = len;
+    bonus[b] = am[u + 1];
+  }
+}
+
+char g_msg[256];
+
+nl_status fail(const char *fmt, ...) __attribute__((format(printf, 1, 2)));
+nl_status fail(const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof g_msg, fmt, ap);
+  va_end(ap);
+  return nl::api_error(NL_EINVAL, g_msg);
+}
+
+nl_status launched(const char *who) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    snprintf(g_msg, sizeof g_msg, "%s: launch failed: %s", who, hipGetErrorString(e));
+    return nl::api_error(NL_EHIP, g_msg);
+  }
+  return nl::api_error(NL_OK, "");
+}
+
+}  // namespace
+
+extern "C" nl_status nested_tree_build(const double *p, int32_t D, int32_t R, int32_t N, int32_t *parent,
+                                       int32_t *depth, int32_t *rank, double *prio, uint64_t *anc, int32_t *count,
+                                       void *stream) {
+  if (D < 1) return fail("nested_tree_build: D must be >= 1 (got %d)", D);
+  if (R < 1 || R > NL_TREE_MAX_RANKS) return fail("nested_tree_build: R must be in 1..%d (got %d)", NL_TREE_MAX_RANKS, R);
+  if (N < 1 || N > NL_TREE_MAX_NODES) return fail("nested_tree_build: N must be in 1..%d (got %d)", NL_TREE_MAX_NODES, N);
+  if (!p || !parent || !depth || !rank || !prio || !anc || !count)
+    return fail("nested_tree_build: NULL pointer");
+  hipLaunchKernelGGL(tree_build_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), p, D, R, N, parent,
+                     depth, rank, prio, anc, count);
+  return launched("nested_tree_build");
+}
+
+extern "C" nl_status nested_tree_accept(const int32_t *parent, int32_t N, int32_t B, const int32_t *draft,
+                                        const int32_t *argmax, int32_t *n_acc, int32_t *path, int32_t *bonus,
+                                        void *stream) {
+  if (N < 1 || N > NL_TREE_MAX_NODES) return fail("nested_tree_accept: N must be in 1..%d (got %d)", NL_TREE_MAX_NODES, N);
+  if (B < 1) return fail("nested_tree_accept: B must be >= 1 (got %d)", B);
+  if (!parent || !draft || !argmax || !n_acc || !path || !bonus) return fail("nested_tree_accept: NULL pointer");
+  hipLaunchKernelGGL(tree_accept_kernel, dim3((unsigned)B), dim3(64), 0, static_cast<hipStream_t>(stream), parent, N,
+                     draft, argmax, n_acc, path, bonus);
+  return launched("nested_tree_accept");
+}

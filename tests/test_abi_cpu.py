@@ -17,7 +17,7 @@ def declared_symbols():
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
         txt = open(h).read()
         txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-        names |= set(re.findall(r"\b(nested_(?:linear|encode|w4w8)\w*)\s*\(", txt))
+        names |= set(re.findall(r"\b(nested_(?:linear|encode|w4w8|tree)\w*)\s*\(", txt))
     return names
 
 
@@ -130,3 +130,14 @@ def test_encoder_rejects_bad_arguments_without_touching_the_gpu():
     assert L.nested_encode_fit_levels(16, 100, -1, out, 256, sz.value, None) == nl.NL_EINVAL
     assert L.nested_encode_fit_levels(16, 100, 60, out, 256, sz.value - 8, None) == nl.NL_EINVAL
     assert L.nested_encode_fit_levels(16, 100, 60, out, 300, sz.value, None) == nl.NL_EINVAL
+
+
+def test_tree_calls_reject_bad_arguments():
+    L = nl.lib()
+    for D, R, N in [(0, 4, 8), (3, 0, 8), (3, 17, 8), (3, 4, 0), (3, 4, 65)]:
+        assert L.nested_tree_build(16, D, R, N, 16, 16, 16, 16, 16, 16, None) == nl.NL_EINVAL
+    assert L.nested_tree_build(None, 3, 4, 8, 16, 16, 16, 16, 16, 16, None) == nl.NL_EINVAL
+    for N, B in [(0, 4), (65, 4), (8, 0)]:
+        assert L.nested_tree_accept(16, N, B, 16, 16, 16, 16, 16, None) == nl.NL_EINVAL
+    assert L.nested_tree_accept(16, 8, 4, None, 16, 16, 16, 16, None) == nl.NL_EINVAL
+    assert b"N must be" in L.nested_linear_last_error() or L.nested_linear_last_error()
