@@ -19,7 +19,9 @@ tree-attention mask of the forum post's POC section 6 tree.
 Readings (listed with the design notes):
   * the quantiser runs in fp32 on bf16 inputs: s = fp32(max|x| / 7), the
     quotients are correctly rounded fp32 divisions, round() is
-    round-half-even, x - q4 s is an fp32 product then an fp32 difference;
+    round-half-even, and the residual x - q4 s is formed exactly and rounded
+    once to fp32 (eq. 13 is stated over the reals; forming it exactly is the
+    plainest fp32 rendering, and it is what a fused multiply-add computes);
     a zero vector stores s = 0 and zero codes;
   * planes are two's-complement nibbles, dimension k in byte k/2 (low nibble
     for even k), 64 bytes per (position, KV head) row; the scale is fp32;
@@ -46,7 +48,9 @@ def quantize(x_bf16):
     sc = s[:, None]
     with np.errstate(divide="ignore", invalid="ignore"):
         q4 = np.where(sc > 0, np.clip(np.rint(x / sc), -8, 7), 0).astype(np.float32)
-        r = (x - (q4 * sc).astype(np.float32)).astype(np.float32)
+        # exact in fp64 (a 4-bit integer times an fp32 scale, then a difference
+        # of nearby values), rounded once to fp32
+        r = (x.astype(np.float64) - q4.astype(np.float64) * sc.astype(np.float64)).astype(np.float32)
         qr = np.where(sc > 0, np.clip(np.rint(r / (sc / np.float32(16.0))), -8, 7), 0)
     return q4.astype(np.int8), qr.astype(np.int8), s
 
