@@ -34,6 +34,7 @@ EXPORTS = (
     "nested_encode_normalize", "nested_encode_fit_workspace_bytes", "nested_encode_fit_levels",
     "nested_w4w8_create", "nested_w4w8_destroy", "nested_w4w8_workspace_bytes", "nested_w4w8_verify",
     "nested_w4w8_draft", "nested_tree_build", "nested_tree_accept",
+    "nested_kv_write", "nested_kv_attention_workspace_bytes", "nested_kv_attention",
 )
 
 
@@ -109,6 +110,9 @@ def lib() -> ctypes.CDLL:
             "nested_w4w8_draft": [P, P, i32, P, P, sz, P],
             "nested_tree_build": [P, i32, i32, i32, P, P, P, P, P, P, P],
             "nested_tree_accept": [P, i32, i32, P, P, P, P, P, P],
+            "nested_kv_write": [P, i32, P, P, P, P, P],
+            "nested_kv_attention_workspace_bytes": [i32, i32, i32, i32, ctypes.POINTER(sz)],
+            "nested_kv_attention": [P, i32, i32, i32, i32, P, P, P, P, P, P, P, i32, P, P, sz, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -425,6 +429,25 @@ def tree_accept(parent, draft_token, argmax, stream=None):
     bonus = torch.empty(B, dtype=torch.int32, device=dev)
     nested_tree_accept(parent, N, B, draft_token, argmax, n, path, bonus, stream)
     return n, path, bonus
+
+
+# --- nested KV cache (include/nested_kv.h) -------------------------------------
+
+def nested_kv_write(x, n: int, row, base, ref, scale, stream=None):
+    _check(lib().nested_kv_write(_ptr(x), int(n), _ptr(row), _ptr(base), _ptr(ref), _ptr(scale), _stream(stream)))
+
+
+def nested_kv_attention_workspace_bytes(T: int, H_q: int, H_kv: int, L: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().nested_kv_attention_workspace_bytes(int(T), int(H_q), int(H_kv), int(L), ctypes.byref(n)))
+    return n.value
+
+
+def nested_kv_attention(q, T: int, H_q: int, H_kv: int, L: int, k_base, k_ref, k_scale, v_base, v_ref, v_scale, anc,
+                        verify: bool, out, ws, stream=None):
+    _check(lib().nested_kv_attention(_ptr(q), int(T), int(H_q), int(H_kv), int(L), _ptr(k_base), _ptr(k_ref),
+                                     _ptr(k_scale), _ptr(v_base), _ptr(v_ref), _ptr(v_scale), _ptr(anc),
+                                     int(bool(verify)), _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 class Linear:

@@ -17,7 +17,7 @@ def declared_symbols():
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
         txt = open(h).read()
         txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-        names |= set(re.findall(r"\b(nested_(?:linear|encode|w4w8|tree)\w*)\s*\(", txt))
+        names |= set(re.findall(r"\b(nested_(?:linear|encode|w4w8|tree|kv)\w*)\s*\(", txt))
     return names
 
 
@@ -141,3 +141,18 @@ def test_tree_calls_reject_bad_arguments():
         assert L.nested_tree_accept(16, N, B, 16, 16, 16, 16, 16, None) == nl.NL_EINVAL
     assert L.nested_tree_accept(16, 8, 4, None, 16, 16, 16, 16, None) == nl.NL_EINVAL
     assert b"N must be" in L.nested_linear_last_error() or L.nested_linear_last_error()
+
+
+def test_kv_calls_reject_bad_arguments():
+    L = nl.lib()
+    sz = ctypes.c_size_t()
+    for T, H_q, H_kv, Lc in [(0, 8, 2, 10), (65, 8, 2, 10), (4, 6, 4, 10), (4, 8, 0, 10), (64, 32, 4, 10), (4, 8, 2, -1)]:
+        assert L.nested_kv_attention_workspace_bytes(T, H_q, H_kv, Lc, ctypes.byref(sz)) == nl.NL_EINVAL
+    assert L.nested_kv_attention_workspace_bytes(16, 32, 8, 4096, ctypes.byref(sz)) == nl.NL_OK and sz.value > 0
+    assert L.nested_kv_write(16, 0, 16, 16, 16, 16, None) == nl.NL_EINVAL
+    assert L.nested_kv_write(None, 4, 16, 16, 16, 16, None) == nl.NL_EINVAL
+    # verify without the refinement planes; small workspace
+    assert L.nested_kv_attention(256, 4, 8, 2, 10, 256, None, 256, 256, None, 256, 256, 1, 256, 256, 1 << 20,
+                                 None) == nl.NL_EINVAL
+    assert L.nested_kv_attention(256, 4, 8, 2, 10, 256, 256, 256, 256, 256, 256, 256, 1, 256, 256, 16,
+                                 None) == nl.NL_EINVAL
