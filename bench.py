@@ -300,12 +300,37 @@ def roofline_leg(nl, call, ncopy, stream, bpw):
             "kernel_source_digest": digest}
 
 
+def graph_us(torch, fn, reps, calls=10):
+    """Average GPU time of fn() (launches only, on the current stream) from
+    replays of a graph of `calls` calls, so host-side call overhead is not
+    measured; events around the replays."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    e1.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps / calls
+
+
 def tree_leg(nl, torch, synth, reps, cpu_seconds=0.0):
     """The draft tree: best-first build of 64 nodes from 8 x 16 rank
     statistics (one workgroup), and greedy acceptance for a batch of 1024
     sequences sharing that tree (one wave each).  Both are latency work;
-    each is timed over back-to-back launches on the stream between two
-    events."""
+    each is timed from replays of a graph of launches."""
     import numpy as np
     D, R, N, B = 8, 16, 64, 1024
     p = synth.make_rank_stats(D, R, cfg=90)
@@ -314,24 +339,17 @@ def tree_leg(nl, torch, synth, reps, cpu_seconds=0.0):
     e1 = torch.cuda.Event(enable_timing=True)
     t = nl.tree_build(pd, N)
     torch.cuda.synchronize()
-    e0.record()
-    for _ in range(reps):
-        nl.nested_tree_build(pd, D, R, N, t["parent"], t["depth"], t["rank"], t["prio"], t["anc"], t["count"])
-    e1.record()
-    e1.synchronize()
-    build_us = e0.elapsed_time(e1) * 1e3 / reps
+    build_us = graph_us(torch, lambda: nl.nested_tree_build(pd, D, R, N, t["parent"], t["depth"], t["rank"],
+                                                            t["prio"], t["anc"], t["count"],
+                                                            torch.cuda.current_stream()), reps)
     par = t["parent"].cpu().numpy()
     draft, argmax = synth.make_tree_tokens(par, B, cfg=90)
     dd = torch.from_numpy(draft).cuda()
     da = torch.from_numpy(argmax).cuda()
     n, path, bonus = nl.tree_accept(t["parent"], dd, da)
     torch.cuda.synchronize()
-    e0.record()
-    for _ in range(reps):
-        nl.nested_tree_accept(t["parent"], N, B, dd, da, n, path, bonus)
-    e1.record()
-    e1.synchronize()
-    acc_us = e0.elapsed_time(e1) * 1e3 / reps
+    acc_us = graph_us(torch, lambda: nl.nested_tree_accept(t["parent"], N, B, dd, da, n, path, bonus,
+                                                           torch.cuda.current_stream()), reps)
     mean_acc = float(n.float().mean().item()) + 1.0
     # expected tokens per check from the statistics: the sum of the node priorities + 1
     out = {"build": {"D": D, "R": R, "N": N, "us": round(build_us, 2)},
@@ -352,6 +370,58 @@ def tree_leg(nl, torch, synth, reps, cpu_seconds=0.0):
         out["cpu_baseline"] = {"value": round(k * B / dt), "unit": "sequences/s", "cores": 1, "kind": "oracle",
                                "sample": f"{k} build(s) + {k * B} acceptances in {dt:.1f} s"}
     log(f"[bench] tree: build {build_us:.1f} us, accept {acc_us:.1f} us per {B} sequences")
+    return out
+
+
+def kv_leg(nl, torch, synth, reps):
+    """Nested KV attention of one Llama-8B-like layer (32 query heads, 8 KV
+    heads, d = 128): verify (KV8) of a 16-token tree and a draft step (KV4,
+    one token) at 4096 and 32768 context positions, plus the writer for 16
+    tokens.  Bytes are the KV rows the call reads (planes and scales); times
+    come from graph replays (host call overhead excluded)."""
+    import numpy as np
+    H_q, H_kv = 32, 8
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    rng = np.random.default_rng(91)
+    out = {"heads": [H_q, H_kv], "cases": {}}
+    for L in (4096, 32768):
+        for T, verify in ((16, True), (1, False)):
+            P = L + T
+            rows = P * H_kv
+            kb = torch.from_numpy(rng.integers(0, 256, (rows, 64), dtype=np.uint8)).cuda()
+            kr = torch.from_numpy(rng.integers(0, 256, (rows, 64), dtype=np.uint8)).cuda()
+            vb = torch.from_numpy(rng.integers(0, 256, (rows, 64), dtype=np.uint8)).cuda()
+            vr = torch.from_numpy(rng.integers(0, 256, (rows, 64), dtype=np.uint8)).cuda()
+            ks = torch.from_numpy(rng.uniform(0.01, 0.05, rows).astype(np.float32)).cuda()
+            vs = torch.from_numpy(rng.uniform(0.01, 0.05, rows).astype(np.float32)).cuda()
+            q = torch.from_numpy(synth.make_x(T * H_q, 128, cfg=91, idx=T).view(np.int16)).cuda()
+            anc = torch.from_numpy(np.array([(1 << (t + 1)) - 1 for t in range(T)], np.uint64).view(np.int64)).cuda()
+            ws = torch.empty(nl.nested_kv_attention_workspace_bytes(T, H_q, H_kv, L), dtype=torch.uint8,
+                             device="cuda")
+            o = torch.empty((T, H_q, 128), dtype=torch.float32, device="cuda")
+
+            def call():
+                nl.nested_kv_attention(q, T, H_q, H_kv, L, kb, kr if verify else None, ks, vb,
+                                       vr if verify else None, vs, anc, verify, o, ws, torch.cuda.current_stream())
+            us = graph_us(torch, call, reps)
+            b = P * H_kv * 2 * ((128 if verify else 64) + 4)
+            key = f"{'verify' if verify else 'draft'}_T{T}_L{L}"
+            out["cases"][key] = {"us": round(us, 2), "kv_bytes": b, "GBps": round(b / us / 1e3, 1),
+                                 "frac_hbm_peak": round(b / us / 1e3 / HBM_PEAK_GBPS, 4)}
+            log(f"[bench] kv {key}: {us:.1f} us, {b / us / 1e3:.0f} GB/s of KV")
+            del kb, kr, vb, vr, ks, vs, ws
+    # the writer: K and V of 16 tokens x 8 KV heads
+    n = 16 * H_kv
+    x = torch.from_numpy(synth.make_x(n, 128, cfg=92).view(np.int16)).cuda()
+    rowi = torch.arange(n, dtype=torch.int32, device="cuda")
+    base = torch.empty((n, 64), dtype=torch.uint8, device="cuda")
+    ref = torch.empty_like(base)
+    sc = torch.empty(n, dtype=torch.float32, device="cuda")
+    out["write_16_tokens_us"] = round(graph_us(torch, lambda: nl.nested_kv_write(x, n, rowi, base, ref, sc,
+                                                                                  torch.cuda.current_stream()),
+                                               reps), 2)
+    out["bound"] = "VALU (fp32 dot products and softmax, four lanes per query row)"
     return out
 
 
@@ -877,6 +947,9 @@ def main():
     # ---- the draft tree (build once from the statistics, accept per step)
     draft_tree = tree_leg(nl, torch, synth, args.reps, cpu_seconds=0.0 if args.no_cpu_baseline else 2.0)
 
+    # ---- nested KV cache: tree-masked attention over KV8 / KV4
+    kv_cache = kv_leg(nl, torch, synth, args.reps)
+
     # ---- the offline encoder (dense W -> planes) and the level fit
     encoder = encoder_leg(nl, torch, synth, args.reps, cpu_seconds=0.0 if args.no_cpu_baseline else 3.0)
 
@@ -930,6 +1003,7 @@ def main():
         "model_pass": model,
         "w4w8": w4w8,
         "draft_tree": draft_tree,
+        "nested_kv": kv_cache,
         "encoder": encoder,
         "decoder_layer": layer,
         "stream_read_GBps_torch_sum": round(stream_gbps, 1),

@@ -4,14 +4,16 @@
 // kv_write_kernel: one wave per 128-value row; lane l holds dimensions 2l and
 // 2l + 1 (one byte of each plane).  The row maximum is a wave reduction.
 //
-// kv_attn_kernel: one workgroup per (64-position chunk, KV head).  It decodes
-// the chunk's K and V rows into LDS as the exact integer codes (16 q4 + q_r
-// for KV8, q4 for KV4; the row scale is applied to the score and to the
-// softmax weight), then four lanes per query row (32 dimensions each) run
-// an online softmax over the chunk's visible keys.  Partial (max, sum,
-// output) per chunk go to the workspace; kv_combine_kernel merges them.
+// kv_attn_kernel: one workgroup per (span of positions, KV head), at most 64
+// spans per head.  For each 64-position sub-chunk it decodes the K and V rows
+// into LDS as the exact integer codes (16 q4 + q_r for KV8, q4 for KV4; the
+// row scale is applied to the score and to the softmax weight), then four
+// lanes per query row (32 dimensions each) run an online softmax over the
+// visible keys, eight keys per rescale.  Partial (max, sum, output) per span
+// go to the workspace; kv_combine_kernel merges them.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -65,6 +67,8 @@ struct AttnArgs {
   float *part_o;   // [chunks][H_kv][RQ][128]
   float *part_ml;  // [chunks][H_kv][RQ][2]
   int T, H_q, H_kv, L, g, RQ;
+  int span;        // key positions per workgroup (a multiple of 64)
+  int G;           // key groups per query row (power of two, <= 16)
 };
 
 template <bool VERIFY>
@@ -74,31 +78,11 @@ __global__ __launch_bounds__(1024) void kv_attn_kernel(AttnArgs a) {
   __shared__ float ksc[kChunk], vsc[kChunk];
   const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int P = a.L + a.T;
-  const int p0 = c * kChunk, nk = min(kChunk, P - p0);
-
-  // decode: item = (key, plane K or V, 16-byte piece)
-  for (int it = tid; it < nk * 8; it += blockDim.x) {
-    const int key = it >> 3, isv = (it >> 2) & 1, pc = it & 3;
-    const size_t row = (size_t)(p0 + key) * a.H_kv + h;
-    const uint8_t *bp = (isv ? a.vb : a.kb) + row * 64 + pc * 16;
-    const uint4 b = *reinterpret_cast<const uint4 *>(bp);
-    uint4 r = make_uint4(0, 0, 0, 0);
-    if constexpr (VERIFY) r = *reinterpret_cast<const uint4 *>((isv ? a.vr : a.kr) + row * 64 + pc * 16);
-    const uint32_t bw[4] = {b.x, b.y, b.z, b.w}, rw[4] = {r.x, r.y, r.z, r.w};
-    float *dst = (isv ? vc[key] : kc[key]) + pc * 32;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        dst[q * 8 + i] = VERIFY ? (float)(16 * nib(bw[q], i) + nib(rw[q], i)) : (float)nib(bw[q], i);
-    if (pc == 0) {
-      const float sc = (isv ? a.vs : a.ks)[row] * (VERIFY ? 0.0625f : 1.0f);
-      if (isv) vsc[key] = sc; else ksc[key] = sc;
-    }
-  }
-  __syncthreads();
-
-  const int r = tid >> 2, part = tid & 3;
+  const int pb = c * a.span, pe = min(pb + a.span, P);
+  // thread = (query row, dimension quarter, key group): the G key groups of
+  // a (row, quarter) are adjacent lanes and the 4 quarters of a (row, group)
+  // are G lanes apart, so both reductions are lane exchanges in one wave
+  const int G = a.G, grp = tid & (G - 1), part = (tid / G) & 3, r = tid / (4 * G);
   const bool act = r < a.RQ;
   const int t = act ? r / a.g : 0, j = h * a.g + (act ? r % a.g : 0);
   float q[32];
@@ -117,31 +101,91 @@ __global__ __launch_bounds__(1024) void kv_attn_kernel(AttnArgs a) {
     }
   }
   const uint64_t am = a.anc[t];
+  // keys in blocks of 8: eight independent dot products, one block maximum,
+  // one rescale of the running output per block
+  constexpr int kB = 8;
   float m = -INFINITY, l = 0.0f, o[32];
 #pragma unroll
   for (int k = 0; k < 32; ++k) o[k] = 0.0f;
-  for (int key = 0; key < nk; ++key) {
-    const float *kr = kc[key] + part * 32;
-    float dot = 0.0f;
+  for (int p0 = pb; p0 < pe; p0 += kChunk) {
+    const int nk = min(kChunk, pe - p0);
+    __syncthreads();   // the previous sub-chunk's LDS reads are done
+    // decode: item = (key, plane K or V, 16-byte piece)
+    for (int it = tid; it < nk * 8; it += blockDim.x) {
+      const int key = it >> 3, isv = (it >> 2) & 1, pc = it & 3;
+      const size_t row = (size_t)(p0 + key) * a.H_kv + h;
+      const uint8_t *bp = (isv ? a.vb : a.kb) + row * 64 + pc * 16;
+      const uint4 b = *reinterpret_cast<const uint4 *>(bp);
+      uint4 rf = make_uint4(0, 0, 0, 0);
+      if constexpr (VERIFY) rf = *reinterpret_cast<const uint4 *>((isv ? a.vr : a.kr) + row * 64 + pc * 16);
+      const uint32_t bw[4] = {b.x, b.y, b.z, b.w}, rw[4] = {rf.x, rf.y, rf.z, rf.w};
+      float *dst = (isv ? vc[key] : kc[key]) + pc * 32;
 #pragma unroll
-    for (int k = 0; k < 32; ++k) dot += q[k] * kr[k];
-    dot += __shfl_xor(dot, 1);
-    dot += __shfl_xor(dot, 2);
-    const int pos = p0 + key;
-    const bool vis = pos < a.L || ((am >> (pos - a.L)) & 1ull);
-    if (vis) {
-      const float sc = dot * ksc[key];
-      const float mn = fmaxf(m, sc);
-      const float al = expf(m - mn), be = expf(sc - mn);
-      l = l * al + be;
-      const float wv = be * vsc[key];
-      const float *vr = vc[key] + part * 32;
+      for (int w4 = 0; w4 < 4; ++w4)
 #pragma unroll
-      for (int k = 0; k < 32; ++k) o[k] = o[k] * al + wv * vr[k];
+        for (int i = 0; i < 8; ++i)
+          dst[w4 * 8 + i] = VERIFY ? (float)(16 * nib(bw[w4], i) + nib(rw[w4], i)) : (float)nib(bw[w4], i);
+      if (pc == 0) {
+        const float sc = (isv ? a.vs : a.ks)[row] * (VERIFY ? 0.0625f : 1.0f);
+        if (isv) vsc[key] = sc; else ksc[key] = sc;
+      }
+    }
+    __syncthreads();
+
+    // this group's keys: grp, grp + G, ... of the sub-chunk
+    const int nkg = (nk - grp + G - 1) / G;
+    for (int k0 = 0; k0 < nkg; k0 += kB) {
+      float sc[kB];
+#pragma unroll 2
+      for (int u = 0; u < kB; ++u) {
+        const int key = grp + G * min(k0 + u, max(nkg - 1, 0));
+        const float *kr = kc[min(key, nk - 1)] + part * 32;
+        float dot = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) dot += q[k] * kr[k];
+        sc[u] = dot;
+      }
+      float bm = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        sc[u] += __shfl_xor(sc[u], G);
+        sc[u] += __shfl_xor(sc[u], 2 * G);
+        const int key = min(grp + G * (k0 + u), nk - 1), pos = p0 + key;   // clamped: in bounds
+        const bool vis = k0 + u < nkg && (pos < a.L || ((am >> (pos - a.L)) & 1ull));
+        sc[u] = vis ? sc[u] * ksc[key] : -INFINITY;
+        bm = fmaxf(bm, sc[u]);
+      }
+      if (bm == -INFINITY) continue;   // nothing visible in this block
+      const float mn = fmaxf(m, bm);
+      const float al = expf(m - mn);
+      l *= al;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) o[k] *= al;
+#pragma unroll 1
+      for (int u = 0; u < kB; ++u) {
+        if (sc[u] == -INFINITY) continue;
+        const int key = grp + G * (k0 + u);
+        const float be = expf(sc[u] - mn);
+        l += be;
+        const float wv = be * vsc[key];
+        const float *vr = vc[key] + part * 32;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) o[k] += wv * vr[k];
+      }
       m = mn;
     }
   }
-  if (act) {
+  // merge the G key groups' (max, sum, output) of each (row, quarter)
+  for (int st = 1; st < G; st <<= 1) {
+    const float mo = __shfl_xor(m, st), lo = __shfl_xor(l, st);
+    const float M = fmaxf(m, mo);
+    const float wa = M == -INFINITY ? 0.0f : expf(m - M), wb = M == -INFINITY ? 0.0f : expf(mo - M);
+    l = l * wa + lo * wb;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) o[k] = o[k] * wa + __shfl_xor(o[k], st) * wb;
+    m = M;
+  }
+  if (act && grp == 0) {
     const size_t base = ((size_t)c * a.H_kv + h) * a.RQ + r;
     float4 *op = reinterpret_cast<float4 *>(a.part_o + base * kD + part * 32);
 #pragma unroll
@@ -153,24 +197,41 @@ __global__ __launch_bounds__(1024) void kv_attn_kernel(AttnArgs a) {
   }
 }
 
-// One wave per (KV head, query row): 2 dimensions per lane.
-__global__ __launch_bounds__(64) void kv_combine_kernel(AttnArgs a, int chunks, float *out) {
-  const int h = blockIdx.y, r = blockIdx.x, lane = threadIdx.x;
+// One workgroup per (KV head, query row): wave 0 turns the chunks' maxima
+// and sums into weights (at most 64 chunks, one per lane), then four waves
+// add the weighted chunk outputs, all loads in flight, 2 dimensions a lane.
+__global__ __launch_bounds__(256) void kv_combine_kernel(AttnArgs a, int chunks, float *out) {
+  __shared__ float wsh[64];
+  __shared__ float osum[4][kD];
+  __shared__ float lsh;
+  const int h = blockIdx.y, r = blockIdx.x, tid = threadIdx.x;
   const int t = r / a.g, j = h * a.g + r % a.g;
-  float M = -INFINITY;
-  for (int c = 0; c < chunks; ++c) M = fmaxf(M, a.part_ml[(((size_t)c * a.H_kv + h) * a.RQ + r) * 2]);
-  float Ls = 0.0f, o0 = 0.0f, o1 = 0.0f;
-  for (int c = 0; c < chunks; ++c) {
-    const size_t base = ((size_t)c * a.H_kv + h) * a.RQ + r;
-    const float mc = a.part_ml[base * 2];
-    if (mc == -INFINITY) continue;   // no visible key in this chunk
-    const float w = expf(mc - M);
-    Ls += a.part_ml[base * 2 + 1] * w;
-    const float2 v = reinterpret_cast<const float2 *>(a.part_o + base * kD)[lane];
-    o0 += v.x * w;
-    o1 += v.y * w;
+  if (tid < 64) {
+    const size_t base = ((size_t)tid * a.H_kv + h) * a.RQ + r;
+    const float mc = tid < chunks ? a.part_ml[base * 2] : -INFINITY;
+    const float lc = tid < chunks ? a.part_ml[base * 2 + 1] : 0.0f;
+    float M = mc;
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    const float w = mc == -INFINITY ? 0.0f : expf(mc - M);   // a chunk with no visible key weighs 0
+    float ls = lc * w;
+    for (int o = 32; o >= 1; o >>= 1) ls += __shfl_xor(ls, o);
+    wsh[tid] = w;
+    if (tid == 0) lsh = ls;
   }
-  reinterpret_cast<float2 *>(out + ((size_t)t * a.H_q + j) * kD)[lane] = make_float2(o0 / Ls, o1 / Ls);
+  __syncthreads();
+  const int cg = tid >> 6, ld = tid & 63;
+  float o0 = 0.0f, o1 = 0.0f;
+#pragma unroll 16
+  for (int cc = cg; cc < chunks; cc += 4) {
+    const float2 v = reinterpret_cast<const float2 *>(a.part_o + (((size_t)cc * a.H_kv + h) * a.RQ + r) * kD)[ld];
+    o0 += wsh[cc] * v.x;
+    o1 += wsh[cc] * v.y;
+  }
+  osum[cg][2 * ld] = o0;
+  osum[cg][2 * ld + 1] = o1;
+  __syncthreads();
+  if (tid < kD)
+    out[((size_t)t * a.H_q + j) * kD + tid] = (osum[0][tid] + osum[1][tid] + osum[2][tid] + osum[3][tid]) / lsh;
 }
 
 char g_msg[256];
@@ -193,8 +254,14 @@ nl_status launched(const char *who) {
   return nl::api_error(NL_OK, "");
 }
 
+// Key positions per workgroup: 64-key sub-chunks, as many per workgroup as
+// keep the chunks of a head at 64 or fewer (the combine's one-lane-per-chunk
+// weights).
+int attn_span(int P) { return (P + 64 * kChunk - 1) / (64 * kChunk) * kChunk; }
+int attn_chunks(int P) { return (P + attn_span(P) - 1) / attn_span(P); }
+
 size_t attn_ws(int T, int H_q, int H_kv, int L) {
-  const int RQ = T * (H_q / H_kv), chunks = (L + T + kChunk - 1) / kChunk;
+  const int RQ = T * (H_q / H_kv), chunks = attn_chunks(L + T);
   const size_t o = (size_t)chunks * H_kv * RQ * kD * 4;
   return ((o + 255) & ~(size_t)255) + (size_t)chunks * H_kv * RQ * 8;
 }
@@ -257,17 +324,22 @@ extern "C" nl_status nested_kv_attention(const void *q, int32_t T, int32_t H_q, 
   a.L = L;
   a.g = H_q / H_kv;
   a.RQ = T * a.g;
-  const int chunks = (L + T + kChunk - 1) / kChunk;
+  a.span = attn_span(L + T);
+  const int chunks = attn_chunks(L + T);
   const size_t o = (size_t)chunks * H_kv * a.RQ * kD * 4;
   a.part_o = static_cast<float *>(ws);
   a.part_ml = reinterpret_cast<float *>(static_cast<char *>(ws) + ((o + 255) & ~(size_t)255));
-  const int threads = (4 * a.RQ + 63) / 64 * 64;
+  // key groups: as many as keep 4 * RQ * G <= 1024 threads, at most 16
+  // (a power of two); at least 256 threads share the decode
+  a.G = 1;
+  while (a.G < 16 && 4 * a.RQ * a.G * 2 <= 1024) a.G *= 2;
+  const int threads = std::max(256, (4 * a.RQ * a.G + 63) / 64 * 64);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (verify)
     hipLaunchKernelGGL(kv_attn_kernel<true>, dim3((unsigned)chunks, (unsigned)H_kv), dim3(threads), 0, s, a);
   else
     hipLaunchKernelGGL(kv_attn_kernel<false>, dim3((unsigned)chunks, (unsigned)H_kv), dim3(threads), 0, s, a);
   if (nl_status st = launched(who)) return st;
-  hipLaunchKernelGGL(kv_combine_kernel, dim3((unsigned)a.RQ, (unsigned)H_kv), dim3(64), 0, s, a, chunks, out);
+  hipLaunchKernelGGL(kv_combine_kernel, dim3((unsigned)a.RQ, (unsigned)H_kv), dim3(256), 0, s, a, chunks, out);
   return launched(who);
 }
