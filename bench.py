@@ -421,7 +421,7 @@ def kv_leg(nl, torch, synth, reps):
     out["write_16_tokens_us"] = round(graph_us(torch, lambda: nl.nested_kv_write(x, n, rowi, base, ref, sc,
                                                                                   torch.cuda.current_stream()),
                                                reps), 2)
-    out["bound"] = "VALU (fp32 dot products and softmax, four lanes per query row)"
+    out["bound"] = "VALU (K/V decode into LDS and the softmax; both products on MFMA)"
     return out
 
 

@@ -4,13 +4,13 @@
 // kv_write_kernel: one wave per 128-value row; lane l holds dimensions 2l and
 // 2l + 1 (one byte of each plane).  The row maximum is a wave reduction.
 //
-// kv_attn_kernel: one workgroup per (span of positions, KV head), at most 64
-// spans per head.  For each 64-position sub-chunk it decodes the K and V rows
-// into LDS as the exact integer codes (16 q4 + q_r for KV8, q4 for KV4; the
-// row scale is applied to the score and to the softmax weight), then four
-// lanes per query row (32 dimensions each) run an online softmax over the
-// visible keys, eight keys per rescale.  Partial (max, sum, output) per span
-// go to the workspace; kv_combine_kernel merges them.
+// kv_attn_mfma_kernel: one workgroup per (span of positions, KV head, block
+// of 64 query rows), at most 64 spans per head.  For each 64-position
+// sub-chunk it decodes the K and V rows into LDS as the exact integer codes
+// (16 q4 + q_r for KV8, q4 for KV4; the row scales are applied to the score
+// and to the softmax weight), and both products run on the matrix cores.
+// Partial (max, sum, output) per span go to the workspace; kv_combine_kernel
+// merges them.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -68,131 +68,249 @@ struct AttnArgs {
   float *part_ml;  // [chunks][H_kv][RQ][2]
   int T, H_q, H_kv, L, g, RQ;
   int span;        // key positions per workgroup (a multiple of 64)
-  int G;           // key groups per query row (power of two, <= 16)
 };
 
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ _Float16 code(uint32_t b, uint32_t r, int i, bool verify) {
+  return (_Float16)(verify ? 16 * nib(b, i) + nib(r, i) : nib(b, i));   // |code| <= 136: exact
+}
+
+// MFMA attention: one workgroup of four waves per (span, KV head, block of
+// 64 query rows); wave w owns the 16 rows 64 z + 16 w .. +15 (rows past RQ
+// are zero queries whose results are dropped).  Per 64-key sub-chunk the
+// four waves decode K key-major and V dimension-major into LDS as fp16
+// integer codes (exact), then each wave with live rows computes
+//   S = Q K^T        16 v_mfma_f32_16x16x32_f16 (4 key tiles x 4 dim steps),
+//                    Q widened to fp16 with a power of two per row (exact
+//                    unless an element is below 2^-30 of its row maximum);
+//   online softmax   one rescale per sub-chunk, row reductions across the
+//                    16 key lanes of the C layout;
+//   O += P' V        32 MFMAs: P' = p * v_scale / (largest v_scale of the
+//                    sub-chunk) goes through a per-wave LDS tile as an fp16
+//                    pair hi + lo (about 22 significant bits), and the
+//                    sub-chunk's product is scaled back in fp32.
+// C layout of a 16x16 tile: lane (lr = lane & 15, lg = lane >> 4) holds rows
+// 4 lg .. 4 lg + 3 of column lr; an A/B operand lane holds row/column lr and
+// the 8 reduction elements 8 lg .. 8 lg + 7 of a 32-wide step.
 template <bool VERIFY>
-__global__ __launch_bounds__(1024) void kv_attn_kernel(AttnArgs a) {
-  __shared__ float kc[kChunk][kD + 4];
-  __shared__ float vc[kChunk][kD + 4];
+__global__ __launch_bounds__(256) void kv_attn_mfma_kernel(AttnArgs a) {
+  constexpr int kKP = kD + 8;      // K: [key][dim] pitch (halves)
+  constexpr int kVP = kChunk + 8;  // V: [dim][key] pitch (halves)
+  constexpr int kPP = kChunk + 8;  // P': [row][key] pitch (halves)
+  __shared__ __attribute__((aligned(16))) _Float16 kt[kChunk * kKP];
+  __shared__ __attribute__((aligned(16))) _Float16 vt[kD * kVP];
+  __shared__ __attribute__((aligned(16))) _Float16 pt[4][2][16 * kPP];   // per wave: P' hi, lo
   __shared__ float ksc[kChunk], vsc[kChunk];
   const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int r0 = 64 * blockIdx.z + 16 * wave;   // this wave's first query row
+  const bool live = r0 < a.RQ;                   // wave-uniform
   const int P = a.L + a.T;
   const int pb = c * a.span, pe = min(pb + a.span, P);
-  // thread = (query row, dimension quarter, key group): the G key groups of
-  // a (row, quarter) are adjacent lanes and the 4 quarters of a (row, group)
-  // are G lanes apart, so both reductions are lane exchanges in one wave
-  const int G = a.G, grp = tid & (G - 1), part = (tid / G) & 3, r = tid / (4 * G);
-  const bool act = r < a.RQ;
-  const int t = act ? r / a.g : 0, j = h * a.g + (act ? r % a.g : 0);
-  float q[32];
-  const float qs = 0.08838834764831845f;   // 1/sqrt(128)
+
+  // Q operand: row r0 + lr, dimensions 32 st + 8 lg .. +8
+  half8 qa[4];
+  float qinv[4];
+  uint64_t am[4];
   {
-    const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + ((size_t)t * a.H_q + j) * kD + part * 32);
+    const int qrow = r0 + lr;
+    const bool real = qrow < a.RQ;
+    const int t = real ? qrow / a.g : 0, j = h * a.g + (real ? qrow % a.g : 0);
+    const uint16_t *qp = a.q + ((size_t)t * a.H_q + j) * kD;
+    float qf[32];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint4 v = qp[u];
+    for (int st = 0; st < 4; ++st) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(qp + 32 * st + 8 * lg);
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        q[u * 8 + 2 * k] = __uint_as_float(w[k] << 16) * qs;
-        q[u * 8 + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u) * qs;
+        qf[8 * st + 2 * k] = real ? __uint_as_float(w[k] << 16) : 0.0f;
+        qf[8 * st + 2 * k + 1] = real ? __uint_as_float(w[k] & 0xFFFF0000u) : 0.0f;
       }
     }
+    float qm = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) qm = fmaxf(qm, fabsf(qf[k]));
+    qm = fmaxf(qm, __shfl_xor(qm, 16));
+    qm = fmaxf(qm, __shfl_xor(qm, 32));
+    int qe = 0;
+    if (qm > 0.0f) {
+      int E;
+      frexpf(qm, &E);
+      qe = 15 - E;   // row maximum * 2^qe in [2^14, 2^15)
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) qa[st][k] = (_Float16)ldexpf(qf[8 * st + k], qe);
+    const float qi = ldexpf(0.08838834764831845f, -qe);   // 2^-qe / sqrt(128)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qinv[i] = __shfl(qi, 4 * lg + i);
+      const int row = r0 + 4 * lg + i;
+      am[i] = a.anc[row < a.RQ ? row / a.g : 0];
+    }
   }
-  const uint64_t am = a.anc[t];
-  // keys in blocks of 8: eight independent dot products, one block maximum,
-  // one rescale of the running output per block
-  constexpr int kB = 8;
-  float m = -INFINITY, l = 0.0f, o[32];
+
+  float m[4], l[4];
+  floatx4 o[8];
 #pragma unroll
-  for (int k = 0; k < 32; ++k) o[k] = 0.0f;
+  for (int i = 0; i < 4; ++i) {
+    m[i] = -INFINITY;
+    l[i] = 0.0f;
+  }
+#pragma unroll
+  for (int d = 0; d < 8; ++d) o[d] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  _Float16 *ph = pt[wave][0], *pl = pt[wave][1];
+  const float unit = VERIFY ? 0.0625f : 1.0f;
+
   for (int p0 = pb; p0 < pe; p0 += kChunk) {
-    const int nk = min(kChunk, pe - p0);
-    __syncthreads();   // the previous sub-chunk's LDS reads are done
-    // decode: item = (key, plane K or V, 16-byte piece)
-    for (int it = tid; it < nk * 8; it += blockDim.x) {
-      const int key = it >> 3, isv = (it >> 2) & 1, pc = it & 3;
-      const size_t row = (size_t)(p0 + key) * a.H_kv + h;
-      const uint8_t *bp = (isv ? a.vb : a.kb) + row * 64 + pc * 16;
-      const uint4 b = *reinterpret_cast<const uint4 *>(bp);
-      uint4 rf = make_uint4(0, 0, 0, 0);
-      if constexpr (VERIFY) rf = *reinterpret_cast<const uint4 *>((isv ? a.vr : a.kr) + row * 64 + pc * 16);
-      const uint32_t bw[4] = {b.x, b.y, b.z, b.w}, rw[4] = {rf.x, rf.y, rf.z, rf.w};
-      float *dst = (isv ? vc[key] : kc[key]) + pc * 32;
+    const int nk = min(kChunk, pe - p0);   // >= 1; keys past nk repeat key nk - 1 and are masked
+    __syncthreads();                       // the previous sub-chunk's LDS reads are done
+    for (int it = tid; it < 256; it += blockDim.x) {
+      if (it < 128) {   // K: key it / 2, dimensions 64 (it & 1) .. +64
+        const int key = it >> 1, hh = it & 1;
+        const size_t row = (size_t)(p0 + min(key, nk - 1)) * a.H_kv + h;
+        const uint4 *bp = reinterpret_cast<const uint4 *>(a.kb + row * 64 + hh * 32);
+        const uint4 b0 = bp[0], b1 = bp[1];
+        uint4 q0 = make_uint4(0, 0, 0, 0), q1 = q0;
+        if constexpr (VERIFY) {
+          const uint4 *rp = reinterpret_cast<const uint4 *>(a.kr + row * 64 + hh * 32);
+          q0 = rp[0];
+          q1 = rp[1];
+        }
+        const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        const uint32_t rw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
-      for (int w4 = 0; w4 < 4; ++w4)
+        for (int w = 0; w < 8; ++w) {
+          half8 hv;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          dst[w4 * 8 + i] = VERIFY ? (float)(16 * nib(bw[w4], i) + nib(rw[w4], i)) : (float)nib(bw[w4], i);
-      if (pc == 0) {
-        const float sc = (isv ? a.vs : a.ks)[row] * (VERIFY ? 0.0625f : 1.0f);
-        if (isv) vsc[key] = sc; else ksc[key] = sc;
+          for (int i = 0; i < 8; ++i) hv[i] = code(bw[w], rw[w], i, VERIFY);
+          *reinterpret_cast<half8 *>(kt + key * kKP + hh * 64 + 8 * w) = hv;
+        }
+        if (hh == 0) ksc[key] = a.ks[row] * unit;
+      } else {          // V: keys 8 kg .. +8 x dimensions 8 dg .. +8, stored transposed
+        const int dg = it & 15, kg = (it >> 4) & 7;
+        uint32_t bw[8], rw[8];
+        size_t rows[8];
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          rows[kk] = (size_t)(p0 + min(8 * kg + kk, nk - 1)) * a.H_kv + h;
+          bw[kk] = reinterpret_cast<const uint32_t *>(a.vb + rows[kk] * 64)[dg];
+          rw[kk] = VERIFY ? reinterpret_cast<const uint32_t *>(a.vr + rows[kk] * 64)[dg] : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          half8 hv;
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk) hv[kk] = code(bw[kk], rw[kk], i, VERIFY);
+          *reinterpret_cast<half8 *>(vt + (8 * dg + i) * kVP + 8 * kg) = hv;
+        }
+        if (dg == 0)
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk) vsc[8 * kg + kk] = a.vs[rows[kk]] * unit;
       }
     }
     __syncthreads();
+    if (!live) continue;
 
-    // this group's keys: grp, grp + G, ... of the sub-chunk
-    const int nkg = (nk - grp + G - 1) / G;
-    for (int k0 = 0; k0 < nkg; k0 += kB) {
-      float sc[kB];
-#pragma unroll 2
-      for (int u = 0; u < kB; ++u) {
-        const int key = grp + G * min(k0 + u, max(nkg - 1, 0));
-        const float *kr = kc[min(key, nk - 1)] + part * 32;
-        float dot = 0.0f;
+    float vm = vsc[lane];   // largest V scale of the sub-chunk
 #pragma unroll
-        for (int k = 0; k < 32; ++k) dot += q[k] * kr[k];
-        sc[u] = dot;
+    for (int o2 = 1; o2 < 64; o2 <<= 1) vm = fmaxf(vm, __shfl_xor(vm, o2));
+    const float vinv = vm > 0.0f ? 1.0f / vm : 0.0f;
+
+    floatx4 sc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      sc[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const half8 kb8 = *reinterpret_cast<const half8 *>(kt + (16 * t + lr) * kKP + 32 * st + 8 * lg);
+        sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[st], kb8, sc[t], 0, 0, 0);
       }
-      float bm = -INFINITY;
-#pragma unroll
-      for (int u = 0; u < kB; ++u) {
-        sc[u] += __shfl_xor(sc[u], G);
-        sc[u] += __shfl_xor(sc[u], 2 * G);
-        const int key = min(grp + G * (k0 + u), nk - 1), pos = p0 + key;   // clamped: in bounds
-        const bool vis = k0 + u < nkg && (pos < a.L || ((am >> (pos - a.L)) & 1ull));
-        sc[u] = vis ? sc[u] * ksc[key] : -INFINITY;
-        bm = fmaxf(bm, sc[u]);
-      }
-      if (bm == -INFINITY) continue;   // nothing visible in this block
-      const float mn = fmaxf(m, bm);
-      const float al = expf(m - mn);
-      l *= al;
-#pragma unroll
-      for (int k = 0; k < 32; ++k) o[k] *= al;
-#pragma unroll 1
-      for (int u = 0; u < kB; ++u) {
-        if (sc[u] == -INFINITY) continue;
-        const int key = grp + G * (k0 + u);
-        const float be = expf(sc[u] - mn);
-        l += be;
-        const float wv = be * vsc[key];
-        const float *vr = vc[key] + part * 32;
-#pragma unroll
-        for (int k = 0; k < 32; ++k) o[k] += wv * vr[k];
-      }
-      m = mn;
     }
-  }
-  // merge the G key groups' (max, sum, output) of each (row, quarter)
-  for (int st = 1; st < G; st <<= 1) {
-    const float mo = __shfl_xor(m, st), lo = __shfl_xor(l, st);
-    const float M = fmaxf(m, mo);
-    const float wa = M == -INFINITY ? 0.0f : expf(m - M), wb = M == -INFINITY ? 0.0f : expf(mo - M);
-    l = l * wa + lo * wb;
+    // lane holds S[row 4 lg + i][key 16 t + lr]
+    float tmax[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-    for (int k = 0; k < 32; ++k) o[k] = o[k] * wa + __shfl_xor(o[k], st) * wb;
-    m = M;
-  }
-  if (act && grp == 0) {
-    const size_t base = ((size_t)c * a.H_kv + h) * a.RQ + r;
-    float4 *op = reinterpret_cast<float4 *>(a.part_o + base * kD + part * 32);
+    for (int t = 0; t < 4; ++t) {
+      const int key = 16 * t + lr, pos = p0 + key;
+      const float ks = ksc[key];
+      const int bit = min(max(pos - a.L, 0), 63);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) op[u] = make_float4(o[4 * u], o[4 * u + 1], o[4 * u + 2], o[4 * u + 3]);
-    if (part == 0) {
-      a.part_ml[base * 2] = m;
-      a.part_ml[base * 2 + 1] = l;
+      for (int i = 0; i < 4; ++i) {
+        const bool vis = key < nk && (pos < a.L || ((am[i] >> bit) & 1ull));
+        sc[t][i] = vis ? sc[t][i] * qinv[i] * ks : -INFINITY;
+        tmax[i] = fmaxf(tmax[i], sc[t][i]);
+      }
+    }
+#pragma unroll
+    for (int o2 = 1; o2 < 16; o2 <<= 1)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tmax[i] = fmaxf(tmax[i], __shfl_xor(tmax[i], o2));
+    float psum[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float mn = fmaxf(m[i], tmax[i]);
+      const float al = mn == -INFINITY ? 1.0f : expf(m[i] - mn);
+      m[i] = mn;
+      l[i] *= al;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) o[d][i] *= al;
+      psum[i] = 0.0f;
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float vs = vsc[16 * t + lr] * vinv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = sc[t][i] == -INFINITY ? 0.0f : expf(sc[t][i] - m[i]);
+        psum[i] += p;
+        const float x = p * vs;
+        const _Float16 hi = (_Float16)x;
+        ph[(4 * lg + i) * kPP + 16 * t + lr] = hi;
+        pl[(4 * lg + i) * kPP + 16 * t + lr] = (_Float16)(x - (float)hi);   // x - hi is exact
+      }
+    }
+#pragma unroll
+    for (int o2 = 1; o2 < 16; o2 <<= 1)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) psum[i] += __shfl_xor(psum[i], o2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) l[i] += psum[i];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's P' tile is in LDS
+
+    floatx4 oc[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) oc[d] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const half8 pah = *reinterpret_cast<const half8 *>(ph + lr * kPP + 32 * w + 8 * lg);
+      const half8 pal = *reinterpret_cast<const half8 *>(pl + lr * kPP + 32 * w + 8 * lg);
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        const half8 vb8 = *reinterpret_cast<const half8 *>(vt + (16 * d + lr) * kVP + 32 * w + 8 * lg);
+        oc[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pah, vb8, oc[d], 0, 0, 0);
+        oc[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pal, vb8, oc[d], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < 8; ++d) o[d] += vm * oc[d];
+  }
+  if (!live) return;
+  // partials: lane holds O[row 4 lg + i][dimension 16 d + lr]
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = r0 + 4 * lg + i;
+    if (row < a.RQ) {
+      const size_t base = ((size_t)c * a.H_kv + h) * a.RQ + row;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) a.part_o[base * kD + 16 * d + lr] = o[d][i];
+      if (lr == 0) {
+        a.part_ml[base * 2] = m[i];
+        a.part_ml[base * 2 + 1] = l[i];
+      }
     }
   }
 }
@@ -329,16 +447,12 @@ extern "C" nl_status nested_kv_attention(const void *q, int32_t T, int32_t H_q, 
   const size_t o = (size_t)chunks * H_kv * a.RQ * kD * 4;
   a.part_o = static_cast<float *>(ws);
   a.part_ml = reinterpret_cast<float *>(static_cast<char *>(ws) + ((o + 255) & ~(size_t)255));
-  // key groups: as many as keep 4 * RQ * G <= 1024 threads, at most 16
-  // (a power of two); at least 256 threads share the decode
-  a.G = 1;
-  while (a.G < 16 && 4 * a.RQ * a.G * 2 <= 1024) a.G *= 2;
-  const int threads = std::max(256, (4 * a.RQ * a.G + 63) / 64 * 64);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)chunks, (unsigned)H_kv, (unsigned)((a.RQ + 63) / 64));
   if (verify)
-    hipLaunchKernelGGL(kv_attn_kernel<true>, dim3((unsigned)chunks, (unsigned)H_kv), dim3(threads), 0, s, a);
+    hipLaunchKernelGGL(kv_attn_mfma_kernel<true>, grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(kv_attn_kernel<false>, dim3((unsigned)chunks, (unsigned)H_kv), dim3(threads), 0, s, a);
+    hipLaunchKernelGGL(kv_attn_mfma_kernel<false>, grid, dim3(256), 0, s, a);
   if (nl_status st = launched(who)) return st;
   hipLaunchKernelGGL(kv_combine_kernel, dim3((unsigned)a.RQ, (unsigned)H_kv), dim3(256), 0, s, a, chunks, out);
   return launched(who);
