@@ -29,9 +29,6 @@ namespace {
 constexpr int kD = NL_KV_HEAD_DIM;
 constexpr int kChunk = 64;   // key positions per workgroup
 
-__device__ __forceinline__ int nib(uint32_t w, int i) {   // two's-complement nibble i of w
-  return ((int)(w << (28 - 4 * i))) >> 28;
-}
 
 __global__ __launch_bounds__(256) void kv_write_kernel(const uint32_t *x, int n, const int32_t *row, uint8_t *base,
                                                        uint8_t *ref, float *scale) {
@@ -65,7 +62,7 @@ struct AttnArgs {
   const float *ks, *vs;
   const uint64_t *anc;
   float *part_o;   // [chunks][H_kv][RQ][128]
-  float *part_ml;  // [chunks][H_kv][RQ][2]
+  float *part_ml;  // [chunks][H_kv][RQ][2]: running maximum (base-2 units), sum
   int T, H_q, H_kv, L, g, RQ;
   int span;        // key positions per workgroup (a multiple of 64)
 };
@@ -73,50 +70,100 @@ struct AttnArgs {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ _Float16 code(uint32_t b, uint32_t r, int i, bool verify) {
-  return (_Float16)(verify ? 16 * nib(b, i) + nib(r, i) : nib(b, i));   // |code| <= 136: exact
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// Offset-binary codes of the 8 dimensions in one word of each plane: byte k
+// of E holds dimension 2k, byte k of O dimension 2k + 1, as u = 16 (q4 + 8) +
+// (q_r + 8) for KV8 or u = q4 + 8 for KV4 (a two's-complement nibble plus 8
+// is the nibble with its top bit flipped).
+template <bool VERIFY>
+__device__ __forceinline__ void ucodes(uint32_t b, uint32_t r, uint32_t &E, uint32_t &O) {
+  const uint32_t bx = b ^ 0x88888888u;
+  if constexpr (VERIFY) {
+    const uint32_t rx = r ^ 0x88888888u;
+    E = ((bx & 0x0F0F0F0Fu) << 4) | (rx & 0x0F0F0F0Fu);
+    O = (bx & 0xF0F0F0F0u) | ((rx >> 4) & 0x0F0F0F0Fu);
+  } else {
+    E = bx & 0x0F0F0F0Fu;
+    O = (bx >> 4) & 0x0F0F0F0Fu;
+  }
 }
+
+// fp16 pair {byte K of lo, byte K of hi} as the signed codes: 1024 + u is an
+// fp16 integer (bits 0x6400 | u), and subtracting 1024 + the offset is exact.
+template <bool VERIFY, int K>
+__device__ __forceinline__ uint32_t hpair(uint32_t hi, uint32_t lo) {
+  const uint32_t bits = __builtin_amdgcn_perm(hi, lo, K | (0x0c << 8) | ((4 + K) << 16) | (0x0c << 24)) | 0x64006400u;
+  const _Float16 off = VERIFY ? (_Float16)1160.0f : (_Float16)1032.0f;
+  const half2v h = __builtin_bit_cast(half2v, bits) - half2v{off, off};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// 16-lane row maximum through DPP: swap within pairs, within quads, then
+// mirror across the half row and across the row.
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, dppf<0xB1>(v));
+  v = fmaxf(v, dppf<0x4E>(v));
+  v = fmaxf(v, dppf<0x141>(v));
+  return fmaxf(v, dppf<0x140>(v));
+}
+
+// One thread's share of a 64-key sub-chunk: threads 0..127 read half a K
+// row (32 bytes of each plane), threads 128..255 one word of each plane of
+// 8 V rows.  Loads are issued one sub-chunk ahead of their use.
+template <bool VERIFY>
+struct Fill {
+  uint32_t b[8], r[8];
+  float sc[8];
+};
 
 // MFMA attention: one workgroup of four waves per (span, KV head, block of
 // 64 query rows); wave w owns the 16 rows 64 z + 16 w .. +15 (rows past RQ
-// are zero queries whose results are dropped).  Per 64-key sub-chunk the
-// four waves decode K key-major and V dimension-major into LDS as fp16
-// integer codes (exact), then each wave with live rows computes
-//   S = Q K^T        16 v_mfma_f32_16x16x32_f16 (4 key tiles x 4 dim steps),
+// are zero queries whose results are dropped).  Per 64-key sub-chunk
+// threads 0..127 decode K key-major and threads 128..255 V dimension-major
+// into LDS as fp16 integer codes (exact; the planes are loaded one sub-chunk
+// ahead), then each wave with live rows computes, transposed so that a lane
+// owns one query row:
+//   S^T = K Q^T      16 v_mfma_f32_16x16x32_f16 (4 key tiles x 4 dim steps),
 //                    Q widened to fp16 with a power of two per row (exact
 //                    unless an element is below 2^-30 of its row maximum);
-//   online softmax   one rescale per sub-chunk, row reductions across the
-//                    16 key lanes of the C layout;
-//   O += P' V        32 MFMAs: P' = p * v_scale / (largest v_scale of the
-//                    sub-chunk) goes through a per-wave LDS tile as an fp16
-//                    pair hi + lo (about 22 significant bits), and the
-//                    sub-chunk's product is scaled back in fp32.
+//   online softmax   in base 2 (log2 e folded into the query scale), one
+//                    rescale per sub-chunk; the visibility mask is applied
+//                    only where the sub-chunk reaches the tree or the end;
+//   O^T += V^T P'^T  32 MFMAs: P' = p * v_scale / (largest v_scale of the
+//                    sub-chunk) is an fp16 pair hi + lo (about 22
+//                    significant bits) built in registers; O is kept in
+//                    units of the latest nonzero such scale.
 // C layout of a 16x16 tile: lane (lr = lane & 15, lg = lane >> 4) holds rows
 // 4 lg .. 4 lg + 3 of column lr; an A/B operand lane holds row/column lr and
-// the 8 reduction elements 8 lg .. 8 lg + 7 of a 32-wide step.
+// the 8 reduction elements 8 lg .. 8 lg + 7 of a 32-wide step (any order
+// works as long as A and B agree: the P' V step uses keys 4 lg .. +3 and
+// 16 + 4 lg .. +3 of each 32-key window, where the S^T tiles left them).
 template <bool VERIFY>
 __global__ __launch_bounds__(256) void kv_attn_mfma_kernel(AttnArgs a) {
   constexpr int kKP = kD + 8;      // K: [key][dim] pitch (halves)
   constexpr int kVP = kChunk + 8;  // V: [dim][key] pitch (halves)
-  constexpr int kPP = kChunk + 8;  // P': [row][key] pitch (halves)
   __shared__ __attribute__((aligned(16))) _Float16 kt[kChunk * kKP];
   __shared__ __attribute__((aligned(16))) _Float16 vt[kD * kVP];
-  __shared__ __attribute__((aligned(16))) _Float16 pt[4][2][16 * kPP];   // per wave: P' hi, lo
-  __shared__ float ksc[kChunk], vsc[kChunk];
+  __shared__ __attribute__((aligned(16))) float ksc[kChunk], vsc[kChunk];
   const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-  const int r0 = 64 * blockIdx.z + 16 * wave;   // this wave's first query row
-  const bool live = r0 < a.RQ;                   // wave-uniform
+  const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int r0 = 64 * blockIdx.z + 16 * (tid >> 6);   // this wave's first query row
+  const bool live = r0 < a.RQ;                          // wave-uniform
   const int P = a.L + a.T;
   const int pb = c * a.span, pe = min(pb + a.span, P);
 
   // Q operand: row r0 + lr, dimensions 32 st + 8 lg .. +8
+  const int qrow = r0 + lr;
+  const bool real = qrow < a.RQ;
   half8 qa[4];
-  float qinv[4];
-  uint64_t am[4];
+  float qinv;
+  uint64_t am;
   {
-    const int qrow = r0 + lr;
-    const bool real = qrow < a.RQ;
     const int t = real ? qrow / a.g : 0, j = h * a.g + (real ? qrow % a.g : 0);
     const uint16_t *qp = a.q + ((size_t)t * a.H_q + j) * kD;
     float qf[32];
@@ -145,82 +192,97 @@ __global__ __launch_bounds__(256) void kv_attn_mfma_kernel(AttnArgs a) {
     for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int k = 0; k < 8; ++k) qa[st][k] = (_Float16)ldexpf(qf[8 * st + k], qe);
-    const float qi = ldexpf(0.08838834764831845f, -qe);   // 2^-qe / sqrt(128)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      qinv[i] = __shfl(qi, 4 * lg + i);
-      const int row = r0 + 4 * lg + i;
-      am[i] = a.anc[row < a.RQ ? row / a.g : 0];
-    }
+    qinv = ldexpf(0.12751743082459868f, -qe);   // 2^-qe log2(e) / sqrt(128): scores in base 2
+    am = a.anc[t];
   }
 
-  float m[4], l[4];
+  float m = -INFINITY, l = 0.0f, R = 1.0f;   // O = o * R
   floatx4 o[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m[i] = -INFINITY;
-    l[i] = 0.0f;
-  }
-#pragma unroll
   for (int d = 0; d < 8; ++d) o[d] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-  _Float16 *ph = pt[wave][0], *pl = pt[wave][1];
   const float unit = VERIFY ? 0.0625f : 1.0f;
 
-  for (int p0 = pb; p0 < pe; p0 += kChunk) {
-    const int nk = min(kChunk, pe - p0);   // >= 1; keys past nk repeat key nk - 1 and are masked
-    __syncthreads();                       // the previous sub-chunk's LDS reads are done
-    for (int it = tid; it < 256; it += blockDim.x) {
-      if (it < 128) {   // K: key it / 2, dimensions 64 (it & 1) .. +64
-        const int key = it >> 1, hh = it & 1;
-        const size_t row = (size_t)(p0 + min(key, nk - 1)) * a.H_kv + h;
-        const uint4 *bp = reinterpret_cast<const uint4 *>(a.kb + row * 64 + hh * 32);
-        const uint4 b0 = bp[0], b1 = bp[1];
-        uint4 q0 = make_uint4(0, 0, 0, 0), q1 = q0;
-        if constexpr (VERIFY) {
-          const uint4 *rp = reinterpret_cast<const uint4 *>(a.kr + row * 64 + hh * 32);
-          q0 = rp[0];
-          q1 = rp[1];
-        }
-        const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-        const uint32_t rw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+  const bool kside = tid < 128;   // wave-uniform
+  const int fkey = tid >> 1, fhh = tid & 1;               // K side
+  const int fdg = tid & 15, fkg = (tid >> 4) & 7;         // V side
+  const uint32_t rs = (uint32_t)a.H_kv * 64;              // bytes between positions
+  Fill<VERIFY> f;
+  auto load = [&](int q0) {
+    const int n = min(kChunk, pe - q0);   // keys past n repeat key n - 1 (masked later)
+    const size_t cr = (size_t)q0 * a.H_kv + h;   // first row of the sub-chunk
+    if (kside) {
+      const uint32_t kr = (uint32_t)min(fkey, n - 1);
+      const uint32_t off = kr * rs + fhh * 32;
+      const uint4 *bp = reinterpret_cast<const uint4 *>(a.kb + cr * 64 + off);
+      const uint4 b0 = bp[0], b1 = bp[1];
+      f.b[0] = b0.x; f.b[1] = b0.y; f.b[2] = b0.z; f.b[3] = b0.w;
+      f.b[4] = b1.x; f.b[5] = b1.y; f.b[6] = b1.z; f.b[7] = b1.w;
+      if constexpr (VERIFY) {
+        const uint4 *rp = reinterpret_cast<const uint4 *>(a.kr + cr * 64 + off);
+        const uint4 r0v = rp[0], r1v = rp[1];
+        f.r[0] = r0v.x; f.r[1] = r0v.y; f.r[2] = r0v.z; f.r[3] = r0v.w;
+        f.r[4] = r1v.x; f.r[5] = r1v.y; f.r[6] = r1v.z; f.r[7] = r1v.w;
+      }
+      f.sc[0] = a.ks[cr + kr * a.H_kv];
+    } else {
 #pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          half8 hv;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) hv[i] = code(bw[w], rw[w], i, VERIFY);
-          *reinterpret_cast<half8 *>(kt + key * kKP + hh * 64 + 8 * w) = hv;
-        }
-        if (hh == 0) ksc[key] = a.ks[row] * unit;
-      } else {          // V: keys 8 kg .. +8 x dimensions 8 dg .. +8, stored transposed
-        const int dg = it & 15, kg = (it >> 4) & 7;
-        uint32_t bw[8], rw[8];
-        size_t rows[8];
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          rows[kk] = (size_t)(p0 + min(8 * kg + kk, nk - 1)) * a.H_kv + h;
-          bw[kk] = reinterpret_cast<const uint32_t *>(a.vb + rows[kk] * 64)[dg];
-          rw[kk] = VERIFY ? reinterpret_cast<const uint32_t *>(a.vr + rows[kk] * 64)[dg] : 0u;
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          half8 hv;
-#pragma unroll
-          for (int kk = 0; kk < 8; ++kk) hv[kk] = code(bw[kk], rw[kk], i, VERIFY);
-          *reinterpret_cast<half8 *>(vt + (8 * dg + i) * kVP + 8 * kg) = hv;
-        }
-        if (dg == 0)
-#pragma unroll
-          for (int kk = 0; kk < 8; ++kk) vsc[8 * kg + kk] = a.vs[rows[kk]] * unit;
+      for (int kk = 0; kk < 8; ++kk) {
+        const uint32_t kr = (uint32_t)min(8 * fkg + kk, n - 1);
+        const uint32_t off = kr * rs + fdg * 4;
+        f.b[kk] = *reinterpret_cast<const uint32_t *>(a.vb + cr * 64 + off);
+        if constexpr (VERIFY) f.r[kk] = *reinterpret_cast<const uint32_t *>(a.vr + cr * 64 + off);
+        f.sc[kk] = a.vs[cr + kr * a.H_kv];
       }
     }
+  };
+  if (pb < pe) load(pb);
+
+  for (int p0 = pb; p0 < pe; p0 += kChunk) {
+    const int nk = min(kChunk, pe - p0);   // >= 1; keys past nk are masked
+    __syncthreads();                       // the previous sub-chunk's LDS reads are done
+    if (kside) {   // K row fkey, dimensions 64 fhh .. +64, key-major
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        uint32_t E, O;
+        ucodes<VERIFY>(f.b[w], f.r[w], E, O);
+        uint4 v;
+        v.x = hpair<VERIFY, 0>(O, E);
+        v.y = hpair<VERIFY, 1>(O, E);
+        v.z = hpair<VERIFY, 2>(O, E);
+        v.w = hpair<VERIFY, 3>(O, E);
+        *reinterpret_cast<uint4 *>(kt + fkey * kKP + fhh * 64 + 8 * w) = v;
+      }
+      if (fhh == 0) ksc[fkey] = f.sc[0] * unit;
+    } else {       // V rows 8 fkg .. +8, dimensions 8 fdg .. +8, dimension-major
+      uint32_t E[8], O[8];
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) ucodes<VERIFY>(f.b[kk], f.r[kk], E[kk], O[kk]);
+#define NL_VROW(I, X)                                                                             \
+  {                                                                                               \
+    uint4 v;                                                                                      \
+    v.x = hpair<VERIFY, (I) / 2>(X[1], X[0]);                                                     \
+    v.y = hpair<VERIFY, (I) / 2>(X[3], X[2]);                                                     \
+    v.z = hpair<VERIFY, (I) / 2>(X[5], X[4]);                                                     \
+    v.w = hpair<VERIFY, (I) / 2>(X[7], X[6]);                                                     \
+    *reinterpret_cast<uint4 *>(vt + (8 * fdg + (I)) * kVP + 8 * fkg) = v;                         \
+  }
+      NL_VROW(0, E) NL_VROW(1, O) NL_VROW(2, E) NL_VROW(3, O)
+      NL_VROW(4, E) NL_VROW(5, O) NL_VROW(6, E) NL_VROW(7, O)
+#undef NL_VROW
+      if (fdg == 0)
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) vsc[8 * fkg + kk] = f.sc[kk] * unit;
+    }
+    if (p0 + kChunk < pe) load(p0 + kChunk);   // in flight during this sub-chunk's products
     __syncthreads();
     if (!live) continue;
 
-    float vm = vsc[lane];   // largest V scale of the sub-chunk
-#pragma unroll
-    for (int o2 = 1; o2 < 64; o2 <<= 1) vm = fmaxf(vm, __shfl_xor(vm, o2));
+    const float4 v4 = reinterpret_cast<const float4 *>(vsc)[lr];   // largest V scale of the sub-chunk
+    const float vm = row_max(fmaxf(fmaxf(v4.x, v4.y), fmaxf(v4.z, v4.w)));
     const float vinv = vm > 0.0f ? 1.0f / vm : 0.0f;
+    const float Rn = vm > 0.0f ? vm : R;
 
+    // lane holds S[row lr][key 16 t + 4 lg + i]
     floatx4 sc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -228,90 +290,82 @@ __global__ __launch_bounds__(256) void kv_attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const half8 kb8 = *reinterpret_cast<const half8 *>(kt + (16 * t + lr) * kKP + 32 * st + 8 * lg);
-        sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[st], kb8, sc[t], 0, 0, 0);
+        sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb8, qa[st], sc[t], 0, 0, 0);
       }
+      const float4 k4 = reinterpret_cast<const float4 *>(ksc)[4 * t + lg];
+      sc[t][0] *= qinv * k4.x;
+      sc[t][1] *= qinv * k4.y;
+      sc[t][2] *= qinv * k4.z;
+      sc[t][3] *= qinv * k4.w;
     }
-    // lane holds S[row 4 lg + i][key 16 t + lr]
-    float tmax[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if (p0 + kChunk > a.L) {   // the sub-chunk reaches the tree or the span's end
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = 16 * t + 4 * lg + i, pos = p0 + key;
+          const uint32_t bit = (uint32_t)min(max(pos - a.L, 0), 63);
+          const bool vis = (key < nk) & ((pos < a.L) | (((am >> bit) & 1ull) != 0));
+          sc[t][i] = vis ? sc[t][i] : -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) mx = fmaxf(mx, fmaxf(fmaxf(sc[t][0], sc[t][1]), fmaxf(sc[t][2], sc[t][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx);
+    const float msub = mn == -INFINITY ? 0.0f : mn;   // nothing visible yet: every weight is 2^-inf = 0
+    const float al = __builtin_amdgcn_exp2f(m - msub);
+    m = mn;
+    l *= al;
+    const float f_o = al * (R / Rn);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) o[d] *= f_o;
+    R = Rn;
+    // P'^T operands of the two 32-key windows: keys 32 w + 4 lg + i (tile 2w)
+    // then 32 w + 16 + 4 lg + i (tile 2w + 1)
+    half8 bh[2], bl[2];
+    float ps = 0.0f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int key = 16 * t + lr, pos = p0 + key;
-      const float ks = ksc[key];
-      const int bit = min(max(pos - a.L, 0), 63);
+      const float4 s4 = reinterpret_cast<const float4 *>(vsc)[4 * t + lg];
+      const float vsk[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool vis = key < nk && (pos < a.L || ((am[i] >> bit) & 1ull));
-        sc[t][i] = vis ? sc[t][i] * qinv[i] * ks : -INFINITY;
-        tmax[i] = fmaxf(tmax[i], sc[t][i]);
-      }
-    }
-#pragma unroll
-    for (int o2 = 1; o2 < 16; o2 <<= 1)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) tmax[i] = fmaxf(tmax[i], __shfl_xor(tmax[i], o2));
-    float psum[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float mn = fmaxf(m[i], tmax[i]);
-      const float al = mn == -INFINITY ? 1.0f : expf(m[i] - mn);
-      m[i] = mn;
-      l[i] *= al;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) o[d][i] *= al;
-      psum[i] = 0.0f;
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const float vs = vsc[16 * t + lr] * vinv;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = sc[t][i] == -INFINITY ? 0.0f : expf(sc[t][i] - m[i]);
-        psum[i] += p;
-        const float x = p * vs;
+        const float p = __builtin_amdgcn_exp2f(sc[t][i] - msub);
+        ps += p;
+        const float x = p * (vsk[i] * vinv);
         const _Float16 hi = (_Float16)x;
-        ph[(4 * lg + i) * kPP + 16 * t + lr] = hi;
-        pl[(4 * lg + i) * kPP + 16 * t + lr] = (_Float16)(x - (float)hi);   // x - hi is exact
+        bh[t >> 1][4 * (t & 1) + i] = hi;
+        bl[t >> 1][4 * (t & 1) + i] = (_Float16)(x - (float)hi);   // x - hi is exact
       }
     }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    l += ps;
 #pragma unroll
-    for (int o2 = 1; o2 < 16; o2 <<= 1)
+    for (int d = 0; d < 8; ++d)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) psum[i] += __shfl_xor(psum[i], o2);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) l[i] += psum[i];
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's P' tile is in LDS
-
-    floatx4 oc[8];
-#pragma unroll
-    for (int d = 0; d < 8; ++d) oc[d] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      const half8 pah = *reinterpret_cast<const half8 *>(ph + lr * kPP + 32 * w + 8 * lg);
-      const half8 pal = *reinterpret_cast<const half8 *>(pl + lr * kPP + 32 * w + 8 * lg);
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const half8 vb8 = *reinterpret_cast<const half8 *>(vt + (16 * d + lr) * kVP + 32 * w + 8 * lg);
-        oc[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pah, vb8, oc[d], 0, 0, 0);
-        oc[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pal, vb8, oc[d], 0, 0, 0);
+      for (int w = 0; w < 2; ++w) {
+        const _Float16 *vp = vt + (16 * d + lr) * kVP + 32 * w + 4 * lg;
+        const uint2 v0 = *reinterpret_cast<const uint2 *>(vp);
+        const uint2 v1 = *reinterpret_cast<const uint2 *>(vp + 16);
+        const half8 va = __builtin_bit_cast(half8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, bh[w], o[d], 0, 0, 0);
+        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, bl[w], o[d], 0, 0, 0);
       }
-    }
-#pragma unroll
-    for (int d = 0; d < 8; ++d) o[d] += vm * oc[d];
   }
-  if (!live) return;
-  // partials: lane holds O[row 4 lg + i][dimension 16 d + lr]
+  if (!live || !real) return;
+  // partials: lane holds O[row qrow][dimension 16 d + 4 lg + i]
+  const size_t base = ((size_t)c * a.H_kv + h) * a.RQ + qrow;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = r0 + 4 * lg + i;
-    if (row < a.RQ) {
-      const size_t base = ((size_t)c * a.H_kv + h) * a.RQ + row;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) a.part_o[base * kD + 16 * d + lr] = o[d][i];
-      if (lr == 0) {
-        a.part_ml[base * 2] = m[i];
-        a.part_ml[base * 2 + 1] = l[i];
-      }
-    }
+  for (int d = 0; d < 8; ++d)
+    *reinterpret_cast<float4 *>(a.part_o + base * kD + 16 * d + 4 * lg) =
+        make_float4(o[d][0] * R, o[d][1] * R, o[d][2] * R, o[d][3] * R);
+  if (lg == 0) {
+    a.part_ml[base * 2] = m;
+    a.part_ml[base * 2 + 1] = l;
   }
 }
 
@@ -330,7 +384,7 @@ __global__ __launch_bounds__(256) void kv_combine_kernel(AttnArgs a, int chunks,
     const float lc = tid < chunks ? a.part_ml[base * 2 + 1] : 0.0f;
     float M = mc;
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    const float w = mc == -INFINITY ? 0.0f : expf(mc - M);   // a chunk with no visible key weighs 0
+    const float w = mc == -INFINITY ? 0.0f : exp2f(mc - M);   // a chunk with no visible key weighs 0
     float ls = lc * w;
     for (int o = 32; o >= 1; o >>= 1) ls += __shfl_xor(ls, o);
     wsh[tid] = w;
