@@ -14,6 +14,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -277,84 +278,90 @@ __global__ __launch_bounds__(256) void kv_attn_mfma_kernel(AttnArgs a) {
     __syncthreads();
     if (!live) continue;
 
-    const float4 v4 = reinterpret_cast<const float4 *>(vsc)[lr];   // largest V scale of the sub-chunk
-    const float vm = row_max(fmaxf(fmaxf(v4.x, v4.y), fmaxf(v4.z, v4.w)));
-    const float vinv = vm > 0.0f ? 1.0f / vm : 0.0f;
-    const float Rn = vm > 0.0f ? vm : R;
+    auto step = [&](auto masked) {
+      const float4 v4 = reinterpret_cast<const float4 *>(vsc)[lr];   // largest V scale of the sub-chunk
+      const float vm = row_max(fmaxf(fmaxf(v4.x, v4.y), fmaxf(v4.z, v4.w)));
+      const float vinv = vm > 0.0f ? 1.0f / vm : 0.0f;
+      const float Rn = vm > 0.0f ? vm : R;
 
-    // lane holds S[row lr][key 16 t + 4 lg + i]
-    floatx4 sc[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      sc[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const half8 kb8 = *reinterpret_cast<const half8 *>(kt + (16 * t + lr) * kKP + 32 * st + 8 * lg);
-        sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb8, qa[st], sc[t], 0, 0, 0);
-      }
-      const float4 k4 = reinterpret_cast<const float4 *>(ksc)[4 * t + lg];
-      sc[t][0] *= qinv * k4.x;
-      sc[t][1] *= qinv * k4.y;
-      sc[t][2] *= qinv * k4.z;
-      sc[t][3] *= qinv * k4.w;
-    }
-    if (p0 + kChunk > a.L) {   // the sub-chunk reaches the tree or the span's end
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = 16 * t + 4 * lg + i, pos = p0 + key;
-          const uint32_t bit = (uint32_t)min(max(pos - a.L, 0), 63);
-          const bool vis = (key < nk) & ((pos < a.L) | (((am >> bit) & 1ull) != 0));
-          sc[t][i] = vis ? sc[t][i] : -INFINITY;
+      // lane holds S[row lr][key 16 t + 4 lg + i]
+      floatx4 sc[4];
+  #pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        sc[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  #pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const half8 kb8 = *reinterpret_cast<const half8 *>(kt + (16 * t + lr) * kKP + 32 * st + 8 * lg);
+          sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb8, qa[st], sc[t], 0, 0, 0);
         }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) mx = fmaxf(mx, fmaxf(fmaxf(sc[t][0], sc[t][1]), fmaxf(sc[t][2], sc[t][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(m, mx);
-    const float msub = mn == -INFINITY ? 0.0f : mn;   // nothing visible yet: every weight is 2^-inf = 0
-    const float al = __builtin_amdgcn_exp2f(m - msub);
-    m = mn;
-    l *= al;
-    const float f_o = al * (R / Rn);
-#pragma unroll
-    for (int d = 0; d < 8; ++d) o[d] *= f_o;
-    R = Rn;
-    // P'^T operands of the two 32-key windows: keys 32 w + 4 lg + i (tile 2w)
-    // then 32 w + 16 + 4 lg + i (tile 2w + 1)
-    half8 bh[2], bl[2];
-    float ps = 0.0f;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const float4 s4 = reinterpret_cast<const float4 *>(vsc)[4 * t + lg];
-      const float vsk[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(sc[t][i] - msub);
-        ps += p;
-        const float x = p * (vsk[i] * vinv);
-        const _Float16 hi = (_Float16)x;
-        bh[t >> 1][4 * (t & 1) + i] = hi;
-        bl[t >> 1][4 * (t & 1) + i] = (_Float16)(x - (float)hi);   // x - hi is exact
+        const float4 k4 = reinterpret_cast<const float4 *>(ksc)[4 * t + lg];
+        sc[t][0] *= qinv * k4.x;
+        sc[t][1] *= qinv * k4.y;
+        sc[t][2] *= qinv * k4.z;
+        sc[t][3] *= qinv * k4.w;
       }
-    }
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
-    l += ps;
-#pragma unroll
-    for (int d = 0; d < 8; ++d)
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const _Float16 *vp = vt + (16 * d + lr) * kVP + 32 * w + 4 * lg;
-        const uint2 v0 = *reinterpret_cast<const uint2 *>(vp);
-        const uint2 v1 = *reinterpret_cast<const uint2 *>(vp + 16);
-        const half8 va = __builtin_bit_cast(half8, make_uint4(v0.x, v0.y, v1.x, v1.y));
-        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, bh[w], o[d], 0, 0, 0);
-        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, bl[w], o[d], 0, 0, 0);
+      if constexpr (decltype(masked)::value) {   // the sub-chunk reaches the tree or the span's end
+  #pragma unroll
+        for (int t = 0; t < 4; ++t)
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = 16 * t + 4 * lg + i, pos = p0 + key;
+            const uint32_t bit = (uint32_t)min(max(pos - a.L, 0), 63);
+            const bool vis = (key < nk) & ((pos < a.L) | (((am >> bit) & 1ull) != 0));
+            sc[t][i] = vis ? sc[t][i] : -INFINITY;
+          }
       }
+      float mx = -INFINITY;
+  #pragma unroll
+      for (int t = 0; t < 4; ++t) mx = fmaxf(mx, fmaxf(fmaxf(sc[t][0], sc[t][1]), fmaxf(sc[t][2], sc[t][3])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m, mx);
+      const float msub = mn == -INFINITY ? 0.0f : mn;   // nothing visible yet: every weight is 2^-inf = 0
+      const float al = __builtin_amdgcn_exp2f(m - msub);
+      m = mn;
+      l *= al;
+      const float f_o = al * (R / Rn);
+  #pragma unroll
+      for (int d = 0; d < 8; ++d) o[d] *= f_o;
+      R = Rn;
+      // P'^T operands of the two 32-key windows: keys 32 w + 4 lg + i (tile 2w)
+      // then 32 w + 16 + 4 lg + i (tile 2w + 1)
+      half8 bh[2], bl[2];
+      float ps = 0.0f;
+  #pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float4 s4 = reinterpret_cast<const float4 *>(vsc)[4 * t + lg];
+        const float vsk[4] = {s4.x, s4.y, s4.z, s4.w};
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = __builtin_amdgcn_exp2f(sc[t][i] - msub);
+          ps += p;
+          const float x = p * (vsk[i] * vinv);
+          const _Float16 hi = (_Float16)x;
+          bh[t >> 1][4 * (t & 1) + i] = hi;
+          bl[t >> 1][4 * (t & 1) + i] = (_Float16)(x - (float)hi);   // x - hi is exact
+        }
+      }
+      ps += __shfl_xor(ps, 16);
+      ps += __shfl_xor(ps, 32);
+      l += ps;
+  #pragma unroll
+      for (int d = 0; d < 8; ++d)
+  #pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const _Float16 *vp = vt + (16 * d + lr) * kVP + 32 * w + 4 * lg;
+          const uint2 v0 = *reinterpret_cast<const uint2 *>(vp);
+          const uint2 v1 = *reinterpret_cast<const uint2 *>(vp + 16);
+          const half8 va = __builtin_bit_cast(half8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+          o[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, bh[w], o[d], 0, 0, 0);
+          o[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, bl[w], o[d], 0, 0, 0);
+        }
+    };
+    if (p0 + kChunk > a.L)
+      step(std::true_type{});
+    else
+      step(std::false_type{});   // context keys only: nothing to mask
   }
   if (!live || !real) return;
   // partials: lane holds O[row qrow][dimension 16 d + 4 lg + i]
@@ -378,6 +385,17 @@ __global__ __launch_bounds__(256) void kv_combine_kernel(AttnArgs a, int chunks,
   __shared__ float lsh;
   const int h = blockIdx.y, r = blockIdx.x, tid = threadIdx.x;
   const int t = r / a.g, j = h * a.g + r % a.g;
+  const int cg = tid >> 6, ld = tid & 63;
+  // every load is issued before any result is needed: each thread's two
+  // dimensions of chunks cg, cg + 4, ... and wave 0's (max, sum) pairs
+  float2 v[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int cc = cg + 4 * k;
+    v[k] = cc < chunks
+               ? reinterpret_cast<const float2 *>(a.part_o + (((size_t)cc * a.H_kv + h) * a.RQ + r) * kD)[ld]
+               : make_float2(0.0f, 0.0f);
+  }
   if (tid < 64) {
     const size_t base = ((size_t)tid * a.H_kv + h) * a.RQ + r;
     const float mc = tid < chunks ? a.part_ml[base * 2] : -INFINITY;
@@ -391,13 +409,13 @@ __global__ __launch_bounds__(256) void kv_combine_kernel(AttnArgs a, int chunks,
     if (tid == 0) lsh = ls;
   }
   __syncthreads();
-  const int cg = tid >> 6, ld = tid & 63;
   float o0 = 0.0f, o1 = 0.0f;
-#pragma unroll 16
-  for (int cc = cg; cc < chunks; cc += 4) {
-    const float2 v = reinterpret_cast<const float2 *>(a.part_o + (((size_t)cc * a.H_kv + h) * a.RQ + r) * kD)[ld];
-    o0 += wsh[cc] * v.x;
-    o1 += wsh[cc] * v.y;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int cc = cg + 4 * k;
+    const float w = cc < chunks ? wsh[cc] : 0.0f;
+    o0 += w * v[k].x;
+    o1 += w * v[k].y;
   }
   osum[cg][2 * ld] = o0;
   osum[cg][2 * ld + 1] = o1;
