@@ -2,12 +2,15 @@
 (include/nested_kv.h) with the oracle (oracle/kv.py).
 
 The writer's codes and scales are integer/fp32 decisions taken the same way
-on both sides (correctly rounded fp32 divisions, round half to even, no
-fused multiply-add), so the planes are compared byte for byte.  The
-attention runs in fp32 against the fp64 oracle: a score is a 128-term fp32
-dot product (relative error ~1e-6) and the output an fp32 running sum over
-at most a few thousand keys, so |dO| <= 5e-4 * max|v_hat| holds with a wide
-margin.
+on both sides (correctly rounded fp32 divisions, round half to even, the
+residual formed exactly), so the planes are compared byte for byte.  The
+attention runs on fp16 matrix cores against the fp64 oracle: the query is
+widened to fp16 exactly (a power of two per row), the K/V codes are exact
+fp16 integers whose products land exactly in fp32 accumulators, a score is
+an fp32 sum of 128 terms (relative error ~1e-5 at worst), the softmax
+weights times the V scales travel as an fp16 pair hi + lo (~22 bits), and
+the output is an fp32 sum over at most a few thousand keys, so
+|dO| <= 5e-4 * max|v_hat| holds with a wide margin.
 """
 import numpy as np
 import pytest
