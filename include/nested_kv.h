@@ -54,9 +54,9 @@ nl_status nested_kv_attention_workspace_bytes(int32_t T, int32_t H_q, int32_t H_
  * nested_kv_attention_workspace_bytes(...).  Two launches: the positions
  * are split into spans of 64-position sub-chunks (at most 64 spans per KV
  * head), each span's partial softmax state is written to ws, then the spans
- * are combined.  Both products run on fp16 matrix cores; the result is
- * within about 1e-5 of max|v| of the exact attention over the dequantised
- * cache.
+ * are combined.  Both products run on fp16 matrix cores with exact integer
+ * K/V codes and fp32 accumulation; the result is held to within 5e-4 of
+ * max|v| of the exact attention over the dequantised cache.
  * Errors: NL_EINVAL (T outside 1..64, H_kv < 1, H_q not a multiple of H_kv,
  * T * H_q / H_kv > 256, L < 0, NULL pointer, small or misaligned ws),
  * NL_EHIP.
