@@ -711,6 +711,8 @@ def main():
                     help="run only the encoder leg and the counter calibration copy (for rocprofv3)")
     ap.add_argument("--pmc-summary-encoder", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the encoder's traffic summary from two rocprofv3 --pmc runs of --encoder-only")
+    ap.add_argument("--kv-only", action="store_true",
+                    help="run only the nested-KV leg (writer and tree attention) and print its JSON")
     ap.add_argument("--w4w8-only", action="store_true",
                     help="run only the W4/W8 leg and the counter calibration copy (for rocprofv3)")
     ap.add_argument("--pmc-summary-w4w8", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -748,6 +750,9 @@ def main():
         w48 = w4w8_leg(nl, torch, synth, args.reps, args.pool_gib, roofline_only=True)
         calib = copy_calibration(torch)
         print(json.dumps({"w4w8": w48, "copy_calibration": calib}), flush=True)
+        return
+    if args.kv_only:
+        print(json.dumps({"nested_kv": kv_leg(nl, torch, synth, args.reps)}), flush=True)
         return
     if args.encoder_only:
         enc = encoder_leg(nl, torch, synth, args.reps)

@@ -69,7 +69,12 @@ def test_write_matches_oracle(nl, torch_cuda):
     np.testing.assert_array_equal(sc.cpu().numpy()[rows], s)
 
 
-CASES = [(1, 8, 8, 0), (5, 6, 2, 64), (16, 32, 8, 1000), (64, 4, 1, 300), (16, 32, 8, 4096), (3, 2, 2, 127)]
+# (T, H_q, H_kv, L): a single row; GQA with a ragged sub-chunk; the 8B-class
+# heads; 256 query rows per KV head (four row blocks); 80 rows (a partial
+# second row block); positions ending exactly on a sub-chunk boundary; a
+# context that spans several 64-key sub-chunks per workgroup
+CASES = [(1, 8, 8, 0), (5, 6, 2, 64), (16, 32, 8, 1000), (64, 4, 1, 300), (16, 32, 8, 4096), (3, 2, 2, 127),
+         (20, 8, 2, 777), (16, 4, 4, 2032), (2, 4, 1, 9000)]
 
 
 @pytest.mark.parametrize("T,H_q,H_kv,L", CASES, ids=[f"T{a}-Hq{b}-Hkv{c}-L{d}" for a, b, c, d in CASES])
@@ -124,3 +129,40 @@ def test_draft_reads_no_refinement(nl, torch_cuda):
     with pytest.raises(nl.NLError):
         nl.nested_kv_attention(d(q.view(np.int16)), T, H_q, H_kv, L, kb, None, ks, vb, None, vs,
                                d(anc.view(np.int64)), True, out, ws)
+
+
+def test_attention_scale_extremes(nl, torch_cuda):
+    # V scales spread over ~e^+-6 and zero K and V vectors: the kernel's
+    # per-sub-chunk V-scale normalisation and its zero-scale guards
+    rng = np.random.default_rng(17)
+    T, H_q, H_kv, L = 16, 8, 2, 700
+    P = L + T
+    kx = vectors(rng, P * H_kv).reshape(P * H_kv, 128)
+    vx = synth.f32_to_bf16_bits(rng.standard_normal((P * H_kv, 128)).astype(np.float32)
+                                * np.exp(rng.normal(0, 2.0, (P * H_kv, 1))).astype(np.float32))
+    kx[rng.choice(P * H_kv, 40, replace=False)] = 0
+    vx[rng.choice(P * H_kv, 40, replace=False)] = 0
+    vx[2 * 64 * H_kv:3 * 64 * H_kv] = 0                 # a whole sub-chunk of zero values
+    q = vectors(rng, T * H_q).reshape(T, H_q, 128)
+    anc = tree.build(synth.make_rank_stats(8, 4, cfg=17), T)["anc"]
+    kb, kr, ks = write(nl, torch_cuda, kx, np.arange(P * H_kv), P * H_kv)
+    vb, vr, vs = write(nl, torch_cuda, vx, np.arange(P * H_kv), P * H_kv)
+    d = lambda a: torch_cuda.from_numpy(np.ascontiguousarray(a)).cuda()
+    ws = torch_cuda.empty(nl.nested_kv_attention_workspace_bytes(T, H_q, H_kv, L), dtype=torch_cuda.uint8,
+                          device="cuda")
+    out = torch_cuda.empty((T, H_q, 128), dtype=torch_cuda.float32, device="cuda")
+    qk4, qkr, sk = kv.quantize(kx)
+    qv4, qvr, sv = kv.quantize(vx)
+    for verify in (True, False):
+        nl.nested_kv_attention(d(q.view(np.int16)), T, H_q, H_kv, L, kb, kr, ks, vb, vr, vs,
+                               d(anc.view(np.int64)), verify, out, ws)
+        got = out.cpu().numpy().astype(np.float64)
+        kh = kv.dequant(qk4, qkr, sk, verify).reshape(P, H_kv, 128)
+        vh = kv.dequant(qv4, qvr, sv, verify).reshape(P, H_kv, 128)
+        want = kv.attention(q, kh, vh, L, anc, H_kv)
+        assert np.isfinite(got).all()
+        # each output is held to the largest |v_hat| of its own KV head
+        for h in range(H_kv):
+            js = slice(h * (H_q // H_kv), (h + 1) * (H_q // H_kv))
+            err = np.abs(got[:, js] - want[:, js]).max() / np.abs(vh[:, h]).max()
+            assert err <= TOL, (verify, h, err)
