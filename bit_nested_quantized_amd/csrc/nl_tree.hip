@@ -4,8 +4,10 @@
 // Build: one wave.  Candidate slot s < R is the root's child of rank s; slot
 // R + k R + r is node k's child of rank r, so slot order is push order and
 // "largest priority, then smallest slot" is the heap-with-counter order.
-// Each step is a wave-wide argmax over the live slots in LDS; the winner
-// becomes node k and its R children are written by R lanes.
+// Lane l keeps the priorities of slots l, l + 64, ... in registers, and the
+// probability rows the build can reach sit in LDS.  Each step is a wave-wide
+// argmax (largest priority, then smallest slot); the winner becomes node k,
+// its slot dies, and the lanes that own its children's slots compute them.
 //
 // Accept: one wave per sequence; lane c holds node c's parent and token, and
 // each step is one ballot for the child of the current node whose token is
@@ -25,51 +27,99 @@ namespace {
 
 constexpr int kMaxSlots = NL_TREE_MAX_RANKS * (1 + NL_TREE_MAX_NODES);
 
+// One reduction step of (priority, slot) under "larger priority, then
+// smaller slot" (associative and commutative, so any exchange pattern that
+// reaches every lane gives every lane the same winner).
+__device__ __forceinline__ void arg_merge(double &bp, int &bs, double op, int os) {
+  if (op > bp || (op == bp && os < bs)) {
+    bp = op;
+    bs = os;
+  }
+}
+template <int CTRL>
+__device__ __forceinline__ int dppi(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ void arg_dpp(double &bp, int &bs) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(bp);
+  const unsigned lo = (unsigned)dppi<CTRL>((int)(unsigned)b), hi = (unsigned)dppi<CTRL>((int)(unsigned)(b >> 32));
+  arg_merge(bp, bs, __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo)), dppi<CTRL>(bs));
+}
+
 __global__ __launch_bounds__(64) void tree_build_kernel(const double *p, int D, int R, int N, int32_t *parent,
                                                         int32_t *depth, int32_t *rank, double *prio,
                                                         uint64_t *anc, int32_t *count) {
-  __shared__ double cp[kMaxSlots];
-  __shared__ int ndep[NL_TREE_MAX_NODES];
+  constexpr int kJ = (kMaxSlots + 63) / 64;   // slots per lane: slot lane + 64 j
+  __shared__ double pl[(NL_TREE_MAX_NODES + 1) * NL_TREE_MAX_RANKS];
+  __shared__ int ndep[NL_TREE_MAX_NODES], npar[NL_TREE_MAX_NODES], nrank[NL_TREE_MAX_NODES];
   __shared__ uint64_t nanc[NL_TREE_MAX_NODES];
+  __shared__ double nprio[NL_TREE_MAX_NODES];
   const int lane = threadIdx.x;
-  const int S = R + N * R;
-  for (int s = lane; s < S; s += 64) cp[s] = s < R ? p[s] : -1.0;   // depth-1 paths
+  // a node's depth is at most N, so rows 0 .. min(D, N + 1) - 1 of p are all
+  // the build reads
+  const int rows = min(D, N + 1);
+  for (int i = lane; i < rows * R; i += 64) pl[i] = p[i];
+  double cp[kJ];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const int s = lane + 64 * j;
+    cp[j] = s < R ? p[s] : -1.0;   // depth-1 paths; -1 marks a dead or unwritten slot
+  }
   __syncthreads();
   int k = 0;
   for (; k < N; ++k) {
     double bp = -1.0;
     int bs = 0x7FFFFFFF;
-    for (int s = lane; s < S; s += 64)
-      if (cp[s] > bp) {   // ascending slots: an equal later slot never wins
-        bp = cp[s];
-        bs = s;
+#pragma unroll
+    for (int j = 0; j < kJ; ++j)
+      if (cp[j] > bp) {   // ascending slots: an equal later slot never wins
+        bp = cp[j];
+        bs = lane + 64 * j;
       }
-    for (int o = 32; o >= 1; o >>= 1) {
-      const double op = __shfl_xor(bp, o);
-      const int os = __shfl_xor(bs, o);
-      if (op > bp || (op == bp && os < bs)) {
-        bp = op;
-        bs = os;
-      }
-    }
+    // within rows of 16 lanes by DPP (pairs, quads, half-row and row
+    // mirrors), then across rows by two lane exchanges
+    arg_dpp<0xB1>(bp, bs);
+    arg_dpp<0x4E>(bp, bs);
+    arg_dpp<0x141>(bp, bs);
+    arg_dpp<0x140>(bp, bs);
+    arg_merge(bp, bs, __shfl_xor(bp, 16), __shfl_xor(bs, 16));
+    arg_merge(bp, bs, __shfl_xor(bp, 32), __shfl_xor(bs, 32));
     if (bp < 0.0) break;   // no live candidate (uniform)
     const int par = bs < R ? -1 : (bs - R) / R;
     const int rk = bs < R ? bs : (bs - R) % R;
     const int dep = par < 0 ? 1 : ndep[par] + 1;
     const uint64_t am = (par < 0 ? 0ull : nanc[par]) | (1ull << k);
-    __syncthreads();
+    // the winner's slot dies; node k's children take slots R + k R .. + R - 1,
+    // at most one per lane since R <= 16 (the winner's slot lies below them)
+    const int first = R + k * R;
+    const int off = (lane - first) & 63;
+    const bool add = dep < D && off < R;
+    const int jn = (first + off) >> 6, jw = bs >> 6;
+    const bool own = (bs & 63) == lane;
+    const double val = add ? bp * pl[dep * R + off] : -1.0;
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      if (own && j == jw) cp[j] = -1.0;
+      if (add && j == jn) cp[j] = val;
+    }
     if (lane == 0) {
-      cp[bs] = -1.0;
       ndep[k] = dep;
       nanc[k] = am;
-      parent[k] = par;
-      depth[k] = dep;
-      rank[k] = rk;
-      prio[k] = bp;
-      anc[k] = am;
+      npar[k] = par;
+      nrank[k] = rk;
+      nprio[k] = bp;
     }
-    if (dep < D && lane < R) cp[R + k * R + lane] = bp * p[dep * R + lane];
-    __syncthreads();
+    // one wave: its LDS accesses complete in program order, so the next
+    // step's reads see these writes; the clobber keeps the compiler's order
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+  if (lane < k) {   // the nodes go out together, one per lane (N <= 64)
+    parent[lane] = npar[lane];
+    depth[lane] = ndep[lane];
+    rank[lane] = nrank[lane];
+    prio[lane] = nprio[lane];
+    anc[lane] = nanc[lane];
   }
   if (lane == 0) *count = k;
 }
