@@ -147,7 +147,9 @@ struct Fill {
 template <bool VERIFY>
 __global__ __launch_bounds__(256) void kv_attn_mfma_kernel(AttnArgs a) {
   constexpr int kKP = kD + 8;      // K: [key][dim] pitch (halves)
-  constexpr int kVP = kChunk + 8;  // V: [dim][key] pitch (halves)
+  constexpr int kVP = kChunk + 8;  // V: [dim][key] pitch (halves); the 8-key block b of
+                                   // dimension row r sits at block b ^ ((r >> 4) & 7), which
+                                   // keeps the fill's 16-byte stores off shared banks
   __shared__ __attribute__((aligned(16))) _Float16 kt[kChunk * kKP];
   __shared__ __attribute__((aligned(16))) _Float16 vt[kD * kVP];
   __shared__ __attribute__((aligned(16))) float ksc[kChunk], vsc[kChunk];
@@ -265,7 +267,7 @@ __global__ __launch_bounds__(256) void kv_attn_mfma_kernel(AttnArgs a) {
     v.y = hpair<VERIFY, (I) / 2>(X[3], X[2]);                                                     \
     v.z = hpair<VERIFY, (I) / 2>(X[5], X[4]);                                                     \
     v.w = hpair<VERIFY, (I) / 2>(X[7], X[6]);                                                     \
-    *reinterpret_cast<uint4 *>(vt + (8 * fdg + (I)) * kVP + 8 * fkg) = v;                         \
+    *reinterpret_cast<uint4 *>(vt + (8 * fdg + (I)) * kVP + 8 * (fkg ^ ((fdg >> 1) & 7))) = v;   \
   }
       NL_VROW(0, E) NL_VROW(1, O) NL_VROW(2, E) NL_VROW(3, O)
       NL_VROW(4, E) NL_VROW(5, O) NL_VROW(6, E) NL_VROW(7, O)
@@ -350,9 +352,9 @@ __global__ __launch_bounds__(256) void kv_attn_mfma_kernel(AttnArgs a) {
       for (int d = 0; d < 8; ++d)
   #pragma unroll
         for (int w = 0; w < 2; ++w) {
-          const _Float16 *vp = vt + (16 * d + lr) * kVP + 32 * w + 4 * lg;
-          const uint2 v0 = *reinterpret_cast<const uint2 *>(vp);
-          const uint2 v1 = *reinterpret_cast<const uint2 *>(vp + 16);
+          const _Float16 *vr = vt + (16 * d + lr) * kVP + 4 * (lg & 1);
+          const uint2 v0 = *reinterpret_cast<const uint2 *>(vr + 8 * ((4 * w + (lg >> 1)) ^ d));
+          const uint2 v1 = *reinterpret_cast<const uint2 *>(vr + 8 * ((4 * w + 2 + (lg >> 1)) ^ d));
           const half8 va = __builtin_bit_cast(half8, make_uint4(v0.x, v0.y, v1.x, v1.y));
           o[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, bh[w], o[d], 0, 0, 0);
           o[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, bl[w], o[d], 0, 0, 0);
