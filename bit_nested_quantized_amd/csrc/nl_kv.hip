@@ -147,9 +147,9 @@ struct Fill {
 template <bool VERIFY>
 __global__ __launch_bounds__(256) void kv_attn_mfma_kernel(AttnArgs a) {
   constexpr int kKP = kD + 8;      // K: [key][dim] pitch (halves)
-  constexpr int kVP = kChunk + 8;  // V: [dim][key] pitch (halves); the 8-key block b of
-                                   // dimension row r sits at block b ^ ((r >> 4) & 7), which
-                                   // keeps the fill's 16-byte stores off shared banks
+  constexpr int kVP = kChunk + 8;  // V: [dim][8-key block] pitch (halves); block b of
+                                   // dimension row r sits at b ^ ((r >> 4) & 7), which keeps
+                                   // the fill's 16-byte stores off shared banks
   __shared__ __attribute__((aligned(16))) _Float16 kt[kChunk * kKP];
   __shared__ __attribute__((aligned(16))) _Float16 vt[kD * kVP];
   __shared__ __attribute__((aligned(16))) float ksc[kChunk], vsc[kChunk];
@@ -208,6 +208,9 @@ __global__ __launch_bounds__(256) void kv_attn_mfma_kernel(AttnArgs a) {
   const bool kside = tid < 128;   // wave-uniform
   const int fkey = tid >> 1, fhh = tid & 1;               // K side
   const int fdg = tid & 15, fkg = (tid >> 4) & 7;         // V side
+  // V block fkg holds the 8 keys a P'V operand lane reads together: keys
+  // 4 (fkg & 3) .. +3 and 16 + 4 (fkg & 3) .. +3 of the 32-key window fkg / 4
+  auto vkey = [&](int kk) { return 32 * (fkg >> 2) + 4 * (fkg & 3) + (kk & 3) + 16 * (kk >> 2); };
   const uint32_t rs = (uint32_t)a.H_kv * 64;              // bytes between positions
   Fill<VERIFY> f;
   auto load = [&](int q0) {
@@ -230,7 +233,7 @@ __global__ __launch_bounds__(256) void kv_attn_mfma_kernel(AttnArgs a) {
     } else {
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        const uint32_t kr = (uint32_t)min(8 * fkg + kk, n - 1);
+        const uint32_t kr = (uint32_t)min(vkey(kk), n - 1);
         const uint32_t off = kr * rs + fdg * 4;
         f.b[kk] = *reinterpret_cast<const uint32_t *>(a.vb + cr * 64 + off);
         if constexpr (VERIFY) f.r[kk] = *reinterpret_cast<const uint32_t *>(a.vr + cr * 64 + off);
@@ -274,7 +277,7 @@ __global__ __launch_bounds__(256) void kv_attn_mfma_kernel(AttnArgs a) {
 #undef NL_VROW
       if (fdg == 0)
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) vsc[8 * fkg + kk] = f.sc[kk] * unit;
+        for (int kk = 0; kk < 8; ++kk) vsc[vkey(kk)] = f.sc[kk] * unit;
     }
     if (p0 + kChunk < pe) load(p0 + kChunk);   // in flight during this sub-chunk's products
     __syncthreads();
@@ -352,10 +355,7 @@ __global__ __launch_bounds__(256) void kv_attn_mfma_kernel(AttnArgs a) {
       for (int d = 0; d < 8; ++d)
   #pragma unroll
         for (int w = 0; w < 2; ++w) {
-          const _Float16 *vr = vt + (16 * d + lr) * kVP + 4 * (lg & 1);
-          const uint2 v0 = *reinterpret_cast<const uint2 *>(vr + 8 * ((4 * w + (lg >> 1)) ^ d));
-          const uint2 v1 = *reinterpret_cast<const uint2 *>(vr + 8 * ((4 * w + 2 + (lg >> 1)) ^ d));
-          const half8 va = __builtin_bit_cast(half8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+          const half8 va = *reinterpret_cast<const half8 *>(vt + (16 * d + lr) * kVP + 8 * ((4 * w + lg) ^ d));
           o[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, bh[w], o[d], 0, 0, 0);
           o[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, bl[w], o[d], 0, 0, 0);
         }
