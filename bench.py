@@ -52,6 +52,11 @@ W48_TS = (1, 16, 64)
 W48_KERNEL = "w48_kernel<true, 1>"   # verify, one 16-token tile
 W48_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w48_kernel_verify_T16_proj7b8b_traffic.txt")
 W48_SOURCES = ("nl_w4w8.hip",)
+KV_KERNEL = "kv_attn_mfma_kernel<true>"   # verify attention over KV8
+KV_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kv_attn_mfma_kernel_verify_T16_L32768_traffic.txt")
+KV_SOURCES = ("nl_kv.hip",)
+KV_TITLE = ("verify over KV8, 16-token tree, 32768 context positions, 32 query heads over 8 KV heads,\n"
+            "d = 128; algorithmic bytes: the K and V planes and scales read, 69239808 per launch")
 
 
 def log(*a):
@@ -373,6 +378,29 @@ def tree_leg(nl, torch, synth, reps, cpu_seconds=0.0):
     return out
 
 
+def kv_case(nl, torch, synth, rng, H_q, H_kv, L, T, verify):
+    """Synthetic KV planes and scales, queries and masks of one attention call;
+    returns (call, bytes of KV the call reads)."""
+    import numpy as np
+    P = L + T
+    rows = P * H_kv
+    kb = torch.from_numpy(rng.integers(0, 256, (rows, 64), dtype=np.uint8)).cuda()
+    kr = torch.from_numpy(rng.integers(0, 256, (rows, 64), dtype=np.uint8)).cuda()
+    vb = torch.from_numpy(rng.integers(0, 256, (rows, 64), dtype=np.uint8)).cuda()
+    vr = torch.from_numpy(rng.integers(0, 256, (rows, 64), dtype=np.uint8)).cuda()
+    ks = torch.from_numpy(rng.uniform(0.01, 0.05, rows).astype(np.float32)).cuda()
+    vs = torch.from_numpy(rng.uniform(0.01, 0.05, rows).astype(np.float32)).cuda()
+    q = torch.from_numpy(synth.make_x(T * H_q, 128, cfg=91, idx=T).view(np.int16)).cuda()
+    anc = torch.from_numpy(np.array([(1 << (t + 1)) - 1 for t in range(T)], np.uint64).view(np.int64)).cuda()
+    ws = torch.empty(nl.nested_kv_attention_workspace_bytes(T, H_q, H_kv, L), dtype=torch.uint8, device="cuda")
+    o = torch.empty((T, H_q, 128), dtype=torch.float32, device="cuda")
+
+    def call():
+        nl.nested_kv_attention(q, T, H_q, H_kv, L, kb, kr if verify else None, ks, vb,
+                               vr if verify else None, vs, anc, verify, o, ws, torch.cuda.current_stream())
+    return call, P * H_kv * 2 * ((128 if verify else 64) + 4)
+
+
 def kv_leg(nl, torch, synth, reps):
     """Nested KV attention of one Llama-8B-like layer (32 query heads, 8 KV
     heads, d = 128): verify (KV8) of a 16-token tree and a draft step (KV4,
@@ -381,36 +409,21 @@ def kv_leg(nl, torch, synth, reps):
     come from graph replays (host call overhead excluded)."""
     import numpy as np
     H_q, H_kv = 32, 8
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
     rng = np.random.default_rng(91)
     out = {"heads": [H_q, H_kv], "cases": {}}
     for L in (4096, 32768):
         for T, verify in ((16, True), (1, False)):
-            P = L + T
-            rows = P * H_kv
-            kb = torch.from_numpy(rng.integers(0, 256, (rows, 64), dtype=np.uint8)).cuda()
-            kr = torch.from_numpy(rng.integers(0, 256, (rows, 64), dtype=np.uint8)).cuda()
-            vb = torch.from_numpy(rng.integers(0, 256, (rows, 64), dtype=np.uint8)).cuda()
-            vr = torch.from_numpy(rng.integers(0, 256, (rows, 64), dtype=np.uint8)).cuda()
-            ks = torch.from_numpy(rng.uniform(0.01, 0.05, rows).astype(np.float32)).cuda()
-            vs = torch.from_numpy(rng.uniform(0.01, 0.05, rows).astype(np.float32)).cuda()
-            q = torch.from_numpy(synth.make_x(T * H_q, 128, cfg=91, idx=T).view(np.int16)).cuda()
-            anc = torch.from_numpy(np.array([(1 << (t + 1)) - 1 for t in range(T)], np.uint64).view(np.int64)).cuda()
-            ws = torch.empty(nl.nested_kv_attention_workspace_bytes(T, H_q, H_kv, L), dtype=torch.uint8,
-                             device="cuda")
-            o = torch.empty((T, H_q, 128), dtype=torch.float32, device="cuda")
-
-            def call():
-                nl.nested_kv_attention(q, T, H_q, H_kv, L, kb, kr if verify else None, ks, vb,
-                                       vr if verify else None, vs, anc, verify, o, ws, torch.cuda.current_stream())
+            call, b = kv_case(nl, torch, synth, rng, H_q, H_kv, L, T, verify)
             us = graph_us(torch, call, reps)
-            b = P * H_kv * 2 * ((128 if verify else 64) + 4)
             key = f"{'verify' if verify else 'draft'}_T{T}_L{L}"
             out["cases"][key] = {"us": round(us, 2), "kv_bytes": b, "GBps": round(b / us / 1e3, 1),
                                  "frac_hbm_peak": round(b / us / 1e3 / HBM_PEAK_GBPS, 4)}
             log(f"[bench] kv {key}: {us:.1f} us, {b / us / 1e3:.0f} GB/s of KV")
-            del kb, kr, vb, vr, ks, vs, ws
+            del call
+    tr = stored_traffic(kernel_source_digest(KV_SOURCES), KV_TRAFFIC_FILE)
+    # counter traffic of the verify attention launch at 32768 positions (the
+    # combine's partials are written here and read by the second launch)
+    out["cases"]["verify_T16_L32768"]["attention_launch_traffic_bytes"] = None if tr is None else round(tr)
     # the writer: K and V of 16 tokens x 8 KV heads
     n = 16 * H_kv
     x = torch.from_numpy(synth.make_x(n, 128, cfg=92).view(np.int16)).cuda()
@@ -674,7 +687,7 @@ def pmc_summary(fetch_dir, write_dir, out_path, kernel=ROOFLINE_KERNEL, prefix="
     fetch = sum(f_fwd) / len(f_fwd) * 1024 * kf
     write = sum(w_fwd) / len(w_fwd) * 1024 * kw
     summ = {"--roofline-only": "--pmc-summary", "--encoder-only": "--pmc-summary-encoder",
-            "--w4w8-only": "--pmc-summary-w4w8"}[flag]
+            "--w4w8-only": "--pmc-summary-w4w8", "--kv-traffic-only": "--pmc-summary-kv"}[flag]
     text = (f"HBM traffic of {display or kernel} ({title})\n"
             f"commands:\n"
             f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -o p -- python3 bench.py {flag}\n"
@@ -711,6 +724,10 @@ def main():
                     help="run only the encoder leg and the counter calibration copy (for rocprofv3)")
     ap.add_argument("--pmc-summary-encoder", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the encoder's traffic summary from two rocprofv3 --pmc runs of --encoder-only")
+    ap.add_argument("--kv-traffic-only", action="store_true",
+                    help="run only eager calls of the 32768-position verify attention, for the HBM counters")
+    ap.add_argument("--pmc-summary-kv", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise --kv-traffic-only FETCH_SIZE / WRITE_SIZE runs into the KV traffic file")
     ap.add_argument("--kv-only", action="store_true",
                     help="run only the nested-KV leg (writer and tree attention) and print its JSON")
     ap.add_argument("--w4w8-only", action="store_true",
@@ -728,6 +745,10 @@ def main():
     if args.pmc_summary_encoder:
         pmc_summary(*args.pmc_summary_encoder, ENC_TRAFFIC_FILE, kernel=ENC_KERNEL, prefix="", title=ENC_TITLE,
                     flag="--encoder-only", digest=kernel_source_digest(ENC_SOURCES), display=ENC_KERNEL_NAME)
+        return
+    if args.pmc_summary_kv:
+        pmc_summary(*args.pmc_summary_kv, KV_TRAFFIC_FILE, kernel=KV_KERNEL, prefix="", title=KV_TITLE,
+                    flag="--kv-traffic-only", digest=kernel_source_digest(KV_SOURCES))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -750,6 +771,14 @@ def main():
         w48 = w4w8_leg(nl, torch, synth, args.reps, args.pool_gib, roofline_only=True)
         calib = copy_calibration(torch)
         print(json.dumps({"w4w8": w48, "copy_calibration": calib}), flush=True)
+        return
+    if args.kv_traffic_only:
+        call, b = kv_case(nl, torch, synth, np.random.default_rng(91), 32, 8, 32768, 16, True)
+        for _ in range(20):
+            call()
+        torch.cuda.synchronize()
+        calib = copy_calibration(torch)
+        print(json.dumps({"kv_traffic_case": {"kv_bytes": b, "calls": 20}, "copy_calibration": calib}), flush=True)
         return
     if args.kv_only:
         print(json.dumps({"nested_kv": kv_leg(nl, torch, synth, args.reps)}), flush=True)
