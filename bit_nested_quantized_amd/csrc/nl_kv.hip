@@ -66,6 +66,7 @@ struct AttnArgs {
   float *part_ml;  // [chunks][H_kv][RQ][2]: running maximum (base-2 units), sum
   int T, H_q, H_kv, L, g, RQ;
   int span;        // key positions per workgroup (a multiple of 64)
+  int chunks;      // spans per KV head
 };
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -153,9 +154,15 @@ __global__ __launch_bounds__(256) void kv_attn_mfma_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 kt[kChunk * kKP];
   __shared__ __attribute__((aligned(16))) _Float16 vt[kD * kVP];
   __shared__ __attribute__((aligned(16))) float ksc[kChunk], vsc[kChunk];
-  const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  // The two KV heads of a pair share every 128-byte line of the cache (64
+  // bytes each), so their workgroups get linear ids 8 apart: the dispatcher
+  // deals ids round-robin over the 8 XCDs, which puts both on one XCD and
+  // its L2 then fetches each line once.  Ids past the last pair exit.
+  const int npair = (a.H_kv + 1) >> 1, bid = blockIdx.x, q = (bid >> 4) * 8 + (bid & 7);
+  const int c = q / npair, h = 2 * (q % npair) + ((bid >> 3) & 1), tid = threadIdx.x;
+  if (c >= a.chunks || h >= a.H_kv) return;   // whole workgroup, before any barrier
   const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-  const int r0 = 64 * blockIdx.z + 16 * (tid >> 6);   // this wave's first query row
+  const int r0 = 64 * blockIdx.y + 16 * (tid >> 6);   // this wave's first query row
   const bool live = r0 < a.RQ;                          // wave-uniform
   const int P = a.L + a.T;
   const int pb = c * a.span, pe = min(pb + a.span, P);
@@ -518,11 +525,13 @@ extern "C" nl_status nested_kv_attention(const void *q, int32_t T, int32_t H_q, 
   a.RQ = T * a.g;
   a.span = attn_span(L + T);
   const int chunks = attn_chunks(L + T);
+  a.chunks = chunks;
   const size_t o = (size_t)chunks * H_kv * a.RQ * kD * 4;
   a.part_o = static_cast<float *>(ws);
   a.part_ml = reinterpret_cast<float *>(static_cast<char *>(ws) + ((o + 255) & ~(size_t)255));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)chunks, (unsigned)H_kv, (unsigned)((a.RQ + 63) / 64));
+  const int pairs = chunks * ((H_kv + 1) / 2);   // (span, KV-head pair) tasks, 16 ids per 8
+  const dim3 grid((unsigned)((pairs + 7) / 8 * 16), (unsigned)((a.RQ + 63) / 64));
   if (verify)
     hipLaunchKernelGGL(kv_attn_mfma_kernel<true>, grid, dim3(256), 0, s, a);
   else
