@@ -71,6 +71,7 @@ struct AttnArgs {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
@@ -145,7 +146,12 @@ struct Fill {
 // the 8 reduction elements 8 lg .. 8 lg + 7 of a 32-wide step (any order
 // works as long as A and B agree: the P' V step uses keys 4 lg .. +3 and
 // 16 + 4 lg .. +3 of each 32-key window, where the S^T tiles left them).
-template <bool VERIFY>
+//
+// SPLIT (at most 16 query rows per KV head): the four waves share the 16 rows
+// and split each sub-chunk's keys, 16 per wave (4 score MFMAs, and the P' V
+// step as 16 v_mfma_f32_16x16x16_f16); at the span's end the four softmax
+// states merge in the freed K/V tiles.
+template <bool VERIFY, bool SPLIT>
 __global__ __launch_bounds__(256) void kv_attn_mfma_kernel(AttnArgs a) {
   constexpr int kKP = kD + 8;      // K: [key][dim] pitch (halves)
   constexpr int kVP = kChunk + 8;  // V: [dim][8-key block] pitch (halves); block b of
@@ -162,7 +168,8 @@ __global__ __launch_bounds__(256) void kv_attn_mfma_kernel(AttnArgs a) {
   const int c = q / npair, h = 2 * (q % npair) + ((bid >> 3) & 1), tid = threadIdx.x;
   if (c >= a.chunks || h >= a.H_kv) return;   // whole workgroup, before any barrier
   const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-  const int r0 = 64 * blockIdx.y + 16 * (tid >> 6);   // this wave's first query row
+  const int wave = tid >> 6;
+  const int r0 = SPLIT ? 0 : 64 * blockIdx.y + 16 * wave;   // this wave's first query row
   const bool live = r0 < a.RQ;                          // wave-uniform
   const int P = a.L + a.T;
   const int pb = c * a.span, pe = min(pb + a.span, P);
@@ -296,36 +303,40 @@ __global__ __launch_bounds__(256) void kv_attn_mfma_kernel(AttnArgs a) {
       const float vinv = vm > 0.0f ? 1.0f / vm : 0.0f;
       const float Rn = vm > 0.0f ? vm : R;
 
-      // lane holds S[row lr][key 16 t + 4 lg + i]
-      floatx4 sc[4];
-  #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        sc[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-  #pragma unroll
+      // lane holds S[row lr][key 16 t + 4 lg + i] for this wave's tiles t
+      constexpr int NT = SPLIT ? 1 : 4;
+      const int t0 = SPLIT ? wave : 0;
+      floatx4 sc[NT];
+#pragma unroll
+      for (int u = 0; u < NT; ++u) {
+        const int t = t0 + u;
+        floatx4 &sct = sc[u];
+        sct = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
         for (int st = 0; st < 4; ++st) {
           const half8 kb8 = *reinterpret_cast<const half8 *>(kt + (16 * t + lr) * kKP + 32 * st + 8 * lg);
-          sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb8, qa[st], sc[t], 0, 0, 0);
+          sct = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb8, qa[st], sct, 0, 0, 0);
         }
         const float4 k4 = reinterpret_cast<const float4 *>(ksc)[4 * t + lg];
-        sc[t][0] *= qinv * k4.x;
-        sc[t][1] *= qinv * k4.y;
-        sc[t][2] *= qinv * k4.z;
-        sc[t][3] *= qinv * k4.w;
+        sct[0] *= qinv * k4.x;
+        sct[1] *= qinv * k4.y;
+        sct[2] *= qinv * k4.z;
+        sct[3] *= qinv * k4.w;
       }
       if constexpr (decltype(masked)::value) {   // the sub-chunk reaches the tree or the span's end
-  #pragma unroll
-        for (int t = 0; t < 4; ++t)
-  #pragma unroll
+#pragma unroll
+        for (int u = 0; u < NT; ++u)
+#pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int key = 16 * t + 4 * lg + i, pos = p0 + key;
+            const int key = 16 * (t0 + u) + 4 * lg + i, pos = p0 + key;
             const uint32_t bit = (uint32_t)min(max(pos - a.L, 0), 63);
             const bool vis = (key < nk) & ((pos < a.L) | (((am >> bit) & 1ull) != 0));
-            sc[t][i] = vis ? sc[t][i] : -INFINITY;
+            sc[u][i] = vis ? sc[u][i] : -INFINITY;
           }
       }
       float mx = -INFINITY;
-  #pragma unroll
-      for (int t = 0; t < 4; ++t) mx = fmaxf(mx, fmaxf(fmaxf(sc[t][0], sc[t][1]), fmaxf(sc[t][2], sc[t][3])));
+#pragma unroll
+      for (int u = 0; u < NT; ++u) mx = fmaxf(mx, fmaxf(fmaxf(sc[u][0], sc[u][1]), fmaxf(sc[u][2], sc[u][3])));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float mn = fmaxf(m, mx);
@@ -334,18 +345,46 @@ __global__ __launch_bounds__(256) void kv_attn_mfma_kernel(AttnArgs a) {
       m = mn;
       l *= al;
       const float f_o = al * (R / Rn);
-  #pragma unroll
+#pragma unroll
       for (int d = 0; d < 8; ++d) o[d] *= f_o;
       R = Rn;
+      if constexpr (SPLIT) {
+        // P'^T operand of this wave's 16 keys (16 t0 + 4 lg + i); the V^T
+        // operand is half of the 8-key block that holds them
+        half4 bh, bl;
+        const float4 s4 = reinterpret_cast<const float4 *>(vsc)[4 * t0 + lg];
+        const float vsk[4] = {s4.x, s4.y, s4.z, s4.w};
+        float ps = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = __builtin_amdgcn_exp2f(sc[0][i] - msub);
+          ps += p;
+          const float x = p * (vsk[i] * vinv);
+          const _Float16 hi = (_Float16)x;
+          bh[i] = hi;
+          bl[i] = (_Float16)(x - (float)hi);   // x - hi is exact
+        }
+        ps += __shfl_xor(ps, 16);
+        ps += __shfl_xor(ps, 32);
+        l += ps;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+          const half4 va = *reinterpret_cast<const half4 *>(vt + (16 * d + lr) * kVP +
+                                                             8 * ((4 * (t0 >> 1) + lg) ^ d) + 4 * (t0 & 1));
+          o[d] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, bh, o[d], 0, 0, 0);
+          o[d] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, bl, o[d], 0, 0, 0);
+        }
+        return;
+      }
       // P'^T operands of the two 32-key windows: keys 32 w + 4 lg + i (tile 2w)
       // then 32 w + 16 + 4 lg + i (tile 2w + 1)
       half8 bh[2], bl[2];
       float ps = 0.0f;
-  #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
         const float4 s4 = reinterpret_cast<const float4 *>(vsc)[4 * t + lg];
         const float vsk[4] = {s4.x, s4.y, s4.z, s4.w};
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float p = __builtin_amdgcn_exp2f(sc[t][i] - msub);
           ps += p;
@@ -358,9 +397,9 @@ __global__ __launch_bounds__(256) void kv_attn_mfma_kernel(AttnArgs a) {
       ps += __shfl_xor(ps, 16);
       ps += __shfl_xor(ps, 32);
       l += ps;
-  #pragma unroll
+#pragma unroll
       for (int d = 0; d < 8; ++d)
-  #pragma unroll
+#pragma unroll
         for (int w = 0; w < 2; ++w) {
           const half8 va = *reinterpret_cast<const half8 *>(vt + (16 * d + lr) * kVP + 8 * ((4 * w + lg) ^ d));
           o[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, bh[w], o[d], 0, 0, 0);
@@ -371,6 +410,55 @@ __global__ __launch_bounds__(256) void kv_attn_mfma_kernel(AttnArgs a) {
       step(std::true_type{});
     else
       step(std::false_type{});   // context keys only: nothing to mask
+  }
+  if constexpr (SPLIT) {
+    // the four waves' states for the same 16 rows: O (times R) into the
+    // freed K/V tiles, (max, sum) into the scale arrays, then wave w merges
+    // dimension tiles 2w and 2w + 1
+    __syncthreads();
+    float *own = reinterpret_cast<float *>(wave < 2 ? static_cast<void *>(kt) : static_cast<void *>(vt)) +
+                 (wave & 1) * 16 * kD;
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+      *reinterpret_cast<float4 *>(own + lr * kD + 16 * d + 4 * lg) =
+          make_float4(o[d][0] * R, o[d][1] * R, o[d][2] * R, o[d][3] * R);
+    if (lg == 0) {
+      ksc[16 * wave + lr] = m;
+      vsc[16 * wave + lr] = l;
+    }
+    __syncthreads();
+    float M = -INFINITY, L = 0.0f, ew[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, ksc[16 * w + lr]);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = ksc[16 * w + lr];
+      ew[w] = mw == -INFINITY ? 0.0f : exp2f(mw - M);   // a wave that saw no visible key weighs 0
+      L += ew[w] * vsc[16 * w + lr];
+    }
+    if (!real) return;
+    const size_t base = ((size_t)c * a.H_kv + h) * a.RQ + qrow;
+#pragma unroll
+    for (int dd = 2 * wave; dd < 2 * wave + 2; ++dd) {
+      float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float *src = reinterpret_cast<const float *>(w < 2 ? static_cast<const void *>(kt)
+                                                                 : static_cast<const void *>(vt)) +
+                           (w & 1) * 16 * kD + lr * kD + 16 * dd + 4 * lg;
+        const float4 v = *reinterpret_cast<const float4 *>(src);
+        acc.x += ew[w] * v.x;
+        acc.y += ew[w] * v.y;
+        acc.z += ew[w] * v.z;
+        acc.w += ew[w] * v.w;
+      }
+      *reinterpret_cast<float4 *>(a.part_o + base * kD + 16 * dd + 4 * lg) = acc;
+    }
+    if (wave == 0 && lg == 0) {
+      a.part_ml[base * 2] = M;
+      a.part_ml[base * 2 + 1] = L;
+    }
+    return;
   }
   if (!live || !real) return;
   // partials: lane holds O[row qrow][dimension 16 d + 4 lg + i]
@@ -531,11 +619,17 @@ extern "C" nl_status nested_kv_attention(const void *q, int32_t T, int32_t H_q, 
   a.part_ml = reinterpret_cast<float *>(static_cast<char *>(ws) + ((o + 255) & ~(size_t)255));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int pairs = chunks * ((H_kv + 1) / 2);   // (span, KV-head pair) tasks, 16 ids per 8
-  const dim3 grid((unsigned)((pairs + 7) / 8 * 16), (unsigned)((a.RQ + 63) / 64));
-  if (verify)
-    hipLaunchKernelGGL(kv_attn_mfma_kernel<true>, grid, dim3(256), 0, s, a);
+  // up to 16 query rows per KV head: the four waves split the keys instead
+  const bool split = a.RQ <= 16;
+  const dim3 grid((unsigned)((pairs + 7) / 8 * 16), split ? 1u : (unsigned)((a.RQ + 63) / 64));
+  if (verify && split)
+    hipLaunchKernelGGL((kv_attn_mfma_kernel<true, true>), grid, dim3(256), 0, s, a);
+  else if (verify)
+    hipLaunchKernelGGL((kv_attn_mfma_kernel<true, false>), grid, dim3(256), 0, s, a);
+  else if (split)
+    hipLaunchKernelGGL((kv_attn_mfma_kernel<false, true>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(kv_attn_mfma_kernel<false>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((kv_attn_mfma_kernel<false, false>), grid, dim3(256), 0, s, a);
   if (nl_status st = launched(who)) return st;
   hipLaunchKernelGGL(kv_combine_kernel, dim3((unsigned)a.RQ, (unsigned)H_kv), dim3(256), 0, s, a, chunks, out);
   return launched(who);
