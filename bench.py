@@ -52,7 +52,7 @@ W48_TS = (1, 16, 64)
 W48_KERNEL = "w48_kernel<true, 1>"   # verify, one 16-token tile
 W48_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w48_kernel_verify_T16_proj7b8b_traffic.txt")
 W48_SOURCES = ("nl_w4w8.hip",)
-KV_KERNEL = "kv_attn_mfma_kernel<true>"   # verify attention over KV8
+KV_KERNEL = "kv_attn_mfma_kernel<true, false>"   # verify attention over KV8, query rows split over waves
 KV_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kv_attn_mfma_kernel_verify_T16_L32768_traffic.txt")
 KV_SOURCES = ("nl_kv.hip",)
 KV_TITLE = ("verify over KV8, 16-token tree, 32768 context positions, 32 query heads over 8 KV heads,\n"
