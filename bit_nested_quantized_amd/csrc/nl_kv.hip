@@ -5,7 +5,8 @@
 // 2l + 1 (one byte of each plane).  The row maximum is a wave reduction.
 //
 // kv_attn_mfma_kernel: one workgroup per (span of positions, KV head, block
-// of 64 query rows), at most 64 spans per head.  For each 64-position
+// of 64 query rows; with 16 or fewer rows the waves split keys instead), at
+// most 64 spans per head, in an XCD-aware order.  For each 64-position
 // sub-chunk it decodes the K and V rows into LDS as the exact integer codes
 // (16 q4 + q_r for KV8, q4 for KV4; the row scales are applied to the score
 // and to the softmax weight), and both products run on the matrix cores.
