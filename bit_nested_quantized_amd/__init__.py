@@ -29,7 +29,9 @@ EXPORTS = (
     "nested_linear_group_destroy", "nested_linear_group_workspace_bytes",
     "nested_linear_verify_grouped", "nested_linear_draft_grouped", "nested_linear_decode",
     "nested_linear_info", "nested_linear_timing_begin", "nested_linear_timing_end",
-    "nested_linear_last_error",
+    "nested_linear_last_error", "nested_linear_verify_multi", "nested_linear_draft_multi",
+    "nested_linear_multi_workspace_bytes", "nested_linear_workspace_status", "nested_linear_set_tuning",
+    "nested_linear_describe_call",
     "nested_encode_rotate", "nested_encode_quantize", "nested_encode_workspace_bytes", "nested_encode",
     "nested_encode_normalize", "nested_encode_fit_workspace_bytes", "nested_encode_fit_levels",
     "nested_w4w8_create", "nested_w4w8_destroy", "nested_w4w8_workspace_bytes", "nested_w4w8_verify",
@@ -96,6 +98,12 @@ def lib() -> ctypes.CDLL:
             "nested_linear_info": [P] + [ctypes.POINTER(i32)] * 5 + [ctypes.POINTER(ctypes.c_float)],
             "nested_linear_timing_begin": [i32],
             "nested_linear_timing_end": [ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(i32)],
+            "nested_linear_verify_multi": [P, i32, P, i32, P, P, sz, P],
+            "nested_linear_draft_multi": [P, i32, P, i32, P, P, sz, P],
+            "nested_linear_multi_workspace_bytes": [P, i32, i32, ctypes.POINTER(sz)],
+            "nested_linear_workspace_status": [P, ctypes.POINTER(ctypes.c_uint32), i32, P],
+            "nested_linear_set_tuning": [i32, ctypes.c_double],
+            "nested_linear_describe_call": [P, i32, i32, i32, i32, i32, ctypes.POINTER(i32), i32],
             "nested_encode_rotate": [i32, i32, P, P, P, P, P],
             "nested_encode_quantize": [P, ctypes.POINTER(nl_codes), P],
             "nested_encode_workspace_bytes": [i32, i32, i32, ctypes.POINTER(sz)],
@@ -131,6 +139,10 @@ def _check(st: int):
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def _stream(stream):
@@ -170,6 +182,57 @@ def nested_linear_verify(h, x, T: int, y, ws, stream=None):
 def nested_linear_draft(h, x, T: int, y, ws, stream=None):
     _check(lib().nested_linear_draft(h, _ptr(x), int(T), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
                                      _stream(stream)))
+
+
+def _handles(hs):
+    return (ctypes.c_void_p * len(hs))(*[h.value for h in hs])
+
+
+def nested_linear_verify_multi(hs, x, T: int, ys, ws, stream=None):
+    yp = (ctypes.c_void_p * len(ys))(*[y.data_ptr() for y in ys])
+    _check(lib().nested_linear_verify_multi(_handles(hs), len(hs), _ptr(x), int(T), yp, _ptr(ws), _nbytes(ws),
+                                            _stream(stream)))
+
+
+def nested_linear_draft_multi(hs, x, T: int, ys, ws, stream=None):
+    yp = (ctypes.c_void_p * len(ys))(*[y.data_ptr() for y in ys])
+    _check(lib().nested_linear_draft_multi(_handles(hs), len(hs), _ptr(x), int(T), yp, _ptr(ws), _nbytes(ws),
+                                           _stream(stream)))
+
+
+def nested_linear_multi_workspace_bytes(hs, T_max: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().nested_linear_multi_workspace_bytes(_handles(hs), len(hs), int(T_max), ctypes.byref(n)))
+    return n.value
+
+
+def nested_linear_workspace_status(ws, clear: bool = False, stream=None) -> int:
+    """Error word of a workspace (waits that gave up); synchronises."""
+    e = ctypes.c_uint32(0)
+    _check(lib().nested_linear_workspace_status(_ptr(ws), ctypes.byref(e), int(bool(clear)), _stream(stream)))
+    return int(e.value)
+
+
+def nested_linear_describe_call(d_outs, d_in: int, bits: int, two_sided: bool, T: int) -> dict:
+    """The launch plan of a call (host query; bits = 0 for the draft)."""
+    n = len(d_outs)
+    arr = (ctypes.c_int32 * n)(*[int(d) for d in d_outs])
+    buf = (ctypes.c_int32 * (8 + 6 * n))()
+    _check(lib().nested_linear_describe_call(arr, n, int(d_in), int(bits), int(bool(two_sided)), int(T), buf,
+                                             8 + 6 * n))
+    v = list(buf)
+    keys = ("local", "mt", "waves", "n_rot", "n_con", "n_fin", "lds", "blob")
+    d = dict(zip(keys, v[:8]))
+    d["jobs"] = [dict(zip(("S", "cps", "rt", "kw", "n_rb", "n_sb"), v[8 + 6 * i: 14 + 6 * i])) for i in range(n)]
+    return d
+
+
+NL_TUNE = {"splits": 1, "row_tiles": 2, "waves_per_tile": 3, "local_t": 4, "cus": 5, "lat_us": 6, "hbm_gbs": 7,
+           "split_us": 8, "xdma_gbs": 9, "spin_limit": 10, "wait_extra": 11, "waves": 12}
+
+
+def nested_linear_set_tuning(knob: str, value: float):
+    _check(lib().nested_linear_set_tuning(NL_TUNE[knob], float(value)))
 
 
 def nested_linear_prepare_input(h, x, T: int, ws, stream=None):
@@ -241,10 +304,6 @@ def nested_linear_info(h) -> dict:
 
 
 # --- encoder (include/nested_encode.h) ----------------------------------------
-
-def _nbytes(t):
-    return 0 if t is None else t.numel() * t.element_size()
-
 
 def nested_encode_rotate(d_out: int, d_in: int, w, sign_in, sign_out, wt, stream=None):
     _check(lib().nested_encode_rotate(int(d_out), int(d_in), _ptr(w), _ptr(sign_in), _ptr(sign_out),

@@ -15,6 +15,7 @@
 #include <vector>
 
 #include "../../include/nested_linear.h"
+#include "nl_fwd.h"
 #include "nl_kernels.h"
 
 using namespace nl;
@@ -159,7 +160,7 @@ static bool live(const void *p) {
   std::lock_guard<std::mutex> lk(g_live_mu);
   return g_live.count(p) != 0;
 }
-static bool valid(nl_handle h) { return h && live(h) && h->magic == kMagic; }
+static bool valid(const nl_linear *h) { return h && live(h) && h->magic == kMagic; }
 static bool valid(nl_group_handle g) { return g && live(g) && g->magic == kGroupMagic; }
 
 extern "C" const char *nested_linear_last_error(void) { return g_err.c_str(); }
@@ -209,7 +210,8 @@ extern "C" nl_status nested_linear_create(const nl_desc *d, nl_handle *out) {
   const size_t o_rsc = align256(o_bsc + tcs * kScaleBlockBytes);
   const size_t o_si = align256(o_rsc + (bits ? tcs * kScaleBlockBytes : 0));
   const size_t o_so = align256(o_si + d->d_in);
-  const size_t total = align256(o_so + (d->sign_out ? d->d_out : 0));
+  const size_t o_lut = align256(o_so + (d->sign_out ? d->d_out : 0));
+  const size_t total = align256(o_lut + 256 * sizeof(uint2));
   hipError_t e = hipMalloc(&h->mem, total);
   if (e != hipSuccess) {
     delete h;
@@ -227,6 +229,9 @@ extern "C" nl_status nested_linear_create(const nl_desc *d, nl_handle *out) {
   L.sign_in = (const int8_t *)(m + o_si);
   L.sign_out = d->sign_out ? (const int8_t *)(m + o_so) : nullptr;
   build_lut(d->levels, L.lut, &L.kinv, &h->level_err);
+  L.lut256 = (const uint2 *)(m + o_lut);
+  uint2 lut256[256];
+  for (int i = 0; i < 256; ++i) lut256[i] = make_uint2(L.lut[i & 15], L.lut[i >> 4]);
 
   RepackArgs ra;
   ra.base_codes = d->base_codes;
@@ -245,6 +250,7 @@ extern "C" nl_status nested_linear_create(const nl_desc *d, nl_handle *out) {
   e = launch_repack(ra, bits, nullptr);
   if (e == hipSuccess) e = hipMemcpy(m + o_si, si.data(), si.size(), hipMemcpyHostToDevice);
   if (e == hipSuccess && d->sign_out) e = hipMemcpy(m + o_so, so.data(), so.size(), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(m + o_lut, lut256, sizeof lut256, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     (void)hipFree(h->mem);
@@ -337,21 +343,6 @@ static Plan make_plan(int d_out, int n_tiles, int n_chunks, bool sign_out, int b
 }
 
 static int mt_for(int T) { return (T + 15) / 16; }
-
-extern "C" nl_status nested_linear_workspace_bytes(nl_handle h, int32_t T_max, size_t *bytes) {
-  if (!valid(h)) return fail(NL_EINVAL, "workspace_bytes: invalid handle");
-  if (!bytes) return fail(NL_EINVAL, "workspace_bytes: NULL bytes");
-  if (T_max < 1) return fail(NL_EINVAL, "workspace_bytes: T_max must be >= 1");
-  if (T_max > NL_MAX_T) return fail(NL_EUNSUPPORTED, "workspace_bytes: T_max > %d", NL_MAX_T);
-  size_t mx = 0;
-  for (int T = 1; T <= T_max; ++T) {
-    Plan p = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, h->b_out, T, mt_for(T), 1, T,
-                       tile_waves(mt_for(T)));
-    mx = p.total > mx ? p.total : mx;
-  }
-  *bytes = mx;
-  return ok();
-}
 
 static nl_status check_call(nl_handle h, const char *who, int verify, int32_t T, const void *ws,
                             size_t ws_bytes, Plan *plan) {
@@ -552,40 +543,371 @@ extern "C" nl_status nested_linear_timing_end(float *us, int32_t capacity, int32
   return ok();
 }
 
-static nl_status forward(nl_handle h, int verify, const void *x, int32_t T, float *y, void *ws,
-                         size_t ws_bytes, void *stream, const char *who) {
-  Plan p;
-  nl_status st = check_call(h, who, verify, T, ws, ws_bytes, &p);
-  if (st != NL_OK) return st;
-  if (!x || !y) return fail(NL_EINVAL, "%s: NULL x or y", who);
+// ---------------------------------------------------------------------------
+// Single-launch forward (nl_fwd.hip): plan and workspace of one call over n
+// linears that read the same x (n = 1 for nested_linear_verify / draft).
+// ---------------------------------------------------------------------------
+struct JobPlan {
+  int rt, kw, S, cps, n_rb, n_sb;
+  size_t o_xb, o_part, o_ysum;
+  int ctr_split, ctr_sb;
+};
+struct Plan2 {
+  int n, T, mt, nw, blob, tm, SB, OB;
+  bool local, two;
+  int n_rot, n_con, n_fin, n_ctr, rot_groups;
+  size_t lds, total;
+  JobPlan j[kMaxJobs];
+};
+
+// Tuning knobs (nested_linear_set_tuning): forced split count, row tiles and
+// waves per tile (0 = planner's choice), the largest T of the local form, and
+// the cost model's rates.
+static int g_t_S = 0, g_t_rt = 0, g_t_kw = 0, g_t_local = 2, g_t_cus = 256, g_t_nw = 0;
+static double g_t_lat_us = 2.0, g_t_hbm_gbs = 6500.0, g_t_split_us = 1.5, g_t_xdma_gbs = 100.0;
+static uint32_t g_spin_limit = 1u << 22;
+static uint32_t g_wait_extra = 0;
+
+// Bytes of one tile-chunk (16 rows x 512 columns) in a pass.
+static double tc_bytes(int bits) { return 16.0 * 512.0 * (0.265625 + (bits ? bits / 8.0 + 1.0 / 64.0 : 0.0)); }
+
+// Local form: transform passes a split [c_lo, c_hi) needs (at most 2).
+static int local_passes(int T, int n_chunks, int cps, int SB, int G) {
+  int np = 0;
+  for (int c_lo = 0; c_lo < n_chunks; c_lo += cps) {
+    const int c_hi = std::min(n_chunks, c_lo + cps);
+    const int sb0 = (c_lo * kChunk) / SB, sb1 = (c_hi * kChunk + SB - 1) / SB;
+    const int per = G * (4096 / SB);
+    np = std::max(np, (T * (sb1 - sb0) + per - 1) / per);
+  }
+  return np;
+}
+
+// Split count, row tiles per workgroup and waves per tile of one linear, by a
+// small cost model (microseconds).  A wave streams its chunks through a ring
+// of ns register sets, so it spends about one memory round trip (lat) per ns
+// chunks, or its compute if that is longer (the waves of a SIMD share it);
+// the call takes about the larger of the slowest wave of each round of
+// workgroups and the HBM time of all bytes, plus the split-K reduction and
+// the x' copies into LDS.  Ties go to more active waves, then fewer splits.
+static void choose_job(int n_tiles, int n_chunks, int T, int bits, int mt, int nw, int ns, bool two, bool local,
+                       int SB, int blob, int lds_fixed, double cus, JobPlan &jp) {
+  const int G = nw / 4;
+  const int budget = 160 * 1024 - lds_fixed;
+  const int kc_max = std::max(1, budget / blob);
+  const double tcb = tc_bytes(bits);
+  const double t_c = (bits ? 0.35 : 0.15) * (1.0 + 0.6 * (mt - 1));  // us per chunk, one wave on its SIMD
+  const double total = (double)n_tiles * n_chunks * tcb;
+  double best = 1e30;
+  jp.S = jp.cps = jp.rt = jp.kw = 0;
+  for (int cps0 = n_chunks; cps0 >= 1; --cps0) {
+    const int S = (n_chunks + cps0 - 1) / cps0, cps = (n_chunks + S - 1) / S;
+    if (cps != cps0) continue;  // each split count once
+    if (cps > kc_max) continue;
+    if (g_t_S > 0 && S != g_t_S) continue;
+    if (local && local_passes(T, n_chunks, cps, SB, G) > 2) continue;
+    for (int rt = 1; rt <= nw; ++rt) {
+      if (two && (rt & (rt - 1))) continue;  // row blocks inside one output superblock
+      if (g_t_rt > 0 && rt != g_t_rt) continue;
+      for (int kw = 1; rt * kw <= nw && kw <= cps; ++kw) {
+        if (g_t_kw > 0 && kw != g_t_kw) continue;
+        const int n_rb = (n_tiles + rt - 1) / rt, n_wg = n_rb * S;
+        const int rounds = (int)std::ceil(n_wg / cus);
+        const int wc = (cps + kw - 1) / kw;               // chunks of the busiest wave
+        const int active = rt * ((cps + wc - 1) / wc);    // waves that have chunks
+        const double share = std::max(1.0, active / 4.0);  // waves per SIMD
+        const double t_wave = wc * std::max(g_t_lat_us / std::min(ns, wc), t_c * share) + g_t_lat_us;
+        const double xdma = local ? 0.0 : cps * (double)blob / (g_t_xdma_gbs * 1e3);
+        const double split = S > 1 ? g_t_split_us + 2.0 * S * T * n_tiles * 16.0 * 4.0 / (g_t_hbm_gbs * 1e3) : 0.0;
+        // the slowest wave chain and the HBM time overlap but not completely:
+        // a smooth maximum (4-norm) keeps both in view
+        const double a = rounds * (t_wave + xdma), b = total / (g_t_hbm_gbs * 1e3);
+        const double cost = std::pow(std::pow(a, 4.0) + std::pow(b, 4.0), 0.25) + split + 1e-3 * (nw - active) + 1e-4 * S;
+        if (cost < best) {
+          best = cost;
+          jp.S = S;
+          jp.cps = cps;
+          jp.rt = rt;
+          jp.kw = kw;
+        }
+      }
+    }
+  }
+  if (jp.S == 0) {  // forced knobs that fit nothing: the plainest plan that fits
+    jp.cps = std::min(kc_max, n_chunks);
+    jp.S = (n_chunks + jp.cps - 1) / jp.cps;
+    jp.cps = (n_chunks + jp.S - 1) / jp.S;
+    jp.rt = 1;
+    jp.kw = std::min(nw, jp.cps);
+  }
+  jp.n_rb = (n_tiles + jp.rt - 1) / jp.rt;
+}
+
+// The shape facts a plan depends on.
+struct CallShape {
+  int d_out, n_tiles, n_chunks, b_in, b_out;
+  bool sign_out;
+};
+static CallShape shape_of(const nl_linear *h) {
+  return CallShape{h->d_out, h->n_tiles, h->n_chunks, h->b_in, h->b_out, h->has_sign_out};
+}
+
+static Plan2 make_plan2(const CallShape *hs, int n, int T, int bits) {
+  Plan2 p;
+  memset(&p, 0, sizeof p);
+  p.n = n;
+  p.T = T;
+  p.mt = mt_for(T);
+  // one token tile: eight waves with a four-set ring for the draft (its sets
+  // are small), twelve for verify; the knob forces either
+  p.nw = p.mt != 1 ? fwd_waves(p.mt) : (g_t_nw == 8 || (g_t_nw == 0 && bits == 0)) ? 8 : 12;
+  p.blob = blob_bytes(T);
+  p.tm = blob_tm(T);
+  const CallShape *h0 = &hs[0];
+  p.SB = std::max(h0->b_in, kChunk);
+  p.two = h0->sign_out;
+  p.OB = p.two ? std::max(h0->b_out, kChunk) : 0;
+  const int G = p.nw / 4;
+  const int n_chunks = h0->n_chunks;
+  const int n_sbi = (n_chunks * kChunk) / p.SB;
+  p.local = !p.two && p.mt == 1 && T <= g_t_local;
+  if (p.local) {  // every linear's K must fit two transform passes at some split count
+    for (int c = n_chunks; c >= 1; --c)
+      if (local_passes(T, n_chunks, c, p.SB, G) <= 2) {
+        if ((c * p.blob) > 160 * 1024 - kLdsX - G * kFwhtArea) p.local = false;
+        break;
+      }
+  }
+  const int lds_fixed = kLdsX + (p.local ? G * kFwhtArea + 16 : 0);
+  // rotation: one 256-thread transform group per workgroup while that takes
+  // at most 32 workgroups, more groups per workgroup beyond
+  const int task_groups = (n * T * n_sbi + (4096 / p.SB) - 1) / (4096 / p.SB);
+  p.rot_groups = std::min(G, std::max(1, (task_groups + 31) / 32));
+  p.n_rot = p.local ? 0 : (task_groups + p.rot_groups - 1) / p.rot_groups;
+  // the rotation workgroups hold their CUs until the hand-over
+  const double cus_free = std::max(32.0, (double)g_t_cus - p.n_rot);
+  double total_tc = 0;
+  for (int i = 0; i < n; ++i) total_tc += (double)hs[i].n_tiles;
+  size_t off = kCtrBytes;
+  int ctr = kCtrFixed, con = 0, fin_tasks = 0;
+  int lds_blob = 0;
+  for (int i = 0; i < n; ++i) {
+    const CallShape *h = &hs[i];
+    JobPlan &jp = p.j[i];
+    const double cus = std::max(1.0, cus_free * h->n_tiles / total_tc);
+    choose_job(h->n_tiles, n_chunks, T, bits, p.mt, p.nw, fwd_ring_sets(bits, p.mt, p.local, p.nw), p.two, p.local, p.SB,
+               p.blob, lds_fixed, cus, jp);
+    jp.n_sb = p.two ? (h->d_out + p.OB - 1) / p.OB : 0;
+    jp.o_xb = off;
+    off = align256(off + (size_t)n_chunks * p.blob);
+    jp.o_part = off;
+    if (jp.S > 1) off = align256(off + (size_t)jp.S * T * h->d_out * 4);
+    jp.o_ysum = off;
+    if (p.two) off = align256(off + (size_t)T * h->d_out * 4);
+    jp.ctr_split = ctr;
+    if (jp.S > 1) ctr += jp.n_rb;
+    jp.ctr_sb = ctr;
+    if (p.two) ctr += 2 * jp.n_sb;
+    con += jp.n_rb * jp.S;
+    fin_tasks += T * jp.n_sb;
+    lds_blob = std::max(lds_blob, jp.cps * p.blob);
+  }
+  p.n_ctr = ctr;
+  p.n_con = con;
+  p.n_fin = p.two ? (fin_tasks + G * (4096 / p.OB) - 1) / (G * (4096 / p.OB)) : 0;
+  size_t lds = kLdsX + (size_t)std::max(p.nw * p.mt * 1024, ((lds_blob + 15) & ~15) + (p.local ? G * kFwhtArea : 0));
+  if (p.n_rot || p.n_fin) lds = std::max(lds, (size_t)kLdsX + G * kFwhtArea);
+  p.lds = lds;
+  p.total = off;
+  return p;
+}
+
+static nl_status forward_n(const nl_linear *const *hs, int n, int verify, const void *x, int32_t T, float *const *ys,
+                           void *ws, size_t ws_bytes, void *stream, const char *who) {
+  if (n < 1 || n > kMaxJobs) return fail(NL_EINVAL, "%s: between 1 and %d linears per call (got %d)", who, kMaxJobs, n);
+  for (int i = 0; i < n; ++i) {
+    if (!valid(hs[i])) return fail(NL_EINVAL, "%s: linear %d is not a valid handle", who, i);
+    if (verify && !hs[i]->bits) return fail(NL_EINVAL, "%s: linear %d has no residual (draft only)", who, i);
+    if (hs[i]->d_in != hs[0]->d_in) return fail(NL_EINVAL, "%s: linear %d differs in d_in", who, i);
+    if (verify && hs[i]->bits != hs[0]->bits)
+      return fail(NL_EINVAL, "%s: linear %d differs in residual bits", who, i);
+    if (hs[i]->has_sign_out != hs[0]->has_sign_out || (hs[0]->has_sign_out && hs[i]->b_out != hs[0]->b_out))
+      return fail(NL_EINVAL, "%s: linear %d differs in the output rotation (presence or block)", who, i);
+    if (!ys || !ys[i]) return fail(NL_EINVAL, "%s: NULL y", who);
+  }
+  if (T < 1) return fail(NL_EINVAL, "%s: T must be >= 1 (got %d)", who, T);
+  if (T > NL_MAX_T) return fail(NL_EUNSUPPORTED, "%s: T = %d exceeds %d", who, T, NL_MAX_T);
+  if (!x) return fail(NL_EINVAL, "%s: NULL x", who);
   if ((uintptr_t)x & 15) return fail(NL_EINVAL, "%s: x must be 16-byte aligned", who);
+  if (!ws) return fail(NL_EINVAL, "%s: NULL workspace", who);
+  if ((uintptr_t)ws & 255) return fail(NL_EINVAL, "%s: workspace must be 256-byte aligned", who);
+  const int bits = verify ? hs[0]->bits : 0;
+  CallShape cs[kMaxJobs];
+  for (int i = 0; i < n; ++i) cs[i] = shape_of(hs[i]);
+  Plan2 p = make_plan2(cs, n, T, bits);
+  if (ws_bytes < p.total) return fail(NL_EINVAL, "%s: workspace too small (%zu < %zu)", who, ws_bytes, p.total);
+  if (p.n_ctr > kCtrLines) return fail(NL_EUNSUPPORTED, "%s: the call needs %d counters (> %d)", who, p.n_ctr, kCtrLines);
+  if (p.total > 0x7FFFFFF0u) return fail(NL_EUNSUPPORTED, "%s: workspace layout beyond 2 GiB", who);
   char *w = (char *)ws;
-  FwdArgs f;
-  memset(&f, 0, sizeof f);
-  f.rot = rot_args(h, x, T, w, p);
-  GemmArgs &g = f.g;
-  g.lin = h->dev;
-  g.xh = (const uint16_t *)(w + p.o_xh);
-  g.meta = (const float *)(w + p.o_meta);
-  g.T = T;
-  g.d_out = h->d_out;
-  g.n_tiles = h->n_tiles;
-  g.n_chunks = h->n_chunks;
-  g.Kp = h->n_chunks * kChunk;
-  g.Gp = h->n_chunks * 4;
-  g.cps = p.cps;
-  g.ldo = h->d_out;
-  g.n_rb = p.n_rb;
-  g.n_experts = 1;
-  f.fin.sign_out = h->dev.sign_out;
-  f.fin.b = h->b_out;
-  f.fin.lb = log2i(h->b_out);
-  f.fin.rsqrt_b = (float)(1.0 / std::sqrt((double)h->b_out));
-  fill_launch(f, p, 1, w, y, h->d_out);
-  const int n_fin = p.mode == kOutTwoSided ? finish_workgroups(T, h->d_out, p.sb_rows) : 0;
+  FwdArgs2 a;
+  memset(&a, 0, sizeof a);
+  a.x = (const uint16_t *)x;
+  a.ws = w;
+  a.T = T;
+  a.d_in = hs[0]->d_in;
+  a.n_chunks = hs[0]->n_chunks;
+  a.Kp = hs[0]->n_chunks * kChunk;
+  a.lb_in = log2i(hs[0]->b_in);
+  a.SB = p.SB;
+  a.rsqrt_in = (float)(1.0 / std::sqrt((double)hs[0]->b_in));
+  a.lb_out = p.two ? log2i(hs[0]->b_out) : 0;
+  a.OB = p.OB;
+  a.rsqrt_out = p.two ? (float)(1.0 / std::sqrt((double)hs[0]->b_out)) : 0.f;
+  a.blob = p.blob;
+  a.tm = p.tm;
+  a.n_jobs = n;
+  a.n_rot = p.n_rot;
+  a.n_con = p.n_con;
+  a.n_fin = p.n_fin;
+  a.rot_groups = p.rot_groups;
+  a.spin_limit = g_spin_limit;
+  a.wait_extra = g_wait_extra;
+  int con = 0;
+  for (int i = 0; i < n; ++i) {
+    const JobPlan &jp = p.j[i];
+    FwdJob &J = a.job[i];
+    J.lin = hs[i]->dev;
+    J.y = ys[i];
+    J.part = (float *)(w + jp.o_part);
+    J.ysum = p.two ? (float *)(w + jp.o_ysum) : nullptr;
+    J.xb = (int)jp.o_xb;
+    J.d_out = hs[i]->d_out;
+    J.n_tiles = hs[i]->n_tiles;
+    J.rt = jp.rt;
+    J.kw = jp.kw;
+    J.n_rb = jp.n_rb;
+    J.S = jp.S;
+    J.cps = jp.cps;
+    J.con0 = con;
+    J.ctr_split = jp.ctr_split;
+    J.ctr_sb = jp.ctr_sb;
+    J.n_sb = jp.n_sb;
+    con += jp.n_rb * jp.S;
+  }
   hipEvent_t e0, e1;
   timing_slot((hipStream_t)stream, &e0, &e1);
-  HIP_OR_FAIL(launch_forward(f, verify ? h->bits : 0, p.mt, p.tw, n_fin, (hipStream_t)stream, e0, e1));
+  HIP_OR_FAIL(launch_forward2(a, bits, p.mt, p.nw, p.local, p.lds, (hipStream_t)stream, e0, e1));
+  return ok();
+}
+
+static nl_status forward(nl_handle h, int verify, const void *x, int32_t T, float *y, void *ws,
+                         size_t ws_bytes, void *stream, const char *who) {
+  if (!valid(h)) return fail(NL_EINVAL, "%s: invalid handle", who);
+  const nl_linear *hs[1] = {h};
+  float *ys[1] = {y};
+  return forward_n(hs, 1, verify, x, T, ys, ws, ws_bytes, stream, who);
+}
+
+extern "C" nl_status nested_linear_describe_call(const int32_t *d_out, int32_t n, int32_t d_in, int32_t bits,
+                                                 int32_t two_sided, int32_t T, int32_t *out, int32_t out_len) {
+  if (!d_out || !out || n < 1 || n > kMaxJobs || T < 1 || T > NL_MAX_T || d_in < NL_GROUP || d_in % NL_GROUP ||
+      (bits != 0 && bits != 6 && bits != 7 && bits != 8))
+    return fail(NL_EINVAL, "describe_call: bad arguments");
+  CallShape cs[kMaxJobs];
+  for (int i = 0; i < n; ++i) {
+    if (d_out[i] < 1) return fail(NL_EINVAL, "describe_call: d_out[%d] < 1", i);
+    cs[i] = CallShape{d_out[i], (d_out[i] + kTileRows - 1) / kTileRows, (d_in + kChunk - 1) / kChunk, block_size(d_in),
+                      block_size(d_out[i]), two_sided != 0};
+  }
+  const Plan2 p = make_plan2(cs, n, T, bits);
+  int32_t v[8 + 6 * kMaxJobs] = {p.local, p.mt, p.nw, p.n_rot, p.n_con, p.n_fin, (int32_t)p.lds, p.blob};
+  for (int i = 0; i < n; ++i) {
+    const JobPlan &jp = p.j[i];
+    const int32_t jv[6] = {jp.S, jp.cps, jp.rt, jp.kw, jp.n_rb, jp.n_sb};
+    memcpy(v + 8 + 6 * i, jv, sizeof jv);
+  }
+  memcpy(out, v, sizeof(int32_t) * std::min<int>(out_len, 8 + 6 * n));
+  return ok();
+}
+
+extern "C" nl_status nested_linear_verify_multi(const nl_handle *hs, int32_t n, const void *x, int32_t T,
+                                                float *const *ys, void *ws, size_t ws_bytes, void *stream) {
+  if (!hs) return fail(NL_EINVAL, "verify_multi: NULL handles");
+  return forward_n((const nl_linear *const *)hs, n, 1, x, T, ys, ws, ws_bytes, stream, "verify_multi");
+}
+
+extern "C" nl_status nested_linear_draft_multi(const nl_handle *hs, int32_t n, const void *x, int32_t T,
+                                               float *const *ys, void *ws, size_t ws_bytes, void *stream) {
+  if (!hs) return fail(NL_EINVAL, "draft_multi: NULL handles");
+  return forward_n((const nl_linear *const *)hs, n, 0, x, T, ys, ws, ws_bytes, stream, "draft_multi");
+}
+
+extern "C" nl_status nested_linear_multi_workspace_bytes(const nl_handle *hs, int32_t n, int32_t T_max,
+                                                         size_t *bytes) {
+  if (!hs || !bytes || n < 1 || n > kMaxJobs) return fail(NL_EINVAL, "multi_workspace_bytes: bad arguments");
+  if (T_max < 1) return fail(NL_EINVAL, "multi_workspace_bytes: T_max must be >= 1");
+  if (T_max > NL_MAX_T) return fail(NL_EUNSUPPORTED, "multi_workspace_bytes: T_max > %d", NL_MAX_T);
+  for (int i = 0; i < n; ++i) {
+    if (!valid(hs[i])) return fail(NL_EINVAL, "multi_workspace_bytes: linear %d is not a valid handle", i);
+    if (hs[i]->d_in != hs[0]->d_in) return fail(NL_EINVAL, "multi_workspace_bytes: linear %d differs in d_in", i);
+  }
+  size_t mx = 0;
+  CallShape cs[kMaxJobs];
+  for (int i = 0; i < n; ++i) cs[i] = shape_of(hs[i]);
+  for (int T = 1; T <= T_max; ++T)
+    for (int b = 0; b < 2; ++b) mx = std::max(mx, make_plan2(cs, n, T, b ? hs[0]->bits : 0).total);
+  *bytes = mx;
+  return ok();
+}
+
+extern "C" nl_status nested_linear_workspace_bytes(nl_handle h, int32_t T_max, size_t *bytes) {
+  if (!valid(h)) return fail(NL_EINVAL, "workspace_bytes: invalid handle");
+  if (!bytes) return fail(NL_EINVAL, "workspace_bytes: NULL bytes");
+  if (T_max < 1) return fail(NL_EINVAL, "workspace_bytes: T_max must be >= 1");
+  if (T_max > NL_MAX_T) return fail(NL_EUNSUPPORTED, "workspace_bytes: T_max > %d", NL_MAX_T);
+  size_t mx = 0;
+  const CallShape hs[1] = {shape_of(h)};
+  for (int T = 1; T <= T_max; ++T) {
+    // the staged calls' layout and the single launch's, draft and verify
+    Plan p = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, h->b_out, T, mt_for(T), 1, T,
+                       tile_waves(mt_for(T)));
+    mx = std::max(mx, p.total);
+    mx = std::max(mx, make_plan2(hs, 1, T, 0).total);
+    if (h->bits) mx = std::max(mx, make_plan2(hs, 1, T, h->bits).total);
+  }
+  *bytes = mx;
+  return ok();
+}
+
+extern "C" nl_status nested_linear_set_tuning(int32_t knob, double value) {
+  switch (knob) {
+    case NL_TUNE_SPLITS: g_t_S = (int)value; break;
+    case NL_TUNE_ROW_TILES: g_t_rt = (int)value; break;
+    case NL_TUNE_WAVES_PER_TILE: g_t_kw = (int)value; break;
+    case NL_TUNE_LOCAL_T: g_t_local = (int)value; break;
+    case NL_TUNE_CUS: g_t_cus = value >= 1 ? (int)value : 256; break;
+    case NL_TUNE_LAT_US: g_t_lat_us = value > 0 ? value : 2.0; break;
+    case NL_TUNE_HBM_GBS: g_t_hbm_gbs = value > 0 ? value : 6500.0; break;
+    case NL_TUNE_SPLIT_US: g_t_split_us = value >= 0 ? value : 1.5; break;
+    case NL_TUNE_XDMA_GBS: g_t_xdma_gbs = value > 0 ? value : 100.0; break;
+    case NL_TUNE_SPIN_LIMIT: g_spin_limit = value >= 1 ? (uint32_t)value : (1u << 22); break;
+    case NL_TUNE_WAIT_EXTRA: g_wait_extra = value >= 0 ? (uint32_t)value : 0u; break;
+    case NL_TUNE_WAVES: g_t_nw = ((int)value == 8 || (int)value == 12) ? (int)value : 0; break;
+    default: return fail(NL_EINVAL, "set_tuning: unknown knob %d", knob);
+  }
+  return ok();
+}
+
+extern "C" nl_status nested_linear_workspace_status(void *ws, uint32_t *errors, int32_t clear, void *stream) {
+  if (!ws || !errors) return fail(NL_EINVAL, "workspace_status: NULL workspace or errors");
+  if ((uintptr_t)ws & 255) return fail(NL_EINVAL, "workspace_status: workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  HIP_OR_FAIL(hipStreamSynchronize(s));
+  HIP_OR_FAIL(hipMemcpy(errors, ws, sizeof(uint32_t), hipMemcpyDeviceToHost));
+  if (clear) {
+    HIP_OR_FAIL(hipMemsetAsync(ws, 0, kCtrBytes, s));
+    HIP_OR_FAIL(hipStreamSynchronize(s));
+  }
   return ok();
 }
 

@@ -1,0 +1,269 @@
+// nl_dev.h -- device helpers shared by the gfx950 kernels of the nested linear:
+// MFMA operand types, the workgroup Walsh-Hadamard transforms (POC recipe
+// section 1 of the forum post "bit-nested"), activation loads, the
+// agent-coherent hand-over primitives and the weight register sets.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nl_kernels.h"
+
+#define NL_GLOBAL __attribute__((address_space(1)))
+#define NL_LOCAL __attribute__((address_space(3)))
+#define NL_CONST __attribute__((address_space(4)))
+
+namespace nl {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ half8 as_half8(const uint32_t *p) {
+  u32x4 v = {p[0], p[1], p[2], p[3]};
+  return __builtin_bit_cast(half8, v);
+}
+
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+__device__ __forceinline__ float bf16_to_float(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+
+// Workgroup barrier for hand-offs through LDS only: waits for this wave's LDS
+// operations, not for its outstanding global loads (the release fence of
+// __syncthreads would wait for every one of them, stalling the weight stream).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ===========================================================================
+// Workgroup Walsh-Hadamard transforms (POC section 1: Sylvester H, applied
+// block-diagonally).  A workgroup of 256 threads transforms 4096 values:
+// 4096/SB independent "tasks" of SB = 2^n values (n in 9..12), TPS = SB/16
+// threads per task, 16 values per thread.  Butterflies run unnormalised over
+// the low `lb` bits of the element index i (block 2^lb).  The 16 values of a
+// thread pass through three layouts (the stages commute, so their order is
+// free):
+//   B  i = 16*lt + j           low 4 bits in registers; contiguous values
+//                              (16-byte loads of x, 16-byte stores of x')
+//   C  i = (lt&15) + 16*j + 256*(lt>>4)   bits 4..7 in registers
+//   A  i = TPS*j + lt          top 4 bits in registers
+// with padded LDS transposes B->C->A->B in between.
+// ===========================================================================
+__device__ __forceinline__ int lds_pad(int i) { return i + (i >> 4); }
+
+__device__ __forceinline__ void bfly16(float (&v)[16], int bit) {
+  const int h = 1 << bit;
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (!(j & h)) {
+      const float x0 = v[j], x1 = v[j | h];
+      v[j] = x0 + x1;
+      v[j | h] = x0 - x1;
+    }
+}
+
+// v: layout B on entry and on exit (thread lt of the task holds points
+// 16*lt + j).  The transform is a butterfly on every index bit below LB;
+// four bits are done in registers at a time, with LDS transposes
+//   B (bits 0-3 in registers) -> C (bits 4-7) -> A (bits N-4..N-1, those
+//   from 8 up) -> B.
+// N = log2 of the task size SB, LB = log2 of the Hadamard block (LB <= N);
+// both compile-time, so every LDS address is a base plus an immediate.
+// xch: this task's LDS (SB + SB/16 floats).  idle: a thread (uniformly per
+// wave) that only keeps the barrier count.
+template <int N, int LB>
+__device__ __forceinline__ void fwht_bt(float (&v)[16], float *xch, int lt, bool idle) {
+  constexpr int TPS = 1 << (N - 4);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (q < LB) bfly16(v, q);
+  const int cbase = (lt & 15) + 256 * (lt >> 4);
+  float *pb = xch + lds_pad(16 * lt);             // B: + j
+  float *pc = xch + lds_pad(cbase);               // C: + 17 j
+  float *pa = xch + lt + (lt >> 4);               // A: + (TPS + TPS / 16) j
+  lds_barrier();
+  if (!idle)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) pb[j] = v[j];
+  lds_barrier();
+  if (!idle)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = pc[17 * j];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (4 + q < LB) bfly16(v, q);
+  lds_barrier();
+  if (!idle)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) pc[17 * j] = v[j];
+  lds_barrier();
+  if (!idle)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = pa[(TPS + TPS / 16) * j];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    constexpr int base = N - 4;
+    if (base + q >= 8 && base + q < LB) bfly16(v, q);
+  }
+  lds_barrier();
+  if (!idle)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) pa[(TPS + TPS / 16) * j] = v[j];
+  lds_barrier();
+  if (!idle)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = pb[j];
+}
+
+// The transform for a task of SB = max(2^lb, 512) points (one uniform
+// dispatch on the block size; lb is 7..12 since d_in is a multiple of 128).
+__device__ __forceinline__ void fwht_b(float (&v)[16], float *xch, int lt, int lb, bool idle) {
+  switch (lb) {
+    case 7: fwht_bt<9, 7>(v, xch, lt, idle); break;
+    case 8: fwht_bt<9, 8>(v, xch, lt, idle); break;
+    case 9: fwht_bt<9, 9>(v, xch, lt, idle); break;
+    case 10: fwht_bt<10, 10>(v, xch, lt, idle); break;
+    case 11: fwht_bt<11, 11>(v, xch, lt, idle); break;
+    default: fwht_bt<12, 12>(v, xch, lt, idle); break;
+  }
+}
+
+// v: layout A on entry, layout B on exit (the output rotation, whose input
+// loads are coalesced in layout A).
+__device__ __forceinline__ void fwht_tasks(float (&v)[16], float *xch, int lt, int TPS, int n, int lb) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (n - 4 + q < lb) bfly16(v, q);
+  lds_barrier();
+#pragma unroll
+  for (int j = 0; j < 16; ++j) xch[lds_pad(TPS * j + lt)] = v[j];
+  lds_barrier();
+  const int cbase = (lt & 15) + 256 * (lt >> 4);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = xch[lds_pad(cbase + 16 * j)];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (4 + q < n - 4 && 4 + q < lb) bfly16(v, q);
+  lds_barrier();
+#pragma unroll
+  for (int j = 0; j < 16; ++j) xch[lds_pad(cbase + 16 * j)] = v[j];
+  lds_barrier();
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = xch[lds_pad(16 * lt + j)];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (q < lb) bfly16(v, q);
+}
+
+// 16 consecutive activations (columns k0 .. k0 + 15 of row xrow) and their
+// signs: two 16-byte loads of x, one of the signs.  Rows of x and the sign
+// vector are 16-byte aligned and d_in is a multiple of 128, so a group of 16
+// is wholly inside or wholly past d_in.  Outside (xrow < 0 or k0 >= d_in)
+// the loads read the first 16 columns and the values become zeros.
+struct XRaw {
+  u32x4 a, b, s;
+  bool in;
+};
+__device__ __forceinline__ XRaw load_x16(const uint16_t *x, const int8_t *sign, int xrow, int k0, int d_in) {
+  XRaw r;
+  r.in = xrow >= 0 && k0 < d_in;
+  const size_t off = r.in ? (size_t)xrow * d_in + k0 : 0;
+  // global address space: a generic (flat) load would also count in lgkmcnt,
+  // and waiting for it would wait for every load in flight
+  const NL_GLOBAL u32x4 *xp = (const NL_GLOBAL u32x4 *)(x + off);
+  const NL_GLOBAL u32x4 *sp = (const NL_GLOBAL u32x4 *)(sign + (r.in ? k0 : 0));
+  r.a = xp[0];
+  r.b = xp[1];
+  r.s = sp[0];
+  return r;
+}
+// x * sign in fp32 (exact: bf16 widens exactly, signs are +-1, i.e. bytes
+// 0x01 / 0xFF, so the sign byte's top bit flips the sign bit), zero outside;
+// bit operations only, no branches.
+__device__ __forceinline__ void cvt_x16(float (&v)[16], const XRaw &r) {
+  const uint32_t xw[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+  const uint32_t sw[4] = {r.s.x, r.s.y, r.s.z, r.s.w};
+  const uint32_t keep = r.in ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t hb = (j & 1) ? (xw[j >> 1] & 0xFFFF0000u) : (xw[j >> 1] << 16);
+    const uint32_t sbit = (sw[j >> 2] << (24 - 8 * (j & 3))) & 0x80000000u;
+    v[j] = __uint_as_float((hb ^ sbit) & keep);
+  }
+}
+
+// Column offset, inside its 128-column group, of run r (0..15) of the
+// contraction's activation layout: run = step * 4 + quarter holds the 8
+// columns 32 * quarter + 8 * step .. + 8 (the MFMA A operand of lanes with
+// l >> 4 == quarter at step `step`).
+__device__ __forceinline__ int run_col(int r) { return 32 * (r & 3) + 8 * (r >> 2); }
+
+// ===========================================================================
+// Hand-over between the workgroups of one launch.  Data written by one
+// workgroup and read by another (on any XCD) goes through agent-scope (sc1)
+// stores and loads, and a counter is bumped only after the writer's stores
+// are acknowledged (s_waitcnt vmcnt(0) in every thread, then a barrier), so
+// no L2 write-back or invalidate is needed.  Counters are 64-byte apart; the
+// launch leaves every counter at zero.
+// ===========================================================================
+constexpr int kSc1 = 16;  // cache policy of a buffer op: agent-coherent (sc1), as st_dev
+__device__ __forceinline__ void st_dev(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t *p) {
+  return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ctr_add(uint32_t *p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ uint32_t *ctr_at(uint32_t *c, int i) { return c + kCtrStride * i; }
+
+// Wait until at most n of this wave's vector-memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int BITS>
+struct WRegs {
+  u32x4 b[kBasePieces];
+  u32x4 r[BITS > 0 ? BITS : 1];
+  uint64_t sb, sr;  // the row's 4 group scales (fp16) of each plane
+};
+
+// An ordered no-op on every register of a set: work on the set cannot be
+// scheduled above it, so the wait for the set's loads lands here.
+template <int BITS>
+__device__ __forceinline__ void pin(WRegs<BITS> &w) {
+#pragma unroll
+  for (int i = 0; i < kBasePieces; ++i) asm volatile("" : "+v"(w.b[i]));
+  asm volatile("" : "+v"(w.sb));
+  if constexpr (BITS > 0) {
+#pragma unroll
+    for (int i = 0; i < BITS; ++i) asm volatile("" : "+v"(w.r[i]));
+    asm volatile("" : "+v"(w.sr));
+  }
+}
+
+// A wave-uniform pointer in an SGPR pair (the copies' scalar base operand).
+__device__ __forceinline__ const void *sgpr_ptr(const void *p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+}  // namespace nl

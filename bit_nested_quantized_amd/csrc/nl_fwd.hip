@@ -1,0 +1,768 @@
+// nl_fwd.hip -- single-launch forward of the bit-nested quantized linear on
+// gfx950 (see nl_fwd.h for the roles of the workgroups).
+//
+// The method is the verifier forward of the forum post "bit-nested", POC
+// recipe section 4: x' = H_i S_i x (section 1), y~ = (Q_base + Q_resid) x'
+// with the 2-bit Lloyd-Max base (section 2) and the uniform b-bit residual
+// (section 3), and optionally y = S_o H_o y~.  The draft reads only the base
+// planes (BitNest, section 3.3 "Dual-Plane Weight Storage").
+//
+// Contraction.  A wave owns one 16-row tile and a run of 512-column chunks.
+// Per 128-column group its 64 lanes hold the group's codes of the tile in the
+// MFMA B-operand layout (nl_layout.h); the base codes become kappa*L[c] fp16
+// through a byte-indexed LDS table, the residual fields u = q + 2^(b-1)
+// become the exact fp16 subnormals u * 2^-24, and v_mfma_f32_16x16x32_f16
+// contracts both against x' read from LDS (16 tokens per MFMA).  The group
+// scales are applied in fp32 to the two MFMA results, where the residual's
+// offset 2^(b-1) is removed with the group sums of x' (a small offset: the
+// cancellation costs a few bits of the fp32 sums, not the eleven a 1024 bias
+// would), and the chunk's activation scale at the end of the chunk.  Weight loads go through a ring of register sets, issued before
+// the workgroup waits for x', so the weight stream starts at once.
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include "nl_dev.h"
+#include "nl_fwd.h"
+#include "nl_kernels.h"
+
+namespace nl {
+
+// LDS byte offset of the base table entry for byte Q of a code dword (the
+// table sits at LDS offset 0, 8 bytes per entry): one shift of the selected
+// byte (SDWA).
+template <int Q>
+__device__ __forceinline__ uint32_t lut_off(uint32_t w) {
+  uint32_t r;
+  if constexpr (Q == 0)
+    asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(w));
+  else if constexpr (Q == 1)
+    asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(w));
+  else if constexpr (Q == 2)
+    asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(w));
+  else
+    asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(w));
+  return r;
+}
+
+// The lane's two code dwords of one group -> 16 fp16x2 base operands
+// (kappa * L[c], nl_layout.h), one table read per byte of codes.  The table
+// is the first thing in the kernel's LDS, which holds no static variables,
+// so a table offset is its LDS address.
+__device__ __forceinline__ uint2 lut_at(uint32_t off) {
+  const uint64_t v = *(const NL_LOCAL uint64_t *)(size_t)off;
+  return make_uint2((uint32_t)v, (uint32_t)(v >> 32));
+}
+__device__ __forceinline__ void unpack_base2(const uint32_t *b, uint32_t *out) {
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const uint2 e0 = lut_at(lut_off<0>(b[w]));
+    const uint2 e1 = lut_at(lut_off<1>(b[w]));
+    const uint2 e2 = lut_at(lut_off<2>(b[w]));
+    const uint2 e3 = lut_at(lut_off<3>(b[w]));
+    out[8 * w + 0] = e0.x;
+    out[8 * w + 1] = e0.y;
+    out[8 * w + 2] = e1.x;
+    out[8 * w + 3] = e1.y;
+    out[8 * w + 4] = e2.x;
+    out[8 * w + 5] = e2.y;
+    out[8 * w + 6] = e3.x;
+    out[8 * w + 7] = e3.y;
+  }
+}
+
+// Wait until a counter reaches n (uniform caller: one thread).  Producers have
+// lower workgroup indices and workgroups are dispatched in index order, so
+// they are running or done; the spin limit only bounds the wait should that
+// ever fail.  Returns false when the wait gave up (counted in the error word).
+__device__ bool wait_count(const uint32_t *c, uint32_t n, uint32_t limit, uint32_t *err) {
+  for (uint32_t it = 0; ld_dev(c) < n; ++it) {
+    if (it >= limit) {
+      ctr_add(err, 1u);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return true;
+}
+
+// Take one token of a semaphore (finish tasks).  Same conditions as above.
+__device__ bool take_one(uint32_t *sem, uint32_t extra, uint32_t limit, uint32_t *err) {
+  for (uint32_t it = 0; ld_dev(sem) < 1u + extra; ++it) {
+    if (it >= limit) {
+      ctr_add(err, 1u);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  __hip_atomic_fetch_sub(sem, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
+__device__ __forceinline__ const NL_CONST FwdJob &job_at(const FwdArgs2 &a, int j) {
+  return *(const NL_CONST FwdJob *)&a.job[j];
+}
+
+// Offset of run (g, s, q) of token t inside a blob, in bytes.
+__device__ __forceinline__ int blob_run(int g, int s, int q, int t, int T) { return (((g * 4 + s) * 4 + q) * T + t) * 16; }
+
+// One thread's 16 rotated activations (columns k0 .. k0 + 15 of one token):
+// sign, block transform, the chunk's power-of-two scale (32 threads share a
+// 512-column chunk) and fp16 rounding.  xch: the task's transform area.
+struct XOut {
+  uint32_t w[8];
+  float gs;  // sum of the fp16 values of the thread's 128-column group (8 threads)
+  int e;     // scale exponent: the chunk was multiplied by 2^e
+};
+// A wave none of whose lanes has a task (wave-uniform) only keeps the
+// transform's barrier count and returns zeros.
+__device__ __forceinline__ XOut rotate16(const XRaw &xr, float *xch, int lt, int lb, bool has_task) {
+  XOut o;
+  if (!__any(has_task)) {
+#pragma unroll
+    for (int k = 0; k < 6; ++k) lds_barrier();  // the barriers of fwht_bt
+#pragma unroll
+    for (int h = 0; h < 8; ++h) o.w[h] = 0u;
+    o.gs = 0.f;
+    o.e = 0;
+    return o;
+  }
+  float v[16];
+  cvt_x16(v, xr);
+  fwht_b(v, xch, lt, lb, false);
+  float m = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(v[j]));
+#pragma unroll
+  for (int d = 1; d < 32; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+  int e = 0;
+  if (m > 0.0f) {
+    int ex;
+    frexpf(m, &ex);  // m in [2^(ex-1), 2^ex): the largest lands in [2^14, 2^15)
+    e = 15 - ex;
+    e = e > 120 ? 120 : (e < -120 ? -120 : e);
+  }
+  float gs = 0.f;
+#pragma unroll
+  for (int h = 0; h < 8; ++h) {
+    const _Float16 q0 = (_Float16)ldexpf(v[2 * h], e), q1 = (_Float16)ldexpf(v[2 * h + 1], e);
+    gs += (float)q0 + (float)q1;
+    o.w[h] = (uint32_t)__builtin_bit_cast(uint16_t, q0) | ((uint32_t)__builtin_bit_cast(uint16_t, q1) << 16);
+  }
+#pragma unroll
+  for (int d = 1; d < 8; d <<= 1) gs += __shfl_xor(gs, d, 64);
+  o.gs = gs;
+  o.e = e;
+  return o;
+}
+
+// ===========================================================================
+// Rotation role: task = (job, token, superblock of SB columns), 4096 / SB
+// tasks per 256 threads, rot_groups such groups per workgroup (the rest of
+// the workgroup only keeps the barrier count): the transform is VALU work,
+// so fewer groups per CU finish sooner.  Ready line k is waited on by the
+// contraction workgroups j with j % 8 == k.  Stores go to the job's blobs with agent-scope
+// (sc1) buffer stores; once every thread's stores are acknowledged the
+// workgroup adds one to each of the 8 ready lines.
+// ===========================================================================
+template <int NW>
+__device__ void rot_role(const FwdArgs2 &a, int b, char *smem) {
+  const int grp = threadIdx.x >> 8, tid = threadIdx.x & 255;
+  const int SB = a.SB, TPS = SB >> 4, per_grp = 4096 / SB;
+  const int lt = tid % TPS, tl = tid / TPS;
+  const int n_sb = a.Kp / SB, T = a.T;
+  const int task = (b * a.rot_groups + grp) * per_grp + tl;
+  const bool valid = grp < a.rot_groups && task < a.n_jobs * T * n_sb;
+  const int tk = valid ? task : 0;
+  const int j = tk / (T * n_sb), rem = tk - j * (T * n_sb);
+  const int t = rem / n_sb, sbi = rem - t * n_sb;
+  const int k0 = sbi * SB + 16 * lt;
+  // per-lane job: select among the uniform descriptors
+  const int8_t *sign = a.job[0].lin.sign_in;
+  int xb = a.job[0].xb;
+#pragma unroll
+  for (int q = 1; q < kMaxJobs; ++q)
+    if (j == q) {
+      sign = a.job[q].lin.sign_in;
+      xb = a.job[q].xb;
+    }
+  const XRaw xr = load_x16(a.x, sign, valid ? t : -1, k0, a.d_in);
+  float *xch = reinterpret_cast<float *>(smem + kLdsX + grp * kFwhtArea) + tl * (SB + (SB >> 4));
+  const XOut o = rotate16(xr, xch, lt, a.lb_in, valid);
+  if (valid) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(a.ws, 0, 0x7FFFFFF0, 0x00020000);
+    const int c = k0 >> 9, g = (k0 >> 7) & 3, q = (k0 >> 5) & 3, s0 = (k0 >> 3) & 3;
+    const int base = xb + c * a.blob;
+    const u32x4 lo = {o.w[0], o.w[1], o.w[2], o.w[3]}, hi = {o.w[4], o.w[5], o.w[6], o.w[7]};
+    __builtin_amdgcn_raw_buffer_store_b128(lo, rs, base + blob_run(g, s0, q, t, T), 0, kSc1);
+    __builtin_amdgcn_raw_buffer_store_b128(hi, rs, base + blob_run(g, s0 + 1, q, t, T), 0, kSc1);
+    float *meta = reinterpret_cast<float *>(a.ws + base + T * 1024);
+    if ((lt & 7) == 0) st_dev(meta + g * a.tm + t, o.gs);
+    if ((lt & 31) == 0) st_dev(meta + 4 * a.tm + t, ldexpf(a.rsqrt_in, -o.e));
+  }
+  wait_stores();
+  __syncthreads();
+  // lines nobody waits on (fewer than 8 contraction workgroups) stay zero
+  uint32_t *ctr = reinterpret_cast<uint32_t *>(a.ws);
+  if ((int)threadIdx.x < min(8, a.n_con)) ctr_add(ctr_at(ctr, kCtrReady + threadIdx.x), 1u);  // result unused
+}
+
+// ===========================================================================
+// Local form: the contraction workgroup rotates the superblocks its K-range
+// [c_lo, c_hi) touches into its LDS blobs itself.  G groups of 256 threads,
+// at most two passes; every x load is issued before any is used.
+// ===========================================================================
+template <int NW>
+struct LocalX {
+  XRaw r[2];
+};
+
+template <int NW>
+__device__ __forceinline__ void local_tasks(const FwdArgs2 &a, int c_lo, int c_hi, int p, int &t, int &kb,
+                                            bool &valid) {
+  constexpr int G = NW / 4;
+  const int grp = threadIdx.x >> 8, tid = threadIdx.x & 255;
+  const int SB = a.SB, TPS = SB >> 4, per_grp = 4096 / SB;
+  const int tl = tid / TPS;
+  const int sb0 = (c_lo * kChunk) / SB, sb1 = (c_hi * kChunk + SB - 1) / SB, nsb = sb1 - sb0;
+  const int task = (p * G + grp) * per_grp + tl;
+  valid = task < a.T * nsb;
+  t = valid ? task / nsb : 0;
+  kb = (sb0 + (valid ? task % nsb : 0)) * SB;
+}
+
+template <int NW>
+__device__ __forceinline__ void local_load(const FwdArgs2 &a, const int8_t *sign, int c_lo, int c_hi, int np,
+                                           LocalX<NW> &lx) {
+  const int lt = (threadIdx.x & 255) % (a.SB >> 4);
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    int t, kb;
+    bool valid;
+    local_tasks<NW>(a, c_lo, c_hi, p, t, kb, valid);
+    lx.r[p] = load_x16(a.x, sign, (valid && p < np) ? t : -1, kb + 16 * lt, a.d_in);
+  }
+}
+
+template <int NW>
+__device__ __forceinline__ void local_rotate(const FwdArgs2 &a, int c_lo, int c_hi, int np, const LocalX<NW> &lx,
+                                             char *smem, int fwht_off) {
+  const int grp = threadIdx.x >> 8, tid = threadIdx.x & 255;
+  const int SB = a.SB, TPS = SB >> 4;
+  const int lt = tid % TPS, tl = tid / TPS;
+  const int T = a.T;
+  float *xch = reinterpret_cast<float *>(smem + fwht_off + grp * kFwhtArea) + tl * (SB + (SB >> 4));
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    if (p >= np) break;  // uniform
+    int t, kb;
+    bool valid;
+    local_tasks<NW>(a, c_lo, c_hi, p, t, kb, valid);
+    const XOut o = rotate16(lx.r[p], xch, lt, a.lb_in, valid);
+    const int k0 = kb + 16 * lt, c = k0 >> 9;
+    if (valid && c >= c_lo && c < c_hi) {
+      const int g = (k0 >> 7) & 3, q = (k0 >> 5) & 3, s0 = (k0 >> 3) & 3;
+      char *bl = smem + kLdsX + (c - c_lo) * a.blob;
+      *reinterpret_cast<uint4 *>(bl + blob_run(g, s0, q, t, T)) = make_uint4(o.w[0], o.w[1], o.w[2], o.w[3]);
+      *reinterpret_cast<uint4 *>(bl + blob_run(g, s0 + 1, q, t, T)) = make_uint4(o.w[4], o.w[5], o.w[6], o.w[7]);
+      float *meta = reinterpret_cast<float *>(bl + T * 1024);
+      if ((lt & 7) == 0) meta[g * a.tm + t] = o.gs;
+      if ((lt & 31) == 0) meta[4 * a.tm + t] = ldexpf(a.rsqrt_in, -o.e);
+    }
+  }
+}
+
+// ===========================================================================
+// Contraction role.
+// ===========================================================================
+template <int BITS, int MT, int NW, bool LOCAL>
+__device__ void con_role(const FwdArgs2 &a, int cb, char *smem) {
+  int j = 0;
+#pragma unroll
+  for (int q = 1; q < kMaxJobs; ++q)
+    if (q < a.n_jobs && cb >= a.job[q].con0) j = q;
+  const NL_CONST FwdJob &J = job_at(a, j);
+  const NL_CONST LinearDev &L = J.lin;
+  uint32_t *ctr = reinterpret_cast<uint32_t *>(a.ws);
+  const int i = cb - J.con0;
+  const int S = J.S, sp = i % S, rb = i / S;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int tl = lane & 15, kq = lane >> 4;
+  const int rt = J.rt, kw = J.kw;
+  const int my_t = wave % rt, my_k = wave / rt;
+  const int tile_id = rb * rt + my_t;
+  const bool wact = my_k < kw && tile_id < J.n_tiles;
+  const int tile = min(tile_id, J.n_tiles - 1);
+  const int c_lo = sp * J.cps, c_hi = min(a.n_chunks, c_lo + J.cps), nck = c_hi - c_lo;
+  const int per = (nck + kw - 1) / kw;
+  const int w_lo = c_lo + min(my_k * per, nck), w_hi = c_lo + min(my_k * per + per, nck);
+  int wn = wact ? w_hi - w_lo : 0;
+  const int T = a.T;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(NL_LOCAL void *)smem;
+
+  // ---- byte table into LDS (local form: wave 0, two 1 KiB copies; the
+  // hand-over form copies it beside x')
+  if (LOCAL && wave == 0) {
+    const void *src = sgpr_ptr(L.lut256);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      __builtin_amdgcn_global_load_lds((const NL_GLOBAL void *)((const char *)src + q * 1024 + lane * 16),
+                                       (NL_LOCAL void *)(size_t)(lds0 + kLdsLut + q * 1024), 16, 0, 0);
+  }
+
+  // ---- weight ring: raw buffer loads through descriptors that end at the
+  // wave's last chunk (requests past it return zeros with no memory access).
+  constexpr int NS = fwd_ring_sets(BITS, MT, LOCAL, NW);
+  constexpr int kRaw = 0x00020000;
+  constexpr int kNt = 2;  // non-temporal: streamed once
+  const size_t tc0 = (size_t)tile * a.n_chunks;
+  const int lim = wn > 0 ? w_hi : 0;
+  const __amdgpu_buffer_rsrc_t rbs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)sgpr_ptr(L.base + tc0 * 128), 0, lim * kBaseBlockBytes, kRaw);
+  const __amdgpu_buffer_rsrc_t rbsc =
+      __builtin_amdgcn_make_buffer_rsrc((void *)sgpr_ptr(L.bscale + tc0 * 16), 0, lim * kScaleBlockBytes, kRaw);
+  __amdgpu_buffer_rsrc_t rrs = rbs, rrsc = rbsc;
+  if constexpr (BITS > 0) {
+    rrs = __builtin_amdgcn_make_buffer_rsrc((void *)sgpr_ptr(L.resid + tc0 * (64 * BITS)), 0,
+                                            lim * resid_block_bytes(BITS), kRaw);
+    rrsc = __builtin_amdgcn_make_buffer_rsrc((void *)sgpr_ptr(L.rscale + tc0 * 16), 0, lim * kScaleBlockBytes, kRaw);
+  }
+  auto fence = []() { asm volatile("" ::: "memory"); };
+  auto loadw = [&](WRegs<BITS> &w, int c) {
+#pragma unroll
+    for (int q = 0; q < kBasePieces; ++q) {
+      w.b[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rbs, (c * 128 + q * 64 + lane) * 16, 0, kNt));
+      fence();
+    }
+    w.sb = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rbsc, (c * 16 + tl) * 8, 0, 0));
+    fence();
+    if constexpr (BITS > 0) {
+#pragma unroll
+      for (int q = 0; q < BITS; ++q) {
+        w.r[q] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rrs, (c * 64 * BITS + q * 64 + lane) * 16, 0, kNt));
+        fence();
+      }
+      w.sr = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rrsc, (c * 16 + tl) * 8, 0, 0));
+      fence();
+    }
+  };
+  // Order of the wave's memory requests.  A CU's requests are taken in
+  // issue order, so a small load issued behind the weight stream waits for
+  // it.  The local form therefore issues its activation loads first; the
+  // hand-over form requests one weight set per wave before the wait and the
+  // x' copy before the remaining sets.  Each wave then waits only for what
+  // it issued before its last weight loads (in-order counter), and the
+  // barrier makes every wave's copy visible.
+  constexpr int LW = kBasePieces + 1 + (BITS > 0 ? BITS + 1 : 0);  // loads per set
+  constexpr int NS0 = LOCAL ? NS : (BITS > 0 ? 1 : 2);              // sets before the x' copy
+  static_assert(LW * NS <= 63, "wait count");
+  WRegs<BITS> w[NS];
+  bool okw = true;
+  if constexpr (LOCAL) {
+    constexpr int G = NW / 4;
+    const int sb0 = (c_lo * kChunk) / a.SB, sb1 = (c_hi * kChunk + a.SB - 1) / a.SB;
+    const int np = (T * (sb1 - sb0) + G * (4096 / a.SB) - 1) / (G * (4096 / a.SB));
+    LocalX<NW> lx;
+    local_load<NW>(a, L.sign_in, c_lo, c_hi, np, lx);
+    fence();
+#pragma unroll
+    for (int k = 0; k < NS; ++k) loadw(w[k], w_lo + k);
+    wait_vm<LW * NS>();  // the activations (and the table) have landed
+    const int fwht_off = kLdsX + ((J.cps * a.blob + 15) & ~15);
+    local_rotate<NW>(a, c_lo, c_hi, np, lx, smem, fwht_off);
+    lds_barrier();
+  } else {
+    // wave 0 polls the ready line with no weight loads of its own in flight
+    // (its wait would otherwise wait for them) and requests its first sets
+    // after the wait
+    fence();
+    if (wave != 0) {
+#pragma unroll
+      for (int k = 0; k < NS0; ++k) loadw(w[k], w_lo + k);
+    }
+    volatile NL_LOCAL uint32_t *flag = (volatile NL_LOCAL uint32_t *)(size_t)(lds0 + kLdsFlag);
+    if (wave == 0) {
+      uint32_t got = 1;
+      if (lane == 0)
+        got = wait_count(ctr_at(ctr, kCtrReady + (cb & 7)), (uint32_t)a.n_rot + a.wait_extra, a.spin_limit,
+                         ctr_at(ctr, kCtrErr));
+      if (lane == 0) *flag = got;
+    }
+    lds_barrier();
+    okw = *flag != 0;
+    if (wave == 1 % NW) {  // the byte table (another wave than the poller)
+      const void *lsrc = sgpr_ptr(L.lut256);
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        __builtin_amdgcn_global_load_lds((const NL_GLOBAL void *)((const char *)lsrc + q * 1024 + lane * 16),
+                                         (NL_LOCAL void *)(size_t)(lds0 + kLdsLut + q * 1024), 16, 0, 0);
+    }
+    if (okw) {  // every wave copies a share of the K-range's x'
+      const char *src = (const char *)sgpr_ptr(a.ws + J.xb + (size_t)c_lo * a.blob);
+      const int bytes = nck * a.blob, n_ins = (bytes + 1023) >> 10;
+      for (int q = wave; q < n_ins; q += NW) {
+        const int off = q * 1024 + lane * 16;
+        if (off < bytes)
+          __builtin_amdgcn_global_load_lds((const NL_GLOBAL void *)(src + off),
+                                           (NL_LOCAL void *)(size_t)(lds0 + kLdsX + q * 1024), 16, 0, 0);
+      }
+    }
+    fence();
+    if (wave == 0) {  // all its sets after its share of the copy
+#pragma unroll
+      for (int k = 0; k < NS; ++k) loadw(w[k], w_lo + k);
+      wait_vm<LW * NS>();
+    } else {
+#pragma unroll
+      for (int k = NS0; k < NS; ++k) loadw(w[k], w_lo + k);
+      wait_vm<LW * (NS - NS0)>();  // this wave's share of the copy (and its first sets) landed
+    }
+    lds_barrier();
+  }
+  if (!okw) wn = 0;
+
+  // ---- contraction
+  const float kinv = L.kinv;
+  const int tm = a.tm, blob = a.blob;
+  int a_off[MT], m_off[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    a_off[m] = (kq * T + min(16 * m + tl, T - 1)) * 16;
+    m_off[m] = T * 1024 + min(16 * m + 4 * kq, tm - 4) * 4;  // + 4 tm g: group sums, + 16 tm: scale
+  }
+  const int gs_stride = 64 * T;  // bytes between the runs of consecutive (group, step)
+  floatx4 acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](WRegs<BITS> &wr, int cl) {
+    pin(wr);
+    const char *xb = smem + kLdsX + cl * blob;
+    const uint32_t *bw = reinterpret_cast<const uint32_t *>(wr.b);
+    const uint32_t *rw = reinterpret_cast<const uint32_t *>(wr.r);
+    floatx4 accC[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) accC[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < kChunkGroups; ++g) {
+      constexpr bool HA = MT == 1;  // one token tile: the group's activations are read first
+      half8 A[4];
+      auto act = [&](int m, int s) -> half8 {
+        if constexpr (HA) return A[s];
+        return *reinterpret_cast<const half8 *>(xb + (g * 4 + s) * gs_stride + a_off[m]);
+      };
+      if constexpr (HA) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) A[s] = *reinterpret_cast<const half8 *>(xb + (g * 4 + s) * gs_stride + a_off[0]);
+      }
+      uint32_t bq[16];
+      unpack_base2(bw + 2 * g, bq);
+      uint32_t rq[16];
+      if constexpr (BITS > 0) unpack_resid<BITS, true>(rw + g * BITS, rq);
+      const float sb = h2f((uint32_t)(wr.sb >> (16 * g)) & 0xFFFFu) * kinv;
+      // residual: s_r * (2^24 * sum(u 2^-24 x') - 2^(b-1) * sum(x'))
+      float srA = 0.f, srB = 0.f;
+      if constexpr (BITS > 0) {
+        const float sr = h2f((uint32_t)(wr.sr >> (16 * g)) & 0xFFFFu);
+        srA = sr * 16777216.0f;
+        srB = -sr * (float)(1 << (BITS - 1));
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        floatx4 aB = {0.f, 0.f, 0.f, 0.f}, aR = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const half8 av = act(m, s);
+          aB = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, as_half8(bq + 4 * s), aB, 0, 0, 0);
+          if constexpr (BITS > 0) aR = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, as_half8(rq + 4 * s), aR, 0, 0, 0);
+        }
+        // With s_r = 0 both residual fmas return accC unchanged, so verify
+        // with zero residual scales equals the draft bit for bit.
+        floatx4 xs = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (BITS > 0) xs = *reinterpret_cast<const floatx4 *>(xb + m_off[m] + g * 4 * tm);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          accC[m][e] = fmaf(sb, aB[e], accC[m][e]);
+          if constexpr (BITS > 0) accC[m][e] = fmaf(srA, aR[e], fmaf(srB, xs[e], accC[m][e]));
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const floatx4 ts = *reinterpret_cast<const floatx4 *>(xb + m_off[m] + 16 * tm);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[m][e] = fmaf(ts[e], accC[m][e], acc[m][e]);
+    }
+  };
+
+  {
+    // chunk ci of the wave uses set ci % NS; after it, the set is refilled
+    // with chunk ci + NS.  NS chunks per trip (the compiler's waits stay
+    // counted), the last wn % NS after the loop.
+    int ci = 0;
+#pragma unroll 1
+    for (; ci + NS <= wn; ci += NS) {
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        compute(w[k], w_lo + ci + k - c_lo);
+        fence();
+        loadw(w[k], w_lo + ci + k + NS);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NS - 1; ++k)
+      if (ci + k < wn) compute(w[k], w_lo + ci + k - c_lo);
+  }
+  if (!okw) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] = floatx4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+  }
+  wait_vm<0>();  // the ring's padding loads
+
+  // ---- waves of one row tile add their sums (in wave order) through LDS
+  lds_barrier();  // every wave is done with the blobs
+  float *red = reinterpret_cast<float *>(smem + kLdsX);
+  if (kw > 1) {
+    if (wact && my_k > 0) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[((wave * MT + m) * 4 + e) * 64 + lane] = acc[m][e];
+    }
+    lds_barrier();
+    if (wact && my_k == 0) {
+      for (int k = 1; k < kw; ++k) {
+        const int w2 = my_t + k * rt;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[m][e] += red[((w2 * MT + m) * 4 + e) * 64 + lane];
+      }
+    }
+  }
+
+  // ---- output
+  const int d_out = J.d_out;
+  const bool two = J.ysum != nullptr;
+  const int row = tile * kTileRows + tl;
+  const bool mine = wact && my_k == 0 && row < d_out;
+  auto put = [&](float *out, bool coh) {
+    if (!mine) return;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * m + 4 * kq + e;
+        if (t < T) {
+          float *p = out + (size_t)t * d_out + row;
+          if (coh) st_dev(p, acc[m][e]); else *p = acc[m][e];
+        }
+      }
+  };
+  uint32_t *flag = reinterpret_cast<uint32_t *>(smem + kLdsFlag);
+  bool have_sum = true;  // this workgroup holds (or has written) the final sums of its rows
+  if (S == 1) {
+    put(two ? J.ysum : J.y, two);
+  } else {
+    put(J.part + (size_t)sp * T * d_out, true);
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t *cnt = ctr_at(ctr, J.ctr_split + rb);
+      const bool last = ctr_add(cnt, 1u) == (uint32_t)(S - 1);
+      if (last) st_dev(cnt, 0u);
+      *flag = last;
+    }
+    __syncthreads();
+    have_sum = *reinterpret_cast<volatile uint32_t *>(flag) != 0;
+    if (have_sum) {
+      // the last of the row block's splits adds the partials in split order
+      constexpr int NT = NW * 64;
+      const int r0 = rb * rt * kTileRows;
+      const int rows_here = min(rt * kTileRows, d_out - r0), total = T * rows_here;
+      for (int base = 0; base < total; base += 4 * NT) {
+        size_t o[4];
+        bool okk[4];
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int idx = base + e4 * NT + (int)threadIdx.x, t = idx / rows_here, r = idx % rows_here;
+          okk[e4] = idx < total;
+          o[e4] = okk[e4] ? (size_t)t * d_out + r0 + r : 0;
+        }
+        for (int s0 = 0; s0 < S; s0 += 8) {
+          float u[4][8];
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) u[e4][q] = ld_dev(J.part + (size_t)min(s0 + q, S - 1) * T * d_out + o[e4]);
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[e4] += (s0 + q < S) ? u[e4][q] : 0.f;
+        }
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          if (!okk[e4]) continue;
+          if (two) st_dev(J.ysum + o[e4], v[e4]); else J.y[o[e4]] = v[e4];
+        }
+      }
+    }
+  }
+  if (two && have_sum) {
+    // count the row block into its output superblock; the last one releases
+    // one token per finish task (token) of the superblock
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int r0 = rb * rt * kTileRows, sbi = r0 / a.OB;
+      const int rb_in_sb = (min(a.OB, d_out - sbi * a.OB) + rt * kTileRows - 1) / (rt * kTileRows);
+      uint32_t *cnt = ctr_at(ctr, J.ctr_sb + sbi);
+      if (ctr_add(cnt, 1u) == (uint32_t)(rb_in_sb - 1)) {
+        st_dev(cnt, 0u);
+        ctr_add(ctr_at(ctr, J.ctr_sb + J.n_sb + sbi), (uint32_t)T);
+      }
+    }
+  }
+  if constexpr (!LOCAL) {
+    // the last workgroup to pass the wait on a ready line clears the line
+    if (threadIdx.x == 0) {
+      const int line = cb & 7;
+      const uint32_t waiters = (uint32_t)((a.n_con - 1 - line) / 8 + 1);
+      if (ctr_add(ctr_at(ctr, kCtrExit + line), 1u) == waiters - 1) {
+        st_dev(ctr_at(ctr, kCtrReady + line), 0u);
+        st_dev(ctr_at(ctr, kCtrExit + line), 0u);
+      }
+    }
+  }
+}
+
+// ===========================================================================
+// Finish role (two-sided): task = (job, token, output superblock of OB rows);
+// 4096 / OB tasks per 256 threads.  Takes a token of its superblock, reads
+// the summed rows and applies y = S_o H_o y~.
+// ===========================================================================
+template <int NW>
+__device__ void fin_role(const FwdArgs2 &a, int b, char *smem) {
+  constexpr int G = NW / 4;
+  const int grp = threadIdx.x >> 8, tid = threadIdx.x & 255;
+  const int OB = a.OB, TPS = OB >> 4, per_grp = 4096 / OB, n = 31 - __builtin_clz(OB);
+  const int lt = tid % TPS, tl = tid / TPS;
+  const int task = (b * G + grp) * per_grp + tl;
+  uint32_t *ctr = reinterpret_cast<uint32_t *>(a.ws);
+  // task -> (job, token, superblock); jobs differ in n_sb
+  int j = 0, rem = task;
+#pragma unroll
+  for (int q = 0; q < kMaxJobs - 1; ++q) {
+    const int nt = q < a.n_jobs ? a.T * a.job[q].n_sb : 0;
+    if (j == q && rem >= nt && q + 1 < a.n_jobs) {
+      rem -= nt;
+      j = q + 1;
+    }
+  }
+  const float *ysum = a.job[0].ysum;
+  float *y = a.job[0].y;
+  const int8_t *so = a.job[0].lin.sign_out;
+  int dj = a.job[0].d_out, nsbj = a.job[0].n_sb, csb = a.job[0].ctr_sb;
+#pragma unroll
+  for (int q = 1; q < kMaxJobs; ++q)
+    if (j == q) {
+      ysum = a.job[q].ysum;
+      y = a.job[q].y;
+      so = a.job[q].lin.sign_out;
+      dj = a.job[q].d_out;
+      nsbj = a.job[q].n_sb;
+      csb = a.job[q].ctr_sb;
+    }
+  const bool valid = rem < a.T * nsbj && j < a.n_jobs;
+  const int t = valid ? rem / nsbj : 0, sbi = valid ? rem % nsbj : 0;
+  const int r0 = sbi * OB;
+  float *xch = reinterpret_cast<float *>(smem + kLdsX + grp * kFwhtArea) + tl * (OB + (OB >> 4));
+  uint32_t *flag = reinterpret_cast<uint32_t *>(smem + kLdsFlag) + grp * per_grp + tl;
+  if (lt == 0)
+    *flag = valid ? take_one(ctr_at(ctr, csb + nsbj + sbi), a.wait_extra, a.spin_limit, ctr_at(ctr, kCtrErr)) : 1u;
+  __syncthreads();
+  const bool okw = *reinterpret_cast<volatile uint32_t *>(flag) != 0;
+  float v[16];
+  const float *ys = ysum + (size_t)t * dj;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) v[q] = ld_dev(ys + min(r0 + TPS * q + lt, dj - 1));
+  fwht_tasks(v, xch, lt, TPS, n, a.lb_out);
+  if (!valid) return;
+  float *yo = y + (size_t)t * dj;
+  const int rr = r0 + 16 * lt;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int r = rr + q;
+    if (r < dj) yo[r] = okw ? v[q] * a.rsqrt_out * (float)so[r] : __builtin_nanf("");
+  }
+}
+
+// ===========================================================================
+// The kernel: role by workgroup index.
+// ===========================================================================
+template <int BITS, int MT, int NW, bool LOCAL>
+__global__ __launch_bounds__(NW * 64) void fwd_kernel(const FwdArgs2 a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  int b = blockIdx.x;
+  if constexpr (!LOCAL) {
+    if (b < a.n_rot) {
+      rot_role<NW>(a, b, smem);
+      return;
+    }
+    b -= a.n_rot;
+  }
+  if (b < a.n_con) {
+    con_role<BITS, MT, NW, LOCAL>(a, b, smem);
+    return;
+  }
+  fin_role<NW>(a, b - a.n_con, smem);
+}
+
+template <int BITS, int MT, int NW, bool LOCAL>
+static void launch_fwd_t(const FwdArgs2 &a, size_t lds, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  const dim3 grid(a.n_rot + a.n_con + a.n_fin), block(NW * 64);
+  if (ev0)
+    hipExtLaunchKernelGGL(fwd_kernel<BITS, MT, NW, LOCAL>, grid, block, lds, s, ev0, ev1, 0, a);
+  else
+    fwd_kernel<BITS, MT, NW, LOCAL><<<grid, block, lds, s>>>(a);
+}
+
+template <int BITS>
+static hipError_t launch_fwd_bits(const FwdArgs2 &a, int mt, int nw, bool local, size_t lds, hipStream_t s,
+                                  hipEvent_t ev0, hipEvent_t ev1) {
+  if (mt == 1 && nw == 8) {
+    if (local) launch_fwd_t<BITS, 1, 8, true>(a, lds, s, ev0, ev1);
+    else launch_fwd_t<BITS, 1, 8, false>(a, lds, s, ev0, ev1);
+    return hipGetLastError();
+  }
+  if (nw != fwd_waves(mt)) return hipErrorInvalidValue;
+  if (local) {
+    if (mt != 1) return hipErrorInvalidValue;
+    launch_fwd_t<BITS, 1, 12, true>(a, lds, s, ev0, ev1);
+    return hipGetLastError();
+  }
+  switch (mt) {
+    case 1: launch_fwd_t<BITS, 1, 12, false>(a, lds, s, ev0, ev1); break;
+    case 2: launch_fwd_t<BITS, 2, 12, false>(a, lds, s, ev0, ev1); break;
+    case 3: launch_fwd_t<BITS, 3, 8, false>(a, lds, s, ev0, ev1); break;
+    case 4: launch_fwd_t<BITS, 4, 8, false>(a, lds, s, ev0, ev1); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_forward2(const FwdArgs2 &a, int bits, int mt, int nw, bool local, size_t lds, hipStream_t s,
+                           hipEvent_t ev0, hipEvent_t ev1) {
+  if (a.SB < 512 || a.SB > 4096 || lds > 160 * 1024) return hipErrorInvalidValue;
+  if (a.n_fin > 0 && (a.OB < 512 || a.OB > 4096)) return hipErrorInvalidValue;
+  switch (bits) {
+    case 0: return launch_fwd_bits<0>(a, mt, nw, local, lds, s, ev0, ev1);
+    case 6: return launch_fwd_bits<6>(a, mt, nw, local, lds, s, ev0, ev1);
+    case 7: return launch_fwd_bits<7>(a, mt, nw, local, lds, s, ev0, ev1);
+    case 8: return launch_fwd_bits<8>(a, mt, nw, local, lds, s, ev0, ev1);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace nl

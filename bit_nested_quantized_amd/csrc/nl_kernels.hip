@@ -17,29 +17,9 @@
 #include <hip/hip_fp16.h>
 
 #include "nl_kernels.h"
-
-#define NL_GLOBAL __attribute__((address_space(1)))
-#define NL_LOCAL __attribute__((address_space(3)))
-#define NL_CONST __attribute__((address_space(4)))
+#include "nl_dev.h"
 
 namespace nl {
-
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ half8 as_half8(const uint32_t *p) {
-  u32x4 v = {p[0], p[1], p[2], p[3]};
-  return __builtin_bit_cast(half8, v);
-}
-
-__device__ __forceinline__ float h2f(uint32_t bits16) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
-}
-
-__device__ __forceinline__ float bf16_to_float(uint16_t b) {
-  return __builtin_bit_cast(float, (uint32_t)b << 16);
-}
 
 // ===========================================================================
 // Create-time repack.  One wave per tile-chunk; lane l handles row
@@ -170,165 +150,6 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeArgs a) {
   }
 }
 
-// ===========================================================================
-// Workgroup Walsh-Hadamard transforms (POC section 1: Sylvester H, applied
-// block-diagonally).  A workgroup of 256 threads transforms 4096 values:
-// 4096/SB independent "tasks" of SB = 2^n values (n in 9..12), TPS = SB/16
-// threads per task, 16 values per thread.  Butterflies run unnormalised over
-// the low `lb` bits of the element index i (block 2^lb).  The 16 values of a
-// thread pass through three layouts (the stages commute, so their order is
-// free):
-//   B  i = 16*lt + j           low 4 bits in registers; contiguous values
-//                              (16-byte loads of x, 16-byte stores of x')
-//   C  i = (lt&15) + 16*j + 256*(lt>>4)   bits 4..7 in registers
-//   A  i = TPS*j + lt          top 4 bits in registers
-// with padded LDS transposes B->C->A->B in between.
-// ===========================================================================
-__device__ __forceinline__ int lds_pad(int i) { return i + (i >> 4); }
-
-__device__ __forceinline__ void bfly16(float (&v)[16], int bit) {
-  const int h = 1 << bit;
-#pragma unroll
-  for (int j = 0; j < 16; ++j)
-    if (!(j & h)) {
-      const float x0 = v[j], x1 = v[j | h];
-      v[j] = x0 + x1;
-      v[j | h] = x0 - x1;
-    }
-}
-
-// v: layout B on entry and on exit (thread lt of the task holds points
-// 16*lt + j).  The transform is a butterfly on every index bit below LB;
-// four bits are done in registers at a time, with LDS transposes
-//   B (bits 0-3 in registers) -> C (bits 4-7) -> A (bits N-4..N-1, those
-//   from 8 up) -> B.
-// N = log2 of the task size SB, LB = log2 of the Hadamard block (LB <= N);
-// both compile-time, so every LDS address is a base plus an immediate.
-// xch: this task's LDS (SB + SB/16 floats).  idle: a thread (uniformly per
-// wave) that only keeps the barrier count.
-template <int N, int LB>
-__device__ __forceinline__ void fwht_bt(float (&v)[16], float *xch, int lt, bool idle) {
-  constexpr int TPS = 1 << (N - 4);
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    if (q < LB) bfly16(v, q);
-  const int cbase = (lt & 15) + 256 * (lt >> 4);
-  float *pb = xch + lds_pad(16 * lt);             // B: + j
-  float *pc = xch + lds_pad(cbase);               // C: + 17 j
-  float *pa = xch + lt + (lt >> 4);               // A: + (TPS + TPS / 16) j
-  __syncthreads();
-  if (!idle)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) pb[j] = v[j];
-  __syncthreads();
-  if (!idle)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = pc[17 * j];
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    if (4 + q < LB) bfly16(v, q);
-  __syncthreads();
-  if (!idle)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) pc[17 * j] = v[j];
-  __syncthreads();
-  if (!idle)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = pa[(TPS + TPS / 16) * j];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    constexpr int base = N - 4;
-    if (base + q >= 8 && base + q < LB) bfly16(v, q);
-  }
-  __syncthreads();
-  if (!idle)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) pa[(TPS + TPS / 16) * j] = v[j];
-  __syncthreads();
-  if (!idle)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = pb[j];
-}
-
-// The transform for a task of SB = max(2^lb, 512) points (one uniform
-// dispatch on the block size; lb is 7..12 since d_in is a multiple of 128).
-__device__ __forceinline__ void fwht_b(float (&v)[16], float *xch, int lt, int lb, bool idle) {
-  switch (lb) {
-    case 7: fwht_bt<9, 7>(v, xch, lt, idle); break;
-    case 8: fwht_bt<9, 8>(v, xch, lt, idle); break;
-    case 9: fwht_bt<9, 9>(v, xch, lt, idle); break;
-    case 10: fwht_bt<10, 10>(v, xch, lt, idle); break;
-    case 11: fwht_bt<11, 11>(v, xch, lt, idle); break;
-    default: fwht_bt<12, 12>(v, xch, lt, idle); break;
-  }
-}
-
-// v: layout A on entry, layout B on exit (the output rotation, whose input
-// loads are coalesced in layout A).
-__device__ __forceinline__ void fwht_tasks(float (&v)[16], float *xch, int lt, int TPS, int n, int lb) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    if (n - 4 + q < lb) bfly16(v, q);
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 16; ++j) xch[lds_pad(TPS * j + lt)] = v[j];
-  __syncthreads();
-  const int cbase = (lt & 15) + 256 * (lt >> 4);
-#pragma unroll
-  for (int j = 0; j < 16; ++j) v[j] = xch[lds_pad(cbase + 16 * j)];
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    if (4 + q < n - 4 && 4 + q < lb) bfly16(v, q);
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 16; ++j) xch[lds_pad(cbase + 16 * j)] = v[j];
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 16; ++j) v[j] = xch[lds_pad(16 * lt + j)];
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    if (q < lb) bfly16(v, q);
-}
-
-// 16 consecutive activations (columns k0 .. k0 + 15 of row xrow) and their
-// signs: two 16-byte loads of x, one of the signs.  Rows of x and the sign
-// vector are 16-byte aligned and d_in is a multiple of 128, so a group of 16
-// is wholly inside or wholly past d_in.  Outside (xrow < 0 or k0 >= d_in)
-// the loads read the first 16 columns and the values become zeros.
-struct XRaw {
-  u32x4 a, b, s;
-  bool in;
-};
-__device__ __forceinline__ XRaw load_x16(const uint16_t *x, const int8_t *sign, int xrow, int k0, int d_in) {
-  XRaw r;
-  r.in = xrow >= 0 && k0 < d_in;
-  const size_t off = r.in ? (size_t)xrow * d_in + k0 : 0;
-  // global address space: a generic (flat) load would also count in lgkmcnt,
-  // and waiting for it would wait for every load in flight
-  const NL_GLOBAL u32x4 *xp = (const NL_GLOBAL u32x4 *)(x + off);
-  const NL_GLOBAL u32x4 *sp = (const NL_GLOBAL u32x4 *)(sign + (r.in ? k0 : 0));
-  r.a = xp[0];
-  r.b = xp[1];
-  r.s = sp[0];
-  return r;
-}
-// x * sign in fp32 (exact: bf16 widens exactly, signs are +-1)
-__device__ __forceinline__ void cvt_x16(float (&v)[16], const XRaw &r) {
-  const uint32_t xw[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
-  const uint32_t sw[4] = {r.s.x, r.s.y, r.s.z, r.s.w};
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const uint32_t h = (xw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-    const int sg = (int)(int8_t)((sw[j >> 2] >> (8 * (j & 3))) & 0xFFu);
-    v[j] = r.in ? __uint_as_float(h << 16) * (float)sg : 0.0f;
-  }
-}
-
-// Column offset, inside its 128-column group, of run r (0..15) of the
-// contraction's activation layout: run = step * 4 + quarter holds the 8
-// columns 32 * quarter + 8 * step .. + 8 (the MFMA A operand of lanes with
-// l >> 4 == quarter at step `step`).
-__device__ __forceinline__ int run_col(int r) { return 32 * (r & 3) + 8 * (r >> 2); }
 
 // Largest e with offsets[e] <= row (the expert of a pair).
 __device__ __forceinline__ int expert_of(const int32_t *offsets, int n, int row) {
@@ -390,32 +211,6 @@ __device__ __forceinline__ bool expert_active(const int32_t *offsets, int e, int
   return r1 > r0 && r0 >= 0 && r0 < R;
 }
 
-// ===========================================================================
-// Hand-over between the workgroups of one launch.  Data written by one
-// workgroup and read by another (on any XCD) goes through agent-scope (sc1)
-// stores and loads, and a counter is bumped only after the writer's stores
-// are acknowledged (s_waitcnt vmcnt(0) in every thread, then a barrier), so
-// no L2 write-back or invalidate is needed.  Counters are 64-byte apart; the
-// launch leaves every counter at zero.
-// ===========================================================================
-constexpr int kSc1 = 16;  // cache policy of a buffer op: agent-coherent (sc1), as st_dev
-__device__ __forceinline__ void st_dev(float *p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_dev(uint32_t *p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_dev(const float *p) {
-  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t ld_dev(const uint32_t *p) {
-  return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t ctr_add(uint32_t *p, uint32_t v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ uint32_t *ctr_at(uint32_t *c, int i) { return c + kCtrStride * i; }
 
 // Wait for a token on semaphore `sem` and take it (the output rotation's
 // hand-over; same dispatch-order argument and spin limit as wait_ready).
@@ -446,7 +241,7 @@ __device__ void wait_ready(const uint32_t *line, uint32_t n, uint32_t *err) {
 }
 
 // ===========================================================================
-// Input rotation (POC section 1: x' = H_i S_i x, "once per Linear").
+// Input rotation (POC section 1: x' = H_i S_i x, computed a single time for each linear and call).
 // Task = (row of x', superblock of SB = max(b, 512) columns), so every
 // 512-column chunk lies in one task; a workgroup runs 4096/SB tasks.  Each
 // chunk is scaled by 2^s (its largest magnitude lands in [2^14, 2^15]) and
@@ -631,18 +426,6 @@ struct LocalPlan {
   static constexpr int bytes = o_f + (4096 + 256) * 4;      // + one FWHT area
 };
 
-// Wait until at most n of this wave's vector-memory operations are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-template <int BITS>
-struct WRegs {
-  u32x4 b[kBasePieces];
-  u32x4 r[BITS > 0 ? BITS : 1];
-  uint64_t sb, sr;  // the row's 4 group scales (fp16) of each plane
-};
 
 // Register sets in the weight ring of a tile wave: deeper where the
 // accumulators leave room (one or two token tiles), deepest for the draft,
@@ -655,35 +438,15 @@ __host__ __device__ constexpr int ring_sets() {
   return BITS == 0 ? 4 : 3;
 }
 
-// An ordered no-op on every register of a set: work on the set cannot be
-// scheduled above it, so the wait for the set's loads lands here.
-template <int BITS>
-__device__ __forceinline__ void pin(WRegs<BITS> &w) {
-#pragma unroll
-  for (int i = 0; i < kBasePieces; ++i) asm volatile("" : "+v"(w.b[i]));
-  asm volatile("" : "+v"(w.sb));
-  if constexpr (BITS > 0) {
-#pragma unroll
-    for (int i = 0; i < BITS; ++i) asm volatile("" : "+v"(w.r[i]));
-    asm volatile("" : "+v"(w.sr));
-  }
-}
 
-// A wave-uniform pointer in an SGPR pair (the copies' scalar base operand).
-__device__ __forceinline__ const void *sgpr_ptr(const void *p) {
-  const uint64_t v = (uint64_t)(uintptr_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (const void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
-
+// Direct global -> LDS copies (16 or 4 bytes per lane): lane i's bytes land
+// at lds + i * size.  The compiler's builtin sets M0 itself, so no register is
+// written behind its back.
 __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, const void *base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               ::"s"(lds), "v"(voff), "s"(base) : "memory", "m0");
+  __builtin_amdgcn_global_load_lds((const NL_GLOBAL void *)((const char *)base + voff), (NL_LOCAL void *)(size_t)lds, 16, 0, 0);
 }
 __device__ __forceinline__ void dma4(uint32_t lds, uint32_t voff, const void *base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
-               ::"s"(lds), "v"(voff), "s"(base) : "memory", "m0");
+  __builtin_amdgcn_global_load_lds((const NL_GLOBAL void *)((const char *)base + voff), (NL_LOCAL void *)(size_t)lds, 4, 0, 0);
 }
 // A rotation task's x' is acknowledged (wait_stores) by the thread calling
 // this with k < 8: it adds one to ready line k.  The last task to count on

@@ -58,8 +58,10 @@ struct LinearDev {
   const int8_t *sign_out;   // [d_out] or null
   uint32_t lut[16];         // fp16x2 {kappa*L[i & 3], kappa*L[i >> 2]}
   float kinv;               // 1 / kappa
-  int32_t pad_[3];
+  int32_t pad_;
+  const uint2 *lut256;      // [256] byte-indexed base table (two fp16x2 per byte of codes)
 };
+static_assert(sizeof(LinearDev) == 128, "descriptor size");
 
 // ---------------------------------------------------------------------------
 // Residual unpack: the lane's `bits` dwords of one group -> 16 fp16x2 pairs,
@@ -100,14 +102,18 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
   return (a & sconst(m)) | o;
 }
 
-template <int BITS>
+// SUB: the halves are the fp16 subnormals u * 2^-24 instead (exact; no
+// exponent bits are set), for a contraction that removes the smaller offset
+// 2^(b-1) * 2^-24 with the activations' group sums.
+template <int BITS, bool SUB = false>
 __device__ __forceinline__ void unpack_resid(const uint32_t *d, uint32_t *out) {
-  const uint32_t K = vconst(0x64006400u);
+  const uint32_t K = SUB ? 0u : vconst(0x64006400u);
   if constexpr (BITS == 8) {
-    const uint32_t K8 = 0x64646464u;
+    const uint32_t K8 = SUB ? 0u : 0x64646464u;
 #pragma unroll
     for (int P = 0; P < 16; ++P)
-      out[P] = __builtin_amdgcn_perm(K8, d[P >> 1], (P & 1) ? 0x04030402u : 0x04010400u);
+      out[P] = SUB ? __builtin_amdgcn_perm(0u, d[P >> 1], (P & 1) ? 0x0c030c02u : 0x0c010c00u)
+                   : __builtin_amdgcn_perm(K8, d[P >> 1], (P & 1) ? 0x04030402u : 0x04010400u);
   } else if constexpr (BITS == 6) {
 #pragma unroll
     for (int P = 0; P < 6; ++P) out[P] = and_or(d[P], 0x003F003Fu, K);

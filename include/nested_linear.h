@@ -13,8 +13,8 @@
  * where Q_base[r,k] = levels[c(r,k)] * s_base[r, k/128] is the 2-bit
  * Lloyd-Max base and Q_resid[r,k] = q(r,k) * s_resid[r, k/128] the uniform
  * b-bit residual (b = 6, 7 or 8), both in the rotated basis.  The draft
- * forward is the same without Q_resid ("The draft forward is the same but
- * without y_r", section 4); it reads only the base planes, the dual-plane
+ * forward drops the Q_resid term and nothing else (section 4); it reads only
+ * the base planes, the dual-plane
  * principle of the BitNest paper (page 2, section 3.3 "Dual-Plane Weight
  * Storage").  H is the normalised Sylvester-Hadamard matrix applied
  * block-diagonally with block b = the largest power of two dividing the
@@ -60,7 +60,7 @@ typedef enum {
  *   base_scales  [d_out][G] fp16 bit patterns (one scale per row and 128-group).
  *   resid_codes  [d_out][G][16*b] bytes: 128 b-bit two's-complement fields,
  *                field j at bits [j*b, j*b + b) of the group's little-endian
- *                bit string (POC section 3: "uniform symmetric b-bit").
+ *                bit string (POC section 3: the residual grid is uniform and symmetric).
  *   resid_scales [d_out][G] fp16 bit patterns.
  *   sign_in      [d_in] int8, each +1 or -1 (S_i).
  *   sign_out     [d_out] int8 (S_o), or NULL: the output then stays in the
@@ -101,9 +101,17 @@ nl_status nested_linear_destroy(nl_handle h);
  * concurrently.  It must be zero-filled once before its first use: its
  * first 1 MiB holds the counters through which the workgroups of one launch
  * hand work to each other, and every call leaves them at zero again, so later
- * calls (of any linear, any T) need no clearing.  Its first 32-bit word counts waits
- * that ran into the kernels' spin limit; it stays zero unless the
- * workgroup-ordering assumption the launch relies on is broken.
+ * calls (of any linear, any T) need no clearing.
+ *
+ * Ordering assumption.  Inside one launch a workgroup only ever waits for
+ * workgroups of lower index (the activation rotation, split partial sums, the
+ * output rotation's inputs), and the GPU dispatches the workgroups of a
+ * launch in index order, so every awaited workgroup is running or done.
+ * Each wait is still bounded by a spin limit (about a tenth of a second).  A
+ * wait that gives up adds one to the workspace's first 32-bit word (the error
+ * word), the outputs it would have fed are written as NaN, and the launch
+ * ends normally; such a workspace must be reset with
+ * nested_linear_workspace_status(..., clear = 1) before its next use.
  */
 nl_status nested_linear_workspace_bytes(nl_handle h, int32_t T_max, size_t *bytes);
 
@@ -127,11 +135,76 @@ nl_status nested_linear_verify(nl_handle h, const void *x_bf16, int32_t T, float
                                void *ws, size_t ws_bytes, void *hip_stream);
 
 /*
- * Draft forward (POC section 4, "the same but without y_r"): as verify with
- * Q_resid omitted; only the base planes and base scales are read.
+ * Draft forward (POC section 4: the verifier without its residual term): as
+ * verify with Q_resid omitted; only the base planes and base scales are read.
  */
 nl_status nested_linear_draft(nl_handle h, const void *x_bf16, int32_t T, float *y,
                               void *ws, size_t ws_bytes, void *hip_stream);
+
+/*
+ * Verify / draft of n linears (1 <= n <= 4) that read the same activations,
+ * in one launch: y_i = linear i applied to x (for instance the q, k and v
+ * projections of an attention block, or the gate and up projections of an
+ * MLP).  The linears share d_in, the residual bits (verify), and the output
+ * rotation's presence and block; each keeps its own signs, planes, scales and
+ * levels, and each output ys[i] is [T][d_out_i] fp32.  ys is a host array of n
+ * device pointers.  The workspace must hold
+ * nested_linear_multi_workspace_bytes(hs, n, T) bytes; the other rules are
+ * those of nested_linear_verify.  The result equals n separate calls (each
+ * linear's contraction order is the same).
+ */
+nl_status nested_linear_verify_multi(const nl_handle *hs /* host array */, int32_t n, const void *x_bf16,
+                                     int32_t T, float *const *ys /* host array */, void *ws, size_t ws_bytes,
+                                     void *hip_stream);
+nl_status nested_linear_draft_multi(const nl_handle *hs, int32_t n, const void *x_bf16, int32_t T,
+                                    float *const *ys, void *ws, size_t ws_bytes, void *hip_stream);
+nl_status nested_linear_multi_workspace_bytes(const nl_handle *hs, int32_t n, int32_t T_max, size_t *bytes);
+
+/*
+ * Host query of the launch plan a verify or draft call would use (no device
+ * work, no handle needed): n linears of d_out[i] x d_in read by one call,
+ * bits = their residual bits for verify or 0 for the draft, two_sided != 0
+ * when they carry sign_out, T tokens.  out[0 .. 8 + 6 n) receives (truncated
+ * to out_len): local form (0/1), 16-token tiles, waves per workgroup,
+ * rotation / contraction / finish workgroups, LDS bytes per workgroup, bytes
+ * per x' chunk blob; then per linear: splits of K, chunks per split, row
+ * tiles per workgroup, waves per row tile, row blocks, output superblocks.
+ * Errors: NL_EINVAL.
+ */
+nl_status nested_linear_describe_call(const int32_t *d_out /* host array */, int32_t n, int32_t d_in, int32_t bits,
+                                      int32_t two_sided, int32_t T, int32_t *out /* host */, int32_t out_len);
+
+/*
+ * Reads the error word of a workspace (waits that gave up, see
+ * nested_linear_workspace_bytes) into *errors after synchronising hip_stream;
+ * with clear != 0 it then zeroes the workspace's counter region (its first
+ * MiB) and synchronises again, which makes a workspace usable after a call
+ * that reported errors.  Not for use inside graph capture (it synchronises).
+ * Errors: NL_EINVAL (NULL or misaligned pointers), NL_EHIP.
+ */
+nl_status nested_linear_workspace_status(void *ws, uint32_t *errors /* host */, int32_t clear, void *hip_stream);
+
+/*
+ * Tuning hook of the launch planner and the waits (process-wide, not
+ * thread-safe; results do not depend on it beyond the summation order of
+ * split-K partial sums).  value <= 0 restores a knob's default where a
+ * default exists.
+ */
+typedef enum {
+  NL_TUNE_SPLITS = 1,          /* force the split count of K (0: planner) */
+  NL_TUNE_ROW_TILES = 2,       /* force 16-row tiles per workgroup (0: planner) */
+  NL_TUNE_WAVES_PER_TILE = 3,  /* force waves sharing a row tile (0: planner) */
+  NL_TUNE_LOCAL_T = 4,         /* largest T rotated inside each workgroup (default 2; 0 disables) */
+  NL_TUNE_CUS = 5,             /* compute units the planner fills (default 256) */
+  NL_TUNE_LAT_US = 6,          /* planner: memory round trip under load, us (default 2) */
+  NL_TUNE_HBM_GBS = 7,         /* planner: HBM stream rate, GB/s (default 6500) */
+  NL_TUNE_SPLIT_US = 8,        /* planner: cost of a split-K reduction, us (default 1.5) */
+  NL_TUNE_XDMA_GBS = 9,        /* planner: per-CU rate of the x' copy into LDS, GB/s (default 100) */
+  NL_TUNE_SPIN_LIMIT = 10,     /* polls before a wait gives up (default 2^22) */
+  NL_TUNE_WAIT_EXTRA = 11,     /* test hook: added to every wait target, > 0 makes the waits give up */
+  NL_TUNE_WAVES = 12           /* waves per workgroup up to 16 tokens: 0 auto (8 draft, 12 verify), 8 or 12 */
+} nl_tuning;
+nl_status nested_linear_set_tuning(int32_t knob, double value);
 
 /*
  * The three stages of a draft/verify call as separate kernel launches, for
@@ -139,8 +212,8 @@ nl_status nested_linear_draft(nl_handle h, const void *x_bf16, int32_t T, float 
  * verify fuse them into one launch).  They must run in this order, on one
  * stream, with one workspace and the same T; they leave the workspace
  * counters untouched:
- *   prepare_input  x' = H_i S_i x into ws (POC section 1, "rotate the
- *                  activation once per Linear");
+ *   prepare_input  x' = H_i S_i x into ws (POC section 1: the activation
+ *                  is rotated a single time per linear and call);
  *   contract       y~ = Q x' from the packed planes (verify != 0 adds the
  *                  residual); writes partial sums into ws, or y directly
  *                  when the linear is one-sided and needs no reduction;
