@@ -55,7 +55,6 @@ def lib():
         L.nlo_resid_code.restype = i
         L.nlo_dequant_row.argtypes = [i, i, i, P, P, P, P, P, i, P]
         L.nlo_rotate_input.argtypes = [i, P, P, i, P]
-        L.nlo_rotate_output.argtypes = [i, P, i, P]
         L.nlo_forward_rows.argtypes = [i, i, i, i, P, P, P, P, P, P, P, P, i, i, i, P]
         L.nlo_forward_rows.restype = i
         L.nlo_decode.argtypes = [i, i, P, P, i, i, P, P]

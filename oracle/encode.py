@@ -49,7 +49,7 @@ QUANTILES = (0.125, 0.375, 0.625, 0.875)
 
 
 def rot_fwd(W, sign_in, sign_out=None) -> np.ndarray:
-    """W~ = H_o S_o W S_i H_i in fp64 (POC section 1, the math and rot_fwd):
+    """W~ = H_o S_o W S_i H_i in fp64 (POC section 1, "Rotation"):
     the input side first (each row times S_i, then the block Hadamard along
     d_in), then, in the two-sided form, the output side (each row times its
     S_o sign, then the block Hadamard along d_out)."""

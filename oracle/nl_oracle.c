@@ -156,17 +156,6 @@ void nlo_rotate_input(int d_in, const int8_t *sign_in, const uint16_t *x_bf16,
     }
 }
 
-/* Output rotation of POC section 1/4: y = S_o (H_o y~), in place on
- * y [T][d_out]. */
-void nlo_rotate_output(int d_out, const int8_t *sign_out, int T, double *y)
-{
-    for (int t = 0; t < T; ++t) {
-        double *v = y + (size_t)t * d_out;
-        nlo_fwht(v, d_out);
-        for (int r = 0; r < d_out; ++r) v[r] *= (double)sign_out[r];
-    }
-}
-
 /* The forward of one nested Linear for rows [row0, row1) (POC section 4):
  *   x'  = H_i S_i x
  *   y~  = W~ x'           (W~ in verify mode includes the residual)

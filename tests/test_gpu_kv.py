@@ -72,8 +72,8 @@ def test_write_matches_oracle(nl, torch_cuda):
 # (T, H_q, H_kv, L): a single row; GQA with a ragged sub-chunk; the 8B-class
 # heads; 256 query rows per KV head (four row blocks); 80 rows (a partial
 # second row block); positions ending exactly on a sub-chunk boundary; a
-# context that spans several 64-key sub-chunks per workgroup; 32 rows (two
-# computing waves of a two-wave workgroup)
+# context that spans several 64-key sub-chunks per workgroup; 32 rows (two of
+# the four waves of a row block hold live rows)
 CASES = [(1, 8, 8, 0), (5, 6, 2, 64), (16, 32, 8, 1000), (64, 4, 1, 300), (16, 32, 8, 4096), (3, 2, 2, 127),
          (20, 8, 2, 777), (16, 4, 4, 2032), (2, 4, 1, 9000), (8, 12, 3, 500)]
 

@@ -413,11 +413,12 @@ def test_grouped_partial_workgroups(nl, torch_cuda):
         assert rel_err(a, oracle.forward_grouped(experts, pt, off, x, verify)) <= TOL
 
 
-@pytest.mark.parametrize("T", [1, 4])
+@pytest.mark.parametrize("T", [1, 2, 4])
 @pytest.mark.parametrize("two", [False, True])
 def test_grouped_few_tokens(nl, torch_cuda, T, two):
-    # a block of at most 4 tokens: each contraction workgroup rotates its
-    # expert's rows itself
+    # with at most 2 tokens each contraction workgroup rotates its expert's
+    # rows itself (T = 2 is that form's limit); T = 4 takes the rotation
+    # workgroups
     experts, pt, off = make_moe(16, 512, 2048, 8, T, 4, 0.62, two, cfg=75 + T)
     x = synth.make_x(T, 2048, cfg=75, idx=T)
     for verify in (False, True):

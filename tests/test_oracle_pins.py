@@ -316,3 +316,70 @@ def test_residual_codes_in_range():
         q = synth.make_resid_codes(64, 512, bits, cfg=96, idx=bits)
         qm = (1 << (bits - 1)) - 1
         assert q.min() >= -qm and q.max() <= qm
+
+
+# --- the grouped (mixture-of-experts) forward ("The verify's own cost") -------
+#
+# Pair p, routed to expert e by offsets[e] <= p < offsets[e+1], is expert e's
+# Linear applied to token pair_token[p].  The pins below hold forward_grouped to
+# that definition through the dense brute force and through unit inputs that
+# pick known columns, so a wrong expert, a wrong token or a shifted offset fails.
+
+def _unit_rows(lin, js):
+    """Rows x_t = S_i H_i e_{j_t} (so x' = e_j), exact in bf16 for b a power of 4."""
+    d_in = lin["d_in"]
+    b = _bs(d_in)
+    X = np.zeros((len(js), d_in))
+    for t, j in enumerate(js):
+        blk = j // b
+        X[t, blk * b:(blk + 1) * b] = sylvester(b)[:, j % b]
+    X = X * lin["sign_in"]
+    xb = synth.f32_to_bf16_bits(X.astype(np.float32))
+    assert np.array_equal(synth.bf16_bits_to_f32(xb).astype(np.float64), X)
+    return xb
+
+
+@pytest.mark.parametrize("verify", [False, True])
+def test_grouped_equals_per_pair_brute_force(orc, verify):
+    d_out, d_in, bits = 48, 256, 7
+    experts = [synth.make_linear(d_out, d_in, bits, cfg=95, idx=e, two_sided=e == 1, keep_codes=True)
+               for e in range(4)]
+    # expert 2 gets no pairs; token 3 is routed twice; tokens appear out of order
+    offsets = np.array([0, 3, 5, 5, 8])
+    pair_token = np.array([4, 0, 3, 3, 1, 2, 0, 4])
+    x = synth.make_x(5, d_in, cfg=95, idx=0)
+    y = orc.forward_grouped(experts, pair_token, offsets, x, verify)
+    assert y.shape == (8, d_out)
+    for e in range(4):
+        for p in range(offsets[e], offsets[e + 1]):
+            ref = brute_force(experts[e], x[pair_token[p]:pair_token[p] + 1], verify)[0]
+            np.testing.assert_allclose(y[p], ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+
+
+def test_grouped_unit_inputs_return_each_experts_column(orc):
+    # Every token is a unit input e_j; pair p of expert e must return column
+    # j(pair_token[p]) of expert e's W~, which differs between experts.
+    d_in = 1024
+    experts = [synth.make_linear(32, d_in, 8, cfg=96, idx=e, two_sided=False, keep_codes=True) for e in range(3)]
+    for lin in experts[1:]:                       # one sign vector for all (x is shared)
+        lin["sign_in"] = experts[0]["sign_in"]
+    js = [7, 1000, 0, 513]
+    x = _unit_rows(experts[0], js)
+    offsets = np.array([0, 2, 2, 6])               # the middle expert is empty
+    pair_token = np.array([3, 1, 0, 1, 2, 3])
+    y = orc.forward_grouped(experts, pair_token, offsets, x, True)
+    for e in range(3):
+        W = dense_weights(experts[e], True)
+        for p in range(offsets[e], offsets[e + 1]):
+            np.testing.assert_allclose(y[p], W[:, js[pair_token[p]]], rtol=1e-14, atol=1e-300)
+
+
+def test_grouped_single_expert_holding_every_pair(orc):
+    lin = synth.make_linear(40, 512, 6, cfg=97, idx=0, keep_codes=True)
+    x = synth.make_x(6, 512, cfg=97, idx=0)
+    pair_token = np.array([5, 5, 2, 0, 1, 3, 4])
+    y = orc.forward_grouped([lin], pair_token, np.array([0, 7]), x, True)
+    np.testing.assert_allclose(y, brute_force(lin, x[pair_token], True), rtol=0,
+                               atol=1e-12 * np.abs(y).max())
+    # no pairs at all: an empty result of the right width
+    assert orc.forward_grouped([lin], np.zeros(0, np.int64), np.array([0, 0]), x, False).shape == (0, 40)
