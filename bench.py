@@ -1,25 +1,25 @@
 #!/usr/bin/env python3
 """Benchmark of the bit-nested quantized linear on one MI355X.
 
-Workload: the 7B/8B-class projections (4096x4096, 1024x4096, 14336x4096,
-4096x14336), 2-bit Lloyd-Max base + 6-bit residual with fp16 group-128
-scales, bf16 N(0,1) activations, in the one-sided form y = (Q_b + Q_r) H S x.
-One step = a draft and a verify pass over all four projections at each of
-T = 1, 4, 8, 16 and 32 draft-tree tokens (40 calls, one kernel launch each),
-captured in one HIP graph.  Weights rotate through a pool of distinct copies
-larger than the 256 MB Infinity Cache, so every call streams its weights from
-HBM.  Inputs are resident in HBM before the timed region.
+Workload of the headline: the 7B/8B-class projections (4096x4096, 1024x4096,
+14336x4096, 4096x14336), 2-bit Lloyd-Max base + 6-bit residual with fp16
+group-128 scales, bf16 N(0,1) activations, one-sided y = (Q_b + Q_r) H S x.
+One step = a verify pass over the four projections at each of T = 1, 4, 8,
+16 and 32 draft-tree tokens (20 calls, one kernel launch each), captured in
+one HIP graph.  Weights rotate through a pool of distinct copies larger than
+the 256 MB Infinity Cache, so every call streams its weights from HBM.
+Inputs are resident in HBM before the timed region.
 
-value = effective weight GB/s of a step: algorithmic bytes (codes + fp16
-scales: 0.265625 B/weight draft, 1.03125 B/weight verify) over the step time.
-per_case gives the microseconds per pass over the four projections and the
-weight GB/s for T = 1, 4, 8, 16, 32 and 64 (graph-amortised), the
-launch-inclusive time of one eager call, and the two-sided form at T = 1, 16.
-decoder_layer sums the seven calls of one layer (q, k, v, o, gate, up, down)
-from those per-shape times; model_pass times whole passes as one graph each:
-the Llama-8B-shaped one (7-bit, T = 16, lm_head included) and the 31B-class
-dense one (8-bit, 64 layers, draft at T = 1, verify at T = 64); moe_block times
-one MoE block of grouped calls.
+value = effective weight GB/s of the verify step: algorithmic bytes (codes +
+fp16 scales, 1.03125 B/weight at 6 bits) over the step time.  per_case gives,
+for verify and draft at T = 1, 4, 8, 16, 32 and 64, the microseconds per pass
+over the four projections (median, p10, p90 over graph replays), the weight
+GB/s and its fraction of the 8 TB/s peak and of the measured streaming-read
+reference, and max|dy| / max|y_oracle| of that case on sampled rows.  Further
+rows: the 1024x1024 int8 linear, the two-sided form, one decoder layer with
+q/k/v and gate/up fused into one launch each, whole Llama-8B-shaped and
+31B-class passes, the MoE block (correlated and iid routing), and the NEXT
+formats (W4/W8 planes, draft tree, nested KV, encoder).
 Prints one JSON line on stdout; progress goes to stderr.
 """
 import argparse
@@ -32,7 +32,8 @@ import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-sys.path.insert(0, ROOT)
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
 
 SHAPES = [("q/o", 4096, 4096), ("k/v", 1024, 4096), ("gate/up", 14336, 4096), ("down", 4096, 14336)]
 STEP_TS = [1, 4, 8, 16, 32]
@@ -40,9 +41,17 @@ CASE_TS = [1, 4, 8, 16, 32, 64]
 BITS = 6
 HBM_PEAK_GBPS = 8000.0
 LAYERS = 32             # decoder layers of the 7B/8B-class model
-ROOFLINE_TS = (8, 16)   # verify launches of forward_kernel<6, 1, 4> (one 16-token tile, rotation workgroups)
-ROOFLINE_KERNEL = "forward_kernel<6, 1, 4>"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "forward_kernel_6bit_verify_T8_T16_proj7b8b_traffic.txt")
+ERR_ROWS = 512          # output rows per projection checked against the oracle in each case
+ROOFLINE_TS = (8, 16)   # launches of the roofline kernels (one 16-token tile, rotation workgroups)
+FWD_SOURCES = ("nl_fwd.hip", "nl_fwd.h", "nl_dev.h", "nl_layout.h")
+ROOF = {  # mode -> (kernel, bits, waves, traffic summary)
+    "verify": ("fwd_kernel<6, 1, 12, false>", 6, 12,
+               os.path.join(ROOT, "profiles", "fwd_kernel_6bit_verify_T8_T16_proj7b8b_traffic.txt")),
+    "draft": ("fwd_kernel<0, 1, 8, false>", 0, 8,
+              os.path.join(ROOT, "profiles", "fwd_kernel_draft_T8_T16_proj7b8b_traffic.txt")),
+}
+UTIL_FILE = os.path.join(ROOT, "profiles", "fwd_kernel_utilisation_T8_T16_proj7b8b.txt")
+STREAM_BYTES = 4 << 30  # streaming-read reference buffer (16x the Infinity Cache)
 ENC_BITS = 7            # the encoder leg writes 7-bit residuals (the post's bf16-noise-floor width)
 ENC_KERNEL = "tile_kernel<0, 7,"   # fused 7-bit encode, any block size (kernel-name match)
 ENC_KERNEL_NAME = "tile_kernel<0, 7, LOG2B>"
@@ -63,7 +72,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_digest(files=("nl_kernels.hip", "nl_kernels.h", "nl_layout.h")):
+def kernel_source_digest(files=FWD_SOURCES):
     """Digest of the kernel sources, to tie stored counter readings to them."""
     h = hashlib.sha256()
     for f in files:
@@ -75,10 +84,9 @@ def kernel_source_digest(files=("nl_kernels.hip", "nl_kernels.h", "nl_layout.h")
 ENC_SOURCES = ("nl_encode.hip",)
 
 
-def stored_traffic(digest, path=None):
-    """HBM bytes per launch of the roofline kernel from the committed counter
-    summary, when it was taken on the current kernel sources."""
-    path = TRAFFIC_FILE if path is None else path
+def stored_traffic(digest, path):
+    """HBM bytes per launch of a kernel from its committed counter summary,
+    when the summary was taken on the current kernel sources."""
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -89,30 +97,278 @@ def stored_traffic(digest, path=None):
     return float(m_val.group(1))
 
 
-MOE_EXPERTS, MOE_HIDDEN, MOE_INTER, MOE_TOPK, MOE_T, MOE_BITS, MOE_RHO = 256, 2048, 512, 8, 16, 8, 0.62
-# whole-model passes: (name, layer shapes q k v o gate up down, layers, residual bits, verify T, draft T,
-# lm_head shape or None, synthetic config id)
+def pstats(samples):
+    """Median, p10 and p90 of a list of microsecond samples."""
+    import numpy as np
+    a = np.asarray(samples, np.float64)
+    return {"us": round(float(np.median(a)), 2), "p10": round(float(np.percentile(a, 10)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2), "samples": int(a.size)}
+
+
+def replay_samples(torch, g, reps):
+    """Per-replay microseconds of a captured graph: one event pair around each
+    of `reps` back-to-back replays (after one untimed replay)."""
+    g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e3 for a, b in ev]
+
+
+def capture(torch, fn):
+    """fn(stream) once eagerly on a side stream (warm-up), then captured."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn(torch.cuda.current_stream())
+    return g
+
+
+def rate(bytes_, us, stream_gbps):
+    gbps = bytes_ / us / 1e3
+    return {"GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+            "frac_stream_ref": None if not stream_gbps else round(gbps / stream_gbps, 4)}
+
+
+def rel_err(y, ref):
+    import numpy as np
+    return float(np.abs(y.astype(np.float64) - ref).max() / max(float(np.abs(ref).max()), 1e-300))
+
+
+def dev_arrays(torch, lin):
+    import numpy as np
+    return {k: (None if lin[k] is None else torch.from_numpy(np.ascontiguousarray(lin[k]).view(dt)).cuda())
+            for k, dt in [("base_codes", np.uint8), ("base_scales", np.int16), ("resid_codes", np.uint8),
+                          ("resid_scales", np.int16), ("sign_in", np.int8), ("sign_out", np.int8)]}
+
+
+def check_status(nl, ws, what):
+    """A wait that gave up would leave NaN outputs and a nonzero error word."""
+    e = nl.nested_linear_workspace_status(ws)
+    if e:
+        raise SystemExit(f"bench: {e} wait(s) gave up in {what}")
+
+
+# --- the streaming-read reference ---------------------------------------------
+
+def stream_ref_leg(nl, torch, reps=8):
+    """Read rate of a plain hand-written streaming-read kernel (16-byte
+    nontemporal loads, nothing computed) over a 4 GiB buffer: the measured
+    ceiling the weight streams are set against."""
+    src = torch.ones(STREAM_BYTES // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1 << 20, dtype=torch.int32, device="cuda")
+    out = {}
+    for grid in (1024, 2048, 4096):
+        nl.nested_linear_stream_read(src, sink, grid)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            nl.nested_linear_stream_read(src, sink, grid)
+        e1.record()
+        e1.synchronize()
+        out[grid] = STREAM_BYTES * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, sink
+    torch.cuda.empty_cache()
+    best = max(out, key=out.get)
+    log(f"[bench] streaming-read reference: {out[best]:.0f} GB/s (grid {best})")
+    return {"GBps": round(out[best], 1), "frac_hbm_peak": round(out[best] / HBM_PEAK_GBPS, 4),
+            "kernel": "stream_read_kernel (16-byte nontemporal loads, 8 per lane in flight, 256 threads)",
+            "bytes": STREAM_BYTES, "grid": best, "by_grid": {str(k): round(v, 1) for k, v in out.items()}}
+
+
+# --- the roofline kernels -------------------------------------------------------
+
+def roofline_leg(nl, call, ncopy, stream, bpw, mode):
+    """Roofline of one forward kernel: eager launches at T = 8 and 16 over the
+    four projections (every one of them runs that kernel), each timed by a
+    HIP event pair attached to its own dispatch (the library's timing hook),
+    so a duration is the kernel's execution as the kernel trace reports it."""
+    import torch
+    kernel, bits, waves, traffic_file = ROOF[mode]
+    verify = mode == "verify"
+    for _, o, i in SHAPES:
+        for T in ROOFLINE_TS:
+            p = nl.nested_linear_describe_call([o], i, bits, False, T)
+            assert p["mt"] == 1 and not p["local"] and p["waves"] == waves, (o, i, T, p)
+    plan = []
+    for si, (name, o, i) in enumerate(SHAPES):
+        for T in ROOFLINE_TS:
+            for r in range(2):
+                for cp in range(ncopy):
+                    plan.append((si, cp, T, o * i * bpw(verify)))
+    for si, cp, T, _ in plan[:8]:          # warm the code objects
+        call(si, cp, T, verify, stream)
+    torch.cuda.synchronize()
+    nl.nested_linear_timing_begin(len(plan))
+    for si, cp, T, _ in plan:
+        call(si, cp, T, verify, stream)
+    durs = nl.nested_linear_timing_end(len(plan))
+    assert len(durs) == len(plan), (len(durs), len(plan))
+    avg_us = sum(durs) / len(durs)
+    avg_bytes = sum(b for *_, b in plan) / len(plan)
+    achieved = avg_bytes / avg_us / 1e3
+    digest = kernel_source_digest()
+    traffic = stored_traffic(digest, traffic_file)
+    log(f"[bench] roofline {kernel}: {avg_us:.2f} us/launch, {achieved:.0f} GB/s")
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None if traffic is None else round(traffic),
+            "kernel": f"{kernel} ({mode}, T = 8 and 16, the four projections)",
+            "avg_launch_us": round(avg_us, 2), "avg_algorithmic_bytes": int(avg_bytes),
+            "launches": len(durs), "timing": "HIP events attached to each dispatch",
+            "kernel_source_digest": digest}
+
+
+# --- the 1024x1024 int8 linear ----------------------------------------------------
+
+def single1024_leg(nl, torch, synth, reps, stream_gbps, pool_bytes=512 << 20):
+    """1024x1024 linear with an int8 residual, verify and draft at T = 1 and
+    16; a graph of calls over a pool of copies (so weights come from HBM)."""
+    import numpy as np
+    import oracle
+    lin = synth.make_linear(1024, 1024, 8, cfg=0, idx=0, two_sided=False)
+    d = dev_arrays(torch, lin)
+    bpw8 = synth.bytes_per_weight(8)
+    ncopy = max(2, math.ceil(pool_bytes / (1024 * 1024 * bpw8)))
+    hs = [nl.nested_linear_create(1024, 1024, 8, levels=lin["levels"], **d) for _ in range(ncopy)]
+    del d
+    x = synth.make_x(16, 1024, cfg=0, idx=16)
+    xd = torch.from_numpy(x.view(np.int16)).cuda()
+    ws = torch.zeros(nl.nested_linear_workspace_bytes(hs[0], 16), dtype=torch.uint8, device="cuda")
+    y = torch.empty((16, 1024), dtype=torch.float32, device="cuda")
+    out = {"workload": "1024x1024, 2-bit base + int8 residual, one-sided", "pool_copies": ncopy}
+    for T in (1, 16):
+        for verify in (True, False):
+            fn = nl.nested_linear_verify if verify else nl.nested_linear_draft
+            fn(hs[0], xd, T, y, ws)
+            check_status(nl, ws, "1024x1024")
+            err = rel_err(y[:T].cpu().numpy(), oracle.forward(lin, x[:T], verify))
+
+            def calls(s):
+                for h in hs:
+                    fn(h, xd, T, y, ws, s)
+
+            g = capture(torch, calls)
+            st = pstats([u / ncopy for u in replay_samples(torch, g, reps)])
+            del g
+            b = 1024 * 1024 * synth.bytes_per_weight(8 if verify else 0)
+            out[f"{'verify' if verify else 'draft'}_T{T}"] = dict(st, **rate(b, st["us"], stream_gbps),
+                                                                  max_rel_err=float(f"{err:.3g}"))
+            log(f"[bench] 1024x1024 {'verify' if verify else 'draft'} T={T}: {st['us']:.2f} us")
+    check_status(nl, ws, "1024x1024")
+    for h in hs:
+        nl.nested_linear_destroy(h)
+    return out
+
+
+# --- a decoder layer with fused launches ---------------------------------------------
+
+LAYER = [("q", 4096, 4096), ("k", 1024, 4096), ("v", 1024, 4096), ("o", 4096, 4096), ("gate", 14336, 4096),
+         ("up", 14336, 4096), ("down", 4096, 14336)]
+
+
+def make_layer_launches(nl, torch, handles, xs, ys, ws, T, verify):
+    """The four launches of one decoder layer: q, k, v fused (one launch on
+    the shared input), o, gate and up fused, down.  handles: dict name -> h."""
+    single = nl.nested_linear_verify if verify else nl.nested_linear_draft
+    multi = nl.nested_linear_verify_multi if verify else nl.nested_linear_draft_multi
+
+    def run(s):
+        multi([handles["q"], handles["k"], handles["v"]], xs[4096], T, [ys["q"], ys["k"], ys["v"]], ws, s)
+        single(handles["o"], xs[4096], T, ys["o"], ws, s)
+        multi([handles["gate"], handles["up"]], xs[4096], T, [ys["gate"], ys["up"]], ws, s)
+        single(handles["down"], xs[14336], T, ys["down"], ws, s)
+    return run
+
+
+def layer_workspace_bytes(nl, h, T):
+    return max(nl.nested_linear_multi_workspace_bytes([h["q"], h["k"], h["v"]], T),
+               nl.nested_linear_multi_workspace_bytes([h["gate"], h["up"]], T),
+               nl.nested_linear_workspace_bytes(h["o"], T), nl.nested_linear_workspace_bytes(h["down"], T))
+
+
+def decoder_layer_leg(nl, torch, synth, reps, stream_gbps, pool_gib):
+    """One decoder layer of the 7B/8B-class model, 6-bit: q/k/v fused into one
+    launch and gate/up into another (they share their input), o and down
+    alone; layers rotate through a pool of copies; verify and draft at T = 1
+    and 16 (and verify at 32 and 64)."""
+    import numpy as np
+    import oracle
+    bpw = lambda v: synth.bytes_per_weight(BITS if v else 0)
+    layer_bytes = sum(o * i for _, o, i in LAYER) * bpw(True)
+    ncopy = max(2, math.ceil(pool_gib * 2 ** 30 / layer_bytes))
+    lins = {name: synth.make_linear(o, i, BITS, cfg=5, idx=k, two_sided=False) for k, (name, o, i) in enumerate(LAYER)}
+    pool = []
+    for _ in range(ncopy):
+        pool.append({name: nl.nested_linear_create(lin["d_out"], lin["d_in"], BITS, levels=lin["levels"],
+                                                   **dev_arrays(torch, lin)) for name, lin in lins.items()})
+    xh = {4096: synth.make_x(64, 4096, cfg=5, idx=100), 14336: synth.make_x(64, 14336, cfg=5, idx=101)}
+    xs = {k: torch.from_numpy(v.view(np.int16)).cuda() for k, v in xh.items()}
+    ys = {name: torch.empty((64, o), dtype=torch.float32, device="cuda") for name, o, _ in LAYER}
+    ws = torch.zeros(layer_workspace_bytes(nl, pool[0], 64), dtype=torch.uint8, device="cuda")
+    out = {"linears": "q, k, v fused (4096+1024+1024 x 4096); o 4096x4096; gate, up fused (2 x 14336x4096); "
+                      "down 4096x14336; four launches per layer", "layers": LAYERS, "pool_copies": ncopy}
+    for T in (1, 16, 32, 64):
+        for verify in ((True, False) if T <= 16 else (True,)):
+            run0 = make_layer_launches(nl, torch, pool[0], xs, ys, ws, T, verify)
+            run0(torch.cuda.current_stream())
+            check_status(nl, ws, "decoder layer")
+            err = 0.0
+            for name, o, i in LAYER:
+                ref = oracle.forward(lins[name], xh[i][:T], verify, rows=(0, ERR_ROWS))
+                err = max(err, rel_err(ys[name][:T, :ERR_ROWS].cpu().numpy(), ref))
+            runs = [make_layer_launches(nl, torch, p, xs, ys, ws, T, verify) for p in pool]
+            g = capture(torch, lambda s: [r(s) for r in runs])
+            st = pstats([u / ncopy for u in replay_samples(torch, g, reps)])
+            del g
+            key = f"{'verify' if verify else 'draft'}_T{T}"
+            out[key] = dict(st, **rate(sum(o * i for _, o, i in LAYER) * bpw(verify), st["us"], stream_gbps),
+                            ms_per_model=round(st["us"] * LAYERS / 1e3, 3), max_rel_err=float(f"{err:.3g}"))
+            log(f"[bench] decoder layer {key}: {st['us']:.1f} us ({out[key]['GBps']:.0f} GB/s)")
+    check_status(nl, ws, "decoder layer")
+    for p in pool:
+        for h in p.values():
+            nl.nested_linear_destroy(h)
+    torch.cuda.empty_cache()
+    return out
+
+
+# --- whole dense-model passes ---------------------------------------------------------
+
+# (name, layer shapes q k v o gate up down, layers, residual bits, verify T, draft T, lm_head shape or None,
+# synthetic config id)
 MODELS = [
     ("llama8b_shaped", [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096), (14336, 4096), (14336, 4096),
                         (4096, 14336)], 32, 7, 16, 16, (128256, 4096), 2),
     ("dense31b_class", [(5120, 5120), (1024, 5120), (1024, 5120), (5120, 5120), (25600, 5120), (25600, 5120),
                         (5120, 25600)], 64, 8, 64, 1, None, 3),
 ]
-MOE_ROUTINGS = 8
 
 
-def model_leg(nl, torch, synth, reps, spec):
-    """Verify and draft passes over every linear weight of a dense model,
-    each captured as one graph: per layer q, k, v, o, gate, up, down, then
-    the lm_head if there is one.  Every linear owns its own device copy of
-    its planes, made from one synthetic linear per shape (values do not
-    change the work); an lm_head repeats the codes of a generated 4096-row
-    block with per-row scales."""
+def model_leg(nl, torch, synth, reps, spec, stream_gbps):
+    """Verify and draft passes over every linear weight of a dense model, each
+    captured as one graph: per layer q/k/v as one fused launch, o, gate/up as
+    one fused launch, down, then the lm_head if there is one.  Every linear
+    owns its own device copy of its planes, made from one synthetic linear
+    per shape (values do not change the work); an lm_head repeats the codes
+    of a generated 4096-row block with per-row scales."""
     import numpy as np
+    import oracle
     name, layer, n_layers, bits, t_verify, t_draft, head, cfg = spec
 
     def make(o, i, idx):
-        if o <= 2 * 4096 or (o, i) != head:
+        if (o, i) != head:
             return synth.make_linear(o, i, bits, cfg=cfg, idx=idx, two_sided=False)
         lin = dict(synth.make_linear(4096, i, bits, cfg=cfg, idx=idx, two_sided=False))
         lin["d_out"] = o
@@ -122,187 +378,162 @@ def model_leg(nl, torch, synth, reps, spec):
         lin["resid_scales"] = synth.make_scales(o, i, cfg, idx, synth.STREAM_RESID_SCALE)
         return lin
 
+    names = ["q", "k", "v", "o", "gate", "up", "down"]
     shapes = sorted(set(layer) | ({head} if head else set()))
-    dev = {}
-    for si, (o, i) in enumerate(shapes):
-        lin = make(o, i, si)
-        dev[(o, i)] = (lin["levels"], {
-            key: (None if lin[key] is None else torch.from_numpy(np.ascontiguousarray(lin[key]).view(dt)).cuda())
-            for key, dt in [("base_codes", np.uint8), ("base_scales", np.int16), ("resid_codes", np.uint8),
-                            ("resid_scales", np.int16), ("sign_in", np.int8), ("sign_out", np.int8)]})
-        del lin
-    seq = [s_ for _ in range(n_layers) for s_ in layer] + ([head] if head else [])
-    handles = [nl.nested_linear_create(o, i, bits, levels=dev[(o, i)][0], **dev[(o, i)][1]) for o, i in seq]
+    lins = {sh: make(*sh, si) for si, sh in enumerate(shapes)}
+    dev = {sh: dev_arrays(torch, lin) for sh, lin in lins.items()}
+    layers = [{n: nl.nested_linear_create(o, i, bits, levels=lins[(o, i)]["levels"], **dev[(o, i)])
+               for n, (o, i) in zip(names, layer)} for _ in range(n_layers)]
+    hh = nl.nested_linear_create(*head, bits, levels=lins[head]["levels"], **dev[head]) if head else None
     del dev
     t_max = max(t_verify, t_draft)
-    first = {}
-    for h, sh in zip(handles, seq):
-        first.setdefault(sh, h)
-    ws = torch.zeros(max(nl.nested_linear_workspace_bytes(h, t_max) for h in first.values()),
-                     dtype=torch.uint8, device="cuda")
-    xs = {i: torch.from_numpy(synth.make_x(t_max, i, cfg=cfg, idx=200 + i).view(np.int16)).cuda()
-          for i in sorted({i for _, i in shapes})}
-    ys = {o: torch.empty((t_max, o), dtype=torch.float32, device="cuda") for o, _ in shapes}
-    out = {"linears": len(seq), "layers": n_layers,
+    hidden, inter = layer[0][1], layer[6][1]
+    ws_b = layer_workspace_bytes(nl, layers[0], t_max)
+    if hh is not None:
+        ws_b = max(ws_b, nl.nested_linear_workspace_bytes(hh, t_max))
+    ws = torch.zeros(ws_b, dtype=torch.uint8, device="cuda")
+    xh = {i: synth.make_x(t_max, i, cfg=cfg, idx=200 + i) for i in sorted({i for _, i in shapes})}
+    xs = {i: torch.from_numpy(v.view(np.int16)).cuda() for i, v in xh.items()}
+    ys = {n: torch.empty((t_max, o), dtype=torch.float32, device="cuda") for n, (o, _) in zip(names, layer)}
+    yh = torch.empty((t_max, head[0]), dtype=torch.float32, device="cuda") if head else None
+    seq = [sh for _ in range(n_layers) for sh in layer] + ([head] if head else [])
+    out = {"linears": len(seq), "layers": n_layers, "launches_per_pass": 4 * n_layers + (1 if head else 0),
            "workload": f"{name}: {n_layers} layers of q, k, v, o, gate, up, down ("
                        + ", ".join(f"{o}x{i}" for o, i in layer) + ")"
                        + (f" + lm_head {head[0]}x{head[1]}" if head else "")
-                       + f", {bits}-bit residual; verify at T = {t_verify}, draft at T = {t_draft}; one graph per pass"}
+                       + f", {bits}-bit residual; verify at T = {t_verify}, draft at T = {t_draft}; "
+                         "q/k/v and gate/up fused into one launch each; one graph per pass"}
     for verify in (True, False):
-        fn = nl.nested_linear_verify if verify else nl.nested_linear_draft
         T = t_verify if verify else t_draft
+        single = nl.nested_linear_verify if verify else nl.nested_linear_draft
+        multi = nl.nested_linear_verify_multi if verify else nl.nested_linear_draft_multi
 
-        def passes(st):
-            for h, (o, i) in zip(handles, seq):
-                fn(h, xs[i], T, ys[o], ws, st)
+        def passes(s):
+            for L in layers:
+                multi([L["q"], L["k"], L["v"]], xs[hidden], T, [ys["q"], ys["k"], ys["v"]], ws, s)
+                single(L["o"], xs[hidden], T, ys["o"], ws, s)
+                multi([L["gate"], L["up"]], xs[hidden], T, [ys["gate"], ys["up"]], ws, s)
+                single(L["down"], xs[inter], T, ys["down"], ws, s)
+            if hh is not None:
+                single(hh, xs[head[1]], T, yh, ws, s)
 
-        g = torch.cuda.CUDAGraph()
-        st = torch.cuda.Stream()
-        st.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(st):
-            passes(st)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            passes(torch.cuda.current_stream())
-        g.replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            g.replay()
-        e1.record()
-        e1.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
-        wb = sum(o * i for o, i in seq) * synth.bytes_per_weight(bits if verify else 0)
-        out["verify" if verify else "draft"] = {"T": T, "us_per_pass": round(us, 1), "weight_bytes": int(wb),
-                                                "GBps": round(wb / us / 1e3, 1),
-                                                "frac_hbm_peak": round(wb / us / 1e3 / HBM_PEAK_GBPS, 3)}
+        passes(torch.cuda.current_stream())
+        check_status(nl, ws, name)
+        err = 0.0
+        for n, (o, i) in zip(names, layer):      # the last layer's outputs, sampled rows
+            ref = oracle.forward(lins[(o, i)], xh[i][:T], verify, rows=(0, ERR_ROWS))
+            err = max(err, rel_err(ys[n][:T, :ERR_ROWS].cpu().numpy(), ref))
+        if head:
+            ref = oracle.forward(lins[head], xh[head[1]][:T], verify, rows=(0, ERR_ROWS))
+            err = max(err, rel_err(yh[:T, :ERR_ROWS].cpu().numpy(), ref))
+        g = capture(torch, passes)
+        st = pstats(replay_samples(torch, g, reps))
         del g
-    for h in handles:
-        nl.nested_linear_destroy(h)
+        wb = sum(o * i for o, i in seq) * synth.bytes_per_weight(bits if verify else 0)
+        out["verify" if verify else "draft"] = dict({"T": T, "us_per_pass": st["us"], "p10": st["p10"],
+                                                     "p90": st["p90"], "weight_bytes": int(wb)},
+                                                    **rate(wb, st["us"], stream_gbps),
+                                                    max_rel_err=float(f"{err:.3g}"))
+    check_status(nl, ws, name)
+    for L in layers:
+        for h in L.values():
+            nl.nested_linear_destroy(h)
+    if hh is not None:
+        nl.nested_linear_destroy(hh)
     torch.cuda.empty_cache()
     return out
 
 
-def moe_leg(nl, torch, synth, reps):
+# --- the MoE block -----------------------------------------------------------------------
+
+MOE_EXPERTS, MOE_HIDDEN, MOE_INTER, MOE_TOPK, MOE_T, MOE_BITS = 256, 2048, 512, 8, 16, 8
+MOE_ROUTINGS = 8
+
+
+def moe_leg(nl, torch, synth, reps, stream_gbps):
     """MoE block verify and draft: 256 routed experts (hidden 2048, expert
-    intermediate 512) plus one shared expert, top-8 routing of a 16-token block
-    with correlated router logits, 2-bit base + 8-bit residual; one grouped
-    call per projection (gate, up, down).  Every expert owns its own device
-    copy of its planes (all made from one synthetic linear per shape: values
-    do not change the work), and passes cycle through 8 routings so the 1 GB
-    expert set streams from HBM."""
+    intermediate 512) plus one shared expert, top-8 routing of a 16-token
+    block, 2-bit base + 8-bit residual; one grouped call per projection.  Gate
+    and up read the block's 16 token rows; down reads each pair's own
+    512-wide row (P rows, pair_token = 0..P-1).  Two routings: router logits
+    correlated across the block (rho = 0.62, about 47 experts awake) and iid
+    (rho = 0, about 102).  Every expert owns its own device copy of its planes
+    and passes cycle through 8 routings so the expert set streams from HBM."""
     import numpy as np
+    import oracle
     n = MOE_EXPERTS + 1
     shapes = {"gate": (MOE_INTER, MOE_HIDDEN), "up": (MOE_INTER, MOE_HIDDEN), "down": (MOE_HIDDEN, MOE_INTER)}
-    groups, handles = {}, []
+    groups, handles, lins = {}, [], {}
     for k, (o, i) in shapes.items():
         lin = synth.make_linear(o, i, MOE_BITS, cfg=4, idx=len(groups), two_sided=False)
-        d = {key: (None if lin[key] is None else torch.from_numpy(np.ascontiguousarray(lin[key]).view(dt)).cuda())
-             for key, dt in [("base_codes", np.uint8), ("base_scales", np.int16), ("resid_codes", np.uint8),
-                             ("resid_scales", np.int16), ("sign_in", np.int8), ("sign_out", np.int8)]}
+        lins[k] = lin
+        d = dev_arrays(torch, lin)
         hs = [nl.nested_linear_create(o, i, MOE_BITS, levels=lin["levels"], **d) for _ in range(n)]
         handles += hs
         groups[k] = nl.nested_linear_group_create(hs)
         del d
-    routes = []
-    for r in range(MOE_ROUTINGS):
-        _, pt, off = synth.router_topk(MOE_T, MOE_EXPERTS, MOE_TOPK, MOE_RHO, cfg=4, idx=r)
-        pt = np.concatenate([pt, np.arange(MOE_T, dtype=np.int32)]).astype(np.int32)   # shared expert last
-        off = np.concatenate([off, [off[-1] + MOE_T]]).astype(np.int32)
-        P = len(pt)
-        active = int(np.count_nonzero(np.diff(off)))
-        routes.append((torch.from_numpy(pt).cuda(), torch.from_numpy(off).cuda(), P, active))
-    Pmax = max(r[2] for r in routes)
-    ws = {k: torch.zeros(nl.nested_linear_group_workspace_bytes(g, Pmax), dtype=torch.uint8, device="cuda")
-          for k, g in groups.items()}
-    x = torch.from_numpy(synth.make_x(MOE_T, MOE_HIDDEN, cfg=4, idx=100).view(np.int16)).cuda()
-    # down-projection inputs: one synthetic 512-vector per token, routed by the
-    # same pairs (the grouped call takes at most 64 input rows)
-    h = torch.from_numpy(synth.make_x(MOE_T, MOE_INTER, cfg=4, idx=101).view(np.int16)).cuda()
-    yg = torch.empty((Pmax, MOE_INTER), dtype=torch.float32, device="cuda")
-    yu = torch.empty_like(yg)
-    yd = torch.empty((Pmax, MOE_HIDDEN), dtype=torch.float32, device="cuda")
-    out = {}
-    for verify in (True, False):
-        fn = nl.nested_linear_verify_grouped if verify else nl.nested_linear_draft_grouped
+    x_np = synth.make_x(MOE_T, MOE_HIDDEN, cfg=4, idx=100)
+    x = torch.from_numpy(x_np.view(np.int16)).cuda()
+    out = {"workload": (f"{MOE_EXPERTS} experts + 1 shared, hidden {MOE_HIDDEN}, expert intermediate {MOE_INTER}, "
+                        f"top-{MOE_TOPK} of a {MOE_T}-token block, {MOE_BITS}-bit residual; gate, up: one grouped "
+                        f"call each on the token rows; down: one grouped call on per-pair rows")}
+    for rho in (0.62, 0.0):
+        routes = []
+        for r in range(MOE_ROUTINGS):
+            _, pt, off = synth.router_topk(MOE_T, MOE_EXPERTS, MOE_TOPK, rho, cfg=4, idx=r)
+            pt = np.concatenate([pt, np.arange(MOE_T, dtype=np.int32)]).astype(np.int32)   # shared expert last
+            off = np.concatenate([off, [off[-1] + MOE_T]]).astype(np.int32)
+            P = len(pt)
+            active = int(np.count_nonzero(np.diff(off)))
+            routes.append((torch.from_numpy(pt).cuda(), torch.from_numpy(off).cuda(),
+                           torch.arange(P, dtype=torch.int32, device="cuda"), P, active, pt, off))
+        Pmax = max(r[3] for r in routes)
+        ws = {k: torch.zeros(nl.nested_linear_group_workspace_bytes(g, Pmax), dtype=torch.uint8, device="cuda")
+              for k, g in groups.items()}
+        # down-projection inputs: one synthetic 512-wide row per pair
+        h_np = synth.make_x(Pmax, MOE_INTER, cfg=4, idx=101)
+        h = torch.from_numpy(h_np.view(np.int16)).cuda()
+        yg = torch.empty((Pmax, MOE_INTER), dtype=torch.float32, device="cuda")
+        yu = torch.empty_like(yg)
+        yd = torch.empty((Pmax, MOE_HIDDEN), dtype=torch.float32, device="cuda")
+        res = {"active_experts_avg": round(sum(r[4] for r in routes) / MOE_ROUTINGS, 1)}
+        for verify in (True, False):
+            fn = nl.nested_linear_verify_grouped if verify else nl.nested_linear_draft_grouped
 
-        def passes(s):
-            for pt, off, P, _ in routes:
-                fn(groups["gate"], pt, off, P, x, MOE_T, yg, ws["gate"], s)
-                fn(groups["up"], pt, off, P, x, MOE_T, yu, ws["up"], s)
-                fn(groups["down"], pt, off, P, h, MOE_T, yd, ws["down"], s)
+            def passes(s):
+                for pt, off, ident, P, *_ in routes:
+                    fn(groups["gate"], pt, off, P, x, MOE_T, MOE_T, yg, ws["gate"], s)
+                    fn(groups["up"], pt, off, P, x, MOE_T, MOE_T, yu, ws["up"], s)
+                    fn(groups["down"], ident, off, P, h, P, MOE_T, yd, ws["down"], s)
 
-        g = torch.cuda.CUDAGraph()
-        st = torch.cuda.Stream()
-        st.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(st):
-            passes(st)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            passes(torch.cuda.current_stream())
-        g.replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            g.replay()
-        e1.record()
-        e1.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / (reps * MOE_ROUTINGS)
-        per_expert = 3 * MOE_INTER * MOE_HIDDEN * synth.bytes_per_weight(MOE_BITS if verify else 0)
-        touched = sum(r[3] for r in routes) / MOE_ROUTINGS * per_expert
-        out["verify" if verify else "draft"] = {"us_per_block": round(us, 2), "GBps": round(touched / us / 1e3, 1),
-                                                "frac_hbm_peak": round(touched / us / 1e3 / HBM_PEAK_GBPS, 3)}
-        del g
-    out["active_experts_avg"] = round(sum(r[3] for r in routes) / MOE_ROUTINGS, 1)
-    out["workload"] = (f"{MOE_EXPERTS} experts + 1 shared, hidden {MOE_HIDDEN}, expert intermediate {MOE_INTER}, "
-                       f"top-{MOE_TOPK} of a {MOE_T}-token block (router correlation {MOE_RHO}), "
-                       f"{MOE_BITS}-bit residual; gate, up, down: one grouped call each")
+            # parity of the first routing (all experts share one synthetic linear per projection)
+            pt_d, off_d, ident, P, _, pt_np, off_np = routes[0]
+            fn(groups["gate"], pt_d, off_d, P, x, MOE_T, MOE_T, yg, ws["gate"])
+            fn(groups["down"], ident, off_d, P, h, P, MOE_T, yd, ws["down"])
+            for k in ("gate", "down"):
+                check_status(nl, ws[k], "moe")
+            e_g = rel_err(yg[:P].cpu().numpy(), oracle.forward(lins["gate"], x_np[pt_np], verify))
+            e_d = rel_err(yd[:P].cpu().numpy(), oracle.forward(lins["down"], h_np[:P], verify))
+            g = capture(torch, passes)
+            st = pstats([u / MOE_ROUTINGS for u in replay_samples(torch, g, reps)])
+            del g
+            per_expert = 3 * MOE_INTER * MOE_HIDDEN * synth.bytes_per_weight(MOE_BITS if verify else 0)
+            touched = res["active_experts_avg"] * per_expert
+            res["verify" if verify else "draft"] = dict({"us_per_block": st["us"], "p10": st["p10"],
+                                                         "p90": st["p90"]}, **rate(touched, st["us"], stream_gbps),
+                                                        weight_bytes=int(touched),
+                                                        max_rel_err=float(f"{max(e_g, e_d):.3g}"))
+        for k in ws:
+            check_status(nl, ws[k], "moe")
+        out[f"rho_{rho}"] = res
+        log(f"[bench] moe block rho={rho}: {res['active_experts_avg']} experts, verify "
+            f"{res['verify']['us_per_block']} us, draft {res['draft']['us_per_block']} us")
     for g in groups.values():
         nl.nested_linear_group_destroy(g)
     for hnd in handles:
         nl.nested_linear_destroy(hnd)
-    log(f"[bench] moe block: verify {out['verify']['us_per_block']} us, draft {out['draft']['us_per_block']} us")
+    torch.cuda.empty_cache()
     return out
-
-
-def roofline_leg(nl, call, ncopy, stream, bpw):
-    """Roofline of the dominant kernel, forward_kernel<6, 1, 4>: eager verify
-    launches at T = 8 and 16 over the four projections, each timed by a HIP
-    event pair attached to its own dispatch (the library's timing hook), so
-    a duration is the kernel's execution as the kernel trace reports it."""
-    import torch
-    n = 0
-    plan = []
-    for si, (name, o, i) in enumerate(SHAPES):
-        for T in ROOFLINE_TS:
-            for r in range(2):
-                for cp in range(ncopy):
-                    plan.append((si, cp, T, o * i * bpw(True)))
-    for si, cp, T, _ in plan[:8]:          # warm the code objects
-        call(si, cp, T, True, stream)
-    torch.cuda.synchronize()
-    nl.nested_linear_timing_begin(len(plan))
-    for si, cp, T, _ in plan:
-        call(si, cp, T, True, stream)
-    durs = nl.nested_linear_timing_end(len(plan))
-    assert len(durs) == len(plan), (len(durs), len(plan))
-    avg_us = sum(durs) / len(durs)
-    avg_bytes = sum(b for *_, b in plan) / len(plan)
-    achieved = avg_bytes / avg_us / 1e3
-    digest = kernel_source_digest()
-    traffic = stored_traffic(digest)
-    log(f"[bench] roofline {ROOFLINE_KERNEL}: {avg_us:.2f} us/launch, {achieved:.0f} GB/s")
-    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None if traffic is None else round(traffic),
-            "kernel": ROOFLINE_KERNEL + " (verify, T = 8 and 16, the four projections)",
-            "avg_launch_us": round(avg_us, 2), "avg_algorithmic_bytes": int(avg_bytes),
-            "launches": len(durs), "timing": "HIP events attached to each dispatch",
-            "kernel_source_digest": digest}
 
 
 def graph_us(torch, fn, reps, calls=10):
@@ -646,39 +877,45 @@ def copy_calibration(torch):
             "write_bytes": COPY_FLOATS * 4, "launches": 3}
 
 
-ROOFLINE_TITLE = ("verify, T = 8 and 16, 4096x4096, 1024x4096, 14336x4096,\n"
-                  "4096x14336, 2-bit base + 6-bit residual, one-sided")
+
+
+ROOFLINE_TITLE = ("{mode}, T = 8 and 16, 4096x4096, 1024x4096, 14336x4096,\n"
+                  "4096x14336, 2-bit base{resid}, one-sided")
 W48_TITLE = ("verify at T = 16, W4 base + 4-bit refinement planes of 4096x4096, 1024x4096,\n"
              "14336x4096, 4096x14336")
 ENC_TITLE = ("one-sided fused encode of dense fp32 4096x4096, 1024x4096, 14336x4096,\n"
              "4096x14336 into 2-bit base + 7-bit residual planes")
 
 
-def pmc_summary(fetch_dir, write_dir, out_path, kernel=ROOFLINE_KERNEL, prefix="void nl::",
-                title=ROOFLINE_TITLE, flag="--roofline-only", digest=None, display=None):
-    """Per-launch HBM traffic of the roofline kernel from two rocprofv3 --pmc
-    runs of `bench.py --roofline-only` (FETCH_SIZE, then WRITE_SIZE), each
-    counter scaled by what it reads for the calibration copy.  The encoder's
-    kernel is summarised the same way from runs of `bench.py --encoder-only`
-    (any kernel-name prefix)."""
+def counter_rows(d, counter):
+    """(kernel name, value) of every dispatch in the rocprofv3 csv files under d."""
     import csv
     import glob
+    out = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return out
 
-    def rows(d, counter):
-        out = []
-        for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
-            for r in csv.DictReader(open(f)):
-                if r["Counter_Name"] == counter:
-                    out.append((r["Kernel_Name"], float(r["Counter_Value"])))
-        return out
+
+def kernel_match(name, kernel, prefix):
+    return name.startswith(prefix + kernel) if prefix else kernel in name
+
+
+def pmc_summary(fetch_dir, write_dir, out_path, kernel, prefix="void nl::", title="", flag="--roofline-only",
+                digest=None, display=None):
+    """Per-launch HBM traffic of one kernel from two rocprofv3 --pmc runs of
+    `bench.py <flag>` (FETCH_SIZE, then WRITE_SIZE), each counter scaled by
+    what it reads for the calibration copy of known size."""
 
     def split(rs):
-        fwd = [v for k, v in rs if (k.startswith(prefix + kernel) if prefix else kernel in k)]
+        fwd = [v for k, v in rs if kernel_match(k, kernel, prefix)]
         cpy = [v for k, v in rs if "elementwise" in k and "MulFunctor" in k]
         return fwd, cpy
 
-    f_fwd, f_cpy = split(rows(fetch_dir, "FETCH_SIZE"))
-    w_fwd, w_cpy = split(rows(write_dir, "WRITE_SIZE"))
+    f_fwd, f_cpy = split(counter_rows(fetch_dir, "FETCH_SIZE"))
+    w_fwd, w_cpy = split(counter_rows(write_dir, "WRITE_SIZE"))
     if not f_fwd or not w_fwd or not f_cpy or not w_cpy:
         raise SystemExit(f"pmc summary: missing rows ({len(f_fwd)} {len(w_fwd)} {len(f_cpy)} {len(w_cpy)})")
     known = COPY_FLOATS * 4
@@ -707,19 +944,57 @@ def pmc_summary(fetch_dir, write_dir, out_path, kernel=ROOFLINE_KERNEL, prefix="
     print(text, end="")
 
 
+UTIL_COUNTERS = ("VALUBusy", "MfmaUtil", "OccupancyPercent", "MeanOccupancyPerCU", "MemUnitStalled", "TA_BUSY_avr",
+                 "SQ_WAIT_INST_ANY", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_VMEM_RD", "SQ_WAVES",
+                 "SQ_BUSY_CYCLES")
+
+
+def util_summary(dirs, out_path):
+    """Utilisation counters of the two roofline kernels from rocprofv3 --pmc
+    runs of `bench.py --roofline-only` (one pass per directory): the mean per
+    dispatch of each counter found."""
+    lines = ["Utilisation counters of the forward kernels (verify and draft, T = 8 and 16, 4096x4096, 1024x4096,",
+             "14336x4096, 4096x14336, one-sided), mean per dispatch over the --roofline-only launches",
+             "commands (one counter pass each):"]
+    passes = {0: "VALUBusy MfmaUtil OccupancyPercent MemUnitStalled TA_BUSY_avr",
+              1: "MeanOccupancyPerCU SQ_WAIT_INST_ANY SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_VMEM_RD SQ_WAVES"}
+    for k, d in enumerate(dirs):
+        lines.append(f"  rocprofv3 --pmc {passes.get(k, '<counters>')} --output-format csv -d <dir{k}> -o p -- "
+                     f"python3 bench.py --roofline-only")
+    lines.append(f"  python3 bench.py --util-summary {' '.join(f'<dir{k}>' for k in range(len(dirs)))}")
+    for mode, (kernel, *_rest) in ROOF.items():
+        vals = {}
+        for d in dirs:
+            for c in UTIL_COUNTERS:
+                rs = [v for k, v in counter_rows(d, c) if kernel_match(k, kernel, "void nl::")]
+                if rs:
+                    vals[c] = (sum(rs) / len(rs), len(rs))
+        lines.append(f"{kernel} ({mode}):")
+        for c, (v, n) in vals.items():
+            lines.append(f"  {c}: {v:.4g} (mean of {n} dispatches)")
+    lines.append(f"kernel source digest: {kernel_source_digest()}")
+    text = "\n".join(lines) + "\n"
+    with open(out_path, "w") as fh:
+        fh.write(text)
+    print(text, end="")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--pool-gib", type=float, default=1.2)
-    ap.add_argument("--reps", type=int, default=10, help="graph replays per per-case timing")
+    ap.add_argument("--reps", type=int, default=15, help="graph replays per per-case timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next", action="store_true", help="skip the W4/W8, tree, KV and encoder legs")
     ap.add_argument("--roofline-only", action="store_true",
                     help="run only the roofline launches and the counter calibration copy (for rocprofv3)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="write the traffic summary from two rocprofv3 --pmc runs of --roofline-only")
+                    help="write the verify and draft traffic summaries from two --pmc runs of --roofline-only")
+    ap.add_argument("--util-summary", nargs="+", metavar="DIR",
+                    help="write the utilisation counter summary from --pmc runs of --roofline-only")
     ap.add_argument("--encoder-only", action="store_true",
                     help="run only the encoder leg and the counter calibration copy (for rocprofv3)")
     ap.add_argument("--pmc-summary-encoder", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -736,7 +1011,12 @@ def main():
                     help="write the W4/W8 kernel's traffic summary from two rocprofv3 --pmc runs of --w4w8-only")
     args = ap.parse_args()
     if args.pmc_summary:
-        pmc_summary(*args.pmc_summary, TRAFFIC_FILE)
+        for mode, (kernel, bits, _, path) in ROOF.items():
+            pmc_summary(*args.pmc_summary, path, kernel=kernel,
+                        title=ROOFLINE_TITLE.format(mode=mode, resid=" + 6-bit residual" if bits else ""))
+        return
+    if args.util_summary:
+        util_summary(args.util_summary, UTIL_FILE)
         return
     if args.pmc_summary_w4w8:
         pmc_summary(*args.pmc_summary_w4w8, W48_TRAFFIC_FILE, kernel=W48_KERNEL, prefix="", title=W48_TITLE,
@@ -795,75 +1075,47 @@ def main():
     # ---- weights: one synthetic linear per shape, repacked into a pool of copies
     set_bytes = sum(o * i for _, o, i in SHAPES) * bpw(True)
     ncopy = max(2, math.ceil(args.pool_gib * 2 ** 30 / set_bytes))
-    lins, handles, xs, wss, ys = [], [], [], [], []
+    lins, handles, xs, xh, wss, ys = [], [], [], [], [], []
     t0 = time.time()
-
-    def to_dev(lin):
-        return {k: (None if lin[k] is None else torch.from_numpy(np.ascontiguousarray(lin[k]).view(dt)).to(dev))
-                for k, dt in [("base_codes", np.uint8), ("base_scales", np.int16), ("resid_codes", np.uint8),
-                              ("resid_scales", np.int16), ("sign_in", np.int8), ("sign_out", np.int8)]}
-
     for si, (name, o, i) in enumerate(SHAPES):
         lin = synth.make_linear(o, i, BITS, cfg=1, idx=si, two_sided=False)
         lins.append(lin)
-        d = to_dev(lin)
+        d = dev_arrays(torch, lin)
         handles.append([nl.nested_linear_create(o, i, BITS, levels=lin["levels"], **d) for _ in range(ncopy)])
         del d
-        xs.append(torch.from_numpy(synth.make_x(max(CASE_TS), i, cfg=1, idx=si).view(np.int16)).to(dev))
+        xh.append(synth.make_x(max(CASE_TS), i, cfg=1, idx=si))
+        xs.append(torch.from_numpy(xh[-1].view(np.int16)).to(dev))
         wss.append(torch.zeros(nl.nested_linear_workspace_bytes(handles[-1][0], max(CASE_TS)),
                                dtype=torch.uint8, device=dev))
         ys.append(torch.empty((max(CASE_TS), o), dtype=torch.float32, device=dev))
         log(f"[bench] {name} {o}x{i}: {ncopy} copies created ({time.time() - t0:.1f}s)")
     torch.cuda.synchronize()
 
-    def call(si, copy, T, verify, stream):
+    def call(si, copy, T, verify, stream=None):
         fn = nl.nested_linear_verify if verify else nl.nested_linear_draft
         fn(handles[si][copy], xs[si], T, ys[si], wss[si], stream)
 
-    def capture(calls, call_fn=call):
-        g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            for cl in calls:
-                call_fn(*cl, stream=s)
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            cs = torch.cuda.current_stream()
-            for cl in calls:
-                call_fn(*cl, stream=cs)
-        return g
-
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-
-    def time_graph(g, reps):
-        g.replay()
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(reps):
-            g.replay()
-        e1.record()
-        e1.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / reps  # us per replay
-
     stream = torch.cuda.current_stream()
     if args.roofline_only:
-        roofline = roofline_leg(nl, call, ncopy, stream, bpw)
+        roof = {m: roofline_leg(nl, call, ncopy, stream, bpw, m) for m in ROOF}
+        for ws in wss:
+            check_status(nl, ws, "roofline")
         calib = copy_calibration(torch)
-        print(json.dumps({"roofline": roofline, "copy_calibration": calib}), flush=True)
+        print(json.dumps({"roofline": roof, "copy_calibration": calib}), flush=True)
         return
 
-    # ---- the step: 40 calls, weights rotating through the pool
+    # ---- the streaming-read reference (the measured ceiling)
+    sref = stream_ref_leg(nl, torch)
+    stream_gbps = sref["GBps"]
+
+    # ---- the step: 20 verify calls, weights rotating through the pool
     seq, c = [], 0
     for T in STEP_TS:
-        for verify in (True, False):
-            for si in range(len(SHAPES)):
-                seq.append((si, c % ncopy, T, verify))
-                c += 1
+        for si in range(len(SHAPES)):
+            seq.append((si, c % ncopy, T, True))
+            c += 1
     step_bytes = sum(SHAPES[si][1] * SHAPES[si][2] * bpw(v) for si, _, _, v in seq)
-    g = capture(seq)
+    g = capture(torch, lambda s: [call(*cl, stream=s) for cl in seq])
     # a replay reproduces the eager outputs bit for bit (rows the step writes)
     rows = max(STEP_TS)
     eager = [y[:rows].clone() for y in ys]
@@ -876,6 +1128,8 @@ def main():
     for _ in range(args.warmup):
         g.replay()
     torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(args.steps):
         g.replay()
@@ -883,37 +1137,44 @@ def main():
     e1.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    for ws in wss:
+        check_status(nl, ws, "the step")
+    del g
     log(f"[bench] step: {ms_per_step:.3f} ms, {value:.1f} GB/s ({args.steps} steps)")
 
-    # ---- per case: graphs of ncopy calls of one (shape, mode, T)
+    # ---- per case: µs per pass over the four projections (replays of a graph
+    # of ncopy passes), per-shape means, and the error on sampled rows
+    import oracle
+    refs = {(si, v): oracle.forward(lins[si], xh[si], v, rows=(0, ERR_ROWS))
+            for si in range(len(SHAPES)) for v in (True, False)}
     per_case = {}
     for T in CASE_TS:
         for verify in (True, False):
-            tot_us, tot_b, shp = 0.0, 0.0, {}
+            err = 0.0
+            for si in range(len(SHAPES)):
+                call(si, 0, T, verify)
+                err = max(err, rel_err(ys[si][:T, :ERR_ROWS].cpu().numpy(), refs[(si, verify)][:T]))
+                check_status(nl, wss[si], f"T={T}")
+            gp = capture(torch, lambda s: [call(si, cp, T, verify, s) for cp in range(ncopy)
+                                           for si in range(len(SHAPES))])
+            st = pstats([u / ncopy for u in replay_samples(torch, gp, args.reps)])
+            del gp
+            shp, tot_b = {}, 0.0
             for si, (name, o, i) in enumerate(SHAPES):
-                gc = capture([(si, cp, T, verify) for cp in range(ncopy)])
-                us = time_graph(gc, args.reps) / ncopy
-                del gc
+                gs = capture(torch, lambda s: [call(si, cp, T, verify, s) for cp in range(ncopy)])
+                us = float(np.mean(replay_samples(torch, gs, max(3, args.reps // 3)))) / ncopy
+                del gs
                 b = o * i * bpw(verify)
-                shp[name] = {"us": round(us, 2), "GBps": round(b / us / 1e3, 1)}
-                tot_us += us
                 tot_b += b
+                shp[name] = {"us": round(us, 2), "GBps": round(b / us / 1e3, 1)}
             key = f"{'verify' if verify else 'draft'}_T{T}"
-            per_case[key] = {"us_per_pass": round(tot_us, 2), "GBps": round(tot_b / tot_us / 1e3, 1),
-                             "frac_hbm_peak": round(tot_b / tot_us / 1e3 / HBM_PEAK_GBPS, 3), "shapes": shp}
-            log(f"[bench] {key}: {tot_us:.1f} us per pass over the 4 projections, {tot_b / tot_us / 1e3:.0f} GB/s")
-
-    # ---- one decoder layer of the 7B/8B-class model: q, k, v, o, gate, up and
-    # down run as seven sequential calls of the four shapes above
-    layer = {"linears": "q, o: 4096x4096; k, v: 1024x4096; gate, up: 14336x4096; down: 4096x14336",
-             "layers": LAYERS, "us_per_layer": {}, "ms_per_model": {}}
-    for key, c in per_case.items():
-        sh = c["shapes"]
-        us = 2 * sh["q/o"]["us"] + 2 * sh["k/v"]["us"] + 2 * sh["gate/up"]["us"] + sh["down"]["us"]
-        layer["us_per_layer"][key] = round(us, 1)
-        layer["ms_per_model"][key] = round(us * LAYERS / 1e3, 2)
-    log(f"[bench] decoder layer, verify T=16: {layer['us_per_layer']['verify_T16']:.1f} us "
-        f"({layer['ms_per_model']['verify_T16']:.2f} ms for {LAYERS} layers)")
+            per_case[key] = dict({"us_per_pass": st["us"], "p10": st["p10"], "p90": st["p90"]},
+                                 **rate(tot_b, st["us"], stream_gbps), max_rel_err=float(f"{err:.3g}"),
+                                 shapes=shp)
+            log(f"[bench] {key}: {st['us']:.1f} us per pass [{st['p10']:.1f}, {st['p90']:.1f}], "
+                f"{per_case[key]['GBps']:.0f} GB/s, err {err:.2e}")
+    for ws in wss:
+        check_status(nl, ws, "per case")
 
     # ---- launch-inclusive single calls (eager, one call between events), verify
     single = {}
@@ -932,79 +1193,86 @@ def main():
             tot += durs[len(durs) // 2]
         single[f"verify_T{T}_us_per_pass_median"] = round(tot, 2)
 
-    # ---- the two-sided form (y = S_o H_o y~) at T = 1 and 16, verify
-    two_handles, two_ws = [], []
+    # ---- the two-sided form (y = S_o H_o y~) at T = 1 and 16
+    two_lins, two_handles, two_ws = [], [], []
     for si, (name, o, i) in enumerate(SHAPES):
         lin2 = synth.make_linear(o, i, BITS, cfg=1, idx=si, two_sided=True)
-        d = to_dev(lin2)
-        two_handles.append([nl.nested_linear_create(o, i, BITS, levels=lin2["levels"], **d)
-                            for _ in range(ncopy)])
+        two_lins.append(lin2)
+        d = dev_arrays(torch, lin2)
+        two_handles.append([nl.nested_linear_create(o, i, BITS, levels=lin2["levels"], **d) for _ in range(ncopy)])
         two_ws.append(torch.zeros(nl.nested_linear_workspace_bytes(two_handles[-1][0], 16),
                                   dtype=torch.uint8, device=dev))
         del d
 
-    def call2(si, copy, T, verify, stream):
+    def call2(si, copy, T, verify, s=None):
         fn = nl.nested_linear_verify if verify else nl.nested_linear_draft
-        fn(two_handles[si][copy], xs[si], T, ys[si], two_ws[si], stream)
+        fn(two_handles[si][copy], xs[si], T, ys[si], two_ws[si], s)
 
     two_sided = {}
     for T in (1, 16):
-        tot_us, tot_b = 0.0, 0.0
-        for si, (name, o, i) in enumerate(SHAPES):
-            gc = capture([(si, cp, T, True) for cp in range(ncopy)], call2)
-            tot_us += time_graph(gc, args.reps) / ncopy
-            tot_b += o * i * bpw(True)
-            del gc
-        two_sided[f"verify_T{T}"] = {"us_per_pass": round(tot_us, 2), "GBps": round(tot_b / tot_us / 1e3, 1)}
+        for verify in (True, False):
+            err = 0.0
+            for si, (name, o, i) in enumerate(SHAPES):
+                call2(si, 0, T, verify)
+                b_out = nl.nested_linear_info(two_handles[si][0])["block_out"]
+                ref = oracle.forward(two_lins[si], xh[si][:T], verify, rows=(0, b_out))
+                err = max(err, rel_err(ys[si][:T, :b_out].cpu().numpy(), ref))
+                check_status(nl, two_ws[si], "two-sided")
+            gp = capture(torch, lambda s: [call2(si, cp, T, verify, s) for cp in range(ncopy)
+                                           for si in range(len(SHAPES))])
+            st = pstats([u / ncopy for u in replay_samples(torch, gp, args.reps)])
+            del gp
+            tot_b = sum(o * i * bpw(verify) for _, o, i in SHAPES)
+            two_sided[f"{'verify' if verify else 'draft'}_T{T}"] = dict(
+                {"us_per_pass": st["us"], "p10": st["p10"], "p90": st["p90"]}, **rate(tot_b, st["us"], stream_gbps),
+                max_rel_err=float(f"{err:.3g}"))
     for hs in two_handles:
         for h in hs:
             nl.nested_linear_destroy(h)
     del two_handles, two_ws
 
-    roofline = roofline_leg(nl, call, ncopy, stream, bpw)
+    roofline = roofline_leg(nl, call, ncopy, stream, bpw, "verify")
+    roofline_draft = roofline_leg(nl, call, ncopy, stream, bpw, "draft")
+    for ws in wss:
+        check_status(nl, ws, "roofline")
+    for hs in handles:
+        for h in hs:
+            nl.nested_linear_destroy(h)
+    torch.cuda.empty_cache()
+
+    # ---- the 1024x1024 int8 linear
+    single1024 = single1024_leg(nl, torch, synth, args.reps, stream_gbps)
+
+    # ---- one decoder layer with fused launches
+    layer = decoder_layer_leg(nl, torch, synth, args.reps, stream_gbps, args.pool_gib)
 
     # ---- the MoE block (grouped calls)
-    moe = moe_leg(nl, torch, synth, args.reps)
+    moe = moe_leg(nl, torch, synth, args.reps, stream_gbps)
 
     # ---- whole dense-model passes (one graph per pass)
     model = {}
     for spec in MODELS:
-        m = model_leg(nl, torch, synth, 3, spec)
+        m = model_leg(nl, torch, synth, 5, spec, stream_gbps)
         model[spec[0]] = m
         log(f"[bench] {spec[0]} pass: verify T={m['verify']['T']} {m['verify']['us_per_pass']:.0f} us "
             f"({m['verify']['GBps']:.0f} GB/s), draft T={m['draft']['T']} {m['draft']['us_per_pass']:.0f} us "
             f"({m['draft']['GBps']:.0f} GB/s)")
 
-    # ---- the BitNest W4/W8 dual-plane format (same contraction, other planes)
-    w4w8 = w4w8_leg(nl, torch, synth, args.reps, args.pool_gib)
-
-    # ---- the draft tree (build once from the statistics, accept per step)
-    draft_tree = tree_leg(nl, torch, synth, args.reps, cpu_seconds=0.0 if args.no_cpu_baseline else 2.0)
-
-    # ---- nested KV cache: tree-masked attention over KV8 / KV4
-    kv_cache = kv_leg(nl, torch, synth, args.reps)
-
-    # ---- the offline encoder (dense W -> planes) and the level fit
-    encoder = encoder_leg(nl, torch, synth, args.reps, cpu_seconds=0.0 if args.no_cpu_baseline else 3.0)
-
-    # ---- streaming reference on the same GPU (torch reduction over 2 GiB)
-    big = torch.ones(2 ** 29, dtype=torch.float32, device=dev)
-    big.sum()
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(5):
-        big.sum()
-    e1.record()
-    e1.synchronize()
-    stream_gbps = 5 * big.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del big
+    nxt = {}
+    if not args.no_next:
+        # ---- the BitNest W4/W8 dual-plane format (same contraction, other planes)
+        nxt["w4w8"] = w4w8_leg(nl, torch, synth, args.reps, args.pool_gib)
+        # ---- the draft tree (build once from the statistics, accept per step)
+        nxt["draft_tree"] = tree_leg(nl, torch, synth, args.reps, cpu_seconds=0.0 if args.no_cpu_baseline else 2.0)
+        # ---- nested KV cache: tree-masked attention over KV8 / KV4
+        nxt["nested_kv"] = kv_leg(nl, torch, synth, args.reps)
+        # ---- the offline encoder (dense W -> planes) and the level fit
+        nxt["encoder"] = encoder_leg(nl, torch, synth, args.reps, cpu_seconds=0.0 if args.no_cpu_baseline else 3.0)
 
     # ---- CPU baseline: the fp64 oracle on the step's calls, host cores
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        xh = [synth.make_x(max(STEP_TS), i, cfg=1, idx=si) for si, (_, o, i) in enumerate(SHAPES)]
-        log(f"[bench] cpu baseline: oracle over the step's 40 calls, {oracle.num_threads()} threads")
+        log(f"[bench] cpu baseline: oracle over the step's {len(seq)} calls, {oracle.num_threads()} threads")
         t0 = time.time()
         nsteps = 0
         while True:
@@ -1016,8 +1284,8 @@ def main():
         dt = time.time() - t0
         cpu = {"value": round(nsteps * step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
                "kind": "oracle",
-               "sample": f"{nsteps} full step(s) of the same workload (40 calls, {step_bytes / 1e9:.3f} GB of "
-                         f"weights each) in {dt:.1f} s"}
+               "sample": f"{nsteps} full step(s) of the same workload ({len(seq)} verify calls, "
+                         f"{step_bytes / 1e9:.3f} GB of weights each) in {dt:.1f} s"}
         log(f"[bench] cpu baseline: {dt:.1f} s, {cpu['value']} GB/s")
 
     out = {
@@ -1027,21 +1295,20 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "fp16-mfma/fp32", "data": "synthetic",
         "config": {"workload": "7B/8B-class projections 4096x4096, 1024x4096, 14336x4096, 4096x14336; "
                                "2-bit Lloyd-Max base + 6-bit residual, fp16 group-128 scales; bf16 x; "
-                               "one-sided y = (Q_b + Q_r) H S x; draft and verify at T=1,4,8,16,32",
+                               "one-sided y = (Q_b + Q_r) H S x; verify at T=1,4,8,16,32, one launch per call",
                    "calls_per_step": len(seq), "weight_bytes_per_step": int(step_bytes),
                    "pool_copies": ncopy, "pool_bytes": int(ncopy * set_bytes)},
+        "stream_ref": sref,
         "per_case": per_case,
         "single_call": single,
         "two_sided": two_sided,
+        "single_1024_int8": single1024,
+        "decoder_layer": layer,
         "moe_block": moe,
         "model_pass": model,
-        "w4w8": w4w8,
-        "draft_tree": draft_tree,
-        "nested_kv": kv_cache,
-        "encoder": encoder,
-        "decoder_layer": layer,
-        "stream_read_GBps_torch_sum": round(stream_gbps, 1),
+        **nxt,
         "roofline": roofline,
+        "roofline_draft": roofline_draft,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

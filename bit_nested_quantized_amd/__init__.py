@@ -31,7 +31,7 @@ EXPORTS = (
     "nested_linear_info", "nested_linear_timing_begin", "nested_linear_timing_end",
     "nested_linear_last_error", "nested_linear_verify_multi", "nested_linear_draft_multi",
     "nested_linear_multi_workspace_bytes", "nested_linear_workspace_status", "nested_linear_set_tuning",
-    "nested_linear_describe_call",
+    "nested_linear_describe_call", "nested_linear_stream_read",
     "nested_encode_rotate", "nested_encode_quantize", "nested_encode_workspace_bytes", "nested_encode",
     "nested_encode_normalize", "nested_encode_fit_workspace_bytes", "nested_encode_fit_levels",
     "nested_w4w8_create", "nested_w4w8_destroy", "nested_w4w8_workspace_bytes", "nested_w4w8_verify",
@@ -92,8 +92,8 @@ def lib() -> ctypes.CDLL:
             "nested_linear_group_create": [P, i32, ctypes.POINTER(P)],
             "nested_linear_group_destroy": [P],
             "nested_linear_group_workspace_bytes": [P, i32, ctypes.POINTER(sz)],
-            "nested_linear_verify_grouped": [P, P, P, i32, P, i32, P, P, sz, P],
-            "nested_linear_draft_grouped": [P, P, P, i32, P, i32, P, P, sz, P],
+            "nested_linear_verify_grouped": [P, P, P, i32, P, i32, i32, P, P, sz, P],
+            "nested_linear_draft_grouped": [P, P, P, i32, P, i32, i32, P, P, sz, P],
             "nested_linear_decode": [P, i32, i32, P, P, P],
             "nested_linear_info": [P] + [ctypes.POINTER(i32)] * 5 + [ctypes.POINTER(ctypes.c_float)],
             "nested_linear_timing_begin": [i32],
@@ -104,6 +104,7 @@ def lib() -> ctypes.CDLL:
             "nested_linear_workspace_status": [P, ctypes.POINTER(ctypes.c_uint32), i32, P],
             "nested_linear_set_tuning": [i32, ctypes.c_double],
             "nested_linear_describe_call": [P, i32, i32, i32, i32, i32, ctypes.POINTER(i32), i32],
+            "nested_linear_stream_read": [P, sz, P, i32, P],
             "nested_encode_rotate": [i32, i32, P, P, P, P, P],
             "nested_encode_quantize": [P, ctypes.POINTER(nl_codes), P],
             "nested_encode_workspace_bytes": [i32, i32, i32, ctypes.POINTER(sz)],
@@ -213,6 +214,12 @@ def nested_linear_workspace_status(ws, clear: bool = False, stream=None) -> int:
     return int(e.value)
 
 
+def nested_linear_stream_read(src, sink, grid: int = 0, stream=None):
+    """Streaming-read reference: one launch reading all of ``src`` once."""
+    _check(lib().nested_linear_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), int(grid),
+                                           _stream(stream)))
+
+
 def nested_linear_describe_call(d_outs, d_in: int, bits: int, two_sided: bool, T: int) -> dict:
     """The launch plan of a call (host query; bits = 0 for the draft)."""
     n = len(d_outs)
@@ -267,14 +274,14 @@ def nested_linear_group_workspace_bytes(g, P_max: int) -> int:
     return n.value
 
 
-def nested_linear_verify_grouped(g, pair_token, offsets, P: int, x, T: int, y, ws, stream=None):
-    _check(lib().nested_linear_verify_grouped(g, _ptr(pair_token), _ptr(offsets), int(P), _ptr(x), int(T),
+def nested_linear_verify_grouped(g, pair_token, offsets, P: int, x, x_rows: int, T: int, y, ws, stream=None):
+    _check(lib().nested_linear_verify_grouped(g, _ptr(pair_token), _ptr(offsets), int(P), _ptr(x), int(x_rows), int(T),
                                               _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
                                               _stream(stream)))
 
 
-def nested_linear_draft_grouped(g, pair_token, offsets, P: int, x, T: int, y, ws, stream=None):
-    _check(lib().nested_linear_draft_grouped(g, _ptr(pair_token), _ptr(offsets), int(P), _ptr(x), int(T),
+def nested_linear_draft_grouped(g, pair_token, offsets, P: int, x, x_rows: int, T: int, y, ws, stream=None):
+    _check(lib().nested_linear_draft_grouped(g, _ptr(pair_token), _ptr(offsets), int(P), _ptr(x), int(x_rows), int(T),
                                              _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
                                              _stream(stream)))
 

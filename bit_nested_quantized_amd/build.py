@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnested_linear.so")
-SOURCES = ["nl_kernels.hip", "nl_fwd.hip", "nl_api.hip", "nl_encode.hip", "nl_w4w8.hip", "nl_tree.hip", "nl_kv.hip"]
+SOURCES = ["nl_kernels.hip", "nl_fwd.hip", "nl_api.hip", "nl_encode.hip", "nl_w4w8.hip", "nl_tree.hip", "nl_kv.hip", "nl_stream.hip"]
 FLAGS_C = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
     # packed fp32 VALU ops stay off: the compiler's own scalar code is used

@@ -109,6 +109,10 @@ static float h_bits2f(uint16_t b) {
   return (float)h;
 }
 
+// Largest relative error of a base level as the kernels hold it (create
+// refuses levels beyond it).
+constexpr float kMaxLevelRelErr = 2e-3f;
+
 // Pick kappa so that fp16(kappa * levels[c]) is as close as possible to
 // kappa * levels[c] for all four levels (relative error), then build the
 // fp16x2 pair table used by the kernels' base unpack.
@@ -181,6 +185,16 @@ extern "C" nl_status nested_linear_create(const nl_desc *d, nl_handle *out) {
     return fail(NL_EINVAL, "create: residual arrays given with residual_bits == 0");
   for (int c = 0; c < 4; ++c)
     if (!std::isfinite(d->levels[c])) return fail(NL_EINVAL, "create: level %d is not finite", c);
+  {  // the kernels hold the levels as fp16 after one exact rescale: refuse
+     // levels that fp16 cannot hold within the output tolerance
+    uint32_t lut[16];
+    float kinv, err;
+    build_lut(d->levels, lut, &kinv, &err);
+    if (!(err <= kMaxLevelRelErr))
+      return fail(NL_EUNSUPPORTED,
+                  "create: levels (%g, %g, %g, %g) span too wide a ratio for fp16 (relative error %.3g > %g)",
+                  d->levels[0], d->levels[1], d->levels[2], d->levels[3], err, kMaxLevelRelErr);
+  }
 
   // Signs: copied to the host once and checked to be +-1.
   std::vector<int8_t> si(d->d_in), so(d->sign_out ? d->d_out : 0);
@@ -503,6 +517,16 @@ static void timing_slot(hipStream_t s, hipEvent_t *e0, hipEvent_t *e1) {
   *e0 = g_timing.ev[2 * g_timing.used];
   *e1 = g_timing.ev[2 * g_timing.used + 1];
   ++g_timing.used;
+}
+
+extern "C" nl_status nested_linear_stream_read(const void *src, size_t bytes, uint32_t *sink, int32_t grid,
+                                               void *stream) {
+  if (!src || !sink) return fail(NL_EINVAL, "stream_read: NULL pointer");
+  if (bytes == 0 || (bytes & 15) || ((uintptr_t)src & 15))
+    return fail(NL_EINVAL, "stream_read: bytes must be a positive multiple of 16 and src 16-byte aligned");
+  if (grid < 0 || grid > (1 << 20)) return fail(NL_EINVAL, "stream_read: grid must be in [0, 2^20]");
+  HIP_OR_FAIL(launch_stream_read(src, bytes, sink, grid ? grid : 2048, (hipStream_t)stream));
+  return ok();
 }
 
 extern "C" nl_status nested_linear_timing_begin(int32_t capacity) {
@@ -1016,13 +1040,13 @@ extern "C" nl_status nested_linear_group_workspace_bytes(nl_group_handle g, int3
 }
 
 static nl_status grouped(nl_group_handle g, int verify, const int32_t *pair_token,
-                         const int32_t *offsets, int32_t P, const void *x, int32_t T, float *y,
+                         const int32_t *offsets, int32_t P, const void *x, int32_t x_rows, int32_t T, float *y,
                          void *ws, size_t ws_bytes, void *stream, const char *who) {
   if (!valid(g)) return fail(NL_EINVAL, "%s: invalid handle", who);
   if (verify && !g->bits) return fail(NL_EINVAL, "%s: the experts have no residual", who);
   if (!pair_token || !offsets || !x || !y || !ws) return fail(NL_EINVAL, "%s: NULL pointer", who);
   if ((uintptr_t)x & 15) return fail(NL_EINVAL, "%s: x must be 16-byte aligned", who);
-  if (P < 1 || T < 1) return fail(NL_EINVAL, "%s: P and T must be >= 1", who);
+  if (P < 1 || T < 1 || x_rows < 1) return fail(NL_EINVAL, "%s: P, x_rows and T must be >= 1", who);
   if (T > NL_MAX_T) return fail(NL_EUNSUPPORTED, "%s: T = %d exceeds %d", who, T, NL_MAX_T);
   if ((uintptr_t)ws & 255) return fail(NL_EINVAL, "%s: workspace must be 256-byte aligned", who);
   Plan p = group_plan(g, P, T);
@@ -1039,7 +1063,7 @@ static nl_status grouped(nl_group_handle g, int verify, const int32_t *pair_toke
   r.pair_token = pair_token;
   r.offsets = offsets;
   r.n_experts = g->n;
-  r.x_rows = T;
+  r.x_rows = x_rows;
   r.rows = P;
   r.lb = log2i(g->b_in);
   r.xh = (uint16_t *)(w + p.o_xh);
@@ -1085,14 +1109,14 @@ static nl_status grouped(nl_group_handle g, int verify, const int32_t *pair_toke
 
 extern "C" nl_status nested_linear_verify_grouped(nl_group_handle g, const int32_t *pair_token,
                                                   const int32_t *offsets, int32_t P, const void *x,
-                                                  int32_t T, float *y, void *ws, size_t ws_bytes,
-                                                  void *stream) {
-  return grouped(g, 1, pair_token, offsets, P, x, T, y, ws, ws_bytes, stream, "verify_grouped");
+                                                  int32_t x_rows, int32_t T, float *y, void *ws,
+                                                  size_t ws_bytes, void *stream) {
+  return grouped(g, 1, pair_token, offsets, P, x, x_rows, T, y, ws, ws_bytes, stream, "verify_grouped");
 }
 
 extern "C" nl_status nested_linear_draft_grouped(nl_group_handle g, const int32_t *pair_token,
                                                  const int32_t *offsets, int32_t P, const void *x,
-                                                 int32_t T, float *y, void *ws, size_t ws_bytes,
-                                                 void *stream) {
-  return grouped(g, 0, pair_token, offsets, P, x, T, y, ws, ws_bytes, stream, "draft_grouped");
+                                                 int32_t x_rows, int32_t T, float *y, void *ws,
+                                                 size_t ws_bytes, void *stream) {
+  return grouped(g, 0, pair_token, offsets, P, x, x_rows, T, y, ws, ws_bytes, stream, "draft_grouped");
 }

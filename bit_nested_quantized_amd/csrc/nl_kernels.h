@@ -140,6 +140,9 @@ hipError_t launch_decode(const DecodeArgs &a, int bits, int ntiles, hipStream_t 
 hipError_t launch_rotate_in(const RotInArgs &a, int rows, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs &a, int bits, int mt, int splits, hipStream_t s);
 hipError_t launch_finish(const FinishArgs &a, hipStream_t s);
+// Streaming-read reference (nl_stream.hip): reads bytes (a multiple of 16)
+// from src once; sink holds one word per workgroup of the grid.
+hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, int grid, hipStream_t s);
 // ev0/ev1 (optional): events that record the kernel's own start and end
 // (attached to the dispatch, not queued beside it).
 hipError_t launch_forward(const FwdArgs &f, int bits, int mt, int tw, int n_fin, hipStream_t s,

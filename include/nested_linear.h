@@ -85,8 +85,11 @@ typedef struct {
  * Copies and repacks everything into library-owned device memory laid out
  * for the gfx950 kernels; the caller may free its arrays when this returns.
  * Synchronises the device.  Errors: NL_EINVAL (shape, bits, NULL pointer,
- * a sign not +-1, non-finite level), NL_ENOMEM, NL_EHIP.  *out is set only
- * on success.  A handle is immutable after create: concurrent calls on
+ * a sign not +-1, non-finite level), NL_EUNSUPPORTED (levels whose fp16
+ * copy, after the one common rescale that create searches for, errs by more
+ * than 2e-3 relative: a nonzero level some 1e10 times smaller than the
+ * largest falls below fp16's subnormal range), NL_ENOMEM, NL_EHIP.  *out is
+ * set only on success.  A handle is immutable after create: concurrent calls on
  * different streams are safe when each uses its own workspace.
  */
 nl_status nested_linear_create(const nl_desc *desc, nl_handle *out);
@@ -242,14 +245,21 @@ nl_status nested_linear_group_destroy(nl_group_handle g);
 nl_status nested_linear_group_workspace_bytes(nl_group_handle g, int32_t P_max,
                                               size_t *bytes);
 /*
- * Pair p (0 <= p < P) routes token pair_token[p] to the expert e with
- * expert_offsets[e] <= p < expert_offsets[e+1]; pairs are sorted by expert
- * and an expert receives each token at most once, so at most T pairs (rows
- * of an expert past the first 16 * ceil(T / 16) are not computed).
- *   pair_token     [P] int32 device, values in [0, T)
+ * Pair p (0 <= p < P) applies expert e, the one with
+ * expert_offsets[e] <= p < expert_offsets[e+1], to row pair_token[p] of x;
+ * pairs are sorted by expert.  x holds either one row per token (gate / up
+ * projections: an expert receives each token at most once) or one row per
+ * pair (the down projection, whose input is each pair's own activation:
+ * pair_token[p] = p and x_rows = P).
+ *   pair_token     [P] int32 device, values in [0, x_rows); a value outside
+ *                  reads as a zero row
  *   expert_offsets [n+1] int32 device, non-decreasing, [0] = 0, [n] = P
- *   x              [T][d_in] bf16; y [P][d_out] fp32, row p = expert e's
- *                  forward of token pair_token[p].
+ *   x              [x_rows][d_in] bf16 device
+ *   T              at most this many pairs go to any one expert (1..64; the
+ *                  tokens of the block); rows of an expert past the first
+ *                  16 * ceil(T / 16) are not computed
+ *   y              [P][d_out] fp32, row p = expert e's forward of x row
+ *                  pair_token[p].
  * Offsets and tokens stay on the device: experts with no pairs cost no
  * weight traffic and the host never synchronises.  The offsets and tokens
  * are trusted to satisfy the rules above (they are not validated on the
@@ -259,11 +269,11 @@ nl_status nested_linear_group_workspace_bytes(nl_group_handle g, int32_t P_max,
  */
 nl_status nested_linear_verify_grouped(nl_group_handle g, const int32_t *pair_token,
                                        const int32_t *expert_offsets, int32_t P,
-                                       const void *x_bf16, int32_t T, float *y,
+                                       const void *x_bf16, int32_t x_rows, int32_t T, float *y,
                                        void *ws, size_t ws_bytes, void *hip_stream);
 nl_status nested_linear_draft_grouped(nl_group_handle g, const int32_t *pair_token,
                                       const int32_t *expert_offsets, int32_t P,
-                                      const void *x_bf16, int32_t T, float *y,
+                                      const void *x_bf16, int32_t x_rows, int32_t T, float *y,
                                       void *ws, size_t ws_bytes, void *hip_stream);
 
 /*
@@ -299,6 +309,20 @@ nl_status nested_linear_info(nl_handle h, int32_t *d_out, int32_t *d_in, int32_t
  */
 nl_status nested_linear_timing_begin(int32_t capacity);
 nl_status nested_linear_timing_end(float *us, int32_t capacity, int32_t *count);
+
+/*
+ * Measurement aid: the streaming-read reference.  One launch reads every
+ * byte of [src, src + bytes) once from device memory with 16-byte
+ * nontemporal loads (the load kind the forward streams its weights with) and
+ * computes nothing else, so bytes / duration is the read rate this GPU
+ * reaches in practice, the measured ceiling set beside the nominal peak.
+ *   src   device, 16-byte aligned; bytes a positive multiple of 16
+ *   sink  device, at least `grid` 32-bit words (practically never written)
+ *   grid  workgroups of 256 threads (0: 2048)
+ * Asynchronous on hip_stream.  Errors: NL_EINVAL, NL_EHIP.
+ */
+nl_status nested_linear_stream_read(const void *src, size_t bytes, uint32_t *sink, int32_t grid,
+                                    void *hip_stream);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char *nested_linear_last_error(void);

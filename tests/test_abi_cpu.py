@@ -57,6 +57,18 @@ def test_create_rejects_null_and_bad_shapes():
     assert b"level" in L.nested_linear_last_error()
 
 
+def test_create_rejects_levels_fp16_cannot_hold():
+    # one common rescale puts the largest level in [1024, 2048); a level 1e12
+    # times smaller is below fp16's smallest subnormal whatever the rescale
+    # (relative error 1).  The check runs before any device pointer is read.
+    L = nl.lib()
+    h = ctypes.c_void_p()
+    for lv in [(-1.0, 1e-12, 0.5, 1.0), (-3e4, -2.0, 1e-9, 5e-4)]:
+        d = nl.nl_desc(16, 1024, 0, 1, 1, None, None, 1, None, (ctypes.c_float * 4)(*lv))
+        assert L.nested_linear_create(ctypes.byref(d), ctypes.byref(h)) == nl.NL_EUNSUPPORTED
+        assert b"ratio" in L.nested_linear_last_error()
+
+
 def test_calls_reject_invalid_handles():
     L = nl.lib()
     n = ctypes.c_size_t()

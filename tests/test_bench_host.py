@@ -38,7 +38,8 @@ def _counter_csv(path, counter, rows):
 
 
 def test_pmc_summary_scales_each_counter_by_the_copy(tmp_path):
-    kern = f"void nl::{bench.ROOFLINE_KERNEL}(nl::FwdArgs)"
+    kernel = bench.ROOF["verify"][0]
+    kern = f"void nl::{kernel}(nl::FwdArgs2)"
     copy = "void at::native::elementwise_kernel<MulFunctor<float>>(int, F)"
     known = bench.COPY_FLOATS * 4
     # the copy reads half its bytes on FETCH_SIZE (scale 2) and all on WRITE_SIZE (scale 1)
@@ -48,7 +49,7 @@ def test_pmc_summary_scales_each_counter_by_the_copy(tmp_path):
     _counter_csv(str(tmp_path / "w" / "run" / "p_counter_collection.csv"), "WRITE_SIZE",
                  [(kern, 10.0), (kern, 30.0), (copy, known / 1024)])
     out = tmp_path / "traffic.txt"
-    bench.pmc_summary(str(tmp_path / "f"), str(tmp_path / "w"), str(out))
+    bench.pmc_summary(str(tmp_path / "f"), str(tmp_path / "w"), str(out), kernel=kernel)
     text = out.read_text()
     # medians of the copy rows set the scales; the kernel rows are averaged
     kf = known / ((known / 2048) * 1024)
@@ -62,23 +63,52 @@ def test_pmc_summary_without_kernel_rows_fails(tmp_path):
     _counter_csv(str(tmp_path / "f" / "p_counter_collection.csv"), "FETCH_SIZE", [("void other(int)", 1.0)])
     _counter_csv(str(tmp_path / "w" / "p_counter_collection.csv"), "WRITE_SIZE", [("void other(int)", 1.0)])
     with pytest.raises(SystemExit):
-        bench.pmc_summary(str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "t.txt"))
+        bench.pmc_summary(str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "t.txt"),
+                          kernel=bench.ROOF["draft"][0])
 
 
-def test_stored_traffic_only_for_the_current_sources(tmp_path, monkeypatch):
+def test_stored_traffic_only_for_the_current_sources(tmp_path):
     path = tmp_path / "traffic.txt"
     digest = bench.kernel_source_digest()
     path.write_text(f"hbm bytes per launch: 38336215\nkernel source digest: {digest}\n")
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(path))
-    assert bench.stored_traffic(digest) == 38336215.0
-    assert bench.stored_traffic("0" * 16) is None
+    assert bench.stored_traffic(digest, str(path)) == 38336215.0
+    assert bench.stored_traffic("0" * 16, str(path)) is None
     path.write_text("hbm bytes per launch: 1\n")
-    assert bench.stored_traffic(digest) is None
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "absent.txt"))
-    assert bench.stored_traffic(digest) is None
+    assert bench.stored_traffic(digest, str(path)) is None
+    assert bench.stored_traffic(digest, str(tmp_path / "absent.txt")) is None
 
 
-def test_committed_traffic_summary_matches_its_kernel_name():
-    text = open(bench.TRAFFIC_FILE).read()
-    assert bench.ROOFLINE_KERNEL in text
-    assert re.search(r"hbm bytes per launch: \d+", text)
+def test_committed_traffic_summaries_match_their_kernel_names():
+    for mode, (kernel, _, _, path) in bench.ROOF.items():
+        if not os.path.exists(path):
+            pytest.skip(f"no counter summary for the {mode} kernel yet")
+        text = open(path).read()
+        assert kernel in text
+        assert re.search(r"hbm bytes per launch: \d+", text)
+
+
+def test_roofline_kernels_are_the_forward_instantiations():
+    # the names match the launcher's template instantiations in nl_fwd.hip
+    src = open(os.path.join(ROOT, "bit_nested_quantized_amd", "csrc", "nl_fwd.hip")).read()
+    assert "void fwd_kernel(const FwdArgs2 a)" in src
+    for kernel, bits, waves, _ in bench.ROOF.values():
+        assert kernel == f"fwd_kernel<{bits}, 1, {waves}, false>"
+
+
+def test_pstats_percentiles():
+    st = bench.pstats([float(v) for v in range(1, 101)])
+    assert st["us"] == 50.5 and st["samples"] == 100
+    assert abs(st["p10"] - 10.9) < 1e-9 and abs(st["p90"] - 90.1) < 1e-9
+
+
+def test_util_summary_reads_each_pass(tmp_path):
+    vk = f"void nl::{bench.ROOF['verify'][0]}(nl::FwdArgs2)"
+    dk = f"void nl::{bench.ROOF['draft'][0]}(nl::FwdArgs2)"
+    _counter_csv(str(tmp_path / "a" / "p_counter_collection.csv"), "VALUBusy", [(vk, 40.0), (vk, 60.0), (dk, 20.0)])
+    _counter_csv(str(tmp_path / "b" / "p_counter_collection.csv"), "SQ_WAVES", [(vk, 3072.0), (dk, 2048.0)])
+    out = tmp_path / "util.txt"
+    bench.util_summary([str(tmp_path / "a"), str(tmp_path / "b")], str(out))
+    text = out.read_text()
+    assert "VALUBusy: 50 (mean of 2 dispatches)" in text
+    assert "VALUBusy: 20 (mean of 1 dispatches)" in text
+    assert "SQ_WAVES: 3072" in text and "SQ_WAVES: 2048" in text

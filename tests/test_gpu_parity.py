@@ -50,8 +50,10 @@ def block(n):
 
 def run(nl, torch, lin, x, verify, L=None):
     L = L or nl.Linear(lin)
-    y = L.forward(to_dev(torch, x), verify)
+    ws = L.workspace(x.shape[0])
+    y = L.forward(to_dev(torch, x), verify, ws=ws)
     torch.cuda.synchronize()
+    assert nl.nested_linear_workspace_status(ws) == 0   # no wait gave up
     return y.cpu().numpy()
 
 
@@ -335,20 +337,23 @@ def make_moe(n_exp, d_out, d_in, bits, T, k, rho, two, cfg, shared=True):
     return experts, pt.astype(np.int32), off
 
 
-def run_grouped(nl, torch, experts, pt, off, x, verify):
+def run_grouped(nl, torch, experts, pt, off, x, verify, T=None):
+    """One grouped call twice on one workspace.  x holds x_rows rows (tokens,
+    or one per pair); T bounds the pairs of any one expert (default x_rows)."""
     Ls = [nl.Linear(e) for e in experts]
     g = nl.nested_linear_group_create([L.h for L in Ls])
     try:
-        P, T = len(pt), x.shape[0]
+        P, x_rows = len(pt), x.shape[0]
+        T = x_rows if T is None else T
         ws = torch.zeros(nl.nested_linear_group_workspace_bytes(g, P), dtype=torch.uint8, device="cuda")
         y = torch.full((P, experts[0]["d_out"]), float("nan"), dtype=torch.float32, device="cuda")
         fn = nl.nested_linear_verify_grouped if verify else nl.nested_linear_draft_grouped
         pt_d = torch.from_numpy(pt).to("cuda")
         off_d = torch.from_numpy(off).to("cuda")
         xd = to_dev(torch, x)
-        fn(g, pt_d, off_d, P, xd, T, y, ws)
+        fn(g, pt_d, off_d, P, xd, x_rows, T, y, ws)
         a = y.cpu().numpy()
-        fn(g, pt_d, off_d, P, xd, T, y, ws)   # same workspace again
+        fn(g, pt_d, off_d, P, xd, x_rows, T, y, ws)   # same workspace again
         b = y.cpu().numpy()
         torch.cuda.synchronize()
         assert int(ws[:COUNTER_BYTES].count_nonzero()) == 0
@@ -411,6 +416,28 @@ def test_grouped_partial_workgroups(nl, torch_cuda):
     for verify in (False, True):
         a, _, _ = run_grouped(nl, torch_cuda, experts, pt, off, x, verify)
         assert rel_err(a, oracle.forward_grouped(experts, pt, off, x, verify)) <= TOL
+
+
+@pytest.mark.parametrize("two", [False, True])
+@pytest.mark.parametrize("T", [16, 2])
+def test_grouped_down_projection_per_pair_rows(nl, torch_cuda, two, T):
+    # The MoE down projection: each pair's own 512-wide activation, so x has
+    # one row per pair (pair_token = 0..P-1) while no expert gets more than T
+    # pairs.  64 routed experts, top-8 of a T-token block plus the shared
+    # expert: P = 9 T rows of x.
+    experts, pt, off = make_moe(64, 2048, 512, 8, T, 8, 0.62, two, cfg=77 + T)
+    P = len(pt)
+    assert P == 9 * T
+    xp = synth.make_x(P, 512, cfg=77, idx=T)
+    ident = np.arange(P, dtype=np.int32)
+    for verify in (False, True):
+        a, b, _ = run_grouped(nl, torch_cuda, experts, ident, off, xp, verify, T=T)
+        assert rel_err(a, oracle.forward_grouped(experts, ident, off, xp, verify)) <= TOL
+        np.testing.assert_array_equal(a, b)
+        # pair p of expert e is expert e applied to x row p
+        e = int(np.searchsorted(off, P - 1, side="right") - 1)
+        ref = oracle.forward(experts[e], xp[P - 1:P], verify)
+        assert rel_err(a[P - 1:P], ref) <= TOL
 
 
 @pytest.mark.parametrize("T", [1, 2, 4])
