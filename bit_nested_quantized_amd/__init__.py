@@ -31,7 +31,7 @@ EXPORTS = (
     "nested_linear_info", "nested_linear_timing_begin", "nested_linear_timing_end",
     "nested_linear_last_error", "nested_linear_verify_multi", "nested_linear_draft_multi",
     "nested_linear_multi_workspace_bytes", "nested_linear_workspace_status", "nested_linear_set_tuning",
-    "nested_linear_describe_call", "nested_linear_stream_read",
+    "nested_linear_describe_call", "nested_linear_stream_read", "nested_linear_forward_static",
     "nested_encode_rotate", "nested_encode_quantize", "nested_encode_workspace_bytes", "nested_encode",
     "nested_encode_normalize", "nested_encode_fit_workspace_bytes", "nested_encode_fit_levels",
     "nested_w4w8_create", "nested_w4w8_destroy", "nested_w4w8_workspace_bytes", "nested_w4w8_verify",
@@ -105,6 +105,7 @@ def lib() -> ctypes.CDLL:
             "nested_linear_set_tuning": [i32, ctypes.c_double],
             "nested_linear_describe_call": [P, i32, i32, i32, i32, i32, ctypes.POINTER(i32), i32],
             "nested_linear_stream_read": [P, sz, P, i32, P],
+            "nested_linear_forward_static": [P, i32, P, i32, P, P],
             "nested_encode_rotate": [i32, i32, P, P, P, P, P],
             "nested_encode_quantize": [P, ctypes.POINTER(nl_codes), P],
             "nested_encode_workspace_bytes": [i32, i32, i32, ctypes.POINTER(sz)],
@@ -212,6 +213,11 @@ def nested_linear_workspace_status(ws, clear: bool = False, stream=None) -> int:
     e = ctypes.c_uint32(0)
     _check(lib().nested_linear_workspace_status(_ptr(ws), ctypes.byref(e), int(bool(clear)), _stream(stream)))
     return int(e.value)
+
+
+def nested_linear_forward_static(h, verify: bool, x, T: int, y, stream=None):
+    """Verify or draft forward on the library's static scratch (no allocation)."""
+    _check(lib().nested_linear_forward_static(h, int(bool(verify)), _ptr(x), int(T), _ptr(y), _stream(stream)))
 
 
 def nested_linear_stream_read(src, sink, grid: int = 0, stream=None):

@@ -832,6 +832,65 @@ static nl_status forward(nl_handle h, int verify, const void *x, int32_t T, floa
   return forward_n(hs, 1, verify, x, T, ys, ws, ws_bytes, stream, who);
 }
 
+// ---------------------------------------------------------------------------
+// Forward without allocation: the workspace is a static device array, one per
+// GPU, held until the process ends.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kScratchBytes];
+static std::mutex g_scratch_mu;
+static char *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this GPU's copy of the array, looked up once per device
+// with that device current (the array's name is a host-side stand-in).
+static nl_status scratch_on_current_device(char **out) {
+  int dev = 0;
+  HIP_OR_FAIL(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(NL_EUNSUPPORTED, "forward_static: device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(NL_EHIP, "forward_static: hipGetSymbolAddress failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = (char *)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return NL_OK;
+}
+
+// Zero the first n words (the counters a call uses; a fill kernel rather than
+// a memset, so that the call can be captured into a graph).
+__global__ __launch_bounds__(256) void clear_words_kernel(uint32_t *p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
+}
+
+extern "C" nl_status nested_linear_forward_static(nl_handle h, int32_t verify, const void *x, int32_t T, float *y,
+                                                  void *stream) {
+  const char *who = "forward_static";
+  if (!valid(h)) return fail(NL_EINVAL, "%s: invalid handle", who);
+  if (verify && !h->bits) return fail(NL_EINVAL, "%s: the linear has no residual (draft only)", who);
+  if (T < 1) return fail(NL_EINVAL, "%s: T must be >= 1 (got %d)", who, T);
+  if (T > NL_MAX_T) return fail(NL_EUNSUPPORTED, "%s: T = %d exceeds %d", who, T, NL_MAX_T);
+  const CallShape cs[1] = {shape_of(h)};
+  const Plan2 p = make_plan2(cs, 1, T, verify ? h->bits : 0);
+  if (p.total > kScratchBytes)
+    return fail(NL_EUNSUPPORTED, "%s: the call needs %zu bytes of scratch, beyond the library's %zu", who, p.total,
+                kScratchBytes);
+  if (p.n_ctr > kCtrLines) return fail(NL_EUNSUPPORTED, "%s: the call needs %d counters (> %d)", who, p.n_ctr, kCtrLines);
+  char *ws = nullptr;
+  const nl_status st = scratch_on_current_device(&ws);
+  if (st != NL_OK) return st;
+  // the previous call on this GPU left its counters at zero unless a wait gave
+  // up; clear them anyway so that no earlier failure carries over
+  const int words = p.n_ctr * kCtrStride;
+  hipLaunchKernelGGL(clear_words_kernel, dim3(std::min(64, (words + 255) / 256)), dim3(256), 0,
+                     (hipStream_t)stream, (uint32_t *)ws, words);
+  HIP_OR_FAIL(hipGetLastError());
+  return forward(h, verify ? 1 : 0, x, T, y, ws, kScratchBytes, stream, who);
+}
+
 extern "C" nl_status nested_linear_describe_call(const int32_t *d_out, int32_t n, int32_t d_in, int32_t bits,
                                                  int32_t two_sided, int32_t T, int32_t *out, int32_t out_len) {
   if (!d_out || !out || n < 1 || n > kMaxJobs || T < 1 || T > NL_MAX_T || d_in < NL_GROUP || d_in % NL_GROUP ||

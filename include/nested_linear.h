@@ -119,6 +119,26 @@ nl_status nested_linear_destroy(nl_handle h);
 nl_status nested_linear_workspace_bytes(nl_handle h, int32_t T_max, size_t *bytes);
 
 /*
+ * Forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * verify (verify != 0) or draft forward of nested_linear_verify / _draft, with
+ * the workspace taken from a static device array inside the library instead of
+ * a caller's buffer.  The array is 32 MiB per GPU, held from the library's
+ * load until the process ends; a call whose plan needs more (a very large
+ * d_out with large T, two-sided) fails with NL_EUNSUPPORTED and must use the
+ * workspace form.  Each call first clears the counters it uses with a small
+ * kernel (two launches per call, both capturable), so a wait that gave up in
+ * an earlier call carries over nothing; such a call's outputs are NaN (this
+ * form has no readable error word).  Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (other streams, other host threads)
+ * race and must be serialised by the caller.  Arguments and other errors are
+ * those of nested_linear_verify.  The call allocates nothing: no hipMalloc,
+ * hipFree or allocating library routine.
+ */
+nl_status nested_linear_forward_static(nl_handle h, int32_t verify, const void *x_bf16, int32_t T, float *y,
+                                       void *hip_stream);
+
+/*
  * Verify forward (POC section 4): y = S_o H_o ((Q_base + Q_resid) H_i S_i x)
  * for T tokens, or the rotated-basis y~ when the linear has no sign_out.
  *   x   [T][d_in] bf16 bit patterns (row-major), 16-byte aligned (rows are
