@@ -42,15 +42,17 @@ BITS = 6
 HBM_PEAK_GBPS = 8000.0
 LAYERS = 32             # decoder layers of the 7B/8B-class model
 ERR_ROWS = 512          # output rows per projection checked against the oracle in each case
-ROOFLINE_TS = (8, 16)   # launches of the roofline kernels (one 16-token tile, rotation workgroups)
-FWD_SOURCES = ("nl_fwd.hip", "nl_fwd.h", "nl_dev.h", "nl_layout.h")
-ROOF = {  # mode -> (kernel, bits, waves, traffic summary)
-    "verify": ("fwd_kernel<6, 1, 12, false>", 6, 12,
-               os.path.join(ROOT, "profiles", "fwd_kernel_6bit_verify_T8_T16_proj7b8b_traffic.txt")),
-    "draft": ("fwd_kernel<0, 1, 8, false>", 0, 8,
-              os.path.join(ROOT, "profiles", "fwd_kernel_draft_T8_T16_proj7b8b_traffic.txt")),
+FWD_SOURCES = ("nl_fwd.hip", "nl_fwd.h", "nl_dev.h", "nl_layout.h", "nl_kernels.hip", "nl_kernels.h")
+# mode -> (kernel, bits, the T of its launches, traffic summary).  The verify
+# step's largest share of time is the single launch at T = 4 and 8; the draft
+# (not in the step) runs the staged-x' launch at every T.
+ROOF = {
+    "verify": ("fwd_kernel<6, 1, 12, false>", 6, (4, 8),
+               os.path.join(ROOT, "profiles", "fwd_kernel_6bit_verify_T4_T8_proj7b8b_traffic.txt")),
+    "draft": ("forward_kernel<0, 1, 4>", 0, (8, 16),
+              os.path.join(ROOT, "profiles", "forward_kernel_draft_T8_T16_proj7b8b_traffic.txt")),
 }
-UTIL_FILE = os.path.join(ROOT, "profiles", "fwd_kernel_utilisation_T8_T16_proj7b8b.txt")
+UTIL_FILE = os.path.join(ROOT, "profiles", "forward_utilisation_roofline_launches_proj7b8b.txt")
 STREAM_BYTES = 4 << 30  # streaming-read reference buffer (16x the Infinity Cache)
 ENC_BITS = 7            # the encoder leg writes 7-bit residuals (the post's bf16-noise-floor width)
 ENC_KERNEL = "tile_kernel<0, 7,"   # fused 7-bit encode, any block size (kernel-name match)
@@ -190,20 +192,21 @@ def stream_ref_leg(nl, torch, reps=8):
 # --- the roofline kernels -------------------------------------------------------
 
 def roofline_leg(nl, call, ncopy, stream, bpw, mode):
-    """Roofline of one forward kernel: eager launches at T = 8 and 16 over the
-    four projections (every one of them runs that kernel), each timed by a
-    HIP event pair attached to its own dispatch (the library's timing hook),
-    so a duration is the kernel's execution as the kernel trace reports it."""
+    """Roofline of one forward kernel: eager launches over the four
+    projections at the T values that select it, each timed by a HIP event
+    pair attached to its own dispatch (the library's timing hook), so a
+    duration is the kernel's execution as the kernel trace reports it."""
     import torch
-    kernel, bits, waves, traffic_file = ROOF[mode]
+    kernel, bits, ts, traffic_file = ROOF[mode]
     verify = mode == "verify"
-    for _, o, i in SHAPES:
-        for T in ROOFLINE_TS:
-            p = nl.nested_linear_describe_call([o], i, bits, False, T)
-            assert p["mt"] == 1 and not p["local"] and p["waves"] == waves, (o, i, T, p)
+    if kernel.startswith("fwd_kernel"):
+        for _, o, i in SHAPES:
+            for T in ts:
+                p = nl.nested_linear_describe_call([o], i, bits, False, T)
+                assert p["mt"] == 1 and not p["local"] and p["waves"] == 12, (o, i, T, p)
     plan = []
     for si, (name, o, i) in enumerate(SHAPES):
-        for T in ROOFLINE_TS:
+        for T in ts:
             for r in range(2):
                 for cp in range(ncopy):
                     plan.append((si, cp, T, o * i * bpw(verify)))
@@ -224,7 +227,7 @@ def roofline_leg(nl, call, ncopy, stream, bpw, mode):
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": None if traffic is None else round(traffic),
-            "kernel": f"{kernel} ({mode}, T = 8 and 16, the four projections)",
+            "kernel": f"{kernel} ({mode}, T = {' and '.join(map(str, ts))}, the four projections)",
             "avg_launch_us": round(avg_us, 2), "avg_algorithmic_bytes": int(avg_bytes),
             "launches": len(durs), "timing": "HIP events attached to each dispatch",
             "kernel_source_digest": digest}
@@ -879,7 +882,7 @@ def copy_calibration(torch):
 
 
 
-ROOFLINE_TITLE = ("{mode}, T = 8 and 16, 4096x4096, 1024x4096, 14336x4096,\n"
+ROOFLINE_TITLE = ("{mode}, T = {ts}, 4096x4096, 1024x4096, 14336x4096,\n"
                   "4096x14336, 2-bit base{resid}, one-sided")
 W48_TITLE = ("verify at T = 16, W4 base + 4-bit refinement planes of 4096x4096, 1024x4096,\n"
              "14336x4096, 4096x14336")
@@ -953,8 +956,9 @@ def util_summary(dirs, out_path):
     """Utilisation counters of the two roofline kernels from rocprofv3 --pmc
     runs of `bench.py --roofline-only` (one pass per directory): the mean per
     dispatch of each counter found."""
-    lines = ["Utilisation counters of the forward kernels (verify and draft, T = 8 and 16, 4096x4096, 1024x4096,",
-             "14336x4096, 4096x14336, one-sided), mean per dispatch over the --roofline-only launches",
+    lines = ["Utilisation counters of the roofline kernels (verify: the single launch at T = 4 and 8; draft: the",
+             "staged-x' launch at T = 8 and 16; 4096x4096, 1024x4096, 14336x4096, 4096x14336, one-sided),",
+             "mean per dispatch over the --roofline-only launches",
              "commands (one counter pass each):"]
     passes = {0: "VALUBusy MfmaUtil OccupancyPercent MemUnitStalled TA_BUSY_avr",
               1: "MeanOccupancyPerCU SQ_WAIT_INST_ANY SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_VMEM_RD SQ_WAVES"}
@@ -1011,9 +1015,10 @@ def main():
                     help="write the W4/W8 kernel's traffic summary from two rocprofv3 --pmc runs of --w4w8-only")
     args = ap.parse_args()
     if args.pmc_summary:
-        for mode, (kernel, bits, _, path) in ROOF.items():
+        for mode, (kernel, bits, ts, path) in ROOF.items():
             pmc_summary(*args.pmc_summary, path, kernel=kernel,
-                        title=ROOFLINE_TITLE.format(mode=mode, resid=" + 6-bit residual" if bits else ""))
+                        title=ROOFLINE_TITLE.format(mode=mode, ts=" and ".join(map(str, ts)),
+                                                    resid=" + 6-bit residual" if bits else ""))
         return
     if args.util_summary:
         util_summary(args.util_summary, UTIL_FILE)

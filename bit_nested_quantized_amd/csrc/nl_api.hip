@@ -459,7 +459,12 @@ extern "C" nl_status nested_linear_finish(nl_handle h, int32_t T, float *y, void
   return ok();
 }
 
-// Counter bases, grid sizes and semaphore lines of one single-launch call.
+// Waits between workgroups: polls before a wait gives up, and extra tokens a
+// wait asks for (set from the host so a lost hand-over can be shown).
+static uint32_t g_spin_limit = 1u << 22;
+static uint32_t g_wait_extra = 0;
+
+// Counter bases, grid sizes and semaphore lines of one call.
 static void fill_launch(FwdArgs &f, const Plan &p, int n_linears, char *ws, float *y, int d_out) {
   f.hv.ctr = (uint32_t *)ws;
   f.hv.y = y;
@@ -482,6 +487,8 @@ static void fill_launch(FwdArgs &f, const Plan &p, int n_linears, char *ws, floa
   f.g.slots = n_linears > 1 && 2 * cap < n_linears;
   f.n_gemm = (f.g.slots ? cap : n_linears) * per;
   f.hv.n_rot = f.n_rot;
+  f.hv.spin_limit = g_spin_limit;
+  f.hv.wait_extra = g_wait_extra;
   f.g.out = p.mode == kOutDirect ? y : (float *)(ws + p.o_part);
   f.g.split_stride = (size_t)p.rows * d_out;
   f.fin.y = y;
@@ -589,8 +596,12 @@ struct Plan2 {
 // the cost model's rates.
 static int g_t_S = 0, g_t_rt = 0, g_t_kw = 0, g_t_local = 2, g_t_cus = 256, g_t_nw = 0;
 static double g_t_lat_us = 2.0, g_t_hbm_gbs = 6500.0, g_t_split_us = 1.5, g_t_xdma_gbs = 100.0;
-static uint32_t g_spin_limit = 1u << 22;
-static uint32_t g_wait_extra = 0;
+// Single-linear calls with T at or above this use the staged-x' launch
+// (forward_kernel: x' passes through LDS a chunk at a time, so no split of K is
+// forced by T), below it the single launch that holds the K-range's x' in LDS.
+// Measured on the 7B/8B-class projections: the latter is ahead for verify up
+// to T = 8, the former from T = 16 on and for the draft at every T.
+static int g_t_staged_v = 9, g_t_staged_d = 1;
 
 // Bytes of one tile-chunk (16 rows x 512 columns) in a pass.
 static double tc_bytes(int bits) { return 16.0 * 512.0 * (0.265625 + (bits ? bits / 8.0 + 1.0 / 64.0 : 0.0)); }
@@ -683,8 +694,8 @@ static Plan2 make_plan2(const CallShape *hs, int n, int T, int bits) {
   p.T = T;
   p.mt = mt_for(T);
   // one token tile: eight waves with a four-set ring for the draft (its sets
-  // are small), twelve for verify; the knob forces either
-  p.nw = p.mt != 1 ? fwd_waves(p.mt) : (g_t_nw == 8 || (g_t_nw == 0 && bits == 0)) ? 8 : 12;
+  // are small; the knob can ask for twelve), twelve for verify
+  p.nw = p.mt != 1 ? fwd_waves(p.mt) : (bits == 0 && g_t_nw != 12) ? 8 : 12;
   p.blob = blob_bytes(T);
   p.tm = blob_tm(T);
   const CallShape *h0 = &hs[0];
@@ -824,9 +835,52 @@ static nl_status forward_n(const nl_linear *const *hs, int n, int verify, const 
   return ok();
 }
 
+// The staged-x' launch of one linear (forward_kernel): rotation workgroups
+// write x' to the workspace, contraction workgroups stage it through LDS one
+// chunk at a time beside their weight stream.
+static nl_status forward_staged(nl_handle h, int verify, const void *x, int32_t T, float *y, void *ws,
+                                size_t ws_bytes, void *stream, const char *who) {
+  Plan p;
+  nl_status st = check_call(h, who, verify, T, ws, ws_bytes, &p);
+  if (st != NL_OK) return st;
+  if (!x || !y) return fail(NL_EINVAL, "%s: NULL x or y", who);
+  if ((uintptr_t)x & 15) return fail(NL_EINVAL, "%s: x must be 16-byte aligned", who);
+  char *w = (char *)ws;
+  FwdArgs f;
+  memset(&f, 0, sizeof f);
+  f.rot = rot_args(h, x, T, w, p);
+  GemmArgs &g = f.g;
+  g.lin = h->dev;
+  g.xh = (const uint16_t *)(w + p.o_xh);
+  g.meta = (const float *)(w + p.o_meta);
+  g.T = T;
+  g.d_out = h->d_out;
+  g.n_tiles = h->n_tiles;
+  g.n_chunks = h->n_chunks;
+  g.Kp = h->n_chunks * kChunk;
+  g.Gp = h->n_chunks * 4;
+  g.cps = p.cps;
+  g.ldo = h->d_out;
+  g.n_rb = p.n_rb;
+  g.n_experts = 1;
+  f.fin.sign_out = h->dev.sign_out;
+  f.fin.b = h->b_out;
+  f.fin.lb = log2i(h->b_out);
+  f.fin.rsqrt_b = (float)(1.0 / std::sqrt((double)h->b_out));
+  fill_launch(f, p, 1, w, y, h->d_out);
+  const int n_fin = p.mode == kOutTwoSided ? finish_workgroups(T, h->d_out, p.sb_rows) : 0;
+  hipEvent_t e0, e1;
+  timing_slot((hipStream_t)stream, &e0, &e1);
+  HIP_OR_FAIL(launch_forward(f, verify ? h->bits : 0, p.mt, p.tw, n_fin, (hipStream_t)stream, e0, e1));
+  return ok();
+}
+
+static bool use_staged(int verify, int T) { return T >= (verify ? g_t_staged_v : g_t_staged_d); }
+
 static nl_status forward(nl_handle h, int verify, const void *x, int32_t T, float *y, void *ws,
                          size_t ws_bytes, void *stream, const char *who) {
   if (!valid(h)) return fail(NL_EINVAL, "%s: invalid handle", who);
+  if (use_staged(verify, T) && T <= NL_MAX_T) return forward_staged(h, verify, x, T, y, ws, ws_bytes, stream, who);
   const nl_linear *hs[1] = {h};
   float *ys[1] = {y};
   return forward_n(hs, 1, verify, x, T, ys, ws, ws_bytes, stream, who);
@@ -873,18 +927,29 @@ extern "C" nl_status nested_linear_forward_static(nl_handle h, int32_t verify, c
   if (verify && !h->bits) return fail(NL_EINVAL, "%s: the linear has no residual (draft only)", who);
   if (T < 1) return fail(NL_EINVAL, "%s: T must be >= 1 (got %d)", who, T);
   if (T > NL_MAX_T) return fail(NL_EUNSUPPORTED, "%s: T = %d exceeds %d", who, T, NL_MAX_T);
-  const CallShape cs[1] = {shape_of(h)};
-  const Plan2 p = make_plan2(cs, 1, T, verify ? h->bits : 0);
-  if (p.total > kScratchBytes)
-    return fail(NL_EUNSUPPORTED, "%s: the call needs %zu bytes of scratch, beyond the library's %zu", who, p.total,
+  size_t total;
+  int n_ctr;
+  if (use_staged(verify, T)) {
+    const Plan p = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, h->b_out, T, mt_for(T), 1, T,
+                             tile_waves(mt_for(T)));
+    total = p.total;
+    n_ctr = p.n_ctr;
+  } else {
+    const CallShape cs[1] = {shape_of(h)};
+    const Plan2 p = make_plan2(cs, 1, T, verify ? h->bits : 0);
+    total = p.total;
+    n_ctr = p.n_ctr;
+  }
+  if (total > kScratchBytes)
+    return fail(NL_EUNSUPPORTED, "%s: the call needs %zu bytes of scratch, beyond the library's %zu", who, total,
                 kScratchBytes);
-  if (p.n_ctr > kCtrLines) return fail(NL_EUNSUPPORTED, "%s: the call needs %d counters (> %d)", who, p.n_ctr, kCtrLines);
+  if (n_ctr > kCtrLines) return fail(NL_EUNSUPPORTED, "%s: the call needs %d counters (> %d)", who, n_ctr, kCtrLines);
   char *ws = nullptr;
   const nl_status st = scratch_on_current_device(&ws);
   if (st != NL_OK) return st;
   // the previous call on this GPU left its counters at zero unless a wait gave
   // up; clear them anyway so that no earlier failure carries over
-  const int words = p.n_ctr * kCtrStride;
+  const int words = n_ctr * kCtrStride;
   hipLaunchKernelGGL(clear_words_kernel, dim3(std::min(64, (words + 255) / 256)), dim3(256), 0,
                      (hipStream_t)stream, (uint32_t *)ws, words);
   HIP_OR_FAIL(hipGetLastError());
@@ -976,6 +1041,8 @@ extern "C" nl_status nested_linear_set_tuning(int32_t knob, double value) {
     case NL_TUNE_SPIN_LIMIT: g_spin_limit = value >= 1 ? (uint32_t)value : (1u << 22); break;
     case NL_TUNE_WAIT_EXTRA: g_wait_extra = value >= 0 ? (uint32_t)value : 0u; break;
     case NL_TUNE_WAVES: g_t_nw = ((int)value == 8 || (int)value == 12) ? (int)value : 0; break;
+    case NL_TUNE_STAGED_T_VERIFY: g_t_staged_v = value > 0 ? (int)value : 9; break;
+    case NL_TUNE_STAGED_T_DRAFT: g_t_staged_d = value > 0 ? (int)value : 1; break;
     default: return fail(NL_EINVAL, "set_tuning: unknown knob %d", knob);
   }
   return ok();
@@ -1084,7 +1151,7 @@ extern "C" nl_status nested_linear_group_destroy(nl_group_handle g) {
 static Plan group_plan(nl_group_handle g, int P, int T) {
   // short experts (K of at most two chunks): eight tile waves, half the
   // workgroups; longer ones keep the deeper register ring of four
-  const int tw = T > kLocalTokens && g->n_chunks <= 2 ? 8 : tile_waves(mt_for(T));
+  const int tw = T > kLocalTokens && g->n_chunks <= 2 && mt_for(T) < 4 ? 8 : tile_waves(mt_for(T));
   return make_plan(g->d_out, g->n_tiles, g->n_chunks, g->has_sign_out, g->b_out, P, mt_for(T), g->n, T, tw);
 }
 

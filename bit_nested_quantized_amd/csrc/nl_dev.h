@@ -41,6 +41,29 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// The barrier of the whole workgroup, as a policy of the transforms below.
+struct WgBar {
+  __device__ __forceinline__ void sync() { lds_barrier(); }
+};
+
+// A barrier among the 4 waves of one 256-thread group through an LDS counter
+// (zero at the group's start), for transforms run by some waves while the
+// others are held up issuing memory requests: an s_barrier would wait for
+// those.  Each sync adds one per wave and waits for 4 more arrivals.
+struct GroupBar {
+  uint32_t addr;  // LDS byte address of the counter
+  uint32_t n;     // arrivals expected by the next sync
+  __device__ __forceinline__ void sync() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS writes have landed
+    n += 4;
+    if ((threadIdx.x & 63) == 0)
+      __hip_atomic_fetch_add((NL_LOCAL uint32_t *)(size_t)addr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    while (*(volatile NL_LOCAL uint32_t *)(size_t)addr < n) {
+    }
+    asm volatile("" ::: "memory");
+  }
+};
+
 // ===========================================================================
 // Workgroup Walsh-Hadamard transforms (POC section 1: Sylvester H, applied
 // block-diagonally).  A workgroup of 256 threads transforms 4096 values:
@@ -77,8 +100,8 @@ __device__ __forceinline__ void bfly16(float (&v)[16], int bit) {
 // both compile-time, so every LDS address is a base plus an immediate.
 // xch: this task's LDS (SB + SB/16 floats).  idle: a thread (uniformly per
 // wave) that only keeps the barrier count.
-template <int N, int LB>
-__device__ __forceinline__ void fwht_bt(float (&v)[16], float *xch, int lt, bool idle) {
+template <int N, int LB, class B>
+__device__ __forceinline__ void fwht_bt(float (&v)[16], float *xch, int lt, bool idle, B &bar) {
   constexpr int TPS = 1 << (N - 4);
 #pragma unroll
   for (int q = 0; q < 4; ++q)
@@ -87,22 +110,22 @@ __device__ __forceinline__ void fwht_bt(float (&v)[16], float *xch, int lt, bool
   float *pb = xch + lds_pad(16 * lt);             // B: + j
   float *pc = xch + lds_pad(cbase);               // C: + 17 j
   float *pa = xch + lt + (lt >> 4);               // A: + (TPS + TPS / 16) j
-  lds_barrier();
+  bar.sync();
   if (!idle)
 #pragma unroll
     for (int j = 0; j < 16; ++j) pb[j] = v[j];
-  lds_barrier();
+  bar.sync();
   if (!idle)
 #pragma unroll
     for (int j = 0; j < 16; ++j) v[j] = pc[17 * j];
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     if (4 + q < LB) bfly16(v, q);
-  lds_barrier();
+  bar.sync();
   if (!idle)
 #pragma unroll
     for (int j = 0; j < 16; ++j) pc[17 * j] = v[j];
-  lds_barrier();
+  bar.sync();
   if (!idle)
 #pragma unroll
     for (int j = 0; j < 16; ++j) v[j] = pa[(TPS + TPS / 16) * j];
@@ -111,11 +134,11 @@ __device__ __forceinline__ void fwht_bt(float (&v)[16], float *xch, int lt, bool
     constexpr int base = N - 4;
     if (base + q >= 8 && base + q < LB) bfly16(v, q);
   }
-  lds_barrier();
+  bar.sync();
   if (!idle)
 #pragma unroll
     for (int j = 0; j < 16; ++j) pa[(TPS + TPS / 16) * j] = v[j];
-  lds_barrier();
+  bar.sync();
   if (!idle)
 #pragma unroll
     for (int j = 0; j < 16; ++j) v[j] = pb[j];
@@ -123,15 +146,20 @@ __device__ __forceinline__ void fwht_bt(float (&v)[16], float *xch, int lt, bool
 
 // The transform for a task of SB = max(2^lb, 512) points (one uniform
 // dispatch on the block size; lb is 7..12 since d_in is a multiple of 128).
-__device__ __forceinline__ void fwht_b(float (&v)[16], float *xch, int lt, int lb, bool idle) {
+template <class B>
+__device__ __forceinline__ void fwht_b(float (&v)[16], float *xch, int lt, int lb, bool idle, B &bar) {
   switch (lb) {
-    case 7: fwht_bt<9, 7>(v, xch, lt, idle); break;
-    case 8: fwht_bt<9, 8>(v, xch, lt, idle); break;
-    case 9: fwht_bt<9, 9>(v, xch, lt, idle); break;
-    case 10: fwht_bt<10, 10>(v, xch, lt, idle); break;
-    case 11: fwht_bt<11, 11>(v, xch, lt, idle); break;
-    default: fwht_bt<12, 12>(v, xch, lt, idle); break;
+    case 7: fwht_bt<9, 7>(v, xch, lt, idle, bar); break;
+    case 8: fwht_bt<9, 8>(v, xch, lt, idle, bar); break;
+    case 9: fwht_bt<9, 9>(v, xch, lt, idle, bar); break;
+    case 10: fwht_bt<10, 10>(v, xch, lt, idle, bar); break;
+    case 11: fwht_bt<11, 11>(v, xch, lt, idle, bar); break;
+    default: fwht_bt<12, 12>(v, xch, lt, idle, bar); break;
   }
+}
+__device__ __forceinline__ void fwht_b(float (&v)[16], float *xch, int lt, int lb, bool idle) {
+  WgBar bar;
+  fwht_b(v, xch, lt, lb, idle, bar);
 }
 
 // v: layout A on entry, layout B on exit (the output rotation, whose input

@@ -85,10 +85,10 @@ struct FwdArgs2 {
 __host__ __device__ constexpr int fwd_waves(int mt) { return mt <= 2 ? 12 : 8; }
 
 // Register sets in a wave's weight ring (within 168 registers for twelve
-// waves, 256 for eight).  The twelve-wave local form keeps its transform's
-// registers live beside the ring, so its verify ring has one set.
+// waves, 256 for eight).  In the local form the waves that rotate x request
+// their sets only after the transform, so no wave holds both.
 __host__ __device__ constexpr int fwd_ring_sets(int bits, int mt, bool local, int nw) {
-  return nw == 8 && mt == 1 ? 4 : (mt == 1 ? (bits == 0 ? 4 : (local ? 1 : 2)) : (bits == 0 ? 3 : 2));
+  return (void)local, nw == 8 && mt == 1 ? 4 : (mt == 1 ? (bits == 0 ? 4 : 2) : (bits == 0 ? 3 : 2));
 }
 
 hipError_t launch_forward2(const FwdArgs2 &a, int bits, int mt, int nw, bool local, size_t lds, hipStream_t s,

@@ -114,12 +114,14 @@ struct XOut {
   int e;     // scale exponent: the chunk was multiplied by 2^e
 };
 // A wave none of whose lanes has a task (wave-uniform) only keeps the
-// transform's barrier count and returns zeros.
-__device__ __forceinline__ XOut rotate16(const XRaw &xr, float *xch, int lt, int lb, bool has_task) {
+// transform's barrier count and returns zeros.  B: the barrier the transform
+// synchronises with (the workgroup's, or its own 4-wave group's).
+template <class B>
+__device__ __forceinline__ XOut rotate16(const XRaw &xr, float *xch, int lt, int lb, bool has_task, B &bar) {
   XOut o;
   if (!__any(has_task)) {
 #pragma unroll
-    for (int k = 0; k < 6; ++k) lds_barrier();  // the barriers of fwht_bt
+    for (int k = 0; k < 6; ++k) bar.sync();  // the barriers of fwht_bt
 #pragma unroll
     for (int h = 0; h < 8; ++h) o.w[h] = 0u;
     o.gs = 0.f;
@@ -128,7 +130,7 @@ __device__ __forceinline__ XOut rotate16(const XRaw &xr, float *xch, int lt, int
   }
   float v[16];
   cvt_x16(v, xr);
-  fwht_b(v, xch, lt, lb, false);
+  fwht_b(v, xch, lt, lb, false, bar);
   float m = 0.f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(v[j]));
@@ -187,7 +189,8 @@ __device__ void rot_role(const FwdArgs2 &a, int b, char *smem) {
     }
   const XRaw xr = load_x16(a.x, sign, valid ? t : -1, k0, a.d_in);
   float *xch = reinterpret_cast<float *>(smem + kLdsX + grp * kFwhtArea) + tl * (SB + (SB >> 4));
-  const XOut o = rotate16(xr, xch, lt, a.lb_in, valid);
+  WgBar bar;
+  const XOut o = rotate16(xr, xch, lt, a.lb_in, valid, bar);
   if (valid) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(a.ws, 0, 0x7FFFFFF0, 0x00020000);
     const int c = k0 >> 9, g = (k0 >> 7) & 3, q = (k0 >> 5) & 3, s0 = (k0 >> 3) & 3;
@@ -216,48 +219,49 @@ struct LocalX {
   XRaw r[2];
 };
 
-template <int NW>
-__device__ __forceinline__ void local_tasks(const FwdArgs2 &a, int c_lo, int c_hi, int p, int &t, int &kb,
-                                            bool &valid) {
-  constexpr int G = NW / 4;
-  const int grp = threadIdx.x >> 8, tid = threadIdx.x & 255;
+// Task of rotating group rg (of nrg) in pass p: (token t, superblock at
+// column kb); 4096 / SB tasks per group and pass.
+__device__ __forceinline__ void local_tasks(const FwdArgs2 &a, int c_lo, int c_hi, int p, int rg, int nrg, int &t,
+                                            int &kb, bool &valid) {
+  const int tid = threadIdx.x & 255;
   const int SB = a.SB, TPS = SB >> 4, per_grp = 4096 / SB;
   const int tl = tid / TPS;
   const int sb0 = (c_lo * kChunk) / SB, sb1 = (c_hi * kChunk + SB - 1) / SB, nsb = sb1 - sb0;
-  const int task = (p * G + grp) * per_grp + tl;
+  const int task = (p * nrg + rg) * per_grp + tl;
   valid = task < a.T * nsb;
   t = valid ? task / nsb : 0;
   kb = (sb0 + (valid ? task % nsb : 0)) * SB;
 }
 
 template <int NW>
-__device__ __forceinline__ void local_load(const FwdArgs2 &a, const int8_t *sign, int c_lo, int c_hi, int np,
-                                           LocalX<NW> &lx) {
+__device__ __forceinline__ void local_load(const FwdArgs2 &a, const int8_t *sign, int c_lo, int c_hi, int np, int rg,
+                                           int nrg, LocalX<NW> &lx) {
   const int lt = (threadIdx.x & 255) % (a.SB >> 4);
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     int t, kb;
     bool valid;
-    local_tasks<NW>(a, c_lo, c_hi, p, t, kb, valid);
+    local_tasks(a, c_lo, c_hi, p, rg, nrg, t, kb, valid);
     lx.r[p] = load_x16(a.x, sign, (valid && p < np) ? t : -1, kb + 16 * lt, a.d_in);
   }
 }
 
+// The rotating group's transforms and their blob writes; bar: the group's barrier.
 template <int NW>
-__device__ __forceinline__ void local_rotate(const FwdArgs2 &a, int c_lo, int c_hi, int np, const LocalX<NW> &lx,
-                                             char *smem, int fwht_off) {
-  const int grp = threadIdx.x >> 8, tid = threadIdx.x & 255;
+__device__ __forceinline__ void local_rotate(const FwdArgs2 &a, int c_lo, int c_hi, int np, int rg, int nrg,
+                                             const LocalX<NW> &lx, char *smem, int fwht_off, GroupBar &bar) {
+  const int tid = threadIdx.x & 255;
   const int SB = a.SB, TPS = SB >> 4;
   const int lt = tid % TPS, tl = tid / TPS;
   const int T = a.T;
-  float *xch = reinterpret_cast<float *>(smem + fwht_off + grp * kFwhtArea) + tl * (SB + (SB >> 4));
+  float *xch = reinterpret_cast<float *>(smem + fwht_off + rg * kFwhtArea) + tl * (SB + (SB >> 4));
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     if (p >= np) break;  // uniform
     int t, kb;
     bool valid;
-    local_tasks<NW>(a, c_lo, c_hi, p, t, kb, valid);
-    const XOut o = rotate16(lx.r[p], xch, lt, a.lb_in, valid);
+    local_tasks(a, c_lo, c_hi, p, rg, nrg, t, kb, valid);
+    const XOut o = rotate16(lx.r[p], xch, lt, a.lb_in, valid, bar);
     const int k0 = kb + 16 * lt, c = k0 >> 9;
     if (valid && c >= c_lo && c < c_hi) {
       const int g = (k0 >> 7) & 3, q = (k0 >> 5) & 3, s0 = (k0 >> 3) & 3;
@@ -299,15 +303,6 @@ __device__ void con_role(const FwdArgs2 &a, int cb, char *smem) {
   const int T = a.T;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(NL_LOCAL void *)smem;
 
-  // ---- byte table into LDS (local form: wave 0, two 1 KiB copies; the
-  // hand-over form copies it beside x')
-  if (LOCAL && wave == 0) {
-    const void *src = sgpr_ptr(L.lut256);
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-      __builtin_amdgcn_global_load_lds((const NL_GLOBAL void *)((const char *)src + q * 1024 + lane * 16),
-                                       (NL_LOCAL void *)(size_t)(lds0 + kLdsLut + q * 1024), 16, 0, 0);
-  }
 
   // ---- weight ring: raw buffer loads through descriptors that end at the
   // wave's last chunk (requests past it return zeros with no memory access).
@@ -348,29 +343,67 @@ __device__ void con_role(const FwdArgs2 &a, int cb, char *smem) {
   };
   // Order of the wave's memory requests.  A CU's requests are taken in
   // issue order, so a small load issued behind the weight stream waits for
-  // it.  The local form therefore issues its activation loads first; the
-  // hand-over form requests one weight set per wave before the wait and the
-  // x' copy before the remaining sets.  Each wave then waits only for what
-  // it issued before its last weight loads (in-order counter), and the
-  // barrier makes every wave's copy visible.
+  // it.  The local form therefore issues its activation loads first; in the
+  // hand-over form every wave but the poller requests all of its ring before
+  // the wait (the weights stream while x is rotated elsewhere) and its share
+  // of the x' copy after it; the poller requests its ring after its share.
+  // Each wave then waits for what it issued before its last weight loads
+  // (in-order counter), and the barrier makes every wave's copy visible.
   constexpr int LW = kBasePieces + 1 + (BITS > 0 ? BITS + 1 : 0);  // loads per set
-  constexpr int NS0 = LOCAL ? NS : (BITS > 0 ? 1 : 2);              // sets before the x' copy
+  constexpr int NS0 = NS;                                           // sets before the x' copy
   static_assert(LW * NS <= 63, "wait count");
   WRegs<BITS> w[NS];
   bool okw = true;
   if constexpr (LOCAL) {
+    // The last nrg groups of 4 waves rotate x (the first waves hold the row
+    // tiles, so these are the idle ones when there are idle waves); they
+    // request only x and the byte table before the transform, synchronise
+    // among themselves through LDS counters (an s_barrier would also wait for
+    // the waves still issuing weight requests), then request their own weight
+    // sets.  The other waves request their sets at once and wait on an LDS
+    // count of the rotating waves that are done.
     constexpr int G = NW / 4;
+    const int per_grp = 4096 / a.SB;
     const int sb0 = (c_lo * kChunk) / a.SB, sb1 = (c_hi * kChunk + a.SB - 1) / a.SB;
-    const int np = (T * (sb1 - sb0) + G * (4096 / a.SB) - 1) / (G * (4096 / a.SB));
+    const int ntask = T * (sb1 - sb0);
+    const int nrg = min(G, (ntask + per_grp - 1) / per_grp);
+    const int np = (ntask + nrg * per_grp - 1) / (nrg * per_grp);  // at most 2 (planner)
+    const int rg = (wave >> 2) - (G - nrg);                          // < 0: a streaming wave
+    const uint32_t done = lds0 + kLdsFlag + 16;                      // then one counter per rotating group
+    if (threadIdx.x < 8) *(NL_LOCAL uint32_t *)(size_t)(done + 4 * threadIdx.x) = 0u;
     LocalX<NW> lx;
-    local_load<NW>(a, L.sign_in, c_lo, c_hi, np, lx);
-    fence();
+    if (rg >= 0) {
+      if (wave == 4 * (G - nrg)) {  // the byte table (two 1 KiB copies)
+        const void *src = sgpr_ptr(L.lut256);
 #pragma unroll
-    for (int k = 0; k < NS; ++k) loadw(w[k], w_lo + k);
-    wait_vm<LW * NS>();  // the activations (and the table) have landed
-    const int fwht_off = kLdsX + ((J.cps * a.blob + 15) & ~15);
-    local_rotate<NW>(a, c_lo, c_hi, np, lx, smem, fwht_off);
+        for (int q = 0; q < 2; ++q)
+          __builtin_amdgcn_global_load_lds((const NL_GLOBAL void *)((const char *)src + q * 1024 + lane * 16),
+                                           (NL_LOCAL void *)(size_t)(lds0 + kLdsLut + q * 1024), 16, 0, 0);
+      }
+      local_load<NW>(a, L.sign_in, c_lo, c_hi, np, rg, nrg, lx);
+    }
+    // No weight is requested before the activations have landed: once the
+    // chip's weight stream is queued, any later request (even an L2 hit)
+    // waits behind it for microseconds.  Nobody is held up issuing yet, so
+    // the s_barrier costs little.
+    if (rg >= 0) wait_vm<0>();  // the activations (and the table) have landed
     lds_barrier();
+    if (rg >= 0) {
+      const int fwht_off = kLdsX + ((J.cps * a.blob + 15) & ~15);
+      GroupBar bar{done + 4 + 4 * rg, 0u};
+      local_rotate<NW>(a, c_lo, c_hi, np, rg, nrg, lx, smem, fwht_off, bar);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's blob writes have landed
+      if (lane == 0)
+        __hip_atomic_fetch_add((NL_LOCAL uint32_t *)(size_t)done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      fence();
+#pragma unroll
+      for (int k = 0; k < NS; ++k) loadw(w[k], w_lo + k);
+    } else {
+#pragma unroll
+      for (int k = 0; k < NS; ++k) loadw(w[k], w_lo + k);
+    }
+    while (*(volatile NL_LOCAL uint32_t *)(size_t)done < 4u * nrg) __builtin_amdgcn_s_sleep(1);
+    asm volatile("" ::: "memory");
   } else {
     // wave 0 polls the ready line with no weight loads of its own in flight
     // (its wait would otherwise wait for them) and requests its first sets
@@ -731,10 +764,13 @@ static void launch_fwd_t(const FwdArgs2 &a, size_t lds, hipStream_t s, hipEvent_
 template <int BITS>
 static hipError_t launch_fwd_bits(const FwdArgs2 &a, int mt, int nw, bool local, size_t lds, hipStream_t s,
                                   hipEvent_t ev0, hipEvent_t ev1) {
-  if (mt == 1 && nw == 8) {
-    if (local) launch_fwd_t<BITS, 1, 8, true>(a, lds, s, ev0, ev1);
-    else launch_fwd_t<BITS, 1, 8, false>(a, lds, s, ev0, ev1);
-    return hipGetLastError();
+  if (mt == 1 && nw == 8) {  // the eight-wave one-tile form serves the draft only
+    if constexpr (BITS == 0) {
+      if (local) launch_fwd_t<BITS, 1, 8, true>(a, lds, s, ev0, ev1);
+      else launch_fwd_t<BITS, 1, 8, false>(a, lds, s, ev0, ev1);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
   }
   if (nw != fwd_waves(mt)) return hipErrorInvalidValue;
   if (local) {

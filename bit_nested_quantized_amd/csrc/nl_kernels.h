@@ -89,7 +89,7 @@ enum : int {
   kCtrActive = 17,   // 8 lines: linears with rows (1, or the active experts)
   kCtrFixed = 25,
 };
-constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr uint32_t kSpinLimit = 1u << 22;  // default of Handover::spin_limit
 
 enum : int { kOutDirect = 0, kOutSplit = 1, kOutTwoSided = 2 };
 
@@ -113,6 +113,8 @@ struct Handover {
   int rb_base, ob_base, obr_base;  // first counter of each kind
   int line;           // ready line of the workgroup (set per workgroup)
   int n_rot;          // rotation workgroups of the launch
+  uint32_t spin_limit;  // polls before a wait gives up
+  uint32_t wait_extra;  // added to every wait target (> 0: the waits give up; a test hook)
 };
 
 struct FwdArgs {
@@ -129,7 +131,11 @@ struct FwdArgs {
 // than kLocalTokens tokens) whose experts span at most two chunks of K take
 // eight at any tile count: their workgroups are short, and half as many of
 // them pay more than the register ring they give up.
-constexpr int tile_waves(int mt) { return mt >= 3 ? 8 : 4; }
+// Tile waves per workgroup of the staged kernels by token tiles: four up to
+// two tiles; eight for three (168 registers each); seven for four, whose
+// accumulators and unpacked operands need the 256 registers of an
+// eight-wave workgroup.
+constexpr int tile_waves(int mt) { return mt >= 4 ? 7 : (mt == 3 ? 8 : 4); }
 constexpr int wg_threads(int mt) { return 64 * (tile_waves(mt) + 1); }
 
 int rotate_workgroups(int rows, int Kp, int SB);

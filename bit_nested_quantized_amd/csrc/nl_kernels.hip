@@ -214,30 +214,33 @@ __device__ __forceinline__ bool expert_active(const int32_t *offsets, int e, int
 
 // Wait for a token on semaphore `sem` and take it (the output rotation's
 // hand-over; same dispatch-order argument and spin limit as wait_ready).
-__device__ void take_token(uint32_t *sem, uint32_t *err) {
-  for (uint32_t it = 0; ld_dev(sem) == 0u; ++it) {
-    if (it == kSpinLimit) {
+// Returns false when the wait gave up (counted in the error word).
+__device__ bool take_token(uint32_t *sem, const Handover &hv, uint32_t *err) {
+  for (uint32_t it = 0; ld_dev(sem) < 1u + hv.wait_extra; ++it) {
+    if (it >= hv.spin_limit) {
       ctr_add(err, 1u);
-      return;
+      return false;
     }
     __builtin_amdgcn_s_sleep(2);
   }
   __hip_atomic_fetch_sub(sem, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
 }
 
 // Wait until the ready line `line` has counted `n` rotation workgroups.
 // Only a workgroup whose producers have lower indices waits, and workgroups
 // are dispatched in index order, so the producers are running or done; the
-// spin limit (seconds) only bounds the wait if that ever fails, and counts
-// the event in the error word.
-__device__ void wait_ready(const uint32_t *line, uint32_t n, uint32_t *err) {
-  for (uint32_t it = 0; ld_dev(line) < n; ++it) {
-    if (it == kSpinLimit) {
+// spin limit only bounds the wait if that ever fails, and counts the event in
+// the error word.  Returns false when the wait gave up.
+__device__ bool wait_ready(const uint32_t *line, uint32_t n, const Handover &hv, uint32_t *err) {
+  for (uint32_t it = 0; ld_dev(line) < n + hv.wait_extra; ++it) {
+    if (it >= hv.spin_limit) {
       ctr_add(err, 1u);
-      return;
+      return false;
     }
     __builtin_amdgcn_s_sleep(1);
   }
+  return true;
 }
 
 // ===========================================================================
@@ -430,11 +433,14 @@ struct LocalPlan {
 // Register sets in the weight ring of a tile wave: deeper where the
 // accumulators leave room (one or two token tiles), deepest for the draft,
 // whose sets are a quarter the size.  The in-workgroup rotation (MT = 0)
-// holds its transform registers while the first sets are in flight.
+// holds its transform registers while the first sets are in flight (one set
+// for 7-bit planes, whose unpacking needs the most registers).  Every
+// variant fits its registers without scratch.
 template <int BITS, int MT, int TW>
 __host__ __device__ constexpr int ring_sets() {
-  if constexpr (MT == 0) return BITS == 0 ? 3 : 2;
+  if constexpr (MT == 0) return BITS == 0 ? 3 : (BITS == 7 ? 1 : 2);
   if constexpr (TW == 8) return BITS == 0 ? 2 : 1;  // eight tile waves: 168 registers each
+  if constexpr (TW == 7) return BITS == 0 ? 3 : 2;
   return BITS == 0 ? 4 : 3;
 }
 
@@ -470,9 +476,10 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
   constexpr int TR = LOCAL ? kLocalRows : Pl::TR, XG = LOCAL ? 4 : Pl::XG, NST = LOCAL ? 1 : Pl::NST;
   constexpr int NX = Pl::NX;
   static_assert(!LOCAL || FUSED, "local rotation runs in the single launch only");
-  static_assert(TW == 4 || (TW == 8 && MT > 0), "four tile waves, or eight outside the in-workgroup rotation");
+  static_assert(TW == 4 || ((TW == 7 || TW == 8) && MT > 0), "four tile waves, or seven or eight outside the in-workgroup rotation");
   constexpr int NT = 64 * (TW + 1), RB = 16 * TW;  // threads, rows per block
   __shared__ uint32_t s_flag;
+  __shared__ uint32_t s_lost;  // the loader's wait for x' gave up
 
   // (wave index read as a scalar so per-wave choices stay uniform branches)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -543,7 +550,12 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
       }
     };
     if constexpr (FUSED && !LOCAL) {
-      if (lane == 0) wait_ready(ctr_at(hv.ctr, kCtrReady + hv.line), (uint32_t)hv.n_rot, ctr_at(hv.ctr, kCtrErr));
+      // a wait that gave up leaves stale x': the tile waves then write NaN
+      if (lane == 0) {
+        const bool ok = wait_ready(ctr_at(hv.ctr, kCtrReady + hv.line), (uint32_t)hv.n_rot, hv, ctr_at(hv.ctr, kCtrErr));
+        s_lost = ok ? 0u : 1u;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // visible at the first stage barrier
     }
     // Stage q lives in buffer q % NX.  Barrier #q publishes stage q and
     // tells the loader the tile waves are done with stage q - 1, whose
@@ -846,6 +858,12 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
     }
   }
 
+  if constexpr (FUSED && !LOCAL) {
+    if (s_lost) {  // written by the loader before the first stage barrier
+#pragma unroll
+      for (int m = 0; m < MTC; ++m) acc[m] = floatx4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+    }
+  }
   const int row = tile * kTileRows + tl;  // output row of this lane (B column)
   const bool store = active && row < a.d_out;
   auto put = [&](float *out, size_t ld, bool coh) {
@@ -921,18 +939,23 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
       put(dst, a.ldo, hv.mode == kOutTwoSided);
     }
     if (hv.mode != kOutTwoSided) return;
-    // Two-sided: count the row block into its output superblock; the last
-    // one releases one token per finish task of the superblock.
+    // Two-sided: count the row block into each output superblock it overlaps
+    // (two at most: a superblock holds at least 512 rows, a row block at most
+    // 128, and with seven tile waves the two need not align); a superblock's
+    // last row block releases one token per finish task of it.
     wait_stores();
     __syncthreads();
     if (threadIdx.x == 0) {
-      const int sbi = (rb * RB) / hv.sb_rows;
-      const int rb_in_sb = (min(hv.sb_rows, a.d_out - sbi * hv.sb_rows) + RB - 1) / RB;
-      uint32_t *cnt = ctr_at(hv.ctr, hv.ob_base + lin * hv.n_sb + sbi);
-      if (ctr_add(cnt, 1u) == (uint32_t)(rb_in_sb - 1)) {
-        st_dev(cnt, 0u);
-        const int tasks = a.lins ? min(a.offsets[e + 1], a.T) - a.offsets[e] : a.T;
-        ctr_add(ctr_at(hv.ctr, hv.obr_base + lin * hv.n_sb + sbi), (uint32_t)tasks);
+      const int r0 = rb * RB, r1 = min(r0 + RB, a.d_out);  // rows [r0, r1)
+      for (int sbi = r0 / hv.sb_rows; sbi <= (r1 - 1) / hv.sb_rows; ++sbi) {
+        const int s0 = sbi * hv.sb_rows, s1 = min(s0 + hv.sb_rows, a.d_out);
+        const int rb_in_sb = (s1 - 1) / RB - s0 / RB + 1;  // row blocks overlapping [s0, s1)
+        uint32_t *cnt = ctr_at(hv.ctr, hv.ob_base + lin * hv.n_sb + sbi);
+        if (ctr_add(cnt, 1u) == (uint32_t)(rb_in_sb - 1)) {
+          st_dev(cnt, 0u);
+          const int tasks = a.lins ? min(a.offsets[e + 1], a.T) - a.offsets[e] : a.T;
+          ctr_add(ctr_at(hv.ctr, hv.obr_base + lin * hv.n_sb + sbi), (uint32_t)tasks);
+        }
       }
     }
   }
@@ -982,14 +1005,18 @@ __device__ __forceinline__ void finish_body(const FinishArgs &a, int wg, float *
   float *y = a.y + (size_t)t * a.d_out;
   float v[16];
   if constexpr (FUSED) {
-    if (lt == 0 && valid) {
-      const bool waits = !a.lins || (expert_active(a.offsets, e, a.T) && t < a.offsets[e + 1]);
-      if (waits) take_token(ctr_at(hv.ctr, hv.obr_base + e * n_sb + sb), ctr_at(hv.ctr, kCtrErr));
+    __shared__ uint32_t s_lost[8];  // per task of the workgroup (256 / TPS <= 8): its wait gave up
+    if (lt == 0 && !extra) {
+      bool ok = true;
+      const bool waits = valid && (!a.lins || (expert_active(a.offsets, e, a.T) && t < a.offsets[e + 1]));
+      if (waits) ok = take_token(ctr_at(hv.ctr, hv.obr_base + e * n_sb + sb), hv, ctr_at(hv.ctr, kCtrErr));
+      s_lost[tl] = ok ? 0u : 1u;
     }
     __syncthreads();
+    const bool lost = !extra && s_lost[tl] != 0u;
     const float *ys = hv.ysum + (size_t)t * a.d_out;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = ld_dev(ys + min(rb + TPS * j + lt, a.d_out - 1));
+    for (int j = 0; j < 16; ++j) v[j] = lost ? __builtin_nanf("") : ld_dev(ys + min(rb + TPS * j + lt, a.d_out - 1));
   } else {
     const float *p = a.part + (size_t)t * a.d_out;
 #pragma unroll
@@ -1185,8 +1212,8 @@ static void launch_forward_mt(const FwdArgs &f, dim3 grid, hipStream_t s, hipEve
     forward_kernel<BITS, MT, TW><<<grid, 64 * (TW + 1), 0, s>>>(f);
 }
 
-// (mt, tw): four tile waves up to two token tiles (and always for the
-// in-workgroup rotation), eight from one token tile up.
+// (mt, tw): the pairs the planner picks (tile_waves, and eight tile waves for
+// one or two token tiles of short grouped linears).
 template <int BITS>
 static hipError_t launch_forward_bits(const FwdArgs &f, int mt, int tw, dim3 grid, hipStream_t s, hipEvent_t ev0,
                                       hipEvent_t ev1) {
@@ -1197,7 +1224,7 @@ static hipError_t launch_forward_bits(const FwdArgs &f, int mt, int tw, dim3 gri
     case 2 * 16 + 4: launch_forward_mt<BITS, 2, 4>(f, grid, s, ev0, ev1); break;
     case 2 * 16 + 8: launch_forward_mt<BITS, 2, 8>(f, grid, s, ev0, ev1); break;
     case 3 * 16 + 8: launch_forward_mt<BITS, 3, 8>(f, grid, s, ev0, ev1); break;
-    case 4 * 16 + 8: launch_forward_mt<BITS, 4, 8>(f, grid, s, ev0, ev1); break;
+    case 4 * 16 + 7: launch_forward_mt<BITS, 4, 7>(f, grid, s, ev0, ev1); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -146,9 +146,13 @@ nl_status nested_linear_forward_static(nl_handle h, int32_t verify, const void *
  *       overlap x or ws.
  *   ws  workspace of ws_bytes >= nested_linear_workspace_bytes(h, T).
  * Weight bytes are streamed from HBM once per call for all T tokens.  One
- * kernel launch: its first workgroups rotate x, the next contract (each
- * waits for the rotation through the workspace counters, after requesting
- * its first weights), the last (two-sided form only) apply S_o H_o.
+ * kernel launch, of one of two designs chosen by T (NL_TUNE_STAGED_T_*):
+ * either each contraction workgroup holds its K-range of x' in LDS (rotated
+ * by itself for T <= 2, else by rotation workgroups and handed over through
+ * the workspace), or rotation workgroups write x' and contraction workgroups
+ * stage it through LDS a chunk at a time.  Hand-overs wait on workspace
+ * counters after the weights are requested; the last workgroups (two-sided
+ * form only) apply S_o H_o.
  * Errors: NL_EINVAL (NULL pointer, T < 1, x not 16-byte aligned, small or
  * misaligned ws, linear without a residual), NL_EUNSUPPORTED (T > 64, or d_out beyond what the
  * counter region serves: about 16000 row blocks of 64 or 128 rows), NL_EHIP
@@ -225,7 +229,10 @@ typedef enum {
   NL_TUNE_XDMA_GBS = 9,        /* planner: per-CU rate of the x' copy into LDS, GB/s (default 100) */
   NL_TUNE_SPIN_LIMIT = 10,     /* polls before a wait gives up (default 2^22) */
   NL_TUNE_WAIT_EXTRA = 11,     /* test hook: added to every wait target, > 0 makes the waits give up */
-  NL_TUNE_WAVES = 12           /* waves per workgroup up to 16 tokens: 0 auto (8 draft, 12 verify), 8 or 12 */
+  NL_TUNE_WAVES = 12,          /* draft waves per workgroup up to 16 tokens: 0 or 8 (default), 12 */
+  NL_TUNE_STAGED_T_VERIFY = 13, /* single-linear verify with T at or above this uses the staged-x' launch
+                                   (default 9; 65 never) */
+  NL_TUNE_STAGED_T_DRAFT = 14   /* the same for the draft (default 1: always) */
 } nl_tuning;
 nl_status nested_linear_set_tuning(int32_t knob, double value);
 

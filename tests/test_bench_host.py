@@ -88,11 +88,14 @@ def test_committed_traffic_summaries_match_their_kernel_names():
 
 
 def test_roofline_kernels_are_the_forward_instantiations():
-    # the names match the launcher's template instantiations in nl_fwd.hip
-    src = open(os.path.join(ROOT, "bit_nested_quantized_amd", "csrc", "nl_fwd.hip")).read()
-    assert "void fwd_kernel(const FwdArgs2 a)" in src
-    for kernel, bits, waves, _ in bench.ROOF.values():
-        assert kernel == f"fwd_kernel<{bits}, 1, {waves}, false>"
+    # the names match template instantiations the launchers make
+    fwd = open(os.path.join(ROOT, "bit_nested_quantized_amd", "csrc", "nl_fwd.hip")).read()
+    staged = open(os.path.join(ROOT, "bit_nested_quantized_amd", "csrc", "nl_kernels.hip")).read()
+    assert "void fwd_kernel(const FwdArgs2 a)" in fwd
+    assert "launch_fwd_t<BITS, 1, 12, false>" in fwd
+    assert "launch_forward_mt<BITS, 1, 4>" in staged
+    assert bench.ROOF["verify"][0] == "fwd_kernel<6, 1, 12, false>"
+    assert bench.ROOF["draft"][0] == "forward_kernel<0, 1, 4>"
 
 
 def test_pstats_percentiles():
@@ -103,7 +106,7 @@ def test_pstats_percentiles():
 
 def test_util_summary_reads_each_pass(tmp_path):
     vk = f"void nl::{bench.ROOF['verify'][0]}(nl::FwdArgs2)"
-    dk = f"void nl::{bench.ROOF['draft'][0]}(nl::FwdArgs2)"
+    dk = f"void nl::{bench.ROOF['draft'][0]}(nl::FwdArgs)"
     _counter_csv(str(tmp_path / "a" / "p_counter_collection.csv"), "VALUBusy", [(vk, 40.0), (vk, 60.0), (dk, 20.0)])
     _counter_csv(str(tmp_path / "b" / "p_counter_collection.csv"), "SQ_WAVES", [(vk, 3072.0), (dk, 2048.0)])
     out = tmp_path / "util.txt"
