@@ -947,6 +947,57 @@ def pmc_summary(fetch_dir, write_dir, out_path, kernel, prefix="void nl::", titl
     print(text, end="")
 
 
+def trace_summary(trace_dir):
+    """Kernel-trace summary of the two roofline kernels from one
+    `rocprofv3 --kernel-trace --stats` run of `bench.py --roofline-only`: the
+    launches in the leg's order (8 warm-up launches, then per projection and
+    T two rounds over the weight copies), averaged per (projection, T)."""
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)):
+        rows += list(csv.DictReader(open(f)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    stats = []
+    for f in sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)):
+        stats += list(csv.DictReader(open(f)))
+    for mode, (kernel, bits, ts, traffic_file) in ROOF.items():
+        mine = [r for r in rows if kernel_match(r["Kernel_Name"], kernel, "void nl::")]
+        timed = mine[8:]
+        per = len(SHAPES) * len(ts) * 2
+        if not timed or len(timed) % per:
+            raise SystemExit(f"trace summary: {len(mine)} launches of {kernel}, not 8 + a multiple of {per}")
+        ncopy = len(timed) // per
+        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in timed]
+        bpw = (0.265625 + (bits / 8.0 + 1.0 / 64.0 if bits else 0.0))
+        lines = [f"{kernel}: {mode}, T = {' and '.join(map(str, ts))}, one-sided 2-bit base"
+                 + (f" + {bits}-bit residual" if bits else " (draft: base planes only)")
+                 + ", group-128 fp16 scales,",
+                 "projections " + ", ".join(f"{o}x{i}" for _, o, i in SHAPES)
+                 + f" ({ncopy} distinct weight copies per projection)", "",
+                 "command:",
+                 "  rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o p -- python3 bench.py --roofline-only",
+                 "  python3 bench.py --trace-summary <dir>", ""]
+        for r in stats:
+            if kernel_match(r["Name"], kernel, "void nl::"):
+                lines.append(f"kernel_stats.csv: calls {r['Calls']}, average {float(r['AverageNs']) / 1e3:.2f} us "
+                             f"(all launches, the first 8 warm the code)")
+        lines.append(f"kernel trace, the {len(timed)} timed launches: average {sum(durs) / len(durs):.2f} us")
+        k = 0
+        for _, o, i in SHAPES:
+            for T in ts:
+                d = durs[k:k + 2 * ncopy]
+                k += 2 * ncopy
+                us = sum(d) / len(d)
+                lines.append(f"  {o:>5d}x{i:<5d} T={T:2d}: {us:6.2f} us  ({o * i * bpw / us / 1e3:6.0f} GB/s of weights)")
+        lines.append(f"kernel source digest: {kernel_source_digest()}")
+        name = kernel.split("<")[0] + ("_6bit_verify" if bits else "_draft") + "_T" + "_T".join(map(str, ts))
+        out = os.path.join(ROOT, "profiles", f"{name}_proj7b8b_kernel_stats.txt")
+        with open(out, "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+
+
 UTIL_COUNTERS = ("VALUBusy", "MfmaUtil", "OccupancyPercent", "MeanOccupancyPerCU", "MemUnitStalled", "TA_BUSY_avr",
                  "SQ_WAIT_INST_ANY", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_VMEM_RD", "SQ_WAVES",
                  "SQ_BUSY_CYCLES")
@@ -997,6 +1048,8 @@ def main():
                     help="run only the roofline launches and the counter calibration copy (for rocprofv3)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the verify and draft traffic summaries from two --pmc runs of --roofline-only")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="write the kernel-trace summaries of the roofline kernels from a --kernel-trace run of --roofline-only")
     ap.add_argument("--util-summary", nargs="+", metavar="DIR",
                     help="write the utilisation counter summary from --pmc runs of --roofline-only")
     ap.add_argument("--encoder-only", action="store_true",
@@ -1022,6 +1075,9 @@ def main():
         return
     if args.util_summary:
         util_summary(args.util_summary, UTIL_FILE)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
         return
     if args.pmc_summary_w4w8:
         pmc_summary(*args.pmc_summary_w4w8, W48_TRAFFIC_FILE, kernel=W48_KERNEL, prefix="", title=W48_TITLE,

@@ -395,13 +395,15 @@ __device__ void con_role(const FwdArgs2 &a, int cb, char *smem) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's blob writes have landed
       if (lane == 0)
         __hip_atomic_fetch_add((NL_LOCAL uint32_t *)(size_t)done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      fence();
-#pragma unroll
-      for (int k = 0; k < NS; ++k) loadw(w[k], w_lo + k);
-    } else {
-#pragma unroll
-      for (int k = 0; k < NS; ++k) loadw(w[k], w_lo + k);
     }
+    fence();
+    // Every wave requests its ring at this one place (a rotating wave after
+    // its transform).  With one request site per path the paths meet at the
+    // wait below with different registers in flight, and the compiler then
+    // waits there for all of them: a streaming wave would sit on its whole
+    // ring before it even looks at the count.
+#pragma unroll
+    for (int k = 0; k < NS; ++k) loadw(w[k], w_lo + k);
     while (*(volatile NL_LOCAL uint32_t *)(size_t)done < 4u * nrg) __builtin_amdgcn_s_sleep(1);
     asm volatile("" ::: "memory");
   } else {
