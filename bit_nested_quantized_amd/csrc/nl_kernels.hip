@@ -386,10 +386,11 @@ __global__ __launch_bounds__(256) void rotate_in_kernel(const RotInArgs a) {
 //     and the stage before it back to the loader.
 // In the single launch only the loader waits for the rotation, so the tile
 // waves' first chunks stream in meanwhile.  One workgroup per CU (LDS).
-// Per group: base and residual planes -> fp16 B operands; 4 MFMA steps per
-// plane and token tile; fp32 epilogue
+// Per group: base and residual planes -> fp16 B operands (the residual field
+// u = q + 2^(b-1) as the exact subnormal u * 2^-24); 4 MFMA steps per plane
+// and token tile; fp32 epilogue
 //   acc_chunk = fma(s_b / kappa, A_base, acc_chunk)
-//   acc_chunk = fma(s_r, A_resid - bias * sum(x'), acc_chunk)
+//   acc_chunk = fma(2^24 s_r, A_resid, fma(-2^(b-1) s_r, sum(x'), acc_chunk))
 // and at the end of each chunk acc = fma(tsc, acc_chunk, acc).
 // ===========================================================================
 
@@ -633,7 +634,6 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
     };
     const uint2 *s_lut = reinterpret_cast<const uint2 *>(smem);
     const float kinv = L.kinv;
-    const float bias = BITS > 0 ? resid_bias(BITS > 0 ? BITS : 8) : 0.0f;
     // compute chunk ci (its NST stages, a barrier before every stage but the
     // first overall); refill(g) runs after group g
     auto compute = [&](WRegs<BITS> &w, int ci, auto refill) {
@@ -686,11 +686,18 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
           }
           uint32_t bq[16];
           unpack_base(bw + 2 * g, s_lut, bq);
+          // residual fields u = q + 2^(b-1) as the exact fp16 subnormals
+          // u * 2^-24; the offset leaves in fp32 with the group sums of x':
+          // s_r * (2^24 * sum(u 2^-24 x') - 2^(b-1) * sum(x'))
           uint32_t rq[16];
-          if constexpr (BITS > 0) unpack_resid<BITS>(rw + g * BITS, rq);
+          if constexpr (BITS > 0) unpack_resid<BITS, true>(rw + g * BITS, rq);
           const float sb = h2f((uint32_t)(w.sb >> (16 * g)) & 0xFFFFu) * kinv;
-          float sr = 0.f;
-          if constexpr (BITS > 0) sr = h2f((uint32_t)(w.sr >> (16 * g)) & 0xFFFFu);
+          float srA = 0.f, srB = 0.f;
+          if constexpr (BITS > 0) {
+            const float sr = h2f((uint32_t)(w.sr >> (16 * g)) & 0xFFFFu);
+            srA = sr * 16777216.0f;
+            srB = -sr * (float)(1 << (BITS > 0 ? BITS - 1 : 0));
+          }
 #pragma unroll
           for (int m = 0; m < MTC; ++m) {
             floatx4 aB = {0.f, 0.f, 0.f, 0.f}, aR = {0.f, 0.f, 0.f, 0.f};
@@ -702,12 +709,12 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
                 aR = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, as_half8(rq + 4 * s), aR, 0, 0, 0);
             }
             const floatx4 xsv = sums(m);
-            // Draft and verify round identically: with s_r = 0 the residual
-            // fma returns accC unchanged, so verify(0 residual) == draft bitwise.
+            // Draft and verify round identically: with s_r = 0 both residual
+            // fmas return accC unchanged, so verify(0 residual) == draft bitwise.
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               accC[m][i] = fmaf(sb, aB[i], accC[m][i]);
-              if constexpr (BITS > 0) accC[m][i] = fmaf(sr, aR[i] - bias * xsv[i], accC[m][i]);
+              if constexpr (BITS > 0) accC[m][i] = fmaf(srA, aR[i], fmaf(srB, xsv[i], accC[m][i]));
             }
           }
           refill(g);

@@ -39,13 +39,6 @@ constexpr int kScaleBlockBytes = kTileRows * kChunkGroups * 2;  // 128
 
 __host__ __device__ constexpr int resid_block_bytes(int bits) { return 64 * 16 * bits; }
 
-// fp16 bit pattern 0x6400 | u is exactly 1024 + u for u < 1024.  Residual
-// codes are stored offset by 2^(b-1) (u = q + 2^(b-1), unsigned), so the
-// B operand holds 1024 + 2^(b-1) + q exactly; the constant part is removed in
-// the fp32 epilogue with the group sum of the activations.
-__host__ __device__ constexpr float resid_bias(int bits) {
-  return 1024.0f + (float)(1 << (bits - 1));
-}
 
 // Device-side description of one linear (also an element of a grouped
 // launch's expert array).

@@ -226,8 +226,11 @@ def test_subnormal_and_65504_scales(nl, torch_cuda, base_kind, resid_kind, two):
 
 # --- a lost hand-over ----------------------------------------------------------
 
+# (T, verify): the single launch with rotation workgroups (verify, T = 4) and
+# the staged-x' launch (verify at T = 16, the draft at any T)
+@pytest.mark.parametrize("T,verify", [(4, True), (16, True), (4, False)])
 @pytest.mark.parametrize("two", [False, True])
-def test_lost_handover_is_reported_and_recoverable(nl, torch_cuda, two):
+def test_lost_handover_is_reported_and_recoverable(nl, torch_cuda, two, T, verify):
     # The host raises every wait's target (wait_extra) and shortens the spin
     # limit, so each bounded wait gives up after a few thousand polls: the
     # error word counts them, the outputs those waits fed are NaN, and every
@@ -235,14 +238,16 @@ def test_lost_handover_is_reported_and_recoverable(nl, torch_cuda, two):
     # calls on it.
     torch = torch_cuda
     lin = synth.make_linear(1024, 4096, 6, cfg=146, idx=int(two), two_sided=two)
-    x = synth.make_x(16, 4096, cfg=146, idx=0)
+    x = synth.make_x(T, 4096, cfg=146, idx=0)
     L = nl.Linear(lin)
-    ws = L.workspace(16)
+    ws = L.workspace(T)
     xd = to_dev(torch, x)
+    plan = nl.nested_linear_describe_call([1024], 4096, 6 if verify else 0, two, T)
+    assert not plan["local"], plan  # a form with waits between workgroups
     try:
         nl.nested_linear_set_tuning("spin_limit", 2000)
         nl.nested_linear_set_tuning("wait_extra", 1)
-        y = L.forward(xd, True, ws=ws)
+        y = L.forward(xd, verify, ws=ws)
         torch.cuda.synchronize()
         err = nl.nested_linear_workspace_status(ws)
         yn = y.cpu().numpy()
@@ -253,7 +258,7 @@ def test_lost_handover_is_reported_and_recoverable(nl, torch_cuda, two):
     assert np.isnan(yn).all()
     assert nl.nested_linear_workspace_status(ws, clear=True) == err
     assert nl.nested_linear_workspace_status(ws) == 0
-    y = L.forward(xd, True, ws=ws).cpu().numpy().astype(np.float64)
+    y = L.forward(xd, verify, ws=ws).cpu().numpy().astype(np.float64)
     assert nl.nested_linear_workspace_status(ws) == 0
-    check_tokens(y, oracle.forward(lin, x, True), "after clear")
+    check_tokens(y, oracle.forward(lin, x, verify), "after clear")
     L.close()
