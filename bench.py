@@ -998,6 +998,36 @@ def trace_summary(trace_dir):
         print("\n".join(lines))
 
 
+def all_stats_summary(trace_dir):
+    """Every kernel of one default bench run, from the kernel_stats.csv of
+    `rocprofv3 --kernel-trace --stats` around `bench.py --no-cpu-baseline`."""
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)):
+        rows += list(csv.DictReader(open(f)))
+    if not rows:
+        raise SystemExit(f"all-stats summary: no kernel_stats.csv under {trace_dir}")
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = ["All kernels of one default bench run (the verify step graph, per-case graphs T = 1..64, single",
+             "calls, two-sided legs, the roofline legs, the 1024x1024 linear, the decoder layer, the MoE block,",
+             "whole Llama-8B-shaped and 31B-class passes, and the W4/W8, nested-KV, draft-tree and encoder legs)",
+             "", "command:",
+             "  rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o bench -- python3 bench.py --no-cpu-baseline",
+             "  python3 bench.py --all-stats-summary <dir>", "",
+             f"{'kernel':<72s} {'calls':>7s} {'total ms':>10s} {'avg us':>9s} {'share':>6s}"]
+    for r in rows:
+        name = r["Name"].replace("void ", "")
+        name = name if len(name) <= 72 else name[:69] + "..."
+        lines.append(f"{name:<72s} {int(r['Calls']):>7d} {float(r['TotalDurationNs']) / 1e6:>10.2f} "
+                     f"{float(r['AverageNs']) / 1e3:>9.2f} {float(r['Percentage']):>5.1f}%")
+    lines.append(f"kernel source digest: {kernel_source_digest()}")
+    out = os.path.join(ROOT, "profiles", "bench_all_kernels_proj7b8b_kernel_stats.txt")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 UTIL_COUNTERS = ("VALUBusy", "MfmaUtil", "OccupancyPercent", "MeanOccupancyPerCU", "MemUnitStalled", "TA_BUSY_avr",
                  "SQ_WAIT_INST_ANY", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_VMEM_RD", "SQ_WAVES",
                  "SQ_BUSY_CYCLES")
@@ -1048,6 +1078,8 @@ def main():
                     help="run only the roofline launches and the counter calibration copy (for rocprofv3)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the verify and draft traffic summaries from two --pmc runs of --roofline-only")
+    ap.add_argument("--all-stats-summary", metavar="DIR",
+                    help="write the kernel-stats summary of a --kernel-trace --stats run of the whole bench")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="write the kernel-trace summaries of the roofline kernels from a --kernel-trace run of --roofline-only")
     ap.add_argument("--util-summary", nargs="+", metavar="DIR",
@@ -1078,6 +1110,9 @@ def main():
         return
     if args.trace_summary:
         trace_summary(args.trace_summary)
+        return
+    if args.all_stats_summary:
+        all_stats_summary(args.all_stats_summary)
         return
     if args.pmc_summary_w4w8:
         pmc_summary(*args.pmc_summary_w4w8, W48_TRAFFIC_FILE, kernel=W48_KERNEL, prefix="", title=W48_TITLE,
