@@ -684,6 +684,20 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
             for (int s = 0; s < 4; ++s) A[0][s] = *reinterpret_cast<const half8 *>(xb + (gl * 4 + s) * 4 * TR * 8);
             if constexpr (BITS > 0) xs[0] = *reinterpret_cast<const floatx4 *>(mb + gl * TR);
           }
+          // Three or four token tiles: tile m + 1's activations and sums are
+          // requested before tile m's MFMAs (tile 0's before the unpacking),
+          // so each LDS read's latency passes under other work instead of
+          // stalling the MFMA that needs it (two tiles keep reading at the
+          // MFMAs: with the prefetch their 7- and 8-bit forms spill).
+          constexpr bool PF = MTC >= 3;
+          half8 Ac[4], An[4];
+          floatx4 xc = {0.f, 0.f, 0.f, 0.f}, xn = {0.f, 0.f, 0.f, 0.f};
+          auto load_tile = [&](half8 (&Ad)[4], floatx4 &xd, int m) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Ad[s] = act(m, s);
+            xd = sums(m);
+          };
+          if constexpr (PF) load_tile(Ac, xc, 0);
           uint32_t bq[16];
           unpack_base(bw + 2 * g, s_lut, bq);
           // residual fields u = q + 2^(b-1) as the exact fp16 subnormals
@@ -700,21 +714,29 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
           }
 #pragma unroll
           for (int m = 0; m < MTC; ++m) {
+            if constexpr (PF) {
+              if (m + 1 < MTC) load_tile(An, xn, m + 1);
+            }
             floatx4 aB = {0.f, 0.f, 0.f, 0.f}, aR = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-              const half8 a = act(m, s);
+              const half8 a = PF ? Ac[s] : act(m, s);
               aB = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, as_half8(bq + 4 * s), aB, 0, 0, 0);
               if constexpr (BITS > 0)
                 aR = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, as_half8(rq + 4 * s), aR, 0, 0, 0);
             }
-            const floatx4 xsv = sums(m);
+            const floatx4 xsv = PF ? xc : sums(m);
             // Draft and verify round identically: with s_r = 0 both residual
             // fmas return accC unchanged, so verify(0 residual) == draft bitwise.
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               accC[m][i] = fmaf(sb, aB[i], accC[m][i]);
               if constexpr (BITS > 0) accC[m][i] = fmaf(srA, aR[i], fmaf(srB, xsv[i], accC[m][i]));
+            }
+            if constexpr (PF) {
+#pragma unroll
+              for (int s = 0; s < 4; ++s) Ac[s] = An[s];
+              xc = xn;
             }
           }
           refill(g);
