@@ -85,10 +85,12 @@ struct FwdArgs2 {
 __host__ __device__ constexpr int fwd_waves(int mt) { return mt <= 2 ? 12 : 8; }
 
 // Register sets in a wave's weight ring (within 168 registers for twelve
-// waves, 256 for eight).  In the local form the waves that rotate x request
-// their sets only after the transform, so no wave holds both.
+// waves, 256 for eight; verify at three or four token tiles keeps one, its
+// registers going to the next tile's activations).  In the local form the
+// waves that rotate x request their sets only after the transform, so no
+// wave holds both.
 __host__ __device__ constexpr int fwd_ring_sets(int bits, int mt, bool local, int nw) {
-  return (void)local, nw == 8 && mt == 1 ? 4 : (mt == 1 ? (bits == 0 ? 4 : 2) : (bits == 0 ? 3 : 2));
+  return (void)local, nw == 8 && mt == 1 ? 4 : (mt == 1 ? (bits == 0 ? 4 : 2) : (bits == 0 ? 3 : (mt >= 3 ? 1 : 2)));
 }
 
 hipError_t launch_forward2(const FwdArgs2 &a, int bits, int mt, int nw, bool local, size_t lds, hipStream_t s,

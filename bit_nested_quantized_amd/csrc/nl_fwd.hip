@@ -490,6 +490,18 @@ __device__ void con_role(const FwdArgs2 &a, int cb, char *smem) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) A[s] = *reinterpret_cast<const half8 *>(xb + (g * 4 + s) * gs_stride + a_off[0]);
       }
+      // Three or four token tiles: tile m + 1's activations and sums are
+      // requested before tile m's MFMAs (tile 0's before the unpacking), so
+      // each LDS read's latency passes under other work.
+      constexpr bool PF = MT >= 3;
+      half8 Ac[4], An[4];
+      floatx4 xc = {0.f, 0.f, 0.f, 0.f}, xn = {0.f, 0.f, 0.f, 0.f};
+      auto load_tile = [&](half8 (&Ad)[4], floatx4 &xd, int m) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) Ad[s] = act(m, s);
+        if constexpr (BITS > 0) xd = *reinterpret_cast<const floatx4 *>(xb + m_off[m] + g * 4 * tm);
+      };
+      if constexpr (PF) load_tile(Ac, xc, 0);
       uint32_t bq[16];
       unpack_base2(bw + 2 * g, bq);
       uint32_t rq[16];
@@ -504,21 +516,30 @@ __device__ void con_role(const FwdArgs2 &a, int cb, char *smem) {
       }
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
+        if constexpr (PF) {
+          if (m + 1 < MT) load_tile(An, xn, m + 1);
+        }
         floatx4 aB = {0.f, 0.f, 0.f, 0.f}, aR = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const half8 av = act(m, s);
+          const half8 av = PF ? Ac[s] : act(m, s);
           aB = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, as_half8(bq + 4 * s), aB, 0, 0, 0);
           if constexpr (BITS > 0) aR = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, as_half8(rq + 4 * s), aR, 0, 0, 0);
         }
         // With s_r = 0 both residual fmas return accC unchanged, so verify
         // with zero residual scales equals the draft bit for bit.
         floatx4 xs = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (BITS > 0) xs = *reinterpret_cast<const floatx4 *>(xb + m_off[m] + g * 4 * tm);
+        if constexpr (PF) xs = xc;
+        else if constexpr (BITS > 0) xs = *reinterpret_cast<const floatx4 *>(xb + m_off[m] + g * 4 * tm);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           accC[m][e] = fmaf(sb, aB[e], accC[m][e]);
           if constexpr (BITS > 0) accC[m][e] = fmaf(srA, aR[e], fmaf(srB, xs[e], accC[m][e]));
+        }
+        if constexpr (PF) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) Ac[s] = An[s];
+          xc = xn;
         }
       }
     }
