@@ -661,29 +661,42 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
           xb = reinterpret_cast<const _Float16 *>(smem + Pl::o_x + buf * Pl::XB) + (kq * TR + tl) * 8;
           mb = reinterpret_cast<const float *>(smem + Pl::o_x + buf * Pl::XB + Pl::XI * 1024) + 4 * kq;
         }
+        // One token tile (HA): a group's activations, sums and base table
+        // entries are read before its unpacking, so their LDS latency passes
+        // under it; for the draft, whose unpacking is short, group gl + 1's
+        // are requested before group gl's MFMAs instead (group 0's at the
+        // start of the stage).  More tiles read theirs at the MFMAs: the
+        // registers would not fit.
+        constexpr int HA = MTC == 1 && TW == 4 ? 1 : 0;
+        constexpr bool PIPE = HA && BITS == 0;
+        half8 Ah[2][4];
+        floatx4 xh[2];
+        uint32_t bqh[2][16];
+        auto load_group = [&](int gl, int slot) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) Ah[slot][s] = *reinterpret_cast<const half8 *>(xb + (gl * 4 + s) * 4 * TR * 8);
+          if constexpr (BITS > 0) xh[slot] = *reinterpret_cast<const floatx4 *>(mb + gl * TR);
+          unpack_base(reinterpret_cast<const uint32_t *>(w.b) + 2 * (st * XG + gl), s_lut, bqh[slot]);
+        };
+        if constexpr (PIPE) load_group(0, 0);
 #pragma unroll
         for (int gl = 0; gl < XG; ++gl) {
           const int g = st * XG + gl;
-          // One token tile: the group's activations and sums are read first,
-          // so their LDS latency passes under the unpacking below (more
-          // tiles read theirs at the MFMAs: the registers would not fit).
-          constexpr int HA = MTC == 1 && TW == 4 ? 1 : 0;
-          half8 A[1][4];
-          floatx4 xs[1];
+          const int cur = gl & 1;
+          if constexpr (PIPE) {
+            if (gl + 1 < XG) load_group(gl + 1, cur ^ 1);
+          } else if constexpr (HA) {
+            load_group(gl, cur);
+          }
           auto act = [&](int m, int s) -> half8 {
-            if constexpr (HA) return A[0][s];
+            if constexpr (HA) return Ah[cur][s];
             return *reinterpret_cast<const half8 *>(xb + ((gl * 4 + s) * 4 * TR + 16 * m) * 8);
           };
           auto sums = [&](int m) -> floatx4 {
             if constexpr (BITS == 0) return floatx4{0.f, 0.f, 0.f, 0.f};
-            if constexpr (HA) return xs[0];
+            if constexpr (HA) return xh[cur];
             return *reinterpret_cast<const floatx4 *>(mb + gl * TR + 16 * m);
           };
-          if constexpr (HA) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) A[0][s] = *reinterpret_cast<const half8 *>(xb + (gl * 4 + s) * 4 * TR * 8);
-            if constexpr (BITS > 0) xs[0] = *reinterpret_cast<const floatx4 *>(mb + gl * TR);
-          }
           // Three or four token tiles: tile m + 1's activations and sums are
           // requested before tile m's MFMAs (tile 0's before the unpacking),
           // so each LDS read's latency passes under other work instead of
@@ -699,7 +712,12 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
           };
           if constexpr (PF) load_tile(Ac, xc, 0);
           uint32_t bq[16];
-          unpack_base(bw + 2 * g, s_lut, bq);
+          if constexpr (HA) {
+#pragma unroll
+            for (int k = 0; k < 16; ++k) bq[k] = bqh[cur][k];
+          } else {
+            unpack_base(bw + 2 * g, s_lut, bq);
+          }
           // residual fields u = q + 2^(b-1) as the exact fp16 subnormals
           // u * 2^-24; the offset leaves in fp32 with the group sums of x':
           // s_r * (2^24 * sum(u 2^-24 x') - 2^(b-1) * sum(x'))
