@@ -100,6 +100,11 @@ __device__ __forceinline__ void bfly16(float (&v)[16], int bit) {
 // both compile-time, so every LDS address is a base plus an immediate.
 // xch: this task's LDS (SB + SB/16 floats).  idle: a thread (uniformly per
 // wave) that only keeps the barrier count.
+// Every LDS slot of a layout belongs to one thread, so a thread that writes
+// back the slots it has just read (C -> C, A -> A) races with no other
+// thread: only the barriers after each write, and the one that opens the
+// task area, are needed.
+constexpr int kFwhtBarriers = 4;
 template <int N, int LB, class B>
 __device__ __forceinline__ void fwht_bt(float (&v)[16], float *xch, int lt, bool idle, B &bar) {
   constexpr int TPS = 1 << (N - 4);
@@ -121,7 +126,6 @@ __device__ __forceinline__ void fwht_bt(float (&v)[16], float *xch, int lt, bool
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     if (4 + q < LB) bfly16(v, q);
-  bar.sync();
   if (!idle)
 #pragma unroll
     for (int j = 0; j < 16; ++j) pc[17 * j] = v[j];
@@ -134,7 +138,6 @@ __device__ __forceinline__ void fwht_bt(float (&v)[16], float *xch, int lt, bool
     constexpr int base = N - 4;
     if (base + q >= 8 && base + q < LB) bfly16(v, q);
   }
-  bar.sync();
   if (!idle)
 #pragma unroll
     for (int j = 0; j < 16; ++j) pa[(TPS + TPS / 16) * j] = v[j];
@@ -178,7 +181,7 @@ __device__ __forceinline__ void fwht_tasks(float (&v)[16], float *xch, int lt, i
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     if (4 + q < n - 4 && 4 + q < lb) bfly16(v, q);
-  lds_barrier();
+  // the slots this thread has just read: no barrier before the write-back
 #pragma unroll
   for (int j = 0; j < 16; ++j) xch[lds_pad(cbase + 16 * j)] = v[j];
   lds_barrier();

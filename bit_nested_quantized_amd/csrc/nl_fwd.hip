@@ -121,7 +121,7 @@ __device__ __forceinline__ XOut rotate16(const XRaw &xr, float *xch, int lt, int
   XOut o;
   if (!__any(has_task)) {
 #pragma unroll
-    for (int k = 0; k < 6; ++k) bar.sync();  // the barriers of fwht_bt
+    for (int k = 0; k < kFwhtBarriers; ++k) bar.sync();  // the barriers of fwht_bt
 #pragma unroll
     for (int h = 0; h < 8; ++h) o.w[h] = 0u;
     o.gs = 0.f;
