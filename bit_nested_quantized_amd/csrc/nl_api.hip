@@ -324,6 +324,9 @@ static int env_int(const char *name, int dflt) {
 }
 static const int g_wg_target = env_int("NL_WG_TARGET", 256);
 static const int g_splits = env_int("NL_SPLITS", 0);
+// Tile waves of the staged single launch at one to three token tiles: 4 (one
+// per SIMD) or 8 (two per SIMD); 0 leaves the planner's choice.
+static int g_t_stw = 0;
 
 // tokens: rows of x per linear (T; a grouped call routes each token to an
 // expert at most once).
@@ -358,16 +361,24 @@ static Plan make_plan(int d_out, int n_tiles, int n_chunks, bool sign_out, int b
 
 static int mt_for(int T) { return (T + 15) / 16; }
 
+// Tile waves of the staged single launch (the three-launch form keeps
+// tile_waves: its contraction kernel has one variant per token-tile count).
+static int staged_tile_waves(int T) {
+  const int mt = mt_for(T);
+  if (g_t_stw == 8 && mt <= 3 && T > kLocalTokens) return 8;
+  if (g_t_stw == 4 && mt <= 2) return 4;
+  return tile_waves(mt);
+}
+
 static nl_status check_call(nl_handle h, const char *who, int verify, int32_t T, const void *ws,
-                            size_t ws_bytes, Plan *plan) {
+                            size_t ws_bytes, Plan *plan, int tw) {
   if (!valid(h)) return fail(NL_EINVAL, "%s: invalid handle", who);
   if (verify && !h->bits) return fail(NL_EINVAL, "%s: the linear has no residual (draft only)", who);
   if (T < 1) return fail(NL_EINVAL, "%s: T must be >= 1 (got %d)", who, T);
   if (T > NL_MAX_T) return fail(NL_EUNSUPPORTED, "%s: T = %d exceeds %d", who, T, NL_MAX_T);
   if (!ws) return fail(NL_EINVAL, "%s: NULL workspace", who);
   if ((uintptr_t)ws & 255) return fail(NL_EINVAL, "%s: workspace must be 256-byte aligned", who);
-  *plan = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, h->b_out, T, mt_for(T), 1, T,
-                       tile_waves(mt_for(T)));
+  *plan = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, h->b_out, T, mt_for(T), 1, T, tw);
   if (ws_bytes < plan->total)
     return fail(NL_EINVAL, "%s: workspace too small (%zu < %zu)", who, ws_bytes, plan->total);
   if (plan->n_ctr > kCtrLines)
@@ -398,7 +409,7 @@ static RotInArgs rot_args(nl_handle h, const void *x, int T, char *ws, const Pla
 extern "C" nl_status nested_linear_prepare_input(nl_handle h, const void *x, int32_t T, void *ws,
                                                  size_t ws_bytes, void *stream) {
   Plan p;
-  nl_status st = check_call(h, "prepare_input", 0, T, ws, ws_bytes, &p);
+  nl_status st = check_call(h, "prepare_input", 0, T, ws, ws_bytes, &p, tile_waves(mt_for(T)));
   if (st != NL_OK) return st;
   if (!x) return fail(NL_EINVAL, "prepare_input: NULL x");
   if ((uintptr_t)x & 15) return fail(NL_EINVAL, "prepare_input: x must be 16-byte aligned");
@@ -410,7 +421,7 @@ extern "C" nl_status nested_linear_prepare_input(nl_handle h, const void *x, int
 extern "C" nl_status nested_linear_contract(nl_handle h, int32_t verify, int32_t T, float *y,
                                             void *ws, size_t ws_bytes, void *stream) {
   Plan p;
-  nl_status st = check_call(h, "contract", verify, T, ws, ws_bytes, &p);
+  nl_status st = check_call(h, "contract", verify, T, ws, ws_bytes, &p, tile_waves(mt_for(T)));
   if (st != NL_OK) return st;
   if (!y && !p.finish) return fail(NL_EINVAL, "contract: NULL y");
   char *w = (char *)ws;
@@ -438,7 +449,7 @@ extern "C" nl_status nested_linear_contract(nl_handle h, int32_t verify, int32_t
 extern "C" nl_status nested_linear_finish(nl_handle h, int32_t T, float *y, void *ws, size_t ws_bytes,
                                           void *stream) {
   Plan p;
-  nl_status st = check_call(h, "finish", 0, T, ws, ws_bytes, &p);
+  nl_status st = check_call(h, "finish", 0, T, ws, ws_bytes, &p, tile_waves(mt_for(T)));
   if (st != NL_OK) return st;
   if (!y) return fail(NL_EINVAL, "finish: NULL y");
   if (!p.finish) return ok();
@@ -841,7 +852,7 @@ static nl_status forward_n(const nl_linear *const *hs, int n, int verify, const 
 static nl_status forward_staged(nl_handle h, int verify, const void *x, int32_t T, float *y, void *ws,
                                 size_t ws_bytes, void *stream, const char *who) {
   Plan p;
-  nl_status st = check_call(h, who, verify, T, ws, ws_bytes, &p);
+  nl_status st = check_call(h, who, verify, T, ws, ws_bytes, &p, staged_tile_waves(T));
   if (st != NL_OK) return st;
   if (!x || !y) return fail(NL_EINVAL, "%s: NULL x or y", who);
   if ((uintptr_t)x & 15) return fail(NL_EINVAL, "%s: x must be 16-byte aligned", who);
@@ -931,7 +942,7 @@ extern "C" nl_status nested_linear_forward_static(nl_handle h, int32_t verify, c
   int n_ctr;
   if (use_staged(verify, T)) {
     const Plan p = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, h->b_out, T, mt_for(T), 1, T,
-                             tile_waves(mt_for(T)));
+                             staged_tile_waves(T));
     total = p.total;
     n_ctr = p.n_ctr;
   } else {
@@ -1016,10 +1027,14 @@ extern "C" nl_status nested_linear_workspace_bytes(nl_handle h, int32_t T_max, s
   size_t mx = 0;
   const CallShape hs[1] = {shape_of(h)};
   for (int T = 1; T <= T_max; ++T) {
-    // the staged calls' layout and the single launch's, draft and verify
-    Plan p = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, h->b_out, T, mt_for(T), 1, T,
-                       tile_waves(mt_for(T)));
-    mx = std::max(mx, p.total);
+    // the staged calls' layouts (every tile-wave count the staged launch can
+    // take, so that a size taken before a tuning change stays valid) and the
+    // single launch's, draft and verify
+    for (int tw : {tile_waves(mt_for(T)), 4, 8}) {
+      if (tw != tile_waves(mt_for(T)) && mt_for(T) > (tw == 8 ? 3 : 2)) continue;
+      const Plan p = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, h->b_out, T, mt_for(T), 1, T, tw);
+      mx = std::max(mx, p.total);
+    }
     mx = std::max(mx, make_plan2(hs, 1, T, 0).total);
     if (h->bits) mx = std::max(mx, make_plan2(hs, 1, T, h->bits).total);
   }
@@ -1043,6 +1058,7 @@ extern "C" nl_status nested_linear_set_tuning(int32_t knob, double value) {
     case NL_TUNE_WAVES: g_t_nw = ((int)value == 8 || (int)value == 12) ? (int)value : 0; break;
     case NL_TUNE_STAGED_T_VERIFY: g_t_staged_v = value > 0 ? (int)value : 9; break;
     case NL_TUNE_STAGED_T_DRAFT: g_t_staged_d = value > 0 ? (int)value : 1; break;
+    case NL_TUNE_STAGED_WAVES: g_t_stw = ((int)value == 4 || (int)value == 8) ? (int)value : 0; break;
     default: return fail(NL_EINVAL, "set_tuning: unknown knob %d", knob);
   }
   return ok();

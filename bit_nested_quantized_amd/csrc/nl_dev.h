@@ -297,4 +297,103 @@ __device__ __forceinline__ const void *sgpr_ptr(const void *p) {
   return (const void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
+// The split-K sums of a row block, taken by its last workgroup to arrive:
+//   out[(tb + t) * ld + r0 + r] = sum_s part[s * stride + (tb + t) * ld + r0 + r]
+// for t < nt, r < rows, each output summed in split order from zero (the same
+// order and rounding on every path).  The partials were written by other
+// workgroups with agent-scope stores and are read with agent-scope loads.
+// When ld, stride, r0 and rows are multiples of 4 (partials 16-byte aligned)
+// a thread takes U runs of 4 rows and issues the 16-byte loads of up to 8
+// splits of all of them before its first add, so a row block of 64 tokens
+// costs one or two memory round trips per 8 splits (U = 4 or 2: the
+// kernels whose main loop holds fewer registers take 2, and U = 0 keeps
+// only the single-output form, so that this phase does not raise their
+// allocation); otherwise 4 single outputs per thread and round.
+// RBC > 0: the row block's height as a constant (rows <= RBC), so that the
+// output index splits by a constant divisor.
+template <int NT, int U, int RBC = 0>
+__device__ __forceinline__ void sum_splits(const float *part, size_t stride, int S, float *out, bool coh, size_t ld,
+                                           int tb, int nt, int r0, int rows) {
+  const int rstep = RBC > 0 ? RBC : rows;  // outputs of one token in the index space
+  const size_t span = (size_t)S * stride * 4;
+  const bool vec = U > 0 && ((ld | stride | (size_t)r0 | (size_t)rows) & 3) == 0 && ((uintptr_t)part & 15) == 0 &&
+                   span < 0x7FFFFFFFu;
+  if constexpr (U > 0) if (vec) {
+    constexpr int kRaw = 0x00020000;  // raw 32-bit buffer descriptor word 3
+    const __amdgpu_buffer_rsrc_t pr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)sgpr_ptr(part), 0, (int)span, kRaw);
+    const int rq = rstep >> 2, total = nt * rq;
+    for (int base = 0; base < total; base += U * NT) {
+      // o: float index (within one split) of the thread's run u, or ~0 when
+      // it has none (its loads then read the first run; nothing is stored)
+      uint32_t o[U];
+      floatx4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int idx = base + u * NT + (int)threadIdx.x, t = idx / rq, r4 = idx - t * rq;
+        o[u] = idx < total && 4 * r4 < rows ? (uint32_t)((size_t)(tb + t) * ld + r0 + 4 * r4) : ~0u;
+        v[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+      for (int s0 = 0; s0 < S; s0 += 8) {
+        floatx4 w[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            w[u][q] = __builtin_bit_cast(
+                floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+                             pr, (int)(((uint32_t)min(s0 + q, S - 1) * (uint32_t)stride + (o[u] == ~0u ? 0u : o[u])) * 4u),
+                             0, kSc1));
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            v[u] += (s0 + q < S) ? w[u][q] : floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (o[u] != ~0u) {
+          float *p = out + o[u];
+          if (coh) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st_dev(p + i, v[u][i]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p[i] = v[u][i];
+          }
+        }
+      }
+    }
+    return;
+  }
+  const int total = nt * rstep;
+  for (int base = 0; base < total; base += 4 * NT) {
+    size_t o[4];
+    bool ok[4];
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const int idx = base + e4 * NT + (int)threadIdx.x, t = idx / rstep, r = idx % rstep;
+      ok[e4] = idx < total && r < rows;
+      o[e4] = ok[e4] ? (size_t)(tb + t) * ld + r0 + r : 0;
+    }
+    for (int s0 = 0; s0 < S; s0 += 8) {
+      float u[4][8];
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) u[e4][q] = ld_dev(part + (size_t)min(s0 + q, S - 1) * stride + o[e4]);
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[e4] += (s0 + q < S) ? u[e4][q] : 0.f;
+    }
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      if (!ok[e4]) continue;
+      if (coh) st_dev(out + o[e4], v[e4]); else out[o[e4]] = v[e4];
+    }
+  }
+}
+
 }  // namespace nl

@@ -635,34 +635,8 @@ __device__ void con_role(const FwdArgs2 &a, int cb, char *smem) {
       // the last of the row block's splits adds the partials in split order
       constexpr int NT = NW * 64;
       const int r0 = rb * rt * kTileRows;
-      const int rows_here = min(rt * kTileRows, d_out - r0), total = T * rows_here;
-      for (int base = 0; base < total; base += 4 * NT) {
-        size_t o[4];
-        bool okk[4];
-        float v[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const int idx = base + e4 * NT + (int)threadIdx.x, t = idx / rows_here, r = idx % rows_here;
-          okk[e4] = idx < total;
-          o[e4] = okk[e4] ? (size_t)t * d_out + r0 + r : 0;
-        }
-        for (int s0 = 0; s0 < S; s0 += 8) {
-          float u[4][8];
-#pragma unroll
-          for (int e4 = 0; e4 < 4; ++e4)
-#pragma unroll
-            for (int q = 0; q < 8; ++q) u[e4][q] = ld_dev(J.part + (size_t)min(s0 + q, S - 1) * T * d_out + o[e4]);
-#pragma unroll
-          for (int e4 = 0; e4 < 4; ++e4)
-#pragma unroll
-            for (int q = 0; q < 8; ++q) v[e4] += (s0 + q < S) ? u[e4][q] : 0.f;
-        }
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          if (!okk[e4]) continue;
-          if (two) st_dev(J.ysum + o[e4], v[e4]); else J.y[o[e4]] = v[e4];
-        }
-      }
+      sum_splits<NT, (BITS == 0 || NT > 512 ? 2 : 4)>(J.part, (size_t)T * d_out, S, two ? J.ysum : J.y, two, (size_t)d_out, 0, T,
+                                         r0, min(rt * kTileRows, d_out - r0));
     }
   }
   if (two && have_sum) {

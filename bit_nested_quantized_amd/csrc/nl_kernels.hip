@@ -950,38 +950,12 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
       }
       __syncthreads();
       if (!s_flag) return;
-      // up to 4 outputs per thread and 8 splits per round, every load of a
-      // round issued before its adds (one memory round trip for T <= 16 and
-      // S <= 8); each output still sums its splits in order from zero
-      const float *part = a.out;
-      const int rows_here = min(RB, a.d_out - rb * RB), total = nrows * RB;
-      for (int base = 0; base < total; base += 4 * NT) {
-        size_t o[4];
-        bool ok[4];
-        float v[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const int idx = base + e4 * NT + threadIdx.x, t = idx / RB, r = idx % RB;
-          ok[e4] = idx < total && r < rows_here;
-          o[e4] = (size_t)(row_base + (ok[e4] ? t : 0)) * a.ldo + rb * RB + (ok[e4] ? r : 0);
-        }
-        for (int sp0 = 0; sp0 < hv.S; sp0 += 8) {
-          float u[4][8];
-#pragma unroll
-          for (int e4 = 0; e4 < 4; ++e4)
-#pragma unroll
-            for (int q = 0; q < 8; ++q) u[e4][q] = ld_dev(part + min(sp0 + q, hv.S - 1) * a.split_stride + o[e4]);
-#pragma unroll
-          for (int e4 = 0; e4 < 4; ++e4)
-#pragma unroll
-            for (int q = 0; q < 8; ++q) v[e4] += (sp0 + q < hv.S) ? u[e4][q] : 0.f;
-        }
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          if (!ok[e4]) continue;
-          if (hv.mode == kOutTwoSided) st_dev(dst + o[e4], v[e4]); else dst[o[e4]] = v[e4];
-        }
-      }
+      // 16-byte runs in flight per thread: as many as the main loop's
+      // registers leave room for (eight tile waves: the single-output form,
+      // with which their allocation stays as it is)
+      constexpr int RU = TW == 8 ? 0 : (BITS == 0 && MT < 4 ? 2 : 4);
+      sum_splits<NT, RU, RB>(a.out, a.split_stride, hv.S, dst, hv.mode == kOutTwoSided, a.ldo, row_base,
+                                         nrows, rb * RB, min(RB, a.d_out - rb * RB));
     } else {
       put(dst, a.ldo, hv.mode == kOutTwoSided);
     }

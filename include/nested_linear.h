@@ -232,7 +232,9 @@ typedef enum {
   NL_TUNE_WAVES = 12,          /* draft waves per workgroup up to 16 tokens: 0 or 8 (default), 12 */
   NL_TUNE_STAGED_T_VERIFY = 13, /* single-linear verify with T at or above this uses the staged-x' launch
                                    (default 9; 65 never) */
-  NL_TUNE_STAGED_T_DRAFT = 14   /* the same for the draft (default 1: always) */
+  NL_TUNE_STAGED_T_DRAFT = 14,  /* the same for the draft (default 1: always) */
+  NL_TUNE_STAGED_WAVES = 15     /* tile waves per workgroup of the staged launch at 3..48 tokens: 4 or 8
+                                   (0: planner) */
 } nl_tuning;
 nl_status nested_linear_set_tuning(int32_t knob, double value);
 
