@@ -487,7 +487,9 @@ static void fill_launch(FwdArgs &f, const Plan &p, int n_linears, char *ws, floa
   f.hv.rb_base = kCtrFixed;
   f.hv.ob_base = kCtrFixed + n_linears * p.n_rb;
   f.hv.obr_base = f.hv.ob_base + n_linears * p.n_sb;
-  f.n_rot = p.local ? 0 : rotate_workgroups(p.rows, f.rot.Kp, f.rot.SB);
+  // a rotation workgroup of 512 threads or more runs two transform groups
+  f.rot.groups = 64 * (p.tw + 1) >= 512 ? 2 : 1;
+  f.n_rot = p.local ? 0 : rotate_workgroups(p.rows, f.rot.Kp, f.rot.SB, f.rot.groups);
   // Contraction workgroups: one slot of them per linear, or, when that
   // halves the grid, one per linear that can have rows (each has one at
   // least, so at most rows of them do).  The slot's workgroups then find

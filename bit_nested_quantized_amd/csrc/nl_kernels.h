@@ -42,6 +42,7 @@ struct RotInArgs {
   int rows;                 // rows of x' (tokens, or pairs of a grouped call)
   int d_in, b, lb, SB, Kp, Gp, n_chunks;
   float rsqrt_b;
+  int groups;               // 256-thread transform groups per workgroup (0 or 1: one)
 };
 
 struct GemmArgs {
@@ -138,7 +139,7 @@ struct FwdArgs {
 constexpr int tile_waves(int mt) { return mt >= 4 ? 7 : (mt == 3 ? 8 : 4); }
 constexpr int wg_threads(int mt) { return 64 * (tile_waves(mt) + 1); }
 
-int rotate_workgroups(int rows, int Kp, int SB);
+int rotate_workgroups(int rows, int Kp, int SB, int groups = 1);
 int finish_workgroups(int rows, int d_out, int OB);
 
 hipError_t launch_repack(const RepackArgs &a, int bits, hipStream_t s);

@@ -254,25 +254,30 @@ __device__ bool wait_ready(const uint32_t *line, uint32_t n, const Handover &hv,
 // meta[(c*5+4)*R + r] = tsc.  COH: agent-scope stores (read by other
 // workgroups of the same launch), 16 bytes per store.
 // ===========================================================================
-// Threads past the first 256 (the fifth wave of the single launch) run the
-// same code on a spare LDS area (`spare`, SB + SB/16 floats) and store nothing.
-// Rotation workgroup-task wg: 256 threads transform 4096 values as 4096/SB
-// tasks (row, superblock of SB columns) of TPS = SB/16 threads, 16 values
-// each.  Thread ids from 256 up only keep the barrier count (extra).
+// Rotation workgroup wg: each 256-thread group transforms 4096 values as
+// 4096/SB tasks (row, superblock of SB columns) of TPS = SB/16 threads, 16
+// values each; a workgroup of 512 threads or more runs two groups (a.groups),
+// the first in the LDS area `xch`, the second in `spare` (SB + SB/16 floats
+// per task each).  Threads past the groups (the fifth wave of a 320-thread
+// workgroup, the ninth of 576) run the same code without touching LDS and
+// store nothing: they only keep the barrier count (extra).
 struct RotTask {
-  int row, k0, lt, tl, xrow;
+  int row, k0, lt, tl, grp, xrow;
   bool valid, extra;
   const int8_t *sign;
 };
 __device__ __forceinline__ RotTask rot_task(const RotInArgs &a, int wg, int tid) {
   RotTask t;
   const int SB = a.SB, TPS = SB >> 4;
-  t.extra = tid >= 256;
+  const int ng = a.groups > 1 ? a.groups : 1;
+  t.extra = tid >= 256 * ng;
   if (t.extra) tid = 0;
+  t.grp = tid >> 8;
+  tid &= 255;
   t.lt = tid % TPS;
   t.tl = tid / TPS;
   const int n_sb = a.Kp / SB;
-  const int task = wg * (256 / TPS) + t.tl;
+  const int task = (wg * ng + t.grp) * (256 / TPS) + t.tl;
   t.valid = !t.extra && task < a.rows * n_sb;
   t.row = t.valid ? task / n_sb : 0;
   t.k0 = (t.valid ? task % n_sb : 0) * SB + 16 * t.lt;
@@ -363,7 +368,8 @@ __device__ __forceinline__ void rotate_body(const RotInArgs &a, int wg, float *x
   const RotTask t = rot_task(a, wg, threadIdx.x);
   const XRaw xr = load_x16(a.x, t.sign, t.xrow, t.k0, a.d_in);
   RotOut o;
-  rot_transform(a, t, xr, t.extra ? spare : xch + t.tl * (a.SB + (a.SB >> 4)), o);
+  // group 0 transforms in xch, group 1 in spare (extra threads touch neither)
+  rot_transform(a, t, xr, (t.extra || t.grp ? spare : xch) + t.tl * (a.SB + (a.SB >> 4)), o);
   rot_store<COH>(a, t, o.w, o.gs, o.s);
 }
 
@@ -1180,8 +1186,8 @@ hipError_t launch_decode(const DecodeArgs &a, int bits, int ntiles, hipStream_t 
   return hipGetLastError();
 }
 
-int rotate_workgroups(int rows, int Kp, int SB) {
-  const int tasks = rows * (Kp / SB), per_wg = 4096 / SB;
+int rotate_workgroups(int rows, int Kp, int SB, int groups) {
+  const int tasks = rows * (Kp / SB), per_wg = (groups > 1 ? groups : 1) * (4096 / SB);
   return (tasks + per_wg - 1) / per_wg;
 }
 
