@@ -64,6 +64,31 @@ struct GroupBar {
   }
 };
 
+// Reductions over aligned groups of 32 and 8 lanes without an LDS round trip
+// (a shuffle through ds_bpermute waits ~100 cycles per step): DPP moves for
+// the steps within a row of 16 lanes (quad swaps for distances 1 and 2, the
+// half-row mirror for 4, the row mirror for 8) and a bit-mode swizzle (xor
+// 16) for the last step of 32.  After each step every lane of the group
+// holds the same value, so pairing a lane with the mirrored lane of the
+// other half gives what an xor butterfly gives, bit for bit.  Every lane of
+// the wave must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float max_lanes32(float m) {
+  m = fmaxf(m, dpp_mov<0xB1>(m));   // quad_perm [1, 0, 3, 2]
+  m = fmaxf(m, dpp_mov<0x4E>(m));   // quad_perm [2, 3, 0, 1]
+  m = fmaxf(m, dpp_mov<0x141>(m));  // row_half_mirror
+  m = fmaxf(m, dpp_mov<0x140>(m));  // row_mirror
+  return fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, m), 0x401F)));
+}
+__device__ __forceinline__ float sum_lanes8(float s) {
+  s += dpp_mov<0xB1>(s);
+  s += dpp_mov<0x4E>(s);
+  return s + dpp_mov<0x141>(s);
+}
+
 // ===========================================================================
 // Workgroup Walsh-Hadamard transforms (POC section 1: Sylvester H, applied
 // block-diagonally).  A workgroup of 256 threads transforms 4096 values:

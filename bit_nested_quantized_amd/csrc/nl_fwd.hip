@@ -134,8 +134,7 @@ __device__ __forceinline__ XOut rotate16(const XRaw &xr, float *xch, int lt, int
   float m = 0.f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(v[j]));
-#pragma unroll
-  for (int d = 1; d < 32; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+  m = max_lanes32(m);
   int e = 0;
   if (m > 0.0f) {
     int ex;
@@ -150,8 +149,7 @@ __device__ __forceinline__ XOut rotate16(const XRaw &xr, float *xch, int lt, int
     gs += (float)q0 + (float)q1;
     o.w[h] = (uint32_t)__builtin_bit_cast(uint16_t, q0) | ((uint32_t)__builtin_bit_cast(uint16_t, q1) << 16);
   }
-#pragma unroll
-  for (int d = 1; d < 8; d <<= 1) gs += __shfl_xor(gs, d, 64);
+  gs = sum_lanes8(gs);
   o.gs = gs;
   o.e = e;
   return o;

@@ -313,8 +313,7 @@ __device__ __forceinline__ void rot_transform(const RotInArgs &a, const RotTask 
   float m = 0.f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(v[j]));
-#pragma unroll
-  for (int d = 1; d < 32; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+  m = max_lanes32(m);
   int s = 0;
   if (m > 0.0f) {
     int e;
@@ -329,8 +328,7 @@ __device__ __forceinline__ void rot_transform(const RotInArgs &a, const RotTask 
     gs += (float)q0 + (float)q1;
     o.w[h] = (uint32_t)__builtin_bit_cast(uint16_t, q0) | ((uint32_t)__builtin_bit_cast(uint16_t, q1) << 16);
   }
-#pragma unroll
-  for (int d = 1; d < 8; d <<= 1) gs += __shfl_xor(gs, d, 64);
+  gs = sum_lanes8(gs);
   o.gs = gs;
   o.s = s;
 }
@@ -823,8 +821,7 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
         float mx = 0.f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(v[j]));
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        mx = max_lanes32(mx);
         int sc = 0;
         if (mx > 0.0f) {
           int ex;
@@ -840,8 +837,7 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
           gs += (float)q0 + (float)q1;
           wv[h] = (uint32_t)__builtin_bit_cast(uint16_t, q0) | ((uint32_t)__builtin_bit_cast(uint16_t, q1) << 16);
         }
-#pragma unroll
-        for (int o = 1; o < 8; o <<= 1) gs += __shfl_xor(gs, o, 64);
+        gs = sum_lanes8(gs);
         const int k0 = kb + 16 * lt;
         if (!valid || k0 < kbeg || k0 >= kend) return;
         const int cl = (k0 >> 9) - c_begin;
