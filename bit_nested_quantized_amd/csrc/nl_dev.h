@@ -330,10 +330,9 @@ __device__ __forceinline__ const void *sgpr_ptr(const void *p) {
 // When ld, stride, r0 and rows are multiples of 4 (partials 16-byte aligned)
 // a thread takes U runs of 4 rows and issues the 16-byte loads of up to 8
 // splits of all of them before its first add, so a row block of 64 tokens
-// costs one or two memory round trips per 8 splits (U = 4 or 2: the
-// kernels whose main loop holds fewer registers take 2, and U = 0 keeps
-// only the single-output form, so that this phase does not raise their
-// allocation); otherwise 4 single outputs per thread and round.
+// costs one or two memory round trips per 8 splits (U = 2 or 4; U = 0 keeps
+// only the single-output form); otherwise 4 single outputs per thread and
+// round.
 // RBC > 0: the row block's height as a constant (rows <= RBC), so that the
 // output index splits by a constant divisor.
 template <int NT, int U, int RBC = 0>

@@ -633,7 +633,8 @@ __device__ void con_role(const FwdArgs2 &a, int cb, char *smem) {
       // the last of the row block's splits adds the partials in split order
       constexpr int NT = NW * 64;
       const int r0 = rb * rt * kTileRows;
-      sum_splits<NT, (BITS == 0 || NT > 512 ? 2 : 4)>(J.part, (size_t)T * d_out, S, two ? J.ysum : J.y, two, (size_t)d_out, 0, T,
+      // two 16-byte runs in flight per thread (four: slower at four token tiles)
+      sum_splits<NT, 2>(J.part, (size_t)T * d_out, S, two ? J.ysum : J.y, two, (size_t)d_out, 0, T,
                                          r0, min(rt * kTileRows, d_out - r0));
     }
   }

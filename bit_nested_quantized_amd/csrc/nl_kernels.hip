@@ -952,10 +952,12 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
       }
       __syncthreads();
       if (!s_flag) return;
-      // 16-byte runs in flight per thread: as many as the main loop's
-      // registers leave room for (eight tile waves: the single-output form,
-      // with which their allocation stays as it is)
-      constexpr int RU = TW == 8 ? 0 : (BITS == 0 && MT < 4 ? 2 : 4);
+      // 16-byte runs in flight per thread: two (measured faster than four
+      // wherever the main loop holds many registers); the draft at four token
+      // tiles takes four, with which its code needs no private segment;
+      // eight tile waves keep the single-output form, with which their
+      // allocation stays as it is
+      constexpr int RU = TW == 8 ? 0 : (BITS == 0 && MT == 4 ? 4 : 2);
       sum_splits<NT, RU, RB>(a.out, a.split_stride, hv.S, dst, hv.mode == kOutTwoSided, a.ldo, row_base,
                                          nrows, rb * RB, min(RB, a.d_out - rb * RB));
     } else {
