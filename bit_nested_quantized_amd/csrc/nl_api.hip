@@ -616,6 +616,11 @@ static double g_t_lat_us = 2.0, g_t_hbm_gbs = 6500.0, g_t_split_us = 1.5, g_t_xd
 // to T = 8, the former from T = 16 on and for the draft at every T.
 static int g_t_staged_v = 9, g_t_staged_d = 1;
 
+// One pass of the in-workgroup transform (4096 points per 256 threads) in
+// the local form, us: it runs while the weight stream is queued (measured
+// 2.6-4.8 us there, 1.4 us in a rotation workgroup of its own).
+static const double kRotPassUs = 3.0;
+
 // Bytes of one tile-chunk (16 rows x 512 columns) in a pass.
 static double tc_bytes(int bits) { return 16.0 * 512.0 * (0.265625 + (bits ? bits / 8.0 + 1.0 / 64.0 : 0.0)); }
 
@@ -666,10 +671,12 @@ static void choose_job(int n_tiles, int n_chunks, int T, int bits, int mt, int n
         const double share = std::max(1.0, active / 4.0);  // waves per SIMD
         const double t_wave = wc * std::max(g_t_lat_us / std::min(ns, wc), t_c * share) + g_t_lat_us;
         const double xdma = local ? 0.0 : cps * (double)blob / (g_t_xdma_gbs * 1e3);
+        // local form: each pass of the workgroup's transform precedes its contraction
+        const double rot = local ? kRotPassUs * local_passes(T, n_chunks, cps, SB, G) : 0.0;
         const double split = S > 1 ? g_t_split_us + 2.0 * S * T * n_tiles * 16.0 * 4.0 / (g_t_hbm_gbs * 1e3) : 0.0;
         // the slowest wave chain and the HBM time overlap but not completely:
         // a smooth maximum (4-norm) keeps both in view
-        const double a = rounds * (t_wave + xdma), b = total / (g_t_hbm_gbs * 1e3);
+        const double a = rounds * (t_wave + xdma + rot), b = total / (g_t_hbm_gbs * 1e3);
         const double cost = std::pow(std::pow(a, 4.0) + std::pow(b, 4.0), 0.25) + split + 1e-3 * (nw - active) + 1e-4 * S;
         if (cost < best) {
           best = cost;
