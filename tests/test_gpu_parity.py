@@ -325,6 +325,25 @@ def test_split_k_shape_matches_oracle(nl, torch_cuda):
     assert rel_err(y, ref) <= TOL
 
 
+@pytest.mark.parametrize("T", [12, 24])
+@pytest.mark.parametrize("two", [False, True])
+def test_staged_eight_tile_waves_knob(nl, torch_cuda, T, two):
+    # the staged launch with eight tile waves at one and two token tiles (a
+    # tuning knob; by default only short grouped linears take it): split
+    # counts double, the output superblocks of the two-sided form hold more
+    # row blocks
+    torch = torch_cuda
+    lin = synth.make_linear(2048, 4096, 6, cfg=71, idx=0, two_sided=two)
+    x = synth.make_x(T, 4096, cfg=71, idx=0)
+    nl.nested_linear_set_tuning("staged_waves", 8)
+    try:
+        for verify in (True, False):
+            y = run(nl, torch, lin, x, verify)
+            assert rel_err(y, oracle.forward(lin, x, verify)) <= TOL
+    finally:
+        nl.nested_linear_set_tuning("staged_waves", 0)
+
+
 # --- grouped mixture-of-experts projections ---------------------------------------
 
 def make_moe(n_exp, d_out, d_in, bits, T, k, rho, two, cfg, shared=True):
