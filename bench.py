@@ -456,16 +456,18 @@ MOE_ROUTINGS = 8
 def moe_leg(nl, torch, synth, reps, stream_gbps):
     """MoE block verify and draft: 256 routed experts (hidden 2048, expert
     intermediate 512) plus one shared expert, top-8 routing of a 16-token
-    block, 2-bit base + 8-bit residual; one grouped call per projection.  Gate
-    and up read the block's 16 token rows; down reads each pair's own
-    512-wide row (P rows, pair_token = 0..P-1).  Two routings: router logits
+    block, 2-bit base + 8-bit residual.  Gate and up share their input, so
+    each expert holds them as one stacked matrix (512 gate rows, then 512 up
+    rows) and one grouped call on the block's 16 token rows computes both;
+    down is a second grouped call on each pair's own 512-wide row (P rows,
+    pair_token = 0..P-1).  Two routings: router logits
     correlated across the block (rho = 0.62, about 47 experts awake) and iid
     (rho = 0, about 102).  Every expert owns its own device copy of its planes
     and passes cycle through 8 routings so the expert set streams from HBM."""
     import numpy as np
     import oracle
     n = MOE_EXPERTS + 1
-    shapes = {"gate": (MOE_INTER, MOE_HIDDEN), "up": (MOE_INTER, MOE_HIDDEN), "down": (MOE_HIDDEN, MOE_INTER)}
+    shapes = {"gate_up": (2 * MOE_INTER, MOE_HIDDEN), "down": (MOE_HIDDEN, MOE_INTER)}
     groups, handles, lins = {}, [], {}
     for k, (o, i) in shapes.items():
         lin = synth.make_linear(o, i, MOE_BITS, cfg=4, idx=len(groups), two_sided=False)
@@ -478,8 +480,9 @@ def moe_leg(nl, torch, synth, reps, stream_gbps):
     x_np = synth.make_x(MOE_T, MOE_HIDDEN, cfg=4, idx=100)
     x = torch.from_numpy(x_np.view(np.int16)).cuda()
     out = {"workload": (f"{MOE_EXPERTS} experts + 1 shared, hidden {MOE_HIDDEN}, expert intermediate {MOE_INTER}, "
-                        f"top-{MOE_TOPK} of a {MOE_T}-token block, {MOE_BITS}-bit residual; gate, up: one grouped "
-                        f"call each on the token rows; down: one grouped call on per-pair rows")}
+                        f"top-{MOE_TOPK} of a {MOE_T}-token block, {MOE_BITS}-bit residual; gate and up stacked "
+                        f"into one {2 * MOE_INTER}x{MOE_HIDDEN} matrix per expert, one grouped call on the token rows; "
+                        f"down: one grouped call on per-pair rows")}
     for rho in (0.62, 0.0):
         routes = []
         for r in range(MOE_ROUTINGS):
@@ -496,8 +499,7 @@ def moe_leg(nl, torch, synth, reps, stream_gbps):
         # down-projection inputs: one synthetic 512-wide row per pair
         h_np = synth.make_x(Pmax, MOE_INTER, cfg=4, idx=101)
         h = torch.from_numpy(h_np.view(np.int16)).cuda()
-        yg = torch.empty((Pmax, MOE_INTER), dtype=torch.float32, device="cuda")
-        yu = torch.empty_like(yg)
+        ygu = torch.empty((Pmax, 2 * MOE_INTER), dtype=torch.float32, device="cuda")
         yd = torch.empty((Pmax, MOE_HIDDEN), dtype=torch.float32, device="cuda")
         res = {"active_experts_avg": round(sum(r[4] for r in routes) / MOE_ROUTINGS, 1)}
         for verify in (True, False):
@@ -505,17 +507,16 @@ def moe_leg(nl, torch, synth, reps, stream_gbps):
 
             def passes(s):
                 for pt, off, ident, P, *_ in routes:
-                    fn(groups["gate"], pt, off, P, x, MOE_T, MOE_T, yg, ws["gate"], s)
-                    fn(groups["up"], pt, off, P, x, MOE_T, MOE_T, yu, ws["up"], s)
+                    fn(groups["gate_up"], pt, off, P, x, MOE_T, MOE_T, ygu, ws["gate_up"], s)
                     fn(groups["down"], ident, off, P, h, P, MOE_T, yd, ws["down"], s)
 
             # parity of the first routing (all experts share one synthetic linear per projection)
             pt_d, off_d, ident, P, _, pt_np, off_np = routes[0]
-            fn(groups["gate"], pt_d, off_d, P, x, MOE_T, MOE_T, yg, ws["gate"])
+            fn(groups["gate_up"], pt_d, off_d, P, x, MOE_T, MOE_T, ygu, ws["gate_up"])
             fn(groups["down"], ident, off_d, P, h, P, MOE_T, yd, ws["down"])
-            for k in ("gate", "down"):
+            for k in ("gate_up", "down"):
                 check_status(nl, ws[k], "moe")
-            e_g = rel_err(yg[:P].cpu().numpy(), oracle.forward(lins["gate"], x_np[pt_np], verify))
+            e_g = rel_err(ygu[:P].cpu().numpy(), oracle.forward(lins["gate_up"], x_np[pt_np], verify))
             e_d = rel_err(yd[:P].cpu().numpy(), oracle.forward(lins["down"], h_np[:P], verify))
             g = capture(torch, passes)
             st = pstats([u / MOE_ROUTINGS for u in replay_samples(torch, g, reps)])

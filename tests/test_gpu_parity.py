@@ -381,7 +381,7 @@ def run_grouped(nl, torch, experts, pt, off, x, verify, T=None):
         nl.nested_linear_group_destroy(g)
 
 
-@pytest.mark.parametrize("d_out,d_in", [(512, 2048), (2048, 512)])
+@pytest.mark.parametrize("d_out,d_in", [(512, 2048), (1024, 2048), (2048, 512)])
 @pytest.mark.parametrize("two", [False, True])
 @pytest.mark.parametrize("verify", [False, True])
 def test_grouped_moe_block(nl, torch_cuda, d_out, d_in, two, verify):
