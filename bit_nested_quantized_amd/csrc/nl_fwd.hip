@@ -708,6 +708,12 @@ __device__ void fin_role(const FwdArgs2 &a, int b, char *smem) {
   const int r0 = sbi * OB;
   float *xch = reinterpret_cast<float *>(smem + kLdsX + grp * kFwhtArea) + tl * (OB + (OB >> 4));
   uint32_t *flag = reinterpret_cast<uint32_t *>(smem + kLdsFlag) + grp * per_grp + tl;
+  // the thread's 16 output signs (inputs of the call), requested before the
+  // wait on the superblock so that no load is left after the transform
+  const int rr = r0 + 16 * lt;
+  int sg[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) sg[q] = so[min(rr + q, dj - 1)];
   if (lt == 0)
     *flag = valid ? take_one(ctr_at(ctr, csb + nsbj + sbi), a.wait_extra, a.spin_limit, ctr_at(ctr, kCtrErr)) : 1u;
   __syncthreads();
@@ -719,11 +725,10 @@ __device__ void fin_role(const FwdArgs2 &a, int b, char *smem) {
   fwht_tasks(v, xch, lt, TPS, n, a.lb_out);
   if (!valid) return;
   float *yo = y + (size_t)t * dj;
-  const int rr = r0 + 16 * lt;
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int r = rr + q;
-    if (r < dj) yo[r] = okw ? v[q] * a.rsqrt_out * (float)so[r] : __builtin_nanf("");
+    if (r < dj) yo[r] = okw ? v[q] * a.rsqrt_out * (float)sg[q] : __builtin_nanf("");
   }
 }
 

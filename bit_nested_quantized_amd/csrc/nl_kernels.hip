@@ -1028,6 +1028,17 @@ __device__ __forceinline__ void finish_body(const FinishArgs &a, int wg, float *
     so = a.lins[e].sign_out;
   }
   float *y = a.y + (size_t)t * a.d_out;
+  // single launch with the output rotation: the thread's 16 output signs
+  // (inputs of the call), requested before the wait on the superblock so
+  // that no load is left after the transform
+  const int r0 = rb + 16 * lt;
+  int sg[16];
+  if constexpr (FUSED) {
+    if (rotate_out) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sg[j] = so[min(r0 + j, a.d_out - 1)];
+    }
+  }
   float v[16];
   if constexpr (FUSED) {
     __shared__ uint32_t s_lost[8];  // per task of the workgroup (256 / TPS <= 8): its wait gave up
@@ -1065,12 +1076,11 @@ __device__ __forceinline__ void finish_body(const FinishArgs &a, int wg, float *
   if (rotate_out) {
     fwht_tasks(v, x, lt, TPS, n, a.lb);
     // layout B: 16 consecutive outputs per thread
-    const int r0 = rb + 16 * lt;
     if (!valid) return;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int r = r0 + j;
-      if (r < a.d_out) y[r] = v[j] * a.rsqrt_b * (float)so[r];
+      if (r < a.d_out) y[r] = v[j] * a.rsqrt_b * (float)(FUSED ? sg[j] : so[r]);
     }
   } else {
     if (!valid) return;
