@@ -242,7 +242,8 @@ def nested_linear_describe_call(d_outs, d_in: int, bits: int, two_sided: bool, T
 
 NL_TUNE = {"splits": 1, "row_tiles": 2, "waves_per_tile": 3, "local_t": 4, "cus": 5, "lat_us": 6, "hbm_gbs": 7,
            "split_us": 8, "xdma_gbs": 9, "spin_limit": 10, "wait_extra": 11, "waves": 12,
-           "staged_t_verify": 13, "staged_t_draft": 14, "staged_waves": 15}
+           "staged_t_verify": 13, "staged_t_draft": 14, "staged_waves": 15,
+           "multi_staged_t_verify": 16, "multi_staged_t_draft": 17}
 
 
 def nested_linear_set_tuning(knob: str, value: float):

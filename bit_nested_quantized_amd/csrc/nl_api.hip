@@ -615,6 +615,12 @@ static double g_t_lat_us = 2.0, g_t_hbm_gbs = 6500.0, g_t_split_us = 1.5, g_t_xd
 // Measured on the 7B/8B-class projections: the latter is ahead for verify up
 // to T = 8, the former from T = 16 on and for the draft at every T.
 static int g_t_staged_v = 9, g_t_staged_d = 1;
+// Multi-linear calls whose linears share the shape take the staged launch's
+// grouped form from these T on (verify, draft; 65: never).  Measured on gate
+// and up of the 7B/8B-class layer (2 x 14336x4096): verify equal at T = 24-32
+// and 24-28% faster at 48-64; draft 5% faster at 24 and 38% at 64; both
+// slower at T = 16 and below.
+static int g_t_ms_v = 33, g_t_ms_d = 24;
 
 // One pass of the in-workgroup transform (4096 points per 256 threads) in
 // the local form, us: it runs while the weight stream is queued (measured
@@ -777,6 +783,120 @@ static Plan2 make_plan2(const CallShape *hs, int n, int T, int bits) {
   return p;
 }
 
+// ---------------------------------------------------------------------------
+// Multi-linear calls of one shape (gate and up, say) at large T: the staged
+// launch's grouped form.  Linear q is expert q and owns pair rows q*T .. q*T
+// + T - 1 of x' (its own rotation of x with its own signs; pair q*T + t
+// reads token t), and its rows go to its own y.  The expert array, the
+// offsets and the pair tokens live at the end of the workspace, written by
+// a small kernel on the same stream (a kernel, not a copy, so that the call
+// can be captured into a graph).
+// ---------------------------------------------------------------------------
+struct MultiSetupArgs {
+  LinearDev lin[kMaxJobs];
+  int n, T;
+  LinearDev *lins;
+  int32_t *offsets, *pairs;
+};
+static_assert(kMaxJobs <= 4, "GemmArgs::ys holds four outputs");
+
+__global__ __launch_bounds__(256) void multi_setup_kernel(const MultiSetupArgs s) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i == 0) {
+#pragma unroll
+    for (int q = 0; q < kMaxJobs; ++q)
+      if (q < s.n) s.lins[q] = s.lin[q];
+  }
+  if (i <= s.n) s.offsets[i] = i * s.T;
+  if (i < s.n * s.T) s.pairs[i] = i % s.T;
+}
+
+static bool multi_staged_route(const nl_linear *const *hs, int n, int verify, int T) {
+  if (n < 2 || hs[0]->has_sign_out || T < (verify ? g_t_ms_v : g_t_ms_d)) return false;
+  for (int i = 1; i < n; ++i)
+    if (hs[i]->d_out != hs[0]->d_out || hs[i]->b_in != hs[0]->b_in || hs[i]->bits != hs[0]->bits) return false;
+  return true;
+}
+
+struct MultiPlan {
+  Plan p;
+  size_t o_lins, o_off, o_pairs, total;
+};
+static MultiPlan multi_plan(const nl_linear *h0, int n, int T) {
+  MultiPlan m;
+  m.p = make_plan(h0->d_out, h0->n_tiles, h0->n_chunks, false, h0->b_out, n * T, mt_for(T), n, T,
+                  tile_waves(mt_for(T)));
+  m.o_lins = align256(m.p.total);
+  m.o_off = align256(m.o_lins + sizeof(LinearDev) * n);
+  m.o_pairs = align256(m.o_off + sizeof(int32_t) * (n + 1));
+  m.total = align256(m.o_pairs + sizeof(int32_t) * n * T);
+  return m;
+}
+
+static nl_status forward_multi_staged(const nl_linear *const *hs, int n, int verify, const void *x, int32_t T,
+                                      float *const *ys, void *ws, size_t ws_bytes, void *stream, const char *who) {
+  const nl_linear *h0 = hs[0];
+  const MultiPlan m = multi_plan(h0, n, T);
+  const Plan &p = m.p;
+  if (ws_bytes < m.total) return fail(NL_EINVAL, "%s: workspace too small (%zu < %zu)", who, ws_bytes, m.total);
+  if (p.n_ctr > kCtrLines) return fail(NL_EUNSUPPORTED, "%s: the call needs %d counters (> %d)", who, p.n_ctr, kCtrLines);
+  // the eight-tile-wave variants of one and two token tiles have no per-linear outputs
+  if (p.tw == 8 && p.mt < 3) return fail(NL_EUNSUPPORTED, "%s: no staged multi-linear form at T = %d", who, T);
+  char *w = (char *)ws;
+  MultiSetupArgs sa;
+  memset(&sa, 0, sizeof sa);
+  for (int i = 0; i < n; ++i) sa.lin[i] = hs[i]->dev;
+  sa.n = n;
+  sa.T = T;
+  sa.lins = (LinearDev *)(w + m.o_lins);
+  sa.offsets = (int32_t *)(w + m.o_off);
+  sa.pairs = (int32_t *)(w + m.o_pairs);
+  hipLaunchKernelGGL(multi_setup_kernel, dim3((n * T + 256) / 256), dim3(256), 0, (hipStream_t)stream, sa);
+  HIP_OR_FAIL(hipGetLastError());
+
+  FwdArgs f;
+  memset(&f, 0, sizeof f);
+  RotInArgs &r = f.rot;
+  r.x = (const uint16_t *)x;
+  r.lins = sa.lins;
+  r.pair_token = sa.pairs;
+  r.offsets = sa.offsets;
+  r.n_experts = n;
+  r.x_rows = T;
+  r.rows = n * T;
+  r.lb = log2i(h0->b_in);
+  r.xh = (uint16_t *)(w + p.o_xh);
+  r.meta = (float *)(w + p.o_meta);
+  r.d_in = h0->d_in;
+  r.b = h0->b_in;
+  r.SB = h0->b_in > kChunk ? h0->b_in : kChunk;
+  r.Kp = h0->n_chunks * kChunk;
+  r.Gp = h0->n_chunks * 4;
+  r.n_chunks = h0->n_chunks;
+  r.rsqrt_b = (float)(1.0 / std::sqrt((double)h0->b_in));
+  GemmArgs &ga = f.g;
+  ga.lins = sa.lins;
+  ga.offsets = sa.offsets;
+  ga.xh = (const uint16_t *)(w + p.o_xh);
+  ga.meta = (const float *)(w + p.o_meta);
+  ga.T = n * T;
+  ga.d_out = h0->d_out;
+  ga.n_tiles = h0->n_tiles;
+  ga.n_chunks = h0->n_chunks;
+  ga.Kp = r.Kp;
+  ga.Gp = r.Gp;
+  ga.cps = p.cps;
+  ga.ldo = h0->d_out;
+  ga.n_rb = p.n_rb;
+  ga.n_experts = n;
+  for (int i = 0; i < n; ++i) ga.ys[i] = ys[i];
+  fill_launch(f, p, n, w, ys[0], h0->d_out);
+  hipEvent_t e0, e1;
+  timing_slot((hipStream_t)stream, &e0, &e1);
+  HIP_OR_FAIL(launch_forward(f, verify ? h0->bits : 0, p.mt, p.tw, 0, (hipStream_t)stream, e0, e1));
+  return ok();
+}
+
 static nl_status forward_n(const nl_linear *const *hs, int n, int verify, const void *x, int32_t T, float *const *ys,
                            void *ws, size_t ws_bytes, void *stream, const char *who) {
   if (n < 1 || n > kMaxJobs) return fail(NL_EINVAL, "%s: between 1 and %d linears per call (got %d)", who, kMaxJobs, n);
@@ -796,6 +916,7 @@ static nl_status forward_n(const nl_linear *const *hs, int n, int verify, const 
   if ((uintptr_t)x & 15) return fail(NL_EINVAL, "%s: x must be 16-byte aligned", who);
   if (!ws) return fail(NL_EINVAL, "%s: NULL workspace", who);
   if ((uintptr_t)ws & 255) return fail(NL_EINVAL, "%s: workspace must be 256-byte aligned", who);
+  if (multi_staged_route(hs, n, verify, T)) return forward_multi_staged(hs, n, verify, x, T, ys, ws, ws_bytes, stream, who);
   const int bits = verify ? hs[0]->bits : 0;
   CallShape cs[kMaxJobs];
   for (int i = 0; i < n; ++i) cs[i] = shape_of(hs[i]);
@@ -1022,8 +1143,14 @@ extern "C" nl_status nested_linear_multi_workspace_bytes(const nl_handle *hs, in
   size_t mx = 0;
   CallShape cs[kMaxJobs];
   for (int i = 0; i < n; ++i) cs[i] = shape_of(hs[i]);
-  for (int T = 1; T <= T_max; ++T)
+  // the staged grouped form of linears of one shape, at any T (its threshold is a tuning knob)
+  bool one_shape = n >= 2 && !hs[0]->has_sign_out;
+  for (int i = 1; i < n; ++i)
+    one_shape = one_shape && hs[i]->d_out == hs[0]->d_out && hs[i]->b_in == hs[0]->b_in && hs[i]->bits == hs[0]->bits;
+  for (int T = 1; T <= T_max; ++T) {
     for (int b = 0; b < 2; ++b) mx = std::max(mx, make_plan2(cs, n, T, b ? hs[0]->bits : 0).total);
+    if (one_shape) mx = std::max(mx, multi_plan(hs[0], n, T).total);
+  }
   *bytes = mx;
   return ok();
 }
@@ -1068,6 +1195,8 @@ extern "C" nl_status nested_linear_set_tuning(int32_t knob, double value) {
     case NL_TUNE_STAGED_T_VERIFY: g_t_staged_v = value > 0 ? (int)value : 9; break;
     case NL_TUNE_STAGED_T_DRAFT: g_t_staged_d = value > 0 ? (int)value : 1; break;
     case NL_TUNE_STAGED_WAVES: g_t_stw = ((int)value == 4 || (int)value == 8) ? (int)value : 0; break;
+    case NL_TUNE_MULTI_STAGED_T_VERIFY: g_t_ms_v = value > 0 ? (int)value : 33; break;
+    case NL_TUNE_MULTI_STAGED_T_DRAFT: g_t_ms_d = value > 0 ? (int)value : 24; break;
     default: return fail(NL_EINVAL, "set_tuning: unknown knob %d", knob);
   }
   return ok();

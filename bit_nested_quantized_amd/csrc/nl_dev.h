@@ -335,9 +335,12 @@ __device__ __forceinline__ const void *sgpr_ptr(const void *p) {
 // round.
 // RBC > 0: the row block's height as a constant (rows <= RBC), so that the
 // output index splits by a constant divisor.
+// out_tb: the output's row of token 0 (tb, or 0 for an output of the row
+// block's own).
 template <int NT, int U, int RBC = 0>
 __device__ __forceinline__ void sum_splits(const float *part, size_t stride, int S, float *out, bool coh, size_t ld,
-                                           int tb, int nt, int r0, int rows) {
+                                           int tb, int nt, int r0, int rows, int out_tb) {
+  const size_t shift = (size_t)(tb - out_tb) * ld;  // output index = partial index - shift
   const int rstep = RBC > 0 ? RBC : rows;  // outputs of one token in the index space
   const size_t span = (size_t)S * stride * 4;
   const bool vec = U > 0 && ((ld | stride | (size_t)r0 | (size_t)rows) & 3) == 0 && ((uintptr_t)part & 15) == 0 &&
@@ -377,7 +380,7 @@ __device__ __forceinline__ void sum_splits(const float *part, size_t stride, int
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (o[u] != ~0u) {
-          float *p = out + o[u];
+          float *p = out + (o[u] - shift);
           if (coh) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) st_dev(p + i, v[u][i]);
@@ -415,7 +418,7 @@ __device__ __forceinline__ void sum_splits(const float *part, size_t stride, int
 #pragma unroll
     for (int e4 = 0; e4 < 4; ++e4) {
       if (!ok[e4]) continue;
-      if (coh) st_dev(out + o[e4], v[e4]); else out[o[e4]] = v[e4];
+      if (coh) st_dev(out + (o[e4] - shift), v[e4]); else out[o[e4] - shift] = v[e4];
     }
   }
 }

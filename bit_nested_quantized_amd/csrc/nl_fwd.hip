@@ -635,7 +635,7 @@ __device__ void con_role(const FwdArgs2 &a, int cb, char *smem) {
       const int r0 = rb * rt * kTileRows;
       // two 16-byte runs in flight per thread (four: slower at four token tiles)
       sum_splits<NT, 2>(J.part, (size_t)T * d_out, S, two ? J.ysum : J.y, two, (size_t)d_out, 0, T,
-                                         r0, min(rt * kTileRows, d_out - r0));
+                                         r0, min(rt * kTileRows, d_out - r0), 0);
     }
   }
   if (two && have_sum) {

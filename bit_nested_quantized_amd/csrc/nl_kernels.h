@@ -56,6 +56,8 @@ struct GemmArgs {
   int T;                    // rows of x' (tokens or pairs)
   int d_out, n_tiles, n_chunks, Kp, Gp, cps, ldo, n_rb, n_experts;
   int slots;                // grouped: grid slots map to the experts with rows (else slot = expert)
+  float *ys[4];             // one-sided multi-linear form (experts = linears of one x, all rows of
+                            // each): expert e's row t goes to row t of ys[e]; else null
 };
 
 struct FinishArgs {

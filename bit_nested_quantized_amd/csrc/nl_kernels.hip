@@ -915,7 +915,14 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
   }
   const int row = tile * kTileRows + tl;  // output row of this lane (B column)
   const bool store = active && row < a.d_out;
-  auto put = [&](float *out, size_t ld, bool coh) {
+  // multi-linear form: the expert's rows land in its own output from row 0
+  // (it runs at 24 tokens and more; the eight-tile-wave variants of one and
+  // two token tiles, which short grouped experts take, leave it out and keep
+  // their registers)
+  constexpr bool OWN = FUSED && !(TW == 8 && MT < 3);
+  const bool own_out = OWN && a.ys[0] != nullptr;
+  float *const y_own = own_out ? a.ys[min(e, 3)] : nullptr;
+  auto put = [&](float *out, size_t ld, bool coh, int rbase) {
     if (!store) return;
 #pragma unroll
     for (int m = 0; m < MTC; ++m)
@@ -923,25 +930,25 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
       for (int i = 0; i < 4; ++i) {
         const int t = m * 16 + 4 * kq + i;
         if (t < nrows) {
-          float *p = out + (size_t)(row_base + t) * ld + row;
+          float *p = out + (size_t)(rbase + t) * ld + row;
           if (coh) st_dev(p, acc[m][i]); else *p = acc[m][i];
         }
       }
   };
   if constexpr (!FUSED) {
-    put(a.out + split * a.split_stride, a.ldo, false);
+    put(a.out + split * a.split_stride, a.ldo, false, row_base);
     return;
   } else {
     const int lin = a.lins ? e : 0;
     if (hv.mode == kOutDirect) {
-      put(a.out, a.ldo, false);
+      if (own_out) put(y_own, a.ldo, false, 0); else put(a.out, a.ldo, false, row_base);
       return;
     }
     // Split partials, then the last workgroup of the row block to arrive sums
     // them in split order (deterministic) into y (one-sided) or ysum.
     float *dst = hv.mode == kOutTwoSided ? hv.ysum : hv.y;
     if (hv.S > 1) {
-      put(a.out + split * a.split_stride, a.ldo, true);
+      put(a.out + split * a.split_stride, a.ldo, true, row_base);
       wait_stores();
       __syncthreads();
       if (threadIdx.x == 0) {
@@ -958,10 +965,10 @@ __device__ __forceinline__ void contract_body(const GemmArgs &a, int e, int rb, 
       // eight tile waves keep the single-output form, with which their
       // allocation stays as it is
       constexpr int RU = TW == 8 ? 0 : (BITS == 0 && MT == 4 ? 4 : 2);
-      sum_splits<NT, RU, RB>(a.out, a.split_stride, hv.S, dst, hv.mode == kOutTwoSided, a.ldo, row_base,
-                                         nrows, rb * RB, min(RB, a.d_out - rb * RB));
+      sum_splits<NT, RU, RB>(a.out, a.split_stride, hv.S, own_out ? y_own : dst, hv.mode == kOutTwoSided, a.ldo,
+                             row_base, nrows, rb * RB, min(RB, a.d_out - rb * RB), own_out ? 0 : row_base);
     } else {
-      put(dst, a.ldo, hv.mode == kOutTwoSided);
+      put(dst, a.ldo, hv.mode == kOutTwoSided, row_base);
     }
     if (hv.mode != kOutTwoSided) return;
     // Two-sided: count the row block into each output superblock it overlaps

@@ -177,8 +177,14 @@ nl_status nested_linear_draft(nl_handle h, const void *x_bf16, int32_t T, float 
  * levels, and each output ys[i] is [T][d_out_i] fp32.  ys is a host array of n
  * device pointers.  The workspace must hold
  * nested_linear_multi_workspace_bytes(hs, n, T) bytes; the other rules are
- * those of nested_linear_verify.  The result equals n separate calls (each
- * linear's contraction order is the same).
+ * those of nested_linear_verify.  Each linear's arithmetic is that of a
+ * separate call; the split count of K (and with it the order in which the
+ * split partial sums are added) may differ.  Linears of one shape without the
+ * output rotation (gate and up, say) take, from T = 33 for verify and T = 24
+ * for the draft (NL_TUNE_MULTI_STAGED_T_*), the staged-x' launch in its
+ * grouped form: each linear is an expert that takes all T rows; that form
+ * keeps its expert descriptors and row maps in the workspace and writes them
+ * with a small kernel on the same stream before the launch.
  */
 nl_status nested_linear_verify_multi(const nl_handle *hs /* host array */, int32_t n, const void *x_bf16,
                                      int32_t T, float *const *ys /* host array */, void *ws, size_t ws_bytes,
@@ -233,8 +239,12 @@ typedef enum {
   NL_TUNE_STAGED_T_VERIFY = 13, /* single-linear verify with T at or above this uses the staged-x' launch
                                    (default 9; 65 never) */
   NL_TUNE_STAGED_T_DRAFT = 14,  /* the same for the draft (default 1: always) */
-  NL_TUNE_STAGED_WAVES = 15     /* tile waves per workgroup of the staged launch at 3..48 tokens: 4 or 8
+  NL_TUNE_STAGED_WAVES = 15,    /* tile waves per workgroup of the staged launch at 3..48 tokens: 4 or 8
                                    (0: planner) */
+  NL_TUNE_MULTI_STAGED_T_VERIFY = 16, /* *_multi verify of linears of one shape (one-sided) with T at or
+                                         above this takes the staged launch's grouped form (default 33;
+                                         65 never) */
+  NL_TUNE_MULTI_STAGED_T_DRAFT = 17   /* the same for the draft (default 24) */
 } nl_tuning;
 nl_status nested_linear_set_tuning(int32_t knob, double value);
 

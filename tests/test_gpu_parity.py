@@ -344,6 +344,59 @@ def test_staged_eight_tile_waves_knob(nl, torch_cuda, T, two):
         nl.nested_linear_set_tuning("staged_waves", 0)
 
 
+# --- linears that share x in one call (*_multi) ------------------------------------
+
+def run_multi(nl, torch, lins, x, verify):
+    Ls = [nl.Linear(lin) for lin in lins]
+    hs = [L.h for L in Ls]
+    T = x.shape[0]
+    ws = torch.zeros(nl.nested_linear_multi_workspace_bytes(hs, T), dtype=torch.uint8, device="cuda")
+    ys = [torch.full((T, lin["d_out"]), float("nan"), dtype=torch.float32, device="cuda") for lin in lins]
+    fn = nl.nested_linear_verify_multi if verify else nl.nested_linear_draft_multi
+    xd = to_dev(torch, x)
+    fn(hs, xd, T, ys, ws)
+    fn(hs, xd, T, ys, ws)   # the same workspace again
+    torch.cuda.synchronize()
+    assert nl.nested_linear_workspace_status(ws) == 0
+    assert int(ws[:COUNTER_BYTES].count_nonzero()) == 0
+    out = [y.cpu().numpy() for y in ys]
+    del Ls
+    return out
+
+
+@pytest.mark.parametrize("T", [1, 3, 16, 40])
+@pytest.mark.parametrize("two", [False, True])
+def test_multi_linears_of_several_shapes(nl, torch_cuda, T, two):
+    # q/k/v-like: three linears of different d_out on one x, each with its own signs and levels
+    lins = [synth.make_linear(o, 1024, 6, cfg=72, idx=i, two_sided=two) for i, o in enumerate((768, 256, 256))]
+    x = synth.make_x(T, 1024, cfg=72, idx=T)
+    for verify in (True, False):
+        ys = run_multi(nl, torch_cuda, lins, x, verify)
+        for lin, y in zip(lins, ys):
+            assert rel_err(y, oracle.forward(lin, x, verify)) <= TOL
+
+
+@pytest.mark.parametrize("d_out,d_in", [(768, 1024), (2048, 512)])
+@pytest.mark.parametrize("n", [2, 3])
+@pytest.mark.parametrize("T", [1, 17, 40, 64])
+def test_multi_linears_of_one_shape_staged(nl, torch_cuda, d_out, d_in, n, T):
+    # gate/up-like: linears of one shape through the staged launch's grouped
+    # form (forced from T = 1 by the thresholds), each writing its own y: with
+    # K split (768x1024) and without (2048x512, one chunk)
+    lins = [synth.make_linear(d_out, d_in, 7, cfg=73, idx=i) for i in range(n)]
+    x = synth.make_x(T, d_in, cfg=73, idx=T)
+    nl.nested_linear_set_tuning("multi_staged_t_verify", 1)
+    nl.nested_linear_set_tuning("multi_staged_t_draft", 1)
+    try:
+        for verify in (True, False):
+            ys = run_multi(nl, torch_cuda, lins, x, verify)
+            for lin, y in zip(lins, ys):
+                assert rel_err(y, oracle.forward(lin, x, verify)) <= TOL
+    finally:
+        nl.nested_linear_set_tuning("multi_staged_t_verify", 0)
+        nl.nested_linear_set_tuning("multi_staged_t_draft", 0)
+
+
 # --- grouped mixture-of-experts projections ---------------------------------------
 
 def make_moe(n_exp, d_out, d_in, bits, T, k, rho, two, cfg, shared=True):
