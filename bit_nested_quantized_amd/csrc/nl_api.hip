@@ -331,7 +331,7 @@ static int g_t_stw = 0;
 // tokens: rows of x per linear (T; a grouped call routes each token to an
 // expert at most once).
 static Plan make_plan(int d_out, int n_tiles, int n_chunks, bool sign_out, int b_out, int rows, int mt,
-                      int n_linears, int tokens, int tw) {
+                      int n_linears, int tokens, int tw, int b_in) {
   Plan p;
   p.rows = rows;
   p.mt = mt;
@@ -343,6 +343,19 @@ static Plan make_plan(int d_out, int n_tiles, int n_chunks, bool sign_out, int b
   if (g_splits > 0) S = g_splits < n_chunks ? g_splits : n_chunks;
   p.cps = (n_chunks + S - 1) / S;
   p.S = (n_chunks + p.cps - 1) / p.cps;
+  // In-workgroup rotation: a K-range inside one input superblock (SB/512
+  // chunks) takes one transform pass, one that straddles two takes two.
+  // Align the ranges to the superblocks when that keeps the split count.
+  if (g_splits <= 0 && tw == 4 && mt == 1 && tokens <= kLocalTokens) {
+    const int cpsb = std::max(b_in, kChunk) / kChunk;
+    int c = p.cps;
+    if (c < cpsb) {
+      while (cpsb % c) ++c;  // a divisor of the superblock
+    } else {
+      c = (c + cpsb - 1) / cpsb * cpsb;  // whole superblocks
+    }
+    if (c != p.cps && (n_chunks + c - 1) / c == p.S) p.cps = c;
+  }
   p.finish = sign_out || p.S > 1 || n_linears > 1;
   p.mode = sign_out ? kOutTwoSided : (p.S > 1 ? kOutSplit : kOutDirect);
   p.local = tw == 4 && mt == 1 && tokens <= kLocalTokens && p.cps <= kLocalChunks;
@@ -378,7 +391,8 @@ static nl_status check_call(nl_handle h, const char *who, int verify, int32_t T,
   if (T > NL_MAX_T) return fail(NL_EUNSUPPORTED, "%s: T = %d exceeds %d", who, T, NL_MAX_T);
   if (!ws) return fail(NL_EINVAL, "%s: NULL workspace", who);
   if ((uintptr_t)ws & 255) return fail(NL_EINVAL, "%s: workspace must be 256-byte aligned", who);
-  *plan = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, h->b_out, T, mt_for(T), 1, T, tw);
+  *plan = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, h->b_out, T, mt_for(T), 1, T, tw,
+                    h->b_in);
   if (ws_bytes < plan->total)
     return fail(NL_EINVAL, "%s: workspace too small (%zu < %zu)", who, ws_bytes, plan->total);
   if (plan->n_ctr > kCtrLines)
@@ -825,7 +839,7 @@ struct MultiPlan {
 static MultiPlan multi_plan(const nl_linear *h0, int n, int T) {
   MultiPlan m;
   m.p = make_plan(h0->d_out, h0->n_tiles, h0->n_chunks, false, h0->b_out, n * T, mt_for(T), n, T,
-                  tile_waves(mt_for(T)));
+                  tile_waves(mt_for(T)), h0->b_in);
   m.o_lins = align256(m.p.total);
   m.o_off = align256(m.o_lins + sizeof(LinearDev) * n);
   m.o_pairs = align256(m.o_off + sizeof(int32_t) * (n + 1));
@@ -1072,7 +1086,7 @@ extern "C" nl_status nested_linear_forward_static(nl_handle h, int32_t verify, c
   int n_ctr;
   if (use_staged(verify, T)) {
     const Plan p = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, h->b_out, T, mt_for(T), 1, T,
-                             staged_tile_waves(T));
+                             staged_tile_waves(T), h->b_in);
     total = p.total;
     n_ctr = p.n_ctr;
   } else {
@@ -1168,7 +1182,8 @@ extern "C" nl_status nested_linear_workspace_bytes(nl_handle h, int32_t T_max, s
     // single launch's, draft and verify
     for (int tw : {tile_waves(mt_for(T)), 4, 8}) {
       if (tw != tile_waves(mt_for(T)) && mt_for(T) > (tw == 8 ? 3 : 2)) continue;
-      const Plan p = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, h->b_out, T, mt_for(T), 1, T, tw);
+      const Plan p = make_plan(h->d_out, h->n_tiles, h->n_chunks, h->has_sign_out, h->b_out, T, mt_for(T), 1, T, tw,
+                               h->b_in);
       mx = std::max(mx, p.total);
     }
     mx = std::max(mx, make_plan2(hs, 1, T, 0).total);
@@ -1306,7 +1321,8 @@ static Plan group_plan(nl_group_handle g, int P, int T) {
   // short experts (K of at most two chunks): eight tile waves, half the
   // workgroups; longer ones keep the deeper register ring of four
   const int tw = T > kLocalTokens && g->n_chunks <= 2 && mt_for(T) < 4 ? 8 : tile_waves(mt_for(T));
-  return make_plan(g->d_out, g->n_tiles, g->n_chunks, g->has_sign_out, g->b_out, P, mt_for(T), g->n, T, tw);
+  return make_plan(g->d_out, g->n_tiles, g->n_chunks, g->has_sign_out, g->b_out, P, mt_for(T), g->n, T, tw,
+                   g->b_in);
 }
 
 extern "C" nl_status nested_linear_group_workspace_bytes(nl_group_handle g, int32_t P_max,
