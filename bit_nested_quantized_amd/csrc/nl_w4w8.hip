@@ -96,6 +96,29 @@ __device__ __forceinline__ void st_agent(float *p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+constexpr int kSc1 = 16;  // cache policy of a buffer load: agent-coherent (sc1), as ld_agent
+
+// Max and sum over an aligned row of 16 lanes by DPP moves (quad swaps for
+// distances 1 and 2, the half-row mirror for 4, the row mirror for 8; a
+// shuffle through LDS waits ~100 cycles per step).  After each step the
+// lanes of a group hold equal values, so the result is an xor butterfly's,
+// bit for bit.  All 16 lanes of the row must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float m) {
+  m = fmaxf(m, dpp<0xB1>(m));
+  m = fmaxf(m, dpp<0x4E>(m));
+  m = fmaxf(m, dpp<0x141>(m));
+  return fmaxf(m, dpp<0x140>(m));
+}
+__device__ __forceinline__ float row16_sum(float s) {
+  s += dpp<0xB1>(s);
+  s += dpp<0x4E>(s);
+  s += dpp<0x141>(s);
+  return s + dpp<0x140>(s);
+}
 
 // Four fp16 pairs 1024 + u from one dword of each plane (8 columns).
 // lo/hi: per byte j, the offset code of column 2j / 2j + 1.
@@ -159,21 +182,23 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
   }
 
   // x -> x' in LDS.  Item = (token, group, 16-byte piece); the 16 lanes of a
-  // (token, group) are consecutive, so its max and sum are lane exchanges.
-  // Four loads in flight per thread; items past the end reload the last one
+  // (token, group) are consecutive and 16-aligned, so its max and sum are
+  // exchanges within a row of 16 lanes.  Four loads in flight per thread, or
+  // eight from three token tiles on; items past the end reload the last one
   // (in bounds) and are not staged.
+  constexpr int kStage = MT >= 3 ? 8 : 4;
   const int pieces = ng * 16, items = T16 * pieces;
-  for (int it0 = t; it0 < items; it0 += 4 * kThreads) {
-    uint4 v[4];
+  for (int it0 = t; it0 < items; it0 += kStage * kThreads) {
+    uint4 v[kStage];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kStage; ++j) {
       const int it = min(it0 + j * kThreads, items - 1);
       const int tt = it / pieces, pc = it - tt * pieces;
       v[j] = *reinterpret_cast<const uint4 *>(a.x + (size_t)min(tt, a.T - 1) * a.d_in + (size_t)g0 * kGroup +
                                               pc * 8);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kStage; ++j) {
       const int it = it0 + j * kThreads;
       if (it < items) {
         const int tt = it / pieces, pc = it - tt * pieces, gi = pc >> 4, p = pc & 15;
@@ -187,8 +212,7 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
         float m = 0.0f;
 #pragma unroll
         for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(f[q]));
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+        m = row16_max(m);   // the item's 16 lanes are one aligned row, all active
         int e = 0;
         if (m > 0.0f) {
           int E;
@@ -202,8 +226,7 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
           h[q] = (_Float16)ldexpf(f[q], e);
           gs += (float)h[q];
         }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) gs += __shfl_xor(gs, o);
+        gs = row16_sum(gs);
         *reinterpret_cast<half8 *>(xs + (size_t)tt * a.pitch + pc * 8) = h;
         if (p == 0) meta[gi * T16 + tt] = make_float2(ldexpf(1.0f, -e), kBias * gs);
       }
@@ -219,17 +242,23 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
   for (int gg = 0; gg < ngp; gg += kRing) {
 #pragma unroll
     for (int i = 0; i < kRing; ++i) {
+      // slots past the split's last group only keep the ring's loads going
       const int gi = gg + i;
+      const bool live = gi < ng;   // uniform over the workgroup
       const int gc = min(gi, ng - 1);
       uint32_t B[4][4];
-      unpack<VERIFY>(wb[i], VERIFY ? wr[i] : wb[i], B);
-      const float s = gi < ng ? h2f(ws[i]) * sdiv : 0.0f;
+      float s = 0.0f;
+      if (live) {
+        unpack<VERIFY>(wb[i], VERIFY ? wr[i] : wb[i], B);
+        s = h2f(ws[i]) * sdiv;
+      }
       {
         const int g = g0 + min(gi + kRing, ng - 1);
         wb[i] = *reinterpret_cast<const uint4 *>(bp + (size_t)g * 1024);
         if constexpr (VERIFY) wr[i] = *reinterpret_cast<const uint4 *>(rp + (size_t)g * 1024);
         ws[i] = sc[(size_t)g * 16];
       }
+      if (!live) continue;
       floatx4 acc[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -283,6 +312,57 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
            (uint32_t)(a.S - 1);
   __syncthreads();
   if (!last) return;
+  // Each output is summed over the splits in split order from zero.  When
+  // the partials' 32-bit buffer offsets suffice, a thread takes up to two
+  // runs of 4 rows and issues the 16-byte agent-scope loads of up to 8 splits
+  // of both before its first add: a row block of 64 tokens costs two memory
+  // round trips per 8 splits instead of sixteen.  Threads without a run
+  // issue nothing.
+  const size_t pstride = (size_t)a.T * a.rows_pad;
+  if ((size_t)a.S * pstride * 4 < 0x7FFFFFFFu) {
+    const __amdgpu_buffer_rsrc_t pr =
+        __builtin_amdgcn_make_buffer_rsrc(a.part, 0, (int)((size_t)a.S * pstride * 4), 0x00020000);
+    constexpr int kRuns = kRows / 4;
+    const int total = a.T * kRuns;
+    for (int base = 0; base < total; base += 2 * kThreads) {
+      if (base + t >= total) break;   // no barrier follows
+      uint32_t o[2];   // float index of the run in split 0, or ~0u for none
+      floatx4 v[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int idx = base + u * kThreads + t, m = idx / kRuns, r4 = idx - m * kRuns;
+        o[u] = idx < total ? (uint32_t)((size_t)m * a.rows_pad + rb * kRows + 4 * r4) : ~0u;
+        v[u] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+      for (int s0 = 0; s0 < a.S; s0 += 8) {
+        floatx4 w[2][8];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          if (o[u] != ~0u)
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+              w[u][q] = __builtin_bit_cast(
+                  floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+                               pr, (int)(((uint32_t)min(s0 + q, a.S - 1) * (uint32_t)pstride + o[u]) * 4u), 0, kSc1));
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          if (o[u] != ~0u)
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+              if (s0 + q < a.S) v[u] += w[u][q];
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (o[u] == ~0u) continue;
+        const int idx = base + u * kThreads + t, m = idx / kRuns, r = rb * kRows + 4 * (idx - m * kRuns);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (r + i < a.d_out) a.y[(size_t)m * a.d_out + r + i] = v[u][i];
+      }
+    }
+    if (t == 0) __hip_atomic_store(&a.tick[rb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
   // partials in split order, eight loads in flight per output
   for (int idx = t; idx < a.T * kRows; idx += kThreads) {
     const int m = idx / kRows, r = rb * kRows + (idx - m * kRows);

@@ -133,12 +133,13 @@ FULL = [("q/o", 4096, 4096), ("k/v", 1024, 4096), ("gate/up", 14336, 4096), ("do
 
 
 @pytest.mark.parametrize("name,d_out,d_in", FULL, ids=[f[0] for f in FULL])
-def test_full_size_sampled_rows(nl, torch_cuda, name, d_out, d_in):
+@pytest.mark.parametrize("T", [16, 64])
+def test_full_size_sampled_rows(nl, torch_cuda, name, d_out, d_in, T):
     lin = synth.make_w4w8_linear(d_out, d_in, cfg=55, idx=d_out + d_in)
-    x = synth.make_x(16, d_in, cfg=55, idx=1)
+    x = synth.make_x(T, d_in, cfg=55, idx=1)
     L = nl.W4W8Linear(lin)
     try:
-        ws = L.workspace(16)
+        ws = L.workspace(T)
         for verify in (False, True):
             y = L.forward(xdev(torch_cuda, x), verify, ws=ws).cpu().numpy().astype(np.float64)
             mid = d_out // 2 - 37
