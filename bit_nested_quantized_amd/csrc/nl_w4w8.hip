@@ -1,8 +1,9 @@
 // nl_w4w8.hip -- the BitNest W4/W8 dual-plane linear (include/nested_w4w8.h).
 //
 // One launch per call.  A workgroup (8 waves) owns 128 rows and one K-split
-// of whole 128-column groups:
-//   * it converts its K-range of x into LDS as fp16, each (token, group)
+// of whole 128-column groups (about one workgroup per CU):
+//   * it converts its K-range of x into LDS as fp16 (in pieces when the
+//     range does not fit), each (token, group)
 //     scaled by a power of two that puts its largest magnitude in
 //     [2^14, 2^15) (bf16 -> fp16 is then exact), with the inverse scale and
 //     the group's sum of x' beside it (a separate conversion launch cost
@@ -65,7 +66,6 @@ constexpr int ring_depth() { return VERIFY && MT == 2 ? 4 : 6; }
 // Dynamic LDS budget for x' and its metadata, and the workgroups resident
 // per CU: two of 60 KiB up to two token tiles, one of 120 KiB beyond.
 constexpr int lds_budget(int mt) { return mt <= 2 ? 60 * 1024 : 120 * 1024; }
-constexpr int wgs_per_cu(int mt) { return mt <= 2 ? 2 : 1; }
 constexpr int kCus = 256;
 
 struct W48Args {
@@ -76,7 +76,7 @@ struct W48Args {
   float *y;
   float *part;            // [S][T][rows_pad]
   uint32_t *tick;         // [rows_pad / kRows]
-  int d_out, d_in, rows_pad, G, T, S, gps, pitch;
+  int d_out, d_in, rows_pad, G, T, S, gps, pg, pitch;
 };
 
 __device__ __forceinline__ float h2f(uint16_t h) {
@@ -181,57 +181,61 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
     ws[i] = sc[(size_t)g * 16];
   }
 
-  // x -> x' in LDS.  Item = (token, group, 16-byte piece); the 16 lanes of a
-  // (token, group) are consecutive and 16-aligned, so its max and sum are
-  // exchanges within a row of 16 lanes.  Four loads in flight per thread, or
-  // eight from three token tiles on; items past the end reload the last one
-  // (in bounds) and are not staged.
+  // x -> x' in LDS, one piece of the split's groups at a time (groups p0 ..
+  // p0 + pg - 1; pg = the whole split when it fits).  Item = (token, group,
+  // 16-byte run); the 16 lanes of a (token, group) are consecutive and
+  // 16-aligned, so its max and sum are exchanges within a row of 16 lanes.
+  // Four loads in flight per thread, or eight from three token tiles on;
+  // items past the end reload the last one (in bounds) and are not staged.
   constexpr int kStage = MT >= 3 ? 8 : 4;
-  const int pieces = ng * 16, items = T16 * pieces;
-  for (int it0 = t; it0 < items; it0 += kStage * kThreads) {
-    uint4 v[kStage];
+  auto stage = [&](int p0) {
+    const int runs = min(a.pg, ng - p0) * 16, items = T16 * runs;
+    const uint16_t *xg = a.x + (size_t)(g0 + p0) * kGroup;
+    for (int it0 = t; it0 < items; it0 += kStage * kThreads) {
+      uint4 v[kStage];
 #pragma unroll
-    for (int j = 0; j < kStage; ++j) {
-      const int it = min(it0 + j * kThreads, items - 1);
-      const int tt = it / pieces, pc = it - tt * pieces;
-      v[j] = *reinterpret_cast<const uint4 *>(a.x + (size_t)min(tt, a.T - 1) * a.d_in + (size_t)g0 * kGroup +
-                                              pc * 8);
-    }
+      for (int j = 0; j < kStage; ++j) {
+        const int it = min(it0 + j * kThreads, items - 1);
+        const int tt = it / runs, pc = it - tt * runs;
+        v[j] = *reinterpret_cast<const uint4 *>(xg + (size_t)min(tt, a.T - 1) * a.d_in + pc * 8);
+      }
 #pragma unroll
-    for (int j = 0; j < kStage; ++j) {
-      const int it = it0 + j * kThreads;
-      if (it < items) {
-        const int tt = it / pieces, pc = it - tt * pieces, gi = pc >> 4, p = pc & 15;
-        const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-        float f[8];
+      for (int j = 0; j < kStage; ++j) {
+        const int it = it0 + j * kThreads;
+        if (it < items) {
+          const int tt = it / runs, pc = it - tt * runs, gi = pc >> 4, p = pc & 15;
+          const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+          float f[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          f[2 * q] = tt < a.T ? __uint_as_float(w[q] << 16) : 0.0f;
-          f[2 * q + 1] = tt < a.T ? __uint_as_float(w[q] & 0xFFFF0000u) : 0.0f;
+          for (int q = 0; q < 4; ++q) {
+            f[2 * q] = tt < a.T ? __uint_as_float(w[q] << 16) : 0.0f;
+            f[2 * q + 1] = tt < a.T ? __uint_as_float(w[q] & 0xFFFF0000u) : 0.0f;
+          }
+          float m = 0.0f;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(f[q]));
+          m = row16_max(m);   // the item's 16 lanes are one aligned row, all active
+          int e = 0;
+          if (m > 0.0f) {
+            int E;
+            frexpf(m, &E);
+            e = 15 - E;   // m * 2^e in [2^14, 2^15)
+          }
+          half8 h;
+          float gs = 0.0f;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            h[q] = (_Float16)ldexpf(f[q], e);
+            gs += (float)h[q];
+          }
+          gs = row16_sum(gs);
+          *reinterpret_cast<half8 *>(xs + (size_t)tt * a.pitch + pc * 8) = h;
+          if (p == 0) meta[gi * T16 + tt] = make_float2(ldexpf(1.0f, -e), kBias * gs);
         }
-        float m = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(f[q]));
-        m = row16_max(m);   // the item's 16 lanes are one aligned row, all active
-        int e = 0;
-        if (m > 0.0f) {
-          int E;
-          frexpf(m, &E);
-          e = 15 - E;   // m * 2^e in [2^14, 2^15)
-        }
-        half8 h;
-        float gs = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          h[q] = (_Float16)ldexpf(f[q], e);
-          gs += (float)h[q];
-        }
-        gs = row16_sum(gs);
-        *reinterpret_cast<half8 *>(xs + (size_t)tt * a.pitch + pc * 8) = h;
-        if (p == 0) meta[gi * T16 + tt] = make_float2(ldexpf(1.0f, -e), kBias * gs);
       }
     }
-  }
+  };
+  stage(0);
   __syncthreads();
 
   floatx4 yacc[MT];
@@ -240,12 +244,21 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
   const float sdiv = VERIFY ? 1.0f / 16.0f : 1.0f;
   const int ngp = (ng + kRing - 1) / kRing * kRing;
   for (int gg = 0; gg < ngp; gg += kRing) {
+    // With several pieces, pg is a multiple of the ring depth: a piece starts
+    // at the top of a ring round.  Every wave is past the previous piece
+    // before it is overwritten.
+    const int pb = gg - gg % a.pg;
+    if (gg > 0 && pb == gg) {
+      __syncthreads();
+      stage(pb);
+      __syncthreads();
+    }
 #pragma unroll
     for (int i = 0; i < kRing; ++i) {
       // slots past the split's last group only keep the ring's loads going
       const int gi = gg + i;
       const bool live = gi < ng;   // uniform over the workgroup
-      const int gc = min(gi, ng - 1);
+      const int gc = gi - pb;      // the group within the staged piece
       uint32_t B[4][4];
       float s = 0.0f;
       if (live) {
@@ -443,31 +456,31 @@ bool valid(nl_w4w8_handle h) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Plan {
-  int mt, S, gps, pitch;
+  int mt, S, gps, pg, pitch;
   size_t lds, tick_bytes, part_bytes;
   size_t total() const { return tick_bytes + part_bytes; }
 };
 
-// Split count: as many workgroups as fit the chip in one round, partials a
-// small share of the weight bytes (8 S T bytes per row written and read
-// against d_in: S <= 0.03 d_in / T keeps them under a quarter), and K-ranges
-// whose x' fits the LDS.
-Plan make_plan(const nl_w4w8 *h, int T) {
+// Split count: one workgroup per CU in one round (measured best at every T
+// on the 7B/8B-class shapes, also where two would fit: 256 workgroups beat
+// 512), but at least four groups per split, so that the split sums of small
+// shapes stay few.  A K-range whose x' does not fit the LDS is staged in
+// pieces of whole ring rounds.
+Plan make_plan(const nl_w4w8 *h, int T, bool verify) {
   Plan p{};
   p.mt = (T + 15) / 16;
   const int T16 = 16 * p.mt;
+  const int ring = verify && p.mt == 2 ? ring_depth<true, 2>() : ring_depth<false, 1>();
   const int kr_max = (int)((lds_budget(p.mt) / T16 - 16) / 2.0625);
   const int gps_max = std::max(1, kr_max / kGroup);
   const int n_rb = h->rows_pad / kRows;
-  const int s_min = (h->G + gps_max - 1) / gps_max;
-  const int s_fill = std::max(1, wgs_per_cu(p.mt) * kCus / n_rb);
-  const int s_part = std::max(1, (int)(0.03 * h->d_in / T));
-  int S = std::max(s_min, std::min(s_fill, s_part));
+  int S = std::min(kCus / n_rb, h->G / 4);
   S = std::min(std::max(S, 1), h->G);
   p.gps = (h->G + S - 1) / S;
   p.S = (h->G + p.gps - 1) / p.gps;
-  p.pitch = p.gps * kGroup + 8;
-  p.lds = (size_t)T16 * p.pitch * 2 + (size_t)p.gps * T16 * 8;
+  p.pg = p.gps <= gps_max ? p.gps : gps_max / ring * ring;
+  p.pitch = p.pg * kGroup + 8;
+  p.lds = (size_t)T16 * p.pitch * 2 + (size_t)p.pg * T16 * 8;
   p.tick_bytes = align256((size_t)n_rb * 4);
   p.part_bytes = p.S > 1 ? (size_t)p.S * T * h->rows_pad * 4 : 0;
   return p;
@@ -516,7 +529,9 @@ nl_status forward(nl_w4w8_handle h, bool verify, const void *x, int32_t T, float
   if ((uintptr_t)x & 15) return fail(NL_EINVAL, "%s: x must be 16-byte aligned", who);
   if ((uintptr_t)ws & 255) return fail(NL_EINVAL, "%s: ws must be 256-byte aligned", who);
   if (verify && !h->has_ref) return fail(NL_EINVAL, "%s: the linear has no refinement plane", who);
-  const Plan p = make_plan(h, T);
+  const Plan p = make_plan(h, T, verify);
+  if (p.pg < 1 || p.lds > (size_t)lds_budget(p.mt))
+    return fail(NL_EUNSUPPORTED, "%s: no LDS plan for T = %d", who, T);
   if (ws_bytes < p.total())
     return fail(NL_EINVAL, "%s: workspace of %zu bytes is smaller than %zu", who, ws_bytes, p.total());
   W48Args a{};
@@ -535,6 +550,7 @@ nl_status forward(nl_w4w8_handle h, bool verify, const void *x, int32_t T, float
   a.T = T;
   a.S = p.S;
   a.gps = p.gps;
+  a.pg = p.pg;
   a.pitch = p.pitch;
   hipStream_t s = static_cast<hipStream_t>(stream);
   HIP_OR_FAIL(verify ? launch<true>(a, p, s) : launch<false>(a, p, s));
@@ -617,7 +633,7 @@ extern "C" nl_status nested_w4w8_workspace_bytes(nl_w4w8_handle h, int32_t T_max
   if (T_max > NL_MAX_T) return fail(NL_EUNSUPPORTED, "%s: T_max = %d exceeds %d", who, T_max, NL_MAX_T);
   size_t need = 0;
   for (int T = 1; T <= T_max; ++T) {
-    const Plan p = make_plan(h, T);
+    const Plan p = make_plan(h, T, true);   // the partials do not depend on the mode
     need = std::max(need, p.total());
   }
   *bytes = need;

@@ -150,6 +150,27 @@ def test_full_size_sampled_rows(nl, torch_cuda, name, d_out, d_in, T):
         L.close()
 
 
+@pytest.mark.parametrize("T", [17, 40, 64])
+def test_x_staged_in_pieces(nl, torch_cuda, T):
+    """16384 x 2176 (17 groups): two splits of 9 and 8 groups.  At two and
+    four token tiles that is more than the LDS holds, so each split stages x
+    in pieces of whole ring rounds, the last one ragged (T = 40 stages it
+    whole); checked on sampled rows."""
+    d_out, d_in = 16384, 2176
+    lin = synth.make_w4w8_linear(d_out, d_in, cfg=56, idx=T)
+    x = synth.make_x(T, d_in, cfg=56, idx=T)
+    L = nl.W4W8Linear(lin)
+    try:
+        ws = L.workspace(T)
+        for verify in (False, True):
+            y = L.forward(xdev(torch_cuda, x), verify, ws=ws).cpu().numpy().astype(np.float64)
+            for r0, r1 in [(0, 64), (8191, 8319), (d_out - 64, d_out)]:
+                ref = w48.forward(lin, x, verify, rows=(r0, r1))
+                assert np.abs(y[:, r0:r1] - ref).max() <= TOL * np.abs(ref).max(), (verify, r0)
+    finally:
+        L.close()
+
+
 def test_errors(nl, torch_cuda):
     lin = synth.make_w4w8_linear(64, 256, cfg=56)
     L = nl.W4W8Linear(lin)
