@@ -2,8 +2,8 @@
 //
 // One launch per call.  A workgroup (8 waves) owns 128 rows and one K-split
 // of whole 128-column groups (about one workgroup per CU):
-//   * it converts its K-range of x into LDS as fp16 (in pieces when the
-//     range does not fit), each (token, group)
+//   * it converts its K-range of x into LDS as fp16 (the T real tokens only,
+//     in pieces when the range does not fit), each (token, group)
 //     scaled by a power of two that puts its largest magnitude in
 //     [2^14, 2^15) (bf16 -> fp16 is then exact), with the inverse scale and
 //     the group's sum of x' beside it (a separate conversion launch cost
@@ -156,7 +156,9 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
   constexpr float kBias = VERIFY ? 1160.0f : 1032.0f;
   constexpr int kRing = ring_depth<VERIFY, MT>();
   _Float16 *xs = reinterpret_cast<_Float16 *>(smem);
-  float2 *meta = reinterpret_cast<float2 *>(smem + (size_t)T16 * a.pitch * 2);
+  // x' holds the T real tokens only; meta (inverse scale, bias * sum) all
+  // T16 tokens of the tiles, zero past T
+  float2 *meta = reinterpret_cast<float2 *>(smem + (size_t)a.T * a.pitch * 2);
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int rb = blockIdx.x / a.S, sp = blockIdx.x - rb * a.S;
   const int g0 = sp * a.gps;
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
   // items past the end reload the last one (in bounds) and are not staged.
   constexpr int kStage = MT >= 3 ? 8 : 4;
   auto stage = [&](int p0) {
-    const int runs = min(a.pg, ng - p0) * 16, items = T16 * runs;
+    const int npc = min(a.pg, ng - p0), runs = npc * 16, items = a.T * runs;
     const uint16_t *xg = a.x + (size_t)(g0 + p0) * kGroup;
     for (int it0 = t; it0 < items; it0 += kStage * kThreads) {
       uint4 v[kStage];
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
       for (int j = 0; j < kStage; ++j) {
         const int it = min(it0 + j * kThreads, items - 1);
         const int tt = it / runs, pc = it - tt * runs;
-        v[j] = *reinterpret_cast<const uint4 *>(xg + (size_t)min(tt, a.T - 1) * a.d_in + pc * 8);
+        v[j] = *reinterpret_cast<const uint4 *>(xg + (size_t)tt * a.d_in + pc * 8);
       }
 #pragma unroll
       for (int j = 0; j < kStage; ++j) {
@@ -208,8 +210,8 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
           float f[8];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            f[2 * q] = tt < a.T ? __uint_as_float(w[q] << 16) : 0.0f;
-            f[2 * q + 1] = tt < a.T ? __uint_as_float(w[q] & 0xFFFF0000u) : 0.0f;
+            f[2 * q] = __uint_as_float(w[q] << 16);
+            f[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
           }
           float m = 0.0f;
 #pragma unroll
@@ -234,6 +236,10 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
         }
       }
     }
+    for (int i = t; i < npc * (T16 - a.T); i += kThreads) {
+      const int gi = i / (T16 - a.T);
+      meta[gi * T16 + a.T + (i - gi * (T16 - a.T))] = make_float2(0.0f, 0.0f);
+    }
   };
   stage(0);
   __syncthreads();
@@ -242,6 +248,10 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) yacc[mt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   const float sdiv = VERIFY ? 1.0f / 16.0f : 1.0f;
+  // A operand rows: tokens past T read token T - 1 (their meta is zero)
+  int aoff[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) aoff[mt] = min(mt * 16 + (lane & 15), a.T - 1) * a.pitch;
   const int ngp = (ng + kRing - 1) / kRing * kRing;
   for (int gg = 0; gg < ngp; gg += kRing) {
     // With several pieces, pg is a multiple of the ring depth: a piece starts
@@ -281,8 +291,7 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
         __builtin_memcpy(&bh, B[st], 16);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const half8 ah = *reinterpret_cast<const half8 *>(xs + (size_t)(mt * 16 + (lane & 15)) * a.pitch +
-                                                             gc * kGroup + kb * 32 + st * 8);
+          const half8 ah = *reinterpret_cast<const half8 *>(xs + aoff[mt] + gc * kGroup + kb * 32 + st * 8);
           acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc[mt], 0, 0, 0);
         }
       }
@@ -471,8 +480,9 @@ Plan make_plan(const nl_w4w8 *h, int T, bool verify) {
   p.mt = (T + 15) / 16;
   const int T16 = 16 * p.mt;
   const int ring = verify && p.mt == 2 ? ring_depth<true, 2>() : ring_depth<false, 1>();
-  const int kr_max = (int)((lds_budget(p.mt) / T16 - 16) / 2.0625);
-  const int gps_max = std::max(1, kr_max / kGroup);
+  // per group: T rows of 128 fp16 and T16 (inverse scale, bias * sum) pairs;
+  // per row 16 bytes of padding
+  const int gps_max = std::max(1, (lds_budget(p.mt) - 16 * T) / (256 * T + 8 * T16));
   const int n_rb = h->rows_pad / kRows;
   int S = std::min(kCus / n_rb, h->G / 4);
   S = std::min(std::max(S, 1), h->G);
@@ -480,7 +490,7 @@ Plan make_plan(const nl_w4w8 *h, int T, bool verify) {
   p.S = (h->G + p.gps - 1) / p.gps;
   p.pg = p.gps <= gps_max ? p.gps : gps_max / ring * ring;
   p.pitch = p.pg * kGroup + 8;
-  p.lds = (size_t)T16 * p.pitch * 2 + (size_t)p.pg * T16 * 8;
+  p.lds = (size_t)T * p.pitch * 2 + (size_t)p.pg * T16 * 8;
   p.tick_bytes = align256((size_t)n_rb * 4);
   p.part_bytes = p.S > 1 ? (size_t)p.S * T * h->rows_pad * 4 : 0;
   return p;

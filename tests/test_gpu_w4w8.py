@@ -152,11 +152,11 @@ def test_full_size_sampled_rows(nl, torch_cuda, name, d_out, d_in, T):
 
 @pytest.mark.parametrize("T", [17, 40, 64])
 def test_x_staged_in_pieces(nl, torch_cuda, T):
-    """16384 x 2176 (17 groups): two splits of 9 and 8 groups.  At two and
-    four token tiles that is more than the LDS holds, so each split stages x
-    in pieces of whole ring rounds, the last one ragged (T = 40 stages it
-    whole); checked on sampled rows."""
-    d_out, d_in = 16384, 2176
+    """16384 x 4224 (33 groups): two splits of 17 and 16 groups, more than the
+    LDS holds at these T, so each split stages x in pieces of whole ring
+    rounds (12 + 5 groups at T = 17, 6 + 6 + 5 at T = 40 and 64), the last
+    one ragged; checked on sampled rows."""
+    d_out, d_in = 16384, 4224
     lin = synth.make_w4w8_linear(d_out, d_in, cfg=56, idx=T)
     x = synth.make_x(T, d_in, cfg=56, idx=T)
     L = nl.W4W8Linear(lin)
