@@ -4,10 +4,13 @@
 // Build: one wave.  Candidate slot s < R is the root's child of rank s; slot
 // R + k R + r is node k's child of rank r, so slot order is push order and
 // "largest priority, then smallest slot" is the heap-with-counter order.
-// Lane l keeps the priorities of slots l, l + 64, ... in registers, and the
-// probability rows the build can reach sit in LDS.  Each step is a wave-wide
-// argmax (largest priority, then smallest slot); the winner becomes node k,
-// its slot dies, and the lanes that own its children's slots compute them.
+// The probability rows the build can reach sit in LDS.  When every such row
+// is non-increasing in rank (the usual rank statistics), lane l keeps only
+// the next child of node l - 1 (lane 0: the root's), since a node's children
+// are popped in rank order; otherwise lane l keeps the priorities of slots
+// l, l + 64, ... in registers.  Each step is a wave-wide argmax (largest
+// priority, then smallest slot); the winner becomes node k, its slot dies,
+// and the lanes that own its sibling's and children's slots compute them.
 //
 // Accept: one wave per sequence; lane c holds node c's parent and token, and
 // each step is one ballot for the child of the current node whose token is
@@ -47,6 +50,51 @@ __device__ __forceinline__ void arg_dpp(double &bp, int &bs) {
   arg_merge(bp, bs, __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo)), dppi<CTRL>(bs));
 }
 
+// The wave's best (priority, slot): DPP steps within rows of 16 lanes (pairs,
+// quads, half-row and row mirrors), then the four row results read as
+// uniform values and merged.  Every lane returns the winner.
+__device__ __forceinline__ void wave_argmax(double &bp, int &bs) {
+  arg_dpp<0xB1>(bp, bs);
+  arg_dpp<0x4E>(bp, bs);
+  arg_dpp<0x141>(bp, bs);
+  arg_dpp<0x140>(bp, bs);
+  const unsigned long long b = (unsigned long long)__double_as_longlong(bp);
+  const int lo = (int)(unsigned)b, hi = (int)(unsigned)(b >> 32);
+  double best = -2.0;
+  int slot = 0x7FFFFFFF;
+#pragma unroll
+  for (int row = 0; row < 4; ++row) {
+    const unsigned rl = (unsigned)__builtin_amdgcn_readlane(lo, 16 * row);
+    const unsigned rh = (unsigned)__builtin_amdgcn_readlane(hi, 16 * row);
+    arg_merge(best, slot, __longlong_as_double((long long)(((unsigned long long)rh << 32) | rl)),
+              __builtin_amdgcn_readlane(bs, 16 * row));
+  }
+  bp = best;
+  bs = slot;
+}
+
+// The wave's largest value (DPP steps within rows of 16 lanes, then the four
+// row results read as uniform values).
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const unsigned lo = (unsigned)dppi<CTRL>((int)(unsigned)b), hi = (unsigned)dppi<CTRL>((int)(unsigned)(b >> 32));
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+__device__ __forceinline__ double read_lane(double v, int src) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)b, src);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(b >> 32), src);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+__device__ __forceinline__ double wave_max(double v) {
+  v = fmax(v, dpp_d<0xB1>(v));
+  v = fmax(v, dpp_d<0x4E>(v));
+  v = fmax(v, dpp_d<0x141>(v));
+  v = fmax(v, dpp_d<0x140>(v));
+  return fmax(fmax(read_lane(v, 0), read_lane(v, 16)), fmax(read_lane(v, 32), read_lane(v, 48)));
+}
+
 __global__ __launch_bounds__(64) void tree_build_kernel(const double *p, int D, int R, int N, int32_t *parent,
                                                         int32_t *depth, int32_t *rank, double *prio,
                                                         uint64_t *anc, int32_t *count) {
@@ -67,7 +115,63 @@ __global__ __launch_bounds__(64) void tree_build_kernel(const double *p, int D, 
     cp[j] = s < R ? p[s] : -1.0;   // depth-1 paths; -1 marks a dead or unwritten slot
   }
   __syncthreads();
+  // Every row the build reads non-increasing in rank: a node's children are
+  // then popped in rank order (an earlier sibling has the larger or equal
+  // priority and the smaller slot), so the best live slot is always some
+  // node's next child.  Lane l keeps only that candidate for node l - 1
+  // (lane 0: the root), and a step is one argmax over 64 values.  The
+  // products and the tie order are those of the full candidate set.
+  bool ok = true;
+  for (int i = lane; i < rows * R; i += 64)
+    if (i % R + 1 < R && pl[i + 1] > pl[i]) ok = false;
   int k = 0;
+  if (__ballot(!ok) == 0) {
+    double P = 1.0;                       // the node's priority (root: 1)
+    int dep = 0, nr = 0;                  // the node's depth, its next child's rank
+    uint64_t an = 0;                      // the node's ancestor mask
+    double cand = lane == 0 ? pl[0] : -1.0;
+    // requested ahead, so no step waits on LDS: the probability of the
+    // candidate's next sibling, and lane d's rank-0 probability at depth d
+    double pn = lane == 0 && R > 1 ? pl[1] : 0.0;
+    const double p0 = lane < rows ? pl[lane * R] : 0.0;
+    for (; k < N; ++k) {
+      // lane l's candidate slot lies in [R l, R l + R): slot order is lane
+      // order, so the smallest slot of the best priority is the lowest lane
+      // holding it
+      const double bp = wave_max(cand);
+      if (bp < 0.0) break;   // no live candidate (uniform)
+      const int w = __builtin_ctzll(__ballot(cand == bp));   // the winner's lane: its parent + 1
+      const int rk = __builtin_amdgcn_readlane(nr, w);
+      const int wdep = __builtin_amdgcn_readlane(dep, w);
+      const uint64_t wan = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)an, w) |
+                           ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(an >> 32), w) << 32);
+      const int ndp = wdep + 1;
+      const uint64_t am = wan | (1ull << k);
+      if (lane == w) {   // the parent's next child
+        nr = rk + 1;
+        cand = nr < R ? P * pn : -1.0;
+        pn = nr + 1 < R ? pl[dep * R + nr + 1] : 0.0;
+      }
+      // rank-0 probability at the new node's depth (its first child's factor)
+      const double f0 = read_lane(p0, min(ndp, 63));
+      if (lane == k + 1) {   // node k and its first child
+        P = bp;
+        dep = ndp;
+        an = am;
+        nr = 0;
+        cand = ndp < D ? bp * f0 : -1.0;
+        pn = ndp < D && R > 1 ? pl[ndp * R + 1] : 0.0;
+      }
+      if (lane == 0) {
+        ndep[k] = ndp;
+        nanc[k] = am;
+        npar[k] = w - 1;
+        nrank[k] = rk;
+        nprio[k] = bp;
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  } else {
   for (; k < N; ++k) {
     double bp = -1.0;
     int bs = 0x7FFFFFFF;
@@ -77,14 +181,7 @@ __global__ __launch_bounds__(64) void tree_build_kernel(const double *p, int D, 
         bp = cp[j];
         bs = lane + 64 * j;
       }
-    // within rows of 16 lanes by DPP (pairs, quads, half-row and row
-    // mirrors), then across rows by two lane exchanges
-    arg_dpp<0xB1>(bp, bs);
-    arg_dpp<0x4E>(bp, bs);
-    arg_dpp<0x141>(bp, bs);
-    arg_dpp<0x140>(bp, bs);
-    arg_merge(bp, bs, __shfl_xor(bp, 16), __shfl_xor(bs, 16));
-    arg_merge(bp, bs, __shfl_xor(bp, 32), __shfl_xor(bs, 32));
+    wave_argmax(bp, bs);
     if (bp < 0.0) break;   // no live candidate (uniform)
     const int par = bs < R ? -1 : (bs - R) / R;
     const int rk = bs < R ? bs : (bs - R) % R;
@@ -113,6 +210,7 @@ __global__ __launch_bounds__(64) void tree_build_kernel(const double *p, int D, 
     // one wave: its LDS accesses complete in program order, so the next
     // step's reads see these writes; the clobber keeps the compiler's order
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
   }
   if (lane < k) {   // the nodes go out together, one per lane (N <= 64)
     parent[lane] = npar[lane];

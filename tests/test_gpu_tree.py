@@ -36,7 +36,13 @@ CASES = [("stats-8x16-64", synth.make_rank_stats(8, 16, cfg=80), 64),
          ("ties", np.full((3, 4), 0.5), 40),
          ("zeros", np.r_[[[0.6, 0.3, 0.0, 0.0]], [[0.5, 0.0, 0.5, 0.0]]], 20),   # fewer live paths than N
          ("chain", np.full((70, 1), 0.9), 64),
-         ("short", np.array([[0.7, 0.2, 0.1]]), 10)]
+         ("short", np.array([[0.7, 0.2, 0.1]]), 10),
+         # rows non-increasing in rank (the one-candidate-per-node path), with
+         # ties and zeros; and the same statistics with one row out of order
+         # (the path that keeps every candidate)
+         ("sorted-ties-zeros", np.array([[0.5, 0.5, 0.25, 0.0], [1.0, 0.5, 0.5, 0.0], [0.25, 0.25, 0.0, 0.0]]), 64),
+         ("sorted-random", -np.sort(-np.random.default_rng(7).uniform(0, 1, (9, 16)) ** 3, axis=1), 64),
+         ("unsorted-row", synth.make_rank_stats(8, 16, cfg=80)[:, [0, 1, 2, 3, 5, 4] + list(range(6, 16))], 64)]
 
 
 @pytest.mark.parametrize("name,p,N", CASES, ids=[c[0] for c in CASES])
