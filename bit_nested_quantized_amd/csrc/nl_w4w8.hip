@@ -1,7 +1,8 @@
 // nl_w4w8.hip -- the BitNest W4/W8 dual-plane linear (include/nested_w4w8.h).
 //
 // One launch per call.  A workgroup (8 waves) owns 128 rows and one K-split
-// of whole 128-column groups (about one workgroup per CU):
+// of whole 128-column groups (about one workgroup per CU), or, for small
+// T * d_in, 16, 32 or 64 rows and the whole K-range (see w48_kernel):
 //   * it converts its K-range of x into LDS as fp16 (the T real tokens only,
 //     in pieces when the range does not fit), each (token, group)
 //     scaled by a power of two that puts its largest magnitude in
@@ -146,7 +147,12 @@ __device__ __forceinline__ void unpack(const uint4 &b, const uint4 &r, uint32_t 
   }
 }
 
-template <bool VERIFY, int MT>
+// RT: row tiles per workgroup.  RT = 8: each wave owns one 16-row tile of a
+// 128-row block over the split's groups.  RT < 8 (one token tile, the whole
+// K-range in the workgroup): the 8 / RT waves of a tile take every
+// (8 / RT)-th group and add their accumulators through LDS, so no split-K
+// hand-over is needed.
+template <bool VERIFY, int MT, int RT>
 // Two workgroups per CU (4 waves per SIMD, <= 128 VGPRs) up to two token
 // tiles; with three or four the accumulators need more registers and one
 // workgroup per CU runs.
@@ -155,6 +161,7 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
   constexpr int T16 = MT * 16;
   constexpr float kBias = VERIFY ? 1160.0f : 1032.0f;
   constexpr int kRing = ring_depth<VERIFY, MT>();
+  constexpr int KW = 8 / RT, RB = 16 * RT;   // waves per tile, rows per block
   _Float16 *xs = reinterpret_cast<_Float16 *>(smem);
   // x' holds the T real tokens only; meta (inverse scale, bias * sum) all
   // T16 tokens of the tiles, zero past T
@@ -163,9 +170,18 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
   const int rb = blockIdx.x / a.S, sp = blockIdx.x - rb * a.S;
   const int g0 = sp * a.gps;
   const int ng = min(a.G, g0 + a.gps) - g0;
-  const int row = rb * kRows + wave * 16 + (lane & 15);
+  const int tl = wave % RT, ks = wave / RT;   // the wave's tile and K share
+  const int row = rb * RB + tl * 16 + (lane & 15);
   const int kb = lane >> 4;
-  const size_t tile = (size_t)rb * (kRows / 16) + wave;
+  const size_t tile = (size_t)rb * RT + tl;
+  // the wave's groups: split group ks + KW j for j < nwg; gidx(j) the group
+  // a load names (clamped into the split)
+  const int nwg = KW == 1 ? ng : ng > ks ? (ng - ks + KW - 1) / KW : 0;
+  const int nwc = max(nwg, 1) - 1;
+  auto gidx = [&](int j) {
+    if constexpr (KW == 1) return g0 + min(j, ng - 1);
+    else return g0 + min(ks + KW * min(j, nwc), ng - 1);
+  };
   const uint8_t *bp = a.base + tile * a.G * 1024 + lane * 16;            // + g * 1024
   const uint8_t *rp = VERIFY ? a.ref + tile * a.G * 1024 + lane * 16 : nullptr;
   const uint16_t *sc = a.scales + tile * a.G * 16 + (lane & 15);          // + g * 16
@@ -177,7 +193,7 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
   uint16_t ws[kRing];
 #pragma unroll
   for (int i = 0; i < kRing; ++i) {
-    const int g = g0 + min(i, ng - 1);
+    const int g = gidx(i);
     wb[i] = *reinterpret_cast<const uint4 *>(bp + (size_t)g * 1024);
     if constexpr (VERIFY) wr[i] = *reinterpret_cast<const uint4 *>(rp + (size_t)g * 1024);
     ws[i] = sc[(size_t)g * 16];
@@ -252,7 +268,8 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
   int aoff[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) aoff[mt] = min(mt * 16 + (lane & 15), a.T - 1) * a.pitch;
-  const int ngp = (ng + kRing - 1) / kRing * kRing;
+  const int nw0 = (ng + KW - 1) / KW;   // the most groups a wave takes (ks = 0)
+  const int ngp = (nw0 + kRing - 1) / kRing * kRing;
   for (int gg = 0; gg < ngp; gg += kRing) {
     // With several pieces, pg is a multiple of the ring depth: a piece starts
     // at the top of a ring round.  Every wave is past the previous piece
@@ -266,9 +283,9 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
 #pragma unroll
     for (int i = 0; i < kRing; ++i) {
       // slots past the split's last group only keep the ring's loads going
-      const int gi = gg + i;
-      const bool live = gi < ng;   // uniform over the workgroup
-      const int gc = gi - pb;      // the group within the staged piece
+      const int j = gg + i;
+      const bool live = j < nwg;          // uniform over the wave
+      const int gc = ks + KW * j - pb;    // the group within the staged piece
       uint32_t B[4][4];
       float s = 0.0f;
       if (live) {
@@ -276,7 +293,7 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
         s = h2f(ws[i]) * sdiv;
       }
       {
-        const int g = g0 + min(gi + kRing, ng - 1);
+        const int g = gidx(j + kRing);
         wb[i] = *reinterpret_cast<const uint4 *>(bp + (size_t)g * 1024);
         if constexpr (VERIFY) wr[i] = *reinterpret_cast<const uint4 *>(rp + (size_t)g * 1024);
         ws[i] = sc[(size_t)g * 16];
@@ -307,9 +324,23 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
     }
   }
 
+  // the K shares of a tile, added in share order by its first wave
+  if constexpr (KW > 1) {
+    floatx4 *red = reinterpret_cast<floatx4 *>(smem);   // x' is no longer read
+    __syncthreads();
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) red[(wave * MT + mt) * 64 + lane] = yacc[mt];
+    __syncthreads();
+    if (ks == 0)
+      for (int k = 1; k < KW; ++k)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) yacc[mt] += red[((k * RT + tl) * MT + mt) * 64 + lane];
+  }
+  const bool writer = ks == 0;
+
   // outputs: token m = 16 mt + 4 kb + i of this lane's row
   if (a.S == 1) {
-    if (row < a.d_out)
+    if (writer && row < a.d_out)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -324,7 +355,7 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = mt * 16 + kb * 4 + i;
-      if (m < a.T) st_agent(a.part + ((size_t)sp * a.T + m) * a.rows_pad + row, yacc[mt][i]);
+      if (writer && m < a.T) st_agent(a.part + ((size_t)sp * a.T + m) * a.rows_pad + row, yacc[mt][i]);
     }
   stores_done();
   __syncthreads();
@@ -344,7 +375,7 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
   if ((size_t)a.S * pstride * 4 < 0x7FFFFFFFu) {
     const __amdgpu_buffer_rsrc_t pr =
         __builtin_amdgcn_make_buffer_rsrc(a.part, 0, (int)((size_t)a.S * pstride * 4), 0x00020000);
-    constexpr int kRuns = kRows / 4;
+    constexpr int kRuns = RB / 4;
     const int total = a.T * kRuns;
     for (int base = 0; base < total; base += 2 * kThreads) {
       if (base + t >= total) break;   // no barrier follows
@@ -353,7 +384,7 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int idx = base + u * kThreads + t, m = idx / kRuns, r4 = idx - m * kRuns;
-        o[u] = idx < total ? (uint32_t)((size_t)m * a.rows_pad + rb * kRows + 4 * r4) : ~0u;
+        o[u] = idx < total ? (uint32_t)((size_t)m * a.rows_pad + rb * RB + 4 * r4) : ~0u;
         v[u] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
       }
       for (int s0 = 0; s0 < a.S; s0 += 8) {
@@ -376,7 +407,7 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         if (o[u] == ~0u) continue;
-        const int idx = base + u * kThreads + t, m = idx / kRuns, r = rb * kRows + 4 * (idx - m * kRuns);
+        const int idx = base + u * kThreads + t, m = idx / kRuns, r = rb * RB + 4 * (idx - m * kRuns);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (r + i < a.d_out) a.y[(size_t)m * a.d_out + r + i] = v[u][i];
@@ -386,8 +417,8 @@ __global__ __launch_bounds__(kThreads, MT <= 2 ? 4 : 2) void w48_kernel(W48Args 
     return;
   }
   // partials in split order, eight loads in flight per output
-  for (int idx = t; idx < a.T * kRows; idx += kThreads) {
-    const int m = idx / kRows, r = rb * kRows + (idx - m * kRows);
+  for (int idx = t; idx < a.T * RB; idx += kThreads) {
+    const int m = idx / RB, r = rb * RB + (idx - m * RB);
     const float *pp = a.part + (size_t)m * a.rows_pad + r;
     const size_t stride = (size_t)a.T * a.rows_pad;
     float acc = 0.0f;
@@ -465,21 +496,48 @@ bool valid(nl_w4w8_handle h) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Plan {
-  int mt, S, gps, pg, pitch;
+  int mt, rt, S, gps, pg, pitch;
   size_t lds, tick_bytes, part_bytes;
   size_t total() const { return tick_bytes + part_bytes; }
 };
+
+// A workgroup may hold the whole K-range of x' and split it among the waves
+// of each tile (no split-K hand-over) up to one token tile and T * d_in <=
+// 16384 (each workgroup then stages all of x: down, 4096x14336, lost 0.3 us
+// at T = 1 and 1-4 us at T = 2-4 where q/o, k/v and gate/up gained 1-2 us);
+// the LDS that form may use (one workgroup per CU).
+constexpr int kKwMaxTG = 128;   // T times the groups of 128 columns
+constexpr int kKwLds = 150 * 1024;
 
 // Split count: one workgroup per CU in one round (measured best at every T
 // on the 7B/8B-class shapes, also where two would fit: 256 workgroups beat
 // 512), but at least four groups per split, so that the split sums of small
 // shapes stay few.  A K-range whose x' does not fit the LDS is staged in
-// pieces of whole ring rounds.
+// pieces of whole ring rounds.  For small T * d_in (kKwMaxTG), when the
+// whole x' fits, a workgroup takes the whole K-range of 16 RT rows instead,
+// RT the fewest row tiles (1, 2 or 4) that keep the grid within one round.
 Plan make_plan(const nl_w4w8 *h, int T, bool verify) {
   Plan p{};
   p.mt = (T + 15) / 16;
   const int T16 = 16 * p.mt;
   const int ring = verify && p.mt == 2 ? ring_depth<true, 2>() : ring_depth<false, 1>();
+  p.rt = 8;
+  if (p.mt == 1 && T * h->G <= kKwMaxTG) {
+    int rt = 1;
+    while (rt < 8 && h->rows_pad / (16 * rt) > kCus) rt *= 2;
+    const size_t whole = (size_t)T * (h->G * kGroup + 8) * 2 + (size_t)h->G * T16 * 8;
+    if (rt < 8 && whole <= (size_t)kKwLds) {
+      p.rt = rt;
+      p.S = 1;
+      p.gps = p.pg = h->G;
+      p.pitch = h->G * kGroup + 8;
+      // the tiles' K shares are added through the same LDS
+      p.lds = std::max(whole, (size_t)kThreads / 64 * p.mt * 64 * 16);
+      p.tick_bytes = align256((size_t)(h->rows_pad / (16 * rt)) * 4);
+      p.part_bytes = 0;
+      return p;
+    }
+  }
   // per group: T rows of 128 fp16 and T16 (inverse scale, bias * sum) pairs;
   // per row 16 bytes of padding
   const int gps_max = std::max(1, (lds_budget(p.mt) - 16 * T) / (256 * T + 8 * T16));
@@ -500,32 +558,42 @@ Plan make_plan(const nl_w4w8 *h, int T, bool verify) {
 hipError_t allow_lds() {
   static hipError_t e = [] {
     hipError_t r = hipSuccess;
-    auto set = [&](const void *f) {
-      if (r == hipSuccess) r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds_budget(3));
+    auto set = [&](const void *f, int bytes) {
+      if (r == hipSuccess) r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     };
-    set(reinterpret_cast<const void *>(&w48_kernel<true, 3>));
-    set(reinterpret_cast<const void *>(&w48_kernel<true, 4>));
-    set(reinterpret_cast<const void *>(&w48_kernel<false, 3>));
-    set(reinterpret_cast<const void *>(&w48_kernel<false, 4>));
+    set(reinterpret_cast<const void *>(&w48_kernel<true, 3, 8>), lds_budget(3));
+    set(reinterpret_cast<const void *>(&w48_kernel<true, 4, 8>), lds_budget(3));
+    set(reinterpret_cast<const void *>(&w48_kernel<false, 3, 8>), lds_budget(3));
+    set(reinterpret_cast<const void *>(&w48_kernel<false, 4, 8>), lds_budget(3));
+    set(reinterpret_cast<const void *>(&w48_kernel<true, 1, 1>), kKwLds);
+    set(reinterpret_cast<const void *>(&w48_kernel<true, 1, 2>), kKwLds);
+    set(reinterpret_cast<const void *>(&w48_kernel<true, 1, 4>), kKwLds);
+    set(reinterpret_cast<const void *>(&w48_kernel<false, 1, 1>), kKwLds);
+    set(reinterpret_cast<const void *>(&w48_kernel<false, 1, 2>), kKwLds);
+    set(reinterpret_cast<const void *>(&w48_kernel<false, 1, 4>), kKwLds);
     return r;
   }();
   return e;
 }
 
-template <bool V, int MT>
+template <bool V, int MT, int RT>
 hipError_t launch_mt(const W48Args &a, const Plan &p, hipStream_t s) {
-  const dim3 grid((unsigned)(a.rows_pad / kRows * p.S)), block(kThreads);
-  hipLaunchKernelGGL((w48_kernel<V, MT>), grid, block, p.lds, s, a);
+  const dim3 grid((unsigned)(a.rows_pad / (16 * RT) * p.S)), block(kThreads);
+  hipLaunchKernelGGL((w48_kernel<V, MT, RT>), grid, block, p.lds, s, a);
   return hipGetLastError();
 }
 
 template <bool V>
 hipError_t launch(const W48Args &a, const Plan &p, hipStream_t s) {
+  if (p.mt == 1 && p.rt == 1) return launch_mt<V, 1, 1>(a, p, s);
+  if (p.mt == 1 && p.rt == 2) return launch_mt<V, 1, 2>(a, p, s);
+  if (p.mt == 1 && p.rt == 4) return launch_mt<V, 1, 4>(a, p, s);
+  if (p.rt != 8) return hipErrorInvalidValue;
   switch (p.mt) {
-    case 1: return launch_mt<V, 1>(a, p, s);
-    case 2: return launch_mt<V, 2>(a, p, s);
-    case 3: return launch_mt<V, 3>(a, p, s);
-    case 4: return launch_mt<V, 4>(a, p, s);
+    case 1: return launch_mt<V, 1, 8>(a, p, s);
+    case 2: return launch_mt<V, 2, 8>(a, p, s);
+    case 3: return launch_mt<V, 3, 8>(a, p, s);
+    case 4: return launch_mt<V, 4, 8>(a, p, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -540,7 +608,7 @@ nl_status forward(nl_w4w8_handle h, bool verify, const void *x, int32_t T, float
   if ((uintptr_t)ws & 255) return fail(NL_EINVAL, "%s: ws must be 256-byte aligned", who);
   if (verify && !h->has_ref) return fail(NL_EINVAL, "%s: the linear has no refinement plane", who);
   const Plan p = make_plan(h, T, verify);
-  if (p.pg < 1 || p.lds > (size_t)lds_budget(p.mt))
+  if (p.pg < 1 || p.lds > (size_t)(p.rt < 8 ? kKwLds : lds_budget(p.mt)))
     return fail(NL_EUNSUPPORTED, "%s: no LDS plan for T = %d", who, T);
   if (ws_bytes < p.total())
     return fail(NL_EINVAL, "%s: workspace of %zu bytes is smaller than %zu", who, ws_bytes, p.total());

@@ -133,7 +133,7 @@ FULL = [("q/o", 4096, 4096), ("k/v", 1024, 4096), ("gate/up", 14336, 4096), ("do
 
 
 @pytest.mark.parametrize("name,d_out,d_in", FULL, ids=[f[0] for f in FULL])
-@pytest.mark.parametrize("T", [16, 64])
+@pytest.mark.parametrize("T", [4, 16, 64])
 def test_full_size_sampled_rows(nl, torch_cuda, name, d_out, d_in, T):
     lin = synth.make_w4w8_linear(d_out, d_in, cfg=55, idx=d_out + d_in)
     x = synth.make_x(T, d_in, cfg=55, idx=1)
@@ -146,6 +146,27 @@ def test_full_size_sampled_rows(nl, torch_cuda, name, d_out, d_in, T):
             for r0, r1 in [(0, 64), (mid, mid + 64), (d_out - 64, d_out)]:
                 ref = w48.forward(lin, x, verify, rows=(r0, r1))
                 assert np.abs(y[:, r0:r1] - ref).max() <= TOL * np.abs(ref).max(), (verify, r0)
+    finally:
+        L.close()
+
+
+RT_SHAPES = [(6000, 1024), (14336, 512)]
+
+
+@pytest.mark.parametrize("d_out,d_in", RT_SHAPES, ids=[f"{a}x{b}" for a, b in RT_SHAPES])
+@pytest.mark.parametrize("T", [1, 2, 4])
+def test_row_tiles_with_k_shares(nl, torch_cuda, d_out, d_in, T):
+    """For small T * d_in a workgroup holds the whole K-range and splits it
+    among the waves of each of its 16-row tiles: 376 tiles take two tiles
+    per workgroup, 896 take four (the smaller shapes above take one)."""
+    lin = synth.make_w4w8_linear(d_out, d_in, cfg=57, idx=d_out)
+    x = synth.make_x(T, d_in, cfg=57, idx=T)
+    L = nl.W4W8Linear(lin)
+    try:
+        ws = L.workspace(T)
+        for verify in (False, True):
+            y = L.forward(xdev(torch_cuda, x), verify, ws=ws)
+            check(y, w48.forward(lin, x, verify))
     finally:
         L.close()
 
