@@ -60,7 +60,7 @@ ENC_KERNEL_NAME = "tile_kernel<0, 7, LOG2B>"
 ENC_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encoder_tile_kernel_7bit_fused_proj7b8b_traffic.txt")
 FIT_ROWS = 512          # 512 x 4096 = 2^21 samples, the post's ~2M
 W48_TS = (1, 16, 64)
-W48_KERNEL = "w48_kernel<true, 1>"   # verify, one 16-token tile
+W48_KERNEL = "w48_kernel<true, 1, 8>"   # verify, one 16-token tile, 128-row workgroups
 W48_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w48_kernel_verify_T16_proj7b8b_traffic.txt")
 W48_SOURCES = ("nl_w4w8.hip",)
 KV_KERNEL = "kv_attn_mfma_kernel<true, false>"   # verify attention over KV8, query rows split over waves
