@@ -11,7 +11,8 @@ POC recipe:
              code = nearest of 4 Lloyd-Max levels times that scale; levels
              fitted on RMS-normalised rotated weights from the quantiles
              0.125/0.375/0.625/0.875, 60 Lloyd iterations, then symmetrised;
-  section 3  R~ = W~ - Q_base, uniform symmetric b-bit with levels -qm..qm,
+  section 3  R~ = W~ - Q_base on an evenly spaced b-bit grid centred on 0,
+             levels -qm..qm,
              qm = 2^(b-1) - 1, scale = max|block| / qm in fp16.
 GPTQ/LDLQ (the post's calibrated variant of sections 2-3) needs calibration
 data and is not modelled: this is the plain round-to-nearest quantiser.
