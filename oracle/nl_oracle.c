@@ -13,7 +13,7 @@
  *              divides n, capped at 4096; x' = H_i S_i x, y = S_o H_o y~.
  *   section 2  2-bit base: 2 bit-planes + one fp16 scale per (row, 128-group),
  *              code -> one of 4 Lloyd-Max levels times the scale.
- *   section 3  residual: uniform symmetric b-bit integers times one fp16
+ *   section 3  residual: b-bit integers on an evenly spaced grid centred on 0, times one fp16
  *              scale per (row, 128-group), in the same rotated basis.
  *   section 4  verifier forward for one Linear: y~ = (Q_base + Q_resid) x',
  *              draft forward = the same without the residual term.
