@@ -474,6 +474,32 @@ __global__ __launch_bounds__(256) void kv_attn_mfma_kernel(AttnArgs a) {
   }
 }
 
+// Max and sum over the 64 lanes of a wave (all active): DPP steps within
+// rows of 16 lanes (quad swaps, half-row and row mirrors; a shuffle through
+// LDS waits ~100 cycles per step), then the four row results read as
+// uniform values.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_lane(float v, int src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return fmaxf(fmaxf(row_lane(v, 0), row_lane(v, 16)), fmaxf(row_lane(v, 32), row_lane(v, 48)));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  return (row_lane(v, 0) + row_lane(v, 16)) + (row_lane(v, 32) + row_lane(v, 48));
+}
+
 // One workgroup per (KV head, query row): wave 0 turns the chunks' maxima
 // and sums into weights (at most 64 chunks, one per lane), then four waves
 // add the weighted chunk outputs, all loads in flight, 2 dimensions a lane.
@@ -498,11 +524,9 @@ __global__ __launch_bounds__(256) void kv_combine_kernel(AttnArgs a, int chunks,
     const size_t base = ((size_t)tid * a.H_kv + h) * a.RQ + r;
     const float mc = tid < chunks ? a.part_ml[base * 2] : -INFINITY;
     const float lc = tid < chunks ? a.part_ml[base * 2 + 1] : 0.0f;
-    float M = mc;
-    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    const float M = wave_max(mc);
     const float w = mc == -INFINITY ? 0.0f : exp2f(mc - M);   // a chunk with no visible key weighs 0
-    float ls = lc * w;
-    for (int o = 32; o >= 1; o >>= 1) ls += __shfl_xor(ls, o);
+    const float ls = wave_sum(lc * w);
     wsh[tid] = w;
     if (tid == 0) lsh = ls;
   }
