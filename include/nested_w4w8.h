@@ -72,9 +72,11 @@ nl_status nested_w4w8_workspace_bytes(nl_w4w8_handle h, int32_t T_max, size_t *b
 /*
  * Verify forward y = W_target x (eq. 10) and draft forward y = W_draft x
  * (eq. 6).  x [T][d_in] bf16 bit patterns, 16-byte aligned; y [T][d_out]
- * fp32 (must not overlap x or ws).  One kernel launch per call; the
- * workgroups of a row block that finish last sum the split-K partials in
- * split order, so results do not depend on timing.
+ * fp32 (must not overlap x or ws).  One kernel launch per call.  Where K is
+ * split across workgroups, the workgroup of a row block that finishes last
+ * sums the split-K partials in split order; for small T * d_in the waves of
+ * one workgroup split K and add their sums in wave order.  Either way
+ * results do not depend on timing.
  * Errors: NL_EINVAL (NULL pointer, T < 1, misaligned x, small or misaligned
  * ws, verify on a draft-only linear), NL_EUNSUPPORTED (T > 64), NL_EHIP.
  */
